@@ -1,0 +1,49 @@
+"""The CPU oracle against its pins (hand-worked examples, the matrix form, closed forms,
+the LTI convolution, associative-scan order, split/resume, linearity, group sharing), and
+the chunked fp64 model against the oracle for many chunk lengths."""
+import numpy as np
+import pytest
+
+import oracle
+from pins import ALL_PINS, _problem, _close
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default_oracle()
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+@pytest.mark.parametrize("diag", [False, True])
+@pytest.mark.parametrize("chunk", [1, 5, 16, 32, 64, 100, 256])
+def test_chunked_model_matches_recurrence(orc, diag, chunk):
+    """Chunk-size invariance of the two-algorithm form (aiwiki "State Space Duality": the two
+    halves of the loop are separated by the chunk boundary and nothing else), including a
+    last chunk shorter than the others."""
+    rng = np.random.default_rng(100 + chunk)
+    prob = _problem(rng, nb=2, T=100, H=4, G=2, P=5, N=6, diag=diag, decay_scale=3.0)
+    y, fin = orc.forward(*prob)
+    yc, fc = oracle.chunked_forward(*prob, chunk=chunk)
+    _close(yc, y, "chunked y", rtol=1e-11)
+    _close(fc, fin, "chunked final", rtol=1e-11)
+
+
+def test_oracle_empty_sequence(orc):
+    """T = 0: no outputs, the final state is the initial state."""
+    rng = np.random.default_rng(5)
+    x, log_a, Bm, Cm, D, h0 = _problem(rng, nb=2, T=0, H=2, G=1, P=3, N=4)
+    y, fin = orc.forward(x, log_a, Bm, Cm, D, h0)
+    assert y.shape == (2, 0, 2, 3)
+    assert np.array_equal(fin, h0)
+
+
+def test_oracle_threads_do_not_change_result(orc):
+    rng = np.random.default_rng(6)
+    prob = _problem(rng, nb=3, T=50, H=4, G=2, P=4, N=5)
+    y1, f1 = orc.forward(*prob, nthreads=1)
+    y4, f4 = orc.forward(*prob, nthreads=4)
+    assert np.array_equal(y1, y4) and np.array_equal(f1, f4)
