@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked SSD forward on one MI355X.
+
+Prints ONE JSON line on stdout: tokens/s of ssd_forward on the Mamba-2 layer workload
+(B=8, T=2048, H=24, G=1, P=64, N=128, chunk 128, bf16 x/B/C/y, fp32 log a, D and state),
+with TFLOP/s, fraction of MFMA peak, the HBM roofline of the dominant kernel (timed live
+with HIP events recorded around each launch on the launch stream) and the fp64 CPU
+oracle's throughput on this host as a reported baseline.
+
+A step is one ssd_forward over one batch.  Inputs are drawn once (seeded, synthetic) and
+copied to HBM before timing; the timed steps cycle through several copies of the inputs
+and outputs (about 1 GB together) so that no step finds its data in the 256 MB
+last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "walk_kernel_mamba2_layer_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "ssd_chunked_scan_02_amd", "csrc", "ssd_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_counts(cfg):
+    """Work the method must do for one forward over the workload (not what a kernel
+    executes): causal C B^T and (S o L) X inside chunks, plus the chunk-state and carried-
+    state contractions; bytes = every input read once and every output written once."""
+    Bsz, T, H, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["ngroups"]
+    P, N, Q = cfg["headdim"], cfg["dstate"], cfg["chunk"]
+    diag = cfg["decay"] == "diag"
+    Gs = H if diag else G
+    K = N if diag else 1
+    sx = 4 if cfg["dtype"] == "fp32" else 2
+    flops = Bsz * T * (Gs * N * (Q + 1) + H * P * (Q + 1) + 4 * H * N * P)
+    per_token = H * P * (sx + sx) + 2 * G * N * sx + 4 * H * K
+    nbytes = Bsz * T * per_token + (4 * H if cfg["skip"] else 0) \
+        + 4 * Bsz * H * N * P * (int(cfg["init"]) + int(cfg["final"]))
+    return flops, nbytes, per_token
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self):
+        h = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return float(out.value)
+
+    def destroy(self, h):
+        self.lib.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the walk kernel from the committed rocprofv3 counter summary,
+    or None when absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, cfg, min_seconds):
+    """The fp64 oracle as it stands, on this host's cores, over the whole workload, repeated
+    until at least ``min_seconds`` of CPU wall time."""
+    import oracle
+    import ssd_inputs
+    f = ssd_inputs.to_f64
+    args = [f(inp["x"]), f(inp["log_a"]), f(inp["B"]), f(inp["C"]), f(inp.get("D")),
+            f(inp.get("init_state"))]
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(*args, want_final=cfg["final"], nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds and reps >= 1:
+            break
+    tokens = cfg["batch"] * cfg["seqlen"] * reps
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole workload (%d x %d tokens x %d heads), %d run(s) in %.1f s, "
+                      "fp64 sequential recurrence, OpenMP over (batch, head)"
+                      % (cfg["batch"], cfg["seqlen"], cfg["nheads"], reps, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mamba2_layer")
+    ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ssd_inputs
+    import ssd_chunked_scan_02_amd as ssd
+
+    cfg = ssd_inputs.config(args.workload)
+    seed = ssd_inputs.SEEDS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = ssd_inputs.make_inputs(cfg, seed)
+    flops, nbytes, per_token = algorithmic_counts(cfg)
+    copies = args.copies or max(2, math.ceil(1.0e9 / nbytes))
+    log("workload %s seed %d: %.2f GFLOP, %.1f MB algorithmic per step, %d copies"
+        % (args.workload, seed, flops / 1e9, nbytes / 1e6, copies))
+
+    bufs = []
+    for _ in range(copies):
+        g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+        g["y"] = torch.empty_like(g["x"])
+        g["final"] = (torch.empty((cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"]),
+                                  dtype=torch.float32, device=dev) if cfg["final"] else None)
+        bufs.append(g)
+    dims = ssd.dims_for(bufs[0]["x"], bufs[0]["log_a"], bufs[0]["B"])
+    ws = torch.empty(max(1, ssd.ssd_forward_workspace_bytes(dims, cfg["chunk"])),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = HipEvents()
+
+    def step(i, events=None):
+        g = bufs[i % copies]
+        kw = dict(chunk=cfg["chunk"], init_state=g.get("init_state"), y=g["y"],
+                  final_state=g["final"], workspace=ws, stream=stream)
+        if events is None:
+            ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g.get("D"), **kw)
+            return None
+        return ssd.ssd_forward_profiled(g["x"], g["log_a"], g["B"], g["C"], g.get("D"),
+                                        events=events, **kw)[2]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    step_events = [[ev.create() for _ in range(ssd.SSD_MAX_LAUNCHES + 1)] for _ in range(K)]
+    begin, end = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.lib.hipEventRecord(begin, stream.cuda_stream)
+    launches = None
+    for i in range(K):
+        launches = step(i, step_events[i])
+    ev.lib.hipEventRecord(end, stream.cuda_stream)
+    torch.cuda.synchronize()
+    total_ms = ev.elapsed_ms(begin, end)
+    per_kernel = [[ev.elapsed_ms(e[k], e[k + 1]) for e in step_events] for k in range(launches)]
+    for e in step_events:
+        for h in e:
+            ev.destroy(h)
+
+    ms = total_ms / K
+    kernel_avg = [sum(v) / len(v) for v in per_kernel]
+    dom = max(range(launches), key=lambda k: kernel_avg[k])
+    names = ["scores_kernel", "walk_kernel"] if launches == 2 else ["kernel%d" % k for k in range(launches)]
+    log("ms/step %.4f; per kernel avg ms: %s" % (ms, ", ".join("%s %.4f" % (n, t) for n, t in zip(names, kernel_avg))))
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: %d MiB read + %d MiB written" % (args.calibrate_copy_mib, args.calibrate_copy_mib))
+
+    tokens = cfg["batch"] * cfg["seqlen"]
+    tok_s = tokens / (ms / 1e3)
+    tflops = flops / (ms / 1e3) / 1e12
+    peak_tf = FP32_PEAK_TFLOPS if cfg["dtype"] == "fp32" else BF16_PEAK_TFLOPS
+    dom_ms = kernel_avg[dom]
+    achieved = nbytes / (dom_ms / 1e3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": "SSD forward tokens/s + TFLOP/s (% MFMA peak) at B=8,T=2048,H=24,P=64,N=128",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded; x~N(0,1), B,C~N(0,1/N), log a=-softplus(dt)exp(A_log))",
+        "config": {"workload": args.workload, "batch": cfg["batch"], "seqlen": cfg["seqlen"],
+                   "nheads": cfg["nheads"], "ngroups": cfg["ngroups"], "headdim": cfg["headdim"],
+                   "dstate": cfg["dstate"], "chunk": cfg["chunk"], "decay": cfg["decay"],
+                   "parallelism": "single GPU"},
+        "tflops": tflops,
+        "mfma_peak_frac": tflops / peak_tf,
+        "hbm_gbs_whole_step": nbytes / (ms / 1e3) / 1e9,
+        "kernels_ms": {n: t for n, t in zip(names, kernel_avg)},
+        "roofline": {"kernel": names[dom], "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "bytes_per_token": per_token, "tokens_per_launch": tokens},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle (>= %.0f s)..." % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

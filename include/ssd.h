@@ -1,0 +1,133 @@
+/*
+ * ssd.h - C ABI of libssd: the chunked Structured State-Space Duality (SSD) forward pass
+ * and its single-token decode step, as HIP kernels for MI355X (gfx950).
+ *
+ * The operator (llms.blog "State Space Models and Mamba", sections "Continuous-to-Discrete
+ * Discretization" and "The SSD Theoretical Equivalence"; per-state-dimension decay from
+ * "On Structured State-Space Duality", ICML 2026 poster, abstract item (i)): for every batch
+ * entry b and head h, with B/C group g = h / (H/G) ("Multi-Head State Space Layers"),
+ *
+ *     h_t = a_t * h_{t-1} + B_t x_t^T          a_t = exp(log_a[b,t,h])   (scalar decay)
+ *                                              a_t = diag(exp(log_a[b,t,h,:]))  (diagonal)
+ *     y_t = C_t^T h_t + D_h x_t
+ *
+ * with h an N x P fp32 state per (b, h), h_{-1} = init_state (or zeros).  ssd_forward
+ * evaluates it chunk by chunk (aiwiki "State Space Duality", "Two algorithms for one
+ * operator"; llms.blog "The Chunk-Wise SSD Algorithm"): inside a chunk of `chunk` tokens the
+ * quadratic masked form (L o C B^T) X on matrix cores, between chunks one N x P state.
+ *
+ * Layouts: dense, row-major, last index fastest, no padding between rows.
+ *     x, y          [B, T, H, P]    element type `dtype`
+ *     log_a         [B, T, H] (SSD_DECAY_SCALAR) or [B, T, H, N] (SSD_DECAY_DIAG), fp32
+ *     B, C          [B, T, G, N]    element type `dtype`
+ *     D             [H] fp32, may be NULL (no skip term)
+ *     init_state, final_state, state   [B, H, N, P] fp32
+ *
+ * Ownership: every pointer belongs to the caller; the library never allocates, frees or
+ * retains device memory, and keeps no state between calls.  Tensor pointers are DEVICE
+ * pointers; `dims` is a HOST pointer read during the call only.  Work is enqueued on
+ * `stream` (a hipStream_t passed as an opaque pointer; NULL = the default stream) and the
+ * call returns without synchronising: outputs are valid once the stream has reached this
+ * point.  Inputs must not alias outputs (except ssd_step's in-place state).
+ *
+ * Errors: every function returns 0 (SSD_OK) or a negative code, and every argument check
+ * runs before any HIP call, so an invalid call has no effect.  Values are not checked:
+ * log_a must be finite and <= 0 (a in (0, 1]); NaN/Inf inputs propagate to the outputs.
+ * SSD_ERR_HIP reports a failed launch; faults during execution surface at the caller's
+ * next synchronisation of the stream.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of x, B, C, y (log_a, D and states are always fp32). */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Shape of log_a: one decay per (b, t, h), or one per (b, t, h, n). */
+typedef enum { SSD_DECAY_SCALAR = 0, SSD_DECAY_DIAG = 1 } ssd_decay;
+
+typedef struct {
+    int64_t batch;    /* B  >= 0 */
+    int64_t seqlen;   /* T  >= 0 (ssd_step ignores it) */
+    int64_t nheads;   /* H  >= 1 */
+    int64_t ngroups;  /* G  >= 1, divides H */
+    int64_t headdim;  /* P: 16, 32, 64 or 128 */
+    int64_t dstate;   /* N: 16 (fp32 only), 32, 64, 128 or 256; N * P <= 16384 */
+    int32_t dtype;    /* ssd_dtype */
+    int32_t decay;    /* ssd_decay */
+} ssd_dims;
+
+enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID = -1,     /* NULL required pointer, bad dimension, workspace too small */
+    SSD_ERR_UNSUPPORTED = -2, /* valid but not implemented: chunk, N, P or dtype combination */
+    SSD_ERR_ALIGN = -3,       /* a tensor pointer is not 16-byte aligned */
+    SSD_ERR_HIP = -4          /* the HIP runtime rejected a launch */
+};
+
+/*
+ * Bytes of device workspace ssd_forward needs for these dims and chunk length (0 when the
+ * arguments are invalid or unsupported, or when no workspace is needed).  Pure host
+ * arithmetic, no HIP call.
+ */
+size_t ssd_forward_workspace_bytes(const ssd_dims* dims, int chunk);
+
+/*
+ * Chunked SSD forward over a whole sequence (aiwiki "State Space Duality", "Two algorithms
+ * for one operator"; llms.blog "The Chunk-Wise SSD Algorithm").
+ *
+ *   chunk         chunk length Q: 16, 32, 64, 128 or 256.  T need not be a multiple of Q:
+ *                 the last chunk is then shorter (same operator, same result).
+ *   D             [H] skip weights, or NULL for none.
+ *   init_state    state entering token 0, or NULL for zeros.
+ *   y             output [B,T,H,P] in `dtype` (fp32 accumulate, one rounding to bf16).
+ *   final_state   state after token T-1, or NULL to skip writing it.
+ *   workspace     device scratch of at least ssd_forward_workspace_bytes(dims, chunk) bytes
+ *                 (may be NULL when that is 0); its contents are undefined afterwards.
+ *   stream        hipStream_t as an opaque pointer (NULL = default stream).
+ */
+int ssd_forward(const ssd_dims* dims, const void* x, const float* log_a, const void* B,
+                const void* C, const float* D, int chunk, const float* init_state, void* y,
+                float* final_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssd_forward, and in addition records caller-created hipEvent_t handles (passed as opaque
+ * pointers) on `stream` around its kernel launches, for timing each kernel live:
+ * events[k] is recorded right before launch k and events[L] right after the last of the L
+ * launches the call makes; handles past index L are left untouched, and NULL handles are
+ * skipped.  *n_launches (a HOST pointer, may be NULL) receives L (L <= SSD_MAX_LAUNCHES).
+ * With events non-NULL, n_events must be at least SSD_MAX_LAUNCHES + 1, else the call fails
+ * with SSD_ERR_INVALID before doing anything.  Launch order of the scalar-decay path:
+ * 0 = score tiles C B^T, 1 = chunk walk (state and outputs).
+ */
+#define SSD_MAX_LAUNCHES 4
+int ssd_forward_profiled(const ssd_dims* dims, const void* x, const float* log_a, const void* B,
+                         const void* C, const float* D, int chunk, const float* init_state,
+                         void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream, void* const* events, int n_events, int* n_launches);
+
+/*
+ * One decode step for every (b, h): the recurrence above for a single token, updating
+ * `state` in place (llms.blog "The Duality of Inference and Training ...", item 1, linear
+ * recurrence with O(1) memory per step).  dims->seqlen is ignored.
+ *   state    [B,H,N,P] fp32, read and overwritten.
+ *   x_t      [B,H,P];  log_a_t [B,H] or [B,H,N];  B_t, C_t [B,G,N];  D [H] or NULL;
+ *   y_t      [B,H,P] output in `dtype`.
+ */
+int ssd_step(const ssd_dims* dims, float* state, const void* x_t, const float* log_a_t,
+             const void* B_t, const void* C_t, const float* D, void* y_t, void* stream);
+
+/* Static, human-readable description of a return code. */
+const char* ssd_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

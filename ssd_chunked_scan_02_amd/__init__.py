@@ -1,0 +1,215 @@
+"""Python binding of libssd, the MI355X (gfx950) chunked SSD forward.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libssd.so``; torch supplies device memory and the stream.  There is no fallback: if the
+library is not built, or a tensor is not on a GPU, the call raises.
+
+The functions carry the names of the C entry points declared in ``include/ssd.h``:
+  ssd_forward_workspace_bytes(dims, chunk) -> int
+  ssd_forward(x, log_a, B, C, D=None, chunk=..., init_state=None, y=None,
+              final_state=None, workspace=None, stream=None) -> (y, final_state)
+  ssd_forward_profiled(..., events=(hipEvent_t handles)) -> (y, final_state, n_launches)
+  ssd_step(state, x_t, log_a_t, B_t, C_t, D=None, y_t=None, stream=None) -> y_t
+  ssd_strerror(code) -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["SSDError", "Dims", "library_path", "load_library", "dims_for",
+           "ssd_forward_workspace_bytes", "ssd_forward", "ssd_forward_profiled", "ssd_step",
+           "ssd_strerror",
+           "SSD_F32", "SSD_BF16", "SSD_DECAY_SCALAR", "SSD_DECAY_DIAG"]
+
+SSD_F32, SSD_BF16 = 0, 1
+SSD_DECAY_SCALAR, SSD_DECAY_DIAG = 0, 1
+SSD_OK, SSD_ERR_INVALID, SSD_ERR_UNSUPPORTED, SSD_ERR_ALIGN, SSD_ERR_HIP = 0, -1, -2, -3, -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (where, ssd_strerror(code), code))
+
+
+class Dims(ctypes.Structure):
+    """Mirror of ``ssd_dims``."""
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("decay", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.environ.get("SSD_LIBRARY", os.path.join(_HERE, "libssd.so"))
+
+
+_LIB = None
+
+
+def load_library():
+    """Load libssd.so (built in-tree by ``ssd_chunked_scan_02_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError("libssd.so is not built (%s); run "
+                               "`python -m ssd_chunked_scan_02_amd.build` first" % path)
+        lib = ctypes.CDLL(path)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        dp = ctypes.POINTER(Dims)
+        lib.ssd_forward_workspace_bytes.argtypes = [dp, i32]
+        lib.ssd_forward_workspace_bytes.restype = sz
+        lib.ssd_forward.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        lib.ssd_forward.restype = i32
+        lib.ssd_forward_profiled.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp,
+                                             ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
+        lib.ssd_forward_profiled.restype = i32
+        lib.ssd_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.ssd_step.restype = i32
+        lib.ssd_strerror.argtypes = [i32]
+        lib.ssd_strerror.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def ssd_strerror(code: int) -> str:
+    return load_library().ssd_strerror(int(code)).decode()
+
+
+def dims_for(x: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor) -> Dims:
+    """ssd_dims of a forward call: x [B,T,H,P], log_a [B,T,H] or [B,T,H,N], B [B,T,G,N]."""
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [B,T,H,P] and B [B,T,G,N]")
+    bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    decay = SSD_DECAY_DIAG if log_a.dim() == 4 else SSD_DECAY_SCALAR
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+    return Dims(bsz, T, H, G, P, N, _DTYPE_CODE[x.dtype], decay)
+
+
+def ssd_forward_workspace_bytes(dims: Dims, chunk: int) -> int:
+    return int(load_library().ssd_forward_workspace_bytes(ctypes.byref(dims), int(chunk)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_handle(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+SSD_MAX_LAUNCHES = 4
+
+
+def ssd_forward(x, log_a, B, C, D=None, chunk: int = 64, init_state=None, y=None,
+                final_state=None, workspace=None, stream=None):
+    """Run ``ssd_forward`` on the GPU.
+
+    ``y`` and the workspace are allocated when not given.  ``final_state`` may be a tensor
+    to write, True to allocate one, or None/False to skip it.  Returns (y, final_state).
+    """
+    return _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, stream)[:2]
+
+
+def ssd_forward_profiled(x, log_a, B, C, D=None, chunk: int = 64, init_state=None, y=None,
+                         final_state=None, workspace=None, stream=None, events=()):
+    """``ssd_forward_profiled``: as ssd_forward, recording the given hipEvent_t handles
+    (integers) around the kernel launches.  Returns (y, final_state, n_launches)."""
+    return _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, stream,
+                    events=list(events))
+
+
+def _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, stream,
+             events=None):
+    dims = dims_for(x, log_a, B)
+    dev = x.device
+    bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _check(x, "x", (bsz, T, H, P), x.dtype, dev)
+    la_shape = (bsz, T, H, N) if dims.decay == SSD_DECAY_DIAG else (bsz, T, H)
+    _check(log_a, "log_a", la_shape, torch.float32, dev)
+    _check(B, "B", (bsz, T, G, N), x.dtype, dev)
+    _check(C, "C", (bsz, T, G, N), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (bsz, H, N, P), torch.float32, dev)
+    if y is None:
+        y = torch.empty((bsz, T, H, P), dtype=x.dtype, device=dev)
+    _check(y, "y", (bsz, T, H, P), x.dtype, dev)
+    if final_state is True:
+        final_state = torch.empty((bsz, H, N, P), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    _check(final_state, "final_state", (bsz, H, N, P), torch.float32, dev)
+    lib = load_library()
+    need = int(lib.ssd_forward_workspace_bytes(ctypes.byref(dims), int(chunk)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(dims), _ptr(x), _ptr(log_a), _ptr(B), _ptr(C), _ptr(D), int(chunk),
+            _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(workspace), ws_bytes,
+            _stream_handle(stream, dev))
+    if events is None:
+        rc = lib.ssd_forward(*args)
+        launches = None
+    else:
+        n = max(len(events), SSD_MAX_LAUNCHES + 1)
+        arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+        count = ctypes.c_int(0)
+        rc = lib.ssd_forward_profiled(*args, arr, n, ctypes.byref(count))
+        launches = count.value
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_forward")
+    return y, final_state, launches
+
+
+def ssd_step(state, x_t, log_a_t, B_t, C_t, D=None, y_t=None, stream=None):
+    """Run ``ssd_step``: one token for every (batch, head), ``state`` updated in place.
+    state [B,H,N,P] fp32; x_t [B,H,P]; log_a_t [B,H] or [B,H,N]; B_t, C_t [B,G,N]."""
+    bsz, H, N, P = state.shape
+    G = B_t.shape[1]
+    dev = state.device
+    decay = SSD_DECAY_DIAG if log_a_t.dim() == 3 else SSD_DECAY_SCALAR
+    if x_t.dtype not in _DTYPE_CODE:
+        raise TypeError("x_t must be float32 or bfloat16")
+    dims = Dims(bsz, 1, H, G, P, N, _DTYPE_CODE[x_t.dtype], decay)
+    _check(state, "state", (bsz, H, N, P), torch.float32, dev)
+    _check(x_t, "x_t", (bsz, H, P), x_t.dtype, dev)
+    _check(log_a_t, "log_a_t", (bsz, H, N) if decay == SSD_DECAY_DIAG else (bsz, H),
+           torch.float32, dev)
+    _check(B_t, "B_t", (bsz, G, N), x_t.dtype, dev)
+    _check(C_t, "C_t", (bsz, G, N), x_t.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    if y_t is None:
+        y_t = torch.empty((bsz, H, P), dtype=x_t.dtype, device=dev)
+    _check(y_t, "y_t", (bsz, H, P), x_t.dtype, dev)
+    rc = load_library().ssd_step(ctypes.byref(dims), _ptr(state), _ptr(x_t), _ptr(log_a_t),
+                                 _ptr(B_t), _ptr(C_t), _ptr(D), _ptr(y_t),
+                                 _stream_handle(stream, dev))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_step")
+    return y_t

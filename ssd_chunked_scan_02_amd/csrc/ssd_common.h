@@ -1,0 +1,89 @@
+// Device-side helpers shared by the SSD kernels: vector types, MFMA wrappers, 16-byte
+// memory moves and a block-wide inclusive scan.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Per element type: MFMA K-depth handled by one "K block" and elements per 16 bytes.
+//   bf16: one v_mfma_f32_16x16x32_bf16 per K block of 32 (lane group g holds k = 8g..8g+7)
+//   fp32: four v_mfma_f32_16x16x4_f32 per K block of 16 (MFMA i: lane group g holds
+//         k = 4g+i, so a lane's 16-byte read of k = 4g..4g+3 feeds all four)
+template <typename T> struct Traits;
+template <> struct Traits<__bf16> {
+    static constexpr int kKBlock = 32;
+    static constexpr int kVec = 8;   // elements per 16 bytes
+    static constexpr int kPad = 8;   // LDS row padding in elements (16 bytes)
+};
+template <> struct Traits<float> {
+    static constexpr int kKBlock = 16;
+    static constexpr int kVec = 4;
+    static constexpr int kPad = 4;
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f32x4 as_f32x4(uint4 v) { return __builtin_bit_cast(f32x4, v); }
+
+__device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v) { return (T)v; }
+
+// Four consecutive elements as one 8-byte (bf16) or 16-byte (fp32) store.
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+    *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// Block-wide inclusive scan of one value per thread (kThreads threads).  `scratch` holds
+// kWaves values of type V in LDS.  Contains two __syncthreads().
+template <typename V>
+__device__ __forceinline__ V block_inclusive_scan(V v, V* scratch) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        V o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) scratch[wave] = v;
+    __syncthreads();
+    V prefix = 0;
+    for (int w = 0; w < wave; ++w) prefix += scratch[w];
+    __syncthreads();
+    return v + prefix;
+}
+
+// Maps a launch index to a work index so that each of the 8 XCDs (which receive workgroups
+// round-robin) gets one contiguous range of work: neighbouring heads of one (batch, group)
+// then share that XCD's L2.  Returns -1 for padding workgroups.
+__device__ __forceinline__ int64_t xcd_work_index(int64_t bid, int64_t per_xcd, int64_t total) {
+    const int64_t w = (bid % 8) * per_xcd + bid / 8;
+    return w < total ? w : -1;
+}
+
+}  // namespace ssd

@@ -1,0 +1,503 @@
+// HIP kernels of the chunked SSD forward and the decode step, for gfx950 (MI355X).
+//
+// Forward = two launches per call:
+//   scores_kernel  S = C B^T for every (batch, group, chunk): the query-key products of the
+//                  attention form (llms.blog "The SSD Theoretical Equivalence": Q = C, K = B),
+//                  computed once per group and shared by all its heads.  Only the causal
+//                  16x16 tiles (s <= t) are formed, stored fp32 in MFMA accumulator order.
+//   walk_kernel    one workgroup per (batch, head) walks the chunks in order, keeping the
+//                  N x P fp32 state in registers (aiwiki "State Space Duality", "Two
+//                  algorithms for one operator"; llms.blog "The Chunk-Wise SSD Algorithm"):
+//                    y_chunk = (S o L) X  +  exp(cum_t) C_t H_{k-1}  +  D x
+//                    H_k     = exp(cum_last) H_{k-1} + (exp(cum_last - cum_s) B_s)^T X
+//                  with L_ts = exp(cum_t - cum_s) for s <= t (selected before the exp) and
+//                  cum the running sum of log a inside the chunk.  Each workgroup reads its
+//                  x once and writes y once; the state never leaves the chip.
+//
+// MFMA tiling (16x16 tiles, 4 waves of 64 lanes): the accumulator of a 16x16 MFMA holds,
+// in lane l, rows 4*(l/16)+i (i = 0..3) of column l%16.  Products whose operand comes out
+// of an accumulator (the masked scores, the state) use it in place by giving each lane
+// group the K indices its accumulator rows hold; the partner operand is read from LDS in
+// the same K order.  Everything a lane reads or writes along a row is 8 or 16 bytes wide.
+
+#include <type_traits>
+
+#include "ssd_common.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+namespace {
+
+template <typename T> __device__ __forceinline__ T vec_elem(uint4 u, int j);
+template <> __device__ __forceinline__ __bf16 vec_elem<__bf16>(uint4 u, int j) { return as_bf16x8(u)[j]; }
+template <> __device__ __forceinline__ float vec_elem<float>(uint4 u, int j) { return as_f32x4(u)[j]; }
+
+// Four consecutive elements into LDS (8 bytes for bf16, 16 for fp32).
+__device__ __forceinline__ void lds_store4(__bf16* p, __bf16 a, __bf16 b, __bf16 c, __bf16 d) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{a, b, c, d};
+}
+__device__ __forceinline__ void lds_store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// acc += A_blk * B_blk over one K block; a and b are a lane's 16 bytes of each operand.
+__device__ __forceinline__ f32x4 mma_block(f32x4 acc, uint4 a, uint4 b, __bf16) {
+    return mfma_bf16(as_bf16x8(a), as_bf16x8(b), acc);
+}
+__device__ __forceinline__ f32x4 mma_block(f32x4 acc, uint4 a, uint4 b, float) {
+    const f32x4 av = as_f32x4(a), bv = as_f32x4(b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = mfma_f32(av[i], bv[i], acc);
+    return acc;
+}
+
+// exp of a non-positive log-decay difference.  fp32 inputs keep the running sums in fp64
+// and use the accurate expf; bf16 inputs use the hardware exp2-based __expf.
+__device__ __forceinline__ float decay_exp(double d) { return expf((float)d); }
+__device__ __forceinline__ float decay_exp(float d) { return __expf(d); }
+
+__host__ __device__ constexpr int tile_index(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
+
+// ---------------------------------------------------------------------------------------
+// scores_kernel: one workgroup per (batch, group, chunk); wave w forms causal tiles
+// w, w+4, ...  Tile (tb, sb) holds S^T[s][t] = C_t . B_s for s in block sb, t in block tb,
+// lane l storing its 4 accumulator values at offset 4*l.
+template <typename T, int N>
+__global__ void __launch_bounds__(kThreads) scores_kernel(ScoresParams prm) {
+    using TR = Traits<T>;
+    constexpr int KB = TR::kKBlock;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int l16 = lane % 16, lg = lane / 16;
+    const int64_t blk = blockIdx.x;
+    const int c = (int)(blk % prm.nchunks);
+    const int64_t bg = blk / prm.nchunks;
+    const int64_t b = bg / prm.ngroups;
+    const int64_t g = bg % prm.ngroups;
+    const int Q = prm.chunk, nt = Q / 16, ntiles = nt * (nt + 1) / 2;
+    const int64_t t0 = (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, prm.seqlen - t0);
+    const T* Bm = static_cast<const T*>(prm.Bm);
+    const T* Cm = static_cast<const T*>(prm.Cm);
+    float* out = prm.scores + blk * (int64_t)ntiles * 256;
+    const uint4 zero = {0u, 0u, 0u, 0u};
+
+    int idx = 0;
+    for (int tb = 0; tb < nt; ++tb) {
+        for (int sb = 0; sb <= tb; ++sb, ++idx) {
+            if (idx % kWaves != wave) continue;
+            const int s = 16 * sb + l16, t = 16 * tb + l16;
+            const T* brow = Bm + ((b * prm.seqlen + t0 + s) * prm.ngroups + g) * N;
+            const T* crow = Cm + ((b * prm.seqlen + t0 + t) * prm.ngroups + g) * N;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < N / KB; ++kb) {
+                const int k0 = kb * KB + (KB / 4) * lg;
+                const uint4 av = s < len ? ld16(brow + k0) : zero;
+                const uint4 bv = t < len ? ld16(crow + k0) : zero;
+                acc = mma_block(acc, av, bv, T());
+            }
+            *reinterpret_cast<f32x4*>(out + idx * 256 + lane * 4) = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// walk_kernel: one workgroup per (batch, head); see the file header.
+//
+// LDS:  Xt [P][QP]  x of the chunk, transposed (tokens contiguous)
+//       Bt [N][QP]  (exp(cum_last - cum_s) * B_s) of the chunk, transposed
+//       Ht [P][NP]  the state entering the chunk, transposed (state dims contiguous), in T
+//       cum[256]    running log-decay sums of the chunk
+// Registers: the fp32 state, tiles (nb, pb) dealt to the 4 waves round-robin; the output
+// accumulators of one 16-token block at a time (blocks dealt to waves round-robin).
+template <typename T, int N, int P>
+__global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
+    using TR = Traits<T>;
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    constexpr int KB = TR::kKBlock;
+    constexpr int VE = TR::kVec;
+    constexpr int PB = P / 16;
+    constexpr int NB = N / 16;
+    constexpr int NTILE = NB * PB;
+    constexpr int TPW = (NTILE + kWaves - 1) / kWaves;
+    constexpr int NP = N + TR::kPad;
+
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
+    if (unit < 0) return;
+    const int64_t b = unit / H;
+    const int64_t h = unit % H;
+    const int64_t g = h / (H / G);
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int l16 = lane % 16, lg = lane / 16;
+    const int koff = (KB / 4) * lg;  // this lane group's first K index inside a K block
+    const int Q = prm.chunk;
+    const int QK = (Q + KB - 1) / KB * KB;
+    const int QP = QK + TR::kPad;
+    const int nt = Q / 16;
+    const int ntiles = nt * (nt + 1) / 2;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* Xt = reinterpret_cast<T*>(smem);
+    T* Bt = Xt + P * QP;
+    T* Ht = Bt + N * QP;
+    CT* cum = reinterpret_cast<CT*>(Ht + P * NP);
+    CT* scan_tmp = cum + 256;
+
+    const T* xg = static_cast<const T*>(prm.x);
+    const T* Bg = static_cast<const T*>(prm.Bm);
+    const T* Cg = static_cast<const T*>(prm.Cm);
+    T* yg = static_cast<T*>(prm.y);
+    const uint4 zero = {0u, 0u, 0u, 0u};
+
+    // ---- state registers, from init_state or zero
+    f32x4 hs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kWaves * j;
+        if (tile < NTILE && prm.init) {
+            const int nb = tile / PB, pb = tile % PB;
+            const float* src = prm.init + (unit * N + 16 * nb + 4 * lg) * P + 16 * pb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hs[j][i] = src[i * P];
+        }
+    }
+    auto write_state_lds = [&]() {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                lds_store4(Ht + (16 * pb + l16) * NP + 16 * nb + 4 * lg, (T)hs[j][0], (T)hs[j][1],
+                           (T)hs[j][2], (T)hs[j][3]);
+            }
+        }
+    };
+    write_state_lds();
+
+    const float dskip = prm.D ? prm.D[h] : 0.f;
+    const float* scores_bg = prm.scores + (b * G + g) * (int64_t)prm.nchunks * ntiles * 256;
+
+    for (int c = 0; c < prm.nchunks; ++c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+
+        // ---- 1. running sum of log a inside the chunk (tokens past the end add 0)
+        CT v = 0;
+        if (tid < len) v = (CT)prm.log_a[(b * Tn + t0 + tid) * H + h];
+        v = block_inclusive_scan(v, scan_tmp);
+        if (tid < Q) cum[tid] = v;
+        __syncthreads();
+        const CT cum_last = cum[Q - 1];
+
+        // ---- 2. stage x^T and (w o B)^T; rows past the chunk's end are zero
+        for (int item = tid; item < (QK / 4) * (P / VE); item += kThreads) {
+            const int rg = item / (P / VE), cc = item % (P / VE);
+            uint4 u[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r = 4 * rg + k;
+                u[k] = r < len ? ld16(xg + ((b * Tn + t0 + r) * H + h) * P + cc * VE) : zero;
+            }
+#pragma unroll
+            for (int j = 0; j < VE; ++j)
+                lds_store4(Xt + (cc * VE + j) * QP + 4 * rg, vec_elem<T>(u[0], j), vec_elem<T>(u[1], j),
+                           vec_elem<T>(u[2], j), vec_elem<T>(u[3], j));
+        }
+        for (int item = tid; item < (QK / 4) * (N / VE); item += kThreads) {
+            const int rg = item / (N / VE), cc = item % (N / VE);
+            uint4 u[4];
+            float w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r = 4 * rg + k;
+                const bool ok = r < len;
+                u[k] = ok ? ld16(Bg + ((b * Tn + t0 + r) * G + g) * N + cc * VE) : zero;
+                w[k] = ok ? decay_exp(cum_last - cum[r]) : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < VE; ++j)
+                lds_store4(Bt + (cc * VE + j) * QP + 4 * rg,
+                           from_f32<T>(w[0] * to_f32(vec_elem<T>(u[0], j))),
+                           from_f32<T>(w[1] * to_f32(vec_elem<T>(u[1], j))),
+                           from_f32<T>(w[2] * to_f32(vec_elem<T>(u[2], j))),
+                           from_f32<T>(w[3] * to_f32(vec_elem<T>(u[3], j))));
+        }
+        __syncthreads();
+
+        // ---- 3. outputs: y^T[p][t] for 16-token blocks tb = wave, wave+4, ...
+        const float* scores_c = scores_bg + (int64_t)c * ntiles * 256;
+        for (int tb = wave; tb < nt; tb += kWaves) {
+            const int tl = 16 * tb + l16;  // this lane's token inside the chunk
+            const bool tvalid = tl < len;
+            const int64_t trow = b * Tn + t0 + tl;
+            f32x4 acc[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            // carried state: C_t . H_{k-1}, then the decay from the chunk start, exp(cum_t)
+            const T* crow = Cg + (trow * G + g) * N;
+#pragma unroll
+            for (int kb = 0; kb < N / KB; ++kb) {
+                const uint4 cv = tvalid ? ld16(crow + kb * KB + koff) : zero;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+                    acc[pb] = mma_block(acc[pb], ld16(Ht + (16 * pb + l16) * NP + kb * KB + koff), cv, T());
+            }
+            const CT cum_t = cum[tl];
+            const float ec = decay_exp(cum_t);
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) acc[pb] *= ec;
+
+            // within the chunk: (S o L) X, mask selected before the exp
+            auto masked_tile = [&](int sb) -> f32x4 {
+                f32x4 s4 = as_f32x4(ld16(scores_c + tile_index(tb, sb) * 256 + lane * 4));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 16 * sb + 4 * lg + i;
+                    const bool causal = s <= tl;
+                    const CT d = causal ? (CT)(cum_t - cum[s]) : (CT)0;
+                    s4[i] = causal ? s4[i] * decay_exp(d) : 0.f;
+                }
+                return s4;
+            };
+            if constexpr (std::is_same<T, __bf16>::value) {
+                for (int k = 0; 2 * k <= tb; ++k) {
+                    const f32x4 m0 = masked_tile(2 * k);
+                    const f32x4 m1 = (2 * k + 1 <= tb) ? masked_tile(2 * k + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    const bf16x8 bop = {(__bf16)m0[0], (__bf16)m0[1], (__bf16)m0[2], (__bf16)m0[3],
+                                        (__bf16)m1[0], (__bf16)m1[1], (__bf16)m1[2], (__bf16)m1[3]};
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) {
+                        const T* xr = Xt + (16 * pb + l16) * QP + 32 * k + 4 * lg;
+                        const uint2 lo = ld8(xr), hi = ld8(xr + 16);
+                        const uint4 a = {lo.x, lo.y, hi.x, hi.y};
+                        acc[pb] = mfma_bf16(as_bf16x8(a), bop, acc[pb]);
+                    }
+                }
+            } else {
+                for (int sb = 0; sb <= tb; ++sb) {
+                    const f32x4 m = masked_tile(sb);
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) {
+                        const f32x4 xa = as_f32x4(ld16(Xt + (16 * pb + l16) * QP + 16 * sb + 4 * lg));
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[pb] = mfma_f32(xa[i], m[i], acc[pb]);
+                    }
+                }
+            }
+
+            // skip term and store
+            if (prm.D) {
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[pb][i] += dskip * to_f32(Xt[(16 * pb + 4 * lg + i) * QP + tl]);
+            }
+            if (tvalid) {
+                T* yr = yg + (trow * H + h) * P + 4 * lg;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+                    store4(yr + 16 * pb, acc[pb][0], acc[pb][1], acc[pb][2], acc[pb][3]);
+            }
+        }
+
+        // ---- 4. state: H_k = exp(cum_last) H_{k-1} + (w o B)^T X
+        const float el = decay_exp(cum_last);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                f32x4 a = hs[j] * el;
+                const T* br = Bt + (16 * nb + l16) * QP + koff;
+                const T* xr = Xt + (16 * pb + l16) * QP + koff;
+                for (int kb = 0; kb < QK / KB; ++kb) a = mma_block(a, ld16(br + kb * KB), ld16(xr + kb * KB), T());
+                hs[j] = a;
+            }
+        }
+        __syncthreads();
+        write_state_lds();
+    }
+
+    if (prm.final_state) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                float* dst = prm.final_state + (unit * N + 16 * nb + 4 * lg) * P + 16 * pb + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * P] = hs[j][i];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode step: one workgroup per (batch, head); thread (r, p) updates state rows
+// n = r, r + R, ... of column p and the column's readout is summed over r in LDS.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) step_kernel(StepParams prm) {
+    const int64_t unit = blockIdx.x;
+    const int64_t H = prm.nheads, G = prm.ngroups;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int P = prm.headdim, N = prm.dstate;
+    const int R = kThreads / P;
+    const int p = threadIdx.x % P, r = threadIdx.x / P;
+    const T* xt = static_cast<const T*>(prm.x_t);
+    const T* Bt = static_cast<const T*>(prm.B_t) + (b * G + g) * N;
+    const T* Ct = static_cast<const T*>(prm.C_t) + (b * G + g) * N;
+    const float xp = to_f32(xt[unit * P + p]);
+    const float a_head = prm.diag ? 0.f : expf(prm.log_a_t[unit]);
+    float* st = prm.state + unit * N * P;
+    float acc = 0.f;
+    for (int n = r; n < N; n += R) {
+        const float a = prm.diag ? expf(prm.log_a_t[unit * N + n]) : a_head;
+        const float s = a * st[n * P + p] + to_f32(Bt[n]) * xp;
+        st[n * P + p] = s;
+        acc += to_f32(Ct[n]) * s;
+    }
+    __shared__ float red[kThreads];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (r == 0) {
+        float sum = 0.f;
+        for (int q = 0; q < R; ++q) sum += red[q * P + p];
+        if (prm.D) sum += prm.D[h] * xp;
+        static_cast<T*>(prm.y_t)[unit * P + p] = from_f32<T>(sum);
+    }
+}
+
+// final_state = init_state (or zeros) for an empty sequence.
+__global__ void __launch_bounds__(kThreads) copy_state_kernel(const float* src, float* dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T> constexpr int kBytes = sizeof(T);
+
+template <typename T, int N, int P>
+size_t walk_lds_bytes_t(int chunk) {
+    const int KB = Traits<T>::kKBlock;
+    const int QK = (chunk + KB - 1) / KB * KB;
+    const int QP = QK + Traits<T>::kPad;
+    const int NP = N + Traits<T>::kPad;
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    return (size_t)(P * QP + N * QP + P * NP) * sizeof(T) + (256 + kWaves) * sizeof(CT);
+}
+
+// Records the caller's timing event k, if one was given.
+bool mark(const ForwardLaunch& fl, int k, hipStream_t stream) {
+    if (!fl.events || k >= fl.n_events || !fl.events[k]) return true;
+    return hipEventRecord(fl.events[k], stream) == hipSuccess;
+}
+
+template <typename T, int N, int P>
+int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
+    const int Q = fl.chunk;
+    const int nt = Q / 16;
+    const int ntiles = nt * (nt + 1) / 2;
+    ScoresParams sp{fl.Bm, fl.Cm, fl.scores, fl.seqlen, fl.ngroups, Q, fl.nchunks};
+    const int64_t nscore = fl.batch * fl.ngroups * fl.nchunks;
+    (void)ntiles;
+    if (!mark(fl, 0, stream)) return -1;
+    hipLaunchKernelGGL((scores_kernel<T, N>), dim3((unsigned)nscore), dim3(kThreads), 0, stream, sp);
+    if (hipGetLastError() != hipSuccess) return -1;
+
+    const int64_t units = fl.batch * fl.nheads;
+    const int64_t per_xcd = (units + 7) / 8;
+    WalkParams wp{fl.x, fl.log_a, fl.Bm, fl.Cm, fl.D, fl.scores, fl.init, fl.y, fl.final_state,
+                  fl.batch, fl.seqlen, fl.nheads, fl.ngroups, Q, fl.nchunks, per_xcd};
+    const size_t lds = walk_lds_bytes_t<T, N, P>(Q);
+    // Allow the full 160 KiB of LDS, once per device.
+    static bool attr_set[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    if (!attr_set[dev]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_kernel<T, N, P>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
+            return -1;
+        attr_set[dev] = true;
+    }
+    if (!mark(fl, 1, stream)) return -1;
+    hipLaunchKernelGGL((walk_kernel<T, N, P>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp);
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (!mark(fl, 2, stream)) return -1;
+    if (fl.n_launches) *fl.n_launches = 2;
+    return 0;
+}
+
+// The (element type, N, P) instantiations the library ships.
+#define SSD_FOR_EACH_SHAPE(X)                                                                       \
+    X(__bf16, 32, 16) X(__bf16, 32, 32) X(__bf16, 32, 64) X(__bf16, 32, 128)                        \
+    X(__bf16, 64, 16) X(__bf16, 64, 32) X(__bf16, 64, 64) X(__bf16, 64, 128)                        \
+    X(__bf16, 128, 16) X(__bf16, 128, 32) X(__bf16, 128, 64) X(__bf16, 128, 128)                    \
+    X(__bf16, 256, 16) X(__bf16, 256, 32) X(__bf16, 256, 64)                                        \
+    X(float, 16, 16) X(float, 16, 32) X(float, 16, 64) X(float, 16, 128)                            \
+    X(float, 32, 16) X(float, 32, 32) X(float, 32, 64) X(float, 32, 128)                            \
+    X(float, 64, 16) X(float, 64, 32) X(float, 64, 64) X(float, 64, 128)                            \
+    X(float, 128, 16) X(float, 128, 32) X(float, 128, 64) X(float, 128, 128)                        \
+    X(float, 256, 16) X(float, 256, 32) X(float, 256, 64)
+
+}  // namespace
+
+bool shape_supported(int dtype, int N, int P) {
+#define SSD_MATCH(TT, NN, PP) \
+    if ((std::is_same<TT, float>::value ? 0 : 1) == dtype && N == NN && P == PP) return true;
+    SSD_FOR_EACH_SHAPE(SSD_MATCH)
+#undef SSD_MATCH
+    return false;
+}
+
+size_t walk_lds_bytes(int dtype, int N, int P, int chunk) {
+#define SSD_LDS(TT, NN, PP) \
+    if ((std::is_same<TT, float>::value ? 0 : 1) == dtype && N == NN && P == PP) return walk_lds_bytes_t<TT, NN, PP>(chunk);
+    SSD_FOR_EACH_SHAPE(SSD_LDS)
+#undef SSD_LDS
+    return 0;
+}
+
+size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk) {
+    const int64_t nt = chunk / 16;
+    return (size_t)(batch * ngroups * nchunks) * (size_t)(nt * (nt + 1) / 2) * 256 * sizeof(float);
+}
+
+int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
+    if (fl.seqlen == 0) {
+        if (fl.final_state) {
+            const int64_t n = fl.batch * fl.nheads * fl.dstate * fl.headdim;
+            if (n > 0) {
+                if (!mark(fl, 0, stream)) return -1;
+                hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                                   dim3(kThreads), 0, stream, fl.init, fl.final_state, n);
+                if (hipGetLastError() != hipSuccess) return -1;
+                if (!mark(fl, 1, stream)) return -1;
+                if (fl.n_launches) *fl.n_launches = 1;
+            }
+        }
+        return 0;
+    }
+#define SSD_LAUNCH(TT, NN, PP) \
+    if ((std::is_same<TT, float>::value ? 0 : 1) == fl.dtype && fl.dstate == NN && fl.headdim == PP) \
+        return launch_forward_t<TT, NN, PP>(fl, stream);
+    SSD_FOR_EACH_SHAPE(SSD_LAUNCH)
+#undef SSD_LAUNCH
+    return -2;
+}
+
+int launch_step(const StepParams& sp, int dtype, int64_t units, hipStream_t stream) {
+    if (units == 0) return 0;
+    if (dtype == 0)
+        hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)units), dim3(kThreads), 0, stream, sp);
+    else
+        hipLaunchKernelGGL(step_kernel<__bf16>, dim3((unsigned)units), dim3(kThreads), 0, stream, sp);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace ssd

@@ -1,0 +1,79 @@
+// Host-side launch interface between the C ABI (ssd_api.cpp) and the kernels
+// (ssd_kernels.hip).  Kernel parameter blocks are passed by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct ScoresParams {
+    const void* Bm;
+    const void* Cm;
+    float* scores;
+    int64_t seqlen;
+    int64_t ngroups;
+    int chunk;
+    int nchunks;
+};
+
+struct WalkParams {
+    const void* x;
+    const float* log_a;
+    const void* Bm;
+    const void* Cm;
+    const float* D;
+    const float* scores;
+    const float* init;
+    void* y;
+    float* final_state;
+    int64_t batch, seqlen, nheads, ngroups;
+    int chunk;
+    int nchunks;
+    int64_t per_xcd;
+};
+
+struct StepParams {
+    float* state;
+    const void* x_t;
+    const float* log_a_t;
+    const void* B_t;
+    const void* C_t;
+    const float* D;
+    void* y_t;
+    int64_t nheads, ngroups;
+    int headdim, dstate, diag;
+};
+
+// Everything one forward call needs, already validated.
+struct ForwardLaunch {
+    int dtype;  // 0 fp32, 1 bf16
+    int decay;  // 0 scalar, 1 diagonal
+    int64_t batch, seqlen, nheads, ngroups, headdim, dstate;
+    int chunk, nchunks;
+    const void* x;
+    const float* log_a;
+    const void* Bm;
+    const void* Cm;
+    const float* D;
+    const float* init;
+    void* y;
+    float* final_state;
+    float* scores;  // workspace
+    // optional timing events (hipEvent_t): events[k] before launch k, events[L] after the last
+    hipEvent_t const* events;
+    int n_events;
+    int* n_launches;
+};
+
+bool shape_supported(int dtype, int N, int P);
+size_t walk_lds_bytes(int dtype, int N, int P, int chunk);
+size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk);
+// 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.
+int launch_forward(const ForwardLaunch& fl, hipStream_t stream);
+int launch_step(const StepParams& sp, int dtype, int64_t units, hipStream_t stream);
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+}  // namespace ssd

@@ -1,0 +1,91 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI binding and
+the fp64 oracle on the same stored inputs, and compare them by relative L2 error."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import ssd_inputs
+import ssd_chunked_scan_02_amd as ssd
+
+# relative L2 error bounds: fp32 inputs, bf16 inputs (accumulation in fp32 in both)
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def announce(msg: str):
+    print("[gpu case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = float(np.linalg.norm(want.ravel()))
+    num = float(np.linalg.norm((got - want).ravel()))
+    return num / den if den > 0 else num
+
+
+def to_gpu(inp: dict) -> dict:
+    return {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+
+
+def gpu_forward(g: dict, chunk: int, want_final: bool):
+    y, fin = ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g.get("D"), chunk=chunk,
+                             init_state=g.get("init_state"), final_state=bool(want_final))
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def oracle_forward(inp: dict, units=None):
+    """fp64 oracle on the stored inputs; ``units`` = list of (b, h) to evaluate (each head is
+    independent), or None for all.  Returns dict (b, h) -> (y [T,P], final [N,P]).
+    Sampled units are gathered into one oracle call (one unit per batch row) so that the
+    oracle's threads share them."""
+    f = ssd_inputs.to_f64
+    nb, T, H, P = inp["x"].shape
+    G = inp["B"].shape[2]
+    if units is None:
+        units = [(b, h) for b in range(nb) for h in range(H)]
+    if not units:
+        return {}
+    bs = torch.tensor([u[0] for u in units])
+    hs = torch.tensor([u[1] for u in units])
+    gs = hs // (H // G)
+    x = f(inp["x"][bs, :, hs].unsqueeze(2))                 # [U, T, 1, P]
+    la = f(inp["log_a"][bs, :, hs].unsqueeze(2))            # [U, T, 1] or [U, T, 1, N]
+    Bm = f(inp["B"][bs, :, gs].unsqueeze(2))
+    Cm = f(inp["C"][bs, :, gs].unsqueeze(2))
+    h0 = None if inp.get("init_state") is None else f(inp["init_state"][bs, hs].unsqueeze(1))
+    y, fin = oracle.forward(x, la, Bm, Cm, None, h0)
+    if inp.get("D") is not None:
+        d = f(inp["D"])[hs.numpy()]
+        y = y + d[:, None, None, None] * x
+    return {u: (y[i, :, 0], fin[i, 0]) for i, u in enumerate(units)}
+
+
+def compare(inp: dict, y_gpu, fin_gpu, ref: dict, dtype: str, check_final: bool, label: str):
+    """relL2 over the evaluated units of y, of the SSD part y - D x, and of the final state."""
+    yg = y_gpu.float().cpu().numpy().astype(np.float64)
+    x = ssd_inputs.to_f64(inp["x"])
+    D = ssd_inputs.to_f64(inp.get("D"))
+    keys = sorted(ref)
+    got_y = np.stack([yg[b, :, h] for (b, h) in keys])
+    want_y = np.stack([ref[k][0] for k in keys])
+    skip = np.stack([(D[h] if D is not None else 0.0) * x[b, :, h] for (b, h) in keys])
+    e_y = rel_l2(got_y, want_y)
+    e_ssd = rel_l2(got_y - skip, want_y - skip)
+    msg = "%s: relL2 y %.3e  ssd-part %.3e" % (label, e_y, e_ssd)
+    tol = TOL[dtype]
+    ok = e_y <= tol and e_ssd <= tol
+    if check_final:
+        fg = fin_gpu.cpu().numpy().astype(np.float64)
+        e_f = rel_l2(np.stack([fg[b, h] for (b, h) in keys]), np.stack([ref[k][1] for k in keys]))
+        msg += "  final %.3e" % e_f
+        ok = ok and e_f <= tol
+    announce(msg + "  (tol %.0e)" % tol)
+    assert np.all(np.isfinite(got_y)), label + ": non-finite outputs"
+    assert ok, msg
+    return e_y

@@ -1,0 +1,144 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every function that
+include/ssd.h declares, sizes workspaces, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ssd_chunked_scan_02_amd as ssd
+from ssd_chunked_scan_02_amd import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.library_path()):
+        from ssd_chunked_scan_02_amd.build import build
+        build()
+    return ssd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["ssd_forward", "ssd_forward_profiled",
+                                    "ssd_forward_workspace_bytes", "ssd_step", "ssd_strerror"]
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert ssd.ssd_strerror(code)
+    assert "unknown" in ssd.ssd_strerror(7)
+
+
+def mamba2_dims(**kw):
+    d = dict(batch=8, seqlen=2048, nheads=24, ngroups=1, headdim=64, dstate=128, dtype=1, decay=0)
+    d.update(kw)
+    return Dims(**d)
+
+
+def test_workspace_bytes(lib):
+    # causal 16x16 score tiles per (batch, group, chunk), fp32: 8*1*16 chunks * 36 tiles * 1 KiB
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 128) == 8 * 16 * 36 * 1024
+    # ragged: 2050 tokens -> 17 chunks
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=2050), 128) == 8 * 17 * 36 * 1024
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(ngroups=8, nheads=64), 64) == 8 * 8 * 32 * 10 * 1024
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=0), 128) == 0
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 48) == 0        # unsupported chunk
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(nheads=5, ngroups=2), 64) == 0
+
+
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced: validation fails first
+
+
+def call_forward(lib, dims, chunk=128, ptrs=None, ws_bytes=1 << 30, **over):
+    p = dict(x=FAKE, log_a=FAKE, B=FAKE, C=FAKE, D=None, init=None, y=FAKE, final=None, ws=FAKE)
+    p.update(ptrs or {})
+    p.update(over)
+    return lib.ssd_forward(ctypes.byref(dims), p["x"], p["log_a"], p["B"], p["C"], p["D"], chunk,
+                           p["init"], p["y"], p["final"], p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value", [("batch", -1), ("seqlen", -5), ("nheads", 0),
+                                         ("ngroups", 0), ("headdim", 0), ("dstate", -2),
+                                         ("dtype", 7), ("decay", 3)])
+def test_forward_rejects_bad_dims(lib, field, value):
+    assert call_forward(lib, mamba2_dims(**{field: value})) == ssd.SSD_ERR_INVALID
+
+
+def test_forward_rejects_groups_not_dividing_heads(lib):
+    assert call_forward(lib, mamba2_dims(nheads=6, ngroups=4)) == ssd.SSD_ERR_INVALID
+
+
+@pytest.mark.parametrize("chunk", [0, 8, 48, 100, 512])
+def test_forward_rejects_unsupported_chunk(lib, chunk):
+    assert call_forward(lib, mamba2_dims(), chunk=chunk) == ssd.SSD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("over", [dict(dstate=48), dict(headdim=96), dict(dstate=512),
+                                  dict(dstate=256, headdim=128), dict(dstate=16)])
+def test_forward_rejects_unsupported_shapes(lib, over):
+    assert call_forward(lib, mamba2_dims(**over)) == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_fp32_shapes_that_exceed_lds_are_unsupported(lib):
+    assert call_forward(lib, mamba2_dims(dtype=0), chunk=256) == ssd.SSD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["x", "log_a", "B", "C", "y"])
+def test_forward_rejects_null_required_pointer(lib, name):
+    assert call_forward(lib, mamba2_dims(), **{name: None}) == ssd.SSD_ERR_INVALID
+
+
+@pytest.mark.parametrize("name", ["x", "log_a", "B", "C", "D", "init", "y", "final", "ws"])
+def test_forward_rejects_misaligned_pointer(lib, name):
+    assert call_forward(lib, mamba2_dims(), **{name: FAKE + 4}) == ssd.SSD_ERR_ALIGN
+
+
+def test_forward_rejects_small_workspace(lib):
+    need = ssd.ssd_forward_workspace_bytes(mamba2_dims(), 128)
+    assert call_forward(lib, mamba2_dims(), ws_bytes=need - 1) == ssd.SSD_ERR_INVALID
+    assert call_forward(lib, mamba2_dims(), ws=None) == ssd.SSD_ERR_INVALID
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # nothing to do: returns success without touching the (fake) pointers or the GPU
+    assert call_forward(lib, mamba2_dims(batch=0), ptrs=dict(x=None, log_a=None, B=None, C=None,
+                                                             y=None, ws=None), ws_bytes=0) == 0
+
+
+def call_step(lib, dims, **over):
+    p = dict(state=FAKE, x=FAKE, la=FAKE, B=FAKE, C=FAKE, D=None, y=FAKE)
+    p.update(over)
+    return lib.ssd_step(ctypes.byref(dims), p["state"], p["x"], p["la"], p["B"], p["C"], p["D"],
+                        p["y"], None)
+
+
+def test_step_rejects_bad_arguments(lib):
+    d = mamba2_dims(batch=4, nheads=64, ngroups=8)
+    assert call_step(lib, mamba2_dims(nheads=0)) == ssd.SSD_ERR_INVALID
+    assert call_step(lib, d, state=None) == ssd.SSD_ERR_INVALID
+    assert call_step(lib, d, y=None) == ssd.SSD_ERR_INVALID
+    assert call_step(lib, d, x=FAKE + 2) == ssd.SSD_ERR_ALIGN
+    assert call_step(lib, mamba2_dims(dstate=48)) == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_profiled_forward_rejects_short_event_array(lib):
+    d = mamba2_dims()
+    events = (ctypes.c_void_p * 2)(None, None)
+    n = ctypes.c_int(-1)
+    rc = lib.ssd_forward_profiled(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 128, None, FAKE,
+                                  None, FAKE, 1 << 30, None, events, 2, ctypes.byref(n))
+    assert rc == ssd.SSD_ERR_INVALID and n.value == 0
