@@ -20,6 +20,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-Wall", "-Wno-unused-result"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+DEVICE_SOURCES = ["ssd_kernels.hip", "ssd_fast.hip"]
 
 
 def _run(cmd):
@@ -37,14 +38,15 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libssd.so next to this file; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", CSRC]
-    k_obj = os.path.join(BUILD_DIR, "ssd_kernels.o")
+    objs, logs = [], []
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        logs.append(_run([HIPCC, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj]))
+        objs.append(obj)
     a_obj = os.path.join(BUILD_DIR, "ssd_api.o")
-    logs = [
-        _run([HIPCC, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, "ssd_kernels.hip"), "-o", k_obj]),
-        _run([HIPCC, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "ssd_api.cpp"), "-o", a_obj]),
-    ]
+    logs.append(_run([HIPCC, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "ssd_api.cpp"), "-o", a_obj]))
     tmp = LIBRARY + ".tmp%d" % os.getpid()
-    logs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, k_obj, a_obj, "-o", tmp]))
+    logs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, a_obj, "-o", tmp]))
     os.replace(tmp, LIBRARY)
     if verbose:
         for log in logs:

@@ -40,6 +40,8 @@ int check_dims(const ssd_dims* d, bool forward) {
 size_t workspace_needed(const ssd_dims* d, int chunk) {
     if (d->seqlen == 0 || d->batch == 0) return 0;
     const int64_t nchunks = (d->seqlen + chunk - 1) / chunk;
+    if (ssd::fast_path_applies(d->dtype, d->decay, (int)d->dstate, (int)d->headdim, chunk))
+        return ssd::fast_workspace_bytes(d->batch, d->ngroups, nchunks, (int)d->dstate, chunk);
     return ssd::scores_bytes(d->batch, d->ngroups, nchunks, chunk);
 }
 

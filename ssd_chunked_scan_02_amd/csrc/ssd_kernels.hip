@@ -392,12 +392,6 @@ size_t walk_lds_bytes_t(int chunk) {
     return (size_t)(P * QP + N * QP + P * NP) * sizeof(T) + (256 + kWaves) * sizeof(CT);
 }
 
-// Records the caller's timing event k, if one was given.
-bool mark(const ForwardLaunch& fl, int k, hipStream_t stream) {
-    if (!fl.events || k >= fl.n_events || !fl.events[k]) return true;
-    return hipEventRecord(fl.events[k], stream) == hipSuccess;
-}
-
 template <typename T, int N, int P>
 int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int Q = fl.chunk;
@@ -406,7 +400,7 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     ScoresParams sp{fl.Bm, fl.Cm, fl.scores, fl.seqlen, fl.ngroups, Q, fl.nchunks};
     const int64_t nscore = fl.batch * fl.ngroups * fl.nchunks;
     (void)ntiles;
-    if (!mark(fl, 0, stream)) return -1;
+    if (!record_event(fl, 0, stream)) return -1;
     hipLaunchKernelGGL((scores_kernel<T, N>), dim3((unsigned)nscore), dim3(kThreads), 0, stream, sp);
     if (hipGetLastError() != hipSuccess) return -1;
 
@@ -425,10 +419,10 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
             return -1;
         attr_set[dev] = true;
     }
-    if (!mark(fl, 1, stream)) return -1;
+    if (!record_event(fl, 1, stream)) return -1;
     hipLaunchKernelGGL((walk_kernel<T, N, P>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp);
     if (hipGetLastError() != hipSuccess) return -1;
-    if (!mark(fl, 2, stream)) return -1;
+    if (!record_event(fl, 2, stream)) return -1;
     if (fl.n_launches) *fl.n_launches = 2;
     return 0;
 }
@@ -446,6 +440,11 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     X(float, 256, 16) X(float, 256, 32) X(float, 256, 64)
 
 }  // namespace
+
+bool record_event(const ForwardLaunch& fl, int k, hipStream_t stream) {
+    if (!fl.events || k >= fl.n_events || !fl.events[k]) return true;
+    return hipEventRecord(fl.events[k], stream) == hipSuccess;
+}
 
 bool shape_supported(int dtype, int N, int P) {
 #define SSD_MATCH(TT, NN, PP) \
@@ -473,16 +472,18 @@ int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
         if (fl.final_state) {
             const int64_t n = fl.batch * fl.nheads * fl.dstate * fl.headdim;
             if (n > 0) {
-                if (!mark(fl, 0, stream)) return -1;
+                if (!record_event(fl, 0, stream)) return -1;
                 hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
                                    dim3(kThreads), 0, stream, fl.init, fl.final_state, n);
                 if (hipGetLastError() != hipSuccess) return -1;
-                if (!mark(fl, 1, stream)) return -1;
+                if (!record_event(fl, 1, stream)) return -1;
                 if (fl.n_launches) *fl.n_launches = 1;
             }
         }
         return 0;
     }
+    if (fast_path_applies(fl.dtype, fl.decay, (int)fl.dstate, (int)fl.headdim, fl.chunk))
+        return launch_forward_fast(fl, stream);
 #define SSD_LAUNCH(TT, NN, PP) \
     if ((std::is_same<TT, float>::value ? 0 : 1) == fl.dtype && fl.dstate == NN && fl.headdim == PP) \
         return launch_forward_t<TT, NN, PP>(fl, stream);

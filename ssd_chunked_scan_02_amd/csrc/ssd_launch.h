@@ -46,6 +46,31 @@ struct StepParams {
     int headdim, dstate, diag;
 };
 
+struct PrepParams {
+    const void* Bm;
+    const void* Cm;
+    __bf16* pairs;  // score tile pairs, bf16, lane order
+    __bf16* bt;     // B^T per chunk, tokens in MFMA K order
+    int64_t seqlen;
+    int64_t ngroups;
+    int nchunks;
+};
+
+struct Walk2Params {
+    const void* x;
+    const float* log_a;
+    const void* Cm;
+    const float* D;
+    const __bf16* pairs;
+    const __bf16* bt;
+    const float* init;
+    void* y;
+    float* final_state;
+    int64_t batch, seqlen, nheads, ngroups;
+    int nchunks;
+    int64_t per_xcd;
+};
+
 // Everything one forward call needs, already validated.
 struct ForwardLaunch {
     int dtype;  // 0 fp32, 1 bf16
@@ -68,6 +93,12 @@ struct ForwardLaunch {
 };
 
 bool shape_supported(int dtype, int N, int P);
+// Records the caller's timing event k (if any) on the stream; false on a HIP error.
+bool record_event(const ForwardLaunch& fl, int k, hipStream_t stream);
+// The pipelined bf16 path (ssd_fast.hip) and its workspace.
+bool fast_path_applies(int dtype, int decay, int N, int P, int chunk);
+size_t fast_workspace_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int N, int chunk);
+int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream);
 size_t walk_lds_bytes(int dtype, int N, int P, int chunk);
 size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk);
 // 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.
