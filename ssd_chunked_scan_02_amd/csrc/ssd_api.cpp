@@ -33,13 +33,16 @@ int check_dims(const ssd_dims* d, bool forward) {
     const double big = (double)d->batch * (double)(T > 0 ? T : 1) * (double)d->nheads *
                        (double)(d->headdim > d->dstate ? d->headdim : d->dstate);
     if (big > (double)kMaxElems * 1024.0) return SSD_ERR_INVALID;
-    if (!ssd::shape_supported(d->dtype, (int)d->dstate, (int)d->headdim)) return SSD_ERR_UNSUPPORTED;
+    if (!forward || d->decay == SSD_DECAY_SCALAR) {
+        if (!ssd::shape_supported(d->dtype, (int)d->dstate, (int)d->headdim)) return SSD_ERR_UNSUPPORTED;
+    }
     return SSD_OK;
 }
 
 size_t workspace_needed(const ssd_dims* d, int chunk) {
     if (d->seqlen == 0 || d->batch == 0) return 0;
     const int64_t nchunks = (d->seqlen + chunk - 1) / chunk;
+    if (d->decay == SSD_DECAY_DIAG) return 0;
     if (ssd::fast_path_applies(d->dtype, d->decay, (int)d->dstate, (int)d->headdim, chunk))
         return ssd::fast_workspace_bytes(d->batch, d->ngroups, nchunks, (int)d->dstate, chunk);
     return ssd::scores_bytes(d->batch, d->ngroups, nchunks, chunk);
@@ -49,7 +52,11 @@ int check_forward(const ssd_dims* d, int chunk) {
     int rc = check_dims(d, true);
     if (rc != SSD_OK) return rc;
     if (!valid_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
-    if (d->decay != SSD_DECAY_SCALAR) return SSD_ERR_UNSUPPORTED;
+    if (d->decay == SSD_DECAY_DIAG) {
+        const size_t lds = ssd::diag_lds_bytes(d->dtype, (int)d->dstate, (int)d->headdim, chunk);
+        if (lds == 0 || lds > ssd::kMaxLds) return SSD_ERR_UNSUPPORTED;
+        return SSD_OK;
+    }
     if (ssd::walk_lds_bytes(d->dtype, (int)d->dstate, (int)d->headdim, chunk) > ssd::kMaxLds)
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;

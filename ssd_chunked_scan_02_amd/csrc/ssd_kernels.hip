@@ -482,6 +482,7 @@ int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
         }
         return 0;
     }
+    if (fl.decay == 1) return launch_forward_diag(fl, stream);
     if (fast_path_applies(fl.dtype, fl.decay, (int)fl.dstate, (int)fl.headdim, fl.chunk))
         return launch_forward_fast(fl, stream);
 #define SSD_LAUNCH(TT, NN, PP) \

@@ -99,6 +99,9 @@ bool record_event(const ForwardLaunch& fl, int k, hipStream_t stream);
 bool fast_path_applies(int dtype, int decay, int N, int P, int chunk);
 size_t fast_workspace_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int N, int chunk);
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream);
+// The diagonal-decay walk (ssd_diag.hip): LDS bytes (0 = unsupported) and launch.
+size_t diag_lds_bytes(int dtype, int N, int P, int chunk);
+int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream);
 size_t walk_lds_bytes(int dtype, int N, int P, int chunk);
 size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk);
 // 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.

@@ -49,15 +49,34 @@ def mamba2_dims(**kw):
     return Dims(**d)
 
 
+def n_pairs(nt):
+    m = nt // 2
+    return m * (m + 1) if nt % 2 == 0 else (m + 1) * (m + 1)
+
+
 def test_workspace_bytes(lib):
-    # causal 16x16 score tiles per (batch, group, chunk), fp32: 8*1*16 chunks * 36 tiles * 1 KiB
-    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 128) == 8 * 16 * 36 * 1024
+    # bf16, scalar decay, head dim 64, N in {64,128}, chunk in {64,128}: per (batch, group,
+    # chunk) the bf16 score-tile pairs (1 KiB each) and the B^T operand (N * chunk * 2 bytes)
+    fast = lambda nblk, N, Q: nblk * (n_pairs(Q // 16) * 1024 + N * Q * 2)
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 128) == fast(8 * 16, 128, 128)
     # ragged: 2050 tokens -> 17 chunks
-    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=2050), 128) == 8 * 17 * 36 * 1024
-    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(ngroups=8, nheads=64), 64) == 8 * 8 * 32 * 10 * 1024
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=2050), 128) == fast(8 * 17, 128, 128)
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(ngroups=8, nheads=64), 64) == fast(8 * 8 * 32, 128, 64)
+    # other shapes: causal 16x16 fp32 score tiles per (batch, group, chunk)
+    tiles = lambda nblk, Q: nblk * (Q // 16) * (Q // 16 + 1) // 2 * 1024
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(dtype=0), 64) == tiles(8 * 32, 64)
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(headdim=32), 256) == tiles(8 * 8, 256)
+    # diagonal decay needs no workspace
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(decay=1, dstate=64), 64) == 0
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=0), 128) == 0
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 48) == 0        # unsupported chunk
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(nheads=5, ngroups=2), 64) == 0
+
+
+def test_diag_shapes_supported_and_not(lib):
+    d = mamba2_dims(decay=1, dstate=64)
+    assert call_forward(lib, d, chunk=128) == ssd.SSD_ERR_UNSUPPORTED      # diag chunk <= 64
+    assert call_forward(lib, mamba2_dims(decay=1, dstate=256), chunk=64) == ssd.SSD_ERR_UNSUPPORTED
 
 
 FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced: validation fails first

@@ -20,7 +20,7 @@ def _units(cfg, n, seed):
     return [(u // cfg["nheads"], u % cfg["nheads"]) for u in picks]
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "mamba2_layer", "long_seq", "gqa_decode"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "mamba2_layer", "long_seq", "gqa_decode", "diag_multiscale"])
 def test_full_workload_sampled(name):
     cfg = ssd_inputs.config(name)
     seed = ssd_inputs.SEEDS[name]

@@ -155,3 +155,49 @@ def test_split_resume_matches_whole():
         ef = (fb - fin).norm() / fin.norm()
         announce("split at %d: relL2 y %.2e final %.2e" % (t1, e, ef))
         assert e < 1e-2 and ef < 1e-4
+
+
+# ---- diagonal (per-state-dimension) decay -----------------------------------------------
+DIAG_SMALL = [
+    dict(batch=2, seqlen=300, nheads=4),                                   # ragged tail
+    dict(batch=1, seqlen=256, nheads=2, dstate=128, headdim=32),
+    dict(batch=2, seqlen=200, nheads=2, dtype="fp32", dstate=32, headdim=32, chunk=32),
+    dict(batch=1, seqlen=190, nheads=3, dtype="fp32", dstate=64, headdim=64, init=True),
+]
+
+
+@pytest.mark.parametrize("over", DIAG_SMALL, ids=lambda o: "-".join("%s%s" % kv for kv in o.items()))
+def test_diag_small(over):
+    cfg = ssd_inputs.config("diag_multiscale", **over)
+    _run(cfg, 41, "diag")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_diag_chunk_sizes(chunk):
+    cfg = ssd_inputs.config("diag_multiscale", batch=1, seqlen=333, nheads=2, chunk=chunk, init=True)
+    _run(cfg, 43, "diag chunk=%d" % chunk)
+
+
+def test_diag_equal_rates_match_scalar_oracle():
+    """A per-dimension decay that is the same for every n is the scalar-decay model."""
+    cfg = ssd_inputs.config("mamba2_layer", batch=2, seqlen=300, nheads=3, dstate=64, chunk=64, init=True)
+    inp = ssd_inputs.make_inputs(cfg, 47)
+    announce("diag with equal rates vs scalar oracle")
+    ref = oracle_forward(inp)
+    diag = dict(inp)
+    diag["log_a"] = inp["log_a"][..., None].expand(-1, -1, -1, 64).contiguous()
+    y, fin = gpu_forward(to_gpu(diag), 64, True)
+    compare(inp, y, fin, ref, "bf16", True, "diag equal rates")
+
+
+def test_diag_extreme_rates():
+    """Per-dimension steps down to -1e4 (the state dimension forgets within one token)."""
+    cfg = ssd_inputs.config("diag_multiscale", batch=1, seqlen=256, nheads=2, init=True)
+    inp = ssd_inputs.make_inputs(cfg, 53)
+    gen = torch.Generator().manual_seed(7)
+    mult = torch.exp(torch.rand(inp["log_a"].shape, generator=gen) * 8.0)
+    inp["log_a"] = torch.clamp(inp["log_a"] * mult, min=-1e4).contiguous()
+    announce("diag extreme rates")
+    y, fin = gpu_forward(to_gpu(inp), 64, True)
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+    compare(inp, y, fin, oracle_forward(inp), "bf16", True, "diag extreme rates")
