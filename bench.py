@@ -29,8 +29,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "walk_kernel_mamba2_layer_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "ssd_chunked_scan_02_amd", "csrc", "ssd_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "ssd_chunked_scan_02_amd", "csrc")
 
 
 def log(*a):
@@ -83,17 +83,32 @@ class HipEvents:
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel and ABI source: counter figures taken on other sources are stale."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the walk kernel from the committed rocprofv3 counter summary,
-    or None when absent or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def kernel_names(cfg):
+    """Kernels one forward launches, in order (mirrors the library's dispatch)."""
+    Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
+    if cfg["decay"] == "diag":
+        return ["walk_diag_kernel<%d,%d>" % (N, P)]
+    if cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128):
+        return ["prep_kernel<%d,%d>" % (N, Q), "walk5_kernel<%d,%d>" % (N, Q)]
+    return ["scores_kernel<%d>" % N, "walk_kernel<%d,%d>" % (N, P)]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none or it was taken on different kernel sources."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (kernel.split("<")[0], workload))
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -157,7 +172,7 @@ def main():
     torch.cuda.set_device(dev)
     inp = ssd_inputs.make_inputs(cfg, seed)
     flops, nbytes, per_token = algorithmic_counts(cfg)
-    copies = args.copies or max(2, math.ceil(1.0e9 / nbytes))
+    copies = args.copies or min(64, max(2, math.ceil(1.0e9 / nbytes)))
     log("workload %s seed %d: %.2f GFLOP, %.1f MB algorithmic per step, %d copies"
         % (args.workload, seed, flops / 1e9, nbytes / 1e6, copies))
 
@@ -207,16 +222,21 @@ def main():
     ms = total_ms / K
     kernel_avg = [sum(v) / len(v) for v in per_kernel]
     dom = max(range(launches), key=lambda k: kernel_avg[k])
-    names = ["scores_kernel", "walk_kernel"] if launches == 2 else ["kernel%d" % k for k in range(launches)]
+    names = kernel_names(cfg)
+    if len(names) != launches:
+        names = ["launch%d" % k for k in range(launches)]
     log("ms/step %.4f; per kernel avg ms: %s" % (ms, ", ".join("%s %.4f" % (n, t) for n, t in zip(names, kernel_avg))))
 
     if args.calibrate_copy_mib:
+        # a plain streaming kernel of known traffic for the counter calibration: torch's
+        # elementwise negation reads and writes calibrate_copy_mib MiB each
         n = args.calibrate_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
         torch.cuda.synchronize()
-        log("calibration copy: %d MiB read + %d MiB written" % (args.calibrate_copy_mib, args.calibrate_copy_mib))
+        dst = torch.neg(src)
+        torch.cuda.synchronize()
+        del dst
+        log("calibration: neg kernel reading and writing %d MiB each" % args.calibrate_copy_mib)
 
     tokens = cfg["batch"] * cfg["seqlen"]
     tok_s = tokens / (ms / 1e3)
@@ -224,7 +244,7 @@ def main():
     peak_tf = FP32_PEAK_TFLOPS if cfg["dtype"] == "fp32" else BF16_PEAK_TFLOPS
     dom_ms = kernel_avg[dom]
     achieved = nbytes / (dom_ms / 1e3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(args.workload, names[dom])
     result = {
         "metric": "SSD forward tokens/s + TFLOP/s (% MFMA peak) at B=8,T=2048,H=24,P=64,N=128",
         "value": tok_s,
