@@ -97,7 +97,7 @@ def kernel_names(cfg):
     if cfg["decay"] == "diag":
         return ["walk_diag_kernel<%d,%d>" % (N, P)]
     if cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128):
-        return ["prep_kernel<%d,%d>" % (N, Q), "walk5_kernel<%d,%d>" % (N, Q)]
+        return ["prep_kernel<%d,%d>" % (N, Q), "walk_fast_kernel<%d,%d>" % (N, Q)]
     return ["scores_kernel<%d>" % N, "walk_kernel<%d,%d>" % (N, P)]
 
 

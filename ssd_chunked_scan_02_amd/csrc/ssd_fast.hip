@@ -7,14 +7,14 @@
 //                 "pairs" (two 16x16 tiles along s) and the B^T MFMA operand fragments, both
 //                 stored in the lane order the walk reads them, so each is one coalesced
 //                 16-byte load per lane.
-//   walk5_kernel  one workgroup (8 waves, two roles) per (batch, head) walks the chunks with
-//                 the fp32 N x P state in registers.  Every global operand of chunk c+1 is
-//                 loaded into registers right after its last use in chunk c (one register
+//   walk_fast_kernel  one workgroup (8 waves, two roles) per (batch, head) walks the chunks
+//                 with the fp32 N x P state in registers.  Every global operand of chunk c+1
+//                 is loaded into registers right after its last use in chunk c (one register
 //                 set, rolling), and the one workgroup barrier per chunk orders LDS only, so
-//                 those loads stay in flight across it.  x is staged row-major in LDS and read as MFMA operands
-//                 that contract over tokens with the transposing LDS read ds_read_b64_tr_b16
-//                 (a 16-lane group whose lane 4j+q points at row r_j, columns 4q..4q+3 returns
-//                 in lane i column i of rows r_0..r_3).
+//                 those loads stay in flight across it.  x is staged row-major in LDS and read
+//                 as MFMA operands that contract over tokens with the transposing LDS read
+//                 ds_read_b64_tr_b16 (a 16-lane group whose lane 4j+q points at row r_j,
+//                 columns 4q..4q+3 returns in lane i column i of rows r_0..r_3).
 //
 // Token order inside a 32-token MFMA step: lane group g, element j holds token
 //   kperm(g, j) = 4g + j (j < 4),  16 + 4g + (j - 4) (j >= 4),
@@ -22,10 +22,10 @@
 // intra-chunk product straight from registers.
 //
 // Decay mask without an exp per score: for a 16-token output block tb starting at token a
-// and any token s before that block, exp(cum_t - cum_s) = f_t * beta(tb, sb) * u_s with
-//   f_t = exp(cum_t - cum_a),  beta(tb, sb) = exp(cum_a - cum_e),  u_s = exp(cum_e - cum_s),
-// e the last token of s's 16-token block; each factor is exp of a non-positive number.  Only
-// the scores of the 32-token step that contains the diagonal block take exact exps.
+// and any token s before that block, exp(cum_t - cum_s) = f_t * U(tb, s) with
+//   f_t = exp(cum_t - cum_a),  U(tb, s) = exp(cum_a - cum_s),
+// both exp of a non-positive number; U is one table per chunk, so a masked score costs one
+// multiply.  Only the 16x16 diagonal block of each output block takes exact exps.
 
 #include "ssd_common.h"
 #include "ssd_launch.h"
@@ -40,9 +40,6 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 constexpr int kP = 64;            // head dim handled here
 constexpr int kXStr = kP + 8;     // LDS row stride of the x tile, elements
 constexpr float kLog2e = 1.4426950408889634f;
-// s_waitcnt immediate with lgkmcnt = 0 and the vector-memory and export counters left at
-// their maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int kWaitLgkm0 = 0xC07F;
 
 __host__ __device__ constexpr int pair_base(int tb) {
     return (tb % 2 == 0) ? (tb / 2) * (tb / 2 + 1) : (tb / 2 + 1) * (tb / 2 + 1);
@@ -87,7 +84,9 @@ __device__ __forceinline__ void unpack8(bf16x8 v, float (&f)[8]) {
 // C rows in LDS and writes its share of
 //   pairs[(b,g,c)][pair(tb,k)][lane][8]: S^T[32k + kperm(lg, j)][16 tb + l16] (0 where the
 //       second tile lies above the diagonal), pair(tb,k) = pair_base(tb) + k, 2k <= tb;
-//   btf[(b,g,c)][nb][k][lane][8]: B[32k + kperm(lg, j)][16 nb + l16]  (the B^T operand).
+//   btf[(b,g,c)][nb][k][lane][8]: B[32k + kperm(lg, j)][16 nb + l16]  (the B^T operand);
+//   la_t[b][h][c Q + t] = log a[b][c Q + t][h] for the group's heads and this part's quarter of
+//       the chunk (0 past the sequence end), so the walk reads a head's chunk contiguously.
 constexpr int kPrepParts = 4;
 
 template <int N, int Q>
@@ -130,6 +129,17 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepParams prm) {
     }
     __syncthreads();
 
+    {
+        const int64_t HG = prm.nheads / prm.ngroups, tpad = (int64_t)prm.nchunks * Q;
+        constexpr int QP = Q / kPrepParts;
+        for (int id = tid; id < HG * QP; id += kThreads) {
+            const int t = part * QP + id % QP;
+            const int64_t h = g * HG + id / QP;
+            const float v = t < len ? prm.log_a[(b * prm.seqlen + t0 + t) * prm.nheads + h] : 0.f;
+            prm.la_t[(b * prm.nheads + h) * tpad + t0 + t] = v;
+        }
+    }
+
     __bf16* btf = prm.bt + blk * (int64_t)NB * KS * 512 + lane * 8;
     for (int f = worker; f < NB * KS; f += WORKERS) {
         const int nb = f / KS, k = f % KS;
@@ -160,8 +170,9 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepParams prm) {
 }
 
 // ---------------------------------------------------------------------------------------
-// walk5_kernel: 8 waves per (batch, head) in two roles; wave i runs on SIMD i % 4, so each
-// SIMD interleaves one wave of each role.
+// walk_fast_kernel: 8 waves per (batch, head) in two roles; wave i runs on SIMD i % 4, so
+// each SIMD interleaves one wave of each role.  Each role body is compiled once per wave
+// index, so every causal branch and block index below is resolved at compile time.
 //   output waves 0-3: y of their 16-token blocks for chunk c, from H_{k-1} (LDS), the staged
 //       x and decay factors of chunk c, C rows and score pairs (registers).
 //   state waves 4-7: H_k = exp(cum_last) H_{k-1} + B^T (w o X) for chunk c, written to the
@@ -169,12 +180,15 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepParams prm) {
 //       log a (wave-wide DPP scan), decay factors, x staged raw and weighted by w.
 // One LDS barrier per chunk; everything written for chunk c+1 goes to the other of two
 // buffers, whose previous contents (chunk c-1) every wave finished before the last barrier.
+//
+// Global addresses are a wave-uniform 64-bit base per chunk plus a 32-bit per-lane byte
+// offset (the host only takes this path when every offset inside a chunk fits).
 constexpr int kWalkWaves = 8;
 constexpr int kWalkThreads = kWalkWaves * kWave;
 
 // 16-token block handled by output wave `ow` in its r-th round (snake order balances the
 // causal work across the four output waves).
-__device__ __forceinline__ int wave_tb(int r, int ow) { return (r % 2 == 0) ? 4 * r + ow : 4 * r + 3 - ow; }
+__host__ __device__ constexpr int wave_tb(int r, int ow) { return (r % 2 == 0) ? 4 * r + ow : 4 * r + 3 - ow; }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row broadcasts.
 template <int CTRL, int ROWS>
@@ -191,339 +205,440 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     return x;
 }
 
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
+// 16-byte global load at a uniform base plus a per-lane byte offset.
+__device__ __forceinline__ uint4 ldg16(const void* base, uint32_t off) {
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
+}
+
+// Raw buffer resource over `bytes` bytes at `base`: buffer stores at or past that many bytes
+// are dropped by the hardware range check, which masks a short chunk's tail rows without a
+// branch.  The last word is the gfx9 default format (32-bit data, no swizzle).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
+}
+
+// Orders this wave's LDS writes before its later LDS reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 template <int N, int Q>
 struct WalkShape {
     static constexpr int NT = Q / 16, TBW = NT / 4, KS = Q / 32, KN = N / 32, NBW = N / 64;
     static constexpr int LA = Q / 64, QW = Q / 4, XCH = QW * 8 / kWave, NPAIR = n_pairs(NT);
     static constexpr int PB = kP / 16, HS = N + 8;
-    static constexpr int FSZ = 4 * Q + NT * NT + NT;  // floats of one decay-factor buffer
-    static constexpr size_t lds_bytes = (size_t)(4 * Q * kXStr + 2 * kP * HS) * 2 + (size_t)2 * FSZ * 4;
+    // one decay-factor buffer, floats: cum2 [Q] (log2 e times the running sum of log a),
+    // f [Q], w [Q], U [NT][Q], ea [NT]
+    static constexpr int FSZ = 3 * Q + NT * Q + NT;
+    static constexpr int YROWS = 16 * TBW;  // output rows of one output wave per chunk
+    static constexpr size_t lds_bytes =
+        (size_t)(4 * Q * kXStr + 2 * kP * HS + 4 * YROWS * kXStr) * 2 + (size_t)2 * FSZ * 4;
 };
 
+// Factors of one chunk, with cum the running sum of log a inside the chunk (inclusive),
+// a = 16 tb the first token of block tb and e the last token of the chunk:
+//   f[t]     = exp(cum_t - cum_{a(t)}), a(t) the first token of t's block   (<= 1)
+//   w[s]     = exp(cum_e - cum_s)                                            (<= 1)
+//   U[tb][s] = exp(cum_a - cum_s) for s < a, else 0                          (<= 1)
+//   ea[tb]   = exp(cum_a)                                                    (<= 1)
+// so that exp(cum_t - cum_s) = f[t] U[tb][s] for s before t's block and exp(cum_t) = f[t] ea[tb].
 template <int N, int Q>
-__global__ void __launch_bounds__(kWalkThreads) walk5_kernel(Walk2Params prm) {
+struct WalkLds {
     using WS = WalkShape<N, Q>;
-    constexpr int NT = WS::NT, TBW = WS::TBW, KS = WS::KS, KN = WS::KN, NBW = WS::NBW;
-    constexpr int LA = WS::LA, QW = WS::QW, XCH = WS::XCH, NPAIR = WS::NPAIR, PB = WS::PB, HS = WS::HS;
-    constexpr int FSZ = WS::FSZ;
+    __bf16* Xs;  // [2][Q][kXStr] x
+    __bf16* Xw;  // [2][Q][kXStr] w o x
+    __bf16* Hs;  // [2][kP][HS] H^T, bf16
+    __bf16* Ys;  // [4][YROWS][kXStr] each output wave's rows of y, staged for full-row stores
+    float* Fs;   // [2][FSZ]
+    __device__ explicit WalkLds(unsigned char* smem) {
+        Xs = reinterpret_cast<__bf16*>(smem);
+        Xw = Xs + 2 * Q * kXStr;
+        Hs = Xw + 2 * Q * kXStr;
+        Ys = Hs + 2 * kP * WS::HS;
+        Fs = reinterpret_cast<float*>(Ys + 4 * WS::YROWS * kXStr);
+    }
+    __device__ float* cum2(int buf) const { return Fs + buf * WS::FSZ; }
+    __device__ float* f(int buf) const { return Fs + buf * WS::FSZ + Q; }
+    __device__ float* w(int buf) const { return Fs + buf * WS::FSZ + 2 * Q; }
+    __device__ float* U(int buf) const { return Fs + buf * WS::FSZ + 3 * Q; }
+    __device__ float* ea(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q; }
+};
 
-    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
-    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
-    if (unit < 0) return;
-    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+template <int N, int Q, int OW>
+__device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const WalkLds<N, Q>& L, int64_t b,
+                                                 int64_t h, int64_t g, int lane) {
+    using WS = WalkShape<N, Q>;
+    constexpr int NT = WS::NT, TBW = WS::TBW, KS = WS::KS, KN = WS::KN, NPAIR = WS::NPAIR;
+    constexpr int PB = WS::PB, HS = WS::HS;
+    constexpr int KDMAX = wave_tb(TBW - 1, OW) / 2 > wave_tb(0, OW) / 2 ? wave_tb(TBW - 1, OW) / 2 : wave_tb(0, OW) / 2;
     const int l16 = lane % 16, lg = lane / 16;
-    const int rw = wave % 4;  // index of the wave within its role
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
     const int nchunks = prm.nchunks;
-
-    extern __shared__ __align__(16) unsigned char smem[];
-    __bf16* Xs = reinterpret_cast<__bf16*>(smem);             // [2][Q][kXStr] x
-    __bf16* Xw = Xs + 2 * Q * kXStr;                           // [2][Q][kXStr] w o x
-    __bf16* Hs = Xw + 2 * Q * kXStr;                           // [2][kP][HS] H^T, bf16
-    float* Fs = reinterpret_cast<float*>(Hs + 2 * kP * HS);    // [2][FSZ] decay factors
-    // one factor buffer: cum2 (log2 e times running sum of log a), u_s, f_t, w_s, beta, exp(cum_a)
-    auto fcum2 = [&](int buf) { return Fs + buf * FSZ; };
-    auto fu = [&](int buf) { return Fs + buf * FSZ + Q; };
-    auto ff = [&](int buf) { return Fs + buf * FSZ + 2 * Q; };
-    auto fw = [&](int buf) { return Fs + buf * FSZ + 3 * Q; };
-    auto fbeta = [&](int buf) { return Fs + buf * FSZ + 4 * Q; };
-    auto fea = [&](int buf) { return Fs + buf * FSZ + 4 * Q + NT * NT; };
-
-    const __bf16* xg = static_cast<const __bf16*>(prm.x);
+    const uint32_t c_row = (uint32_t)(G * N * 2), y_row = (uint32_t)(H * kP * 2);
     const __bf16* Cg = static_cast<const __bf16*>(prm.Cm);
     __bf16* yg = static_cast<__bf16*>(prm.y);
-    const uint4 zero = {0u, 0u, 0u, 0u};
-    const int64_t cbase = (b * G + g) * (int64_t)nchunks;
+    const __bf16* pairs0 = prm.pairs + (b * G + g) * (int64_t)nchunks * NPAIR * 512;
+    const float dskip = prm.D ? prm.D[h] : 0.f;
+    constexpr int YROWS = WS::YROWS, YST = YROWS * 8 / kWave;  // 16-byte stores per lane per chunk
+    __bf16* ys = L.Ys + OW * YROWS * kXStr;
     auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
 
-    if (wave < 4) {
-        // ================================ output waves
-        const int ow = rw;
-        const float dskip = prm.D ? prm.D[h] : 0.f;
-        const bool has_skip = prm.D != nullptr;
-        // Loads are unconditional with rows clamped into the chunk, so the compiler counts the
-        // loads in flight exactly; rows past a short chunk's end are never stored.
-        uint4 cf[TBW][KN], sp[TBW][KS];
-        auto load_c = [&](int c) {
-            const int64_t t0 = (int64_t)c * Q;
-            const int last = chunk_len(c) - 1;
+    // Loads are unconditional with rows clamped into the chunk, so the compiler counts the
+    // loads in flight exactly; rows past a short chunk's end are never stored.
+    uint4 cf[TBW][KN], sp[TBW][KS];
+    auto load_c = [&](int c) {
+        const int last = chunk_len(c) - 1;
+        const void* base = Cg + ((b * Tn + (int64_t)c * Q) * G + g) * N;
+#pragma unroll
+        for (int r = 0; r < TBW; ++r) {
+            const uint32_t off = (uint32_t)min(16 * wave_tb(r, OW) + l16, last) * c_row + 16 * lg;
+#pragma unroll
+            for (int k = 0; k < KN; ++k) cf[r][k] = ldg16(base, off + 64 * k);
+        }
+    };
+    auto load_s = [&](int c) {
+        const void* base = pairs0 + (int64_t)c * NPAIR * 512;
+#pragma unroll
+        for (int r = 0; r < TBW; ++r) {
+            const int tb = wave_tb(r, OW);
+#pragma unroll
+            for (int k = 0; k <= tb / 2; ++k) sp[r][k] = ldg16(base, 16 * lane + (pair_base(tb) + k) * 1024);
+        }
+    };
+    // inside a diagonal block, token 4 lg + j against token l16
+    bool causal[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) causal[j] = 4 * lg + j <= l16;
+
+    load_c(0);
+    load_s(0);
+    {
+        // As many stores as one chunk's outputs, all dropped (empty resource): the loop is then
+        // entered with the same memory operations in flight as each later chunk, and the
+        // compiler's load counting at the loop head stays exact instead of waiting for stores.
+        const __amdgpu_buffer_rsrc_t none = buffer_rsrc(yg + (b * Tn * H + h) * kP, 0u);
+#pragma unroll
+        for (int m = 0; m < YST; ++m) buffer_store16(none, 0u, uint4{0u, 0u, 0u, 0u});
+    }
+    lds_barrier();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int len = chunk_len(c);
+        const int cn = min(c + 1, nchunks - 1);
+        const int buf = c & 1;
+        const __bf16* xsm = L.Xs + buf * Q * kXStr;
+        const __bf16* hcur = L.Hs + buf * kP * HS;
+        const float* cum2 = L.cum2(buf);
+        const float* ffa = L.f(buf);
+        const float* Ut = L.U(buf);
+        const float* ea = L.ea(buf);
+
+        // carried state: acc = exp(cum_a) C_t H_{k-1}  (acc rows: p, columns: t)
+        f32x4 acc[TBW][PB];
+#pragma unroll
+        for (int r = 0; r < TBW; ++r)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) acc[r][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KN; ++k)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                const bf16x8 hf = as_bf16x8(ld16(hcur + (16 * pb + l16) * HS + 32 * k + 8 * lg));
+#pragma unroll
+                for (int r = 0; r < TBW; ++r) acc[r][pb] = mfma_bf16(hf, as_bf16x8(cf[r][k]), acc[r][pb]);
+            }
+        load_c(cn);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
+#pragma unroll
+        for (int r = 0; r < TBW; ++r) {
+            const float sc = ea[wave_tb(r, OW)];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) acc[r][pb] *= sc;
+        }
+
+        // inside the chunk: (S o L) X over the 32-token steps
+#pragma unroll
+        for (int k = 0; k <= KDMAX; ++k) {
+            bf16x8 xf[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) xf[pb] = token_frag(xsm, kXStr, 16 * pb, k, lane);
 #pragma unroll
             for (int r = 0; r < TBW; ++r) {
-                const int t = min(16 * wave_tb(r, ow) + l16, last);
-                const __bf16* crow = Cg + ((b * Tn + t0 + t) * G + g) * N + 8 * lg;
+                const int tb = wave_tb(r, OW);
+                const int kd = tb / 2;  // the step holding the diagonal block
+                if (k > kd) continue;
+                float s8[8];
+                unpack8(as_bf16x8(sp[r][k]), s8);
+                bf16x8 bop;
+                if (k < kd) {
+                    const f32x4 u0 = *reinterpret_cast<const f32x4*>(Ut + tb * Q + 32 * k + 4 * lg);
+                    const f32x4 u1 = *reinterpret_cast<const f32x4*>(Ut + tb * Q + 32 * k + 16 + 4 * lg);
 #pragma unroll
-                for (int k = 0; k < KN; ++k) cf[r][k] = ld16(crow + 32 * k);
-            }
-        };
-        auto load_s = [&](int c) {
-            const __bf16* pairs = prm.pairs + (cbase + c) * NPAIR * 512 + lane * 8;
+                    for (int j = 0; j < 4; ++j) {
+                        bop[j] = (__bf16)(s8[j] * u0[j]);
+                        bop[j + 4] = (__bf16)(s8[j + 4] * u1[j]);
+                    }
+                } else {
+                    // the remaining factor f_t first; then the diagonal block with exact exps
+                    // (and for an odd block, the block before it through U)
+                    const int t = 16 * tb + l16;
+                    const float ft = ffa[t];
 #pragma unroll
-            for (int r = 0; r < TBW; ++r) {
-                const int tb = wave_tb(r, ow);
-#pragma unroll
-                for (int k = 0; k < KS; ++k) sp[r][k] = ld16(pairs + (pair_base(tb) + min(k, tb / 2)) * 512);
-            }
-        };
-        load_c(0);
-        load_s(0);
-        int kdmax = 0;
-#pragma unroll
-        for (int r = 0; r < TBW; ++r) kdmax = max(kdmax, wave_tb(r, ow) / 2);
-        lds_barrier();
-
-        for (int c = 0; c < nchunks; ++c) {
-            const int64_t t0 = (int64_t)c * Q;
-            const int len = chunk_len(c);
-            const int cn = min(c + 1, nchunks - 1);
-            const int buf = c & 1;
-            const __bf16* xsm = Xs + buf * Q * kXStr;
-            const __bf16* hcur = Hs + buf * kP * HS;
-            const float* cum2 = fcum2(buf);
-            const float* uf = fu(buf);
-            const float* ffa = ff(buf);
-            const float* beta = fbeta(buf);
-            const float* ea = fea(buf);
-
-            // carried state: acc = exp(cum_a) C_t H_{k-1}
-            f32x4 acc[TBW][PB];
-#pragma unroll
-            for (int r = 0; r < TBW; ++r)
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) acc[r][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < KN; ++k)
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const bf16x8 hf = as_bf16x8(ld16(hcur + (16 * pb + l16) * HS + 32 * k + 8 * lg));
-#pragma unroll
-                    for (int r = 0; r < TBW; ++r) acc[r][pb] = mfma_bf16(hf, as_bf16x8(cf[r][k]), acc[r][pb]);
-                }
-            load_c(cn);
-#pragma unroll
-            for (int r = 0; r < TBW; ++r) {
-                const float sc = ea[wave_tb(r, ow)];
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) acc[r][pb] *= sc;
-            }
-
-            // inside the chunk: (S o L) X over the 32-token steps
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                if (k > kdmax) break;
-                bf16x8 xf[PB];
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) xf[pb] = token_frag(xsm, kXStr, 16 * pb, k, lane);
-                const f32x4 u0 = *reinterpret_cast<const f32x4*>(uf + 32 * k + 4 * lg);
-                const f32x4 u1 = *reinterpret_cast<const f32x4*>(uf + 32 * k + 16 + 4 * lg);
-#pragma unroll
-                for (int r = 0; r < TBW; ++r) {
-                    const int tb = wave_tb(r, ow);
-                    const int kd = tb / 2;  // step holding the diagonal block
-                    if (k > kd) continue;
-                    float s8[8];
-                    unpack8(as_bf16x8(sp[r][k]), s8);
-                    bf16x8 bop;
-                    if (k < kd) {
-                        const float b0 = beta[tb * NT + 2 * k], b1 = beta[tb * NT + 2 * k + 1];
+                    for (int pb = 0; pb < PB; ++pb) acc[r][pb] *= ft;
+                    const float ct = cum2[t];
+                    const f32x4 cd = *reinterpret_cast<const f32x4*>(cum2 + 16 * tb + 4 * lg);
+                    if (tb % 2 == 0) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            bop[j] = (__bf16)(s8[j] * (b0 * u0[j]));
-                            bop[j + 4] = (__bf16)(s8[j + 4] * (b1 * u1[j]));
+                            const float v = s8[j] * fexp2(ct - cd[j]);
+                            bop[j] = (__bf16)(causal[j] ? v : 0.f);
+                            bop[j + 4] = (__bf16)0.f;
                         }
                     } else {
-                        // remaining factor f_t first, then the exact diagonal step
-                        const int t = 16 * tb + l16;
-                        const float ft = ffa[t];
+                        const f32x4 u0 = *reinterpret_cast<const f32x4*>(Ut + tb * Q + 32 * k + 4 * lg);
 #pragma unroll
-                        for (int pb = 0; pb < PB; ++pb) acc[r][pb] *= ft;
-                        const float ct = cum2[t];
-                        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cum2 + 32 * k + 4 * lg);
-                        const f32x4 c1 = *reinterpret_cast<const f32x4*>(cum2 + 32 * k + 16 + 4 * lg);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const int s = 32 * k + kperm(lg, j);
-                            const float cs = j < 4 ? c0[j] : c1[j - 4];
-                            const bool causal = s <= t;
-                            bop[j] = (__bf16)(causal ? s8[j] * fexp2(causal ? ct - cs : 0.f) : 0.f);
+                        for (int j = 0; j < 4; ++j) {
+                            bop[j] = (__bf16)(s8[j] * (ft * u0[j]));
+                            const float v = s8[j + 4] * fexp2(ct - cd[j]);
+                            bop[j + 4] = (__bf16)(causal[j] ? v : 0.f);
                         }
                     }
-#pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) acc[r][pb] = mfma_bf16(xf[pb], bop, acc[r][pb]);
                 }
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) acc[r][pb] = mfma_bf16(xf[pb], bop, acc[r][pb]);
             }
-            load_s(cn);
-
-            // skip term, outputs
-#pragma unroll
-            for (int r = 0; r < TBW; ++r) {
-                const int t = 16 * wave_tb(r, ow) + l16;
-                if (has_skip) {
-#pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) {
-                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                        const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(xsm + t * kXStr + 16 * pb + 4 * lg);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[r][pb][i] += dskip * (float)x4[i];
-                    }
-                }
-                if (t < len) {
-                    __bf16* yr = yg + ((b * Tn + t0 + t) * H + h) * kP + 4 * lg;
-#pragma unroll
-                    for (int pb = 0; pb < PB; ++pb)
-                        store4(yr + 16 * pb, acc[r][pb][0], acc[r][pb][1], acc[r][pb][2], acc[r][pb][3]);
-                }
-            }
-            lds_barrier();
         }
-    } else {
-        // ================================ state waves
-        const int sw = rw;
-        float la[LA];
-        uint4 xs[XCH];
-        uint4 bt[NBW][KS];
-        // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
-        // quarter of the chunk; rows clamped into the chunk, masked when staged
-        auto load_lax = [&](int c) {
-            const int64_t t0 = (int64_t)c * Q;
-            const int last = chunk_len(c) - 1;
-#pragma unroll
-            for (int j = 0; j < LA; ++j) la[j] = prm.log_a[(b * Tn + t0 + min(lane * LA + j, last)) * H + h];
-#pragma unroll
-            for (int m = 0; m < XCH; ++m) {
-                const int id = lane + kWave * m, row = min(QW * sw + id / 8, last), c16 = id % 8;
-                xs[m] = ld16(xg + ((b * Tn + t0 + row) * H + h) * kP + 8 * c16);
-            }
-        };
-        auto load_b = [&](int c) {
-            const __bf16* btf = prm.bt + (cbase + c) * (N / 16) * KS * 512 + lane * 8;
-#pragma unroll
-            for (int jn = 0; jn < NBW; ++jn)
-#pragma unroll
-                for (int k = 0; k < KS; ++k) bt[jn][k] = ld16(btf + ((sw + 4 * jn) * KS + k) * 512);
-        };
-        // Decay factors of chunk c into factor buffer c & 1 and x of chunk c into the x
-        // buffers c & 1.  Returns exp(cum_last).
-        auto prepare = [&](int c) -> float {
-            const int len = chunk_len(c);
-            const int buf = c & 1;
-            float cum[LA], run = 0.f;
-#pragma unroll
-            for (int j = 0; j < LA; ++j) { run += (lane * LA + j < len) ? la[j] : 0.f; cum[j] = run; }
-            const float incl = wave_inclusive_sum(run);
-            const float excl = incl - run;
-#pragma unroll
-            for (int j = 0; j < LA; ++j) cum[j] = (excl + cum[j]) * kLog2e;
-            const float last2 = __shfl(incl, kWave - 1, kWave) * kLog2e;
-            float* cum2 = fcum2(buf);
-            // this wave's quarter of the tokens: lanes [16 sw, 16 sw + 16)
-            const bool mine = lane / 16 == sw;
-            if (mine) {
-#pragma unroll
-                for (int j = 0; j < LA; ++j) cum2[lane * LA + j] = cum[j];
-            }
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave reads back what it wrote
-            if (mine) {
-#pragma unroll
-                for (int j = 0; j < LA; ++j) {
-                    const int t = lane * LA + j;
-                    fu(buf)[t] = fexp2(cum2[t | 15] - cum[j]);
-                    ff(buf)[t] = fexp2(cum[j] - cum2[t & ~15]);
-                    fw(buf)[t] = fexp2(last2 - cum[j]);
-                }
-            }
-            if (sw == 0) {
-                // block boundary sums straight from the lanes that hold them
-                const float a2 = __shfl(cum[0], (16 * (lane / NT)) / LA, kWave);
-                const float e2 = __shfl(cum[LA - 1], (16 * (lane % NT) + 15) / LA, kWave);
-                if (lane < NT * NT) fbeta(buf)[lane] = (lane % NT) < (lane / NT) ? fexp2(a2 - e2) : 0.f;
-                const float s2 = __shfl(cum[0], (16 * lane) / LA, kWave);
-                if (lane < NT) fea(buf)[lane] = fexp2(s2);
-            }
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            __bf16* xsm = Xs + buf * Q * kXStr;
-            __bf16* xwm = Xw + buf * Q * kXStr;
-            const float* wrow = fw(buf);
-#pragma unroll
-            for (int m = 0; m < XCH; ++m) {
-                const int id = lane + kWave * m, row = QW * sw + id / 8, c16 = id % 8;
-                const uint4 raw = row < len ? xs[m] : zero;
-                st16(xsm + row * kXStr + 8 * c16, raw);
-                const float w = wrow[row];
-                const bf16x8 rv = as_bf16x8(raw);
-                bf16x8 sv;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sv[j] = (__bf16)((float)rv[j] * w);
-                *reinterpret_cast<bf16x8*>(xwm + row * kXStr + 8 * c16) = sv;
-            }
-            return fexp2(last2);
-        };
+        load_s(cn);
+        __builtin_amdgcn_sched_barrier(0);
 
-        f32x4 hs[NBW][PB];
+        // skip term; y through this wave's LDS rows, then stored as whole 128-byte rows (rows
+        // past a short chunk's end fall outside the buffer resource and are dropped)
+#pragma unroll
+        for (int r = 0; r < TBW; ++r) {
+            const int t = 16 * wave_tb(r, OW) + l16;
+            // (no branch on D: a missing skip term adds 0 x; one path keeps the load counting exact)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(xsm + t * kXStr + 16 * pb + 4 * lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[r][pb][i] += dskip * (float)x4[i];
+            }
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+                store4(ys + (16 * r + l16) * kXStr + 16 * pb + 4 * lg, acc[r][pb][0], acc[r][pb][1], acc[r][pb][2],
+                       acc[r][pb][3]);
+        }
+        wave_lds_fence();
+        const __amdgpu_buffer_rsrc_t yr =
+            buffer_rsrc(yg + ((b * Tn + (int64_t)c * Q) * H + h) * kP, (uint32_t)len * y_row);
+#pragma unroll
+        for (int m = 0; m < YST; ++m) {
+            const int id = lane + kWave * m, row = id / 8, c8 = id % 8;
+            const int t = 16 * wave_tb(row / 16, OW) + row % 16;
+            buffer_store16(yr, (uint32_t)t * y_row + 16 * c8, ld16(ys + row * kXStr + 8 * c8));
+        }
+        lds_barrier();
+    }
+}
+
+template <int N, int Q, int SW>
+__device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, int64_t b,
+                                                int64_t h, int64_t g, int64_t unit, int lane) {
+    using WS = WalkShape<N, Q>;
+    constexpr int NT = WS::NT, KS = WS::KS, NBW = WS::NBW, LA = WS::LA, QW = WS::QW, XCH = WS::XCH;
+    constexpr int PB = WS::PB, HS = WS::HS;
+    const int l16 = lane % 16, lg = lane / 16;
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
+    const int nchunks = prm.nchunks;
+    const uint32_t x_row = (uint32_t)(H * kP * 2);
+    const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
+    const __bf16* xg = static_cast<const __bf16*>(prm.x);
+    const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * (N / 16) * KS * 512;
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
+
+    float la[LA];
+    uint4 xs[XCH];
+    uint4 bt[NBW][KS];
+    // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
+    // quarter of the chunk; rows clamped into the chunk, masked when staged
+    auto load_lax = [&](int c) {
+        const int last = chunk_len(c) - 1;
+        const int64_t t0 = (int64_t)c * Q;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) la[j] = la0[t0 + lane * LA + j];
+        const void* xbase = xg + ((b * Tn + t0) * H + h) * kP;
+#pragma unroll
+        for (int m = 0; m < XCH; ++m) {
+            const int id = lane + kWave * m, row = min(QW * SW + id / 8, last), c16 = id % 8;
+            xs[m] = ldg16(xbase, (uint32_t)row * x_row + 16 * c16);
+        }
+    };
+    auto load_b = [&](int c) {
+        const void* base = bt0 + (int64_t)c * (N / 16) * KS * 512;
+#pragma unroll
+        for (int jn = 0; jn < NBW; ++jn)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) bt[jn][k] = ldg16(base, 16 * lane + ((SW + 4 * jn) * KS + k) * 1024);
+    };
+    // Decay factors of chunk c into factor buffer c & 1 and x of chunk c into the x
+    // buffers c & 1.  Returns exp(cum_last).
+    auto prepare = [&](int c) -> float {
+        const int len = chunk_len(c);
+        const int buf = c & 1;
+        float cum[LA], run = 0.f;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) { run += (lane * LA + j < len) ? la[j] : 0.f; cum[j] = run; }
+        const float incl = wave_inclusive_sum(run);
+        const float excl = incl - run;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) cum[j] = (excl + cum[j]) * kLog2e;
+        const float last2 = lane_value(incl, kWave - 1) * kLog2e;
+        // running sum at the first token of this lane's 16-token block
+        const float blk2 = __shfl(cum[0], lane & ~(16 / LA - 1), kWave);
+        // this wave's quarter of the tokens: lanes [16 SW, 16 SW + 16)
+        if (lane / 16 == SW) {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                const int t = lane * LA + j;
+                L.cum2(buf)[t] = cum[j];
+                L.f(buf)[t] = fexp2(cum[j] - blk2);
+                L.w(buf)[t] = fexp2(last2 - cum[j]);
+            }
+        }
+        // rows SW, SW + 4, ... of U
+#pragma unroll
+        for (int tb = SW; tb < NT; tb += 4) {
+            const float ca = lane_value(cum[0], 16 * tb / LA);
+            float* urow = L.U(buf) + tb * Q;
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                const int s = lane * LA + j;
+                urow[s] = s < 16 * tb ? fexp2(ca - cum[j]) : 0.f;
+            }
+        }
+        if (SW == 0) {
+            const float s2 = __shfl(cum[0], (16 * lane) / LA, kWave);
+            if (lane < NT) L.ea(buf)[lane] = fexp2(s2);
+        }
+        wave_lds_fence();  // this wave reads back the w it wrote
+        __bf16* xsm = L.Xs + buf * Q * kXStr;
+        __bf16* xwm = L.Xw + buf * Q * kXStr;
+        const float* wrow = L.w(buf);
+#pragma unroll
+        for (int m = 0; m < XCH; ++m) {
+            const int id = lane + kWave * m, row = QW * SW + id / 8, c16 = id % 8;
+            const uint4 raw = row < len ? xs[m] : zero;
+            st16(xsm + row * kXStr + 8 * c16, raw);
+            const float w = wrow[row];
+            const bf16x8 rv = as_bf16x8(raw);
+            bf16x8 sv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sv[j] = (__bf16)((float)rv[j] * w);
+            *reinterpret_cast<bf16x8*>(xwm + row * kXStr + 8 * c16) = sv;
+        }
+        return fexp2(last2);
+    };
+
+    f32x4 hs[NBW][PB];
+#pragma unroll
+    for (int jn = 0; jn < NBW; ++jn)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+            hs[jn][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (prm.init) {
+                const int n = 16 * (SW + 4 * jn) + 4 * lg;
+                const float* src = prm.init + (unit * N + n) * kP + 16 * pb + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hs[jn][pb][i] = src[i * kP];
+            }
+        }
+    auto write_state = [&](__bf16* hsm) {
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) {
-                hs[jn][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (prm.init) {
-                    const int n = 16 * (sw + 4 * jn) + 4 * lg;
-                    const float* src = prm.init + (unit * N + n) * kP + 16 * pb + l16;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hs[jn][pb][i] = src[i * kP];
-                }
+                const int n = 16 * (SW + 4 * jn) + 4 * lg;
+                store4(hsm + (16 * pb + l16) * HS + n, hs[jn][pb][0], hs[jn][pb][1], hs[jn][pb][2], hs[jn][pb][3]);
             }
-        auto write_state = [&](__bf16* hsm) {
-#pragma unroll
-            for (int jn = 0; jn < NBW; ++jn)
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const int n = 16 * (sw + 4 * jn) + 4 * lg;
-                    store4(hsm + (16 * pb + l16) * HS + n, hs[jn][pb][0], hs[jn][pb][1], hs[jn][pb][2], hs[jn][pb][3]);
-                }
-        };
+    };
 
-        load_lax(0);
-        load_b(0);
-        float el = prepare(0);
-        load_lax(min(1, nchunks - 1));
-        write_state(Hs);
+    load_lax(0);
+    load_b(0);
+    float el = prepare(0);
+    load_lax(min(1, nchunks - 1));
+    write_state(L.Hs);
+    lds_barrier();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int cn = min(c + 1, nchunks - 1);
+        const __bf16* xwm = L.Xw + (c & 1) * Q * kXStr;
+        // H_k = exp(cum_last) H_{k-1} + B^T (w o X)
+#pragma unroll
+        for (int jn = 0; jn < NBW; ++jn)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) hs[jn][pb] *= el;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                const bf16x8 xf = token_frag(xwm, kXStr, 16 * pb, k, lane);
+#pragma unroll
+                for (int jn = 0; jn < NBW; ++jn) hs[jn][pb] = mfma_bf16(as_bf16x8(bt[jn][k]), xf, hs[jn][pb]);
+            }
+        load_b(cn);
+        // the next chunk's factors while the state MFMAs drain, then the state itself.  Run
+        // unconditionally (past the last chunk they fill the unused buffer with zeros), so the
+        // loop body has one path and the compiler's load counting stays exact.
+        el = prepare(c + 1);
+        load_lax(min(c + 2, nchunks - 1));
+        write_state(L.Hs + ((c + 1) & 1) * kP * HS);
         lds_barrier();
+    }
 
-        for (int c = 0; c < nchunks; ++c) {
-            const int cn = min(c + 1, nchunks - 1);
-            const __bf16* xwm = Xw + (c & 1) * Q * kXStr;
-            // H_k = exp(cum_last) H_{k-1} + B^T (w o X)
+    if (prm.final_state) {
 #pragma unroll
-            for (int jn = 0; jn < NBW; ++jn)
+        for (int jn = 0; jn < NBW; ++jn)
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) hs[jn][pb] *= el;
+            for (int pb = 0; pb < PB; ++pb) {
+                const int n = 16 * (SW + 4 * jn) + 4 * lg;
+                float* dst = prm.final_state + (unit * N + n) * kP + 16 * pb + l16;
 #pragma unroll
-            for (int k = 0; k < KS; ++k)
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const bf16x8 xf = token_frag(xwm, kXStr, 16 * pb, k, lane);
-#pragma unroll
-                    for (int jn = 0; jn < NBW; ++jn) hs[jn][pb] = mfma_bf16(as_bf16x8(bt[jn][k]), xf, hs[jn][pb]);
-                }
-            load_b(cn);
-            write_state(Hs + ((c + 1) & 1) * kP * HS);
-            if (c + 1 < nchunks) {
-                el = prepare(c + 1);
-                load_lax(min(c + 2, nchunks - 1));
+                for (int i = 0; i < 4; ++i) dst[i * kP] = hs[jn][pb][i];
             }
-            lds_barrier();
-        }
+    }
+}
 
-        if (prm.final_state) {
-#pragma unroll
-            for (int jn = 0; jn < NBW; ++jn)
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const int n = 16 * (sw + 4 * jn) + 4 * lg;
-                    float* dst = prm.final_state + (unit * N + n) * kP + 16 * pb + l16;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[i * kP] = hs[jn][pb][i];
-                }
-        }
+template <int N, int Q>
+__global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm) {
+    const int64_t H = prm.nheads;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / prm.ngroups);
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    extern __shared__ __align__(16) unsigned char smem[];
+    const WalkLds<N, Q> L(smem);
+    switch (wave) {
+        case 0: walk_output_role<N, Q, 0>(prm, L, b, h, g, lane); break;
+        case 1: walk_output_role<N, Q, 1>(prm, L, b, h, g, lane); break;
+        case 2: walk_output_role<N, Q, 2>(prm, L, b, h, g, lane); break;
+        case 3: walk_output_role<N, Q, 3>(prm, L, b, h, g, lane); break;
+        case 4: walk_state_role<N, Q, 0>(prm, L, b, h, g, unit, lane); break;
+        case 5: walk_state_role<N, Q, 1>(prm, L, b, h, g, unit, lane); break;
+        case 6: walk_state_role<N, Q, 2>(prm, L, b, h, g, unit, lane); break;
+        default: walk_state_role<N, Q, 3>(prm, L, b, h, g, unit, lane); break;
     }
 }
 
@@ -552,9 +667,10 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     __bf16* pairs = reinterpret_cast<__bf16*>(fl.scores);
     const int64_t nblk = fl.batch * fl.ngroups * fl.nchunks;
     __bf16* bt = pairs + nblk * NPAIR * 512;
-    PrepParams pp{fl.Bm, fl.Cm, pairs, bt, fl.seqlen, fl.ngroups, fl.nchunks};
+    float* la_t = reinterpret_cast<float*>(bt + nblk * (N / 16) * (Q / 32) * 512);
+    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, la_t, fl.seqlen, fl.nheads, fl.ngroups, fl.nchunks};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
-    if (!allow_full_lds(reinterpret_cast<const void*>(&walk5_kernel<N, Q>), walk_attr)) return -1;
+    if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q>), walk_attr)) return -1;
     if (!record_event(fl, 0, stream)) return -1;
     const size_t plds = prep_lds<N, Q>();
     hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)(nblk * kPrepParts)), dim3(kThreads), plds, stream, pp);
@@ -562,11 +678,11 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
 
     const int64_t units = fl.batch * fl.nheads;
     const int64_t per_xcd = (units + 7) / 8;
-    Walk2Params wp{fl.x, fl.log_a, fl.Cm, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
+    Walk2Params wp{fl.x, la_t, fl.Cm, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.nchunks, per_xcd};
     if (!record_event(fl, 1, stream)) return -1;
     const size_t wlds = WalkShape<N, Q>::lds_bytes;
-    hipLaunchKernelGGL((walk5_kernel<N, Q>), dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream, wp);
+    hipLaunchKernelGGL((walk_fast_kernel<N, Q>), dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream, wp);
     if (hipGetLastError() != hipSuccess) return -1;
     if (!record_event(fl, 2, stream)) return -1;
     if (fl.n_launches) *fl.n_launches = 2;
@@ -575,13 +691,17 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
 
 }  // namespace
 
-bool fast_path_applies(int dtype, int decay, int N, int P, int chunk) {
-    return dtype == 1 && decay == 0 && P == kP && (N == 64 || N == 128) && (chunk == 64 || chunk == 128);
+bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups) {
+    // byte offsets inside one chunk (chunk rows of x, y, B, C) must fit in 32 bits
+    const bool offsets_fit = (double)chunk * (double)(nheads * P + ngroups * N) * 2.0 < 2147483648.0;
+    return dtype == 1 && decay == 0 && P == kP && (N == 64 || N == 128) && (chunk == 64 || chunk == 128) &&
+           offsets_fit;
 }
 
-size_t fast_workspace_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int N, int chunk) {
+size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t nchunks, int N, int chunk) {
     const int64_t nblk = batch * ngroups * nchunks;
-    return (size_t)nblk * ((size_t)n_pairs(chunk / 16) * 1024 + (size_t)N * chunk * 2);
+    return (size_t)nblk * ((size_t)n_pairs(chunk / 16) * 1024 + (size_t)N * chunk * 2) +
+           (size_t)(batch * nheads * nchunks * chunk) * 4;
 }
 
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream) {

@@ -483,7 +483,7 @@ int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
         return 0;
     }
     if (fl.decay == 1) return launch_forward_diag(fl, stream);
-    if (fast_path_applies(fl.dtype, fl.decay, (int)fl.dstate, (int)fl.headdim, fl.chunk))
+    if (fast_path_applies(fl.dtype, fl.decay, (int)fl.dstate, (int)fl.headdim, fl.chunk, fl.nheads, fl.ngroups))
         return launch_forward_fast(fl, stream);
 #define SSD_LAUNCH(TT, NN, PP) \
     if ((std::is_same<TT, float>::value ? 0 : 1) == fl.dtype && fl.dstate == NN && fl.headdim == PP) \

@@ -49,16 +49,19 @@ struct StepParams {
 struct PrepParams {
     const void* Bm;
     const void* Cm;
+    const float* log_a;
     __bf16* pairs;  // score tile pairs, bf16, lane order
     __bf16* bt;     // B^T per chunk, tokens in MFMA K order
+    float* la_t;    // log a head-major: [batch][nheads][nchunks * chunk], 0 past the end
     int64_t seqlen;
+    int64_t nheads;
     int64_t ngroups;
     int nchunks;
 };
 
 struct Walk2Params {
     const void* x;
-    const float* log_a;
+    const float* la_t;  // log a head-major (PrepParams::la_t)
     const void* Cm;
     const float* D;
     const __bf16* pairs;
@@ -96,8 +99,8 @@ bool shape_supported(int dtype, int N, int P);
 // Records the caller's timing event k (if any) on the stream; false on a HIP error.
 bool record_event(const ForwardLaunch& fl, int k, hipStream_t stream);
 // The pipelined bf16 path (ssd_fast.hip) and its workspace.
-bool fast_path_applies(int dtype, int decay, int N, int P, int chunk);
-size_t fast_workspace_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int N, int chunk);
+bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups);
+size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t nchunks, int N, int chunk);
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream);
 // The diagonal-decay walk (ssd_diag.hip): LDS bytes (0 = unsupported) and launch.
 size_t diag_lds_bytes(int dtype, int N, int P, int chunk);

@@ -56,12 +56,14 @@ def n_pairs(nt):
 
 def test_workspace_bytes(lib):
     # bf16, scalar decay, head dim 64, N in {64,128}, chunk in {64,128}: per (batch, group,
-    # chunk) the bf16 score-tile pairs (1 KiB each) and the B^T operand (N * chunk * 2 bytes)
-    fast = lambda nblk, N, Q: nblk * (n_pairs(Q // 16) * 1024 + N * Q * 2)
-    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 128) == fast(8 * 16, 128, 128)
+    # chunk) the bf16 score-tile pairs (1 KiB each) and the B^T operand (N * chunk * 2 bytes),
+    # plus log a head-major over whole chunks (4 bytes per (batch, head, padded token))
+    fast = lambda batch, heads, groups, nch, N, Q: (batch * groups * nch * (n_pairs(Q // 16) * 1024 + N * Q * 2)
+                                                    + batch * heads * nch * Q * 4)
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 128) == fast(8, 24, 1, 16, 128, 128)
     # ragged: 2050 tokens -> 17 chunks
-    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=2050), 128) == fast(8 * 17, 128, 128)
-    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(ngroups=8, nheads=64), 64) == fast(8 * 8 * 32, 128, 64)
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=2050), 128) == fast(8, 24, 1, 17, 128, 128)
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(ngroups=8, nheads=64), 64) == fast(8, 64, 8, 32, 128, 64)
     # other shapes: causal 16x16 fp32 score tiles per (batch, group, chunk)
     tiles = lambda nblk, Q: nblk * (Q // 16) * (Q // 16 + 1) // 2 * 1024
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(dtype=0), 64) == tiles(8 * 32, 64)
