@@ -80,74 +80,94 @@ __device__ __forceinline__ void unpack8(bf16x8 v, float (&f)[8]) {
 }
 
 // ---------------------------------------------------------------------------------------
-// prep_kernel: kPrepParts workgroups per (batch, group, chunk); each stages the chunk's B and
-// C rows in LDS and writes its share of
+// prep_kernel: one workgroup (8 waves) per (batch, group, chunk).  It reads the chunk's B and
+// C rows once, stages them in LDS (rows past the sequence end as zeros) and writes
 //   pairs[(b,g,c)][pair(tb,k)][lane][8]: S^T[32k + kperm(lg, j)][16 tb + l16] (0 where the
 //       second tile lies above the diagonal), pair(tb,k) = pair_base(tb) + k, 2k <= tb;
+//   ct[(b,g,c)][tb][k][lane][8]: C[16 tb + l16][32k + 8 lg + j]  (the C^T operand);
 //   btf[(b,g,c)][nb][k][lane][8]: B[32k + kperm(lg, j)][16 nb + l16]  (the B^T operand);
-//   la_t[b][h][c Q + t] = log a[b][c Q + t][h] for the group's heads and this part's quarter of
-//       the chunk (0 past the sequence end), so the walk reads a head's chunk contiguously.
-constexpr int kPrepParts = 4;
+//   la_t[b][h][c Q + t] = log a[b][c Q + t][h] for the group's heads (0 past the sequence
+//       end), so the walk reads a head's chunk contiguously.
+constexpr int kPrepWaves = 8;
+constexpr int kPrepThreads = kPrepWaves * kWave;
+// log a items (head, 4 tokens) per prep thread: heads per group up to kPrepLa * 4 * 512 / chunk
+constexpr int kPrepLa = 4;
 
 template <int N, int Q>
-__global__ void __launch_bounds__(kThreads) prep_kernel(PrepParams prm) {
-    constexpr int NT = Q / 16, KS = Q / 32, NB = N / 16;
+__global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepParams prm) {
+    constexpr int NT = Q / 16, KS = Q / 32, NB = N / 16, KN = N / 32;
     constexpr int NPAIR = n_pairs(NT);
     constexpr int NS = N + 8;
-    constexpr int WORKERS = kPrepParts * kWaves;
+    constexpr int ITEMS = Q * (N / 8) / kPrepThreads;  // 16-byte pieces of B (and of C) per thread
     extern __shared__ __align__(16) unsigned char smem[];
     __bf16* Bs = reinterpret_cast<__bf16*>(smem);   // [Q][NS]
     __bf16* Cs = Bs + Q * NS;                       // [Q][NS]
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane % 16, lg = lane / 16;
-    const int part = blockIdx.x % kPrepParts;
-    const int64_t blk = blockIdx.x / kPrepParts;
-    const int worker = part * kWaves + wave;
+    const int64_t blk = blockIdx.x;
     const int c = (int)(blk % prm.nchunks);
     const int64_t bg = blk / prm.nchunks;
     const int64_t b = bg / prm.ngroups, g = bg % prm.ngroups;
     const int64_t t0 = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, prm.seqlen - t0);
-    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm);
-    const __bf16* Cg = static_cast<const __bf16*>(prm.Cm);
+    const int64_t rs = prm.ngroups * N;
+    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm) + ((b * prm.seqlen + t0) * prm.ngroups + g) * N;
+    const __bf16* Cg = static_cast<const __bf16*>(prm.Cm) + ((b * prm.seqlen + t0) * prm.ngroups + g) * N;
     const uint4 zero = {0u, 0u, 0u, 0u};
 
-    constexpr int ITEMS = Q * (N / 8) / kThreads;
+    // every global load first, so one wait covers them all
     uint4 vb[ITEMS], vc[ITEMS];
 #pragma unroll
     for (int m = 0; m < ITEMS; ++m) {
-        const int id = tid + kThreads * m, row = id / (N / 8), c8 = id % (N / 8);
-        const int64_t off = ((b * prm.seqlen + t0 + min(row, len - 1)) * prm.ngroups + g) * N + 8 * c8;
+        const int id = tid + kPrepThreads * m, row = id / (N / 8), c8 = id % (N / 8);
+        const int64_t off = min(row, len - 1) * rs + 8 * c8;
         vb[m] = ld16(Bg + off);
         vc[m] = ld16(Cg + off);
     }
+    // log a head-major: item (head, 4 tokens) gathers 4 rows (consecutive threads read
+    // consecutive heads of a row) and writes 16 contiguous bytes; rows clamped, masked below
+    const int HG = (int)(prm.nheads / prm.ngroups);
+    const int nla = HG * (Q / 4);
+    const float* lag = prm.log_a + (b * prm.seqlen + t0) * prm.nheads + g * HG;
+    f32x4 lv[kPrepLa];
+#pragma unroll
+    for (int i = 0; i < kPrepLa; ++i) {
+        const int id = min(tid + kPrepThreads * i, nla - 1), hl = id % HG, t4 = 4 * (id / HG);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lv[i][j] = lag[(int64_t)min(t4 + j, len - 1) * prm.nheads + hl];
+    }
+    {
+        const int64_t tpad = (int64_t)prm.nchunks * Q;
+        float* dst = prm.la_t + (b * prm.nheads + g * HG) * tpad + t0;
+#pragma unroll
+        for (int i = 0; i < kPrepLa; ++i) {
+            const int id = tid + kPrepThreads * i, hl = id % HG, t4 = 4 * (id / HG);
+            f32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = t4 + j < len ? lv[i][j] : 0.f;
+            if (id < nla) *reinterpret_cast<f32x4*>(dst + hl * tpad + t4) = v;
+        }
+    }
 #pragma unroll
     for (int m = 0; m < ITEMS; ++m) {
-        const int id = tid + kThreads * m, row = id / (N / 8), c8 = id % (N / 8);
+        const int id = tid + kPrepThreads * m, row = id / (N / 8), c8 = id % (N / 8);
         st16(Bs + row * NS + 8 * c8, row < len ? vb[m] : zero);
         st16(Cs + row * NS + 8 * c8, row < len ? vc[m] : zero);
     }
     __syncthreads();
 
-    {
-        const int64_t HG = prm.nheads / prm.ngroups, tpad = (int64_t)prm.nchunks * Q;
-        constexpr int QP = Q / kPrepParts;
-        for (int id = tid; id < HG * QP; id += kThreads) {
-            const int t = part * QP + id % QP;
-            const int64_t h = g * HG + id / QP;
-            const float v = t < len ? prm.log_a[(b * prm.seqlen + t0 + t) * prm.nheads + h] : 0.f;
-            prm.la_t[(b * prm.nheads + h) * tpad + t0 + t] = v;
-        }
+    __bf16* ct = prm.ct + blk * (int64_t)NT * KN * 512 + lane * 8;
+    for (int f = wave; f < NT * KN; f += kPrepWaves) {
+        const int tb = f / KN, k = f % KN;
+        st16(ct + f * 512, ld16(Cs + (16 * tb + l16) * NS + 32 * k + 8 * lg));
     }
-
     __bf16* btf = prm.bt + blk * (int64_t)NB * KS * 512 + lane * 8;
-    for (int f = worker; f < NB * KS; f += WORKERS) {
+    for (int f = wave; f < NB * KS; f += kPrepWaves) {
         const int nb = f / KS, k = f % KS;
         *reinterpret_cast<bf16x8*>(btf + f * 512) = token_frag(Bs, NS, 16 * nb, k, lane);
     }
-
     __bf16* pairs = prm.pairs + blk * (int64_t)NPAIR * 512 + lane * 8;
-    for (int idx = worker; idx < NPAIR; idx += WORKERS) {
+    for (int idx = wave; idx < NPAIR; idx += kPrepWaves) {
         int tb = 0;
         while (pair_base(tb + 1) <= idx) ++tb;
         const int k = idx - pair_base(tb);
@@ -157,7 +177,7 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrepParams prm) {
             const int sb = 2 * k + hh;
             if (sb > tb) continue;
 #pragma unroll
-            for (int kk = 0; kk < N / 32; ++kk) {
+            for (int kk = 0; kk < KN; ++kk) {
                 const bf16x8 a = as_bf16x8(ld16(Bs + (16 * sb + l16) * NS + 32 * kk + 8 * lg));
                 const bf16x8 bb = as_bf16x8(ld16(Cs + (16 * tb + l16) * NS + 32 * kk + 8 * lg));
                 acc[hh] = mfma_bf16(a, bb, acc[hh]);
@@ -284,8 +304,8 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     const int l16 = lane % 16, lg = lane / 16;
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
     const int nchunks = prm.nchunks;
-    const uint32_t c_row = (uint32_t)(G * N * 2), y_row = (uint32_t)(H * kP * 2);
-    const __bf16* Cg = static_cast<const __bf16*>(prm.Cm);
+    const uint32_t y_row = (uint32_t)(H * kP * 2);
+    const __bf16* ct0 = prm.ct + (b * G + g) * (int64_t)nchunks * NT * KN * 512;
     __bf16* yg = static_cast<__bf16*>(prm.y);
     const __bf16* pairs0 = prm.pairs + (b * G + g) * (int64_t)nchunks * NPAIR * 512;
     const float dskip = prm.D ? prm.D[h] : 0.f;
@@ -293,18 +313,15 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     __bf16* ys = L.Ys + OW * YROWS * kXStr;
     auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
 
-    // Loads are unconditional with rows clamped into the chunk, so the compiler counts the
-    // loads in flight exactly; rows past a short chunk's end are never stored.
+    // Operands come from the prep kernel in lane order (one contiguous 1 KiB per load); rows
+    // past a short chunk's end are zeros there and are never stored here.
     uint4 cf[TBW][KN], sp[TBW][KS];
     auto load_c = [&](int c) {
-        const int last = chunk_len(c) - 1;
-        const void* base = Cg + ((b * Tn + (int64_t)c * Q) * G + g) * N;
+        const void* base = ct0 + (int64_t)c * NT * KN * 512;
 #pragma unroll
-        for (int r = 0; r < TBW; ++r) {
-            const uint32_t off = (uint32_t)min(16 * wave_tb(r, OW) + l16, last) * c_row + 16 * lg;
+        for (int r = 0; r < TBW; ++r)
 #pragma unroll
-            for (int k = 0; k < KN; ++k) cf[r][k] = ldg16(base, off + 64 * k);
-        }
+            for (int k = 0; k < KN; ++k) cf[r][k] = ldg16(base, 16 * lane + (wave_tb(r, OW) * KN + k) * 1024);
     };
     auto load_s = [&](int c) {
         const void* base = pairs0 + (int64_t)c * NPAIR * 512;
@@ -667,18 +684,19 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     __bf16* pairs = reinterpret_cast<__bf16*>(fl.scores);
     const int64_t nblk = fl.batch * fl.ngroups * fl.nchunks;
     __bf16* bt = pairs + nblk * NPAIR * 512;
-    float* la_t = reinterpret_cast<float*>(bt + nblk * (N / 16) * (Q / 32) * 512);
-    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, la_t, fl.seqlen, fl.nheads, fl.ngroups, fl.nchunks};
+    __bf16* ct = bt + nblk * (N / 16) * (Q / 32) * 512;
+    float* la_t = reinterpret_cast<float*>(ct + nblk * (Q / 16) * (N / 32) * 512);
+    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.seqlen, fl.nheads, fl.ngroups, fl.nchunks};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q>), walk_attr)) return -1;
     if (!record_event(fl, 0, stream)) return -1;
     const size_t plds = prep_lds<N, Q>();
-    hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)(nblk * kPrepParts)), dim3(kThreads), plds, stream, pp);
+    hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)nblk), dim3(kPrepThreads), plds, stream, pp);
     if (hipGetLastError() != hipSuccess) return -1;
 
     const int64_t units = fl.batch * fl.nheads;
     const int64_t per_xcd = (units + 7) / 8;
-    Walk2Params wp{fl.x, la_t, fl.Cm, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
+    Walk2Params wp{fl.x, la_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.nchunks, per_xcd};
     if (!record_event(fl, 1, stream)) return -1;
     const size_t wlds = WalkShape<N, Q>::lds_bytes;
@@ -692,15 +710,17 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
 }  // namespace
 
 bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups) {
-    // byte offsets inside one chunk (chunk rows of x, y, B, C) must fit in 32 bits
+    // byte offsets inside one chunk (chunk rows of x, y, B, C) must fit in 32 bits, and the prep
+    // kernel moves the log a of at most kPrepLa * 4 * kPrepThreads / chunk heads per group
     const bool offsets_fit = (double)chunk * (double)(nheads * P + ngroups * N) * 2.0 < 2147483648.0;
+    const bool heads_fit = ngroups > 0 && nheads / ngroups <= (int64_t)kPrepLa * 4 * kPrepThreads / chunk;
     return dtype == 1 && decay == 0 && P == kP && (N == 64 || N == 128) && (chunk == 64 || chunk == 128) &&
-           offsets_fit;
+           offsets_fit && heads_fit;
 }
 
 size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t nchunks, int N, int chunk) {
     const int64_t nblk = batch * ngroups * nchunks;
-    return (size_t)nblk * ((size_t)n_pairs(chunk / 16) * 1024 + (size_t)N * chunk * 2) +
+    return (size_t)nblk * ((size_t)n_pairs(chunk / 16) * 1024 + (size_t)N * chunk * 4) +
            (size_t)(batch * nheads * nchunks * chunk) * 4;
 }
 

@@ -52,6 +52,7 @@ struct PrepParams {
     const float* log_a;
     __bf16* pairs;  // score tile pairs, bf16, lane order
     __bf16* bt;     // B^T per chunk, tokens in MFMA K order
+    __bf16* ct;     // C^T per chunk, MFMA lane order
     float* la_t;    // log a head-major: [batch][nheads][nchunks * chunk], 0 past the end
     int64_t seqlen;
     int64_t nheads;
@@ -62,7 +63,7 @@ struct PrepParams {
 struct Walk2Params {
     const void* x;
     const float* la_t;  // log a head-major (PrepParams::la_t)
-    const void* Cm;
+    const __bf16* ct;   // C^T fragments (PrepParams::ct)
     const float* D;
     const __bf16* pairs;
     const __bf16* bt;

@@ -56,9 +56,9 @@ def n_pairs(nt):
 
 def test_workspace_bytes(lib):
     # bf16, scalar decay, head dim 64, N in {64,128}, chunk in {64,128}: per (batch, group,
-    # chunk) the bf16 score-tile pairs (1 KiB each) and the B^T operand (N * chunk * 2 bytes),
-    # plus log a head-major over whole chunks (4 bytes per (batch, head, padded token))
-    fast = lambda batch, heads, groups, nch, N, Q: (batch * groups * nch * (n_pairs(Q // 16) * 1024 + N * Q * 2)
+    # chunk) the bf16 score-tile pairs (1 KiB each) and the B^T and C^T operands (N * chunk * 2
+    # bytes each), plus log a head-major over whole chunks (4 bytes per (batch, head, padded token))
+    fast = lambda batch, heads, groups, nch, N, Q: (batch * groups * nch * (n_pairs(Q // 16) * 1024 + N * Q * 4)
                                                     + batch * heads * nch * Q * 4)
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 128) == fast(8, 24, 1, 16, 128, 128)
     # ragged: 2050 tokens -> 17 chunks
