@@ -489,13 +489,16 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     uint4 xs[XCH];
     uint4 bt[NBW][KS];
     // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
-    // quarter of the chunk; rows clamped into the chunk, masked when staged
-    auto load_lax = [&](int c) {
-        const int last = chunk_len(c) - 1;
+    // quarter of the chunk; rows clamped into the chunk, masked when staged.  Each is loaded
+    // a full chunk ahead of its use.
+    auto load_la = [&](int c) {
         const int64_t t0 = (int64_t)c * Q;
 #pragma unroll
         for (int j = 0; j < LA; ++j) la[j] = la0[t0 + lane * LA + j];
-        const void* xbase = xg + ((b * Tn + t0) * H + h) * kP;
+    };
+    auto load_x = [&](int c) {
+        const int last = chunk_len(c) - 1;
+        const void* xbase = xg + ((b * Tn + (int64_t)c * Q) * H + h) * kP;
 #pragma unroll
         for (int m = 0; m < XCH; ++m) {
             const int id = lane + kWave * m, row = min(QW * SW + id / 8, last), c16 = id % 8;
@@ -509,9 +512,8 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
             for (int k = 0; k < KS; ++k) bt[jn][k] = ldg16(base, 16 * lane + ((SW + 4 * jn) * KS + k) * 1024);
     };
-    // Decay factors of chunk c into factor buffer c & 1 and x of chunk c into the x
-    // buffers c & 1.  Returns exp(cum_last).
-    auto prepare = [&](int c) -> float {
+    // Decay factors of chunk c into factor buffer c & 1.  Returns exp(cum_last).
+    auto factors = [&](int c) -> float {
         const int len = chunk_len(c);
         const int buf = c & 1;
         float cum[LA], run = 0.f;
@@ -549,6 +551,12 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             const float s2 = __shfl(cum[0], (16 * lane) / LA, kWave);
             if (lane < NT) L.ea(buf)[lane] = fexp2(s2);
         }
+        return fexp2(last2);
+    };
+    // x of chunk c into the x buffers c & 1, raw and weighted by w (after factors(c)).
+    auto stage_x = [&](int c) {
+        const int len = chunk_len(c);
+        const int buf = c & 1;
         wave_lds_fence();  // this wave reads back the w it wrote
         __bf16* xsm = L.Xs + buf * Q * kXStr;
         __bf16* xwm = L.Xw + buf * Q * kXStr;
@@ -565,7 +573,6 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             for (int j = 0; j < 8; ++j) sv[j] = (__bf16)((float)rv[j] * w);
             *reinterpret_cast<bf16x8*>(xwm + row * kXStr + 8 * c16) = sv;
         }
-        return fexp2(last2);
     };
 
     f32x4 hs[NBW][PB];
@@ -591,16 +598,26 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             }
     };
 
-    load_lax(0);
+    load_la(0);
     load_b(0);
-    float el = prepare(0);
-    load_lax(min(1, nchunks - 1));
+    load_x(0);
+    float el = factors(0);
+    load_la(min(1, nchunks - 1));
+    stage_x(0);
+    load_x(min(1, nchunks - 1));
     write_state(L.Hs);
     lds_barrier();
 
+    // Per chunk: the next chunk's factors, the state MFMAs, the next chunk's x while they
+    // drain, then the state.  All of it runs unconditionally (past the last chunk the next
+    // chunk's buffers get zeros nobody reads), so the loop body has one path and the
+    // compiler's load counting stays exact.
     for (int c = 0; c < nchunks; ++c) {
         const int cn = min(c + 1, nchunks - 1);
         const __bf16* xwm = L.Xw + (c & 1) * Q * kXStr;
+        const float el_next = factors(c + 1);
+        load_la(min(c + 2, nchunks - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
         // H_k = exp(cum_last) H_{k-1} + B^T (w o X)
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
@@ -615,11 +632,10 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
                 for (int jn = 0; jn < NBW; ++jn) hs[jn][pb] = mfma_bf16(as_bf16x8(bt[jn][k]), xf, hs[jn][pb]);
             }
         load_b(cn);
-        // the next chunk's factors while the state MFMAs drain, then the state itself.  Run
-        // unconditionally (past the last chunk they fill the unused buffer with zeros), so the
-        // loop body has one path and the compiler's load counting stays exact.
-        el = prepare(c + 1);
-        load_lax(min(c + 2, nchunks - 1));
+        stage_x(c + 1);
+        load_x(min(c + 2, nchunks - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        el = el_next;
         write_state(L.Hs + ((c + 1) & 1) * kP * HS);
         lds_barrier();
     }
