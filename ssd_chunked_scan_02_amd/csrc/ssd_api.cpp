@@ -44,7 +44,7 @@ size_t workspace_needed(const ssd_dims* d, int chunk) {
     const int64_t nchunks = (d->seqlen + chunk - 1) / chunk;
     if (d->decay == SSD_DECAY_DIAG) return 0;
     if (ssd::fast_path_applies(d->dtype, d->decay, (int)d->dstate, (int)d->headdim, chunk, d->nheads, d->ngroups))
-        return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, nchunks, (int)d->dstate, chunk);
+        return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, d->seqlen, (int)d->dstate, chunk);
     return ssd::scores_bytes(d->batch, d->ngroups, nchunks, chunk);
 }
 

@@ -205,6 +205,9 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepParams prm) {
 // offset (the host only takes this path when every offset inside a chunk fits).
 constexpr int kWalkWaves = 8;
 constexpr int kWalkThreads = kWalkWaves * kWave;
+// segmented walks: about this many workgroups at once, segments of at least this many chunks
+constexpr int64_t kSegTarget = 256;
+constexpr int64_t kMinSegChunks = 4;
 
 // 16-token block handled by output wave `ow` in its r-th round (snake order balances the
 // causal work across the four output waves).
@@ -294,9 +297,31 @@ struct WalkLds {
     __device__ float* ea(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q; }
 };
 
+// The piece of work of one workgroup: a (batch, head) unit and the chunks [c0, c1) of one
+// segment of its sequence (the whole sequence unless the walk is split into segments).
+struct WalkSpan {
+    int64_t unit, b, h, g;
+    int seg, c0, c1;
+};
+
+__device__ __forceinline__ WalkSpan walk_span(const Walk2Params& prm, int64_t work) {
+    WalkSpan sp;
+    const int64_t units = prm.batch * prm.nheads;
+    sp.seg = (int)(work / units);
+    sp.unit = work % units;
+    sp.b = sp.unit / prm.nheads;
+    sp.h = sp.unit % prm.nheads;
+    sp.g = sp.h / (prm.nheads / prm.ngroups);
+    sp.c0 = sp.seg * prm.seg_chunks;
+    sp.c1 = min(sp.c0 + prm.seg_chunks, prm.nchunks);
+    return sp;
+}
+
 template <int N, int Q, int OW>
-__device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const WalkLds<N, Q>& L, int64_t b,
-                                                 int64_t h, int64_t g, int lane) {
+__device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
+                                                 int lane) {
+    const int64_t b = span.b, h = span.h, g = span.g;
+    const int c0 = span.c0, c1 = span.c1;
     using WS = WalkShape<N, Q>;
     constexpr int NT = WS::NT, TBW = WS::TBW, KS = WS::KS, KN = WS::KN, NPAIR = WS::NPAIR;
     constexpr int PB = WS::PB, HS = WS::HS;
@@ -337,8 +362,8 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
 #pragma unroll
     for (int j = 0; j < 4; ++j) causal[j] = 4 * lg + j <= l16;
 
-    load_c(0);
-    load_s(0);
+    load_c(c0);
+    load_s(c0);
     {
         // As many stores as one chunk's outputs, all dropped (empty resource): the loop is then
         // entered with the same memory operations in flight as each later chunk, and the
@@ -349,9 +374,9 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     }
     lds_barrier();
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = c0; c < c1; ++c) {
         const int len = chunk_len(c);
-        const int cn = min(c + 1, nchunks - 1);
+        const int cn = min(c + 1, c1 - 1);
         const int buf = c & 1;
         const __bf16* xsm = L.Xs + buf * Q * kXStr;
         const __bf16* hcur = L.Hs + buf * kP * HS;
@@ -469,9 +494,14 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     }
 }
 
-template <int N, int Q, int SW>
-__device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, int64_t b,
-                                                int64_t h, int64_t g, int64_t unit, int lane) {
+// FULL: the state waves of the walk (they also stage everything the output waves read).
+// !FULL: the state-only pass of a segmented walk: H over the segment from a zero state, written
+// to seg_state with the segment's total log2-decay in seg_decay; only w o x and w are staged.
+template <int N, int Q, int SW, bool FULL>
+__device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
+                                                int lane) {
+    const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
+    const int c0 = span.c0, c1 = span.c1;
     using WS = WalkShape<N, Q>;
     constexpr int NT = WS::NT, KS = WS::KS, NBW = WS::NBW, LA = WS::LA, QW = WS::QW, XCH = WS::XCH;
     constexpr int PB = WS::PB, HS = WS::HS;
@@ -488,6 +518,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     float la[LA];
     uint4 xs[XCH];
     uint4 bt[NBW][KS];
+    float lsum2 = 0.f, seg2 = 0.f;  // log2 decay of the last factored chunk, of the segment so far
     // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
     // quarter of the chunk; rows clamped into the chunk, masked when staged.  Each is loaded
     // a full chunk ahead of its use.
@@ -531,11 +562,15 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
             for (int j = 0; j < LA; ++j) {
                 const int t = lane * LA + j;
-                L.cum2(buf)[t] = cum[j];
-                L.f(buf)[t] = fexp2(cum[j] - blk2);
+                if (FULL) {
+                    L.cum2(buf)[t] = cum[j];
+                    L.f(buf)[t] = fexp2(cum[j] - blk2);
+                }
                 L.w(buf)[t] = fexp2(last2 - cum[j]);
             }
         }
+        lsum2 = last2;
+        if (!FULL) return fexp2(last2);
         // rows SW, SW + 4, ... of U
 #pragma unroll
         for (int tb = SW; tb < NT; tb += 4) {
@@ -565,7 +600,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         for (int m = 0; m < XCH; ++m) {
             const int id = lane + kWave * m, row = QW * SW + id / 8, c16 = id % 8;
             const uint4 raw = row < len ? xs[m] : zero;
-            st16(xsm + row * kXStr + 8 * c16, raw);
+            if (FULL) st16(xsm + row * kXStr + 8 * c16, raw);
             const float w = wrow[row];
             const bf16x8 rv = as_bf16x8(raw);
             bf16x8 sv;
@@ -581,14 +616,18 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb) {
             hs[jn][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (prm.init) {
+            const float* init = !FULL ? nullptr
+                                : prm.nseg > 1 ? prm.seg_init + (span.seg * prm.batch * prm.nheads + unit) * N * kP
+                                               : (prm.init ? prm.init + unit * N * kP : nullptr);
+            if (init) {
                 const int n = 16 * (SW + 4 * jn) + 4 * lg;
-                const float* src = prm.init + (unit * N + n) * kP + 16 * pb + l16;
+                const float* src = init + n * kP + 16 * pb + l16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) hs[jn][pb][i] = src[i * kP];
             }
         }
     auto write_state = [&](__bf16* hsm) {
+        if (!FULL) return;
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
 #pragma unroll
@@ -598,25 +637,27 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             }
     };
 
-    load_la(0);
-    load_b(0);
-    load_x(0);
-    float el = factors(0);
-    load_la(min(1, nchunks - 1));
-    stage_x(0);
-    load_x(min(1, nchunks - 1));
-    write_state(L.Hs);
+    load_la(c0);
+    load_b(c0);
+    load_x(c0);
+    float el = factors(c0);
+    seg2 += lsum2;
+    load_la(min(c0 + 1, c1 - 1));
+    stage_x(c0);
+    load_x(min(c0 + 1, c1 - 1));
+    write_state(L.Hs + (c0 & 1) * kP * HS);
     lds_barrier();
 
     // Per chunk: the next chunk's factors, the state MFMAs, the next chunk's x while they
     // drain, then the state.  All of it runs unconditionally (past the last chunk the next
     // chunk's buffers get zeros nobody reads), so the loop body has one path and the
     // compiler's load counting stays exact.
-    for (int c = 0; c < nchunks; ++c) {
-        const int cn = min(c + 1, nchunks - 1);
+    for (int c = c0; c < c1; ++c) {
+        const int cn = min(c + 1, c1 - 1);
         const __bf16* xwm = L.Xw + (c & 1) * Q * kXStr;
         const float el_next = factors(c + 1);
-        load_la(min(c + 2, nchunks - 1));
+        if (c + 1 < c1) seg2 += lsum2;
+        load_la(min(c + 2, c1 - 1));
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
         // H_k = exp(cum_last) H_{k-1} + B^T (w o X)
 #pragma unroll
@@ -633,20 +674,23 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             }
         load_b(cn);
         stage_x(c + 1);
-        load_x(min(c + 2, nchunks - 1));
+        load_x(min(c + 2, c1 - 1));
         __builtin_amdgcn_sched_barrier(0);
         el = el_next;
         write_state(L.Hs + ((c + 1) & 1) * kP * HS);
         lds_barrier();
     }
 
-    if (prm.final_state) {
+    float* fin = !FULL ? prm.seg_state + (span.seg * prm.batch * prm.nheads + unit) * N * kP
+                       : (c1 == prm.nchunks && prm.final_state) ? prm.final_state + unit * N * kP : nullptr;
+    if (!FULL && lane == 0) prm.seg_decay[span.seg * prm.batch * prm.nheads + unit] = seg2;
+    if (fin) {
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) {
                 const int n = 16 * (SW + 4 * jn) + 4 * lg;
-                float* dst = prm.final_state + (unit * N + n) * kP + 16 * pb + l16;
+                float* dst = fin + n * kP + 16 * pb + l16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[i * kP] = hs[jn][pb][i];
             }
@@ -655,23 +699,66 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 
 template <int N, int Q>
 __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm) {
-    const int64_t H = prm.nheads;
-    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
-    if (unit < 0) return;
-    const int64_t b = unit / H, h = unit % H, g = h / (H / prm.ngroups);
+    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
+    if (work < 0) return;
+    const WalkSpan span = walk_span(prm, work);
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     extern __shared__ __align__(16) unsigned char smem[];
     const WalkLds<N, Q> L(smem);
     switch (wave) {
-        case 0: walk_output_role<N, Q, 0>(prm, L, b, h, g, lane); break;
-        case 1: walk_output_role<N, Q, 1>(prm, L, b, h, g, lane); break;
-        case 2: walk_output_role<N, Q, 2>(prm, L, b, h, g, lane); break;
-        case 3: walk_output_role<N, Q, 3>(prm, L, b, h, g, lane); break;
-        case 4: walk_state_role<N, Q, 0>(prm, L, b, h, g, unit, lane); break;
-        case 5: walk_state_role<N, Q, 1>(prm, L, b, h, g, unit, lane); break;
-        case 6: walk_state_role<N, Q, 2>(prm, L, b, h, g, unit, lane); break;
-        default: walk_state_role<N, Q, 3>(prm, L, b, h, g, unit, lane); break;
+        case 0: walk_output_role<N, Q, 0>(prm, L, span, lane); break;
+        case 1: walk_output_role<N, Q, 1>(prm, L, span, lane); break;
+        case 2: walk_output_role<N, Q, 2>(prm, L, span, lane); break;
+        case 3: walk_output_role<N, Q, 3>(prm, L, span, lane); break;
+        case 4: walk_state_role<N, Q, 0, true>(prm, L, span, lane); break;
+        case 5: walk_state_role<N, Q, 1, true>(prm, L, span, lane); break;
+        case 6: walk_state_role<N, Q, 2, true>(prm, L, span, lane); break;
+        default: walk_state_role<N, Q, 3, true>(prm, L, span, lane); break;
+    }
+}
+
+// State-only pass of a segmented walk: 4 waves per (segment, batch, head).  Its LDS holds only
+// what those waves use (the factor buffers and w o x); the other views of WalkLds point at the
+// same memory and are never touched when FULL is false.
+template <int N, int Q>
+struct StateLds {
+    static constexpr size_t bytes = (size_t)2 * Q * kXStr * 2 + (size_t)2 * WalkShape<N, Q>::FSZ * 4;
+};
+
+template <int N, int Q>
+__global__ void __launch_bounds__(kThreads) walk_state_kernel(Walk2Params prm) {
+    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
+    if (work < 0) return;
+    const WalkSpan span = walk_span(prm, work);
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    extern __shared__ __align__(16) unsigned char smem[];
+    WalkLds<N, Q> L(smem);
+    L.Xw = reinterpret_cast<__bf16*>(smem);
+    L.Xs = L.Xw;
+    L.Hs = L.Xw;
+    L.Ys = L.Xw;
+    L.Fs = reinterpret_cast<float*>(L.Xw + 2 * Q * kXStr);
+    switch (wave) {
+        case 0: walk_state_role<N, Q, 0, false>(prm, L, span, lane); break;
+        case 1: walk_state_role<N, Q, 1, false>(prm, L, span, lane); break;
+        case 2: walk_state_role<N, Q, 2, false>(prm, L, span, lane); break;
+        default: walk_state_role<N, Q, 3, false>(prm, L, span, lane); break;
+    }
+}
+
+// Chains the segments' local states: seg_init[s] = exp2(seg_decay[s-1]) seg_init[s-1] +
+// seg_state[s-1], seg_init[0] = the initial state (or 0).  One thread per state element.
+__global__ void __launch_bounds__(kThreads) seg_prefix_kernel(Walk2Params prm, int64_t elems_per_unit) {
+    const int64_t units = prm.batch * prm.nheads;
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= units * elems_per_unit) return;
+    const int64_t unit = e / elems_per_unit;
+    float hcur = prm.init ? prm.init[e] : 0.f;
+    for (int s = 0; s < prm.nseg; ++s) {
+        prm.seg_init[s * units * elems_per_unit + e] = hcur;
+        hcur = exp2f(prm.seg_decay[s * units + unit]) * hcur + prm.seg_state[s * units * elems_per_unit + e];
     }
 }
 
@@ -692,56 +779,109 @@ bool allow_full_lds(const void* kernel, bool* done) {
     return true;
 }
 
+// Workspace layout of the fast path (byte offsets), for Q-token chunks.
+struct FastLayout {
+    int64_t nchunks, nblk, units;
+    int nseg, seg_chunks;
+    size_t pairs, bt, ct, la_t, seg_state, seg_decay, seg_init, total;
+};
+
+FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int Q) {
+    FastLayout l;
+    l.nchunks = (seqlen + Q - 1) / Q;
+    l.nblk = batch * ngroups * l.nchunks;
+    l.units = batch * nheads;
+    // Few (batch, head) units on a long sequence: split each sequence into segments of at
+    // least kMinSegChunks chunks so that about kSegTarget workgroups walk at once.
+    l.nseg = 1;
+    if (l.units > 0 && l.units * 2 <= kSegTarget && l.nchunks >= 2 * kMinSegChunks)
+        l.nseg = (int)min(kSegTarget / l.units, l.nchunks / kMinSegChunks);
+    l.seg_chunks = (int)((l.nchunks + l.nseg - 1) / l.nseg);
+    l.nseg = (int)((l.nchunks + l.seg_chunks - 1) / l.seg_chunks);
+    size_t off = 0;
+    l.pairs = off; off += (size_t)l.nblk * n_pairs(Q / 16) * 1024;
+    l.bt = off; off += (size_t)l.nblk * N * Q * 2;
+    l.ct = off; off += (size_t)l.nblk * N * Q * 2;
+    l.la_t = off; off += (size_t)l.units * l.nchunks * Q * 4;
+    l.seg_state = l.seg_decay = l.seg_init = off;
+    if (l.nseg > 1) {
+        l.seg_state = off; off += (size_t)l.nseg * l.units * N * kP * 4;
+        l.seg_init = off; off += (size_t)l.nseg * l.units * N * kP * 4;
+        l.seg_decay = off; off += ((size_t)l.nseg * l.units * 4 + 255) / 256 * 256;
+    }
+    l.total = off;
+    return l;
+}
+
 template <int N, int Q>
 int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
-    constexpr int NPAIR = n_pairs(Q / 16);
     static_assert(WalkShape<N, Q>::lds_bytes <= kMaxLds, "walk LDS budget");
     static bool prep_attr[64] = {}, walk_attr[64] = {};
-    __bf16* pairs = reinterpret_cast<__bf16*>(fl.scores);
-    const int64_t nblk = fl.batch * fl.ngroups * fl.nchunks;
-    __bf16* bt = pairs + nblk * NPAIR * 512;
-    __bf16* ct = bt + nblk * (N / 16) * (Q / 32) * 512;
-    float* la_t = reinterpret_cast<float*>(ct + nblk * (Q / 16) * (N / 32) * 512);
-    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.seqlen, fl.nheads, fl.ngroups, fl.nchunks};
+    const FastLayout lay = fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q);
+    char* ws = reinterpret_cast<char*>(fl.scores);
+    __bf16* pairs = reinterpret_cast<__bf16*>(ws + lay.pairs);
+    __bf16* bt = reinterpret_cast<__bf16*>(ws + lay.bt);
+    __bf16* ct = reinterpret_cast<__bf16*>(ws + lay.ct);
+    float* la_t = reinterpret_cast<float*>(ws + lay.la_t);
+    const int nch = (int)lay.nchunks;
+    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.seqlen, fl.nheads, fl.ngroups, nch};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q>), walk_attr)) return -1;
-    if (!record_event(fl, 0, stream)) return -1;
-    const size_t plds = prep_lds<N, Q>();
-    hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)nblk), dim3(kPrepThreads), plds, stream, pp);
+    int ev = 0;
+    if (!record_event(fl, ev++, stream)) return -1;
+    // (sizes computed first: template commas cannot sit inside the launch macro)
+    const size_t plds = prep_lds<N, Q>(), slds = StateLds<N, Q>::bytes, wlds = WalkShape<N, Q>::lds_bytes;
+    hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)lay.nblk), dim3(kPrepThreads), plds, stream, pp);
     if (hipGetLastError() != hipSuccess) return -1;
 
-    const int64_t units = fl.batch * fl.nheads;
-    const int64_t per_xcd = (units + 7) / 8;
+    const int64_t work = lay.nseg * lay.units;
+    const int64_t per_xcd = (work + 7) / 8;
     Walk2Params wp{fl.x, la_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
-                   fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.nchunks, per_xcd};
-    if (!record_event(fl, 1, stream)) return -1;
-    const size_t wlds = WalkShape<N, Q>::lds_bytes;
+                   fl.batch, fl.seqlen, fl.nheads, fl.ngroups, nch, per_xcd,
+                   lay.seg_chunks, lay.nseg,
+                   reinterpret_cast<float*>(ws + lay.seg_init), reinterpret_cast<float*>(ws + lay.seg_state),
+                   reinterpret_cast<float*>(ws + lay.seg_decay)};
+    if (lay.nseg > 1) {
+        if (!record_event(fl, ev++, stream)) return -1;
+        hipLaunchKernelGGL((walk_state_kernel<N, Q>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), slds, stream,
+                           wp);
+        if (hipGetLastError() != hipSuccess) return -1;
+        if (!record_event(fl, ev++, stream)) return -1;
+        const int64_t elems = (int64_t)N * kP;
+        hipLaunchKernelGGL(seg_prefix_kernel, dim3((unsigned)((lay.units * elems + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, wp, elems);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    if (!record_event(fl, ev++, stream)) return -1;
     hipLaunchKernelGGL((walk_fast_kernel<N, Q>), dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream, wp);
     if (hipGetLastError() != hipSuccess) return -1;
-    if (!record_event(fl, 2, stream)) return -1;
-    if (fl.n_launches) *fl.n_launches = 2;
+    if (!record_event(fl, ev++, stream)) return -1;
+    if (fl.n_launches) *fl.n_launches = ev - 1;
     return 0;
 }
 
 }  // namespace
 
+// Chunks of 256 tokens run as two 128-token chunks: the same operator, evaluated with the
+// state carried at every 128th token instead of every 256th.
+int fast_chunk(int chunk) { return chunk > 128 ? 128 : chunk; }
+
 bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups) {
     // byte offsets inside one chunk (chunk rows of x, y, B, C) must fit in 32 bits, and the prep
     // kernel moves the log a of at most kPrepLa * 4 * kPrepThreads / chunk heads per group
-    const bool offsets_fit = (double)chunk * (double)(nheads * P + ngroups * N) * 2.0 < 2147483648.0;
-    const bool heads_fit = ngroups > 0 && nheads / ngroups <= (int64_t)kPrepLa * 4 * kPrepThreads / chunk;
-    return dtype == 1 && decay == 0 && P == kP && (N == 64 || N == 128) && (chunk == 64 || chunk == 128) &&
-           offsets_fit && heads_fit;
+    const int q = fast_chunk(chunk);
+    const bool offsets_fit = (double)q * (double)(nheads * P + ngroups * N) * 2.0 < 2147483648.0;
+    const bool heads_fit = ngroups > 0 && nheads / ngroups <= (int64_t)kPrepLa * 4 * kPrepThreads / q;
+    return dtype == 1 && decay == 0 && P == kP && (N == 64 || N == 128) &&
+           (chunk == 64 || chunk == 128 || chunk == 256) && offsets_fit && heads_fit;
 }
 
-size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t nchunks, int N, int chunk) {
-    const int64_t nblk = batch * ngroups * nchunks;
-    return (size_t)nblk * ((size_t)n_pairs(chunk / 16) * 1024 + (size_t)N * chunk * 4) +
-           (size_t)(batch * nheads * nchunks * chunk) * 4;
+size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk) {
+    return fast_layout(batch, nheads, ngroups, seqlen, N, fast_chunk(chunk)).total;
 }
 
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream) {
-    const int N = (int)fl.dstate, Q = fl.chunk;
+    const int N = (int)fl.dstate, Q = fast_chunk(fl.chunk);
     if (N == 64 && Q == 64) return launch_fast_t<64, 64>(fl, stream);
     if (N == 64 && Q == 128) return launch_fast_t<64, 128>(fl, stream);
     if (N == 128 && Q == 64) return launch_fast_t<128, 64>(fl, stream);

@@ -73,6 +73,12 @@ struct Walk2Params {
     int64_t batch, seqlen, nheads, ngroups;
     int nchunks;
     int64_t per_xcd;
+    // segmented walks (nseg > 1): chunks per segment, and per (segment, unit) the state at the
+    // segment start, the segment's local final state from a zero start and its log2 decay
+    int seg_chunks, nseg;
+    float* seg_init;
+    float* seg_state;
+    float* seg_decay;
 };
 
 // Everything one forward call needs, already validated.
@@ -101,7 +107,7 @@ bool shape_supported(int dtype, int N, int P);
 bool record_event(const ForwardLaunch& fl, int k, hipStream_t stream);
 // The pipelined bf16 path (ssd_fast.hip) and its workspace.
 bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups);
-size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t nchunks, int N, int chunk);
+size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk);
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream);
 // The diagonal-decay walk (ssd_diag.hip): LDS bytes (0 = unsupported) and launch.
 size_t diag_lds_bytes(int dtype, int N, int P, int chunk);

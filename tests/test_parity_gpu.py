@@ -40,6 +40,21 @@ def test_small_workloads(name, over):
     _run(cfg, 7, "small " + name)
 
 
+SEGMENTED = [
+    # few (batch, head) units on a long sequence: the walk runs in segments (state-only pass,
+    # prefix over segment states, full pass from each segment's start state)
+    dict(batch=1, seqlen=3000, nheads=2, chunk=128, init=True),
+    dict(batch=2, seqlen=2100, nheads=4, ngroups=2, chunk=64, init=True, skip=False),
+    dict(batch=1, seqlen=4100, nheads=1, chunk=256, dstate=64),
+]
+
+
+@pytest.mark.parametrize("over", SEGMENTED, ids=["seg-%d" % i for i in range(len(SEGMENTED))])
+def test_segmented_walk(over):
+    cfg = ssd_inputs.config("mamba2_layer", **over)
+    _run(cfg, 23, "segmented")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
 def test_chunk_sizes(dtype, chunk):
