@@ -74,7 +74,8 @@ struct DiagLayout {
     static constexpr int KB = Traits<T>::kKBlock;
     static constexpr int PADE = Traits<T>::kPad;
     int Q, QK, QP, NP, NT;
-    size_t xt, bt, ht, cc, cf, bu, cum, beta, el, sl, total;
+    bool raw;
+    size_t xt, bt, ht, cc, cf, bu, cum, beta, el, sl, braw, craw, part, total;
     __host__ __device__ DiagLayout(int q) {
         Q = q;
         QK = (q + KB - 1) / KB * KB;
@@ -93,6 +94,15 @@ struct DiagLayout {
         beta = take((size_t)(NT * (NT - 1) / 2 + 1) * N * sizeof(float));
         el = take((size_t)N * sizeof(float));
         sl = take((size_t)(NT * (NT + 1) / 2) * 256 * sizeof(float));  // masked score tiles
+        part = take((size_t)(kThreads / N + 1) * N * sizeof(CT));        // scan partial sums
+        // raw B and C rows for the exact diagonal tiles when they fit in LDS next to the rest
+        // (otherwise those tiles read them from global memory)
+        braw = craw = 0;
+        raw = o + 2 * (((size_t)QK * NP * sizeof(T) + 15) / 16 * 16) <= kMaxLds;
+        if (raw) {
+            braw = take((size_t)QK * NP * sizeof(T));   // B    [QK][NP]
+            craw = take((size_t)QK * NP * sizeof(T));   // C    [QK][NP]
+        }
         total = o;
     }
 };
@@ -127,6 +137,10 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
     T* Cf = reinterpret_cast<T*>(smem + lay.cf);
     T* Bu = reinterpret_cast<T*>(smem + lay.bu);
     CT* cum = reinterpret_cast<CT*>(smem + lay.cum);
+    CT* part = reinterpret_cast<CT*>(smem + lay.part);
+    T* Braw = reinterpret_cast<T*>(smem + lay.braw);
+    T* Craw = reinterpret_cast<T*>(smem + lay.craw);
+    const bool kRawLds = lay.raw;
     float* beta = reinterpret_cast<float*>(smem + lay.beta);
     float* el = reinterpret_cast<float*>(smem + lay.el);
     float* Sl = reinterpret_cast<float*>(smem + lay.sl);
@@ -168,18 +182,28 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
         const int len = (int)min((int64_t)Q, Tn - t0);
         __syncthreads();  // previous chunk done with every LDS buffer
 
-        // ---- 1. log a into LDS, then running sums down each state column (past the end: 0)
+        // ---- 1. log a into LDS, then running sums down each state column (past the end: 0):
+        //         kThreads / N groups of consecutive tokens per column, each summed by one
+        //         thread, then every group offset by the totals of the groups before it
         for (int i = tid; i < QK * N; i += kThreads) {
             const int t = i / N, n = i % N;
             cum[i] = t < len ? (CT)prm.log_a[((b * Tn + t0 + t) * H + h) * N + n] : (CT)0;
         }
         __syncthreads();
-        for (int n = tid; n < N; n += kThreads) {
+        {
+            constexpr int NG = kThreads / N;  // token groups per column
+            const int n = tid % N, grp = tid / N, per = (QK + NG - 1) / NG;
+            const int ta = min(QK, grp * per), tz = min(QK, ta + per);
             CT run = 0;
-            for (int t = 0; t < QK; ++t) {
+            for (int t = ta; t < tz; ++t) {
                 run += cum[t * N + n];
                 cum[t * N + n] = run;
             }
+            part[grp * N + n] = run;
+            __syncthreads();
+            CT off = 0;
+            for (int q = 0; q < grp; ++q) off += part[q * N + n];
+            for (int t = ta; t < tz; ++t) cum[t * N + n] += off;
         }
         __syncthreads();
 
@@ -210,6 +234,10 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
             st16(Cc + t * NP + cc * VE, scale_vec(cv, fe, T()));
             st16(Cf + t * NP + cc * VE, scale_vec(cv, ff_, T()));
             st16(Bu + t * NP + cc * VE, scale_vec(bv, fu, T()));
+            if (kRawLds) {
+                st16(Craw + t * NP + cc * VE, cv);
+                st16(Braw + t * NP + cc * VE, bv);
+            }
         }
         // x^T and (w o B)^T, four tokens per thread and 16-byte global loads
         for (int item = tid; item < (QK / 4) * (P / VE); item += kThreads) {
@@ -248,11 +276,19 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
 
         // ---- 3. masked score tiles S^T[s][t] (s block sb <= t block tb), fp32 in LDS,
         //         accumulator order: lane l holds rows 4(l/16)+i, column l%16
+        // (the costly diagonal tiles first, one per wave, then the others round-robin)
         const int ntiles = nt * (nt + 1) / 2;
-        for (int idx = wave; idx < ntiles; idx += kWaves) {
-            int tb = 0;
-            while (tile_index(tb + 1, 0) <= idx) ++tb;
-            const int sb = idx - tile_index(tb, 0);
+        for (int ord = wave; ord < ntiles; ord += kWaves) {
+            int tb, sb;
+            if (ord < nt) {
+                tb = sb = ord;
+            } else {
+                const int o = ord - nt;  // o-th off-diagonal tile in row order
+                tb = 1;
+                while (offdiag_index(tb + 1, 0) <= o) ++tb;
+                sb = o - offdiag_index(tb, 0);
+            }
+            const int idx = tile_index(tb, sb);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (sb < tb) {
                 const float* bet = beta + offdiag_index(tb, sb) * N;
@@ -268,14 +304,19 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
                 const int t = 16 * tb + l16;
                 // exact: S^T[s][t] = sum_n B_sn C_tn exp(cum_tn - cum_sn), s <= t; raw B and C
                 // rows come from global memory (the chunk's lines are still in cache)
+                // (raw rows from LDS for 2-byte types; rows past the end are zeros there)
                 for (int n = 0; n < N; ++n) {
                     const CT ct = cum[t * N + n];
-                    const float craw = (float)Cg[((b * Tn + t0 + min(t, len - 1)) * G + g) * N + n] * (t < len ? 1.f : 0.f);
+                    const float craw =
+                        kRawLds ? (float)Craw[t * NP + n]
+                                : (float)Cg[((b * Tn + t0 + min(t, len - 1)) * G + g) * N + n] * (t < len ? 1.f : 0.f);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int s = 16 * sb + 4 * lg + i;
                         const bool causal = s <= t && s < len;
-                        const float braw = causal ? (float)Bg[((b * Tn + t0 + s) * G + g) * N + n] : 0.f;
+                        const float braw = !causal ? 0.f
+                                           : kRawLds ? (float)Braw[s * NP + n]
+                                                     : (float)Bg[((b * Tn + t0 + s) * G + g) * N + n];
                         const CT d = causal ? (CT)(ct - cum[s * N + n]) : (CT)0;
                         acc[i] += craw * braw * dexp(d);
                     }
@@ -374,6 +415,355 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// walk_diag_pipe_kernel: the same walk for bf16 inputs and 64-token chunks, pipelined: the
+// next chunk's log a, B, C and x rows are loaded into registers while the current chunk is
+// computed and staged into LDS once it is done, so no phase waits on global memory; every
+// operand (raw B and C included) is read from LDS.  The running sums are kept in rows padded
+// to N + 4 floats so that 16 rows read at once fall on distinct banks.
+constexpr int kDiagQ = 64;
+
+template <int N, int P>
+struct DiagPipeLayout {
+    static constexpr int Q = kDiagQ, NT = Q / 16, QP = Q + 8, NP = N + 8, CS = N + 4;
+    static constexpr int NOFF = NT * (NT - 1) / 2;
+    // offsets in bytes
+    static constexpr size_t xt = 0;                                   // x^T          [P][QP] bf16
+    static constexpr size_t bt = xt + (size_t)P * QP * 2;            // (w o B)^T    [N][QP] bf16
+    static constexpr size_t ht = bt + (size_t)N * QP * 2;            // H^T          [P][NP] bf16
+    static constexpr size_t cc = ht + (size_t)P * NP * 2;            // C o exp(cum) [Q][NP] bf16
+    static constexpr size_t cf = cc + (size_t)Q * NP * 2;            // C o f        [Q][NP] bf16
+    static constexpr size_t bu = cf + (size_t)Q * NP * 2;            // B o u        [Q][NP] bf16
+    static constexpr size_t braw = bu + (size_t)Q * NP * 2;          // B            [Q][NP] bf16
+    static constexpr size_t craw = braw + (size_t)Q * NP * 2;        // C            [Q][NP] bf16
+    static constexpr size_t cum = craw + (size_t)Q * NP * 2;         // running sums [Q][CS] f32
+    static constexpr size_t part = cum + (size_t)Q * CS * 4;         // scan partials [kThreads/N][N]
+    static constexpr size_t beta = part + (size_t)kThreads * 4;      // [NOFF][N]
+    static constexpr size_t el = beta + (size_t)(NOFF + 1) * N * 4;  // [N]
+    static constexpr size_t sl = el + (size_t)N * 4;                  // score tiles [NT(NT+1)/2][256]
+    static constexpr size_t total = sl + (size_t)(NT * (NT + 1) / 2) * 256 * 4;
+};
+
+template <int N, int P>
+__global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm) {
+    using L = DiagPipeLayout<N, P>;
+    constexpr int Q = L::Q, NT = L::NT, QP = L::QP, NP = L::NP, CS = L::CS;
+    constexpr int PB = P / 16, NB = N / 16, NTILE = NB * PB, TPW = (NTILE + kWaves - 1) / kWaves;
+    constexpr int LAI = Q * N / 4 / kThreads;   // 16-byte pieces of log a per thread
+    constexpr int BCI = Q * N / 8 / kThreads;   // 16-byte pieces of B (and of C) per thread
+    constexpr int XI = Q * P / 8 / kThreads;    // 16-byte pieces of x per thread
+    static_assert(LAI >= 1 && BCI >= 1 && XI >= 1, "diag pipe shape");
+
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int l16 = lane % 16, lg = lane / 16;
+    const int nchunks = prm.nchunks;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    __bf16* Xt = reinterpret_cast<__bf16*>(smem + L::xt);
+    __bf16* Bt = reinterpret_cast<__bf16*>(smem + L::bt);
+    __bf16* Ht = reinterpret_cast<__bf16*>(smem + L::ht);
+    __bf16* Cc = reinterpret_cast<__bf16*>(smem + L::cc);
+    __bf16* Cf = reinterpret_cast<__bf16*>(smem + L::cf);
+    __bf16* Bu = reinterpret_cast<__bf16*>(smem + L::bu);
+    __bf16* Braw = reinterpret_cast<__bf16*>(smem + L::braw);
+    __bf16* Craw = reinterpret_cast<__bf16*>(smem + L::craw);
+    float* cum = reinterpret_cast<float*>(smem + L::cum);
+    float* part = reinterpret_cast<float*>(smem + L::part);
+    float* beta = reinterpret_cast<float*>(smem + L::beta);
+    float* el = reinterpret_cast<float*>(smem + L::el);
+    float* Sl = reinterpret_cast<float*>(smem + L::sl);
+
+    const float* lag = prm.log_a;
+    const __bf16* xg = static_cast<const __bf16*>(prm.x);
+    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm);
+    const __bf16* Cg = static_cast<const __bf16*>(prm.Cm);
+    __bf16* yg = static_cast<__bf16*>(prm.y);
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    const float dskip = prm.D ? prm.D[h] : 0.f;
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
+
+    // ---- prefetch registers: one chunk of log a, B, C and x rows (rows clamped into the
+    //      sequence; staged as zeros past its end)
+    uint4 rla[LAI], rb[BCI], rc[BCI], rx[XI];
+    auto load_chunk = [&](int c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int last = chunk_len(c) - 1;
+#pragma unroll
+        for (int m = 0; m < LAI; ++m) {
+            const int id = tid + kThreads * m, t = min(id / (N / 4), last), c4 = id % (N / 4);
+            rla[m] = ld16(lag + ((b * Tn + t0 + t) * H + h) * N + 4 * c4);
+        }
+#pragma unroll
+        for (int m = 0; m < BCI; ++m) {
+            const int id = tid + kThreads * m, t = min(id / (N / 8), last), c8 = id % (N / 8);
+            const int64_t off = ((b * Tn + t0 + t) * G + g) * N + 8 * c8;
+            rb[m] = ld16(Bg + off);
+            rc[m] = ld16(Cg + off);
+        }
+#pragma unroll
+        for (int m = 0; m < XI; ++m) {
+            const int id = tid + kThreads * m, t = min(id / (P / 8), last), c8 = id % (P / 8);
+            rx[m] = ld16(xg + ((b * Tn + t0 + t) * H + h) * P + 8 * c8);
+        }
+    };
+    auto stage_chunk = [&](int c) {
+        const int len = chunk_len(c);
+#pragma unroll
+        for (int m = 0; m < LAI; ++m) {
+            const int id = tid + kThreads * m, t = id / (N / 4), c4 = id % (N / 4);
+            st16(cum + t * CS + 4 * c4, t < len ? rla[m] : zero);
+        }
+#pragma unroll
+        for (int m = 0; m < BCI; ++m) {
+            const int id = tid + kThreads * m, t = id / (N / 8), c8 = id % (N / 8);
+            st16(Braw + t * NP + 8 * c8, t < len ? rb[m] : zero);
+            st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
+        }
+#pragma unroll
+        for (int m = 0; m < XI; ++m) {
+            const int id = tid + kThreads * m, t = id / (P / 8), c8 = id % (P / 8);
+            const bf16x8 v = as_bf16x8(t < len ? rx[m] : zero);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) Xt[(8 * c8 + j) * QP + t] = v[j];
+        }
+    };
+
+    // ---- state registers (tiles (nb, pb) dealt round-robin to the waves)
+    f32x4 hs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kWaves * j;
+        if (tile < NTILE && prm.init) {
+            const int nb = tile / PB, pb = tile % PB;
+            const float* src = prm.init + (unit * N + 16 * nb + 4 * lg) * P + 16 * pb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hs[j][i] = src[i * P];
+        }
+    }
+    auto write_state_lds = [&]() {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                lds_store4(Ht + (16 * pb + l16) * NP + 16 * nb + 4 * lg, hs[j][0], hs[j][1], hs[j][2], hs[j][3]);
+            }
+        }
+    };
+
+    load_chunk(0);
+    write_state_lds();
+    stage_chunk(0);
+    load_chunk(min(1, nchunks - 1));
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = chunk_len(c);
+        __syncthreads();  // chunk c staged; everything of chunk c-1 done
+
+        // ---- 1. running sums down each state column (kThreads / N token groups per column)
+        {
+            constexpr int NGR = kThreads / N, PER = Q / NGR;
+            const int n = tid % N, grp = tid / N;
+            float run = 0.f;
+#pragma unroll
+            for (int t = grp * PER; t < grp * PER + PER; ++t) {
+                run += cum[t * CS + n];
+                cum[t * CS + n] = run;
+            }
+            part[grp * N + n] = run;
+            __syncthreads();
+            float off = 0.f;
+            for (int q = 0; q < grp; ++q) off += part[q * N + n];
+#pragma unroll
+            for (int t = grp * PER; t < grp * PER + PER; ++t) cum[t * CS + n] += off;
+        }
+        __syncthreads();
+
+        // ---- 2. factor tables and scaled operands (all from LDS)
+        if (tid < N) el[tid] = __expf(cum[(Q - 1) * CS + tid]);
+        for (int i = tid; i < L::NOFF * N; i += kThreads) {
+            const int p = i / N, n = i % N;
+            int tb = 1;
+            while (offdiag_index(tb + 1, 0) <= p) ++tb;
+            const int sb = p - offdiag_index(tb, 0);
+            beta[i] = __expf(cum[(16 * tb) * CS + n] - cum[(16 * sb + 15) * CS + n]);
+        }
+        for (int item = tid; item < Q * (N / 8); item += kThreads) {
+            const int t = item / (N / 8), c8 = item % (N / 8);
+            const int a = t & ~15, e = t | 15;
+            const f32x4 ct0 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8);
+            const f32x4 ct1 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8 + 4);
+            const f32x4 ca0 = *reinterpret_cast<const f32x4*>(cum + a * CS + 8 * c8);
+            const f32x4 ca1 = *reinterpret_cast<const f32x4*>(cum + a * CS + 8 * c8 + 4);
+            const f32x4 ce0 = *reinterpret_cast<const f32x4*>(cum + e * CS + 8 * c8);
+            const f32x4 ce1 = *reinterpret_cast<const f32x4*>(cum + e * CS + 8 * c8 + 4);
+            const bf16x8 cv = as_bf16x8(ld16(Craw + t * NP + 8 * c8));
+            const bf16x8 bv = as_bf16x8(ld16(Braw + t * NP + 8 * c8));
+            bf16x8 vcc, vcf, vbu;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float ct = j < 4 ? ct0[j] : ct1[j - 4];
+                const float ca = j < 4 ? ca0[j] : ca1[j - 4];
+                const float ce = j < 4 ? ce0[j] : ce1[j - 4];
+                vcc[j] = (__bf16)((float)cv[j] * __expf(ct));
+                vcf[j] = (__bf16)((float)cv[j] * __expf(ct - ca));
+                vbu[j] = (__bf16)((float)bv[j] * __expf(ce - ct));
+            }
+            *reinterpret_cast<bf16x8*>(Cc + t * NP + 8 * c8) = vcc;
+            *reinterpret_cast<bf16x8*>(Cf + t * NP + 8 * c8) = vcf;
+            *reinterpret_cast<bf16x8*>(Bu + t * NP + 8 * c8) = vbu;
+        }
+        // (w o B)^T: four tokens of one state column per item
+        for (int item = tid; item < (Q / 4) * N; item += kThreads) {
+            const int n = item % N, t4 = 4 * (item / N);
+            const float cl = cum[(Q - 1) * CS + n];
+            float v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[k] = (float)Braw[(t4 + k) * NP + n] * __expf(cl - cum[(t4 + k) * CS + n]);
+            lds_store4(Bt + n * QP + t4, v[0], v[1], v[2], v[3]);
+        }
+        __syncthreads();
+
+        // ---- 3. masked score tiles S^T[s][t] (s block sb <= t block tb), fp32 in LDS, in
+        //         accumulator order (lane l holds rows 4(l/16)+i, column l%16); the costly
+        //         diagonal tiles first, one per wave
+        constexpr int NTILES = NT * (NT + 1) / 2;
+        for (int ord = wave; ord < NTILES; ord += kWaves) {
+            int tb, sb;
+            if (ord < NT) {
+                tb = sb = ord;
+            } else {
+                const int o = ord - NT;
+                tb = 1;
+                while (offdiag_index(tb + 1, 0) <= o) ++tb;
+                sb = o - offdiag_index(tb, 0);
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (sb < tb) {
+                const float* bet = beta + offdiag_index(tb, sb) * N;
+                const int s = 16 * sb + l16, t = 16 * tb + l16;
+#pragma unroll
+                for (int kb = 0; kb < N / 32; ++kb) {
+                    const int k0 = 32 * kb + 8 * lg;
+                    float bf[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) bf[j] = bet[k0 + j];
+                    const uint4 av = ld16(Bu + s * NP + k0);
+                    const uint4 cv = scale_vec(ld16(Cf + t * NP + k0), bf, __bf16());
+                    acc = mfma_bf16(as_bf16x8(av), as_bf16x8(cv), acc);
+                }
+            } else {
+                // exact: S^T[s][t] = sum_n B_sn C_tn exp(cum_tn - cum_sn) for s <= t
+                const int t = 16 * tb + l16;
+                bool causal[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) causal[i] = 4 * lg + i <= l16;
+#pragma unroll 4
+                for (int n = 0; n < N; n += 4) {
+                    const f32x4 ct = *reinterpret_cast<const f32x4*>(cum + t * CS + n);
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    const bf16x4 cr = *reinterpret_cast<const bf16x4*>(Craw + t * NP + n);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int s = 16 * sb + 4 * lg + i;
+                        const f32x4 cs = *reinterpret_cast<const f32x4*>(cum + s * CS + n);
+                        const bf16x4 br = *reinterpret_cast<const bf16x4*>(Braw + s * NP + n);
+                        float sum = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            sum += (float)cr[j] * (float)br[j] * __expf(causal[i] ? ct[j] - cs[j] : 0.f);
+                        acc[i] += causal[i] ? sum : 0.f;
+                    }
+                }
+            }
+            *reinterpret_cast<f32x4*>(Sl + tile_index(tb, sb) * 256 + lane * 4) = acc;
+        }
+        __syncthreads();
+
+        // ---- 4. outputs: carried state (C o exp(cum)) H_{k-1}, plus masked scores times x
+        for (int tb = wave; tb < NT; tb += kWaves) {
+            const int tl = 16 * tb + l16;
+            f32x4 acc[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < N / 32; ++kb) {
+                const uint4 cv = ld16(Cc + tl * NP + 32 * kb + 8 * lg);
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+                    acc[pb] = mfma_bf16(as_bf16x8(ld16(Ht + (16 * pb + l16) * NP + 32 * kb + 8 * lg)), as_bf16x8(cv),
+                                        acc[pb]);
+            }
+            for (int k = 0; 2 * k <= tb; ++k) {
+                const f32x4 m0 = *reinterpret_cast<const f32x4*>(Sl + tile_index(tb, 2 * k) * 256 + lane * 4);
+                const f32x4 m1 = (2 * k + 1 <= tb)
+                                     ? *reinterpret_cast<const f32x4*>(Sl + tile_index(tb, 2 * k + 1) * 256 + lane * 4)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+                const bf16x8 bop = {(__bf16)m0[0], (__bf16)m0[1], (__bf16)m0[2], (__bf16)m0[3],
+                                    (__bf16)m1[0], (__bf16)m1[1], (__bf16)m1[2], (__bf16)m1[3]};
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    const __bf16* xr = Xt + (16 * pb + l16) * QP + 32 * k + 4 * lg;
+                    const uint2 lo = ld8(xr), hi = ld8(xr + 16);
+                    const uint4 a = {lo.x, lo.y, hi.x, hi.y};
+                    acc[pb] = mfma_bf16(as_bf16x8(a), bop, acc[pb]);
+                }
+            }
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[pb][i] += dskip * (float)Xt[(16 * pb + 4 * lg + i) * QP + tl];
+            if (tl < len) {
+                __bf16* yr = yg + ((b * Tn + t0 + tl) * H + h) * P + 4 * lg;
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) store4(yr + 16 * pb, acc[pb][0], acc[pb][1], acc[pb][2], acc[pb][3]);
+            }
+        }
+
+        // ---- 5. state: H_k[n,:] = exp(cum_last,n) H_{k-1}[n,:] + (w o B)^T X
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                f32x4 a = hs[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] *= el[16 * nb + 4 * lg + i];
+                const __bf16* br = Bt + (16 * nb + l16) * QP + 8 * lg;
+                const __bf16* xr = Xt + (16 * pb + l16) * QP + 8 * lg;
+#pragma unroll
+                for (int kb = 0; kb < Q / 32; ++kb)
+                    a = mfma_bf16(as_bf16x8(ld16(br + 32 * kb)), as_bf16x8(ld16(xr + 32 * kb)), a);
+                hs[j] = a;
+            }
+        }
+        __syncthreads();  // every read of chunk c's LDS data done
+        write_state_lds();
+        stage_chunk(c + 1 < nchunks ? c + 1 : c);
+        load_chunk(min(c + 2, nchunks - 1));
+    }
+
+    if (prm.final_state) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                float* dst = prm.final_state + (unit * N + 16 * nb + 4 * lg) * P + 16 * pb + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * P] = hs[j][i];
+            }
+        }
+    }
+}
+
 template <typename T, int N, int P>
 int launch_diag_t(const ForwardLaunch& fl, hipStream_t stream) {
     static bool attr_set[64] = {};
@@ -414,7 +804,37 @@ size_t diag_lds_bytes(int dtype, int N, int P, int chunk) {
     return 0;
 }
 
+template <int N, int P>
+int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
+    static bool attr_set[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    if (!attr_set[dev]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
+            return -1;
+        attr_set[dev] = true;
+    }
+    const int64_t units = fl.batch * fl.nheads;
+    const int64_t per_xcd = (units + 7) / 8;
+    WalkParams wp{fl.x, fl.log_a, fl.Bm, fl.Cm, fl.D, nullptr, fl.init, fl.y, fl.final_state,
+                  fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.chunk, fl.nchunks, per_xcd};
+    const size_t lds = DiagPipeLayout<N, P>::total;
+    if (!record_event(fl, 0, stream)) return -1;
+    hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp);
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (!record_event(fl, 1, stream)) return -1;
+    if (fl.n_launches) *fl.n_launches = 1;
+    return 0;
+}
+
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream) {
+    if (fl.dtype == 1 && fl.chunk == kDiagQ) {
+        if (fl.dstate == 64 && fl.headdim == 64) return launch_diag_pipe_t<64, 64>(fl, stream);
+        if (fl.dstate == 64 && fl.headdim == 32) return launch_diag_pipe_t<64, 32>(fl, stream);
+        if (fl.dstate == 32 && fl.headdim == 64) return launch_diag_pipe_t<32, 64>(fl, stream);
+        if (fl.dstate == 32 && fl.headdim == 32) return launch_diag_pipe_t<32, 32>(fl, stream);
+    }
 #define SSD_DLAUNCH(TT, NN, PP) \
     if ((std::is_same<TT, float>::value ? 0 : 1) == fl.dtype && fl.dstate == NN && fl.headdim == PP) \
         return launch_diag_t<TT, NN, PP>(fl, stream);
