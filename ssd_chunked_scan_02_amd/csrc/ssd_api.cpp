@@ -42,7 +42,9 @@ int check_dims(const ssd_dims* d, bool forward) {
 size_t workspace_needed(const ssd_dims* d, int chunk) {
     if (d->seqlen == 0 || d->batch == 0) return 0;
     const int64_t nchunks = (d->seqlen + chunk - 1) / chunk;
-    if (d->decay == SSD_DECAY_DIAG) return 0;
+    if (d->decay == SSD_DECAY_DIAG)
+        return ssd::diag_workspace_bytes(d->dtype, d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim,
+                                         chunk);
     if (ssd::fast_path_applies(d->dtype, d->decay, (int)d->dstate, (int)d->headdim, chunk, d->nheads, d->ngroups))
         return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, d->seqlen, (int)d->dstate, chunk);
     return ssd::scores_bytes(d->batch, d->ngroups, nchunks, chunk);

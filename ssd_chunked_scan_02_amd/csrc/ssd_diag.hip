@@ -444,7 +444,9 @@ struct DiagPipeLayout {
     static constexpr size_t total = sl + (size_t)(NT * (NT + 1) / 2) * 256 * 4;
 };
 
-template <int N, int P>
+// FULL: the walk.  !FULL: the state-only pass of a segmented walk (H over the segment from a
+// zero state, written to seg_state with the segment's log2 decay per state row in seg_decay).
+template <int N, int P, bool FULL>
 __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm) {
     using L = DiagPipeLayout<N, P>;
     constexpr int Q = L::Q, NT = L::NT, QP = L::QP, NP = L::NP, CS = L::CS;
@@ -455,12 +457,17 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
     static_assert(LAI >= 1 && BCI >= 1 && XI >= 1, "diag pipe shape");
 
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
-    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
-    if (unit < 0) return;
+    const int64_t units = prm.batch * H;
+    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * units);
+    if (work < 0) return;
+    const int seg = (int)(work / units);
+    const int64_t unit = work % units;
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane % 16, lg = lane / 16;
     const int nchunks = prm.nchunks;
+    const int c0 = seg * prm.seg_chunks, c1 = min(c0 + prm.seg_chunks, nchunks);
+    const int64_t sidx = seg * units + unit;  // (segment, unit) index of the segment buffers
 
     extern __shared__ __align__(16) unsigned char smem[];
     __bf16* Xt = reinterpret_cast<__bf16*>(smem + L::xt);
@@ -534,18 +541,22 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
 
     // ---- state registers (tiles (nb, pb) dealt round-robin to the waves)
     f32x4 hs[TPW];
+    const float* init = !FULL ? nullptr
+                        : prm.nseg > 1 ? prm.seg_init + sidx * N * P
+                                       : (prm.init ? prm.init + unit * N * P : nullptr);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int tile = wave + kWaves * j;
-        if (tile < NTILE && prm.init) {
+        if (tile < NTILE && init) {
             const int nb = tile / PB, pb = tile % PB;
-            const float* src = prm.init + (unit * N + 16 * nb + 4 * lg) * P + 16 * pb + l16;
+            const float* src = init + (16 * nb + 4 * lg) * P + 16 * pb + l16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) hs[j][i] = src[i * P];
         }
     }
     auto write_state_lds = [&]() {
+        if (!FULL) return;
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int tile = wave + kWaves * j;
@@ -556,12 +567,13 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
         }
     };
 
-    load_chunk(0);
+    float lsum = 0.f;  // (threads < N) the segment's summed log a of state row tid
+    load_chunk(c0);
     write_state_lds();
-    stage_chunk(0);
-    load_chunk(min(1, nchunks - 1));
+    stage_chunk(c0);
+    load_chunk(min(c0 + 1, c1 - 1));
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = c0; c < c1; ++c) {
         const int64_t t0 = (int64_t)c * Q;
         const int len = chunk_len(c);
         __syncthreads();  // chunk c staged; everything of chunk c-1 done
@@ -586,15 +598,18 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
         __syncthreads();
 
         // ---- 2. factor tables and scaled operands (all from LDS)
-        if (tid < N) el[tid] = __expf(cum[(Q - 1) * CS + tid]);
-        for (int i = tid; i < L::NOFF * N; i += kThreads) {
+        if (tid < N) {
+            el[tid] = __expf(cum[(Q - 1) * CS + tid]);
+            lsum += cum[(Q - 1) * CS + tid];
+        }
+        for (int i = tid; FULL && i < L::NOFF * N; i += kThreads) {
             const int p = i / N, n = i % N;
             int tb = 1;
             while (offdiag_index(tb + 1, 0) <= p) ++tb;
             const int sb = p - offdiag_index(tb, 0);
             beta[i] = __expf(cum[(16 * tb) * CS + n] - cum[(16 * sb + 15) * CS + n]);
         }
-        for (int item = tid; item < Q * (N / 8); item += kThreads) {
+        for (int item = tid; FULL && item < Q * (N / 8); item += kThreads) {
             const int t = item / (N / 8), c8 = item % (N / 8);
             const int a = t & ~15, e = t | 15;
             const f32x4 ct0 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8);
@@ -635,7 +650,7 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
         //         accumulator order (lane l holds rows 4(l/16)+i, column l%16); the costly
         //         diagonal tiles first, one per wave
         constexpr int NTILES = NT * (NT + 1) / 2;
-        for (int ord = wave; ord < NTILES; ord += kWaves) {
+        for (int ord = wave; FULL && ord < NTILES; ord += kWaves) {
             int tb, sb;
             if (ord < NT) {
                 tb = sb = ord;
@@ -688,7 +703,7 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
         __syncthreads();
 
         // ---- 4. outputs: carried state (C o exp(cum)) H_{k-1}, plus masked scores times x
-        for (int tb = wave; tb < NT; tb += kWaves) {
+        for (int tb = wave; FULL && tb < NT; tb += kWaves) {
             const int tl = 16 * tb + l16;
             f32x4 acc[PB];
 #pragma unroll
@@ -746,17 +761,20 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
         }
         __syncthreads();  // every read of chunk c's LDS data done
         write_state_lds();
-        stage_chunk(c + 1 < nchunks ? c + 1 : c);
-        load_chunk(min(c + 2, nchunks - 1));
+        stage_chunk(c + 1 < c1 ? c + 1 : c);
+        load_chunk(min(c + 2, c1 - 1));
     }
 
-    if (prm.final_state) {
+    if (!FULL && tid < N) prm.seg_decay[sidx * N + tid] = lsum * 1.4426950408889634f;
+    float* fin = !FULL ? prm.seg_state + sidx * N * P
+                       : (c1 == nchunks && prm.final_state) ? prm.final_state + unit * N * P : nullptr;
+    if (fin) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int tile = wave + kWaves * j;
             if (tile < NTILE) {
                 const int nb = tile / PB, pb = tile % PB;
-                float* dst = prm.final_state + (unit * N + 16 * nb + 4 * lg) * P + 16 * pb + l16;
+                float* dst = fin + (16 * nb + 4 * lg) * P + 16 * pb + l16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[i * P] = hs[j][i];
             }
@@ -804,32 +822,82 @@ size_t diag_lds_bytes(int dtype, int N, int P, int chunk) {
     return 0;
 }
 
+// Workspace of the pipelined diagonal walk: nothing, or for a segmented walk two fp32 states
+// and a log2 decay per state row for every (segment, unit).
+struct DiagSegLayout {
+    int nseg, seg_chunks;
+    size_t state, init, decay, total;
+};
+
+DiagSegLayout diag_seg_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P) {
+    DiagSegLayout l;
+    const int64_t units = batch * nheads, nchunks = (seqlen + kDiagQ - 1) / kDiagQ;
+    l.nseg = walk_segments(units, nchunks, &l.seg_chunks);
+    l.state = l.init = l.decay = l.total = 0;
+    if (l.nseg > 1) {
+        const size_t st = (size_t)l.nseg * units * N * P * 4;
+        l.state = 0;
+        l.init = st;
+        l.decay = 2 * st;
+        l.total = 2 * st + ((size_t)l.nseg * units * N * 4 + 255) / 256 * 256;
+    }
+    return l;
+}
+
+bool diag_pipe_shape(int dtype, int N, int P, int chunk) {
+    return dtype == 1 && chunk == kDiagQ && (N == 32 || N == 64) && (P == 32 || P == 64);
+}
+
 template <int N, int P>
 int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
-    static bool attr_set[64] = {};
+    static bool attr_set[64][2] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-    if (!attr_set[dev]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P>),
+    if (!attr_set[dev][0]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
             return -1;
-        attr_set[dev] = true;
+        attr_set[dev][0] = true;
     }
+    const DiagSegLayout sl = diag_seg_layout(fl.batch, fl.nheads, fl.seqlen, N, P);
     const int64_t units = fl.batch * fl.nheads;
-    const int64_t per_xcd = (units + 7) / 8;
+    const int64_t per_xcd = (sl.nseg * units + 7) / 8;
+    char* ws = reinterpret_cast<char*>(fl.scores);
     WalkParams wp{fl.x, fl.log_a, fl.Bm, fl.Cm, fl.D, nullptr, fl.init, fl.y, fl.final_state,
-                  fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.chunk, fl.nchunks, per_xcd};
+                  fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.chunk, fl.nchunks, per_xcd,
+                  sl.seg_chunks, sl.nseg,
+                  sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.init) : nullptr,
+                  sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.state) : nullptr,
+                  sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.decay) : nullptr};
     const size_t lds = DiagPipeLayout<N, P>::total;
-    if (!record_event(fl, 0, stream)) return -1;
-    hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp);
+    int ev = 0;
+    if (sl.nseg > 1) {
+        if (!record_event(fl, ev++, stream)) return -1;
+        hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, false>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds,
+                           stream, wp);
+        if (hipGetLastError() != hipSuccess) return -1;
+        if (!record_event(fl, ev++, stream)) return -1;
+        if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1, stream) != 0)
+            return -1;
+    }
+    if (!record_event(fl, ev++, stream)) return -1;
+    hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, true>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream,
+                       wp);
     if (hipGetLastError() != hipSuccess) return -1;
-    if (!record_event(fl, 1, stream)) return -1;
-    if (fl.n_launches) *fl.n_launches = 1;
+    if (!record_event(fl, ev++, stream)) return -1;
+    if (fl.n_launches) *fl.n_launches = ev - 1;
     return 0;
 }
 
+size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk) {
+    if (!diag_pipe_shape(dtype, N, P, chunk)) return 0;
+    return diag_seg_layout(batch, nheads, seqlen, N, P).total;
+}
+
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream) {
-    if (fl.dtype == 1 && fl.chunk == kDiagQ) {
+    if (diag_pipe_shape(fl.dtype, (int)fl.dstate, (int)fl.headdim, fl.chunk)) {
         if (fl.dstate == 64 && fl.headdim == 64) return launch_diag_pipe_t<64, 64>(fl, stream);
         if (fl.dstate == 64 && fl.headdim == 32) return launch_diag_pipe_t<64, 32>(fl, stream);
         if (fl.dstate == 32 && fl.headdim == 64) return launch_diag_pipe_t<32, 64>(fl, stream);

@@ -205,9 +205,6 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepParams prm) {
 // offset (the host only takes this path when every offset inside a chunk fits).
 constexpr int kWalkWaves = 8;
 constexpr int kWalkThreads = kWalkWaves * kWave;
-// segmented walks: about this many workgroups at once, segments of at least this many chunks
-constexpr int64_t kSegTarget = 256;
-constexpr int64_t kMinSegChunks = 4;
 
 // 16-token block handled by output wave `ow` in its r-th round (snake order balances the
 // causal work across the four output waves).
@@ -748,20 +745,6 @@ __global__ void __launch_bounds__(kThreads) walk_state_kernel(Walk2Params prm) {
     }
 }
 
-// Chains the segments' local states: seg_init[s] = exp2(seg_decay[s-1]) seg_init[s-1] +
-// seg_state[s-1], seg_init[0] = the initial state (or 0).  One thread per state element.
-__global__ void __launch_bounds__(kThreads) seg_prefix_kernel(Walk2Params prm, int64_t elems_per_unit) {
-    const int64_t units = prm.batch * prm.nheads;
-    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (e >= units * elems_per_unit) return;
-    const int64_t unit = e / elems_per_unit;
-    float hcur = prm.init ? prm.init[e] : 0.f;
-    for (int s = 0; s < prm.nseg; ++s) {
-        prm.seg_init[s * units * elems_per_unit + e] = hcur;
-        hcur = exp2f(prm.seg_decay[s * units + unit]) * hcur + prm.seg_state[s * units * elems_per_unit + e];
-    }
-}
-
 template <int N, int Q>
 constexpr size_t prep_lds() {
     return (size_t)2 * Q * (N + 8) * 2;
@@ -791,13 +774,7 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
     l.nchunks = (seqlen + Q - 1) / Q;
     l.nblk = batch * ngroups * l.nchunks;
     l.units = batch * nheads;
-    // Few (batch, head) units on a long sequence: split each sequence into segments of at
-    // least kMinSegChunks chunks so that about kSegTarget workgroups walk at once.
-    l.nseg = 1;
-    if (l.units > 0 && l.units * 2 <= kSegTarget && l.nchunks >= 2 * kMinSegChunks)
-        l.nseg = (int)min(kSegTarget / l.units, l.nchunks / kMinSegChunks);
-    l.seg_chunks = (int)((l.nchunks + l.nseg - 1) / l.nseg);
-    l.nseg = (int)((l.nchunks + l.seg_chunks - 1) / l.seg_chunks);
+    l.nseg = walk_segments(l.units, l.nchunks, &l.seg_chunks);
     size_t off = 0;
     l.pairs = off; off += (size_t)l.nblk * n_pairs(Q / 16) * 1024;
     l.bt = off; off += (size_t)l.nblk * N * Q * 2;
@@ -847,10 +824,9 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
                            wp);
         if (hipGetLastError() != hipSuccess) return -1;
         if (!record_event(fl, ev++, stream)) return -1;
-        const int64_t elems = (int64_t)N * kP;
-        hipLaunchKernelGGL(seg_prefix_kernel, dim3((unsigned)((lay.units * elems + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, wp, elems);
-        if (hipGetLastError() != hipSuccess) return -1;
+        if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, lay.units, N, kP, lay.nseg, 0,
+                              stream) != 0)
+            return -1;
     }
     if (!record_event(fl, ev++, stream)) return -1;
     hipLaunchKernelGGL((walk_fast_kernel<N, Q>), dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream, wp);
@@ -887,6 +863,35 @@ int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream) {
     if (N == 128 && Q == 64) return launch_fast_t<128, 64>(fl, stream);
     if (N == 128 && Q == 128) return launch_fast_t<128, 128>(fl, stream);
     return -2;
+}
+
+// Chains the segments' local states, one thread per state element (n, p) of one unit:
+//   seg_init[s] = exp2(decay[s-1]) o seg_init[s-1] + seg_state[s-1],  seg_init[0] = init (or 0),
+// with decay one log2 value per (segment, unit) (scalar decay) or per (segment, unit, n)
+// (diagonal decay).  States are [segment][unit][N][P] fp32.
+__global__ void __launch_bounds__(kThreads) seg_prefix_kernel(const float* init, float* seg_init,
+                                                              const float* seg_state, const float* seg_decay,
+                                                              int64_t units, int N, int P, int nseg, int per_n) {
+    const int64_t epu = (int64_t)N * P;
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= units * epu) return;
+    const int64_t unit = e / epu;
+    const int n = (int)((e % epu) / P);
+    const int64_t dstride = per_n ? N : 1;
+    const int64_t didx = unit * dstride + (per_n ? n : 0);
+    float hcur = init ? init[e] : 0.f;
+    for (int s = 0; s < nseg; ++s) {
+        seg_init[s * units * epu + e] = hcur;
+        hcur = exp2f(seg_decay[s * units * dstride + didx]) * hcur + seg_state[s * units * epu + e];
+    }
+}
+
+int launch_seg_prefix(const float* init, float* seg_init, const float* seg_state, const float* seg_decay,
+                      int64_t units, int N, int P, int nseg, int per_n, hipStream_t stream) {
+    const int64_t total = units * N * P;
+    hipLaunchKernelGGL(seg_prefix_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, init, seg_init, seg_state, seg_decay, units, N, P, nseg, per_n);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace ssd

@@ -32,6 +32,11 @@ struct WalkParams {
     int chunk;
     int nchunks;
     int64_t per_xcd;
+    // segmented walks (nseg > 1), as in Walk2Params
+    int seg_chunks, nseg;
+    float* seg_init;
+    float* seg_state;
+    float* seg_decay;
 };
 
 struct StepParams {
@@ -112,6 +117,10 @@ int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream);
 // The diagonal-decay walk (ssd_diag.hip): LDS bytes (0 = unsupported) and launch.
 size_t diag_lds_bytes(int dtype, int N, int P, int chunk);
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream);
+size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk);
+// Segment prefix of a segmented walk (ssd_fast.hip): per_n = 1 for one decay per state row.
+int launch_seg_prefix(const float* init, float* seg_init, const float* seg_state, const float* seg_decay,
+                      int64_t units, int N, int P, int nseg, int per_n, hipStream_t stream);
 size_t walk_lds_bytes(int dtype, int N, int P, int chunk);
 size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk);
 // 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.
@@ -119,5 +128,18 @@ int launch_forward(const ForwardLaunch& fl, hipStream_t stream);
 int launch_step(const StepParams& sp, int dtype, int64_t units, hipStream_t stream);
 
 constexpr size_t kMaxLds = 160 * 1024;
+
+// Segmented walks: with few (batch, head) units on a long sequence, each sequence is split into
+// segments of at least 4 chunks so that about 256 workgroups walk at once.  Returns the number
+// of segments and sets *seg_chunks (chunks per segment; the last segment may be shorter).
+inline int walk_segments(int64_t units, int64_t nchunks, int* seg_chunks) {
+    constexpr int64_t kTarget = 256, kMinChunks = 4;
+    int64_t nseg = 1;
+    if (units > 0 && units * 2 <= kTarget && nchunks >= 2 * kMinChunks)
+        nseg = (kTarget / units < nchunks / kMinChunks) ? kTarget / units : nchunks / kMinChunks;
+    const int64_t per = (nchunks + nseg - 1) / nseg;
+    *seg_chunks = (int)(per > 0 ? per : 1);
+    return (int)(per > 0 ? (nchunks + per - 1) / per : 1);
+}
 
 }  // namespace ssd

@@ -187,6 +187,19 @@ def test_diag_small(over):
     _run(cfg, 41, "diag")
 
 
+DIAG_SEGMENTED = [
+    # few units on a long sequence: state-only pass, per-row segment prefix, full pass
+    dict(batch=1, seqlen=2000, nheads=2, init=True),
+    dict(batch=2, seqlen=1100, nheads=1, dstate=32, headdim=32, skip=False),
+]
+
+
+@pytest.mark.parametrize("over", DIAG_SEGMENTED, ids=["diag-seg-%d" % i for i in range(len(DIAG_SEGMENTED))])
+def test_diag_segmented(over):
+    cfg = ssd_inputs.config("diag_multiscale", **over)
+    _run(cfg, 59, "diag segmented")
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_diag_chunk_sizes(chunk):
     cfg = ssd_inputs.config("diag_multiscale", batch=1, seqlen=333, nheads=2, chunk=chunk, init=True)
