@@ -91,14 +91,47 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def fast_segments(cfg):
+    """Segments the library splits each (batch, head) sequence into on its bf16 fast path
+    (mirrors its workspace layout: about 256 workgroups, at least 4 chunks per segment)."""
+    q = min(cfg["chunk"], 128)
+    units = cfg["batch"] * cfg["nheads"]
+    nch = -(-cfg["seqlen"] // q)
+    nseg = 1
+    if units > 0 and units * 2 <= 256 and nch >= 8:
+        nseg = min(256 // units, nch // 4)
+    per = -(-nch // nseg)
+    return -(-nch // per)
+
+
 def kernel_names(cfg):
     """Kernels one forward launches, in order (mirrors the library's dispatch)."""
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
     if cfg["decay"] == "diag":
+        if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
+            if fast_segments(dict(cfg, chunk=64)) > 1:
+                return ["walk_diag_pipe_kernel<%d,%d,state>" % (N, P), "seg_prefix_kernel",
+                        "walk_diag_pipe_kernel<%d,%d>" % (N, P)]
+            return ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]
         return ["walk_diag_kernel<%d,%d>" % (N, P)]
-    if cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128):
-        return ["prep_kernel<%d,%d>" % (N, Q), "walk_fast_kernel<%d,%d>" % (N, Q)]
+    if cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256):
+        q = min(Q, 128)
+        if fast_segments(cfg) > 1:
+            return ["prep_kernel<%d,%d>" % (N, q), "walk_state_kernel<%d,%d>" % (N, q), "seg_prefix_kernel",
+                    "walk_fast_kernel<%d,%d>" % (N, q)]
+        return ["prep_kernel<%d,%d>" % (N, q), "walk_fast_kernel<%d,%d>" % (N, q)]
     return ["scores_kernel<%d>" % N, "walk_kernel<%d,%d>" % (N, P)]
+
+
+def kernel_bytes(cfg, name, nbytes):
+    """Algorithmic bytes of one launch of `name`: what of the method's inputs and outputs that
+    kernel itself moves.  The fast path's walk reads x and log a and writes y (B and C reach
+    it through the prep kernel); every other walk moves the whole forward's bytes."""
+    if not name.startswith("walk_fast_kernel"):
+        return nbytes
+    Bsz, T, H, N, P = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["dstate"], cfg["headdim"]
+    return Bsz * T * (H * P * 4 + 4 * H) + (4 * H if cfg["skip"] else 0) \
+        + 4 * Bsz * H * N * P * (int(cfg["init"]) + int(cfg["final"]))
 
 
 def measured_traffic(workload, kernel):
@@ -243,7 +276,8 @@ def main():
     tflops = flops / (ms / 1e3) / 1e12
     peak_tf = FP32_PEAK_TFLOPS if cfg["dtype"] == "fp32" else BF16_PEAK_TFLOPS
     dom_ms = kernel_avg[dom]
-    achieved = nbytes / (dom_ms / 1e3) / 1e9
+    dom_bytes = kernel_bytes(cfg, names[dom], nbytes)
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
     traffic = measured_traffic(args.workload, names[dom])
     result = {
         "metric": "SSD forward tokens/s + TFLOP/s (% MFMA peak) at B=8,T=2048,H=24,P=64,N=128",
@@ -268,8 +302,9 @@ def main():
         "kernels_ms": {n: t for n, t in zip(names, kernel_avg)},
         "roofline": {"kernel": names[dom], "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
-                     "bytes_per_token": per_token, "tokens_per_launch": tokens},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
+                     "bytes_per_token": dom_bytes / tokens, "tokens_per_launch": tokens,
+                     "forward_bytes_per_token": per_token},
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle (>= %.0f s)..." % args.cpu_seconds)
