@@ -88,13 +88,19 @@ __device__ __forceinline__ void unpack8(bf16x8 v, float (&f)[8]) {
 //   btf[(b,g,c)][nb][k][lane][8]: B[32k + kperm(lg, j)][16 nb + l16]  (the B^T operand);
 //   la_t[b][h][c Q + t] = log a[b][c Q + t][h] for the group's heads (0 past the sequence
 //       end), so the walk reads a head's chunk contiguously.
-constexpr int kPrepWaves = 8;
-constexpr int kPrepThreads = kPrepWaves * kWave;
+// waves of one prep workgroup: 16, or fewer when the chunk has fewer 16-byte pieces of B
+template <int N, int Q> struct PrepShape {
+    static constexpr int WAVES = Q * N / 8 / kWave < 16 ? Q * N / 8 / kWave : 16;
+    static constexpr int THREADS = WAVES * kWave;
+};
 // log a items (head, 4 tokens) per prep thread: heads per group up to kPrepLa * 4 * 512 / chunk
+// (the smallest prep workgroup has 512 threads)
 constexpr int kPrepLa = 4;
+constexpr int kPrepMinThreads = 512;
 
 template <int N, int Q>
-__global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrepParams prm) {
+__global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepParams prm) {
+    constexpr int kPrepThreads = PrepShape<N, Q>::THREADS, kPrepWaves = PrepShape<N, Q>::WAVES;
     constexpr int NT = Q / 16, KS = Q / 32, NB = N / 16, KN = N / 32;
     constexpr int NPAIR = n_pairs(NT);
     constexpr int NS = N + 8;
@@ -388,14 +394,17 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         for (int r = 0; r < TBW; ++r)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) acc[r][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 hfa[KN][PB];
 #pragma unroll
         for (int k = 0; k < KN; ++k)
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) {
-                const bf16x8 hf = as_bf16x8(ld16(hcur + (16 * pb + l16) * HS + 32 * k + 8 * lg));
+            for (int pb = 0; pb < PB; ++pb) hfa[k][pb] = as_bf16x8(ld16(hcur + (16 * pb + l16) * HS + 32 * k + 8 * lg));
 #pragma unroll
-                for (int r = 0; r < TBW; ++r) acc[r][pb] = mfma_bf16(hf, as_bf16x8(cf[r][k]), acc[r][pb]);
-            }
+        for (int k = 0; k < KN; ++k)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int r = 0; r < TBW; ++r) acc[r][pb] = mfma_bf16(hfa[k][pb], as_bf16x8(cf[r][k]), acc[r][pb]);
         load_c(cn);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
 #pragma unroll
@@ -661,14 +670,18 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         for (int jn = 0; jn < NBW; ++jn)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) hs[jn][pb] *= el;
+        // every operand read issued before the first MFMA, so LDS latency is paid once
+        bf16x8 xfa[KS][PB];
 #pragma unroll
         for (int k = 0; k < KS; ++k)
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) {
-                const bf16x8 xf = token_frag(xwm, kXStr, 16 * pb, k, lane);
+            for (int pb = 0; pb < PB; ++pb) xfa[k][pb] = token_frag(xwm, kXStr, 16 * pb, k, lane);
 #pragma unroll
-                for (int jn = 0; jn < NBW; ++jn) hs[jn][pb] = mfma_bf16(as_bf16x8(bt[jn][k]), xf, hs[jn][pb]);
-            }
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int jn = 0; jn < NBW; ++jn) hs[jn][pb] = mfma_bf16(as_bf16x8(bt[jn][k]), xfa[k][pb], hs[jn][pb]);
         load_b(cn);
         stage_x(c + 1);
         load_x(min(c + 2, c1 - 1));
@@ -808,7 +821,8 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     if (!record_event(fl, ev++, stream)) return -1;
     // (sizes computed first: template commas cannot sit inside the launch macro)
     const size_t plds = prep_lds<N, Q>(), slds = StateLds<N, Q>::bytes, wlds = WalkShape<N, Q>::lds_bytes;
-    hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)lay.nblk), dim3(kPrepThreads), plds, stream, pp);
+    const unsigned pthreads = PrepShape<N, Q>::THREADS;
+    hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)lay.nblk), dim3(pthreads), plds, stream, pp);
     if (hipGetLastError() != hipSuccess) return -1;
 
     const int64_t work = lay.nseg * lay.units;
@@ -847,7 +861,7 @@ bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nh
     // kernel moves the log a of at most kPrepLa * 4 * kPrepThreads / chunk heads per group
     const int q = fast_chunk(chunk);
     const bool offsets_fit = (double)q * (double)(nheads * P + ngroups * N) * 2.0 < 2147483648.0;
-    const bool heads_fit = ngroups > 0 && nheads / ngroups <= (int64_t)kPrepLa * 4 * kPrepThreads / q;
+    const bool heads_fit = ngroups > 0 && nheads / ngroups <= (int64_t)kPrepLa * 4 * kPrepMinThreads / q;
     return dtype == 1 && decay == 0 && P == kP && (N == 64 || N == 128) &&
            (chunk == 64 || chunk == 128 || chunk == 256) && offsets_fit && heads_fit;
 }
