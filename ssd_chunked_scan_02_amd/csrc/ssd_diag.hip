@@ -422,6 +422,8 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
 // operand (raw B and C included) is read from LDS.  The running sums are kept in rows padded
 // to N + 4 floats so that 16 rows read at once fall on distinct banks.
 constexpr int kDiagQ = 64;
+constexpr int kDiagWaves = 8;
+constexpr int kDiagThreads = kDiagWaves * kWave;
 
 template <int N, int P>
 struct DiagPipeLayout {
@@ -437,24 +439,27 @@ struct DiagPipeLayout {
     static constexpr size_t braw = bu + (size_t)Q * NP * 2;          // B            [Q][NP] bf16
     static constexpr size_t craw = braw + (size_t)Q * NP * 2;        // C            [Q][NP] bf16
     static constexpr size_t cum = craw + (size_t)Q * NP * 2;         // running sums [Q][CS] f32
-    static constexpr size_t part = cum + (size_t)Q * CS * 4;         // scan partials [kThreads/N][N]
-    static constexpr size_t beta = part + (size_t)kThreads * 4;      // [NOFF][N]
+    static constexpr size_t part = cum + (size_t)Q * CS * 4;         // scan partials [threads/N][N]
+    static constexpr size_t beta = part + (size_t)kDiagThreads * 4;  // [NOFF][N]
     static constexpr size_t el = beta + (size_t)(NOFF + 1) * N * 4;  // [N]
-    static constexpr size_t sl = el + (size_t)N * 4;                  // score tiles [NT(NT+1)/2][256]
-    static constexpr size_t total = sl + (size_t)(NT * (NT + 1) / 2) * 256 * 4;
+    // score tiles [NT(NT+1)/2][256], then the second state-dimension half of each diagonal tile
+    static constexpr size_t sl = el + (size_t)N * 4;
+    static constexpr size_t total = sl + (size_t)(NT * (NT + 1) / 2 + NT) * 256 * 4;
 };
 
 // FULL: the walk.  !FULL: the state-only pass of a segmented walk (H over the segment from a
 // zero state, written to seg_state with the segment's log2 decay per state row in seg_decay).
 template <int N, int P, bool FULL>
-__global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm) {
+__global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams prm) {
+    constexpr int kThreads = kDiagThreads, kWaves = kDiagWaves;  // (this kernel's own workgroup)
     using L = DiagPipeLayout<N, P>;
     constexpr int Q = L::Q, NT = L::NT, QP = L::QP, NP = L::NP, CS = L::CS;
     constexpr int PB = P / 16, NB = N / 16, NTILE = NB * PB, TPW = (NTILE + kWaves - 1) / kWaves;
-    constexpr int LAI = Q * N / 4 / kThreads;   // 16-byte pieces of log a per thread
-    constexpr int BCI = Q * N / 8 / kThreads;   // 16-byte pieces of B (and of C) per thread
-    constexpr int XI = Q * P / 8 / kThreads;    // 16-byte pieces of x per thread
-    static_assert(LAI >= 1 && BCI >= 1 && XI >= 1, "diag pipe shape");
+    // 16-byte pieces per chunk of log a, of B (and of C) and of x, and per thread (rounded up;
+    // the pieces past the total are skipped, which is uniform over a wave)
+    constexpr int LAT = Q * N / 4, BCT = Q * N / 8, XT = Q * P / 8;
+    constexpr int LAI = (LAT + kThreads - 1) / kThreads, BCI = (BCT + kThreads - 1) / kThreads;
+    constexpr int XI = (XT + kThreads - 1) / kThreads;
 
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
     const int64_t units = prm.batch * H;
@@ -502,19 +507,21 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
 #pragma unroll
         for (int m = 0; m < LAI; ++m) {
             const int id = tid + kThreads * m, t = min(id / (N / 4), last), c4 = id % (N / 4);
-            rla[m] = ld16(lag + ((b * Tn + t0 + t) * H + h) * N + 4 * c4);
+            if (id < LAT) rla[m] = ld16(lag + ((b * Tn + t0 + t) * H + h) * N + 4 * c4);
         }
 #pragma unroll
         for (int m = 0; m < BCI; ++m) {
             const int id = tid + kThreads * m, t = min(id / (N / 8), last), c8 = id % (N / 8);
             const int64_t off = ((b * Tn + t0 + t) * G + g) * N + 8 * c8;
-            rb[m] = ld16(Bg + off);
-            rc[m] = ld16(Cg + off);
+            if (id < BCT) {
+                rb[m] = ld16(Bg + off);
+                rc[m] = ld16(Cg + off);
+            }
         }
 #pragma unroll
         for (int m = 0; m < XI; ++m) {
             const int id = tid + kThreads * m, t = min(id / (P / 8), last), c8 = id % (P / 8);
-            rx[m] = ld16(xg + ((b * Tn + t0 + t) * H + h) * P + 8 * c8);
+            if (id < XT) rx[m] = ld16(xg + ((b * Tn + t0 + t) * H + h) * P + 8 * c8);
         }
     };
     auto stage_chunk = [&](int c) {
@@ -522,20 +529,24 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
 #pragma unroll
         for (int m = 0; m < LAI; ++m) {
             const int id = tid + kThreads * m, t = id / (N / 4), c4 = id % (N / 4);
-            st16(cum + t * CS + 4 * c4, t < len ? rla[m] : zero);
+            if (id < LAT) st16(cum + t * CS + 4 * c4, t < len ? rla[m] : zero);
         }
 #pragma unroll
         for (int m = 0; m < BCI; ++m) {
             const int id = tid + kThreads * m, t = id / (N / 8), c8 = id % (N / 8);
-            st16(Braw + t * NP + 8 * c8, t < len ? rb[m] : zero);
-            st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
+            if (id < BCT) {
+                st16(Braw + t * NP + 8 * c8, t < len ? rb[m] : zero);
+                st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
+            }
         }
 #pragma unroll
         for (int m = 0; m < XI; ++m) {
             const int id = tid + kThreads * m, t = id / (P / 8), c8 = id % (P / 8);
-            const bf16x8 v = as_bf16x8(t < len ? rx[m] : zero);
+            if (id < XT) {
+                const bf16x8 v = as_bf16x8(t < len ? rx[m] : zero);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) Xt[(8 * c8 + j) * QP + t] = v[j];
+                for (int j = 0; j < 8; ++j) Xt[(8 * c8 + j) * QP + t] = v[j];
+            }
         }
     };
 
@@ -650,18 +661,16 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
         //         accumulator order (lane l holds rows 4(l/16)+i, column l%16); the costly
         //         diagonal tiles first, one per wave
         constexpr int NTILES = NT * (NT + 1) / 2;
-        for (int ord = wave; FULL && ord < NTILES; ord += kWaves) {
-            int tb, sb;
-            if (ord < NT) {
-                tb = sb = ord;
-            } else {
-                const int o = ord - NT;
-                tb = 1;
-                while (offdiag_index(tb + 1, 0) <= o) ++tb;
-                sb = o - offdiag_index(tb, 0);
-            }
+        // items: the two state-dimension halves of every diagonal tile (costly: one wave each),
+        // then the off-diagonal tiles
+        for (int item = wave; FULL && item < 2 * NT + L::NOFF; item += kWaves) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (sb < tb) {
+            float* dst;
+            if (item >= 2 * NT) {
+                const int o = item - 2 * NT;
+                int tb = 1;
+                while (offdiag_index(tb + 1, 0) <= o) ++tb;
+                const int sb = o - offdiag_index(tb, 0);
                 const float* bet = beta + offdiag_index(tb, sb) * N;
                 const int s = 16 * sb + l16, t = 16 * tb + l16;
 #pragma unroll
@@ -674,20 +683,23 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
                     const uint4 cv = scale_vec(ld16(Cf + t * NP + k0), bf, __bf16());
                     acc = mfma_bf16(as_bf16x8(av), as_bf16x8(cv), acc);
                 }
+                dst = Sl + tile_index(tb, sb) * 256;
             } else {
-                // exact: S^T[s][t] = sum_n B_sn C_tn exp(cum_tn - cum_sn) for s <= t
+                // exact: S^T[s][t] = sum_n B_sn C_tn exp(cum_tn - cum_sn) for s <= t, over this
+                // item's half of the state dimensions
+                const int tb = item % NT, nh = item / NT;
                 const int t = 16 * tb + l16;
                 bool causal[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) causal[i] = 4 * lg + i <= l16;
 #pragma unroll 4
-                for (int n = 0; n < N; n += 4) {
+                for (int n = nh * (N / 2); n < (nh + 1) * (N / 2); n += 4) {
                     const f32x4 ct = *reinterpret_cast<const f32x4*>(cum + t * CS + n);
                     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                     const bf16x4 cr = *reinterpret_cast<const bf16x4*>(Craw + t * NP + n);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int s = 16 * sb + 4 * lg + i;
+                        const int s = 16 * tb + 4 * lg + i;
                         const f32x4 cs = *reinterpret_cast<const f32x4*>(cum + s * CS + n);
                         const bf16x4 br = *reinterpret_cast<const bf16x4*>(Braw + s * NP + n);
                         float sum = 0.f;
@@ -697,48 +709,56 @@ __global__ void __launch_bounds__(kThreads) walk_diag_pipe_kernel(WalkParams prm
                         acc[i] += causal[i] ? sum : 0.f;
                     }
                 }
+                dst = Sl + (nh == 0 ? tile_index(tb, tb) : NTILES + tb) * 256;
             }
-            *reinterpret_cast<f32x4*>(Sl + tile_index(tb, sb) * 256 + lane * 4) = acc;
+            *reinterpret_cast<f32x4*>(dst + lane * 4) = acc;
         }
         __syncthreads();
 
-        // ---- 4. outputs: carried state (C o exp(cum)) H_{k-1}, plus masked scores times x
-        for (int tb = wave; FULL && tb < NT; tb += kWaves) {
+        // ---- 4. outputs: carried state (C o exp(cum)) H_{k-1}, plus masked scores times x;
+        //         two waves per 16-token block, each with half of the head dimension
+        for (int item = wave; FULL && item < 2 * NT; item += kWaves) {
+            constexpr int PH = PB / 2;
+            const int tb = item % NT, pb0 = (item / NT) * PH;
             const int tl = 16 * tb + l16;
-            f32x4 acc[PB];
+            f32x4 acc[PH];
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < PH; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < N / 32; ++kb) {
                 const uint4 cv = ld16(Cc + tl * NP + 32 * kb + 8 * lg);
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb)
-                    acc[pb] = mfma_bf16(as_bf16x8(ld16(Ht + (16 * pb + l16) * NP + 32 * kb + 8 * lg)), as_bf16x8(cv),
-                                        acc[pb]);
+                for (int q = 0; q < PH; ++q)
+                    acc[q] = mfma_bf16(as_bf16x8(ld16(Ht + (16 * (pb0 + q) + l16) * NP + 32 * kb + 8 * lg)),
+                                       as_bf16x8(cv), acc[q]);
             }
+            auto tile = [&](int sb) -> f32x4 {
+                f32x4 m = *reinterpret_cast<const f32x4*>(Sl + tile_index(tb, sb) * 256 + lane * 4);
+                if (sb == tb) m += *reinterpret_cast<const f32x4*>(Sl + (NTILES + tb) * 256 + lane * 4);
+                return m;
+            };
             for (int k = 0; 2 * k <= tb; ++k) {
-                const f32x4 m0 = *reinterpret_cast<const f32x4*>(Sl + tile_index(tb, 2 * k) * 256 + lane * 4);
-                const f32x4 m1 = (2 * k + 1 <= tb)
-                                     ? *reinterpret_cast<const f32x4*>(Sl + tile_index(tb, 2 * k + 1) * 256 + lane * 4)
-                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 m0 = tile(2 * k);
+                const f32x4 m1 = (2 * k + 1 <= tb) ? tile(2 * k + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
                 const bf16x8 bop = {(__bf16)m0[0], (__bf16)m0[1], (__bf16)m0[2], (__bf16)m0[3],
                                     (__bf16)m1[0], (__bf16)m1[1], (__bf16)m1[2], (__bf16)m1[3]};
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const __bf16* xr = Xt + (16 * pb + l16) * QP + 32 * k + 4 * lg;
+                for (int q = 0; q < PH; ++q) {
+                    const __bf16* xr = Xt + (16 * (pb0 + q) + l16) * QP + 32 * k + 4 * lg;
                     const uint2 lo = ld8(xr), hi = ld8(xr + 16);
                     const uint4 a = {lo.x, lo.y, hi.x, hi.y};
-                    acc[pb] = mfma_bf16(as_bf16x8(a), bop, acc[pb]);
+                    acc[q] = mfma_bf16(as_bf16x8(a), bop, acc[q]);
                 }
             }
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
+            for (int q = 0; q < PH; ++q)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[pb][i] += dskip * (float)Xt[(16 * pb + 4 * lg + i) * QP + tl];
+                for (int i = 0; i < 4; ++i) acc[q][i] += dskip * (float)Xt[(16 * (pb0 + q) + 4 * lg + i) * QP + tl];
             if (tl < len) {
                 __bf16* yr = yg + ((b * Tn + t0 + tl) * H + h) * P + 4 * lg;
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) store4(yr + 16 * pb, acc[pb][0], acc[pb][1], acc[pb][2], acc[pb][3]);
+                for (int q = 0; q < PH; ++q)
+                    store4(yr + 16 * (pb0 + q), acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
             }
         }
 
@@ -875,16 +895,16 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
     int ev = 0;
     if (sl.nseg > 1) {
         if (!record_event(fl, ev++, stream)) return -1;
-        hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, false>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds,
-                           stream, wp);
+        hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, false>), dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads),
+                           lds, stream, wp);
         if (hipGetLastError() != hipSuccess) return -1;
         if (!record_event(fl, ev++, stream)) return -1;
         if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1, stream) != 0)
             return -1;
     }
     if (!record_event(fl, ev++, stream)) return -1;
-    hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, true>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream,
-                       wp);
+    hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, true>), dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
+                       stream, wp);
     if (hipGetLastError() != hipSuccess) return -1;
     if (!record_event(fl, ev++, stream)) return -1;
     if (fl.n_launches) *fl.n_launches = ev - 1;
