@@ -91,15 +91,16 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def fast_segments(cfg):
-    """Segments the library splits each (batch, head) sequence into on its bf16 fast path
-    (mirrors its workspace layout: about 256 workgroups, at least 4 chunks per segment)."""
+def fast_segments(cfg, target=512):
+    """Segments the library splits each (batch, head) sequence into (mirrors its workspace
+    layout: only with at most 128 units; about `target` workgroups -- 512 on the scalar fast
+    path, 256 on the diagonal one -- and at least 4 chunks per segment)."""
     q = min(cfg["chunk"], 128)
     units = cfg["batch"] * cfg["nheads"]
     nch = -(-cfg["seqlen"] // q)
     nseg = 1
     if units > 0 and units * 2 <= 256 and nch >= 8:
-        nseg = min(256 // units, nch // 4)
+        nseg = min(target // units, nch // 4)
     per = -(-nch // nseg)
     return -(-nch // per)
 
@@ -109,7 +110,7 @@ def kernel_names(cfg):
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
     if cfg["decay"] == "diag":
         if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
-            if fast_segments(dict(cfg, chunk=64)) > 1:
+            if fast_segments(dict(cfg, chunk=64), 256) > 1:
                 return ["walk_diag_pipe_kernel<%d,%d,state>" % (N, P), "seg_prefix_kernel",
                         "walk_diag_pipe_kernel<%d,%d>" % (N, P)]
             return ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]

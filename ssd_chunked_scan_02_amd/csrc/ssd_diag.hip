@@ -852,7 +852,7 @@ struct DiagSegLayout {
 DiagSegLayout diag_seg_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P) {
     DiagSegLayout l;
     const int64_t units = batch * nheads, nchunks = (seqlen + kDiagQ - 1) / kDiagQ;
-    l.nseg = walk_segments(units, nchunks, &l.seg_chunks);
+    l.nseg = walk_segments(units, nchunks, 256, &l.seg_chunks);
     l.state = l.init = l.decay = l.total = 0;
     if (l.nseg > 1) {
         const size_t st = (size_t)l.nseg * units * N * P * 4;
@@ -895,8 +895,12 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
     int ev = 0;
     if (sl.nseg > 1) {
         if (!record_event(fl, ev++, stream)) return -1;
-        hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, false>), dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads),
-                           lds, stream, wp);
+        // (the last segment's local state is never needed: only segments 0 .. nseg-2)
+        WalkParams sp = wp;
+        sp.per_xcd = ((sl.nseg - 1) * units + 7) / 8;
+        sp.nseg = sl.nseg - 1;
+        hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, false>), dim3((unsigned)(8 * sp.per_xcd)), dim3(kDiagThreads),
+                           lds, stream, sp);
         if (hipGetLastError() != hipSuccess) return -1;
         if (!record_event(fl, ev++, stream)) return -1;
         if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1, stream) != 0)

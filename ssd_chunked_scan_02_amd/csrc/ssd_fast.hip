@@ -210,6 +210,7 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
 // Global addresses are a wave-uniform 64-bit base per chunk plus a 32-bit per-lane byte
 // offset (the host only takes this path when every offset inside a chunk fits).
 constexpr int kWalkWaves = 8;
+constexpr int64_t kSegTarget = 512;  // workgroups of a segmented fast walk (two rounds per CU)
 constexpr int kWalkThreads = kWalkWaves * kWave;
 
 // 16-token block handled by output wave `ow` in its r-th round (snake order balances the
@@ -739,7 +740,7 @@ struct StateLds {
 template <int N, int Q>
 __global__ void __launch_bounds__(kThreads) walk_state_kernel(Walk2Params prm) {
     const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
-    if (work < 0) return;
+    if (work < 0 || work >= (prm.nseg - 1) * prm.batch * prm.nheads) return;
     const WalkSpan span = walk_span(prm, work);
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -787,7 +788,9 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
     l.nchunks = (seqlen + Q - 1) / Q;
     l.nblk = batch * ngroups * l.nchunks;
     l.units = batch * nheads;
-    l.nseg = walk_segments(l.units, l.nchunks, &l.seg_chunks);
+    // Two rounds of workgroups per CU for the walk: its time is the same as with one round of
+    // twice-longer segments, while the state-only pass (3 workgroups fit per CU) gets shorter.
+    l.nseg = walk_segments(l.units, l.nchunks, kSegTarget, &l.seg_chunks);
     size_t off = 0;
     l.pairs = off; off += (size_t)l.nblk * n_pairs(Q / 16) * 1024;
     l.bt = off; off += (size_t)l.nblk * N * Q * 2;
@@ -834,8 +837,12 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
                    reinterpret_cast<float*>(ws + lay.seg_decay)};
     if (lay.nseg > 1) {
         if (!record_event(fl, ev++, stream)) return -1;
-        hipLaunchKernelGGL((walk_state_kernel<N, Q>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), slds, stream,
-                           wp);
+        // (the last segment's local state is never needed: only segments 0 .. nseg-2)
+        const int64_t state_work = (lay.nseg - 1) * lay.units;
+        Walk2Params sp = wp;
+        sp.per_xcd = (state_work + 7) / 8;
+        hipLaunchKernelGGL((walk_state_kernel<N, Q>), dim3((unsigned)(8 * sp.per_xcd)), dim3(kThreads), slds, stream,
+                           sp);
         if (hipGetLastError() != hipSuccess) return -1;
         if (!record_event(fl, ev++, stream)) return -1;
         if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, lay.units, N, kP, lay.nseg, 0,
@@ -896,7 +903,8 @@ __global__ void __launch_bounds__(kThreads) seg_prefix_kernel(const float* init,
     float hcur = init ? init[e] : 0.f;
     for (int s = 0; s < nseg; ++s) {
         seg_init[s * units * epu + e] = hcur;
-        hcur = exp2f(seg_decay[s * units * dstride + didx]) * hcur + seg_state[s * units * epu + e];
+        if (s + 1 < nseg)
+            hcur = exp2f(seg_decay[s * units * dstride + didx]) * hcur + seg_state[s * units * epu + e];
     }
 }
 

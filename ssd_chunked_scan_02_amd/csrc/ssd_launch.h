@@ -129,14 +129,15 @@ int launch_step(const StepParams& sp, int dtype, int64_t units, hipStream_t stre
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-// Segmented walks: with few (batch, head) units on a long sequence, each sequence is split into
-// segments of at least 4 chunks so that about 256 workgroups walk at once.  Returns the number
-// of segments and sets *seg_chunks (chunks per segment; the last segment may be shorter).
-inline int walk_segments(int64_t units, int64_t nchunks, int* seg_chunks) {
-    constexpr int64_t kTarget = 256, kMinChunks = 4;
+// Segmented walks: with few (batch, head) units on a long sequence (at most half as many as the
+// 256 CUs), each sequence is split into segments of at least 4 chunks so that about `target`
+// workgroups walk (one per CU per round).  Returns the number of segments and sets *seg_chunks
+// (chunks per segment; the last segment may be shorter).
+inline int walk_segments(int64_t units, int64_t nchunks, int64_t target, int* seg_chunks) {
+    constexpr int64_t kMinChunks = 4, kCUs = 256;
     int64_t nseg = 1;
-    if (units > 0 && units * 2 <= kTarget && nchunks >= 2 * kMinChunks)
-        nseg = (kTarget / units < nchunks / kMinChunks) ? kTarget / units : nchunks / kMinChunks;
+    if (units > 0 && units * 2 <= kCUs && nchunks >= 2 * kMinChunks)
+        nseg = (target / units < nchunks / kMinChunks) ? target / units : nchunks / kMinChunks;
     const int64_t per = (nchunks + nseg - 1) / nseg;
     *seg_chunks = (int)(per > 0 ? per : 1);
     return (int)(per > 0 ? (nchunks + per - 1) / per : 1);
