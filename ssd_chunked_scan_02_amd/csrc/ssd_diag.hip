@@ -423,6 +423,9 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
 // to N + 4 floats so that 16 rows read at once fall on distinct banks.
 constexpr int kDiagQ = 64;
 constexpr int kDiagWaves = 8;
+// largest decay (natural log) inside one 16-token block that a diagonal score tile still splits
+// into two factors: exp(kSplitMax) and exp(-kSplitMax) are far inside the fp32 and bf16 ranges
+constexpr float kSplitMax = 64.f;
 constexpr int kDiagThreads = kDiagWaves * kWave;
 
 template <int N, int P>
@@ -685,28 +688,70 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 }
                 dst = Sl + tile_index(tb, sb) * 256;
             } else {
-                // exact: S^T[s][t] = sum_n B_sn C_tn exp(cum_tn - cum_sn) for s <= t, over this
-                // item's half of the state dimensions
-                const int tb = item % NT, nh = item / NT;
-                const int t = 16 * tb + l16;
+                // Diagonal tile, S^T[s][t] = sum_n B_sn C_tn exp(cum_tn - cum_sn) for s <= t.  For
+                // a state dimension whose decay inside the block stays below e^kSplitMax, the
+                // exponential splits at the block start a into exp(cum_tn - cum_an) <= 1 and
+                // exp(cum_an - cum_sn) <= e^kSplitMax, and the sum over those dimensions is one
+                // MFMA contraction (wave nh = 0); the other dimensions take exact exponentials,
+                // split over the two waves by halves of the state dimension.
+                const int tb = item % NT, nh = item / NT, a = 16 * tb;
+                const int t = a + l16;
                 bool causal[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) causal[i] = 4 * lg + i <= l16;
-#pragma unroll 4
-                for (int n = nh * (N / 2); n < (nh + 1) * (N / 2); n += 4) {
+                // dimensions too fast to split in this block (bit n)
+                uint64_t fast = 0;
+#pragma unroll
+                for (int q = 0; q < (N + kWave - 1) / kWave; ++q) {
+                    const int n = min(q * kWave + lane, N - 1);
+                    const float dec = cum[a * CS + n] - cum[(a + 15) * CS + n];
+                    const uint64_t bits = __ballot(dec > kSplitMax);
+                    fast |= (N >= kWave ? bits : bits & ((1ull << N) - 1)) << (q * kWave);
+                }
+                if (nh == 0) {
+#pragma unroll
+                    for (int kb = 0; kb < N / 32; ++kb) {
+                        const int k0 = 32 * kb + 8 * lg;
+                        const f32x4 ca0 = *reinterpret_cast<const f32x4*>(cum + a * CS + k0);
+                        const f32x4 ca1 = *reinterpret_cast<const f32x4*>(cum + a * CS + k0 + 4);
+                        const f32x4 cs0 = *reinterpret_cast<const f32x4*>(cum + t * CS + k0);
+                        const f32x4 cs1 = *reinterpret_cast<const f32x4*>(cum + t * CS + k0 + 4);
+                        const bf16x8 bv = as_bf16x8(ld16(Braw + t * NP + k0));
+                        const bf16x8 cv = as_bf16x8(ld16(Craw + t * NP + k0));
+                        bf16x8 bo, co;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float ca = j < 4 ? ca0[j] : ca1[j - 4];
+                            const float cl = j < 4 ? cs0[j] : cs1[j - 4];  // cum of this lane's row
+                            const bool split = !((fast >> (k0 + j)) & 1);
+                            bo[j] = (__bf16)(split ? (float)bv[j] * __expf(ca - cl) : 0.f);  // rows s
+                            co[j] = (__bf16)(split ? (float)cv[j] * __expf(cl - ca) : 0.f);  // cols t
+                        }
+                        acc = mfma_bf16(bo, co, acc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = causal[i] ? acc[i] : 0.f;
+                }
+                // exact part: groups of 4 dimensions holding a fast one, alternately to the two waves
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                for (int g4 = nh; g4 < N / 4; g4 += 2) {
+                    const uint32_t gbits = (uint32_t)(fast >> (4 * g4)) & 0xfu;
+                    if (gbits == 0) continue;
+                    const int n = 4 * g4;
                     const f32x4 ct = *reinterpret_cast<const f32x4*>(cum + t * CS + n);
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                     const bf16x4 cr = *reinterpret_cast<const bf16x4*>(Craw + t * NP + n);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int s = 16 * tb + 4 * lg + i;
+                        const int s = a + 4 * lg + i;
                         const f32x4 cs = *reinterpret_cast<const f32x4*>(cum + s * CS + n);
                         const bf16x4 br = *reinterpret_cast<const bf16x4*>(Braw + s * NP + n);
                         float sum = 0.f;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            sum += (float)cr[j] * (float)br[j] * __expf(causal[i] ? ct[j] - cs[j] : 0.f);
-                        acc[i] += causal[i] ? sum : 0.f;
+                        for (int j = 0; j < 4; ++j) {
+                            const bool use = causal[i] && ((gbits >> j) & 1);
+                            sum += use ? (float)cr[j] * (float)br[j] * __expf(ct[j] - cs[j]) : 0.f;
+                        }
+                        acc[i] += sum;
                     }
                 }
                 dst = Sl + (nh == 0 ? tile_index(tb, tb) : NTILES + tb) * 256;
