@@ -93,8 +93,8 @@ def kernel_source_hash():
 
 def fast_segments(cfg, target=512):
     """Segments the library splits each (batch, head) sequence into (mirrors its workspace
-    layout: only with at most 128 units; about `target` workgroups -- 512 on the scalar fast
-    path, 256 on the diagonal one -- and at least 4 chunks per segment)."""
+    layout: only with at most 128 units; about `target` (512) workgroups and at least 4 chunks
+    per segment)."""
     q = min(cfg["chunk"], 128)
     units = cfg["batch"] * cfg["nheads"]
     nch = -(-cfg["seqlen"] // q)
@@ -110,7 +110,7 @@ def kernel_names(cfg):
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
     if cfg["decay"] == "diag":
         if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
-            if fast_segments(dict(cfg, chunk=64), 256) > 1:
+            if fast_segments(dict(cfg, chunk=64), 512) > 1:
                 return ["walk_diag_pipe_kernel<%d,%d,state>" % (N, P), "seg_prefix_kernel",
                         "walk_diag_pipe_kernel<%d,%d>" % (N, P)]
             return ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]

@@ -428,26 +428,29 @@ constexpr int kDiagWaves = 8;
 constexpr float kSplitMax = 64.f;
 constexpr int kDiagThreads = kDiagWaves * kWave;
 
-template <int N, int P>
+// (FULL = false, the state-only pass, keeps only x^T, (w o B)^T, B, the running sums and the
+// state-row decays: the other buffers have size 0, so three such workgroups fit on a CU)
+template <int N, int P, bool FULL = true>
 struct DiagPipeLayout {
     static constexpr int Q = kDiagQ, NT = Q / 16, QP = Q + 8, NP = N + 8, CS = N + 4;
     static constexpr int NOFF = NT * (NT - 1) / 2;
+    static constexpr size_t F = FULL ? 1 : 0;
     // offsets in bytes
     static constexpr size_t xt = 0;                                   // x^T          [P][QP] bf16
     static constexpr size_t bt = xt + (size_t)P * QP * 2;            // (w o B)^T    [N][QP] bf16
     static constexpr size_t ht = bt + (size_t)N * QP * 2;            // H^T          [P][NP] bf16
-    static constexpr size_t cc = ht + (size_t)P * NP * 2;            // C o exp(cum) [Q][NP] bf16
-    static constexpr size_t cf = cc + (size_t)Q * NP * 2;            // C o f        [Q][NP] bf16
-    static constexpr size_t bu = cf + (size_t)Q * NP * 2;            // B o u        [Q][NP] bf16
-    static constexpr size_t braw = bu + (size_t)Q * NP * 2;          // B            [Q][NP] bf16
+    static constexpr size_t cc = ht + F * P * NP * 2;                // C o exp(cum) [Q][NP] bf16
+    static constexpr size_t cf = cc + F * Q * NP * 2;                // C o f        [Q][NP] bf16
+    static constexpr size_t bu = cf + F * Q * NP * 2;                // B o u        [Q][NP] bf16
+    static constexpr size_t braw = bu + F * Q * NP * 2;              // B            [Q][NP] bf16
     static constexpr size_t craw = braw + (size_t)Q * NP * 2;        // C            [Q][NP] bf16
-    static constexpr size_t cum = craw + (size_t)Q * NP * 2;         // running sums [Q][CS] f32
+    static constexpr size_t cum = craw + F * Q * NP * 2;             // running sums [Q][CS] f32
     static constexpr size_t part = cum + (size_t)Q * CS * 4;         // scan partials [threads/N][N]
     static constexpr size_t beta = part + (size_t)kDiagThreads * 4;  // [NOFF][N]
-    static constexpr size_t el = beta + (size_t)(NOFF + 1) * N * 4;  // [N]
+    static constexpr size_t el = beta + F * (NOFF + 1) * N * 4;      // [N]
     // score tiles [NT(NT+1)/2][256], then the second state-dimension half of each diagonal tile
     static constexpr size_t sl = el + (size_t)N * 4;
-    static constexpr size_t total = sl + (size_t)(NT * (NT + 1) / 2 + NT) * 256 * 4;
+    static constexpr size_t total = sl + F * (NT * (NT + 1) / 2 + NT) * 256 * 4;
 };
 
 // FULL: the walk.  !FULL: the state-only pass of a segmented walk (H over the segment from a
@@ -455,7 +458,7 @@ struct DiagPipeLayout {
 template <int N, int P, bool FULL>
 __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams prm) {
     constexpr int kThreads = kDiagThreads, kWaves = kDiagWaves;  // (this kernel's own workgroup)
-    using L = DiagPipeLayout<N, P>;
+    using L = DiagPipeLayout<N, P, FULL>;
     constexpr int Q = L::Q, NT = L::NT, QP = L::QP, NP = L::NP, CS = L::CS;
     constexpr int PB = P / 16, NB = N / 16, NTILE = NB * PB, TPW = (NTILE + kWaves - 1) / kWaves;
     // 16-byte pieces per chunk of log a, of B (and of C) and of x, and per thread (rounded up;
@@ -518,7 +521,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             const int64_t off = ((b * Tn + t0 + t) * G + g) * N + 8 * c8;
             if (id < BCT) {
                 rb[m] = ld16(Bg + off);
-                rc[m] = ld16(Cg + off);
+                if (FULL) rc[m] = ld16(Cg + off);
             }
         }
 #pragma unroll
@@ -539,7 +542,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             const int id = tid + kThreads * m, t = id / (N / 8), c8 = id % (N / 8);
             if (id < BCT) {
                 st16(Braw + t * NP + 8 * c8, t < len ? rb[m] : zero);
-                st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
+                if (FULL) st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
             }
         }
 #pragma unroll
@@ -897,7 +900,9 @@ struct DiagSegLayout {
 DiagSegLayout diag_seg_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P) {
     DiagSegLayout l;
     const int64_t units = batch * nheads, nchunks = (seqlen + kDiagQ - 1) / kDiagQ;
-    l.nseg = walk_segments(units, nchunks, 256, &l.seg_chunks);
+    // two rounds of walk workgroups (one per CU each): the walk takes as long as one round of
+    // twice-longer segments, while the state-only pass (three per CU) gets shorter
+    l.nseg = walk_segments(units, nchunks, 512, &l.seg_chunks);
     l.state = l.init = l.decay = l.total = 0;
     if (l.nseg > 1) {
         const size_t st = (size_t)l.nseg * units * N * P * 4;
@@ -936,7 +941,7 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.init) : nullptr,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.state) : nullptr,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.decay) : nullptr};
-    const size_t lds = DiagPipeLayout<N, P>::total;
+    const size_t lds = DiagPipeLayout<N, P, true>::total, slds = DiagPipeLayout<N, P, false>::total;
     int ev = 0;
     if (sl.nseg > 1) {
         if (!record_event(fl, ev++, stream)) return -1;
@@ -945,7 +950,7 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
         sp.per_xcd = ((sl.nseg - 1) * units + 7) / 8;
         sp.nseg = sl.nseg - 1;
         hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, false>), dim3((unsigned)(8 * sp.per_xcd)), dim3(kDiagThreads),
-                           lds, stream, sp);
+                           slds, stream, sp);
         if (hipGetLastError() != hipSuccess) return -1;
         if (!record_event(fl, ev++, stream)) return -1;
         if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1, stream) != 0)
