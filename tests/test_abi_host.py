@@ -81,6 +81,22 @@ def test_workspace_bytes(lib):
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(nheads=5, ngroups=2), 64) == 0
 
 
+def test_fast_path_limits(lib):
+    """Shapes whose in-chunk byte offsets would not fit in 32 bits, or with more heads per group
+    than the prep kernel moves, leave the bf16 fast path for the generic one (whose workspace is
+    the fp32 score tiles alone)."""
+    tiles = lambda nblk, Q: nblk * (Q // 16) * (Q // 16 + 1) // 2 * 1024
+    # 8 heads per group, d_state 128: one token of x and B, C spans (64 + 128 / 8) * 2 = 160
+    # bytes per head, so a 128-token chunk passes 2^31 bytes from 104858 heads on
+    for nheads, fast in ((104864, False), (104848, True)):
+        d = mamba2_dims(batch=1, seqlen=128, nheads=nheads, ngroups=nheads // 8)
+        assert (ssd.ssd_forward_workspace_bytes(d, 128) != tiles(nheads // 8, 128)) == fast
+    # the prep kernel moves log a for at most 64 heads per group at 128-token chunks
+    for nheads, fast in ((65, False), (64, True)):
+        d = mamba2_dims(batch=1, seqlen=128, nheads=nheads, ngroups=1)
+        assert (ssd.ssd_forward_workspace_bytes(d, 128) != tiles(1, 128)) == fast
+
+
 def test_diag_shapes_supported_and_not(lib):
     d = mamba2_dims(decay=1, dstate=64)
     assert call_forward(lib, d, chunk=128) == ssd.SSD_ERR_UNSUPPORTED      # diag chunk <= 64

@@ -74,6 +74,13 @@ def test_state_and_head_dims(dtype, N, P):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_one_head_per_group(dtype):
+    """H = G: every head has its own B and C (no sharing of the score tiles)."""
+    cfg = ssd_inputs.config("mamba2_layer", batch=2, seqlen=333, nheads=3, ngroups=3, dtype=dtype, init=True)
+    _run(cfg, 61, "H=G %s" % dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_no_skip_term(dtype):
     """D absent: the whole output is the SSD part, so no skip term can mask an error."""
     cfg = ssd_inputs.config("mamba2_layer", batch=2, seqlen=400, nheads=3, dtype=dtype, skip=False)
