@@ -97,14 +97,17 @@ int ssd_forward(const ssd_dims* dims, const void* x, const float* log_a, const v
                 float* final_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * ssd_forward, and in addition records caller-created hipEvent_t handles (passed as opaque
- * pointers) on `stream` around its kernel launches, for timing each kernel live:
- * events[k] is recorded right before launch k and events[L] right after the last of the L
- * launches the call makes; handles past index L are left untouched, and NULL handles are
- * skipped.  *n_launches (a HOST pointer, may be NULL) receives L (L <= SSD_MAX_LAUNCHES).
- * With events non-NULL, n_events must be at least SSD_MAX_LAUNCHES + 1, else the call fails
- * with SSD_ERR_INVALID before doing anything.  Launch order of the scalar-decay path:
- * 0 = score tiles C B^T, 1 = chunk walk (state and outputs).
+ * ssd_forward, and in addition has each of its kernel launches stamp caller-created
+ * hipEvent_t handles (passed as opaque pointers), for timing each kernel live: launch k
+ * records events[2k] when its dispatch starts and events[2k+1] when it ends (the stamps are
+ * taken by the dispatch itself, so no extra packets sit between the kernels), and
+ * hipEventElapsedTime(events[2k], events[2k+1]) is that kernel's run time.  Handles past
+ * index 2L - 1 are left untouched; a NULL pair leaves that launch untimed.  *n_launches (a
+ * HOST pointer, may be NULL) receives the number L of launches (L <= SSD_MAX_LAUNCHES).
+ * With events non-NULL, n_events must be at least 2 * SSD_MAX_LAUNCHES, else the call fails
+ * with SSD_ERR_INVALID before doing anything.  Launch order of the bf16 scalar-decay path:
+ * prep (score tiles C B^T and operand layouts), then for a segmented walk the state-only
+ * pass and the segment prefix, then the chunk walk (states and outputs).
  */
 #define SSD_MAX_LAUNCHES 4
 int ssd_forward_profiled(const ssd_dims* dims, const void* x, const float* log_a, const void* B,

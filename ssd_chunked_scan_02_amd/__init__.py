@@ -138,8 +138,9 @@ def ssd_forward(x, log_a, B, C, D=None, chunk: int = 64, init_state=None, y=None
 
 def ssd_forward_profiled(x, log_a, B, C, D=None, chunk: int = 64, init_state=None, y=None,
                          final_state=None, workspace=None, stream=None, events=()):
-    """``ssd_forward_profiled``: as ssd_forward, recording the given hipEvent_t handles
-    (integers) around the kernel launches.  Returns (y, final_state, n_launches)."""
+    """``ssd_forward_profiled``: as ssd_forward; launch k stamps the hipEvent_t handles
+    (integers) events[2k] at its start and events[2k+1] at its end.
+    Returns (y, final_state, n_launches)."""
     return _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, stream,
                     events=list(events))
 
@@ -177,7 +178,7 @@ def _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, st
         rc = lib.ssd_forward(*args)
         launches = None
     else:
-        n = max(len(events), SSD_MAX_LAUNCHES + 1)
+        n = max(len(events), 2 * SSD_MAX_LAUNCHES)
         arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
         count = ctypes.c_int(0)
         rc = lib.ssd_forward_profiled(*args, arr, n, ctypes.byref(count))

@@ -85,7 +85,7 @@ int ssd_forward_profiled(const ssd_dims* d, const void* x, const float* log_a, c
                          void* y, float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream, void* const* events, int n_events, int* n_launches) {
     if (n_launches) *n_launches = 0;
-    if (events && n_events < SSD_MAX_LAUNCHES + 1) return SSD_ERR_INVALID;
+    if (events && n_events < 2 * SSD_MAX_LAUNCHES) return SSD_ERR_INVALID;
     int rc = check_forward(d, chunk);
     if (rc != SSD_OK) return rc;
     const bool has_tokens = d->batch > 0 && d->seqlen > 0;

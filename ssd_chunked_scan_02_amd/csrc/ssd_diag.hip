@@ -866,12 +866,10 @@ int launch_diag_t(const ForwardLaunch& fl, hipStream_t stream) {
     WalkParams wp{fl.x, fl.log_a, fl.Bm, fl.Cm, fl.D, nullptr, fl.init, fl.y, fl.final_state,
                   fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.chunk, fl.nchunks, per_xcd};
     const size_t lds = DiagLayout<T, N, P>(fl.chunk).total;
-    if (!record_event(fl, 0, stream)) return -1;
-    hipLaunchKernelGGL((walk_diag_kernel<T, N, P>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp);
-    if (hipGetLastError() != hipSuccess) return -1;
-    if (!record_event(fl, 1, stream)) return -1;
-    if (fl.n_launches) *fl.n_launches = 1;
-    return 0;
+    int k = 0;
+    return launch_k(fl, k, walk_diag_kernel<T, N, P>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp)
+               ? 0
+               : -1;
 }
 
 #define SSD_DIAG_SHAPES(X)                                                                         \
@@ -942,27 +940,23 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.state) : nullptr,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.decay) : nullptr};
     const size_t lds = DiagPipeLayout<N, P, true>::total, slds = DiagPipeLayout<N, P, false>::total;
-    int ev = 0;
+    int k = 0;
     if (sl.nseg > 1) {
-        if (!record_event(fl, ev++, stream)) return -1;
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         WalkParams sp = wp;
         sp.per_xcd = ((sl.nseg - 1) * units + 7) / 8;
         sp.nseg = sl.nseg - 1;
-        hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, false>), dim3((unsigned)(8 * sp.per_xcd)), dim3(kDiagThreads),
-                           slds, stream, sp);
-        if (hipGetLastError() != hipSuccess) return -1;
-        if (!record_event(fl, ev++, stream)) return -1;
-        if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1, stream) != 0)
+        if (!launch_k(fl, k, walk_diag_pipe_kernel<N, P, false>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kDiagThreads),
+                      slds, stream, sp))
+            return -1;
+        if (launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1,
+                              stream) != 0)
             return -1;
     }
-    if (!record_event(fl, ev++, stream)) return -1;
-    hipLaunchKernelGGL((walk_diag_pipe_kernel<N, P, true>), dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
-                       stream, wp);
-    if (hipGetLastError() != hipSuccess) return -1;
-    if (!record_event(fl, ev++, stream)) return -1;
-    if (fl.n_launches) *fl.n_launches = ev - 1;
-    return 0;
+    return launch_k(fl, k, walk_diag_pipe_kernel<N, P, true>, dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
+                    stream, wp)
+               ? 0
+               : -1;
 }
 
 size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk) {

@@ -820,13 +820,10 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.seqlen, fl.nheads, fl.ngroups, nch};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q>), walk_attr)) return -1;
-    int ev = 0;
-    if (!record_event(fl, ev++, stream)) return -1;
-    // (sizes computed first: template commas cannot sit inside the launch macro)
+    int k = 0;
     const size_t plds = prep_lds<N, Q>(), slds = StateLds<N, Q>::bytes, wlds = WalkShape<N, Q>::lds_bytes;
     const unsigned pthreads = PrepShape<N, Q>::THREADS;
-    hipLaunchKernelGGL((prep_kernel<N, Q>), dim3((unsigned)lay.nblk), dim3(pthreads), plds, stream, pp);
-    if (hipGetLastError() != hipSuccess) return -1;
+    if (!launch_k(fl, k, prep_kernel<N, Q>, dim3((unsigned)lay.nblk), dim3(pthreads), plds, stream, pp)) return -1;
 
     const int64_t work = lay.nseg * lay.units;
     const int64_t per_xcd = (work + 7) / 8;
@@ -836,25 +833,21 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
                    reinterpret_cast<float*>(ws + lay.seg_init), reinterpret_cast<float*>(ws + lay.seg_state),
                    reinterpret_cast<float*>(ws + lay.seg_decay)};
     if (lay.nseg > 1) {
-        if (!record_event(fl, ev++, stream)) return -1;
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         const int64_t state_work = (lay.nseg - 1) * lay.units;
         Walk2Params sp = wp;
         sp.per_xcd = (state_work + 7) / 8;
-        hipLaunchKernelGGL((walk_state_kernel<N, Q>), dim3((unsigned)(8 * sp.per_xcd)), dim3(kThreads), slds, stream,
-                           sp);
-        if (hipGetLastError() != hipSuccess) return -1;
-        if (!record_event(fl, ev++, stream)) return -1;
-        if (launch_seg_prefix(fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, lay.units, N, kP, lay.nseg, 0,
+        if (!launch_k(fl, k, walk_state_kernel<N, Q>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kThreads), slds, stream,
+                      sp))
+            return -1;
+        if (launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, lay.units, N, kP, lay.nseg, 0,
                               stream) != 0)
             return -1;
     }
-    if (!record_event(fl, ev++, stream)) return -1;
-    hipLaunchKernelGGL((walk_fast_kernel<N, Q>), dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream, wp);
-    if (hipGetLastError() != hipSuccess) return -1;
-    if (!record_event(fl, ev++, stream)) return -1;
-    if (fl.n_launches) *fl.n_launches = ev - 1;
-    return 0;
+    return launch_k(fl, k, walk_fast_kernel<N, Q>, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream,
+                    wp)
+               ? 0
+               : -1;
 }
 
 }  // namespace
@@ -908,12 +901,13 @@ __global__ void __launch_bounds__(kThreads) seg_prefix_kernel(const float* init,
     }
 }
 
-int launch_seg_prefix(const float* init, float* seg_init, const float* seg_state, const float* seg_decay,
-                      int64_t units, int N, int P, int nseg, int per_n, hipStream_t stream) {
+int launch_seg_prefix(const ForwardLaunch& fl, int& k, const float* init, float* seg_init, const float* seg_state,
+                      const float* seg_decay, int64_t units, int N, int P, int nseg, int per_n, hipStream_t stream) {
     const int64_t total = units * N * P;
-    hipLaunchKernelGGL(seg_prefix_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, init, seg_init, seg_state, seg_decay, units, N, P, nseg, per_n);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    return launch_k(fl, k, seg_prefix_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                    stream, init, seg_init, seg_state, seg_decay, units, N, P, nseg, per_n)
+               ? 0
+               : -1;
 }
 
 }  // namespace ssd

@@ -400,9 +400,8 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     ScoresParams sp{fl.Bm, fl.Cm, fl.scores, fl.seqlen, fl.ngroups, Q, fl.nchunks};
     const int64_t nscore = fl.batch * fl.ngroups * fl.nchunks;
     (void)ntiles;
-    if (!record_event(fl, 0, stream)) return -1;
-    hipLaunchKernelGGL((scores_kernel<T, N>), dim3((unsigned)nscore), dim3(kThreads), 0, stream, sp);
-    if (hipGetLastError() != hipSuccess) return -1;
+    int k = 0;
+    if (!launch_k(fl, k, scores_kernel<T, N>, dim3((unsigned)nscore), dim3(kThreads), 0, stream, sp)) return -1;
 
     const int64_t units = fl.batch * fl.nheads;
     const int64_t per_xcd = (units + 7) / 8;
@@ -419,12 +418,9 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
             return -1;
         attr_set[dev] = true;
     }
-    if (!record_event(fl, 1, stream)) return -1;
-    hipLaunchKernelGGL((walk_kernel<T, N, P>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp);
-    if (hipGetLastError() != hipSuccess) return -1;
-    if (!record_event(fl, 2, stream)) return -1;
-    if (fl.n_launches) *fl.n_launches = 2;
-    return 0;
+    return launch_k(fl, k, walk_kernel<T, N, P>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp)
+               ? 0
+               : -1;
 }
 
 // The (element type, N, P) instantiations the library ships.
@@ -440,11 +436,6 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     X(float, 256, 16) X(float, 256, 32) X(float, 256, 64)
 
 }  // namespace
-
-bool record_event(const ForwardLaunch& fl, int k, hipStream_t stream) {
-    if (!fl.events || k >= fl.n_events || !fl.events[k]) return true;
-    return hipEventRecord(fl.events[k], stream) == hipSuccess;
-}
 
 bool shape_supported(int dtype, int N, int P) {
 #define SSD_MATCH(TT, NN, PP) \
@@ -472,12 +463,10 @@ int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
         if (fl.final_state) {
             const int64_t n = fl.batch * fl.nheads * fl.dstate * fl.headdim;
             if (n > 0) {
-                if (!record_event(fl, 0, stream)) return -1;
-                hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                                   dim3(kThreads), 0, stream, fl.init, fl.final_state, n);
-                if (hipGetLastError() != hipSuccess) return -1;
-                if (!record_event(fl, 1, stream)) return -1;
-                if (fl.n_launches) *fl.n_launches = 1;
+                int k = 0;
+                if (!launch_k(fl, k, copy_state_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                              dim3(kThreads), 0, stream, fl.init, fl.final_state, n))
+                    return -1;
             }
         }
         return 0;

@@ -2,6 +2,7 @@
 // (ssd_kernels.hip).  Kernel parameter blocks are passed by value.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -101,15 +102,30 @@ struct ForwardLaunch {
     void* y;
     float* final_state;
     float* scores;  // workspace
-    // optional timing events (hipEvent_t): events[k] before launch k, events[L] after the last
+    // optional timing events (hipEvent_t): events[2k] and events[2k+1] take the start and end of
+    // launch k
     hipEvent_t const* events;
     int n_events;
     int* n_launches;
 };
 
 bool shape_supported(int dtype, int N, int P);
-// Records the caller's timing event k (if any) on the stream; false on a HIP error.
-bool record_event(const ForwardLaunch& fl, int k, hipStream_t stream);
+// Launch k of a forward call (k counts up).  With the caller's timing events the dispatch itself
+// stamps events[2k] when it starts and events[2k+1] when it ends (hipExtLaunchKernel), so timing
+// puts no extra packets between dependent kernels.  Updates *fl.n_launches; false on a HIP error.
+template <typename F, typename... Args>
+bool launch_k(const ForwardLaunch& fl, int& k, F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+              Args... args) {
+    hipEvent_t start = nullptr, stop = nullptr;
+    if (fl.events && 2 * k + 1 < fl.n_events) {
+        start = fl.events[2 * k];
+        stop = fl.events[2 * k + 1];
+    }
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, start, stop, 0u, args...);
+    ++k;
+    if (fl.n_launches) *fl.n_launches = k;
+    return hipGetLastError() == hipSuccess;
+}
 // The pipelined bf16 path (ssd_fast.hip) and its workspace.
 bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups);
 size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk);
@@ -119,8 +135,8 @@ size_t diag_lds_bytes(int dtype, int N, int P, int chunk);
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream);
 size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk);
 // Segment prefix of a segmented walk (ssd_fast.hip): per_n = 1 for one decay per state row.
-int launch_seg_prefix(const float* init, float* seg_init, const float* seg_state, const float* seg_decay,
-                      int64_t units, int N, int P, int nseg, int per_n, hipStream_t stream);
+int launch_seg_prefix(const ForwardLaunch& fl, int& k, const float* init, float* seg_init, const float* seg_state,
+                      const float* seg_decay, int64_t units, int N, int P, int nseg, int per_n, hipStream_t stream);
 size_t walk_lds_bytes(int dtype, int N, int P, int chunk);
 size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk);
 // 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.

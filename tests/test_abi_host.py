@@ -180,8 +180,8 @@ def test_step_rejects_bad_arguments(lib):
 
 def test_profiled_forward_rejects_short_event_array(lib):
     d = mamba2_dims()
-    events = (ctypes.c_void_p * 2)(None, None)
+    events = (ctypes.c_void_p * 7)(*([None] * 7))  # one short of 2 * SSD_MAX_LAUNCHES
     n = ctypes.c_int(-1)
     rc = lib.ssd_forward_profiled(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 128, None, FAKE,
-                                  None, FAKE, 1 << 30, None, events, 2, ctypes.byref(n))
+                                  None, FAKE, 1 << 30, None, events, 7, ctypes.byref(n))
     assert rc == ssd.SSD_ERR_INVALID and n.value == 0

@@ -159,6 +159,34 @@ def test_deterministic_and_writes_every_output():
         assert torch.equal(fin, outs[0][1])
 
 
+@pytest.mark.parametrize("over,launches", [(dict(batch=2, seqlen=333, nheads=3), 2),
+                                            (dict(batch=1, seqlen=3000, nheads=2, init=True), 4)],
+                         ids=["whole", "segmented"])
+def test_profiled_forward_times_each_launch(over, launches):
+    """ssd_forward_profiled: every launch stamps its own start/end event pair, the run times are
+    positive, and the outputs are bitwise those of ssd_forward."""
+    import ssd_chunked_scan_02_amd as ssd
+    from bench import HipEvents
+    cfg = ssd_inputs.config("mamba2_layer", **over)
+    g = to_gpu(ssd_inputs.make_inputs(cfg, 37))
+    announce("profiled forward %s" % over)
+    kw = dict(chunk=cfg["chunk"], init_state=g.get("init_state"), final_state=True)
+    y0, f0 = ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g.get("D"), **kw)
+    ev = HipEvents()
+    events = [ev.create() for _ in range(2 * ssd.SSD_MAX_LAUNCHES)]
+    try:
+        y1, f1, n = ssd.ssd_forward_profiled(g["x"], g["log_a"], g["B"], g["C"], g.get("D"),
+                                             events=events, **kw)
+        torch.cuda.synchronize()
+        assert n == launches
+        times = [ev.elapsed_ms(events[2 * k], events[2 * k + 1]) for k in range(n)]
+        assert all(0.0 < t < 1000.0 for t in times), times
+    finally:
+        for e in events:
+            ev.destroy(e)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)) and torch.equal(f0, f1)
+
+
 def test_split_resume_matches_whole():
     """forward(T1) then forward(T2, init = final1) equals forward(T1 + T2) (chunk-aligned and
     not), up to the bf16 rounding of y."""
