@@ -400,6 +400,13 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         for (int k = 0; k < KN; ++k)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) hfa[k][pb] = as_bf16x8(ld16(hcur + (16 * pb + l16) * HS + 32 * k + 8 * lg));
+        // every x operand of the intra-chunk product too, so their LDS latency overlaps the
+        // carried-state MFMAs
+        bf16x8 xall[KDMAX + 1][PB];
+#pragma unroll
+        for (int k = 0; k <= KDMAX; ++k)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) xall[k][pb] = token_frag(xsm, kXStr, 16 * pb, k, lane);
 #pragma unroll
         for (int k = 0; k < KN; ++k)
 #pragma unroll
@@ -418,9 +425,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         // inside the chunk: (S o L) X over the 32-token steps
 #pragma unroll
         for (int k = 0; k <= KDMAX; ++k) {
-            bf16x8 xf[PB];
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb) xf[pb] = token_frag(xsm, kXStr, 16 * pb, k, lane);
+            const bf16x8* xf = xall[k];
 #pragma unroll
             for (int r = 0; r < TBW; ++r) {
                 const int tb = wave_tb(r, OW);
