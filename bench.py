@@ -177,6 +177,59 @@ def cpu_baseline(inp, cfg, min_seconds):
                       % (cfg["batch"], cfg["seqlen"], cfg["nheads"], reps, el)}
 
 
+def time_decode(ssd, cfg, g, stream, ev, dev):
+    """The workload's decode tail: ssd_step for each of its decode tokens, continuing from the
+    forward's final state.  The steps are captured once in a HIP graph (their launches would
+    otherwise be paced by the host) and one replay is timed with events on the launch stream."""
+    import ctypes
+    import torch
+    steps = cfg["decode_steps"]
+    Bsz, H, N, P = cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"]
+    state = g["final"].clone()
+    y_t = torch.empty((Bsz, H, P), dtype=g["x"].dtype, device=dev)
+    sl = [tuple(g[k][:, i].contiguous() for k in ("x_dec", "log_a_dec", "B_dec", "C_dec"))
+          for i in range(steps)]
+    lib = ssd.load_library()
+    dims = ssd.Dims(Bsz, 1, H, cfg["ngroups"], P, N, ssd.SSD_BF16 if cfg["dtype"] == "bf16" else ssd.SSD_F32,
+                    ssd.SSD_DECAY_SCALAR if cfg["decay"] == "scalar" else ssd.SSD_DECAY_DIAG)
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    args = [(ctypes.byref(dims), ssd._ptr(state), *(ssd._ptr(t) for t in s4), ssd._ptr(g.get("D")),
+             ssd._ptr(y_t), ctypes.c_void_p(cap.cuda_stream)) for s4 in sl]
+
+    def run():
+        for a in args:
+            if lib.ssd_step(*a) != 0:
+                raise RuntimeError("ssd_step failed")
+
+    with torch.cuda.stream(cap):
+        run()  # eager once (the library's first call on a device does its set-up outside capture)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    b, e = ev.create(), ev.create()
+    ev.lib.hipEventRecord(b, cap.cuda_stream)
+    graph.replay()
+    ev.lib.hipEventRecord(e, cap.cuda_stream)
+    torch.cuda.synchronize()
+    us = ev.elapsed_ms(b, e) * 1e3 / steps
+    ev.destroy(b)
+    ev.destroy(e)
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    # per step: the fp32 state read and written once, plus x, y, B, C, log a of one token
+    state_bytes = 2 * Bsz * H * N * P * 4
+    io_bytes = Bsz * H * P * esz * 2 + 2 * Bsz * cfg["ngroups"] * N * esz + Bsz * H * 4
+    log("decode: %d steps, %.2f us/step" % (steps, us))
+    # (each (batch, head) state lands on the same XCD every step, so it stays in that XCD's L2:
+    # the effective rate is not bounded by HBM)
+    return {"steps": steps, "us_per_step": us, "timing": "one replay of a HIP graph of all steps",
+            "bytes_per_step": state_bytes + io_bytes,
+            "effective_gbs": (state_bytes + io_bytes) / (us / 1e6) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +374,8 @@ def main():
                      "bytes_per_token": dom_bytes / tokens, "tokens_per_launch": tokens,
                      "forward_bytes_per_token": per_token},
     }
+    if cfg.get("decode_steps", 0) > 0:
+        result["decode"] = time_decode(ssd, cfg, bufs[0], stream, ev, dev)
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle (>= %.0f s)..." % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)

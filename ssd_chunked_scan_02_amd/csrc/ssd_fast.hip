@@ -135,9 +135,11 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
     const int HG = (int)(prm.nheads / prm.ngroups);
     const int nla = HG * (Q / 4);
     const float* lag = prm.log_a + (b * prm.seqlen + t0) * prm.nheads + g * HG;
+    const int wave0 = tid - lane;  // first thread of this wave
     f32x4 lv[kPrepLa];
 #pragma unroll
     for (int i = 0; i < kPrepLa; ++i) {
+        if (wave0 + kPrepThreads * i >= nla) continue;  // (uniform over the wave)
         const int id = min(tid + kPrepThreads * i, nla - 1), hl = id % HG, t4 = 4 * (id / HG);
 #pragma unroll
         for (int j = 0; j < 4; ++j) lv[i][j] = lag[(int64_t)min(t4 + j, len - 1) * prm.nheads + hl];
@@ -148,6 +150,7 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
 #pragma unroll
         for (int i = 0; i < kPrepLa; ++i) {
             const int id = tid + kPrepThreads * i, hl = id % HG, t4 = 4 * (id / HG);
+            if (wave0 + kPrepThreads * i >= nla) continue;
             f32x4 v;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = t4 + j < len ? lv[i][j] : 0.f;

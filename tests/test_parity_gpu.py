@@ -264,3 +264,45 @@ def test_diag_extreme_rates():
     y, fin = gpu_forward(to_gpu(inp), 64, True)
     assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
     compare(inp, y, fin, oracle_forward(inp), "bf16", True, "diag extreme rates")
+
+
+def test_decode_steps_in_a_hip_graph():
+    """ssd_step launches captured in a HIP graph (as the decode timing replays them) give the
+    eager result bitwise, on every one of several replays with eager work in between."""
+    import ssd_chunked_scan_02_amd as ssd
+    cfg = ssd_inputs.config("gqa_decode", batch=2, seqlen=64, nheads=8, ngroups=2, decode_steps=6,
+                            final=True)
+    g = to_gpu(ssd_inputs.make_inputs(cfg, 43))
+    announce("decode steps in a HIP graph")
+    _, s0 = ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g["D"], chunk=cfg["chunk"],
+                            final_state=True)
+    steps = [tuple(g[k][:, i].contiguous() for k in ("x_dec", "log_a_dec", "B_dec", "C_dec"))
+             for i in range(cfg["decode_steps"])]
+    cap = torch.cuda.Stream()
+    state = s0.clone()
+    ys = [torch.empty((2, 8, 64), dtype=torch.bfloat16, device="cuda") for _ in steps]
+
+    def run(st):
+        for (x, la, bb, cc), y in zip(steps, ys):
+            ssd.ssd_step(st, x, la, bb, cc, D=g["D"], y_t=y, stream=cap)
+
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        run(state)
+    torch.cuda.synchronize()
+    want_state, want_y = state.clone(), [y.clone() for y in ys]
+    graph = torch.cuda.CUDAGraph()
+    state.copy_(s0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        run(state)
+    for rep in range(3):
+        state.copy_(s0)
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, want_state), rep
+        for y, w in zip(ys, want_y):
+            assert torch.equal(y.view(torch.int16), w.view(torch.int16)), rep
