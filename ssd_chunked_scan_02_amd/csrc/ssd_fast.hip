@@ -255,6 +255,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
 }
+// 16-byte load through a buffer resource; reads at or past its size return zeros.
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 
 // Orders this wave's LDS writes before its later LDS reads of other lanes' data.
 __device__ __forceinline__ void wave_lds_fence() {
@@ -509,10 +513,8 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     }
 }
 
-// FULL: the state waves of the walk (they also stage everything the output waves read).
-// !FULL: the state-only pass of a segmented walk: H over the segment from a zero state, written
-// to seg_state with the segment's total log2-decay in seg_decay; only w o x and w are staged.
-template <int N, int Q, int SW, bool FULL>
+// The state waves of the walk (they also stage everything the output waves read).
+template <int N, int Q, int SW>
 __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
                                                 int lane) {
     const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
@@ -533,7 +535,6 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     float la[LA];
     uint4 xs[XCH];
     uint4 bt[NBW][KS];
-    float lsum2 = 0.f, seg2 = 0.f;  // log2 decay of the last factored chunk, of the segment so far
     // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
     // quarter of the chunk; rows clamped into the chunk, masked when staged.  Each is loaded
     // a full chunk ahead of its use.
@@ -577,15 +578,11 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
             for (int j = 0; j < LA; ++j) {
                 const int t = lane * LA + j;
-                if (FULL) {
-                    L.cum2(buf)[t] = cum[j];
-                    L.f(buf)[t] = fexp2(cum[j] - blk2);
-                }
+                L.cum2(buf)[t] = cum[j];
+                L.f(buf)[t] = fexp2(cum[j] - blk2);
                 L.w(buf)[t] = fexp2(last2 - cum[j]);
             }
         }
-        lsum2 = last2;
-        if (!FULL) return fexp2(last2);
         // rows SW, SW + 4, ... of U
 #pragma unroll
         for (int tb = SW; tb < NT; tb += 4) {
@@ -615,7 +612,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         for (int m = 0; m < XCH; ++m) {
             const int id = lane + kWave * m, row = QW * SW + id / 8, c16 = id % 8;
             const uint4 raw = row < len ? xs[m] : zero;
-            if (FULL) st16(xsm + row * kXStr + 8 * c16, raw);
+            st16(xsm + row * kXStr + 8 * c16, raw);
             const float w = wrow[row];
             const bf16x8 rv = as_bf16x8(raw);
             bf16x8 sv;
@@ -631,9 +628,8 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb) {
             hs[jn][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const float* init = !FULL ? nullptr
-                                : prm.nseg > 1 ? prm.seg_init + (span.seg * prm.batch * prm.nheads + unit) * N * kP
-                                               : (prm.init ? prm.init + unit * N * kP : nullptr);
+            const float* init = prm.nseg > 1 ? prm.seg_init + (span.seg * prm.batch * prm.nheads + unit) * N * kP
+                                             : (prm.init ? prm.init + unit * N * kP : nullptr);
             if (init) {
                 const int n = 16 * (SW + 4 * jn) + 4 * lg;
                 const float* src = init + n * kP + 16 * pb + l16;
@@ -642,7 +638,6 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             }
         }
     auto write_state = [&](__bf16* hsm) {
-        if (!FULL) return;
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
 #pragma unroll
@@ -656,7 +651,6 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     load_b(c0);
     load_x(c0);
     float el = factors(c0);
-    seg2 += lsum2;
     load_la(min(c0 + 1, c1 - 1));
     stage_x(c0);
     load_x(min(c0 + 1, c1 - 1));
@@ -671,7 +665,6 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         const int cn = min(c + 1, c1 - 1);
         const __bf16* xwm = L.Xw + (c & 1) * Q * kXStr;
         const float el_next = factors(c + 1);
-        if (c + 1 < c1) seg2 += lsum2;
         load_la(min(c + 2, c1 - 1));
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
         // H_k = exp(cum_last) H_{k-1} + B^T (w o X)
@@ -700,9 +693,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         lds_barrier();
     }
 
-    float* fin = !FULL ? prm.seg_state + (span.seg * prm.batch * prm.nheads + unit) * N * kP
-                       : (c1 == prm.nchunks && prm.final_state) ? prm.final_state + unit * N * kP : nullptr;
-    if (!FULL && lane == 0) prm.seg_decay[span.seg * prm.batch * prm.nheads + unit] = seg2;
+    float* fin = (c1 == prm.nchunks && prm.final_state) ? prm.final_state + unit * N * kP : nullptr;
     if (fin) {
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
@@ -730,41 +721,170 @@ __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm
         case 1: walk_output_role<N, Q, 1>(prm, L, span, lane); break;
         case 2: walk_output_role<N, Q, 2>(prm, L, span, lane); break;
         case 3: walk_output_role<N, Q, 3>(prm, L, span, lane); break;
-        case 4: walk_state_role<N, Q, 0, true>(prm, L, span, lane); break;
-        case 5: walk_state_role<N, Q, 1, true>(prm, L, span, lane); break;
-        case 6: walk_state_role<N, Q, 2, true>(prm, L, span, lane); break;
-        default: walk_state_role<N, Q, 3, true>(prm, L, span, lane); break;
+        case 4: walk_state_role<N, Q, 0>(prm, L, span, lane); break;
+        case 5: walk_state_role<N, Q, 1>(prm, L, span, lane); break;
+        case 6: walk_state_role<N, Q, 2>(prm, L, span, lane); break;
+        default: walk_state_role<N, Q, 3>(prm, L, span, lane); break;
     }
 }
 
-// State-only pass of a segmented walk: 4 waves per (segment, batch, head).  Its LDS holds only
-// what those waves use (the factor buffers and w o x); the other views of WalkLds point at the
-// same memory and are never touched when FULL is false.
+// seg_state_kernel: the state-only pass of a segmented walk, shaped for throughput.  One wave
+// per (segment, batch, head) forms the segment's local state (its final state from a zero start)
+// as one sum over the segment's chunks,
+//   H_seg = sum_c B_c^T (W_c o X_c),   W_s = exp(decay from token s to the segment's end),
+// which equals the chunk recurrence H_k = exp(cum_last) H_{k-1} + B^T (w o X) unrolled.  The
+// chunks are taken last to first, so the decay from a chunk's end to the segment's end is the
+// running sum of the chunks already done, W_s <= 1, and the state registers are only ever
+// accumulated into.  The wave holds the whole N x P state and stages W o x of a chunk in an LDS
+// tile of its own, read back as MFMA operands contracting over tokens (no barrier: LDS serves one
+// wave's accesses in order).  Per chunk it issues the B^T operand loads, reads its operands out
+// of the tile, stages the next chunk into the tile while those loads are in flight, prefetches
+// the chunk after that, and then issues the chunk's MFMAs.
 template <int N, int Q>
-struct StateLds {
-    static constexpr size_t bytes = (size_t)2 * Q * kXStr * 2 + (size_t)2 * WalkShape<N, Q>::FSZ * 4;
+struct SegStateShape {
+    static constexpr int NBK = N / 16, KS = Q / 32, PB = kP / 16, LA = Q / 64, XR = Q * kP / 8 / kWave;
+    // the W o x tile [Q][kXStr] bf16, then W [Q] fp32
+    static constexpr size_t lds_bytes = (size_t)Q * kXStr * 2 + (size_t)Q * 4;
 };
 
 template <int N, int Q>
-__global__ void __launch_bounds__(kThreads) walk_state_kernel(Walk2Params prm) {
-    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
-    if (work < 0 || work >= (prm.nseg - 1) * prm.batch * prm.nheads) return;
+__global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
+    using S = SegStateShape<N, Q>;
+    constexpr int NBK = S::NBK, KS = S::KS, PB = S::PB, LA = S::LA, XR = S::XR;
+    constexpr int NBH = NBK / 2;  // B^T operands load in two halves of the state rows
+    const int64_t units = prm.batch * prm.nheads;
+    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, (prm.nseg - 1) * units);
+    if (work < 0) return;
     const WalkSpan span = walk_span(prm, work);
-    const int lane = threadIdx.x % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x;
+    const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
+    const int c0 = span.c0, c1 = span.c1;
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
+    const int nchunks = prm.nchunks;
+    const uint32_t x_row = (uint32_t)(H * kP * 2);
+    const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
+    __bf16* xg = const_cast<__bf16*>(static_cast<const __bf16*>(prm.x));
+    const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * NBK * KS * 512;
     extern __shared__ __align__(16) unsigned char smem[];
-    WalkLds<N, Q> L(smem);
-    L.Xw = reinterpret_cast<__bf16*>(smem);
-    L.Xs = L.Xw;
-    L.Hs = L.Xw;
-    L.Ys = L.Xw;
-    L.Fs = reinterpret_cast<float*>(L.Xw + 2 * Q * kXStr);
-    switch (wave) {
-        case 0: walk_state_role<N, Q, 0, false>(prm, L, span, lane); break;
-        case 1: walk_state_role<N, Q, 1, false>(prm, L, span, lane); break;
-        case 2: walk_state_role<N, Q, 2, false>(prm, L, span, lane); break;
-        default: walk_state_role<N, Q, 3, false>(prm, L, span, lane); break;
+    __bf16* Xw = reinterpret_cast<__bf16*>(smem);
+    // W, permuted so that the XR rows a lane stages (lane / 8 + 8 m) are contiguous
+    float* wv = reinterpret_cast<float*>(smem + (size_t)Q * kXStr * 2);
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
+    // staging piece m of this lane: row lane / 8 + 8 m, bytes 16 (lane % 8) of it
+    const uint32_t xoff = (uint32_t)(lane / 8) * x_row + 16 * (lane % 8);
+
+    float la[LA];
+    uint4 xs[XR];
+    auto load_la = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < LA; ++j) la[j] = la0[(int64_t)c * Q + lane * LA + j];
+    };
+    // x rows of the chunk through a buffer resource ending with it: rows past a short chunk's
+    // end read as zeros
+    auto load_x = [&](int c) {
+        const __amdgpu_buffer_rsrc_t xr =
+            buffer_rsrc(xg + ((b * Tn + (int64_t)c * Q) * H + h) * kP, (uint32_t)chunk_len(c) * x_row);
+#pragma unroll
+        for (int m = 0; m < XR; ++m) xs[m] = buffer_load16(xr, xoff + (uint32_t)(8 * m) * x_row);
+    };
+    // W o x of chunk c into the tile (from la and xs of chunk c), with sfx2 the log2 decay from
+    // the chunk's end to the segment's end; returns the chunk's own log2 decay
+    auto stage = [&](int c, float sfx2) -> float {
+        const int len = chunk_len(c);
+        float cum[LA], run = 0.f;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) { run += (lane * LA + j < len) ? la[j] : 0.f; cum[j] = run; }
+        const float incl = wave_inclusive_sum(run);
+        const float excl = incl - run;
+        const float last2 = lane_value(incl, kWave - 1) * kLog2e;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+            const int t = lane * LA + j;
+            wv[(t % 8) * (Q / 8) + t / 8] = fexp2(sfx2 + (last2 - (excl + cum[j]) * kLog2e));
+        }
+        wave_lds_fence();
+        float w[XR];
+#pragma unroll
+        for (int q = 0; q < XR / 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(wv + (lane / 8) * (Q / 8) + 4 * q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * q + i] = v[i];
+        }
+#pragma unroll
+        for (int m = 0; m < XR; ++m) {
+            const bf16x8 rv = as_bf16x8(xs[m]);
+            bf16x8 sv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sv[j] = (__bf16)((float)rv[j] * w[m]);
+            *reinterpret_cast<bf16x8*>(Xw + (lane / 8 + 8 * m) * kXStr + 8 * (lane % 8)) = sv;
+        }
+        wave_lds_fence();
+        return last2;
+    };
+
+    f32x4 hs[NBK][PB];
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) hs[nb][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // chunks last to first; sfx2 = log2 decay from the end of the chunk being staged to the
+    // segment's end
+    load_la(c1 - 1);
+    load_x(c1 - 1);
+    float sfx2 = stage(c1 - 1, 0.f);
+    load_la(max(c1 - 2, c0));
+    load_x(max(c1 - 2, c0));
+    for (int c = c1 - 1; c >= c0; --c) {
+        const void* bbase = bt0 + (int64_t)c * NBK * KS * 512;
+        uint4 blo[NBH][KS], bhi[NBH][KS];
+#pragma unroll
+        for (int nb = 0; nb < NBH; ++nb)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) blo[nb][k] = ldg16(bbase, 16 * lane + (nb * KS + k) * 1024);
+        bf16x8 xfa[KS][PB];
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) xfa[k][pb] = token_frag(Xw, kXStr, 16 * pb, k, lane);
+        // the chunk before (at the first chunk: a repeat of it that nobody reads)
+        const float d2 = stage(max(c - 1, c0), sfx2);
+        if (c > c0) sfx2 += d2;
+#pragma unroll
+        for (int nb = 0; nb < NBH; ++nb)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) bhi[nb][k] = ldg16(bbase, 16 * lane + ((NBH + nb) * KS + k) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < NBH; ++nb)
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) hs[nb][pb] = mfma_bf16(as_bf16x8(blo[nb][k]), xfa[k][pb], hs[nb][pb]);
+        load_la(max(c - 2, c0));
+        load_x(max(c - 2, c0));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < NBH; ++nb)
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+                    hs[NBH + nb][pb] = mfma_bf16(as_bf16x8(bhi[nb][k]), xfa[k][pb], hs[NBH + nb][pb]);
     }
+
+    const int64_t sidx = span.seg * units + unit;
+    if (lane == 0) prm.seg_decay[sidx] = sfx2;
+    float* fin = prm.seg_state + sidx * N * kP;
+    const int l16 = lane % 16, lg = lane / 16;
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+            float* dst = fin + (16 * nb + 4 * lg) * kP + 16 * pb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i * kP] = hs[nb][pb][i];
+        }
 }
 
 template <int N, int Q>
@@ -797,7 +917,7 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
     l.nblk = batch * ngroups * l.nchunks;
     l.units = batch * nheads;
     // Two rounds of workgroups per CU for the walk: its time is the same as with one round of
-    // twice-longer segments, while the state-only pass (3 workgroups fit per CU) gets shorter.
+    // twice-longer segments, while the state-only pass (one wave per segment) gets shorter.
     l.nseg = walk_segments(l.units, l.nchunks, kSegTarget, &l.seg_chunks);
     size_t off = 0;
     l.pairs = off; off += (size_t)l.nblk * n_pairs(Q / 16) * 1024;
@@ -829,7 +949,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q>), walk_attr)) return -1;
     int k = 0;
-    const size_t plds = prep_lds<N, Q>(), slds = StateLds<N, Q>::bytes, wlds = WalkShape<N, Q>::lds_bytes;
+    const size_t plds = prep_lds<N, Q>(), slds = SegStateShape<N, Q>::lds_bytes, wlds = WalkShape<N, Q>::lds_bytes;
     const unsigned pthreads = PrepShape<N, Q>::THREADS;
     if (!launch_k(fl, k, prep_kernel<N, Q>, dim3((unsigned)lay.nblk), dim3(pthreads), plds, stream, pp)) return -1;
 
@@ -845,8 +965,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
         const int64_t state_work = (lay.nseg - 1) * lay.units;
         Walk2Params sp = wp;
         sp.per_xcd = (state_work + 7) / 8;
-        if (!launch_k(fl, k, walk_state_kernel<N, Q>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kThreads), slds, stream,
-                      sp))
+        if (!launch_k(fl, k, seg_state_kernel<N, Q>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kWave), slds, stream, sp))
             return -1;
         if (launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, lay.units, N, kP, lay.nseg, 0,
                               stream) != 0)
