@@ -728,6 +728,10 @@ __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm
     }
 }
 
+// log2 weight below which exp2 is 0 in fp32 whatever its last-bit error (the smallest denormal
+// is 2^-149)
+constexpr float kVanish2 = -160.f;
+
 // seg_state_kernel: the state-only pass of a segmented walk, shaped for throughput.  One wave
 // per (segment, batch, head) forms the segment's local state (its final state from a zero start)
 // as one sum over the segment's chunks,
@@ -739,7 +743,9 @@ __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm
 // tile of its own, read back as MFMA operands contracting over tokens (no barrier: LDS serves one
 // wave's accesses in order).  Per chunk it issues the B^T operand loads, reads its operands out
 // of the tile, stages the next chunk into the tile while those loads are in flight, prefetches
-// the chunk after that, and then issues the chunk's MFMAs.
+// the chunk after that, and then issues the chunk's MFMAs.  Once the weights of all tokens left
+// are below 2^-160, where exp2 is 0 in fp32, the rest of the segment would add exact zeros: the
+// wave then only sums the remaining chunks' decay, and the result is the same bit for bit.
 template <int N, int Q>
 struct SegStateShape {
     static constexpr int NBK = N / 16, KS = Q / 32, PB = kP / 16, LA = Q / 64, XR = Q * kP / 8 / kWave;
@@ -848,6 +854,7 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) xfa[k][pb] = token_frag(Xw, kXStr, 16 * pb, k, lane);
         // the chunk before (at the first chunk: a repeat of it that nobody reads)
+        const float bound2 = sfx2;  // every token before chunk c weighs at most 2^bound2
         const float d2 = stage(max(c - 1, c0), sfx2);
         if (c > c0) sfx2 += d2;
 #pragma unroll
@@ -871,6 +878,19 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb)
                     hs[NBH + nb][pb] = mfma_bf16(as_bf16x8(bhi[nb][k]), xfa[k][pb], hs[NBH + nb][pb]);
+        if (bound2 < kVanish2) {
+            // The weights of all earlier tokens are 0 in fp32 (exp2 of less than -160), so the
+            // earlier chunks would add exact zeros: only their decay is still summed.
+            for (int cc = c - 2; cc >= c0; --cc) {
+                load_la(cc);
+                const int len = chunk_len(cc);
+                float run = 0.f;
+#pragma unroll
+                for (int j = 0; j < LA; ++j) run += (lane * LA + j < len) ? la[j] : 0.f;
+                sfx2 += lane_value(wave_inclusive_sum(run), kWave - 1) * kLog2e;
+            }
+            break;
+        }
     }
 
     const int64_t sidx = span.seg * units + unit;

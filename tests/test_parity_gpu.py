@@ -46,6 +46,11 @@ SEGMENTED = [
     dict(batch=1, seqlen=3000, nheads=2, chunk=128, init=True),
     dict(batch=2, seqlen=2100, nheads=4, ngroups=2, chunk=64, init=True, skip=False),
     dict(batch=1, seqlen=4100, nheads=1, chunk=256, dstate=64),
+    # slow decay (softplus(dt) ~ 3e-4): every chunk of a segment weighs in the segment state
+    dict(batch=1, seqlen=3000, nheads=2, chunk=128, init=True, dt_mean=-8.0),
+    # fast decay: the segment state pass stops after the last chunk or two, since every earlier
+    # token's weight is 0 in fp32
+    dict(batch=1, seqlen=3000, nheads=2, chunk=128, init=True, dt_mean=2.0),
 ]
 
 
