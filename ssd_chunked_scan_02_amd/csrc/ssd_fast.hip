@@ -80,8 +80,9 @@ __device__ __forceinline__ void unpack8(bf16x8 v, float (&f)[8]) {
 }
 
 // ---------------------------------------------------------------------------------------
-// prep_kernel: one workgroup (8 waves) per (batch, group, chunk).  It reads the chunk's B and
-// C rows once, stages them in LDS (rows past the sequence end as zeros) and writes
+// prep_kernel: per (batch, group, chunk) one workgroup, or two when that many still fit on the
+// CUs in one round (see below).  It reads the chunk's B and C rows once, stages them in LDS (rows
+// past the sequence end as zeros) and writes
 //   pairs[(b,g,c)][pair(tb,k)][lane][8]: S^T[32k + kperm(lg, j)][16 tb + l16] (0 where the
 //       second tile lies above the diagonal), pair(tb,k) = pair_base(tb) + k, 2k <= tb;
 //   ct[(b,g,c)][tb][k][lane][8]: C[16 tb + l16][32k + 8 lg + j]  (the C^T operand);
@@ -96,6 +97,7 @@ template <int N, int Q> struct PrepShape {
 // log a items (head, 4 tokens) per prep thread: heads per group up to kPrepLa * 4 * 512 / chunk
 // (the smallest prep workgroup has 512 threads)
 constexpr int kPrepLa = 4;
+constexpr int64_t kPrepSplitMax = 256;  // prep workgroups one round of the CUs holds
 constexpr int kPrepMinThreads = 512;
 
 template <int N, int Q>
@@ -110,7 +112,14 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
     __bf16* Cs = Bs + Q * NS;                       // [Q][NS]
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane % 16, lg = lane / 16;
-    const int64_t blk = blockIdx.x;
+    // With prm.split, two workgroups per block on the same XCD (workgroup i runs on XCD i % 8),
+    // which shortens the chain each one waits through: part 0 writes the score pairs, part 1 the
+    // C^T and B^T fragments and log a head-major.  Otherwise one workgroup does all of it.
+    const int64_t bid = blockIdx.x;
+    const int part = prm.split ? (int)((bid / 8) % 2) : -1;
+    const int64_t blk = prm.split ? (bid / 16) * 8 + bid % 8 : bid;
+    if (blk >= prm.nblk) return;
+    const bool do_pairs = part != 1, do_rest = part != 0;
     const int c = (int)(blk % prm.nchunks);
     const int64_t bg = blk / prm.nchunks;
     const int64_t b = bg / prm.ngroups, g = bg % prm.ngroups;
@@ -130,31 +139,33 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
         vb[m] = ld16(Bg + off);
         vc[m] = ld16(Cg + off);
     }
-    // log a head-major: item (head, 4 tokens) gathers 4 rows (consecutive threads read
-    // consecutive heads of a row) and writes 16 contiguous bytes; rows clamped, masked below
-    const int HG = (int)(prm.nheads / prm.ngroups);
-    const int nla = HG * (Q / 4);
-    const float* lag = prm.log_a + (b * prm.seqlen + t0) * prm.nheads + g * HG;
-    const int wave0 = tid - lane;  // first thread of this wave
-    f32x4 lv[kPrepLa];
-#pragma unroll
-    for (int i = 0; i < kPrepLa; ++i) {
-        if (wave0 + kPrepThreads * i >= nla) continue;  // (uniform over the wave)
-        const int id = min(tid + kPrepThreads * i, nla - 1), hl = id % HG, t4 = 4 * (id / HG);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) lv[i][j] = lag[(int64_t)min(t4 + j, len - 1) * prm.nheads + hl];
-    }
-    {
-        const int64_t tpad = (int64_t)prm.nchunks * Q;
-        float* dst = prm.la_t + (b * prm.nheads + g * HG) * tpad + t0;
+    if (do_rest) {
+        // log a head-major: item (head, 4 tokens) gathers 4 rows (consecutive threads read
+        // consecutive heads of a row) and writes 16 contiguous bytes; rows clamped, masked below
+        const int HG = (int)(prm.nheads / prm.ngroups);
+        const int nla = HG * (Q / 4);
+        const float* lag = prm.log_a + (b * prm.seqlen + t0) * prm.nheads + g * HG;
+        const int wave0 = tid - lane;  // first thread of this wave
+        f32x4 lv[kPrepLa];
 #pragma unroll
         for (int i = 0; i < kPrepLa; ++i) {
-            const int id = tid + kPrepThreads * i, hl = id % HG, t4 = 4 * (id / HG);
-            if (wave0 + kPrepThreads * i >= nla) continue;
-            f32x4 v;
+            if (wave0 + kPrepThreads * i >= nla) continue;  // (uniform over the wave)
+            const int id = min(tid + kPrepThreads * i, nla - 1), hl = id % HG, t4 = 4 * (id / HG);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = t4 + j < len ? lv[i][j] : 0.f;
-            if (id < nla) *reinterpret_cast<f32x4*>(dst + hl * tpad + t4) = v;
+            for (int j = 0; j < 4; ++j) lv[i][j] = lag[(int64_t)min(t4 + j, len - 1) * prm.nheads + hl];
+        }
+        {
+            const int64_t tpad = (int64_t)prm.nchunks * Q;
+            float* dst = prm.la_t + (b * prm.nheads + g * HG) * tpad + t0;
+#pragma unroll
+            for (int i = 0; i < kPrepLa; ++i) {
+                const int id = tid + kPrepThreads * i, hl = id % HG, t4 = 4 * (id / HG);
+                if (wave0 + kPrepThreads * i >= nla) continue;
+                f32x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = t4 + j < len ? lv[i][j] : 0.f;
+                if (id < nla) *reinterpret_cast<f32x4*>(dst + hl * tpad + t4) = v;
+            }
         }
     }
 #pragma unroll
@@ -165,16 +176,19 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
     }
     __syncthreads();
 
-    __bf16* ct = prm.ct + blk * (int64_t)NT * KN * 512 + lane * 8;
-    for (int f = wave; f < NT * KN; f += kPrepWaves) {
-        const int tb = f / KN, k = f % KN;
-        st16(ct + f * 512, ld16(Cs + (16 * tb + l16) * NS + 32 * k + 8 * lg));
+    if (do_rest) {
+        __bf16* ct = prm.ct + blk * (int64_t)NT * KN * 512 + lane * 8;
+        for (int f = wave; f < NT * KN; f += kPrepWaves) {
+            const int tb = f / KN, k = f % KN;
+            st16(ct + f * 512, ld16(Cs + (16 * tb + l16) * NS + 32 * k + 8 * lg));
+        }
+        __bf16* btf = prm.bt + blk * (int64_t)NB * KS * 512 + lane * 8;
+        for (int f = wave; f < NB * KS; f += kPrepWaves) {
+            const int nb = f / KS, k = f % KS;
+            *reinterpret_cast<bf16x8*>(btf + f * 512) = token_frag(Bs, NS, 16 * nb, k, lane);
+        }
     }
-    __bf16* btf = prm.bt + blk * (int64_t)NB * KS * 512 + lane * 8;
-    for (int f = wave; f < NB * KS; f += kPrepWaves) {
-        const int nb = f / KS, k = f % KS;
-        *reinterpret_cast<bf16x8*>(btf + f * 512) = token_frag(Bs, NS, 16 * nb, k, lane);
-    }
+    if (!do_pairs) return;
     __bf16* pairs = prm.pairs + blk * (int64_t)NPAIR * 512 + lane * 8;
     for (int idx = wave; idx < NPAIR; idx += kPrepWaves) {
         int tb = 0;
@@ -965,13 +979,16 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     __bf16* ct = reinterpret_cast<__bf16*>(ws + lay.ct);
     float* la_t = reinterpret_cast<float*>(ws + lay.la_t);
     const int nch = (int)lay.nchunks;
-    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.seqlen, fl.nheads, fl.ngroups, nch};
+    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q>), walk_attr)) return -1;
     int k = 0;
     const size_t plds = prep_lds<N, Q>(), slds = SegStateShape<N, Q>::lds_bytes, wlds = WalkShape<N, Q>::lds_bytes;
     const unsigned pthreads = PrepShape<N, Q>::THREADS;
-    if (!launch_k(fl, k, prep_kernel<N, Q>, dim3((unsigned)lay.nblk), dim3(pthreads), plds, stream, pp)) return -1;
+    // split each block over two workgroups when even then they fit on the CUs at once
+    pp.split = 2 * lay.nblk <= kPrepSplitMax ? 1 : 0;
+    const unsigned pgrid = pp.split ? (unsigned)((lay.nblk + 7) / 8 * 16) : (unsigned)lay.nblk;
+    if (!launch_k(fl, k, prep_kernel<N, Q>, dim3(pgrid), dim3(pthreads), plds, stream, pp)) return -1;
 
     const int64_t work = lay.nseg * lay.units;
     const int64_t per_xcd = (work + 7) / 8;

@@ -64,6 +64,8 @@ struct PrepParams {
     int64_t nheads;
     int64_t ngroups;
     int nchunks;
+    int64_t nblk;  // batch * ngroups * nchunks
+    int split;     // 1: two workgroups per block (see prep_kernel)
 };
 
 struct Walk2Params {
