@@ -426,6 +426,11 @@ constexpr int kDiagWaves = 8;
 // largest decay (natural log) inside one 16-token block that a diagonal score tile still splits
 // into two factors: exp(kSplitMax) and exp(-kSplitMax) are far inside the fp32 and bf16 ranges
 constexpr float kSplitMax = 64.f;
+constexpr float kLog2eD = 1.4426950408889634f;
+constexpr float kSplitMax2 = kSplitMax * kLog2eD;  // the same bound in log2 units
+// 2^x on the hardware unit (v_exp_f32); results below the normal range are not kept, which only
+// affects factors under 2^-126.
+__device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kDiagThreads = kDiagWaves * kWave;
 
 // (FULL = false, the state-only pass, keeps only x^T, (w o B)^T, B, the running sums and the
@@ -535,7 +540,11 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 #pragma unroll
         for (int m = 0; m < LAI; ++m) {
             const int id = tid + kThreads * m, t = id / (N / 4), c4 = id % (N / 4);
-            if (id < LAT) st16(cum + t * CS + 4 * c4, t < len ? rla[m] : zero);
+            // log a in log2 units, so that every factor below is one exp2
+            if (id < LAT) {
+                const f32x4 v = __builtin_bit_cast(f32x4, rla[m]) * kLog2eD;
+                st16(cum + t * CS + 4 * c4, t < len ? __builtin_bit_cast(uint4, v) : zero);
+            }
         }
 #pragma unroll
         for (int m = 0; m < BCI; ++m) {
@@ -584,7 +593,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         }
     };
 
-    float lsum = 0.f;  // (threads < N) the segment's summed log a of state row tid
+    float lsum = 0.f;  // (threads < N) the segment's summed log2 a of state row tid
     load_chunk(c0);
     write_state_lds();
     stage_chunk(c0);
@@ -616,7 +625,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 
         // ---- 2. factor tables and scaled operands (all from LDS)
         if (tid < N) {
-            el[tid] = __expf(cum[(Q - 1) * CS + tid]);
+            el[tid] = dexp2(cum[(Q - 1) * CS + tid]);
             lsum += cum[(Q - 1) * CS + tid];
         }
         for (int i = tid; FULL && i < L::NOFF * N; i += kThreads) {
@@ -624,7 +633,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             int tb = 1;
             while (offdiag_index(tb + 1, 0) <= p) ++tb;
             const int sb = p - offdiag_index(tb, 0);
-            beta[i] = __expf(cum[(16 * tb) * CS + n] - cum[(16 * sb + 15) * CS + n]);
+            beta[i] = dexp2(cum[(16 * tb) * CS + n] - cum[(16 * sb + 15) * CS + n]);
         }
         for (int item = tid; FULL && item < Q * (N / 8); item += kThreads) {
             const int t = item / (N / 8), c8 = item % (N / 8);
@@ -643,9 +652,9 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 const float ct = j < 4 ? ct0[j] : ct1[j - 4];
                 const float ca = j < 4 ? ca0[j] : ca1[j - 4];
                 const float ce = j < 4 ? ce0[j] : ce1[j - 4];
-                vcc[j] = (__bf16)((float)cv[j] * __expf(ct));
-                vcf[j] = (__bf16)((float)cv[j] * __expf(ct - ca));
-                vbu[j] = (__bf16)((float)bv[j] * __expf(ce - ct));
+                vcc[j] = (__bf16)((float)cv[j] * dexp2(ct));
+                vcf[j] = (__bf16)((float)cv[j] * dexp2(ct - ca));
+                vbu[j] = (__bf16)((float)bv[j] * dexp2(ce - ct));
             }
             *reinterpret_cast<bf16x8*>(Cc + t * NP + 8 * c8) = vcc;
             *reinterpret_cast<bf16x8*>(Cf + t * NP + 8 * c8) = vcf;
@@ -658,7 +667,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             float v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                v[k] = (float)Braw[(t4 + k) * NP + n] * __expf(cl - cum[(t4 + k) * CS + n]);
+                v[k] = (float)Braw[(t4 + k) * NP + n] * dexp2(cl - cum[(t4 + k) * CS + n]);
             lds_store4(Bt + n * QP + t4, v[0], v[1], v[2], v[3]);
         }
         __syncthreads();
@@ -708,7 +717,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 for (int q = 0; q < (N + kWave - 1) / kWave; ++q) {
                     const int n = min(q * kWave + lane, N - 1);
                     const float dec = cum[a * CS + n] - cum[(a + 15) * CS + n];
-                    const uint64_t bits = __ballot(dec > kSplitMax);
+                    const uint64_t bits = __ballot(dec > kSplitMax2);
                     fast |= (N >= kWave ? bits : bits & ((1ull << N) - 1)) << (q * kWave);
                 }
                 if (nh == 0) {
@@ -727,8 +736,8 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                             const float ca = j < 4 ? ca0[j] : ca1[j - 4];
                             const float cl = j < 4 ? cs0[j] : cs1[j - 4];  // cum of this lane's row
                             const bool split = !((fast >> (k0 + j)) & 1);
-                            bo[j] = (__bf16)(split ? (float)bv[j] * __expf(ca - cl) : 0.f);  // rows s
-                            co[j] = (__bf16)(split ? (float)cv[j] * __expf(cl - ca) : 0.f);  // cols t
+                            bo[j] = (__bf16)(split ? (float)bv[j] * dexp2(ca - cl) : 0.f);  // rows s
+                            co[j] = (__bf16)(split ? (float)cv[j] * dexp2(cl - ca) : 0.f);  // cols t
                         }
                         acc = mfma_bf16(bo, co, acc);
                     }
@@ -743,18 +752,20 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                     const int n = 4 * g4;
                     const f32x4 ct = *reinterpret_cast<const f32x4*>(cum + t * CS + n);
                     const bf16x4 cr = *reinterpret_cast<const bf16x4*>(Craw + t * NP + n);
+                    float cm[4];  // C on the group's fast dimensions only
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cm[j] = ((gbits >> j) & 1) ? (float)cr[j] : 0.f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int s = a + 4 * lg + i;
                         const f32x4 cs = *reinterpret_cast<const f32x4*>(cum + s * CS + n);
                         const bf16x4 br = *reinterpret_cast<const bf16x4*>(Braw + s * NP + n);
+                        // (the exponent is clamped at 0 so that the entries above the diagonal,
+                        // dropped below, stay finite; on and below it, it is <= 0 already)
                         float sum = 0.f;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const bool use = causal[i] && ((gbits >> j) & 1);
-                            sum += use ? (float)cr[j] * (float)br[j] * __expf(ct[j] - cs[j]) : 0.f;
-                        }
-                        acc[i] += sum;
+                        for (int j = 0; j < 4; ++j) sum = fmaf(cm[j] * (float)br[j], dexp2(fminf(ct[j] - cs[j], 0.f)), sum);
+                        acc[i] += causal[i] ? sum : 0.f;
                     }
                 }
                 dst = Sl + (nh == 0 ? tile_index(tb, tb) : NTILES + tb) * 256;
@@ -833,7 +844,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         load_chunk(min(c + 2, c1 - 1));
     }
 
-    if (!FULL && tid < N) prm.seg_decay[sidx * N + tid] = lsum * 1.4426950408889634f;
+    if (!FULL && tid < N) prm.seg_decay[sidx * N + tid] = lsum;
     float* fin = !FULL ? prm.seg_state + sidx * N * P
                        : (c1 == nchunks && prm.final_state) ? prm.final_state + unit * N * P : nullptr;
     if (fin) {
