@@ -82,10 +82,21 @@ class HipEvents:
         self.lib.hipEventDestroy(ctypes.c_void_p(h))
 
 
-def kernel_source_hash():
-    """Hash of every kernel and ABI source: counter figures taken on other sources are stale."""
+# the source file each kernel (by name prefix) and its launch code are compiled from
+KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.hip",
+                  "seg_state_kernel": "ssd_fast.hip", "seg_prefix_kernel": "ssd_fast.hip",
+                  "walk_diag_pipe_kernel": "ssd_diag.hip", "walk_diag_kernel": "ssd_diag.hip",
+                  "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
+                  "step_kernel": "ssd_kernels.hip"}
+
+
+def kernel_source_hash(kernel):
+    """Hash of the sources `kernel` is built from (its .hip file and the shared headers):
+    counter figures taken on other sources are stale."""
+    names = [KERNEL_SOURCES[kernel.split("<")[0]]] + sorted(
+        n for n in os.listdir(CSRC) if n.endswith(".h"))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -146,7 +157,7 @@ def measured_traffic(workload, kernel):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
