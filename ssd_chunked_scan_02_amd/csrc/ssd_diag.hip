@@ -423,8 +423,10 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
 // to N + 4 floats so that 16 rows read at once fall on distinct banks.
 constexpr int kDiagQ = 64;
 constexpr int kDiagWaves = 8;
-// largest decay (natural log) inside one 16-token block that a diagonal score tile still splits
-// into two factors: exp(kSplitMax) and exp(-kSplitMax) are far inside the fp32 and bf16 ranges
+// bound (natural log) on each of the two factors a diagonal score tile splits into: exp(kSplitMax)
+// and exp(-kSplitMax) are far inside the fp32 and bf16 ranges.  With the split taken halfway
+// (in value) through a block's running sums, a state dimension splits when its decay over the
+// block is at most 2 kSplitMax.
 constexpr float kSplitMax = 64.f;
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kSplitMax2 = kSplitMax * kLog2eD;  // the same bound in log2 units
@@ -701,11 +703,13 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 dst = Sl + tile_index(tb, sb) * 256;
             } else {
                 // Diagonal tile, S^T[s][t] = sum_n B_sn C_tn exp(cum_tn - cum_sn) for s <= t.  For
-                // a state dimension whose decay inside the block stays below e^kSplitMax, the
-                // exponential splits at the block start a into exp(cum_tn - cum_an) <= 1 and
-                // exp(cum_an - cum_sn) <= e^kSplitMax, and the sum over those dimensions is one
-                // MFMA contraction (wave nh = 0); the other dimensions take exact exponentials,
-                // split over the two waves by halves of the state dimension.
+                // a state dimension whose decay D over the block is at most 2 kSplitMax, the
+                // exponential splits at m_n = (cum_an + cum_en) / 2 (a, e the block's first and
+                // last token) into exp(cum_tn - m_n) and exp(m_n - cum_sn), each within
+                // e^(+-D/2), and the sum over those dimensions is one MFMA contraction (wave
+                // nh = 0).  (Above the diagonal the two factors can multiply past the fp32 range;
+                // those entries are dropped by a select.)  The other dimensions take exact
+                // exponentials, split over the two waves by halves of the state dimension.
                 const int tb = item % NT, nh = item / NT, a = 16 * tb;
                 const int t = a + l16;
                 bool causal[4];
@@ -717,7 +721,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 for (int q = 0; q < (N + kWave - 1) / kWave; ++q) {
                     const int n = min(q * kWave + lane, N - 1);
                     const float dec = cum[a * CS + n] - cum[(a + 15) * CS + n];
-                    const uint64_t bits = __ballot(dec > kSplitMax2);
+                    const uint64_t bits = __ballot(dec > 2.f * kSplitMax2);
                     fast |= (N >= kWave ? bits : bits & ((1ull << N) - 1)) << (q * kWave);
                 }
                 if (nh == 0) {
@@ -726,6 +730,8 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                         const int k0 = 32 * kb + 8 * lg;
                         const f32x4 ca0 = *reinterpret_cast<const f32x4*>(cum + a * CS + k0);
                         const f32x4 ca1 = *reinterpret_cast<const f32x4*>(cum + a * CS + k0 + 4);
+                        const f32x4 ce0 = *reinterpret_cast<const f32x4*>(cum + (a + 15) * CS + k0);
+                        const f32x4 ce1 = *reinterpret_cast<const f32x4*>(cum + (a + 15) * CS + k0 + 4);
                         const f32x4 cs0 = *reinterpret_cast<const f32x4*>(cum + t * CS + k0);
                         const f32x4 cs1 = *reinterpret_cast<const f32x4*>(cum + t * CS + k0 + 4);
                         const bf16x8 bv = as_bf16x8(ld16(Braw + t * NP + k0));
@@ -733,11 +739,11 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                         bf16x8 bo, co;
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const float ca = j < 4 ? ca0[j] : ca1[j - 4];
+                            const float cm = 0.5f * ((j < 4 ? ca0[j] : ca1[j - 4]) + (j < 4 ? ce0[j] : ce1[j - 4]));
                             const float cl = j < 4 ? cs0[j] : cs1[j - 4];  // cum of this lane's row
                             const bool split = !((fast >> (k0 + j)) & 1);
-                            bo[j] = (__bf16)(split ? (float)bv[j] * dexp2(ca - cl) : 0.f);  // rows s
-                            co[j] = (__bf16)(split ? (float)cv[j] * dexp2(cl - ca) : 0.f);  // cols t
+                            bo[j] = (__bf16)(split ? (float)bv[j] * dexp2(cm - cl) : 0.f);  // rows s
+                            co[j] = (__bf16)(split ? (float)cv[j] * dexp2(cl - cm) : 0.f);  // cols t
                         }
                         acc = mfma_bf16(bo, co, acc);
                     }
