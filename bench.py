@@ -129,7 +129,7 @@ def kernel_names(cfg):
     if cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256):
         q = min(Q, 128)
         if fast_segments(cfg) > 1:
-            return ["prep_kernel<%d,%d>" % (N, q), "seg_state_kernel<%d,%d>" % (N, q), "seg_prefix_kernel",
+            return ["prep_kernel<%d,%d>" % (N, q), "seg_state_kernel<%d,%d>" % (N, q),
                     "walk_fast_kernel<%d,%d>" % (N, q)]
         return ["prep_kernel<%d,%d>" % (N, q), "walk_fast_kernel<%d,%d>" % (N, q)]
     return ["scores_kernel<%d>" % N, "walk_kernel<%d,%d>" % (N, P)]

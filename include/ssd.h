@@ -107,7 +107,8 @@ int ssd_forward(const ssd_dims* dims, const void* x, const float* log_a, const v
  * With events non-NULL, n_events must be at least 2 * SSD_MAX_LAUNCHES, else the call fails
  * with SSD_ERR_INVALID before doing anything.  Launch order of the bf16 scalar-decay path:
  * prep (score tiles C B^T and operand layouts), then for a segmented walk the state-only
- * pass and the segment prefix, then the chunk walk (states and outputs).
+ * pass, then the chunk walk (states and outputs).  The diagonal-decay path's segmented walk runs
+ * its state-only pass, the segment prefix and its walk.
  */
 #define SSD_MAX_LAUNCHES 4
 int ssd_forward_profiled(const ssd_dims* dims, const void* x, const float* log_a, const void* B,

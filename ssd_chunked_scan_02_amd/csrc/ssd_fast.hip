@@ -636,21 +636,42 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         }
     };
 
+    // The state entering the first chunk.  For segment s > 0 of a segmented walk it is the chain
+    // h <- exp2(decay_j) h + state_j over the segments j < s (local states and log2 decays from
+    // seg_state_kernel), started from the caller's initial state.  Where a factor exp2(decay_j)
+    // is exactly 0 the chain restarts at state_j, whatever came before, so the chain is run from
+    // the last such j: on long segments that is a single step.
     f32x4 hs[NBW][PB];
+    auto add_rows = [&](const float* src, float scale) {
+#pragma unroll
+        for (int jn = 0; jn < NBW; ++jn)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                const int n = 16 * (SW + 4 * jn) + 4 * lg;
+                const float* p = src + n * kP + 16 * pb + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hs[jn][pb][i] = scale * hs[jn][pb][i] + p[i * kP];
+            }
+    };
 #pragma unroll
     for (int jn = 0; jn < NBW; ++jn)
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) {
-            hs[jn][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const float* init = prm.nseg > 1 ? prm.seg_init + (span.seg * prm.batch * prm.nheads + unit) * N * kP
-                                             : (prm.init ? prm.init + unit * N * kP : nullptr);
-            if (init) {
-                const int n = 16 * (SW + 4 * jn) + 4 * lg;
-                const float* src = init + n * kP + 16 * pb + l16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) hs[jn][pb][i] = src[i * kP];
+        for (int pb = 0; pb < PB; ++pb) hs[jn][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+        const int64_t units = prm.batch * prm.nheads;
+        int j0 = 0;
+        bool restart = false;
+        for (int j = span.seg - 1; j >= 0; --j)
+            if (exp2f(prm.seg_decay[j * units + unit]) == 0.f) {
+                j0 = j;
+                restart = true;
+                break;
             }
-        }
+        if (!restart && prm.init) add_rows(prm.init + unit * N * kP, 0.f);
+        for (int j = j0; j < span.seg; ++j)
+            add_rows(prm.seg_state + (j * units + unit) * N * kP,
+                     j == j0 && restart ? 0.f : exp2f(prm.seg_decay[j * units + unit]));
+    }
     auto write_state = [&](__bf16* hsm) {
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
@@ -942,7 +963,7 @@ bool allow_full_lds(const void* kernel, bool* done) {
 struct FastLayout {
     int64_t nchunks, nblk, units;
     int nseg, seg_chunks;
-    size_t pairs, bt, ct, la_t, seg_state, seg_decay, seg_init, total;
+    size_t pairs, bt, ct, la_t, seg_state, seg_decay, total;
 };
 
 FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int Q) {
@@ -958,10 +979,9 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
     l.bt = off; off += (size_t)l.nblk * N * Q * 2;
     l.ct = off; off += (size_t)l.nblk * N * Q * 2;
     l.la_t = off; off += (size_t)l.units * l.nchunks * Q * 4;
-    l.seg_state = l.seg_decay = l.seg_init = off;
+    l.seg_state = l.seg_decay = off;
     if (l.nseg > 1) {
         l.seg_state = off; off += (size_t)l.nseg * l.units * N * kP * 4;
-        l.seg_init = off; off += (size_t)l.nseg * l.units * N * kP * 4;
         l.seg_decay = off; off += ((size_t)l.nseg * l.units * 4 + 255) / 256 * 256;
     }
     l.total = off;
@@ -994,8 +1014,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int64_t per_xcd = (work + 7) / 8;
     Walk2Params wp{fl.x, la_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, nch, per_xcd,
-                   lay.seg_chunks, lay.nseg,
-                   reinterpret_cast<float*>(ws + lay.seg_init), reinterpret_cast<float*>(ws + lay.seg_state),
+                   lay.seg_chunks, lay.nseg, reinterpret_cast<float*>(ws + lay.seg_state),
                    reinterpret_cast<float*>(ws + lay.seg_decay)};
     if (lay.nseg > 1) {
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
@@ -1004,9 +1023,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
         sp.per_xcd = (state_work + 7) / 8;
         if (!launch_k(fl, k, seg_state_kernel<N, Q>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kWave), slds, stream, sp))
             return -1;
-        if (launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, lay.units, N, kP, lay.nseg, 0,
-                              stream) != 0)
-            return -1;
+        // (each walk workgroup chains the segment states into its own start state)
     }
     return launch_k(fl, k, walk_fast_kernel<N, Q>, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream,
                     wp)
@@ -1045,8 +1062,9 @@ int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream) {
 
 // Chains the segments' local states, one thread per state element (n, p) of one unit:
 //   seg_init[s] = exp2(decay[s-1]) o seg_init[s-1] + seg_state[s-1],  seg_init[0] = init (or 0),
-// with decay one log2 value per (segment, unit) (scalar decay) or per (segment, unit, n)
-// (diagonal decay).  States are [segment][unit][N][P] fp32.
+// with decay one log2 value per (segment, unit) (per_n = 0) or per (segment, unit, n) (per_n = 1).
+// States are [segment][unit][N][P] fp32.  (The diagonal walk uses it; the scalar walk chains the
+// states in each workgroup.)
 __global__ void __launch_bounds__(kThreads) seg_prefix_kernel(const float* init, float* seg_init,
                                                               const float* seg_state, const float* seg_decay,
                                                               int64_t units, int N, int P, int nseg, int per_n) {

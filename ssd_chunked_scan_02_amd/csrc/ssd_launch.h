@@ -81,10 +81,9 @@ struct Walk2Params {
     int64_t batch, seqlen, nheads, ngroups;
     int nchunks;
     int64_t per_xcd;
-    // segmented walks (nseg > 1): chunks per segment, and per (segment, unit) the state at the
-    // segment start, the segment's local final state from a zero start and its log2 decay
+    // segmented walks (nseg > 1): chunks per segment, and per (segment, unit) the segment's local
+    // final state from a zero start and its log2 decay
     int seg_chunks, nseg;
-    float* seg_init;
     float* seg_state;
     float* seg_decay;
 };

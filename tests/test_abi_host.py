@@ -66,8 +66,8 @@ def test_workspace_bytes(lib):
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(ngroups=8, nheads=64), 64) == fast(8, 64, 8, 32, 128, 64)
     # chunk 256 runs as 128-token chunks; with few (batch, head) units on a long sequence the
     # walk is split into segments (here 32 units, 512 chunks -> 16 segments of 32 chunks), which
-    # adds two fp32 states per (segment, unit) and a padded log2 decay per (segment, unit)
-    seg = 16 * 32 * (2 * 128 * 64 * 4) + (16 * 32 * 4 + 255) // 256 * 256
+    # adds an fp32 state and a log2 decay per (segment, unit), the decays padded to 256 bytes
+    seg = 16 * 32 * (128 * 64 * 4) + (16 * 32 * 4 + 255) // 256 * 256
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(batch=1, nheads=32, seqlen=65536), 256) == \
         fast(1, 32, 1, 512, 128, 128) + seg
     # other shapes: causal 16x16 fp32 score tiles per (batch, group, chunk)
