@@ -74,8 +74,12 @@ def test_workspace_bytes(lib):
     tiles = lambda nblk, Q: nblk * (Q // 16) * (Q // 16 + 1) // 2 * 1024
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(dtype=0), 64) == tiles(8 * 32, 64)
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(headdim=32), 256) == tiles(8 * 8, 256)
-    # diagonal decay needs no workspace
+    # diagonal decay needs no workspace unless its walk is segmented: then per (segment, unit) an
+    # fp32 local state, an fp32 start state and a log2 decay per state row (2 units, 64 chunks ->
+    # 16 segments)
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(decay=1, dstate=64), 64) == 0
+    assert ssd.ssd_forward_workspace_bytes(mamba2_dims(decay=1, dstate=64, batch=1, nheads=2, seqlen=4096), 64) == \
+        2 * 16 * 2 * 64 * 64 * 4 + (16 * 2 * 64 * 4 + 255) // 256 * 256
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=0), 128) == 0
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(), 48) == 0        # unsupported chunk
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(nheads=5, ngroups=2), 64) == 0
