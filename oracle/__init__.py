@@ -13,8 +13,12 @@ Contents
                         and its PyTorch sketch) with the corrections listed in its
                         docstring; it also returns the per-chunk states, for localising
                         kernel bugs.  Pinned against ``forward`` by the CPU tests.
+  discretize            the discretisation front-end (llms.blog "The Selection Mechanism"):
+                        Delta = softplus(dt + bias), log a = -Delta exp(A_log), B-bar = Delta B;
+                        ``discretize.forward_dt`` runs the recurrence in that form.
 """
 from .recurrence import Oracle, build, default_oracle, forward, default_threads
 from .chunked import chunked_forward
+from . import discretize
 
-__all__ = ["Oracle", "build", "default_oracle", "forward", "default_threads", "chunked_forward"]
+__all__ = ["Oracle", "build", "default_oracle", "forward", "default_threads", "chunked_forward", "discretize"]

@@ -302,6 +302,101 @@ def pin_head_decay_is_per_head(orc):
     _close(fp, fin[:, perm], "head permutation final", rtol=0.0)
 
 
+# --- the discretisation front-end (oracle/discretize.py) ---------------------------------
+# These pins take the oracle handle and the discretisation module (or a copy of it with a
+# planted mistake).
+def pin_softplus_values(orc, disc):
+    """softplus where it has a closed form: ln 2 at 0, 1 at ln(e - 1), 2 at ln(e^2 - 1),
+    v + e^-v (to 1e-16) at v = 40, e^v at v = -40, 0 far below and v far above."""
+    e = np.e
+    v = np.array([0.0, np.log(e - 1.0), np.log(e * e - 1.0), 40.0, -40.0, -800.0, 800.0])
+    want = np.array([np.log(2.0), 1.0, 2.0, 40.0 + np.exp(-40.0), np.exp(-40.0), 0.0, 800.0])
+    got = disc.softplus(v)
+    assert np.all(np.abs(got - want) <= 1e-14 * np.maximum(1.0, np.abs(want)) + 1e-300), (got, want)
+    assert abs(got[4] / want[4] - 1.0) < 1e-15  # the tiny value itself, not just |err| < 1e-14
+
+
+def _dt_tensors(rng, nb, T, H, G, P, N):
+    x = rng.standard_normal((nb, T, H, P))
+    Bm = rng.standard_normal((nb, T, G, N)) / np.sqrt(N)
+    Cm = rng.standard_normal((nb, T, G, N)) / np.sqrt(N)
+    D = rng.standard_normal(H)
+    h0 = rng.standard_normal((nb, H, N, P))
+    return x, Bm, Cm, D, h0
+
+
+def pin_dt_one_token(orc, disc):
+    """One token in closed form.  dt + dt_bias = ln(e^2 - 1), so Delta = softplus(.) = 2, and
+    zero-order hold gives A-bar = exp(Delta A) = exp(-2 exp(A_log)) per head (per (head, state
+    dim) for diagonal decay); A_log = ln 1.5 in head 0 (state dim 0) makes that e^-3.  Then
+    h_1 = A-bar h_0 + 2 B x^T (B-bar = Delta B), or + B x^T without the input scale, and
+    y = C . h_1 + D x with the raw x."""
+    rng = np.random.default_rng(31)
+    nb, H, G, P, N = 2, 3, 1, 2, 4
+    x, Bm, Cm, D, h0 = _dt_tensors(rng, nb, 1, H, G, P, N)
+    bias = np.array([0.25, -0.5, 1.0])
+    dt = np.log(np.e ** 2 - 1.0) - np.broadcast_to(bias, (nb, 1, H))
+    for diag in (False, True):
+        A_log = rng.uniform(0.0, np.log(16.0), (H, N) if diag else (H,))
+        A_log.flat[0] = np.log(1.5)
+        for scale in (True, False):
+            y, fin = disc.forward_dt(orc, x, dt, A_log, Bm, Cm, D, dt_bias=bias, scale_input=scale,
+                                     init_state=h0, diag=diag)
+            k = 2.0 if scale else 1.0
+            for b in range(nb):
+                for h in range(H):
+                    abar = np.array([np.exp(-2.0 * np.exp(A_log[h, n] if diag else A_log[h])) for n in range(N)])
+                    if h == 0:
+                        assert abs(abar[0] - np.exp(-3.0)) < 1e-16
+                    want_h = abar[:, None] * h0[b, h] + k * np.outer(Bm[b, 0, 0], x[b, 0, h])
+                    _close(fin[b, h], want_h, "one token final (diag=%d scale=%d)" % (diag, scale), 1e-14)
+                    _close(y[b, 0, h], Cm[b, 0, 0] @ want_h + D[h] * x[b, 0, h],
+                           "one token y (diag=%d scale=%d)" % (diag, scale), 1e-14)
+
+
+def pin_dt_limits(orc, disc):
+    """The two limits of the selection mechanism.  Delta -> 0 (dt = -60): A-bar -> I and
+    B-bar -> 0, so the state is kept and the tokens ignored: y_t = C_t . h_0 + D x_t and
+    final = h_0.  Delta -> infinity (dt = 60, A_log = 0, so Delta = 60 up to e^-60): A-bar -> 0,
+    so only the current token counts: y_t = 60 (C_t . B_t) x_t + D x_t and
+    final = 60 B_{T-1} x_{T-1}^T."""
+    rng = np.random.default_rng(32)
+    nb, T, H, G, P, N = 2, 7, 4, 2, 3, 5
+    x, Bm, Cm, D, h0 = _dt_tensors(rng, nb, T, H, G, P, N)
+    A_log = rng.uniform(0.0, np.log(16.0), H)
+    y, fin = disc.forward_dt(orc, x, np.full((nb, T, H), -60.0), A_log, Bm, Cm, D, init_state=h0)
+    for b in range(nb):
+        for h in range(H):
+            g = h // (H // G)
+            _close(y[b, :, h], Cm[b, :, g] @ h0[b, h] + D[h] * x[b, :, h], "Delta->0 y")
+            _close(fin[b, h], h0[b, h], "Delta->0 final")
+    y, fin = disc.forward_dt(orc, x, np.full((nb, T, H), 60.0), np.zeros(H), Bm, Cm, D, init_state=h0)
+    for b in range(nb):
+        for h in range(H):
+            g = h // (H // G)
+            cb = np.sum(Cm[b, :, g] * Bm[b, :, g], axis=1)
+            _close(y[b, :, h], (60.0 * cb + D[h])[:, None] * x[b, :, h], "Delta->inf y")
+            _close(fin[b, h], 60.0 * np.outer(Bm[b, -1, g], x[b, -1, h]), "Delta->inf final")
+
+
+def pin_dt_diag_equal_rates_is_scalar(orc, disc):
+    """A_log [H,N] whose columns are equal gives the scalar-decay result, bitwise in fp64."""
+    rng = np.random.default_rng(33)
+    nb, T, H, G, P, N = 2, 11, 4, 2, 3, 5
+    x, Bm, Cm, D, h0 = _dt_tensors(rng, nb, T, H, G, P, N)
+    dt = rng.standard_normal((nb, T, H)) - 2.0
+    A_log = rng.uniform(0.0, np.log(16.0), H)
+    bias = rng.standard_normal(H)
+    ys, fs = disc.forward_dt(orc, x, dt, A_log, Bm, Cm, D, dt_bias=bias, init_state=h0)
+    yd, fd = disc.forward_dt(orc, x, dt, np.repeat(A_log[:, None], N, axis=1), Bm, Cm, D, dt_bias=bias,
+                             init_state=h0, diag=True)
+    _close(yd, ys, "diag equal rates y", rtol=0.0)
+    _close(fd, fs, "diag equal rates final", rtol=0.0)
+
+
+DT_PINS = [pin_softplus_values, pin_dt_one_token, pin_dt_limits, pin_dt_diag_equal_rates_is_scalar]
+
+
 ALL_PINS = [
     pin_handworked_scalar, pin_handworked_diag, pin_materialized_scalar, pin_materialized_diag,
     pin_a_one, pin_a_zero, pin_lti_convolution, pin_associative_scan, pin_split_resume,

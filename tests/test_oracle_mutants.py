@@ -7,11 +7,14 @@ import os
 import shutil
 import tempfile
 
+import importlib.util
+
 import pytest
 
 import oracle
+import oracle.discretize
 from oracle.recurrence import SOURCE, Oracle, build
-from pins import ALL_PINS
+from pins import ALL_PINS, DT_PINS
 
 MUTANTS = {
     "decay_dropped": ("decay[n] * state[n * P + p] + bt[n] * xt[p]",
@@ -58,6 +61,57 @@ def test_mutant_is_caught(workdir, name):
     for pin in ALL_PINS:
         try:
             pin(mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "planted mistake %r passed every pin" % name
+
+
+# planted mistakes in a copy of the discretisation front-end (oracle/discretize.py)
+DT_MUTANTS = {
+    "softplus_is_exp": ("np.logaddexp(0.0, np.asarray(v, dtype=np.float64))",
+                        "np.exp(np.asarray(v, dtype=np.float64))"),
+    "softplus_is_identity": ("np.logaddexp(0.0, np.asarray(v, dtype=np.float64))",
+                             "np.asarray(v, dtype=np.float64)"),
+    "A_positive": ("A = -np.exp(A_log)", "A = np.exp(A_log)"),
+    "A_is_A_log": ("A = -np.exp(A_log)", "A = -A_log"),
+    "bias_dropped": ("v = dt if dt_bias is None else dt + np.asarray(dt_bias, dtype=np.float64)[None, None, :]",
+                     "v = dt"),
+    "bias_subtracted": ("else dt + np.asarray(dt_bias", "else dt - np.asarray(dt_bias"),
+    "delta_not_in_decay": ("log_a = delta * A[None, None, :]", "log_a = A[None, None, :] + 0 * delta"),
+    "diag_delta_not_in_decay": ("log_a = delta[..., None] * A[None, None, :, :]",
+                                "log_a = 0 * delta[..., None] + A[None, None, :, :]"),
+    "input_not_scaled": ("xin = x * delta[..., None] if scale_input else x", "xin = x"),
+    "input_always_scaled": ("xin = x * delta[..., None] if scale_input else x", "xin = x * delta[..., None]"),
+    "skip_on_scaled_input": ("[None, None, :, None] * x\n", "[None, None, :, None] * xin\n"),
+    "skip_dropped": ("        y = y + np.asarray(D, dtype=np.float64)[None, None, :, None] * x\n",
+                     "        y = y\n"),
+    "diag_rates_of_first_dim": ("A[None, None, :, :]", "np.repeat(A[:, :1], A.shape[1], axis=1)[None, None]"),
+    "diag_rates_of_first_head": ("A[None, None, :, :]", "np.repeat(A[:1, :], A.shape[0], axis=0)[None, None]"),
+}
+
+
+@pytest.fixture(scope="module")
+def real_oracle():
+    return oracle.default_oracle()
+
+
+@pytest.mark.parametrize("name", sorted(DT_MUTANTS))
+def test_discretization_mutant_is_caught(workdir, real_oracle, name):
+    before, after = DT_MUTANTS[name]
+    src_path = oracle.discretize.__file__
+    with open(src_path) as f:
+        src = f.read()
+    assert src.count(before) == 1, "mutation site for %s must occur exactly once" % name
+    path = os.path.join(workdir, "discretize_%s.py" % name)
+    with open(path, "w") as f:
+        f.write(src.replace(before, after))
+    spec = importlib.util.spec_from_file_location("discretize_%s" % name, path)
+    mutant = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mutant)
+    caught = []
+    for pin in DT_PINS:
+        try:
+            pin(real_oracle, mutant)
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, "planted mistake %r passed every pin" % name

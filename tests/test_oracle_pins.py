@@ -1,11 +1,13 @@
 """The CPU oracle against its pins (hand-worked examples, the matrix form, closed forms,
-the LTI convolution, associative-scan order, split/resume, linearity, group sharing), and
+the LTI convolution, associative-scan order, split/resume, linearity, group sharing, the
+discretisation front-end), and
 the chunked fp64 model against the oracle for many chunk lengths."""
 import numpy as np
 import pytest
 
 import oracle
-from pins import ALL_PINS, _problem, _close
+import oracle.discretize
+from pins import ALL_PINS, DT_PINS, _problem, _close
 
 
 @pytest.fixture(scope="module")
@@ -16,6 +18,11 @@ def orc():
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
 def test_pin(orc, pin):
     pin(orc)
+
+
+@pytest.mark.parametrize("pin", DT_PINS, ids=lambda p: p.__name__)
+def test_discretization_pin(orc, pin):
+    pin(orc, oracle.discretize)
 
 
 @pytest.mark.parametrize("diag", [False, True])
