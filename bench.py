@@ -7,7 +7,8 @@ with TFLOP/s, fraction of MFMA peak, the HBM roofline of the dominant kernel (ti
 with HIP events that each launch's dispatch stamps at its start and end, on the launch
 stream) and the fp64 CPU oracle's throughput on this host as a reported baseline.
 
-A step is one ssd_forward over one batch.  Inputs are drawn once (seeded, synthetic) and
+A step is one ssd_forward over one batch (with --front-end dt, one ssd_forward_dt: log a and
+the input scale formed in the kernels from dt and A_log, the Mamba-2 layer's form).  Inputs are drawn once (seeded, synthetic) and
 copied to HBM before timing; the timed steps cycle through several copies of the inputs
 and outputs (about 1 GB together) so that no step finds its data in the 256 MB
 last-level cache.
@@ -37,10 +38,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_counts(cfg):
+def algorithmic_counts(cfg, front_end="log_a"):
     """Work the method must do for one forward over the workload (not what a kernel
     executes): causal C B^T and (S o L) X inside chunks, plus the chunk-state and carried-
-    state contractions; bytes = every input read once and every output written once."""
+    state contractions; bytes = every input read once and every output written once (with the
+    dt front-end the decay input is dt [B,T,H] and A_log [H] or [H,N] instead of log a)."""
     Bsz, T, H, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["ngroups"]
     P, N, Q = cfg["headdim"], cfg["dstate"], cfg["chunk"]
     diag = cfg["decay"] == "diag"
@@ -48,8 +50,9 @@ def algorithmic_counts(cfg):
     K = N if diag else 1
     sx = 4 if cfg["dtype"] == "fp32" else 2
     flops = Bsz * T * (Gs * N * (Q + 1) + H * P * (Q + 1) + 4 * H * N * P)
-    per_token = H * P * (sx + sx) + 2 * G * N * sx + 4 * H * K
-    nbytes = Bsz * T * per_token + (4 * H if cfg["skip"] else 0) \
+    dt = front_end == "dt"
+    per_token = H * P * (sx + sx) + 2 * G * N * sx + 4 * H * (1 if dt else K)
+    nbytes = Bsz * T * per_token + (4 * H if cfg["skip"] else 0) + (4 * H * K if dt else 0) \
         + 4 * Bsz * H * N * P * (int(cfg["init"]) + int(cfg["final"]))
     return flops, nbytes, per_token
 
@@ -87,7 +90,8 @@ KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.h
                   "seg_state_kernel": "ssd_fast.hip", "seg_prefix_kernel": "ssd_fast.hip",
                   "walk_diag_pipe_kernel": "ssd_diag.hip", "walk_diag_kernel": "ssd_diag.hip",
                   "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
-                  "step_kernel": "ssd_kernels.hip"}
+                  "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
+                  "skip_kernel": "ssd_kernels.hip"}
 
 
 def kernel_source_hash(kernel):
@@ -116,9 +120,14 @@ def fast_segments(cfg, target=512):
     return -(-nch // per)
 
 
-def kernel_names(cfg):
+def kernel_names(cfg, front_end="log_a"):
     """Kernels one forward launches, in order (mirrors the library's dispatch)."""
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
+    if front_end == "dt":
+        fused = (cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64)) if cfg["decay"] == "diag" \
+            else (cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256))
+        if not fused:
+            return ["discretize_kernel"] + kernel_names(cfg) + (["skip_kernel"] if cfg["skip"] else [])
     if cfg["decay"] == "diag":
         if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
             if fast_segments(dict(cfg, chunk=64), 512) > 1:
@@ -165,10 +174,12 @@ def measured_traffic(workload, kernel):
         return None
 
 
-def cpu_baseline(inp, cfg, min_seconds):
+def cpu_baseline(inp, cfg, min_seconds, front_end="log_a"):
     """The fp64 oracle as it stands, on this host's cores, over the whole workload, repeated
-    until at least ``min_seconds`` of CPU wall time."""
+    until at least ``min_seconds`` of CPU wall time (with the dt front-end, the oracle's
+    discretisation followed by its recurrence)."""
     import oracle
+    import oracle.discretize
     import ssd_inputs
     f = ssd_inputs.to_f64
     args = [f(inp["x"]), f(inp["log_a"]), f(inp["B"]), f(inp["C"]), f(inp.get("D")),
@@ -176,7 +187,12 @@ def cpu_baseline(inp, cfg, min_seconds):
     threads = oracle.default_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(*args, want_final=cfg["final"], nthreads=threads)
+        if front_end == "dt":
+            oracle.discretize.forward_dt(oracle.default_oracle(), args[0], f(inp["dt"]), f(inp["A_log"]), args[2],
+                                         args[3], args[4], init_state=args[5], want_final=cfg["final"],
+                                         diag=cfg["decay"] == "diag", nthreads=threads)
+        else:
+            oracle.forward(*args, want_final=cfg["final"], nthreads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds and reps >= 1:
@@ -247,6 +263,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mamba2_layer")
+    ap.add_argument("--front-end", choices=("log_a", "dt"), default="log_a",
+                    help="decay input: log a (ssd_forward), or dt and A_log (ssd_forward_dt)")
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -269,7 +287,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = ssd_inputs.make_inputs(cfg, seed)
-    flops, nbytes, per_token = algorithmic_counts(cfg)
+    fe = args.front_end
+    flops, nbytes, per_token = algorithmic_counts(cfg, fe)
     copies = args.copies or min(64, max(2, math.ceil(1.0e9 / nbytes)))
     log("workload %s seed %d: %.2f GFLOP, %.1f MB algorithmic per step, %d copies"
         % (args.workload, seed, flops / 1e9, nbytes / 1e6, copies))
@@ -282,8 +301,9 @@ def main():
                                   dtype=torch.float32, device=dev) if cfg["final"] else None)
         bufs.append(g)
     dims = ssd.dims_for(bufs[0]["x"], bufs[0]["log_a"], bufs[0]["B"])
-    ws = torch.empty(max(1, ssd.ssd_forward_workspace_bytes(dims, cfg["chunk"])),
-                     dtype=torch.uint8, device=dev)
+    ws_need = (ssd.ssd_forward_dt_workspace_bytes(dims, cfg["chunk"], True) if fe == "dt"
+               else ssd.ssd_forward_workspace_bytes(dims, cfg["chunk"]))
+    ws = torch.empty(max(1, ws_need), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ev = HipEvents()
 
@@ -291,6 +311,12 @@ def main():
         g = bufs[i % copies]
         kw = dict(chunk=cfg["chunk"], init_state=g.get("init_state"), y=g["y"],
                   final_state=g["final"], workspace=ws, stream=stream)
+        if fe == "dt":
+            if events is None:
+                ssd.ssd_forward_dt(g["x"], g["dt"], g["A_log"], g["B"], g["C"], g.get("D"), **kw)
+                return None
+            return ssd.ssd_forward_dt_profiled(g["x"], g["dt"], g["A_log"], g["B"], g["C"], g.get("D"),
+                                               events=events, **kw)[2]
         if events is None:
             ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g.get("D"), **kw)
             return None
@@ -332,7 +358,7 @@ def main():
     ms = total_ms / K
     kernel_avg = [sum(v) / len(v) for v in per_kernel]
     dom = max(range(launches), key=lambda k: kernel_avg[k])
-    names = kernel_names(cfg)
+    names = kernel_names(cfg, fe)
     if len(names) != launches:
         names = ["launch%d" % k for k in range(launches)]
     log("ms/step %.4f (%.4f with per-launch timing); per kernel avg ms: %s"
@@ -356,7 +382,8 @@ def main():
     dom_ms = kernel_avg[dom]
     dom_bytes = kernel_bytes(cfg, names[dom], nbytes)
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
-    traffic = measured_traffic(args.workload, names[dom])
+    profile_key = args.workload if fe == "log_a" else args.workload + "_dt"
+    traffic = measured_traffic(profile_key, names[dom])
     result = {
         "metric": "SSD forward tokens/s + TFLOP/s (% MFMA peak) at B=8,T=2048,H=24,P=64,N=128",
         "value": tok_s,
@@ -369,11 +396,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
-        "data": "synthetic (seeded; x~N(0,1), B,C~N(0,1/N), log a=-softplus(dt)exp(A_log))",
+        "data": ("synthetic (seeded; x~N(0,1), B,C~N(0,1/N), log a=-softplus(dt)exp(A_log))" if fe == "log_a" else
+                 "synthetic (seeded; x~N(0,1), B,C~N(0,1/N), dt and A_log in, log a and the input scale "
+                 "softplus(dt) formed in the kernels)"),
         "config": {"workload": args.workload, "batch": cfg["batch"], "seqlen": cfg["seqlen"],
                    "nheads": cfg["nheads"], "ngroups": cfg["ngroups"], "headdim": cfg["headdim"],
                    "dstate": cfg["dstate"], "chunk": cfg["chunk"], "decay": cfg["decay"],
-                   "parallelism": "single GPU"},
+                   "front_end": fe, "parallelism": "single GPU"},
         "tflops": tflops,
         "mfma_peak_frac": tflops / peak_tf,
         "hbm_gbs_whole_step": nbytes / (ms / 1e3) / 1e9,
@@ -389,7 +418,7 @@ def main():
         result["decode"] = time_decode(ssd, cfg, bufs[0], stream, ev, dev)
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle (>= %.0f s)..." % args.cpu_seconds)
-        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds, fe)
     print(json.dumps(result), flush=True)
 
 

@@ -108,7 +108,9 @@ int ssd_forward(const ssd_dims* dims, const void* x, const float* log_a, const v
  * with SSD_ERR_INVALID before doing anything.  Launch order of the bf16 scalar-decay path:
  * prep (score tiles C B^T and operand layouts), then for a segmented walk the state-only
  * pass, then the chunk walk (states and outputs).  The diagonal-decay path's segmented walk runs
- * its state-only pass, the segment prefix and its walk.
+ * its state-only pass, the segment prefix and its walk.  The generic paths of ssd_forward_dt
+ * (see below) run the discretisation first and, with a skip term and the input scale, a skip
+ * pass last.
  */
 #define SSD_MAX_LAUNCHES 4
 int ssd_forward_profiled(const ssd_dims* dims, const void* x, const float* log_a, const void* B,
@@ -126,6 +128,50 @@ int ssd_forward_profiled(const ssd_dims* dims, const void* x, const float* log_a
  */
 int ssd_step(const ssd_dims* dims, float* state, const void* x_t, const float* log_a_t,
              const void* B_t, const void* C_t, const float* D, void* y_t, void* stream);
+
+/*
+ * The discretisation front-end, fused into the forward pass and the decode step (llms.blog
+ * "State Space Models and Mamba": the zero-order-hold rule A-bar = exp(Delta A) of
+ * "Continuous-to-Discrete Discretization"; the input-dependent step size, A-bar_t =
+ * exp(Delta_t A) and B-bar_t = Delta_t B_t of "The Selection Mechanism").  In place of log_a
+ * these entry points take the step-size pre-activation dt and compute, per (b, t, h):
+ *
+ *     Delta_t = softplus(dt[b,t,h] + dt_bias[h])        (dt_bias may be NULL: no bias)
+ *     log a_t = -Delta_t * exp(A_log[h])                (SSD_DECAY_SCALAR; A_log [H])
+ *     log a_t = -Delta_t * exp(A_log[h,n]) for each n   (SSD_DECAY_DIAG;   A_log [H, N])
+ *
+ * and, when scale_input is nonzero, the input term Delta_t B_t x_t^T in place of B_t x_t^T
+ * (B-bar = Delta B).  The skip term D x_t always uses the raw x_t.  dt, dt_bias and A_log are
+ * fp32 device tensors: dt [B,T,H] for the forward pass, [B,H] for the step.  Everything else
+ * (layouts, ownership, streams, errors) is as for ssd_forward and ssd_step; the workspace size
+ * differs, so it has its own query.  log a is never written to memory on the bf16 paths (scalar
+ * decay with P = 64, N in {64, 128}, chunk in {64, 128, 256}; diagonal decay with N, P in
+ * {32, 64}, chunk 64): their kernels form it from dt as they load each chunk.  Other shapes
+ * first write log a (and Delta x, when scale_input) into the workspace, run the same walk, and
+ * add the skip term afterwards.
+ * Values: dt, dt_bias and A_log must be finite; Delta_t below the fp32 normal range (dt + bias
+ * under about -87) is taken as 0 in the input term, and Delta_t above 2^64 is outside the range
+ * the kernels' exact early exits assume.
+ */
+size_t ssd_forward_dt_workspace_bytes(const ssd_dims* dims, int chunk, int scale_input);
+
+int ssd_forward_dt(const ssd_dims* dims, const void* x, const float* dt, const float* dt_bias,
+                   const float* A_log, int scale_input, const void* B, const void* C,
+                   const float* D, int chunk, const float* init_state, void* y,
+                   float* final_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssd_forward_dt with per-launch timing events, as ssd_forward_profiled. */
+int ssd_forward_dt_profiled(const ssd_dims* dims, const void* x, const float* dt,
+                            const float* dt_bias, const float* A_log, int scale_input,
+                            const void* B, const void* C, const float* D, int chunk,
+                            const float* init_state, void* y, float* final_state,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events, int n_events, int* n_launches);
+
+/* ssd_step with the discretisation front-end: dt_t [B,H], A_log [H] or [H,N]. */
+int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float* dt_t,
+                const float* dt_bias, const float* A_log, int scale_input, const void* B_t,
+                const void* C_t, const float* D, void* y_t, void* stream);
 
 /* Static, human-readable description of a return code. */
 const char* ssd_strerror(int code);

@@ -10,6 +10,10 @@ The functions carry the names of the C entry points declared in ``include/ssd.h`
               final_state=None, workspace=None, stream=None) -> (y, final_state)
   ssd_forward_profiled(..., events=(hipEvent_t handles)) -> (y, final_state, n_launches)
   ssd_step(state, x_t, log_a_t, B_t, C_t, D=None, y_t=None, stream=None) -> y_t
+  ssd_forward_dt_workspace_bytes(dims, chunk, scale_input) -> int
+  ssd_forward_dt(x, dt, A_log, B, C, D=None, dt_bias=None, scale_input=True, chunk=..., ...)
+  ssd_forward_dt_profiled(..., events=(hipEvent_t handles)) -> (y, final_state, n_launches)
+  ssd_step_dt(state, x_t, dt_t, A_log, B_t, C_t, D=None, dt_bias=None, scale_input=True, ...)
   ssd_strerror(code) -> str
 """
 from __future__ import annotations
@@ -21,7 +25,8 @@ import torch
 
 __all__ = ["SSDError", "Dims", "library_path", "load_library", "dims_for",
            "ssd_forward_workspace_bytes", "ssd_forward", "ssd_forward_profiled", "ssd_step",
-           "ssd_strerror",
+           "ssd_forward_dt_workspace_bytes", "ssd_forward_dt", "ssd_forward_dt_profiled",
+           "ssd_step_dt", "ssd_strerror",
            "SSD_F32", "SSD_BF16", "SSD_DECAY_SCALAR", "SSD_DECAY_DIAG"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -73,6 +78,15 @@ def load_library():
         lib.ssd_forward_profiled.restype = i32
         lib.ssd_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.ssd_step.restype = i32
+        lib.ssd_forward_dt_workspace_bytes.argtypes = [dp, i32, i32]
+        lib.ssd_forward_dt_workspace_bytes.restype = sz
+        dt_args = [dp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        lib.ssd_forward_dt.argtypes = dt_args
+        lib.ssd_forward_dt.restype = i32
+        lib.ssd_forward_dt_profiled.argtypes = dt_args + [ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
+        lib.ssd_forward_dt_profiled.restype = i32
+        lib.ssd_step_dt.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+        lib.ssd_step_dt.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -186,6 +200,112 @@ def _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, st
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_forward")
     return y, final_state, launches
+
+
+def ssd_forward_dt_workspace_bytes(dims: Dims, chunk: int, scale_input: bool = True) -> int:
+    return int(load_library().ssd_forward_dt_workspace_bytes(ctypes.byref(dims), int(chunk),
+                                                             1 if scale_input else 0))
+
+
+def ssd_forward_dt(x, dt, A_log, B, C, D=None, dt_bias=None, scale_input: bool = True,
+                   chunk: int = 64, init_state=None, y=None, final_state=None, workspace=None,
+                   stream=None):
+    """Run ``ssd_forward_dt``: the forward pass with log a = -softplus(dt + dt_bias) exp(A_log)
+    formed in the kernels, and (scale_input) the input term scaled by softplus(dt + dt_bias).
+    dt [B,T,H] fp32; A_log [H] (scalar decay) or [H,N] (diagonal decay); dt_bias [H] or None.
+    Returns (y, final_state)."""
+    return _forward_dt(x, dt, A_log, B, C, D, dt_bias, scale_input, chunk, init_state, y,
+                       final_state, workspace, stream)[:2]
+
+
+def ssd_forward_dt_profiled(x, dt, A_log, B, C, D=None, dt_bias=None, scale_input: bool = True,
+                            chunk: int = 64, init_state=None, y=None, final_state=None,
+                            workspace=None, stream=None, events=()):
+    """``ssd_forward_dt_profiled``: as ssd_forward_dt, with per-launch timing events as
+    ssd_forward_profiled.  Returns (y, final_state, n_launches)."""
+    return _forward_dt(x, dt, A_log, B, C, D, dt_bias, scale_input, chunk, init_state, y,
+                       final_state, workspace, stream, events=list(events))
+
+
+def _forward_dt(x, dt, A_log, B, C, D, dt_bias, scale_input, chunk, init_state, y, final_state,
+                workspace, stream, events=None):
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [B,T,H,P] and B [B,T,G,N]")
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+    bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    decay = SSD_DECAY_DIAG if A_log.dim() == 2 else SSD_DECAY_SCALAR
+    dims = Dims(bsz, T, H, G, P, N, _DTYPE_CODE[x.dtype], decay)
+    dev = x.device
+    _check(x, "x", (bsz, T, H, P), x.dtype, dev)
+    _check(dt, "dt", (bsz, T, H), torch.float32, dev)
+    _check(A_log, "A_log", (H, N) if decay == SSD_DECAY_DIAG else (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(B, "B", (bsz, T, G, N), x.dtype, dev)
+    _check(C, "C", (bsz, T, G, N), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (bsz, H, N, P), torch.float32, dev)
+    if y is None:
+        y = torch.empty((bsz, T, H, P), dtype=x.dtype, device=dev)
+    _check(y, "y", (bsz, T, H, P), x.dtype, dev)
+    if final_state is True:
+        final_state = torch.empty((bsz, H, N, P), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    _check(final_state, "final_state", (bsz, H, N, P), torch.float32, dev)
+    lib = load_library()
+    scale = 1 if scale_input else 0
+    need = int(lib.ssd_forward_dt_workspace_bytes(ctypes.byref(dims), int(chunk), scale))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), scale, _ptr(B),
+            _ptr(C), _ptr(D), int(chunk), _ptr(init_state), _ptr(y), _ptr(final_state),
+            _ptr(workspace), ws_bytes, _stream_handle(stream, dev))
+    if events is None:
+        rc = lib.ssd_forward_dt(*args)
+        launches = None
+    else:
+        n = max(len(events), 2 * SSD_MAX_LAUNCHES)
+        arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+        count = ctypes.c_int(0)
+        rc = lib.ssd_forward_dt_profiled(*args, arr, n, ctypes.byref(count))
+        launches = count.value
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_forward_dt")
+    return y, final_state, launches
+
+
+def ssd_step_dt(state, x_t, dt_t, A_log, B_t, C_t, D=None, dt_bias=None, scale_input: bool = True,
+                y_t=None, stream=None):
+    """Run ``ssd_step_dt``: one token with the discretisation front-end, ``state`` updated in
+    place.  dt_t [B,H] fp32; A_log [H] or [H,N]; other arguments as ssd_step."""
+    bsz, H, N, P = state.shape
+    G = B_t.shape[1]
+    dev = state.device
+    decay = SSD_DECAY_DIAG if A_log.dim() == 2 else SSD_DECAY_SCALAR
+    if x_t.dtype not in _DTYPE_CODE:
+        raise TypeError("x_t must be float32 or bfloat16")
+    dims = Dims(bsz, 1, H, G, P, N, _DTYPE_CODE[x_t.dtype], decay)
+    _check(state, "state", (bsz, H, N, P), torch.float32, dev)
+    _check(x_t, "x_t", (bsz, H, P), x_t.dtype, dev)
+    _check(dt_t, "dt_t", (bsz, H), torch.float32, dev)
+    _check(A_log, "A_log", (H, N) if decay == SSD_DECAY_DIAG else (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(B_t, "B_t", (bsz, G, N), x_t.dtype, dev)
+    _check(C_t, "C_t", (bsz, G, N), x_t.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    if y_t is None:
+        y_t = torch.empty((bsz, H, P), dtype=x_t.dtype, device=dev)
+    _check(y_t, "y_t", (bsz, H, P), x_t.dtype, dev)
+    rc = load_library().ssd_step_dt(ctypes.byref(dims), _ptr(state), _ptr(x_t), _ptr(dt_t),
+                                    _ptr(dt_bias), _ptr(A_log), 1 if scale_input else 0,
+                                    _ptr(B_t), _ptr(C_t), _ptr(D), _ptr(y_t),
+                                    _stream_handle(stream, dev))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_step_dt")
+    return y_t
 
 
 def ssd_step(state, x_t, log_a_t, B_t, C_t, D=None, y_t=None, stream=None):

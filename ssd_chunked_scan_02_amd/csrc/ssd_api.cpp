@@ -50,6 +50,23 @@ size_t workspace_needed(const ssd_dims* d, int chunk) {
     return ssd::scores_bytes(d->batch, d->ngroups, nchunks, chunk);
 }
 
+// Workspace of ssd_forward_dt: the fused paths need what ssd_forward needs (plus log2 of the
+// input scale on the scalar fast path); the generic composition adds log a and the scaled input.
+size_t workspace_needed_dt(const ssd_dims* d, int chunk, bool scale_input) {
+    if (d->seqlen == 0 || d->batch == 0) return 0;
+    const int N = (int)d->dstate, P = (int)d->headdim;
+    if (ssd::discretization_fused(d->dtype, d->decay, N, P, chunk, d->nheads, d->ngroups)) {
+        if (d->decay == SSD_DECAY_DIAG)
+            return ssd::diag_workspace_bytes(d->dtype, d->batch, d->nheads, d->seqlen, N, P, chunk);
+        return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, d->seqlen, N, chunk, scale_input);
+    }
+    const size_t own = ssd::generic_workspace_bytes(d->dtype, d->decay, d->batch, d->nheads, d->ngroups,
+                                                    d->seqlen, N, P, chunk);
+    return ssd::dt_generic_layout(own, d->batch, d->seqlen, d->nheads, d->decay == SSD_DECAY_DIAG ? N : 1, P,
+                                  d->dtype == SSD_BF16 ? 2 : 4, scale_input)
+        .total;
+}
+
 int check_forward(const ssd_dims* d, int chunk) {
     int rc = check_dims(d, true);
     if (rc != SSD_OK) return rc;
@@ -62,6 +79,97 @@ int check_forward(const ssd_dims* d, int chunk) {
     if (ssd::walk_lds_bytes(d->dtype, (int)d->dstate, (int)d->headdim, chunk) > ssd::kMaxLds)
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
+}
+
+struct Discretization {
+    const float* dt;
+    const float* dt_bias;
+    const float* A_log;
+    bool scale_input;
+};
+
+// ssd_forward (disc null: log_a given) and ssd_forward_dt (disc set: log_a null).
+int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Discretization* disc,
+                 const void* B, const void* C, const float* D, int chunk, const float* init_state,
+                 void* y, float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                 void* const* events, int n_events, int* n_launches) {
+    if (n_launches) *n_launches = 0;
+    if (events && n_events < 2 * SSD_MAX_LAUNCHES) return SSD_ERR_INVALID;
+    int rc = check_forward(d, chunk);
+    if (rc != SSD_OK) return rc;
+    const bool has_tokens = d->batch > 0 && d->seqlen > 0;
+    const float* decay_in = disc ? disc->dt : log_a;
+    if (has_tokens && (!x || !decay_in || !B || !C || !y)) return SSD_ERR_INVALID;
+    if (has_tokens && disc && !disc->A_log) return SSD_ERR_INVALID;
+    const void* ptrs[] = {x, log_a, B, C, D, init_state, y, final_state, workspace,
+                          disc ? disc->dt : nullptr, disc ? disc->dt_bias : nullptr, disc ? disc->A_log : nullptr};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    const size_t need = disc ? workspace_needed_dt(d, chunk, disc->scale_input) : workspace_needed(d, chunk);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
+    if (d->batch == 0) return SSD_OK;
+    if (d->seqlen == 0 && !final_state) return SSD_OK;
+
+    int count = 0;
+    ssd::ForwardLaunch fl{};
+    fl.dtype = d->dtype;
+    fl.decay = d->decay;
+    fl.batch = d->batch;
+    fl.seqlen = d->seqlen;
+    fl.nheads = d->nheads;
+    fl.ngroups = d->ngroups;
+    fl.headdim = d->headdim;
+    fl.dstate = d->dstate;
+    fl.chunk = chunk;
+    fl.nchunks = (int)((d->seqlen + chunk - 1) / chunk);
+    fl.x = x;
+    fl.log_a = log_a;
+    if (disc) {
+        fl.dt = disc->dt;
+        fl.dt_bias = disc->dt_bias;
+        fl.A_log = disc->A_log;
+        fl.scale_input = disc->scale_input ? 1 : 0;
+    }
+    fl.Bm = B;
+    fl.Cm = C;
+    fl.D = D;
+    fl.init = init_state;
+    fl.y = y;
+    fl.final_state = final_state;
+    fl.scores = static_cast<float*>(workspace);
+    fl.events = reinterpret_cast<hipEvent_t const*>(events);
+    fl.n_events = events ? n_events : 0;
+    fl.n_launches = &count;
+    fl.first_launch = 0;
+    rc = ssd::launch_forward(fl, static_cast<hipStream_t>(stream));
+    if (n_launches) *n_launches = count;
+    if (rc == -2) return SSD_ERR_UNSUPPORTED;
+    return rc == 0 ? SSD_OK : SSD_ERR_HIP;
+}
+
+// ssd_step (disc null) and ssd_step_dt.
+int step_impl(const ssd_dims* d, float* state, const void* x_t, const float* log_a_t, const Discretization* disc,
+              const void* B_t, const void* C_t, const float* D, void* y_t, void* stream) {
+    int rc = check_dims(d, false);
+    if (rc != SSD_OK) return rc;
+    if (d->headdim > 256 || 256 % d->headdim != 0) return SSD_ERR_UNSUPPORTED;
+    if (d->batch == 0) return SSD_OK;
+    const float* decay_in = disc ? disc->dt : log_a_t;
+    if (!state || !x_t || !decay_in || !B_t || !C_t || !y_t || (disc && !disc->A_log)) return SSD_ERR_INVALID;
+    const void* ptrs[] = {state, x_t, log_a_t, B_t, C_t, D, y_t,
+                          disc ? disc->dt : nullptr, disc ? disc->dt_bias : nullptr, disc ? disc->A_log : nullptr};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    ssd::StepParams sp{state, x_t, log_a_t, B_t, C_t, D, y_t, d->nheads, d->ngroups,
+                       (int)d->headdim, (int)d->dstate, d->decay == SSD_DECAY_DIAG ? 1 : 0};
+    if (disc) {
+        sp.dt_t = disc->dt;
+        sp.dt_bias = disc->dt_bias;
+        sp.A_log = disc->A_log;
+        sp.scale_input = disc->scale_input ? 1 : 0;
+    }
+    rc = ssd::launch_step(sp, d->dtype, d->batch * d->nheads, static_cast<hipStream_t>(stream));
+    return rc == 0 ? SSD_OK : SSD_ERR_HIP;
 }
 
 }  // namespace
@@ -84,62 +192,44 @@ int ssd_forward_profiled(const ssd_dims* d, const void* x, const float* log_a, c
                          const void* C, const float* D, int chunk, const float* init_state,
                          void* y, float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream, void* const* events, int n_events, int* n_launches) {
-    if (n_launches) *n_launches = 0;
-    if (events && n_events < 2 * SSD_MAX_LAUNCHES) return SSD_ERR_INVALID;
-    int rc = check_forward(d, chunk);
-    if (rc != SSD_OK) return rc;
-    const bool has_tokens = d->batch > 0 && d->seqlen > 0;
-    if (has_tokens && (!x || !log_a || !B || !C || !y)) return SSD_ERR_INVALID;
-    const void* ptrs[] = {x, log_a, B, C, D, init_state, y, final_state, workspace};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
-    const size_t need = workspace_needed(d, chunk);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
-    if (d->batch == 0) return SSD_OK;
-    if (d->seqlen == 0 && !final_state) return SSD_OK;
+    return forward_impl(d, x, log_a, nullptr, B, C, D, chunk, init_state, y, final_state, workspace,
+                        workspace_bytes, stream, events, n_events, n_launches);
+}
 
-    ssd::ForwardLaunch fl{};
-    fl.dtype = d->dtype;
-    fl.decay = d->decay;
-    fl.batch = d->batch;
-    fl.seqlen = d->seqlen;
-    fl.nheads = d->nheads;
-    fl.ngroups = d->ngroups;
-    fl.headdim = d->headdim;
-    fl.dstate = d->dstate;
-    fl.chunk = chunk;
-    fl.nchunks = (int)((d->seqlen + chunk - 1) / chunk);
-    fl.x = x;
-    fl.log_a = log_a;
-    fl.Bm = B;
-    fl.Cm = C;
-    fl.D = D;
-    fl.init = init_state;
-    fl.y = y;
-    fl.final_state = final_state;
-    fl.scores = static_cast<float*>(workspace);
-    fl.events = reinterpret_cast<hipEvent_t const*>(events);
-    fl.n_events = events ? n_events : 0;
-    fl.n_launches = n_launches;
-    rc = ssd::launch_forward(fl, static_cast<hipStream_t>(stream));
-    if (rc == -2) return SSD_ERR_UNSUPPORTED;
-    return rc == 0 ? SSD_OK : SSD_ERR_HIP;
+size_t ssd_forward_dt_workspace_bytes(const ssd_dims* dims, int chunk, int scale_input) {
+    if (check_forward(dims, chunk) != SSD_OK) return 0;
+    return workspace_needed_dt(dims, chunk, scale_input != 0);
+}
+
+int ssd_forward_dt(const ssd_dims* d, const void* x, const float* dt, const float* dt_bias,
+                   const float* A_log, int scale_input, const void* B, const void* C,
+                   const float* D, int chunk, const float* init_state, void* y,
+                   float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    return ssd_forward_dt_profiled(d, x, dt, dt_bias, A_log, scale_input, B, C, D, chunk, init_state, y,
+                                   final_state, workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+int ssd_forward_dt_profiled(const ssd_dims* d, const void* x, const float* dt,
+                            const float* dt_bias, const float* A_log, int scale_input,
+                            const void* B, const void* C, const float* D, int chunk,
+                            const float* init_state, void* y, float* final_state,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events, int n_events, int* n_launches) {
+    const Discretization disc{dt, dt_bias, A_log, scale_input != 0};
+    return forward_impl(d, x, nullptr, &disc, B, C, D, chunk, init_state, y, final_state, workspace,
+                        workspace_bytes, stream, events, n_events, n_launches);
 }
 
 int ssd_step(const ssd_dims* d, float* state, const void* x_t, const float* log_a_t, const void* B_t,
              const void* C_t, const float* D, void* y_t, void* stream) {
-    int rc = check_dims(d, false);
-    if (rc != SSD_OK) return rc;
-    if (d->headdim > 256 || 256 % d->headdim != 0) return SSD_ERR_UNSUPPORTED;
-    if (d->batch == 0) return SSD_OK;
-    if (!state || !x_t || !log_a_t || !B_t || !C_t || !y_t) return SSD_ERR_INVALID;
-    const void* ptrs[] = {state, x_t, log_a_t, B_t, C_t, D, y_t};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
-    ssd::StepParams sp{state, x_t, log_a_t, B_t, C_t, D, y_t, d->nheads, d->ngroups,
-                       (int)d->headdim, (int)d->dstate, d->decay == SSD_DECAY_DIAG ? 1 : 0};
-    rc = ssd::launch_step(sp, d->dtype, d->batch * d->nheads, static_cast<hipStream_t>(stream));
-    return rc == 0 ? SSD_OK : SSD_ERR_HIP;
+    return step_impl(d, state, x_t, log_a_t, nullptr, B_t, C_t, D, y_t, stream);
+}
+
+int ssd_step_dt(const ssd_dims* d, float* state, const void* x_t, const float* dt_t,
+                const float* dt_bias, const float* A_log, int scale_input, const void* B_t,
+                const void* C_t, const float* D, void* y_t, void* stream) {
+    const Discretization disc{dt_t, dt_bias, A_log, scale_input != 0};
+    return step_impl(d, state, x_t, nullptr, &disc, B_t, C_t, D, y_t, stream);
 }
 
 const char* ssd_strerror(int code) {

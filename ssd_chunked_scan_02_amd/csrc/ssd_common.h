@@ -59,6 +59,32 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
     *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
+// The step size of the discretisation front-end: softplus(v) = log(1 + e^v), written as
+// max(v, 0) + log(1 + e^-|v|) so that no intermediate overflows.
+__device__ __forceinline__ float softplusf(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
+__device__ __forceinline__ double softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
+// log2 softplus(v).  Below v = -20, softplus(v) = e^v (1 - e^v / 2 + ...), so log2 of it is
+// v log2(e) to within 2e-9; that form stays exact where softplus(v) itself underflows.
+__device__ __forceinline__ float log2_softplusf(float v) {
+    return v < -20.f ? v * 1.4426950408889634f : log2f(softplusf(v));
+}
+
+// softplus on the hardware exp2 and log2 units (v_exp_f32, v_log_f32), for the bf16 paths'
+// front-end.  With e = e^-|v| in (0, 1], log(1 + e) is the series e - e^2/2 + e^3/3 - e^4/4
+// below e = 2^-6 (truncation under e^5/5) and log2(1 + e) ln 2 above, where rounding 1 + e
+// costs at most 2^-18 of e: a relative error of a few 1e-6 in all.  Below v = -87 (e under the
+// normal range) the result is max(v, 0) = 0.
+__device__ __forceinline__ float softplus_hw(float v) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(v) * 1.4426950408889634f);
+    const float series = e * (1.f - e * (0.5f - e * (0.33333334f - 0.25f * e)));
+    const float l = e < 0.015625f ? series : __builtin_amdgcn_logf(1.f + e) * 0.6931471805599453f;
+    return fmaxf(v, 0.f) + l;
+}
+// log2 of softplus(v) = sp (from softplus_hw): v log2(e) below v = -20, as in log2_softplusf.
+__device__ __forceinline__ float log2_softplus_hw(float v, float sp) {
+    return v < -20.f ? v * 1.4426950408889634f : __builtin_amdgcn_logf(sp);
+}
+
 // Block-wide inclusive scan of one value per thread (kThreads threads).  `scratch` holds
 // kWaves values of type V in LDS.  Contains two __syncthreads().
 template <typename V>

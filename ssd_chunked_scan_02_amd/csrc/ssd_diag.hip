@@ -462,7 +462,10 @@ struct DiagPipeLayout {
 
 // FULL: the walk.  !FULL: the state-only pass of a segmented walk (H over the segment from a
 // zero state, written to seg_state with the segment's log2 decay per state row in seg_decay).
-template <int N, int P, bool FULL>
+// DT: the discretisation front-end (prm.dt): log a = -softplus(dt + bias) exp(A_log[h, n]) is
+// formed as each chunk is staged, and with prm.scale_input the staged B rows carry the input
+// scale softplus(dt + bias) (B-bar = Delta B: B only ever enters as the key/input side).
+template <int N, int P, bool FULL, bool DT = false>
 __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams prm) {
     constexpr int kThreads = kDiagThreads, kWaves = kDiagWaves;  // (this kernel's own workgroup)
     using L = DiagPipeLayout<N, P, FULL>;
@@ -503,6 +506,18 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     float* Sl = reinterpret_cast<float*>(smem + L::sl);
 
     const float* lag = prm.log_a;
+    const float* dtg = prm.dt;
+    // (DT) this thread's log a factors -exp(A_log[h, n]) log2(e) for its 4 state dims: the la
+    // pieces it stages all sit at n = 4 (tid % (N / 4)), since the thread count is a multiple
+    // of N / 4
+    static_assert(kThreads % (N / 4) == 0, "la pieces of a thread share their state dims");
+    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+    float dt_b = 0.f;
+    if (DT) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a4[j] = -expf(prm.A_log[h * N + 4 * (tid % (N / 4)) + j]) * kLog2eD;
+        dt_b = prm.dt_bias ? prm.dt_bias[h] : 0.f;
+    }
     const __bf16* xg = static_cast<const __bf16*>(prm.x);
     const __bf16* Bg = static_cast<const __bf16*>(prm.Bm);
     const __bf16* Cg = static_cast<const __bf16*>(prm.Cm);
@@ -514,13 +529,18 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     // ---- prefetch registers: one chunk of log a, B, C and x rows (rows clamped into the
     //      sequence; staged as zeros past its end)
     uint4 rla[LAI], rb[BCI], rc[BCI], rx[XI];
+    // (DT) dt of token `lane` of the chunk (Q = 64 tokens, one per lane): each lane forms that
+    // token's step size once, and the threads staging a row take it from that lane
+    static_assert(!DT || Q == kWave, "one token per lane");
+    float rdt = 0.f;
     auto load_chunk = [&](int c) {
         const int64_t t0 = (int64_t)c * Q;
         const int last = chunk_len(c) - 1;
+        if (DT) rdt = dtg[(b * Tn + t0 + min(lane, last)) * H + h];
 #pragma unroll
         for (int m = 0; m < LAI; ++m) {
             const int id = tid + kThreads * m, t = min(id / (N / 4), last), c4 = id % (N / 4);
-            if (id < LAT) rla[m] = ld16(lag + ((b * Tn + t0 + t) * H + h) * N + 4 * c4);
+            if (!DT && id < LAT) rla[m] = ld16(lag + ((b * Tn + t0 + t) * H + h) * N + 4 * c4);
         }
 #pragma unroll
         for (int m = 0; m < BCI; ++m) {
@@ -539,20 +559,31 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     };
     auto stage_chunk = [&](int c) {
         const int len = chunk_len(c);
+        const float delta = DT ? softplus_hw(rdt + dt_b) : 0.f;  // step size of token `lane`
 #pragma unroll
         for (int m = 0; m < LAI; ++m) {
             const int id = tid + kThreads * m, t = id / (N / 4), c4 = id % (N / 4);
+            // (the shuffle outside the branch: every lane of the wave takes part)
+            const float dt_row = DT ? __shfl(delta, t % Q, kWave) : 0.f;
             // log a in log2 units, so that every factor below is one exp2
             if (id < LAT) {
-                const f32x4 v = __builtin_bit_cast(f32x4, rla[m]) * kLog2eD;
+                const f32x4 v = DT ? dt_row * a4 : __builtin_bit_cast(f32x4, rla[m]) * kLog2eD;
                 st16(cum + t * CS + 4 * c4, t < len ? __builtin_bit_cast(uint4, v) : zero);
             }
         }
 #pragma unroll
         for (int m = 0; m < BCI; ++m) {
             const int id = tid + kThreads * m, t = id / (N / 8), c8 = id % (N / 8);
+            const float dt_row = DT ? __shfl(delta, t % Q, kWave) : 0.f;
             if (id < BCT) {
-                st16(Braw + t * NP + 8 * c8, t < len ? rb[m] : zero);
+                uint4 bv = rb[m];
+                if (DT && prm.scale_input) {
+                    bf16x8 sv = as_bf16x8(bv);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sv[j] = (__bf16)((float)sv[j] * dt_row);
+                    bv = __builtin_bit_cast(uint4, sv);
+                }
+                st16(Braw + t * NP + 8 * c8, t < len ? bv : zero);
                 if (FULL) st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
             }
         }
@@ -883,7 +914,7 @@ int launch_diag_t(const ForwardLaunch& fl, hipStream_t stream) {
     WalkParams wp{fl.x, fl.log_a, fl.Bm, fl.Cm, fl.D, nullptr, fl.init, fl.y, fl.final_state,
                   fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.chunk, fl.nchunks, per_xcd};
     const size_t lds = DiagLayout<T, N, P>(fl.chunk).total;
-    int k = 0;
+    int k = fl.first_launch;
     return launch_k(fl, k, walk_diag_kernel<T, N, P>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp)
                ? 0
                : -1;
@@ -933,18 +964,18 @@ bool diag_pipe_shape(int dtype, int N, int P, int chunk) {
     return dtype == 1 && chunk == kDiagQ && (N == 32 || N == 64) && (P == 32 || P == 64);
 }
 
-template <int N, int P>
+template <int N, int P, bool DT>
 int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
-    static bool attr_set[64][2] = {};
+    static bool attr_set[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-    if (!attr_set[dev][0]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, true>),
+    if (!attr_set[dev]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, true, DT>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, false>),
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, false, DT>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
             return -1;
-        attr_set[dev][0] = true;
+        attr_set[dev] = true;
     }
     const DiagSegLayout sl = diag_seg_layout(fl.batch, fl.nheads, fl.seqlen, N, P);
     const int64_t units = fl.batch * fl.nheads;
@@ -955,26 +986,29 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
                   sl.seg_chunks, sl.nseg,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.init) : nullptr,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.state) : nullptr,
-                  sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.decay) : nullptr};
+                  sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.decay) : nullptr,
+                  fl.dt, fl.dt_bias, fl.A_log, fl.scale_input};
     const size_t lds = DiagPipeLayout<N, P, true>::total, slds = DiagPipeLayout<N, P, false>::total;
-    int k = 0;
+    int k = fl.first_launch;
     if (sl.nseg > 1) {
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         WalkParams sp = wp;
         sp.per_xcd = ((sl.nseg - 1) * units + 7) / 8;
         sp.nseg = sl.nseg - 1;
-        if (!launch_k(fl, k, walk_diag_pipe_kernel<N, P, false>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kDiagThreads),
+        if (!launch_k(fl, k, walk_diag_pipe_kernel<N, P, false, DT>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kDiagThreads),
                       slds, stream, sp))
             return -1;
         if (launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1,
                               stream) != 0)
             return -1;
     }
-    return launch_k(fl, k, walk_diag_pipe_kernel<N, P, true>, dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
+    return launch_k(fl, k, walk_diag_pipe_kernel<N, P, true, DT>, dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
                     stream, wp)
                ? 0
                : -1;
 }
+
+bool diag_pipe_applies(int dtype, int N, int P, int chunk) { return diag_pipe_shape(dtype, N, P, chunk); }
 
 size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk) {
     if (!diag_pipe_shape(dtype, N, P, chunk)) return 0;
@@ -983,10 +1017,15 @@ size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t se
 
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream) {
     if (diag_pipe_shape(fl.dtype, (int)fl.dstate, (int)fl.headdim, fl.chunk)) {
-        if (fl.dstate == 64 && fl.headdim == 64) return launch_diag_pipe_t<64, 64>(fl, stream);
-        if (fl.dstate == 64 && fl.headdim == 32) return launch_diag_pipe_t<64, 32>(fl, stream);
-        if (fl.dstate == 32 && fl.headdim == 64) return launch_diag_pipe_t<32, 64>(fl, stream);
-        if (fl.dstate == 32 && fl.headdim == 32) return launch_diag_pipe_t<32, 32>(fl, stream);
+        const bool dt = fl.dt != nullptr;
+        if (fl.dstate == 64 && fl.headdim == 64)
+            return dt ? launch_diag_pipe_t<64, 64, true>(fl, stream) : launch_diag_pipe_t<64, 64, false>(fl, stream);
+        if (fl.dstate == 64 && fl.headdim == 32)
+            return dt ? launch_diag_pipe_t<64, 32, true>(fl, stream) : launch_diag_pipe_t<64, 32, false>(fl, stream);
+        if (fl.dstate == 32 && fl.headdim == 64)
+            return dt ? launch_diag_pipe_t<32, 64, true>(fl, stream) : launch_diag_pipe_t<32, 64, false>(fl, stream);
+        if (fl.dstate == 32 && fl.headdim == 32)
+            return dt ? launch_diag_pipe_t<32, 32, true>(fl, stream) : launch_diag_pipe_t<32, 32, false>(fl, stream);
     }
 #define SSD_DLAUNCH(TT, NN, PP) \
     if ((std::is_same<TT, float>::value ? 0 : 1) == fl.dtype && fl.dstate == NN && fl.headdim == PP) \

@@ -142,9 +142,11 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
     if (do_rest) {
         // log a head-major: item (head, 4 tokens) gathers 4 rows (consecutive threads read
         // consecutive heads of a row) and writes 16 contiguous bytes; rows clamped, masked below
+        // (with the discretisation front-end the same items read dt, laid out as log a, and
+        // turn it into log a and log2 of the input scale)
         const int HG = (int)(prm.nheads / prm.ngroups);
         const int nla = HG * (Q / 4);
-        const float* lag = prm.log_a + (b * prm.seqlen + t0) * prm.nheads + g * HG;
+        const float* lag = (prm.dt ? prm.dt : prm.log_a) + (b * prm.seqlen + t0) * prm.nheads + g * HG;
         const int wave0 = tid - lane;  // first thread of this wave
         f32x4 lv[kPrepLa];
 #pragma unroll
@@ -156,15 +158,33 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
         }
         {
             const int64_t tpad = (int64_t)prm.nchunks * Q;
-            float* dst = prm.la_t + (b * prm.nheads + g * HG) * tpad + t0;
+            const int64_t off0 = (b * prm.nheads + g * HG) * tpad + t0;
+            float* dst = prm.la_t + off0;
 #pragma unroll
             for (int i = 0; i < kPrepLa; ++i) {
                 const int id = tid + kPrepThreads * i, hl = id % HG, t4 = 4 * (id / HG);
                 if (wave0 + kPrepThreads * i >= nla) continue;
-                f32x4 v;
+                f32x4 v, lgv = {0.f, 0.f, 0.f, 0.f};
+                if (prm.dt) {
+                    // log a = -softplus(dt + bias) exp(A_log), and log2 softplus(dt + bias)
+                    const int64_t hh = g * HG + min(id, nla - 1) % HG;
+                    const float bias = prm.dt_bias ? prm.dt_bias[hh] : 0.f;
+                    const float ea = expf(prm.A_log[hh]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = t4 + j < len ? lv[i][j] : 0.f;
-                if (id < nla) *reinterpret_cast<f32x4*>(dst + hl * tpad + t4) = v;
+                    for (int j = 0; j < 4; ++j) {
+                        const float u = lv[i][j] + bias;
+                        const float sp = softplus_hw(u);
+                        v[j] = t4 + j < len ? -sp * ea : 0.f;
+                        lgv[j] = t4 + j < len ? log2_softplus_hw(u, sp) : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = t4 + j < len ? lv[i][j] : 0.f;
+                }
+                if (id < nla) {
+                    *reinterpret_cast<f32x4*>(dst + hl * tpad + t4) = v;
+                    if (prm.lg_t) *reinterpret_cast<f32x4*>(prm.lg_t + off0 + hl * tpad + t4) = lgv;
+                }
             }
         }
     }
@@ -286,8 +306,9 @@ struct WalkShape {
     static constexpr int LA = Q / 64, QW = Q / 4, XCH = QW * 8 / kWave, NPAIR = n_pairs(NT);
     static constexpr int PB = kP / 16, HS = N + 8;
     // one decay-factor buffer, floats: cum2 [Q] (log2 e times the running sum of log a),
-    // f [Q], w [Q], U [NT][Q], ea [NT]
-    static constexpr int FSZ = 3 * Q + NT * Q + NT;
+    // f [Q], w [Q], U [NT][Q], ea [NT], cs2 [Q] (the running sums on the input side of a
+    // factor: cum2 - log2 of the input scale, written only with one)
+    static constexpr int FSZ = 4 * Q + NT * Q + NT;
     static constexpr int YROWS = 16 * TBW;  // output rows of one output wave per chunk
     static constexpr size_t lds_bytes =
         (size_t)(4 * Q * kXStr + 2 * kP * HS + 4 * YROWS * kXStr) * 2 + (size_t)2 * FSZ * 4;
@@ -320,6 +341,7 @@ struct WalkLds {
     __device__ float* w(int buf) const { return Fs + buf * WS::FSZ + 2 * Q; }
     __device__ float* U(int buf) const { return Fs + buf * WS::FSZ + 3 * Q; }
     __device__ float* ea(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q; }
+    __device__ float* cs2(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q + WS::NT; }
 };
 
 // The piece of work of one workgroup: a (batch, head) unit and the chunks [c0, c1) of one
@@ -342,7 +364,7 @@ __device__ __forceinline__ WalkSpan walk_span(const Walk2Params& prm, int64_t wo
     return sp;
 }
 
-template <int N, int Q, int OW>
+template <int N, int Q, int OW, bool DT>
 __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
                                                  int lane) {
     const int64_t b = span.b, h = span.h, g = span.g;
@@ -406,6 +428,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         const __bf16* xsm = L.Xs + buf * Q * kXStr;
         const __bf16* hcur = L.Hs + buf * kP * HS;
         const float* cum2 = L.cum2(buf);
+        const float* cin2 = DT ? L.cs2(buf) : cum2;  // input side of the in-block factors
         const float* ffa = L.f(buf);
         const float* Ut = L.U(buf);
         const float* ea = L.ea(buf);
@@ -471,7 +494,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb) acc[r][pb] *= ft;
                     const float ct = cum2[t];
-                    const f32x4 cd = *reinterpret_cast<const f32x4*>(cum2 + 16 * tb + 4 * lg);
+                    const f32x4 cd = *reinterpret_cast<const f32x4*>(cin2 + 16 * tb + 4 * lg);
                     if (tb % 2 == 0) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -528,7 +551,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
 }
 
 // The state waves of the walk (they also stage everything the output waves read).
-template <int N, int Q, int SW>
+template <int N, int Q, int SW, bool DT>
 __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
                                                 int lane) {
     const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
@@ -541,12 +564,14 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     const int nchunks = prm.nchunks;
     const uint32_t x_row = (uint32_t)(H * kP * 2);
     const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
+    const float* lg0 = DT ? prm.lg_t + unit * (int64_t)nchunks * Q : nullptr;
     const __bf16* xg = static_cast<const __bf16*>(prm.x);
     const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * (N / 16) * KS * 512;
     const uint4 zero = {0u, 0u, 0u, 0u};
     auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
 
     float la[LA];
+    float lgs[DT ? LA : 1];  // (DT) log2 of the input scale of the same tokens
     uint4 xs[XCH];
     uint4 bt[NBW][KS];
     // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
@@ -556,6 +581,9 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         const int64_t t0 = (int64_t)c * Q;
 #pragma unroll
         for (int j = 0; j < LA; ++j) la[j] = la0[t0 + lane * LA + j];
+        if (DT)
+#pragma unroll
+            for (int j = 0; j < LA; ++j) lgs[j] = lg0[t0 + lane * LA + j];
     };
     auto load_x = [&](int c) {
         const int last = chunk_len(c) - 1;
@@ -587,14 +615,20 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         const float last2 = lane_value(incl, kWave - 1) * kLog2e;
         // running sum at the first token of this lane's 16-token block
         const float blk2 = __shfl(cum[0], lane & ~(16 / LA - 1), kWave);
+        // the input side of each factor: with an input scale, exp2(c - cum_s) times the scale of
+        // token s is exp2(c - (cum_s - log2 scale_s))
+        float cin[LA];
+#pragma unroll
+        for (int j = 0; j < LA; ++j) cin[j] = DT ? cum[j] - lgs[j] : cum[j];
         // this wave's quarter of the tokens: lanes [16 SW, 16 SW + 16)
         if (lane / 16 == SW) {
 #pragma unroll
             for (int j = 0; j < LA; ++j) {
                 const int t = lane * LA + j;
                 L.cum2(buf)[t] = cum[j];
+                if (DT) L.cs2(buf)[t] = cin[j];
                 L.f(buf)[t] = fexp2(cum[j] - blk2);
-                L.w(buf)[t] = fexp2(last2 - cum[j]);
+                L.w(buf)[t] = fexp2(last2 - cin[j]);
             }
         }
         // rows SW, SW + 4, ... of U
@@ -605,7 +639,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
             for (int j = 0; j < LA; ++j) {
                 const int s = lane * LA + j;
-                urow[s] = s < 16 * tb ? fexp2(ca - cum[j]) : 0.f;
+                urow[s] = s < 16 * tb ? fexp2(ca - cin[j]) : 0.f;
             }
         }
         if (SW == 0) {
@@ -742,7 +776,9 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     }
 }
 
-template <int N, int Q>
+// DT: with log2 of an input scale per token (prm.lg_t, the discretisation front-end's Delta):
+// the input side of every factor carries it, so the input term is Delta_s B_s x_s^T.
+template <int N, int Q, bool DT>
 __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm) {
     const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
     if (work < 0) return;
@@ -752,20 +788,23 @@ __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm
     extern __shared__ __align__(16) unsigned char smem[];
     const WalkLds<N, Q> L(smem);
     switch (wave) {
-        case 0: walk_output_role<N, Q, 0>(prm, L, span, lane); break;
-        case 1: walk_output_role<N, Q, 1>(prm, L, span, lane); break;
-        case 2: walk_output_role<N, Q, 2>(prm, L, span, lane); break;
-        case 3: walk_output_role<N, Q, 3>(prm, L, span, lane); break;
-        case 4: walk_state_role<N, Q, 0>(prm, L, span, lane); break;
-        case 5: walk_state_role<N, Q, 1>(prm, L, span, lane); break;
-        case 6: walk_state_role<N, Q, 2>(prm, L, span, lane); break;
-        default: walk_state_role<N, Q, 3>(prm, L, span, lane); break;
+        case 0: walk_output_role<N, Q, 0, DT>(prm, L, span, lane); break;
+        case 1: walk_output_role<N, Q, 1, DT>(prm, L, span, lane); break;
+        case 2: walk_output_role<N, Q, 2, DT>(prm, L, span, lane); break;
+        case 3: walk_output_role<N, Q, 3, DT>(prm, L, span, lane); break;
+        case 4: walk_state_role<N, Q, 0, DT>(prm, L, span, lane); break;
+        case 5: walk_state_role<N, Q, 1, DT>(prm, L, span, lane); break;
+        case 6: walk_state_role<N, Q, 2, DT>(prm, L, span, lane); break;
+        default: walk_state_role<N, Q, 3, DT>(prm, L, span, lane); break;
     }
 }
 
 // log2 weight below which exp2 is 0 in fp32 whatever its last-bit error (the smallest denormal
 // is 2^-149)
 constexpr float kVanish2 = -160.f;
+// log2 of the largest input scale (the front-end's Delta) the early exit below allows for: with
+// one, a token weighs at most 2^(decay + 64)
+constexpr float kLog2ScaleMax = 64.f;
 
 // seg_state_kernel: the state-only pass of a segmented walk, shaped for throughput.  One wave
 // per (segment, batch, head) forms the segment's local state (its final state from a zero start)
@@ -788,7 +827,7 @@ struct SegStateShape {
     static constexpr size_t lds_bytes = (size_t)Q * kXStr * 2 + (size_t)Q * 4;
 };
 
-template <int N, int Q>
+template <int N, int Q, bool DT>
 __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     using S = SegStateShape<N, Q>;
     constexpr int NBK = S::NBK, KS = S::KS, PB = S::PB, LA = S::LA, XR = S::XR;
@@ -804,6 +843,7 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     const int nchunks = prm.nchunks;
     const uint32_t x_row = (uint32_t)(H * kP * 2);
     const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
+    const float* lg0 = DT ? prm.lg_t + unit * (int64_t)nchunks * Q : nullptr;
     __bf16* xg = const_cast<__bf16*>(static_cast<const __bf16*>(prm.x));
     const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * NBK * KS * 512;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -815,10 +855,14 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     const uint32_t xoff = (uint32_t)(lane / 8) * x_row + 16 * (lane % 8);
 
     float la[LA];
+    float lgs[DT ? LA : 1];  // (DT) log2 of the input scale of the same tokens
     uint4 xs[XR];
     auto load_la = [&](int c) {
 #pragma unroll
         for (int j = 0; j < LA; ++j) la[j] = la0[(int64_t)c * Q + lane * LA + j];
+        if (DT)
+#pragma unroll
+            for (int j = 0; j < LA; ++j) lgs[j] = lg0[(int64_t)c * Q + lane * LA + j];
     };
     // x rows of the chunk through a buffer resource ending with it: rows past a short chunk's
     // end read as zeros
@@ -841,7 +885,7 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
 #pragma unroll
         for (int j = 0; j < LA; ++j) {
             const int t = lane * LA + j;
-            wv[(t % 8) * (Q / 8) + t / 8] = fexp2(sfx2 + (last2 - (excl + cum[j]) * kLog2e));
+            wv[(t % 8) * (Q / 8) + t / 8] = fexp2(sfx2 + (last2 - (excl + cum[j]) * kLog2e) + (DT ? lgs[j] : 0.f));
         }
         wave_lds_fence();
         float w[XR];
@@ -913,7 +957,7 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb)
                     hs[NBH + nb][pb] = mfma_bf16(as_bf16x8(bhi[nb][k]), xfa[k][pb], hs[NBH + nb][pb]);
-        if (bound2 < kVanish2) {
+        if (bound2 < kVanish2 - (DT ? kLog2ScaleMax : 0.f)) {
             // The weights of all earlier tokens are 0 in fp32 (exp2 of less than -160), so the
             // earlier chunks would add exact zeros: only their decay is still summed.
             for (int cc = c - 2; cc >= c0; --cc) {
@@ -963,10 +1007,12 @@ bool allow_full_lds(const void* kernel, bool* done) {
 struct FastLayout {
     int64_t nchunks, nblk, units;
     int nseg, seg_chunks;
-    size_t pairs, bt, ct, la_t, seg_state, seg_decay, total;
+    size_t pairs, bt, ct, la_t, lg_t, seg_state, seg_decay, total;
 };
 
-FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int Q) {
+// (with_lg: log2 of the input scale head-major, laid out as la_t)
+FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int Q,
+                       bool with_lg = false) {
     FastLayout l;
     l.nchunks = (seqlen + Q - 1) / Q;
     l.nblk = batch * ngroups * l.nchunks;
@@ -979,6 +1025,8 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
     l.bt = off; off += (size_t)l.nblk * N * Q * 2;
     l.ct = off; off += (size_t)l.nblk * N * Q * 2;
     l.la_t = off; off += (size_t)l.units * l.nchunks * Q * 4;
+    l.lg_t = off;
+    if (with_lg) off += (size_t)l.units * l.nchunks * Q * 4;
     l.seg_state = l.seg_decay = off;
     if (l.nseg > 1) {
         l.seg_state = off; off += (size_t)l.nseg * l.units * N * kP * 4;
@@ -988,21 +1036,24 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
     return l;
 }
 
-template <int N, int Q>
+template <int N, int Q, bool DT>
 int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     static_assert(WalkShape<N, Q>::lds_bytes <= kMaxLds, "walk LDS budget");
     static bool prep_attr[64] = {}, walk_attr[64] = {};
-    const FastLayout lay = fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q);
+    const bool with_lg = fl.dt && fl.scale_input;
+    const FastLayout lay = fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q, with_lg);
     char* ws = reinterpret_cast<char*>(fl.scores);
     __bf16* pairs = reinterpret_cast<__bf16*>(ws + lay.pairs);
     __bf16* bt = reinterpret_cast<__bf16*>(ws + lay.bt);
     __bf16* ct = reinterpret_cast<__bf16*>(ws + lay.ct);
     float* la_t = reinterpret_cast<float*>(ws + lay.la_t);
     const int nch = (int)lay.nchunks;
-    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0};
+    float* lg_t = with_lg ? reinterpret_cast<float*>(ws + lay.lg_t) : nullptr;
+    PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.dt, fl.dt_bias, fl.A_log, lg_t,
+                  fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
-    if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q>), walk_attr)) return -1;
-    int k = 0;
+    if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q, DT>), walk_attr)) return -1;
+    int k = fl.first_launch;
     const size_t plds = prep_lds<N, Q>(), slds = SegStateShape<N, Q>::lds_bytes, wlds = WalkShape<N, Q>::lds_bytes;
     const unsigned pthreads = PrepShape<N, Q>::THREADS;
     // split each block over two workgroups when even then they fit on the CUs at once
@@ -1012,7 +1063,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
 
     const int64_t work = lay.nseg * lay.units;
     const int64_t per_xcd = (work + 7) / 8;
-    Walk2Params wp{fl.x, la_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
+    Walk2Params wp{fl.x, la_t, lg_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, nch, per_xcd,
                    lay.seg_chunks, lay.nseg, reinterpret_cast<float*>(ws + lay.seg_state),
                    reinterpret_cast<float*>(ws + lay.seg_decay)};
@@ -1021,11 +1072,11 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
         const int64_t state_work = (lay.nseg - 1) * lay.units;
         Walk2Params sp = wp;
         sp.per_xcd = (state_work + 7) / 8;
-        if (!launch_k(fl, k, seg_state_kernel<N, Q>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kWave), slds, stream, sp))
+        if (!launch_k(fl, k, seg_state_kernel<N, Q, DT>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kWave), slds, stream, sp))
             return -1;
         // (each walk workgroup chains the segment states into its own start state)
     }
-    return launch_k(fl, k, walk_fast_kernel<N, Q>, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream,
+    return launch_k(fl, k, walk_fast_kernel<N, Q, DT>, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream,
                     wp)
                ? 0
                : -1;
@@ -1047,16 +1098,23 @@ bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nh
            (chunk == 64 || chunk == 128 || chunk == 256) && offsets_fit && heads_fit;
 }
 
-size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk) {
-    return fast_layout(batch, nheads, ngroups, seqlen, N, fast_chunk(chunk)).total;
+size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk,
+                            bool with_lg) {
+    return fast_layout(batch, nheads, ngroups, seqlen, N, fast_chunk(chunk), with_lg).total;
 }
 
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream) {
     const int N = (int)fl.dstate, Q = fast_chunk(fl.chunk);
-    if (N == 64 && Q == 64) return launch_fast_t<64, 64>(fl, stream);
-    if (N == 64 && Q == 128) return launch_fast_t<64, 128>(fl, stream);
-    if (N == 128 && Q == 64) return launch_fast_t<128, 64>(fl, stream);
-    if (N == 128 && Q == 128) return launch_fast_t<128, 128>(fl, stream);
+    // (the scaled-input form only when the input scale exists: log a from dt alone needs nothing
+    // in the walk)
+    const bool dt = fl.dt && fl.scale_input;
+    if (N == 64 && Q == 64) return dt ? launch_fast_t<64, 64, true>(fl, stream) : launch_fast_t<64, 64, false>(fl, stream);
+    if (N == 64 && Q == 128)
+        return dt ? launch_fast_t<64, 128, true>(fl, stream) : launch_fast_t<64, 128, false>(fl, stream);
+    if (N == 128 && Q == 64)
+        return dt ? launch_fast_t<128, 64, true>(fl, stream) : launch_fast_t<128, 64, false>(fl, stream);
+    if (N == 128 && Q == 128)
+        return dt ? launch_fast_t<128, 128, true>(fl, stream) : launch_fast_t<128, 128, false>(fl, stream);
     return -2;
 }
 

@@ -20,6 +20,7 @@
 // group the K indices its accumulator rows hold; the partner operand is read from LDS in
 // the same K order.  Everything a lane reads or writes along a row is 8 or 16 bytes wide.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ssd_common.h"
@@ -353,12 +354,21 @@ __global__ void __launch_bounds__(kThreads) step_kernel(StepParams prm) {
     const T* Bt = static_cast<const T*>(prm.B_t) + (b * G + g) * N;
     const T* Ct = static_cast<const T*>(prm.C_t) + (b * G + g) * N;
     const float xp = to_f32(xt[unit * P + p]);
-    const float a_head = prm.diag ? 0.f : expf(prm.log_a_t[unit]);
+    // with the discretisation front-end: Delta = softplus(dt + bias), log a = -Delta exp(A_log)
+    // (per head, or per (head, n)), and the input term scaled by Delta
+    const bool disc = prm.dt_t != nullptr;
+    const float delta = disc ? softplusf(prm.dt_t[unit] + (prm.dt_bias ? prm.dt_bias[h] : 0.f)) : 0.f;
+    const float xin = disc && prm.scale_input ? delta * xp : xp;
+    auto log_a = [&](int n) {
+        if (disc) return -delta * expf(prm.diag ? prm.A_log[h * N + n] : prm.A_log[h]);
+        return prm.diag ? prm.log_a_t[unit * N + n] : prm.log_a_t[unit];
+    };
+    const float a_head = prm.diag ? 0.f : expf(log_a(0));
     float* st = prm.state + unit * N * P;
     float acc = 0.f;
     for (int n = r; n < N; n += R) {
-        const float a = prm.diag ? expf(prm.log_a_t[unit * N + n]) : a_head;
-        const float s = a * st[n * P + p] + to_f32(Bt[n]) * xp;
+        const float a = prm.diag ? expf(log_a(n)) : a_head;
+        const float s = a * st[n * P + p] + to_f32(Bt[n]) * xin;
         st[n * P + p] = s;
         acc += to_f32(Ct[n]) * s;
     }
@@ -377,6 +387,84 @@ __global__ void __launch_bounds__(kThreads) step_kernel(StepParams prm) {
 __global__ void __launch_bounds__(kThreads) copy_state_kernel(const float* src, float* dst, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+// Discretisation front-end for the generic paths: per (b, t, h), Delta = softplus(dt + bias),
+// log a = -Delta exp(A_log) written to la ([B,T,H] with K = 1, or [B,T,H,N] with K = N and
+// A_log [H,N]), and with xs non-null the scaled input Delta x written to xs.  In double, so
+// that the fp32 path's log a carries only its final rounding.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) discretize_kernel(const float* dt, const float* dt_bias,
+                                                              const float* A_log, const T* x, float* la, T* xs,
+                                                              int64_t tokens, int64_t nheads, int K, int P) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < tokens * K; i += stride) {
+        const int64_t th = i / K;  // (b, t, h) row
+        const int64_t h = th % nheads;
+        const int k = (int)(i % K);
+        const double delta = softplus((double)dt[th] + (dt_bias ? (double)dt_bias[h] : 0.0));
+        la[i] = (float)(-delta * exp((double)A_log[h * K + k]));
+    }
+    if (!xs) return;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < tokens * P; i += stride) {
+        const int64_t th = i / P;
+        const int64_t h = th % nheads;
+        const double delta = softplus((double)dt[th] + (dt_bias ? (double)dt_bias[h] : 0.0));
+        xs[i] = from_f32<T>((float)(delta * (double)to_f32(x[i])));
+    }
+}
+
+// y += D[h] x over [B,T,H,P]: the skip term on the raw input, after a walk that ran on the
+// scaled input without one.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) skip_kernel(const T* x, const float* D, T* y, int64_t n, int64_t nheads,
+                                                        int P) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+        const int64_t h = (i / P) % nheads;
+        y[i] = from_f32<T>(to_f32(y[i]) + D[h] * to_f32(x[i]));
+    }
+}
+
+template <typename T>
+int launch_forward_discretized_t(const ForwardLaunch& fl, hipStream_t stream) {
+    const int K = fl.decay == 1 ? (int)fl.dstate : 1;
+    const int P = (int)fl.headdim;
+    const size_t own = generic_workspace_bytes(fl.dtype, fl.decay, fl.batch, fl.nheads, fl.ngroups, fl.seqlen,
+                                               (int)fl.dstate, P, fl.chunk);
+    const DtGenericLayout lay = dt_generic_layout(own, fl.batch, fl.seqlen, fl.nheads, K, P, (int)sizeof(T),
+                                                  fl.scale_input != 0);
+    char* ws = reinterpret_cast<char*>(fl.scores);
+    float* la = reinterpret_cast<float*>(ws + lay.la);
+    T* xs = fl.scale_input ? reinterpret_cast<T*>(ws + lay.xs) : nullptr;
+    const int64_t tokens = fl.batch * fl.seqlen * fl.nheads;
+    const int64_t work = tokens * (K > P ? K : P);
+    const unsigned grid = (unsigned)std::min<int64_t>((work + kThreads - 1) / kThreads, 8192);
+    int k = fl.first_launch;
+    if (!launch_k(fl, k, discretize_kernel<T>, dim3(grid), dim3(kThreads), 0, stream, fl.dt, fl.dt_bias, fl.A_log,
+                  static_cast<const T*>(fl.x), la, xs, tokens, fl.nheads, K, P))
+        return -1;
+    // the walk on log a and (with the input scale) the scaled input; then the skip term
+    ForwardLaunch g = fl;
+    g.dt = g.dt_bias = g.A_log = nullptr;
+    g.scale_input = 0;
+    g.log_a = la;
+    g.first_launch = k;
+    if (xs) {
+        g.x = xs;
+        g.D = nullptr;
+    }
+    const int rc = launch_forward(g, stream);
+    if (rc != 0) return rc;
+    if (xs && fl.D) {
+        k = *fl.n_launches;
+        const int64_t n = tokens * P;
+        const unsigned sgrid = (unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 8192);
+        if (!launch_k(fl, k, skip_kernel<T>, dim3(sgrid), dim3(kThreads), 0, stream, static_cast<const T*>(fl.x), fl.D,
+                      static_cast<T*>(fl.y), n, fl.nheads, P))
+            return -1;
+    }
+    return 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -400,7 +488,7 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     ScoresParams sp{fl.Bm, fl.Cm, fl.scores, fl.seqlen, fl.ngroups, Q, fl.nchunks};
     const int64_t nscore = fl.batch * fl.ngroups * fl.nchunks;
     (void)ntiles;
-    int k = 0;
+    int k = fl.first_launch;
     if (!launch_k(fl, k, scores_kernel<T, N>, dim3((unsigned)nscore), dim3(kThreads), 0, stream, sp)) return -1;
 
     const int64_t units = fl.batch * fl.nheads;
@@ -458,6 +546,13 @@ size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk) 
     return (size_t)(batch * ngroups * nchunks) * (size_t)(nt * (nt + 1) / 2) * 256 * sizeof(float);
 }
 
+size_t generic_workspace_bytes(int dtype, int decay, int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen,
+                               int N, int P, int chunk) {
+    (void)dtype, (void)nheads, (void)N, (void)P;
+    if (decay == 1) return 0;  // the unpipelined diagonal walk keeps everything on chip
+    return scores_bytes(batch, ngroups, (seqlen + chunk - 1) / chunk, chunk);
+}
+
 int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
     if (fl.seqlen == 0) {
         if (fl.final_state) {
@@ -471,6 +566,10 @@ int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
         }
         return 0;
     }
+    if (fl.dt && !discretization_fused(fl.dtype, fl.decay, (int)fl.dstate, (int)fl.headdim, fl.chunk, fl.nheads,
+                                       fl.ngroups))
+        return fl.dtype == 0 ? launch_forward_discretized_t<float>(fl, stream)
+                             : launch_forward_discretized_t<__bf16>(fl, stream);
     if (fl.decay == 1) return launch_forward_diag(fl, stream);
     if (fast_path_applies(fl.dtype, fl.decay, (int)fl.dstate, (int)fl.headdim, fl.chunk, fl.nheads, fl.ngroups))
         return launch_forward_fast(fl, stream);

@@ -38,6 +38,12 @@ struct WalkParams {
     float* seg_init;
     float* seg_state;
     float* seg_decay;
+    // discretisation front-end (pipelined diagonal walk only; dt null otherwise): log a and
+    // the input scale from dt, as in ForwardLaunch
+    const float* dt;
+    const float* dt_bias;
+    const float* A_log;
+    int scale_input;
 };
 
 struct StepParams {
@@ -50,6 +56,11 @@ struct StepParams {
     void* y_t;
     int64_t nheads, ngroups;
     int headdim, dstate, diag;
+    // discretisation front-end (dt_t non-null; log_a_t is then null), as in ForwardLaunch
+    const float* dt_t;
+    const float* dt_bias;
+    const float* A_log;
+    int scale_input;
 };
 
 struct PrepParams {
@@ -60,6 +71,12 @@ struct PrepParams {
     __bf16* bt;     // B^T per chunk, tokens in MFMA K order
     __bf16* ct;     // C^T per chunk, MFMA lane order
     float* la_t;    // log a head-major: [batch][nheads][nchunks * chunk], 0 past the end
+    // discretisation front-end (dt non-null; log_a is then null): log a from dt, and with
+    // lg_t non-null log2 of the input scale softplus(dt + bias), laid out as la_t
+    const float* dt;
+    const float* dt_bias;
+    const float* A_log;
+    float* lg_t;
     int64_t seqlen;
     int64_t nheads;
     int64_t ngroups;
@@ -71,6 +88,7 @@ struct PrepParams {
 struct Walk2Params {
     const void* x;
     const float* la_t;  // log a head-major (PrepParams::la_t)
+    const float* lg_t;  // log2 of the input scale head-major (PrepParams::lg_t), or null
     const __bf16* ct;   // C^T fragments (PrepParams::ct)
     const float* D;
     const __bf16* pairs;
@@ -96,6 +114,13 @@ struct ForwardLaunch {
     int chunk, nchunks;
     const void* x;
     const float* log_a;
+    // discretisation front-end (ssd_forward_dt): with dt non-null, log_a is null and the
+    // kernels form log a = -softplus(dt + dt_bias) exp(A_log), and with scale_input the input
+    // term's scale softplus(dt + dt_bias)
+    const float* dt;
+    const float* dt_bias;
+    const float* A_log;
+    int scale_input;
     const void* Bm;
     const void* Cm;
     const float* D;
@@ -108,6 +133,7 @@ struct ForwardLaunch {
     hipEvent_t const* events;
     int n_events;
     int* n_launches;
+    int first_launch;  // index of this call's first launch (a composed path continues the count)
 };
 
 bool shape_supported(int dtype, int N, int P);
@@ -129,12 +155,15 @@ bool launch_k(const ForwardLaunch& fl, int& k, F kernel, dim3 grid, dim3 block, 
 }
 // The pipelined bf16 path (ssd_fast.hip) and its workspace.
 bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups);
-size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk);
+// (with_lg: the workspace also holds log2 of the input scale, for ssd_forward_dt's scaled input)
+size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk,
+                            bool with_lg = false);
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream);
 // The diagonal-decay walk (ssd_diag.hip): LDS bytes (0 = unsupported) and launch.
 size_t diag_lds_bytes(int dtype, int N, int P, int chunk);
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream);
 size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk);
+bool diag_pipe_applies(int dtype, int N, int P, int chunk);
 // Segment prefix of a segmented walk (ssd_fast.hip): per_n = 1 for one decay per state row.
 int launch_seg_prefix(const ForwardLaunch& fl, int& k, const float* init, float* seg_init, const float* seg_state,
                       const float* seg_decay, int64_t units, int N, int P, int nseg, int per_n, hipStream_t stream);
@@ -143,6 +172,32 @@ size_t scores_bytes(int64_t batch, int64_t ngroups, int64_t nchunks, int chunk);
 // 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.
 int launch_forward(const ForwardLaunch& fl, hipStream_t stream);
 int launch_step(const StepParams& sp, int dtype, int64_t units, hipStream_t stream);
+
+// ssd_forward_dt on the paths whose kernels form log a from dt themselves (the bf16 scalar fast
+// path and the pipelined diagonal walk).  Other shapes take the generic composition below.
+inline bool discretization_fused(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups) {
+    return decay == 1 ? diag_pipe_applies(dtype, N, P, chunk)
+                      : fast_path_applies(dtype, decay, N, P, chunk, nheads, ngroups);
+}
+// Workspace of the generic composition: the walk's own workspace, then log a [B,T,H(,N)] fp32,
+// then (scale_input) the scaled input softplus(dt + bias) x [B,T,H,P] in the element type, each
+// part starting on a 256-byte boundary.
+struct DtGenericLayout {
+    size_t la, xs, total;
+};
+inline DtGenericLayout dt_generic_layout(size_t own, int64_t batch, int64_t seqlen, int64_t nheads, int64_t per_head,
+                                         int64_t headdim, int elem_bytes, bool scale_input) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t tokens = (size_t)batch * (size_t)seqlen * (size_t)nheads;
+    DtGenericLayout l;
+    l.la = up(own);
+    l.xs = up(l.la + tokens * (size_t)per_head * 4);
+    l.total = scale_input ? l.xs + tokens * (size_t)headdim * (size_t)elem_bytes : l.xs;
+    return l;
+}
+// Bytes of the walk's own workspace on the generic (unfused) path of these dims.
+size_t generic_workspace_bytes(int dtype, int decay, int64_t batch, int64_t nheads, int64_t ngroups,
+                               int64_t seqlen, int N, int P, int chunk);
 
 constexpr size_t kMaxLds = 160 * 1024;
 

@@ -10,13 +10,16 @@ dtype with round-to-nearest-even):
   B, C ~ N(0, 1/N)          [B, T, G, N]     (the second parameter of N(.,.) is a variance)
   dt ~ N(mu, 1)             [B, T, H]        (mu = -2; mu = 0 for the tiny fp32 case)
   A_log                     per head ~ U(0, ln 16), zero for the tiny case, or per state
-                            dimension linspace(0, ln 64, N) for the diagonal case
+                            dimension linspace(0, ln 64, N) for the diagonal case (or, in
+                            tests, per (head, state dimension) ~ U(0, ln 64))
   log_a = -softplus(dt) * exp(A_log)   in fp32, stored fp32 (the zero-order-hold decay
                             log of exp(Delta*A) with Delta = softplus(dt), A = -exp(A_log))
   D ~ N(0, 1)               [H]              (absent for the tiny case)
   init_state ~ N(0, 0.1)    [B, H, N, P]     fp32 (long-sequence case only)
 A decode tail of ``decode_steps`` tokens is drawn together with the prompt (T + steps
-tokens) and split off afterwards.
+tokens) and split off afterwards.  The draws dt and A_log are returned as well (A_log as [H]
+for scalar decay, [H, N] for diagonal decay), for the entry points that take them in place of
+log_a.
 """
 from __future__ import annotations
 
@@ -85,6 +88,8 @@ def make_inputs(cfg: dict, seed: int) -> dict:
         a_log = torch.rand(H, generator=gen, dtype=torch.float32) * math.log(16.0)
     elif kind == "linspace64":
         a_log = torch.linspace(0.0, math.log(64.0), N, dtype=torch.float32)
+    elif kind == "rand_hn":
+        a_log = torch.rand((H, N), generator=gen, dtype=torch.float32) * math.log(64.0)
     else:
         raise ValueError(kind)
     D = torch.randn(H, generator=gen, dtype=torch.float32) if cfg["skip"] else None
@@ -98,17 +103,19 @@ def make_inputs(cfg: dict, seed: int) -> dict:
         log_a = -(rate * torch.exp(a_log)[None, None, :])
     else:
         if a_log.shape == (N,):
-            log_a = -(rate[..., None] * torch.exp(a_log)[None, None, None, :])
-        else:
-            log_a = -(rate[..., None] * torch.exp(a_log)[None, None, :, None])
+            a_log = a_log[None, :].expand(H, N)
+        elif a_log.shape == (H,):
+            a_log = a_log[:, None].expand(H, N)
+        log_a = -(rate[..., None] * torch.exp(a_log)[None, None, :, :])
     log_a = log_a.contiguous()
 
     out = dict(x=x[:, :T].to(store).contiguous(), log_a=log_a[:, :T].contiguous(),
                B=Bm[:, :T].to(store).contiguous(), C=Cm[:, :T].to(store).contiguous(),
-               D=D, init_state=init)
+               D=D, init_state=init, dt=dt[:, :T].contiguous(), A_log=a_log.contiguous())
     if steps:
         out["x_dec"] = x[:, T:].to(store).contiguous()
         out["log_a_dec"] = log_a[:, T:].contiguous()
+        out["dt_dec"] = dt[:, T:].contiguous()
         out["B_dec"] = Bm[:, T:].to(store).contiguous()
         out["C_dec"] = Cm[:, T:].to(store).contiguous()
     return out
@@ -119,3 +126,9 @@ def to_f64(t):
     if t is None:
         return None
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def dt_bias(nheads: int, seed: int):
+    """A step-size bias per head, ~ N(0, 0.25) fp32 [H], from its own generator (seed)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    return torch.randn(nheads, generator=gen, dtype=torch.float32) * 0.5

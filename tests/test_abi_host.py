@@ -28,8 +28,10 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ssd_forward", "ssd_forward_profiled",
-                                    "ssd_forward_workspace_bytes", "ssd_step", "ssd_strerror"]
+    assert declared_functions() == ["ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
+                                    "ssd_forward_dt_workspace_bytes", "ssd_forward_profiled",
+                                    "ssd_forward_workspace_bytes", "ssd_step", "ssd_step_dt",
+                                    "ssd_strerror"]
 
 
 def test_library_exports_every_declared_function(lib):
@@ -189,3 +191,68 @@ def test_profiled_forward_rejects_short_event_array(lib):
     rc = lib.ssd_forward_profiled(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 128, None, FAKE,
                                   None, FAKE, 1 << 30, None, events, 7, ctypes.byref(n))
     assert rc == ssd.SSD_ERR_INVALID and n.value == 0
+
+
+# ---- the discretisation front-end (ssd_forward_dt, ssd_step_dt)
+def test_dt_workspace_bytes(lib):
+    # fused bf16 scalar path: ssd_forward's workspace, plus log2 of the input scale head-major
+    # (4 bytes per (batch, head, padded token)) when the input is scaled
+    d = mamba2_dims()
+    plain = ssd.ssd_forward_workspace_bytes(d, 128)
+    assert ssd.ssd_forward_dt_workspace_bytes(d, 128, False) == plain
+    assert ssd.ssd_forward_dt_workspace_bytes(d, 128, True) == plain + 8 * 24 * 16 * 128 * 4
+    # fused diagonal walk: the same as ssd_forward
+    dd = mamba2_dims(decay=1, dstate=64, batch=1, nheads=2, seqlen=4096)
+    assert ssd.ssd_forward_dt_workspace_bytes(dd, 64, True) == ssd.ssd_forward_workspace_bytes(dd, 64)
+    # generic composition: the walk's own workspace, log a, and (scaled) the scaled input, each
+    # part on a 256-byte boundary
+    up = lambda v: (v + 255) // 256 * 256
+    g = mamba2_dims(dtype=0, batch=2, seqlen=300, nheads=3, dstate=64)
+    own = ssd.ssd_forward_workspace_bytes(g, 64)
+    la = 2 * 300 * 3 * 4
+    assert ssd.ssd_forward_dt_workspace_bytes(g, 64, False) == up(up(own) + la)
+    assert ssd.ssd_forward_dt_workspace_bytes(g, 64, True) == up(up(own) + la) + 2 * 300 * 3 * 64 * 4
+    gd = mamba2_dims(decay=1, dtype=0, batch=1, seqlen=100, nheads=2, dstate=16, headdim=32)
+    assert ssd.ssd_forward_dt_workspace_bytes(gd, 32, True) == up(1 * 100 * 2 * 16 * 4) + 100 * 2 * 32 * 4
+    assert ssd.ssd_forward_dt_workspace_bytes(mamba2_dims(seqlen=0), 128, True) == 0
+    assert ssd.ssd_forward_dt_workspace_bytes(mamba2_dims(), 48, True) == 0
+
+
+def call_forward_dt(lib, dims, chunk=128, ws_bytes=1 << 30, **over):
+    p = dict(x=FAKE, dt=FAKE, dt_bias=None, A_log=FAKE, B=FAKE, C=FAKE, D=None, init=None, y=FAKE, final=None,
+             ws=FAKE)
+    p.update(over)
+    return lib.ssd_forward_dt(ctypes.byref(dims), p["x"], p["dt"], p["dt_bias"], p["A_log"], 1, p["B"], p["C"],
+                              p["D"], chunk, p["init"], p["y"], p["final"], p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A_log", "B", "C", "y"])
+def test_forward_dt_rejects_null_required_pointer(lib, name):
+    assert call_forward_dt(lib, mamba2_dims(), **{name: None}) == ssd.SSD_ERR_INVALID
+
+
+@pytest.mark.parametrize("name", ["dt", "dt_bias", "A_log"])
+def test_forward_dt_rejects_misaligned_pointer(lib, name):
+    assert call_forward_dt(lib, mamba2_dims(), **{name: FAKE + 4}) == ssd.SSD_ERR_ALIGN
+
+
+def test_forward_dt_rejects_small_workspace_and_bad_shapes(lib):
+    need = ssd.ssd_forward_dt_workspace_bytes(mamba2_dims(), 128, True)
+    assert call_forward_dt(lib, mamba2_dims(), ws_bytes=need - 1) == ssd.SSD_ERR_INVALID
+    assert call_forward_dt(lib, mamba2_dims(), chunk=48) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_forward_dt(lib, mamba2_dims(nheads=6, ngroups=4)) == ssd.SSD_ERR_INVALID
+    assert call_forward_dt(lib, mamba2_dims(batch=0), x=None, dt=None, A_log=None, B=None, C=None, y=None,
+                           ws=None, ws_bytes=0) == 0
+
+
+def test_step_dt_rejects_bad_arguments(lib):
+    def call(dims, **over):
+        p = dict(state=FAKE, x=FAKE, dt=FAKE, bias=None, A_log=FAKE, B=FAKE, C=FAKE, D=None, y=FAKE)
+        p.update(over)
+        return lib.ssd_step_dt(ctypes.byref(dims), p["state"], p["x"], p["dt"], p["bias"], p["A_log"], 1, p["B"],
+                               p["C"], p["D"], p["y"], None)
+    d = mamba2_dims(batch=4, nheads=64, ngroups=8)
+    assert call(d, dt=None) == ssd.SSD_ERR_INVALID
+    assert call(d, A_log=None) == ssd.SSD_ERR_INVALID
+    assert call(d, bias=FAKE + 8) == ssd.SSD_ERR_ALIGN
+    assert call(mamba2_dims(dstate=48)) == ssd.SSD_ERR_UNSUPPORTED
