@@ -16,9 +16,12 @@ Contents
   discretize            the discretisation front-end (llms.blog "The Selection Mechanism"):
                         Delta = softplus(dt + bias), log a = -Delta exp(A_log), B-bar = Delta B;
                         ``discretize.forward_dt`` runs the recurrence in that form.
+  backward              the adjoint of the recurrence in fp64 (plain C, ``ssd_oracle_bwd.c``):
+                        the gradients of <dy, y> + <dfinal, final> with respect to every input.
 """
 from .recurrence import Oracle, build, default_oracle, forward, default_threads
 from .chunked import chunked_forward
 from . import discretize
+from . import backward
 
-__all__ = ["Oracle", "build", "default_oracle", "forward", "default_threads", "chunked_forward", "discretize"]
+__all__ = ["Oracle", "build", "default_oracle", "forward", "default_threads", "chunked_forward", "discretize", "backward"]

@@ -1,0 +1,65 @@
+"""The oracle's backward pass (oracle/backward.py) against its pins, and planted mistakes in
+copies of its C source, each of which some pin must catch."""
+import os
+import shutil
+import tempfile
+
+import pytest
+
+import oracle
+import oracle.backward as bwd
+from pins_bwd import BWD_PINS
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default_oracle()
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
+def test_backward_pin(orc, pin):
+    pin(orc, bwd.default_adjoint())
+
+
+MUTANTS = {
+    "skip_dropped_from_dx": ("double acc = D ? D[hd] * dyt[p] : 0.0;", "double acc = 0.0;"),
+    "readout_after_dx": ("Gs[n * P + p] += ct[n] * dyt[p];", "Gs[n * P + p] += 0.0 * ct[n] * dyt[p];"),
+    "dx_uses_C": ("acc += Gs[n * P + p] * bt[n];", "acc += Gs[n * P + p] * ct[n];"),
+    "dB_uses_dy": ("gb += Gs[n * P + p] * xt[p];", "gb += Gs[n * P + p] * dyt[p];"),
+    "dC_uses_prev_state": ("gc += ht[n * P + p] * dyt[p];", "gc += hprev[n * P + p] * dyt[p];"),
+    "dloga_uses_current_state": ("acc += Gs[i] * hprev[i];", "acc += Gs[i] * ht[i];"),
+    "dloga_without_a": ("dlog_a[row] = a[0] * acc;", "dlog_a[row] = acc;"),
+    "diag_dloga_summed_over_n": ("dlog_a[row * N + n] = a[n] * acc;", "dlog_a[row * N + n] = a[0] * acc;"),
+    "G_not_decayed": ("for (int64_t p = 0; p < P; ++p) Gs[n * P + p] *= a[n];",
+                      "for (int64_t p = 0; p < P; ++p) Gs[n * P + p] *= 1.0;"),
+    "dfinal_ignored": ("Gs[i] = dfinal ? dfinal[(b * H + hd) * N * P + i] : 0.0;", "Gs[i] = 0.0;"),
+    "dD_wrong_operand": ("dDh += dyt[p] * xt[p];", "dDh += dyt[p] * dyt[p];"),
+    "init_ignored": ("hs[i] = init_state ? init_state[(b * H + hd) * N * P + i] : 0.0;", "hs[i] = 0.0;"),
+    "dB_last_head_only": ("dbt[n] += gb;", "dbt[n] = gb;"),
+}
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="ssd_adjoint_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_backward_mutant_is_caught(orc, workdir, name):
+    before, after = MUTANTS[name]
+    with open(bwd.SOURCE) as f:
+        src = f.read()
+    assert src.count(before) == 1, "mutation site for %s must occur exactly once" % name
+    path = os.path.join(workdir, name + ".c")
+    with open(path, "w") as f:
+        f.write(src.replace(before, after))
+    mutant = bwd.Adjoint(bwd.build(path, os.path.join(workdir, "lib_%s.so" % name)))
+    caught = []
+    for pin in BWD_PINS:
+        try:
+            pin(orc, mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "planted mistake %r passed every pin" % name
