@@ -91,7 +91,8 @@ KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.h
                   "walk_diag_pipe_kernel": "ssd_diag.hip", "walk_diag_kernel": "ssd_diag.hip",
                   "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
                   "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
-                  "skip_kernel": "ssd_kernels.hip"}
+                  "skip_kernel": "ssd_kernels.hip", "bwd_states_kernel": "ssd_bwd.hip",
+                  "bwd_walk_kernel": "ssd_bwd.hip", "zero_kernel": "ssd_bwd.hip", "bwd_reduce_kernel": "ssd_bwd.hip"}
 
 
 def kernel_source_hash(kernel):
@@ -257,12 +258,133 @@ def time_decode(ssd, cfg, g, stream, ev, dev):
             "effective_gbs": (state_bytes + io_bytes) / (us / 1e6) / 1e9}
 
 
+BWD_CHUNK = 32  # tokens per backward chunk (the library's)
+
+
+def backward_counts(cfg):
+    """Work the backward pass must do (scalar decay), with Q the backward chunk: per group the
+    causal C B^T; per head the causal dY X^T, (S o L)^T dY, (L o DYX)^T C and (L o DYX) B
+    ((Q + 1) flops per token and dimension each), and the four N x P contractions of the carried
+    state's terms (B^T G, G x, H dy and the update of G) in the reverse walk; the recomputed
+    state (B^T X) in the checkpoint pass.  Bytes: every input and output gradient once."""
+    Bsz, T, H, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["ngroups"]
+    P, N, Q = cfg["headdim"], cfg["dstate"], BWD_CHUNK
+    sx = 4 if cfg["dtype"] == "fp32" else 2
+    f_walk = Bsz * T * (G * N * (Q + 1) + H * ((2 * P + 2 * N) * (Q + 1) + 8 * N * P))
+    f_states = Bsz * T * H * 2 * N * P
+    nbytes = Bsz * T * (3 * H * P * sx + 2 * G * N * sx + 2 * G * N * 4 + 2 * 4 * H) \
+        + (2 * 4 * H if cfg["skip"] else 0) + 4 * Bsz * H * N * P * (2 * int(cfg["init"]) + int(cfg["final"]))
+    return f_walk, f_states, nbytes
+
+
+def run_backward(args, cfg, inp, dev):
+    """One JSON line for the backward pass on the workload: tokens/s of ssd_backward, the
+    dominant kernel (the reverse walk) against the fp32 matrix peak, and the fp64 adjoint on the
+    host's cores for the first batch element."""
+    import torch
+    import ssd_inputs
+    import ssd_chunked_scan_02_amd as ssd
+    f_walk, f_states, nbytes = backward_counts(cfg)
+    og = ssd_inputs.output_gradients(cfg, ssd_inputs.SEEDS[args.workload] + 1000)
+    copies = args.copies or min(32, max(2, math.ceil(1.0e9 / nbytes)))
+    bufs = []
+    for _ in range(copies):
+        g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+        g["dy"] = og["dy"].to(dev)
+        g["dfinal"] = og["dfinal"].to(dev) if cfg["final"] else None
+        bufs.append(g)
+    dims = ssd.dims_for(bufs[0]["x"], bufs[0]["log_a"], bufs[0]["B"])
+    ws = torch.empty(max(1, ssd.ssd_backward_workspace_bytes(dims)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = HipEvents()
+
+    def step(i, events=None):
+        g = bufs[i % copies]
+        kw = dict(D=g.get("D"), init_state=g.get("init_state"), dfinal=g["dfinal"], want_dD=cfg["skip"],
+                  want_dinit=cfg["init"], workspace=ws, stream=stream)
+        if events is None:
+            ssd.ssd_backward(g["x"], g["log_a"], g["B"], g["C"], g["dy"], **kw)
+            return None
+        return ssd.ssd_backward_profiled(g["x"], g["log_a"], g["B"], g["C"], g["dy"], events=events, **kw)[1]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    begin, end = ev.create(), ev.create()
+    ev.lib.hipEventRecord(begin, stream.cuda_stream)
+    for i in range(K):
+        step(i)
+    ev.lib.hipEventRecord(end, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(begin, end) / K
+    step_events = [[ev.create() for _ in range(2 * ssd.SSD_MAX_LAUNCHES)] for _ in range(K)]
+    launches = None
+    for i in range(K):
+        launches = step(i, step_events[i])
+    torch.cuda.synchronize()
+    per_kernel = [[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in step_events] for k in range(launches)]
+    for e in step_events:
+        for h in e:
+            ev.destroy(h)
+    kernel_avg = [sum(v) / len(v) for v in per_kernel]
+    N, P = cfg["dstate"], cfg["headdim"]
+    names = ["zero_kernel", "bwd_states_kernel<%d,%d>" % (N, P), "bwd_walk_kernel<%d,%d>" % (N, P)] + \
+        (["bwd_reduce_kernel"] if cfg["skip"] else [])
+    if len(names) != launches:
+        names = ["launch%d" % k for k in range(launches)]
+    log("backward ms/step %.4f; per kernel avg ms: %s" % (ms, ", ".join("%s %.4f" % kv for kv in zip(names, kernel_avg))))
+    walk = next((k for k, n in enumerate(names) if n.startswith("bwd_walk")), max(range(launches), key=lambda k: kernel_avg[k]))
+    tokens = cfg["batch"] * cfg["seqlen"]
+    achieved = f_walk / (kernel_avg[walk] / 1e3) / 1e12
+    result = {
+        "metric": "SSD backward tokens/s (gradients of x, log a, B, C, D, init) at B=8,T=2048,H=24,P=64,N=128",
+        "value": tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; the forward workload's inputs, dL/dy ~ N(0,1) in the input dtype)",
+        "config": {"workload": args.workload, "pass": "backward", "batch": cfg["batch"], "seqlen": cfg["seqlen"],
+                   "nheads": cfg["nheads"], "ngroups": cfg["ngroups"], "headdim": P, "dstate": N,
+                   "input_dtype": cfg["dtype"], "backward_chunk": BWD_CHUNK, "parallelism": "single GPU"},
+        "tflops": (f_walk + f_states) / (ms / 1e3) / 1e12,
+        "kernels_ms": {n: t for n, t in zip(names, kernel_avg)},
+        "roofline": {"kernel": names[walk], "bound": "mfma", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS,
+                     "traffic": measured_traffic(args.workload + "_bwd", names[walk]),
+                     "algorithmic_flops_per_launch": f_walk, "hbm_gbs_whole_step": nbytes / (ms / 1e3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        import oracle.backward
+        f = ssd_inputs.to_f64
+        one = lambda t: None if t is None else f(t[:1])
+        threads = oracle.default_threads() if hasattr(oracle, "default_threads") else 1
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.backward.backward(one(inp["x"]), one(inp["log_a"]), one(inp["B"]), one(inp["C"]), f(inp.get("D")),
+                                     one(inp.get("init_state")), one(og["dy"]),
+                                     one(og["dfinal"]) if cfg["final"] else None, nthreads=threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        # (the adjoint runs one (batch, group) pair per thread: the sample has G of them)
+        result["cpu_baseline"] = {"value": cfg["seqlen"] * reps / el, "unit": "tokens/s",
+                                  "cores": min(threads, cfg["ngroups"]),
+                                  "kind": "oracle",
+                                  "sample": "batch element 0 of the workload (%d tokens x %d heads), %d run(s) in "
+                                            "%.1f s, fp64 adjoint of the recurrence, OpenMP over (batch, group)"
+                                            % (cfg["seqlen"], cfg["nheads"], reps, el)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mamba2_layer")
+    ap.add_argument("--backward", action="store_true",
+                    help="time ssd_backward (the gradients) instead of the forward pass")
     ap.add_argument("--front-end", choices=("log_a", "dt"), default="log_a",
                     help="decay input: log a (ssd_forward), or dt and A_log (ssd_forward_dt)")
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = auto)")
@@ -287,6 +409,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = ssd_inputs.make_inputs(cfg, seed)
+    if args.backward:
+        if cfg["decay"] != "scalar":
+            print("the backward pass covers scalar decay only", file=sys.stderr)
+            sys.exit(2)
+        return run_backward(args, cfg, inp, dev)
     fe = args.front_end
     flops, nbytes, per_token = algorithmic_counts(cfg, fe)
     copies = args.copies or min(64, max(2, math.ceil(1.0e9 / nbytes)))

@@ -173,6 +173,43 @@ int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float
                 const float* dt_bias, const float* A_log, int scale_input, const void* B_t,
                 const void* C_t, const float* D, void* y_t, void* stream);
 
+/*
+ * The backward pass of ssd_forward (scalar decay): the gradients of L = <dy, y> + <dfinal,
+ * final_state> with respect to every input, for training.  It is the chain rule through the
+ * recurrence above, evaluated chunk by chunk (the state entering every chunk is recomputed into
+ * the workspace, then a reverse walk carries dL/dh from chunk to chunk); the pages define the
+ * operator, not its gradient.  The result is the gradient of the exact operator: it does not
+ * depend on the forward pass's chunk length.
+ *
+ *   x, log_a, B, C, D, init_state   the forward pass's inputs (D and init_state may be NULL).
+ *   dy            [B,T,H,P] in `dtype`: dL/dy.
+ *   dfinal        [B,H,N,P] fp32 dL/dfinal_state, or NULL for zeros.
+ *   dx            [B,T,H,P] output in `dtype`.
+ *   dlog_a        [B,T,H] fp32 output.
+ *   dB, dC        [B,T,G,N] fp32 outputs (summed over the heads of each group).
+ *   dD            [H] fp32 output, or NULL to skip it.
+ *   dinit         [B,H,N,P] fp32 output dL/dinit_state, or NULL to skip it.
+ *   workspace     device scratch of at least ssd_backward_workspace_bytes(dims) bytes: one fp32
+ *                 N x P state per (batch, head, 32 tokens), plus 4 bytes per (batch, head).
+ * Supported: SSD_DECAY_SCALAR, N in {16, 32, 64, 128}, P in {16, 32, 64}, fp32 or bf16
+ * (else SSD_ERR_UNSUPPORTED).  dB and dC are accumulated with atomic adds, so their last bits
+ * may differ from run to run.
+ */
+size_t ssd_backward_workspace_bytes(const ssd_dims* dims);
+
+int ssd_backward(const ssd_dims* dims, const void* x, const float* log_a, const void* B,
+                 const void* C, const float* D, const float* init_state, const void* dy,
+                 const float* dfinal, void* dx, float* dlog_a, float* dB, float* dC, float* dD,
+                 float* dinit, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssd_backward with per-launch timing events, as ssd_forward_profiled.  Launch order: zeroing of
+ * dB and dC, the state checkpoints, the reverse walk, the dD reduction (when dD is requested). */
+int ssd_backward_profiled(const ssd_dims* dims, const void* x, const float* log_a, const void* B,
+                          const void* C, const float* D, const float* init_state, const void* dy,
+                          const float* dfinal, void* dx, float* dlog_a, float* dB, float* dC,
+                          float* dD, float* dinit, void* workspace, size_t workspace_bytes,
+                          void* stream, void* const* events, int n_events, int* n_launches);
+
 /* Static, human-readable description of a return code. */
 const char* ssd_strerror(int code);
 

@@ -14,6 +14,9 @@ The functions carry the names of the C entry points declared in ``include/ssd.h`
   ssd_forward_dt(x, dt, A_log, B, C, D=None, dt_bias=None, scale_input=True, chunk=..., ...)
   ssd_forward_dt_profiled(..., events=(hipEvent_t handles)) -> (y, final_state, n_launches)
   ssd_step_dt(state, x_t, dt_t, A_log, B_t, C_t, D=None, dt_bias=None, scale_input=True, ...)
+  ssd_backward_workspace_bytes(dims) -> int
+  ssd_backward(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, ...) -> dict of gradients
+  ssd_backward_profiled(..., events=(hipEvent_t handles)) -> (gradients, n_launches)
   ssd_strerror(code) -> str
 """
 from __future__ import annotations
@@ -26,7 +29,8 @@ import torch
 __all__ = ["SSDError", "Dims", "library_path", "load_library", "dims_for",
            "ssd_forward_workspace_bytes", "ssd_forward", "ssd_forward_profiled", "ssd_step",
            "ssd_forward_dt_workspace_bytes", "ssd_forward_dt", "ssd_forward_dt_profiled",
-           "ssd_step_dt", "ssd_strerror",
+           "ssd_step_dt", "ssd_backward_workspace_bytes", "ssd_backward", "ssd_backward_profiled",
+           "ssd_strerror",
            "SSD_F32", "SSD_BF16", "SSD_DECAY_SCALAR", "SSD_DECAY_DIAG"]
 
 SSD_F32, SSD_BF16 = 0, 1
@@ -87,6 +91,13 @@ def load_library():
         lib.ssd_forward_dt_profiled.restype = i32
         lib.ssd_step_dt.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
         lib.ssd_step_dt.restype = i32
+        lib.ssd_backward_workspace_bytes.argtypes = [dp]
+        lib.ssd_backward_workspace_bytes.restype = sz
+        lib.ssd_backward.argtypes = [dp] + [vp] * 15 + [sz, vp]
+        lib.ssd_backward.restype = i32
+        lib.ssd_backward_profiled.argtypes = [dp] + [vp] * 15 + [sz, vp, ctypes.POINTER(vp), i32,
+                                                                 ctypes.POINTER(i32)]
+        lib.ssd_backward_profiled.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -306,6 +317,61 @@ def ssd_step_dt(state, x_t, dt_t, A_log, B_t, C_t, D=None, dt_bias=None, scale_i
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_step_dt")
     return y_t
+
+
+def ssd_backward_workspace_bytes(dims: Dims) -> int:
+    return int(load_library().ssd_backward_workspace_bytes(ctypes.byref(dims)))
+
+
+def ssd_backward_profiled(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, want_dD=True,
+                          want_dinit=True, workspace=None, stream=None, events=()):
+    """``ssd_backward_profiled``: as ssd_backward, launch k stamping events[2k] and events[2k+1].
+    Returns (gradients, n_launches)."""
+    return ssd_backward(x, log_a, B, C, dy, D, init_state, dfinal, want_dD, want_dinit, workspace,
+                        stream, _events=list(events))
+
+
+def ssd_backward(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, want_dD=True,
+                 want_dinit=True, workspace=None, stream=None, _events=None):
+    """Run ``ssd_backward``: gradients of <dy, y> + <dfinal, final_state> for the forward pass
+    on (x, log_a, B, C, D, init_state), scalar decay.  Returns a dict: dx (dtype of x), dlog_a,
+    dB, dC (fp32), dD (fp32 [H], or None) and dinit (fp32 [B,H,N,P], or None)."""
+    dims = dims_for(x, log_a, B)
+    dev = x.device
+    bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _check(x, "x", (bsz, T, H, P), x.dtype, dev)
+    _check(log_a, "log_a", (bsz, T, H), torch.float32, dev)
+    _check(B, "B", (bsz, T, G, N), x.dtype, dev)
+    _check(C, "C", (bsz, T, G, N), x.dtype, dev)
+    _check(dy, "dy", (bsz, T, H, P), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (bsz, H, N, P), torch.float32, dev)
+    _check(dfinal, "dfinal", (bsz, H, N, P), torch.float32, dev)
+    out = dict(dx=torch.empty_like(x), dlog_a=torch.empty((bsz, T, H), dtype=torch.float32, device=dev),
+               dB=torch.empty((bsz, T, G, N), dtype=torch.float32, device=dev),
+               dC=torch.empty((bsz, T, G, N), dtype=torch.float32, device=dev),
+               dD=torch.empty(H, dtype=torch.float32, device=dev) if want_dD else None,
+               dinit=torch.empty((bsz, H, N, P), dtype=torch.float32, device=dev) if want_dinit else None)
+    lib = load_library()
+    need = int(lib.ssd_backward_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(dims), _ptr(x), _ptr(log_a), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
+            _ptr(dy), _ptr(dfinal), _ptr(out["dx"]), _ptr(out["dlog_a"]), _ptr(out["dB"]),
+            _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]), _ptr(workspace), ws_bytes,
+            _stream_handle(stream, dev))
+    if _events is None:
+        rc = lib.ssd_backward(*args)
+    else:
+        n = max(len(_events), 2 * SSD_MAX_LAUNCHES)
+        arr = (ctypes.c_void_p * n)(*(list(_events) + [None] * (n - len(_events))))
+        count = ctypes.c_int(0)
+        rc = lib.ssd_backward_profiled(*args, arr, n, ctypes.byref(count))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_backward")
+    return out if _events is None else (out, count.value)
 
 
 def ssd_step(state, x_t, log_a_t, B_t, C_t, D=None, y_t=None, stream=None):

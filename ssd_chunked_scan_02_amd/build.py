@@ -20,7 +20,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-Wall", "-Wno-unused-result"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
-DEVICE_SOURCES = ["ssd_kernels.hip", "ssd_fast.hip", "ssd_diag.hip"]
+DEVICE_SOURCES = ["ssd_kernels.hip", "ssd_fast.hip", "ssd_diag.hip", "ssd_bwd.hip"]
 
 
 def _run(cmd):

@@ -81,6 +81,15 @@ int check_forward(const ssd_dims* d, int chunk) {
     return SSD_OK;
 }
 
+// Backward pass: scalar decay, N in {16, 32, 64, 128}, P in {16, 32, 64}, either dtype.
+int check_backward(const ssd_dims* d) {
+    int rc = check_dims(d, true);
+    if (rc != SSD_OK) return rc;
+    if (d->decay != SSD_DECAY_SCALAR) return SSD_ERR_UNSUPPORTED;
+    if (!ssd::backward_shape_supported((int)d->dstate, (int)d->headdim)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
 struct Discretization {
     const float* dt;
     const float* dt_bias;
@@ -230,6 +239,73 @@ int ssd_step_dt(const ssd_dims* d, float* state, const void* x_t, const float* d
                 const void* C_t, const float* D, void* y_t, void* stream) {
     const Discretization disc{dt_t, dt_bias, A_log, scale_input != 0};
     return step_impl(d, state, x_t, nullptr, &disc, B_t, C_t, D, y_t, stream);
+}
+
+size_t ssd_backward_workspace_bytes(const ssd_dims* d) {
+    if (check_backward(d) != SSD_OK || d->batch == 0) return 0;
+    return ssd::backward_workspace_bytes(d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim);
+}
+
+int ssd_backward(const ssd_dims* d, const void* x, const float* log_a, const void* B, const void* C,
+                 const float* D, const float* init_state, const void* dy, const float* dfinal, void* dx,
+                 float* dlog_a, float* dB, float* dC, float* dD, float* dinit, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    return ssd_backward_profiled(d, x, log_a, B, C, D, init_state, dy, dfinal, dx, dlog_a, dB, dC, dD, dinit,
+                                 workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, const void* B, const void* C,
+                          const float* D, const float* init_state, const void* dy, const float* dfinal, void* dx,
+                          float* dlog_a, float* dB, float* dC, float* dD, float* dinit, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events, int n_events, int* n_launches) {
+    if (n_launches) *n_launches = 0;
+    if (events && n_events < 2 * SSD_MAX_LAUNCHES) return SSD_ERR_INVALID;
+    int rc = check_backward(d);
+    if (rc != SSD_OK) return rc;
+    const bool has_tokens = d->batch > 0 && d->seqlen > 0;
+    if (has_tokens && (!x || !log_a || !B || !C || !dy || !dx || !dlog_a || !dB || !dC)) return SSD_ERR_INVALID;
+    const void* ptrs[] = {x, log_a, B, C, D, init_state, dy, dfinal, dx, dlog_a, dB, dC, dD, dinit, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    const size_t need = ssd_backward_workspace_bytes(d);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
+    if (d->batch == 0 && !dD) return SSD_OK;
+    ssd::BackwardLaunch bl{};
+    bl.dtype = d->dtype;
+    bl.headdim = d->headdim;
+    bl.dstate = d->dstate;
+    ssd::BwdParams& p = bl.p;
+    p.x = x;
+    p.log_a = log_a;
+    p.Bm = B;
+    p.Cm = C;
+    p.D = D;
+    p.init = init_state;
+    p.dy = dy;
+    p.dfinal = dfinal;
+    p.dx = dx;
+    p.dlog_a = dlog_a;
+    p.dB = dB;
+    p.dC = dC;
+    p.dD = dD;
+    p.dinit = dinit;
+    p.batch = d->batch;
+    p.seqlen = d->seqlen;
+    p.nheads = d->nheads;
+    p.ngroups = d->ngroups;
+    p.nchunks = (int)((d->seqlen + ssd::backward_chunk() - 1) / ssd::backward_chunk());
+    char* ws = static_cast<char*>(workspace);
+    const size_t ck = (size_t)(d->batch * d->nheads * p.nchunks) * (size_t)(d->dstate * d->headdim) * 4;
+    p.ckpt = reinterpret_cast<float*>(ws);
+    p.dD_part = ws ? reinterpret_cast<float*>(ws + (ck + 255) / 256 * 256) : nullptr;
+    int count = 0;
+    bl.events = reinterpret_cast<hipEvent_t const*>(events);
+    bl.n_events = events ? n_events : 0;
+    bl.n_launches = &count;
+    rc = ssd::launch_backward(bl, static_cast<hipStream_t>(stream));
+    if (n_launches) *n_launches = count;
+    if (rc == -2) return SSD_ERR_UNSUPPORTED;
+    return rc == 0 ? SSD_OK : SSD_ERR_HIP;
 }
 
 const char* ssd_strerror(int code) {

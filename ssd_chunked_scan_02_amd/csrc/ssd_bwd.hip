@@ -1,0 +1,493 @@
+// HIP kernels of the SSD backward pass (scalar decay), for gfx950 (MI355X).
+//
+// The gradient of L = <dy, y> + <dfinal, final> through the chunked forward pass, with the
+// state carried between chunks.  Inside a chunk of Q tokens, with cum the running sum of log a
+// (inclusive, restarting at the chunk), L_ts = exp(cum_t - cum_s) for s <= t (0 above),
+// S = C B^T, e_t = exp(cum_t), w_s = exp(cum_last - cum_s), H the state entering the chunk and
+// G the gradient of the state leaving it (dL/dh at the chunk's last token, from everything
+// after it):
+//   y_t  = sum_{s <= t} S_ts L_ts x_s + e_t C_t H + D x_t,     H_out = e_last H + sum_s w_s B_s x_s^T
+// so that, with DYX_ts = dy_t . x_s and M_ts = S_ts L_ts DYX_ts,
+//   dx_s   = sum_t (S o L)_ts dy_t + w_s B_s^T G + D dy_s
+//   dB_s  += sum_t (L o DYX)_ts C_t + w_s G x_s                 (summed over the group's heads)
+//   dC_t  += sum_s (L o DYX)_ts B_s + e_t H dy_t
+//   dcum_t = sum_s M_ts - sum_t' M_t't + e_t C_t . (H dy_t) - w_t B_t . (G x_t)
+//            + [t = last] (e_last <G, H> + sum_s w_s B_s . (G x_s))
+//   dlog a_j = sum_{t >= j in the chunk} dcum_t
+//   G_in   = e_last G + sum_t e_t C_t dy_t^T                    (the gradient entering the chunk)
+// These are the chain rule through the chunk-wise form of aiwiki "State Space Duality" ("Two
+// algorithms for one operator") and llms.blog "The Chunk-Wise SSD Algorithm"; the pages print no
+// backward pass.
+//
+//   bwd_states_kernel  one workgroup per (batch, head) walks forward and writes the state entering
+//                      every chunk (the checkpoints), the state kept in MFMA accumulators.
+//   bwd_walk_kernel    one workgroup per (batch, head) walks the chunks last to first with G in
+//                      accumulators, forms the chunk's gradients from fp32 MFMA products of LDS
+//                      tiles, and adds dB and dC into the group's rows with atomic adds.
+//   bwd_reduce_kernel  dD over the batch from the walk's per-(batch, head) partial sums.
+// The backward chunk (32 tokens) is independent of the forward pass's: the gradient of the
+// operator does not depend on how it is chunked.
+#include <algorithm>
+#include <type_traits>
+
+#include "ssd_common.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kBQ = 32;  // tokens per backward chunk
+
+// acc += A B for one 16x16 tile (fp32 MFMA 16x16x4; lane l gives A(l % 16, k + l / 16) and
+// B(k + l / 16, l % 16) and holds rows 4 (l / 16) + i, column l % 16 of the tile).  Element
+// (m, k) of A is a[m * am + k * ak]; element (k, n) of B is b[k * bk + n * bn].
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float* a, int am, int ak, const float* b, int bk, int bn,
+                                          int K, int lane) {
+    const int r = lane % 16, g = lane / 16;
+#pragma unroll 4
+    for (int k = 0; k < K; k += 4) acc = mfma_f32(a[r * am + (k + g) * ak], b[(k + g) * bk + r * bn], acc);
+    return acc;
+}
+
+// Sum over the 16 lanes of a lane group (the 16 columns of one accumulator row).
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 16);
+    return v;
+}
+
+template <int N, int P>
+struct BwdShape {
+    static constexpr int Q = kBQ, QS = Q + 1, NS = N + 1, PS = P + 1;
+    static constexpr int NB = N / 16, PB = P / 16, QB = Q / 16;
+    static constexpr int NTILE = NB * PB, TPW = (NTILE + kWaves - 1) / kWaves;  // state tiles
+    // walk LDS (floats): X, dY [Q][PS]; B, C [Q][NS]; S o L, L o DYX, M [Q][QS]; H, G [N][PS];
+    // e, w [Q]; row partial sums of B . (G x) and C . (H dy) [Q][NB] each; reduction [kWaves]
+    // (the running sums themselves in a static array of the accumulation type)
+    static constexpr size_t walk_floats = (size_t)2 * Q * PS + 2 * Q * NS + 3 * Q * QS + 2 * N * PS + 2 * Q +
+                                          2 * Q * NB + kWaves;
+    static constexpr size_t walk_lds = walk_floats * 4;
+    // states LDS (floats): w o B [Q][NS], X [Q][PS]
+    static constexpr size_t states_lds = ((size_t)Q * NS + Q * PS) * 4;
+};
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T* p, int64_t i) {
+    return to_f32(p[i]);
+}
+
+// Running sum of log a over one chunk (tokens past len add 0), into cum[0..Q), by wave 0;
+// then e and w.  CT is double for fp32 inputs (as the forward's generic path), and cum keeps it.
+template <typename CT>
+__device__ __forceinline__ void chunk_factors(const float* la, int64_t stride, int len, CT* cum, float* e, float* w,
+                                              int tid) {
+    if (tid < kWave) {
+        CT v = (tid < len && tid < kBQ) ? (CT)la[(int64_t)tid * stride] : (CT)0;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const CT o = __shfl_up(v, off, kWave);
+            if (tid >= off) v += o;
+        }
+        const CT last = __shfl(v, kBQ - 1, kWave);
+        if (tid < kBQ) {
+            cum[tid] = v;
+            e[tid] = (float)exp(v);
+            w[tid] = (float)exp(last - v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T, int N, int P>
+__global__ void __launch_bounds__(kThreads) bwd_states_kernel(BwdParams prm) {
+    using S = BwdShape<N, P>;
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    constexpr int Q = S::Q, NS = S::NS, PS = S::PS, PB = S::PB, NTILE = S::NTILE, TPW = S::TPW;
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* Bw = reinterpret_cast<float*>(smem);
+    float* Xs = Bw + Q * NS;
+    __shared__ CT cum[kBQ];
+    __shared__ float e_unused[kBQ], w_s[kBQ];
+    const T* xg = static_cast<const T*>(prm.x);
+    const T* Bg = static_cast<const T*>(prm.Bm);
+
+    f32x4 hs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kWaves * j;
+        if (tile < NTILE && prm.init) {
+            const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hs[j][i] = prm.init[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16];
+        }
+    }
+    for (int c = 0; c < prm.nchunks; ++c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+        // the checkpoint: the state entering chunk c
+        float* ck = prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ck[(16 * nb + 4 * lg + i) * P + 16 * pb + l16] = hs[j][i];
+            }
+        }
+        chunk_factors<CT>(prm.log_a + (b * Tn + t0) * H + h, H, len, cum, e_unused, w_s, tid);
+        __syncthreads();
+        for (int i = tid; i < Q * N; i += kThreads) {
+            const int s = i / N, n = i % N;
+            Bw[s * NS + n] = s < len ? w_s[s] * ldf(Bg, ((b * Tn + t0 + s) * G + g) * N + n) : 0.f;
+        }
+        for (int i = tid; i < Q * P; i += kThreads) {
+            const int s = i / P, p = i % P;
+            Xs[s * PS + p] = s < len ? ldf(xg, ((b * Tn + t0 + s) * H + h) * P + p) : 0.f;
+        }
+        __syncthreads();
+        const float el = (float)exp(cum[Q - 1]);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                hs[j] = tile_mma(hs[j] * el, Bw + 16 * nb, 1, NS, Xs + 16 * pb, PS, 1, Q, lane);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T, int N, int P>
+__global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
+    using S = BwdShape<N, P>;
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    constexpr int Q = S::Q, QS = S::QS, NS = S::NS, PS = S::PS, NB = S::NB, PB = S::PB, QB = S::QB;
+    constexpr int NTILE = S::NTILE, TPW = S::TPW;
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* Xs = reinterpret_cast<float*>(smem);  // [Q][PS]
+    float* Ys = Xs + Q * PS;                     // dy [Q][PS]
+    float* Bs = Ys + Q * PS;                     // [Q][NS]
+    float* Cs = Bs + Q * NS;                     // [Q][NS]
+    float* Am = Cs + Q * NS;                     // S o L [Q][QS] (rows t, columns s)
+    float* Wm = Am + Q * QS;                     // L o DYX [Q][QS]
+    float* Mm = Wm + Q * QS;                     // M [Q][QS]
+    float* Hs = Mm + Q * QS;                     // H [N][PS]
+    float* Gs = Hs + N * PS;                     // G [N][PS]
+    float* ev = Gs + N * PS;
+    float* wv = ev + Q;
+    float* partB = wv + Q;          // [Q][NB]: B_s . (G x_s) over 16-column pieces
+    float* partC = partB + Q * NB;  // [Q][NB]: C_t . (H dy_t)
+    float* red = partC + Q * NB;    // [kWaves]
+
+    __shared__ CT cum[kBQ];
+    const T* xg = static_cast<const T*>(prm.x);
+    const T* yg = static_cast<const T*>(prm.dy);
+    const T* Bg = static_cast<const T*>(prm.Bm);
+    const T* Cg = static_cast<const T*>(prm.Cm);
+    T* dxg = static_cast<T*>(prm.dx);
+    const float dskip = prm.D ? prm.D[h] : 0.f;
+
+    // G, the gradient of the state leaving the current chunk, in accumulators (tiles of the
+    // N x P state dealt to the waves) and in Gs
+    f32x4 gs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        gs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kWaves * j;
+        if (tile < NTILE && prm.dfinal) {
+            const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gs[j][i] = prm.dfinal[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16];
+        }
+    }
+    auto write_g = [&]() {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Gs[(16 * nb + 4 * lg + i) * PS + 16 * pb + l16] = gs[j][i];
+            }
+        }
+    };
+    write_g();
+    float dD_acc = 0.f;
+
+    for (int c = prm.nchunks - 1; c >= 0; --c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+        // ---- 1. the chunk's x, dy, B, C and entering state into LDS (zeros past the end)
+        for (int i = tid; i < Q * P; i += kThreads) {
+            const int s = i / P, p = i % P;
+            const int64_t off = ((b * Tn + t0 + s) * H + h) * P + p;
+            const float xv = s < len ? ldf(xg, off) : 0.f, yv = s < len ? ldf(yg, off) : 0.f;
+            Xs[s * PS + p] = xv;
+            Ys[s * PS + p] = yv;
+            dD_acc += xv * yv;
+        }
+        for (int i = tid; i < Q * N; i += kThreads) {
+            const int s = i / N, n = i % N;
+            const int64_t off = ((b * Tn + t0 + s) * G + g) * N + n;
+            Bs[s * NS + n] = s < len ? ldf(Bg, off) : 0.f;
+            Cs[s * NS + n] = s < len ? ldf(Cg, off) : 0.f;
+        }
+        const float* ck = prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
+        for (int i = tid; i < N * P; i += kThreads) Hs[(i / P) * PS + i % P] = ck[i];
+        chunk_factors<CT>(prm.log_a + (b * Tn + t0) * H + h, H, len, cum, ev, wv, tid);
+        __syncthreads();
+
+        // ---- 2. S o L, L o DYX and M, one 16 x 16 tile (tb, sb) per wave: rows t, columns s
+        if (wave < QB * QB) {
+            const int tb = wave / QB, sb = wave % QB;
+            f32x4 sa = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Cs + 16 * tb * NS, NS, 1, Bs + 16 * sb * NS, 1, NS, N, lane);
+            f32x4 dyx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Xs + 16 * sb * PS, 1, PS, P, lane);
+            const int s = 16 * sb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * lg + i;
+                const float L = s <= t ? (float)exp(cum[t] - cum[s]) : 0.f;
+                Am[t * QS + s] = sa[i] * L;
+                Wm[t * QS + s] = dyx[i] * L;
+                Mm[t * QS + s] = sa[i] * L * dyx[i];
+            }
+        }
+        __syncthreads();
+
+        // ---- 3. dx, dB, dC (and the state terms of dcum), tiles dealt to the waves
+        const float el = ev[Q - 1];
+        // dx: Q x P tiles (sb, pb)
+        for (int tile = wave; tile < QB * PB; tile += kWaves) {
+            const int sb = tile / PB, pb = tile % PB;
+            // sum_t (S o L)_ts dy_t: A(s, t) = Am[t][s]
+            f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
+            // w_s B_s^T G: A(s, n) = Bs[s][n], B(n, p) = Gs[n][p]
+            const f32x4 bg = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Bs + 16 * sb * NS, NS, 1, Gs + 16 * pb, PS, 1, N, lane);
+            const int p = 16 * pb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * sb + 4 * lg + i;
+                const float v = acc[i] + wv[s] * bg[i] + dskip * Ys[s * PS + p];
+                if (s < len) dxg[((b * Tn + t0 + s) * H + h) * P + p] = from_f32<T>(v);
+            }
+        }
+        // dB: Q x N tiles (sb, nb)
+        for (int tile = wave; tile < QB * NB; tile += kWaves) {
+            const int sb = tile / NB, nb = tile % NB;
+            // sum_t (L o DYX)_ts C_t: A(s, t) = Wm[t][s], B(t, n) = Cs[t][n]
+            const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Wm + 16 * sb, 1, QS, Cs + 16 * nb, NS, 1, Q, lane);
+            // G x_s: A(s, p) = Xs[s][p], B(p, n) = Gs[n][p]
+            const f32x4 gx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Xs + 16 * sb * PS, PS, 1, Gs + 16 * nb * PS, 1, PS, P,
+                                      lane);
+            const int n = 16 * nb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * sb + 4 * lg + i;
+                const float v = acc[i] + wv[s] * gx[i];
+                if (s < len) atomicAdd(prm.dB + ((b * Tn + t0 + s) * G + g) * N + n, v);
+                const float part = group16_sum(Bs[s * NS + n] * gx[i]);
+                if (l16 == 0) partB[s * NB + nb] = part;
+            }
+        }
+        // dC: Q x N tiles (tb, nb)
+        for (int tile = wave; tile < QB * NB; tile += kWaves) {
+            const int tb = tile / NB, nb = tile % NB;
+            // sum_s (L o DYX)_ts B_s: A(t, s) = Wm[t][s], B(s, n) = Bs[s][n]
+            const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Wm + 16 * tb * QS, QS, 1, Bs + 16 * nb, NS, 1, Q, lane);
+            // H dy_t: A(t, p) = Ys[t][p], B(p, n) = Hs[n][p]
+            const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS, P,
+                                      lane);
+            const int n = 16 * nb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * lg + i;
+                const float v = acc[i] + ev[t] * hd[i];
+                if (t < len) atomicAdd(prm.dC + ((b * Tn + t0 + t) * G + g) * N + n, v);
+                const float part = group16_sum(Cs[t * NS + n] * hd[i]);
+                if (l16 == 0) partC[t * NB + nb] = part;
+            }
+        }
+        // <G, H>, block-wide
+        float gh = 0.f;
+        for (int i = tid; i < N * P; i += kThreads) gh += Gs[(i / P) * PS + i % P] * Hs[(i / P) * PS + i % P];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off, kWave);
+        if (lane == 0) red[wave] = gh;
+        __syncthreads();
+
+        // ---- 4. dcum, then dlog a as its reverse running sum (wave 0)
+        if (tid < kWave) {
+            float d = 0.f, wpb = 0.f;
+            if (tid < Q) {
+                const int t = tid;
+                float row = 0.f, col = 0.f, pb_ = 0.f, pc_ = 0.f;
+                for (int s = 0; s <= t; ++s) row += Mm[t * QS + s];
+                for (int u = t; u < Q; ++u) col += Mm[u * QS + t];
+                for (int nb = 0; nb < NB; ++nb) {
+                    pb_ += partB[t * NB + nb];
+                    pc_ += partC[t * NB + nb];
+                }
+                d = row - col + ev[t] * pc_ - wv[t] * pb_;
+                wpb = wv[t] * pb_;
+            }
+            // the last token's term: e_last <G, H> + sum_s w_s B_s . (G x_s)
+            float ws = wpb;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off, kWave);
+            if (tid == Q - 1) {
+                float ghs = 0.f;
+                for (int k = 0; k < kWaves; ++k) ghs += red[k];
+                d += el * ghs + ws;
+            }
+            // reverse inclusive running sum over t
+            float r = tid < Q ? d : 0.f;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float o = __shfl_down(r, off, kWave);
+                if (tid + off < kWave) r += o;
+            }
+            if (tid < len) prm.dlog_a[(b * Tn + t0 + tid) * H + h] = r;
+        }
+
+        // ---- 5. the gradient entering the chunk: G <- e_last G + sum_t e_t C_t dy_t^T
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                // A(n, t) = e_t Cs[t][n] (the e_t folded in through Cs below), B(t, p) = Ys[t][p]
+                f32x4 acc = gs[j] * el;
+                const int r = lane % 16, gq = lane / 16;
+#pragma unroll 4
+                for (int k = 0; k < Q; k += 4)
+                    acc = mfma_f32(Cs[(k + gq) * NS + 16 * nb + r] * ev[k + gq], Ys[(k + gq) * PS + 16 * pb + r], acc);
+                gs[j] = acc;
+            }
+        }
+        __syncthreads();  // every read of Gs, Hs and the chunk tiles above is done
+        write_g();
+    }
+    __syncthreads();
+    if (prm.dinit) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) prm.dinit[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16] = gs[j][i];
+            }
+        }
+    }
+    // dy . x over the unit, for dD
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dD_acc += __shfl_xor(dD_acc, off, kWave);
+    if (lane == 0) red[wave] = dD_acc;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int k = 0; k < kWaves; ++k) s += red[k];
+        prm.dD_part[unit] = s;
+    }
+}
+
+// dD[h] = sum over the batch of the walk's per-(batch, head) sums; dB, dC zeroed by zero_kernel.
+__global__ void __launch_bounds__(kThreads) bwd_reduce_kernel(const float* part, float* dD, int64_t batch, int64_t H) {
+    const int64_t h = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (h >= H) return;
+    float s = 0.f;
+    for (int64_t b = 0; b < batch; ++b) s += part[b * H + h];
+    dD[h] = s;
+}
+
+__global__ void __launch_bounds__(kThreads) zero_kernel(float* a, int64_t n, float* b2, int64_t n2) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) a[i] = 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n2; i += stride) b2[i] = 0.f;
+}
+
+template <typename T, int N, int P>
+int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
+    using S = BwdShape<N, P>;
+    static_assert(S::walk_lds + 1024 <= kMaxLds, "backward walk LDS budget (with its static running sums)");
+    static bool attr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    if (!attr[dev]) {
+        // (the dynamic size the kernel uses, not the whole 160 KiB: its static LDS counts too)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_walk_kernel<T, N, P>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::walk_lds) != hipSuccess)
+            return -1;
+        attr[dev] = true;
+    }
+    const int64_t units = bl.p.batch * bl.p.nheads;
+    BwdParams p = bl.p;
+    p.per_xcd = (units + 7) / 8;
+    const int64_t nbc = bl.p.batch * bl.p.seqlen * bl.p.ngroups * N;
+    int k = 0;
+    if (nbc > 0 &&
+        !launch_k(bl, k, zero_kernel, dim3((unsigned)std::min<int64_t>((nbc + kThreads - 1) / kThreads, 4096)),
+                  dim3(kThreads), 0, stream, p.dB, nbc, p.dC, nbc))
+        return -1;
+    if (units > 0) {
+        if (!launch_k(bl, k, bwd_states_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kThreads),
+                      S::states_lds, stream, p))
+            return -1;
+        if (!launch_k(bl, k, bwd_walk_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kThreads), S::walk_lds,
+                      stream, p))
+            return -1;
+    }
+    if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)((bl.p.nheads + kThreads - 1) / kThreads)),
+                          dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads))
+        return -1;
+    return 0;
+}
+
+#define SSD_BWD_SHAPES(X) \
+    X(16, 16) X(16, 32) X(16, 64) X(32, 16) X(32, 32) X(32, 64) X(64, 16) X(64, 32) X(64, 64) X(128, 16) X(128, 32) X(128, 64)
+
+}  // namespace
+
+bool backward_shape_supported(int N, int P) {
+#define SSD_BWD_MATCH(NN, PP) \
+    if (N == NN && P == PP) return true;
+    SSD_BWD_SHAPES(SSD_BWD_MATCH)
+#undef SSD_BWD_MATCH
+    return false;
+}
+
+size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P) {
+    const int64_t nchunks = (seqlen + kBQ - 1) / kBQ;
+    const size_t ck = (size_t)(batch * nheads * nchunks) * (size_t)N * (size_t)P * 4;
+    return (ck + 255) / 256 * 256 + ((size_t)(batch * nheads) * 4 + 255) / 256 * 256;
+}
+
+int launch_backward(const BackwardLaunch& bl, hipStream_t stream) {
+    const int N = (int)bl.dstate, P = (int)bl.headdim;
+#define SSD_BWD_LAUNCH(NN, PP)                                                             \
+    if (N == NN && P == PP)                                                                \
+        return bl.dtype == 0 ? launch_backward_t<float, NN, PP>(bl, stream)              \
+                             : launch_backward_t<__bf16, NN, PP>(bl, stream);
+    SSD_BWD_SHAPES(SSD_BWD_LAUNCH)
+#undef SSD_BWD_LAUNCH
+    return -2;
+}
+
+int backward_chunk() { return kBQ; }
+
+}  // namespace ssd

@@ -106,6 +106,44 @@ struct Walk2Params {
     float* seg_decay;
 };
 
+// The backward pass (ssd_bwd.hip), scalar decay: inputs, the gradients it writes, and its
+// workspace (the state entering every backward chunk, and per-(batch, head) sums for dD).
+struct BwdParams {
+    const void* x;
+    const float* log_a;
+    const void* Bm;
+    const void* Cm;
+    const float* D;
+    const float* init;
+    const void* dy;
+    const float* dfinal;
+    void* dx;
+    float* dlog_a;
+    float* dB;
+    float* dC;
+    float* dD;
+    float* dinit;
+    float* ckpt;
+    float* dD_part;
+    int64_t batch, seqlen, nheads, ngroups;
+    int nchunks;  // backward chunks (backward_chunk() tokens each)
+    int64_t per_xcd;
+};
+struct BackwardLaunch {
+    int dtype;
+    int64_t headdim, dstate;
+    BwdParams p;
+    // optional timing events, as in ForwardLaunch
+    hipEvent_t const* events;
+    int n_events;
+    int* n_launches;
+};
+bool backward_shape_supported(int N, int P);
+size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P);
+int backward_chunk();
+// 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.
+int launch_backward(const BackwardLaunch& bl, hipStream_t stream);
+
 // Everything one forward call needs, already validated.
 struct ForwardLaunch {
     int dtype;  // 0 fp32, 1 bf16
@@ -140,9 +178,9 @@ bool shape_supported(int dtype, int N, int P);
 // Launch k of a forward call (k counts up).  With the caller's timing events the dispatch itself
 // stamps events[2k] when it starts and events[2k+1] when it ends (hipExtLaunchKernel), so timing
 // puts no extra packets between dependent kernels.  Updates *fl.n_launches; false on a HIP error.
-template <typename F, typename... Args>
-bool launch_k(const ForwardLaunch& fl, int& k, F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-              Args... args) {
+// (L: ForwardLaunch or BackwardLaunch, anything with events, n_events and n_launches)
+template <typename L, typename F, typename... Args>
+bool launch_k(const L& fl, int& k, F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream, Args... args) {
     hipEvent_t start = nullptr, stop = nullptr;
     if (fl.events && 2 * k + 1 < fl.n_events) {
         start = fl.events[2 * k];

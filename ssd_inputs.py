@@ -132,3 +132,13 @@ def dt_bias(nheads: int, seed: int):
     """A step-size bias per head, ~ N(0, 0.25) fp32 [H], from its own generator (seed)."""
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
     return torch.randn(nheads, generator=gen, dtype=torch.float32) * 0.5
+
+
+def output_gradients(cfg: dict, seed: int) -> dict:
+    """Seeded dL/dy (N(0,1) in the storage dtype, [B,T,H,P]) and dL/dfinal (N(0,1) fp32
+    [B,H,N,P]) for backward-pass workloads, from their own generator."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    Bsz, T, H, P, N = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"]
+    dy = torch.randn((Bsz, T, H, P), generator=gen, dtype=torch.float32).to(STORAGE[cfg["dtype"]]).contiguous()
+    dfinal = torch.randn((Bsz, H, N, P), generator=gen, dtype=torch.float32)
+    return dict(dy=dy, dfinal=dfinal)

@@ -28,7 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
+    assert declared_functions() == ["ssd_backward", "ssd_backward_profiled", "ssd_backward_workspace_bytes",
+                                    "ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
                                     "ssd_forward_dt_workspace_bytes", "ssd_forward_profiled",
                                     "ssd_forward_workspace_bytes", "ssd_step", "ssd_step_dt",
                                     "ssd_strerror"]
@@ -256,3 +257,37 @@ def test_step_dt_rejects_bad_arguments(lib):
     assert call(d, A_log=None) == ssd.SSD_ERR_INVALID
     assert call(d, bias=FAKE + 8) == ssd.SSD_ERR_ALIGN
     assert call(mamba2_dims(dstate=48)) == ssd.SSD_ERR_UNSUPPORTED
+
+
+# ---- the backward pass
+def test_backward_workspace_bytes(lib):
+    # one fp32 N x P state per (batch, head, 32 tokens), then 4 bytes per (batch, head), each part
+    # on a 256-byte boundary
+    up = lambda v: (v + 255) // 256 * 256
+    d = mamba2_dims(batch=2, seqlen=300, nheads=4)
+    assert ssd.ssd_backward_workspace_bytes(d) == up(2 * 4 * 10 * 128 * 64 * 4) + up(2 * 4 * 4)
+    assert ssd.ssd_backward_workspace_bytes(mamba2_dims(batch=0)) == 0
+    assert ssd.ssd_backward_workspace_bytes(mamba2_dims(decay=1)) == 0          # scalar decay only
+    assert ssd.ssd_backward_workspace_bytes(mamba2_dims(headdim=128)) == 0      # P <= 64
+
+
+def call_backward(lib, dims, ws_bytes=1 << 30, **over):
+    p = dict(x=FAKE, la=FAKE, B=FAKE, C=FAKE, D=None, init=None, dy=FAKE, dfin=None, dx=FAKE, dla=FAKE, dB=FAKE,
+             dC=FAKE, dD=None, dinit=None, ws=FAKE)
+    p.update(over)
+    return lib.ssd_backward(ctypes.byref(dims), p["x"], p["la"], p["B"], p["C"], p["D"], p["init"], p["dy"],
+                            p["dfin"], p["dx"], p["dla"], p["dB"], p["dC"], p["dD"], p["dinit"], p["ws"], ws_bytes,
+                            None)
+
+
+@pytest.mark.parametrize("name", ["x", "la", "B", "C", "dy", "dx", "dla", "dB", "dC"])
+def test_backward_rejects_null_required_pointer(lib, name):
+    assert call_backward(lib, mamba2_dims(), **{name: None}) == ssd.SSD_ERR_INVALID
+
+
+def test_backward_rejects_bad_arguments(lib):
+    assert call_backward(lib, mamba2_dims(), dD=FAKE + 4) == ssd.SSD_ERR_ALIGN
+    assert call_backward(lib, mamba2_dims(decay=1)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_backward(lib, mamba2_dims(dstate=256)) == ssd.SSD_ERR_UNSUPPORTED
+    need = ssd.ssd_backward_workspace_bytes(mamba2_dims())
+    assert call_backward(lib, mamba2_dims(), ws_bytes=need - 1) == ssd.SSD_ERR_INVALID

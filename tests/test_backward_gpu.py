@@ -1,0 +1,83 @@
+"""ssd_backward on the GPU against the fp64 adjoint (oracle/backward.py), gradient by gradient,
+on the same seeded inputs and output gradients.  Bounds as for the forward pass: relative L2
+<= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs, on dx, dlog a, dB, dC, dD and dinit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.backward
+import ssd_chunked_scan_02_amd as ssd
+import ssd_inputs
+from gpu_helpers import announce, rel_l2, to_gpu, TOL
+
+pytestmark = pytest.mark.gpu
+
+f64 = ssd_inputs.to_f64
+
+CASES = [
+    ("tiny_fp32", dict(seqlen=200, init=True, skip=True), "fp32-n16"),
+    ("tiny_fp32", dict(seqlen=100, nheads=4, ngroups=2, dstate=64, headdim=32, init=True, skip=True,
+                       a_log="uniform16"), "fp32-groups"),
+    ("mamba2_layer", dict(batch=2, seqlen=300, nheads=4), "bf16-n128"),
+    ("mamba2_layer", dict(batch=2, seqlen=150, nheads=4, ngroups=2, dstate=64, init=True), "bf16-n64-init"),
+    ("mamba2_layer", dict(batch=1, seqlen=77, nheads=2, dstate=32, headdim=16, init=True, dt_mean=-8.0), "bf16-slow"),
+    ("mamba2_layer", dict(batch=1, seqlen=64, nheads=2, dt_mean=3.0), "bf16-fast"),
+    # many backward chunks and a ragged tail; eight heads per group (dB, dC summed over them)
+    ("gqa_decode", dict(batch=2, seqlen=1500, nheads=16, ngroups=2, decode_steps=0, init=True), "bf16-long-gqa"),
+    ("tiny_fp32", dict(batch=2, seqlen=1100, nheads=2, dstate=128, headdim=64, init=True, skip=True,
+                       a_log="uniform16", dt_mean=-2.0), "fp32-long"),
+]
+
+
+@pytest.mark.parametrize("name,over,label", CASES, ids=[c[2] for c in CASES])
+def test_backward_matches_adjoint(name, over, label):
+    cfg = ssd_inputs.config(name, **over)
+    announce("backward %s cfg=%s" % (label, {k: cfg[k] for k in ("batch", "seqlen", "nheads", "ngroups", "headdim",
+                                                                   "dstate", "dtype", "init", "skip")}))
+    inp = ssd_inputs.make_inputs(cfg, 71)
+    og = ssd_inputs.output_gradients(cfg, 171)
+    g = to_gpu(dict(inp, **og))
+    got = ssd.ssd_backward(g["x"], g["log_a"], g["B"], g["C"], g["dy"], g.get("D"), init_state=g.get("init_state"),
+                           dfinal=g["dfinal"])
+    torch.cuda.synchronize()
+    want = oracle.backward.backward(f64(inp["x"]), f64(inp["log_a"]), f64(inp["B"]), f64(inp["C"]), f64(inp.get("D")),
+                                    f64(inp.get("init_state")), f64(og["dy"]), f64(og["dfinal"]))
+    tol = TOL[cfg["dtype"]]
+    errs = {}
+    for k in ("dx", "dlog_a", "dB", "dC", "dinit") + (("dD",) if cfg["skip"] else ()):
+        errs[k] = rel_l2(got[k].double().cpu().numpy(), want[k])
+    announce("backward %s: " % label + " ".join("%s %.2e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
+    assert all(np.isfinite(got[k].float().cpu().numpy()).all() for k in errs)
+    assert all(e <= tol for e in errs.values()), errs
+
+
+def test_backward_optional_arguments():
+    """No D, no initial state, no dfinal; dD and dinit not requested: the gradients of
+    <dy, y> alone (the oracle with zeros in their place)."""
+    cfg = ssd_inputs.config("mamba2_layer", batch=1, seqlen=130, nheads=2, skip=False)
+    announce("backward optional arguments")
+    inp = ssd_inputs.make_inputs(cfg, 73)
+    og = ssd_inputs.output_gradients(cfg, 173)
+    g = to_gpu(dict(inp, **og))
+    got = ssd.ssd_backward(g["x"], g["log_a"], g["B"], g["C"], g["dy"], want_dD=False, want_dinit=False)
+    torch.cuda.synchronize()
+    want = oracle.backward.backward(f64(inp["x"]), f64(inp["log_a"]), f64(inp["B"]), f64(inp["C"]), None, None,
+                                    f64(og["dy"]), None)
+    assert got["dD"] is None and got["dinit"] is None
+    for k in ("dx", "dlog_a", "dB", "dC"):
+        e = rel_l2(got[k].double().cpu().numpy(), want[k])
+        assert e <= TOL["bf16"], (k, e)
+
+
+def test_backward_empty_sequence():
+    """T = 0: dinit = dfinal, dD = 0, nothing else to write."""
+    cfg = ssd_inputs.config("tiny_fp32", seqlen=0, init=True, skip=True)
+    announce("backward empty sequence")
+    x = torch.zeros((1, 0, 1, 64), device="cuda")
+    la = torch.zeros((1, 0, 1), device="cuda")
+    Bm = torch.zeros((1, 0, 1, 16), device="cuda")
+    dfinal = torch.randn((1, 1, 16, 64), device="cuda")
+    got = ssd.ssd_backward(x, la, Bm, Bm.clone(), x.clone(), torch.ones(1, device="cuda"),
+                           init_state=torch.ones((1, 1, 16, 64), device="cuda"), dfinal=dfinal)
+    torch.cuda.synchronize()
+    assert torch.equal(got["dinit"], dfinal) and float(got["dD"][0]) == 0.0
