@@ -56,33 +56,65 @@ __device__ __forceinline__ float group16_sum(float v) {
     return v;
 }
 
+// element j of a 16-byte piece as fp32
+template <typename T> __device__ __forceinline__ float piece_elem(uint4 u, int j);
+template <> __device__ __forceinline__ float piece_elem<__bf16>(uint4 u, int j) { return (float)as_bf16x8(u)[j]; }
+template <> __device__ __forceinline__ float piece_elem<float>(uint4 u, int j) { return as_f32x4(u)[j]; }
+
+constexpr int kBWaves = 8;                     // waves per backward workgroup
+constexpr int kBThreads = kBWaves * kWave;
+
 template <int N, int P>
 struct BwdShape {
     static constexpr int Q = kBQ, QS = Q + 1, NS = N + 1, PS = P + 1;
     static constexpr int NB = N / 16, PB = P / 16, QB = Q / 16;
-    static constexpr int NTILE = NB * PB, TPW = (NTILE + kWaves - 1) / kWaves;  // state tiles
-    // walk LDS (floats): X, dY [Q][PS]; B, C [Q][NS]; S o L, L o DYX, M [Q][QS]; H, G [N][PS];
-    // e, w [Q]; row partial sums of B . (G x) and C . (H dy) [Q][NB] each; reduction [kWaves]
-    // (the running sums themselves in a static array of the accumulation type)
-    static constexpr size_t walk_floats = (size_t)2 * Q * PS + 2 * Q * NS + 3 * Q * QS + 2 * N * PS + 2 * Q +
-                                          2 * Q * NB + kWaves;
+    static constexpr int NTILE = NB * PB, TPW = (NTILE + kBWaves - 1) / kBWaves;  // state tiles per wave
+    // walk LDS (floats): X, dY [Q][PS]; B, C [Q][NS]; S o L, L o DYX, DYX [Q][QS]; H, G [N][PS];
+    // e, w, row sums and column sums of M [Q]; row partial sums of B . (G x) and C . (H dy)
+    // [Q][NB] each; reduction [kBWaves]  (the running sums in a static array of their own type)
+    static constexpr size_t walk_floats = (size_t)2 * Q * PS + 2 * Q * NS + 3 * Q * QS + 2 * N * PS + 4 * Q +
+                                          2 * Q * NB + kBWaves;
     static constexpr size_t walk_lds = walk_floats * 4;
     // states LDS (floats): w o B [Q][NS], X [Q][PS]
     static constexpr size_t states_lds = ((size_t)Q * NS + Q * PS) * 4;
 };
 
-template <typename T>
-__device__ __forceinline__ float ldf(const T* p, int64_t i) {
-    return to_f32(p[i]);
-}
+// One chunk's rows of a [.., rows, width] tensor in 16-byte pieces, a chunk ahead of their use:
+// piece u of the chunk is row u / (width / VE), elements VE (u % (width / VE)) .. + VE; rows at
+// or past len are zeros.  Each thread holds pieces tid + kBThreads i.
+template <typename T, int ROWS, int WIDTH>
+struct ChunkRows {
+    static constexpr int VE = 16 / (int)sizeof(T), PER_ROW = WIDTH / VE, PIECES = ROWS * PER_ROW;
+    static constexpr int PT = (PIECES + kBThreads - 1) / kBThreads;
+    uint4 v[PT];
+    // row r of the chunk starts at base + r * stride (elements)
+    __device__ void load(const T* base, int64_t stride, int len, int tid) {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int u = tid + kBThreads * i, r = u / PER_ROW, c = (u % PER_ROW) * VE;
+            v[i] = (u < PIECES && r < len) ? ld16(base + r * stride + c) : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+    // into an fp32 LDS tile with row stride ld
+    __device__ void stage(float* dst, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int u = tid + kBThreads * i, r = u / PER_ROW, c = (u % PER_ROW) * VE;
+            if (u < PIECES)
+#pragma unroll
+                for (int j = 0; j < VE; ++j) dst[r * ld + c + j] = piece_elem<T>(v[i], j);
+        }
+    }
+    __device__ float elem(int i, int j) const { return piece_elem<T>(v[i], j); }
+};
 
-// Running sum of log a over one chunk (tokens past len add 0), into cum[0..Q), by wave 0;
-// then e and w.  CT is double for fp32 inputs (as the forward's generic path), and cum keeps it.
+// Running sum of log a over one chunk from la_v (token tid's log a in lanes tid < Q of wave 0, 0
+// past the chunk's end), into cum[0..Q); then e = exp(cum) and w = exp(cum_last - cum).  CT is
+// double for fp32 inputs (as the forward's generic path), and cum keeps it.
 template <typename CT>
-__device__ __forceinline__ void chunk_factors(const float* la, int64_t stride, int len, CT* cum, float* e, float* w,
-                                              int tid) {
+__device__ __forceinline__ void chunk_factors(float la_v, CT* cum, float* e, float* w, int tid) {
     if (tid < kWave) {
-        CT v = (tid < len && tid < kBQ) ? (CT)la[(int64_t)tid * stride] : (CT)0;
+        CT v = tid < kBQ ? (CT)la_v : (CT)0;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
             const CT o = __shfl_up(v, off, kWave);
@@ -99,7 +131,7 @@ __device__ __forceinline__ void chunk_factors(const float* la, int64_t stride, i
 
 // ---------------------------------------------------------------------------------------
 template <typename T, int N, int P>
-__global__ void __launch_bounds__(kThreads) bwd_states_kernel(BwdParams prm) {
+__global__ void __launch_bounds__(kBThreads) bwd_states_kernel(BwdParams prm) {
     using S = BwdShape<N, P>;
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     constexpr int Q = S::Q, NS = S::NS, PS = S::PS, PB = S::PB, NTILE = S::NTILE, TPW = S::TPW;
@@ -109,8 +141,8 @@ __global__ void __launch_bounds__(kThreads) bwd_states_kernel(BwdParams prm) {
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
     extern __shared__ __align__(16) unsigned char smem[];
-    float* Bw = reinterpret_cast<float*>(smem);
-    float* Xs = Bw + Q * NS;
+    float* Bw = reinterpret_cast<float*>(smem);  // w o B [Q][NS]
+    float* Xs = Bw + Q * NS;                     // [Q][PS]
     __shared__ CT cum[kBQ];
     __shared__ float e_unused[kBQ], w_s[kBQ];
     const T* xg = static_cast<const T*>(prm.x);
@@ -120,42 +152,49 @@ __global__ void __launch_bounds__(kThreads) bwd_states_kernel(BwdParams prm) {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int tile = wave + kWaves * j;
+        const int tile = wave + kBWaves * j;
         if (tile < NTILE && prm.init) {
             const int nb = tile / PB, pb = tile % PB;
 #pragma unroll
             for (int i = 0; i < 4; ++i) hs[j][i] = prm.init[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16];
         }
     }
-    for (int c = 0; c < prm.nchunks; ++c) {
+    ChunkRows<T, Q, N> rb;
+    ChunkRows<T, Q, P> rx;
+    float rla = 0.f;
+    auto load = [&](int c) {
         const int64_t t0 = (int64_t)c * Q;
         const int len = (int)min((int64_t)Q, Tn - t0);
+        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
+        rla = tid < len && tid < Q ? prm.log_a[(b * Tn + t0 + tid) * H + h] : 0.f;
+    };
+    if (prm.nchunks > 0) load(0);
+    for (int c = 0; c < prm.nchunks; ++c) {
         // the checkpoint: the state entering chunk c
         float* ck = prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kWaves * j;
+            const int tile = wave + kBWaves * j;
             if (tile < NTILE) {
                 const int nb = tile / PB, pb = tile % PB;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ck[(16 * nb + 4 * lg + i) * P + 16 * pb + l16] = hs[j][i];
             }
         }
-        chunk_factors<CT>(prm.log_a + (b * Tn + t0) * H + h, H, len, cum, e_unused, w_s, tid);
+        chunk_factors<CT>(rla, cum, e_unused, w_s, tid);
         __syncthreads();
-        for (int i = tid; i < Q * N; i += kThreads) {
-            const int s = i / N, n = i % N;
-            Bw[s * NS + n] = s < len ? w_s[s] * ldf(Bg, ((b * Tn + t0 + s) * G + g) * N + n) : 0.f;
-        }
-        for (int i = tid; i < Q * P; i += kThreads) {
-            const int s = i / P, p = i % P;
-            Xs[s * PS + p] = s < len ? ldf(xg, ((b * Tn + t0 + s) * H + h) * P + p) : 0.f;
-        }
+        rb.stage(Bw, NS, tid);
+        rx.stage(Xs, PS, tid);
         __syncthreads();
+        // w o B in place (rows past the end are zero already)
+        for (int i = tid; i < Q * N; i += kBThreads) Bw[(i / N) * NS + i % N] *= w_s[i / N];
         const float el = (float)exp(cum[Q - 1]);
+        __syncthreads();
+        if (c + 1 < prm.nchunks) load(c + 1);
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kWaves * j;
+            const int tile = wave + kBWaves * j;
             if (tile < NTILE) {
                 const int nb = tile / PB, pb = tile % PB;
                 hs[j] = tile_mma(hs[j] * el, Bw + 16 * nb, 1, NS, Xs + 16 * pb, PS, 1, Q, lane);
@@ -167,11 +206,13 @@ __global__ void __launch_bounds__(kThreads) bwd_states_kernel(BwdParams prm) {
 
 // ---------------------------------------------------------------------------------------
 template <typename T, int N, int P>
-__global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
+__global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
     using S = BwdShape<N, P>;
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     constexpr int Q = S::Q, QS = S::QS, NS = S::NS, PS = S::PS, NB = S::NB, PB = S::PB, QB = S::QB;
     constexpr int NTILE = S::NTILE, TPW = S::TPW;
+    static_assert(2 * QB * QB <= kBWaves, "one S o L or DYX tile per wave");
+    static_assert(Q * 16 == kBThreads, "row and column sums: 16 threads per row");
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
     const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
     if (unit < 0) return;
@@ -185,16 +226,18 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
     float* Cs = Bs + Q * NS;                     // [Q][NS]
     float* Am = Cs + Q * NS;                     // S o L [Q][QS] (rows t, columns s)
     float* Wm = Am + Q * QS;                     // L o DYX [Q][QS]
-    float* Mm = Wm + Q * QS;                     // M [Q][QS]
-    float* Hs = Mm + Q * QS;                     // H [N][PS]
+    float* Dm = Wm + Q * QS;                     // DYX [Q][QS]
+    float* Hs = Dm + Q * QS;                     // H [N][PS]
     float* Gs = Hs + N * PS;                     // G [N][PS]
     float* ev = Gs + N * PS;
     float* wv = ev + Q;
-    float* partB = wv + Q;          // [Q][NB]: B_s . (G x_s) over 16-column pieces
+    float* rowM = wv + Q;           // sum_s M_ts
+    float* colM = rowM + Q;         // sum_t M_ts
+    float* partB = colM + Q;        // [Q][NB]: B_s . (G x_s) over 16-column pieces
     float* partC = partB + Q * NB;  // [Q][NB]: C_t . (H dy_t)
-    float* red = partC + Q * NB;    // [kWaves]
-
+    float* red = partC + Q * NB;    // [kBWaves]
     __shared__ CT cum[kBQ];
+
     const T* xg = static_cast<const T*>(prm.x);
     const T* yg = static_cast<const T*>(prm.dy);
     const T* Bg = static_cast<const T*>(prm.Bm);
@@ -208,7 +251,7 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         gs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int tile = wave + kWaves * j;
+        const int tile = wave + kBWaves * j;
         if (tile < NTILE && prm.dfinal) {
             const int nb = tile / PB, pb = tile % PB;
 #pragma unroll
@@ -218,7 +261,7 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
     auto write_g = [&]() {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kWaves * j;
+            const int tile = wave + kBWaves * j;
             if (tile < NTILE) {
                 const int nb = tile / PB, pb = tile % PB;
 #pragma unroll
@@ -229,54 +272,86 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
     write_g();
     float dD_acc = 0.f;
 
+    // the next chunk's inputs, a chunk ahead (chunks run last to first)
+    ChunkRows<T, Q, P> rx, ry;
+    ChunkRows<T, Q, N> rb, rc;
+    ChunkRows<float, N, P> rh;
+    float rla = 0.f;
+    auto load = [&](int c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
+        ry.load(yg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
+        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rc.load(Cg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rh.load(prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P, P, N, tid);
+        rla = tid < len && tid < Q ? prm.log_a[(b * Tn + t0 + tid) * H + h] : 0.f;
+    };
+    if (prm.nchunks > 0) load(prm.nchunks - 1);
+
     for (int c = prm.nchunks - 1; c >= 0; --c) {
         const int64_t t0 = (int64_t)c * Q;
         const int len = (int)min((int64_t)Q, Tn - t0);
         // ---- 1. the chunk's x, dy, B, C and entering state into LDS (zeros past the end)
-        for (int i = tid; i < Q * P; i += kThreads) {
-            const int s = i / P, p = i % P;
-            const int64_t off = ((b * Tn + t0 + s) * H + h) * P + p;
-            const float xv = s < len ? ldf(xg, off) : 0.f, yv = s < len ? ldf(yg, off) : 0.f;
-            Xs[s * PS + p] = xv;
-            Ys[s * PS + p] = yv;
-            dD_acc += xv * yv;
-        }
-        for (int i = tid; i < Q * N; i += kThreads) {
-            const int s = i / N, n = i % N;
-            const int64_t off = ((b * Tn + t0 + s) * G + g) * N + n;
-            Bs[s * NS + n] = s < len ? ldf(Bg, off) : 0.f;
-            Cs[s * NS + n] = s < len ? ldf(Cg, off) : 0.f;
-        }
-        const float* ck = prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
-        for (int i = tid; i < N * P; i += kThreads) Hs[(i / P) * PS + i % P] = ck[i];
-        chunk_factors<CT>(prm.log_a + (b * Tn + t0) * H + h, H, len, cum, ev, wv, tid);
+        rx.stage(Xs, PS, tid);
+        ry.stage(Ys, PS, tid);
+        rb.stage(Bs, NS, tid);
+        rc.stage(Cs, NS, tid);
+        rh.stage(Hs, PS, tid);
+#pragma unroll
+        for (int i = 0; i < ChunkRows<T, Q, P>::PT; ++i)
+#pragma unroll
+            for (int j = 0; j < ChunkRows<T, Q, P>::VE; ++j) dD_acc += rx.elem(i, j) * ry.elem(i, j);
+        chunk_factors<CT>(rla, cum, ev, wv, tid);
         __syncthreads();
+        if (c > 0) load(c - 1);
 
-        // ---- 2. S o L, L o DYX and M, one 16 x 16 tile (tb, sb) per wave: rows t, columns s
-        if (wave < QB * QB) {
-            const int tb = wave / QB, sb = wave % QB;
-            f32x4 sa = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Cs + 16 * tb * NS, NS, 1, Bs + 16 * sb * NS, 1, NS, N, lane);
-            f32x4 dyx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Xs + 16 * sb * PS, 1, PS, P, lane);
+        // ---- 2. S o L (waves 0 .. 3) and DYX, L o DYX (waves 4 .. 7), one 16 x 16 tile (tb, sb) each:
+        //         rows t, columns s
+        {
+            const int job = wave % (QB * QB), tb = job / QB, sb = job % QB;
+            const bool scores = wave < QB * QB;
+            const f32x4 v = scores ? tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Cs + 16 * tb * NS, NS, 1, Bs + 16 * sb * NS, 1,
+                                              NS, N, lane)
+                                   : tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Xs + 16 * sb * PS, 1,
+                                              PS, P, lane);
             const int s = 16 * sb + l16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * lg + i;
                 const float L = s <= t ? (float)exp(cum[t] - cum[s]) : 0.f;
-                Am[t * QS + s] = sa[i] * L;
-                Wm[t * QS + s] = dyx[i] * L;
-                Mm[t * QS + s] = sa[i] * L * dyx[i];
+                if (scores) {
+                    Am[t * QS + s] = v[i] * L;
+                } else {
+                    Wm[t * QS + s] = v[i] * L;
+                    Dm[t * QS + s] = v[i];
+                }
             }
         }
         __syncthreads();
 
-        // ---- 3. dx, dB, dC (and the state terms of dcum), tiles dealt to the waves
-        const float el = ev[Q - 1];
-        // dx: Q x P tiles (sb, pb)
-        for (int tile = wave; tile < QB * PB; tile += kWaves) {
+        // ---- 3. row and column sums of M = (S o L) o DYX (16 threads per row or column); dx,
+        //         dB, dC and the state terms of dcum, tiles dealt to the waves
+        {
+            const int r = tid / 16, j = tid % 16;
+            float rs = 0.f, cs = 0.f;
+#pragma unroll
+            for (int k = 2 * j; k < 2 * j + 2; ++k) {
+                rs += Am[r * QS + k] * Dm[r * QS + k];
+                cs += Am[k * QS + r] * Dm[k * QS + r];
+            }
+            rs = group16_sum(rs);
+            cs = group16_sum(cs);
+            if (j == 0) {
+                rowM[r] = rs;
+                colM[r] = cs;
+            }
+        }
+        for (int tile = wave; tile < QB * PB; tile += kBWaves) {
             const int sb = tile / PB, pb = tile % PB;
             // sum_t (S o L)_ts dy_t: A(s, t) = Am[t][s]
-            f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
-            // w_s B_s^T G: A(s, n) = Bs[s][n], B(n, p) = Gs[n][p]
+            const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
+            // B_s^T G: A(s, n) = Bs[s][n], B(n, p) = Gs[n][p]
             const f32x4 bg = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Bs + 16 * sb * NS, NS, 1, Gs + 16 * pb, PS, 1, N, lane);
             const int p = 16 * pb + l16;
 #pragma unroll
@@ -286,63 +361,55 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
                 if (s < len) dxg[((b * Tn + t0 + s) * H + h) * P + p] = from_f32<T>(v);
             }
         }
-        // dB: Q x N tiles (sb, nb)
-        for (int tile = wave; tile < QB * NB; tile += kWaves) {
+        for (int tile = wave; tile < QB * NB; tile += kBWaves) {
             const int sb = tile / NB, nb = tile % NB;
-            // sum_t (L o DYX)_ts C_t: A(s, t) = Wm[t][s], B(t, n) = Cs[t][n]
+            // dB: sum_t (L o DYX)_ts C_t (A(s, t) = Wm[t][s], B(t, n) = Cs[t][n]) + w_s G x_s
             const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Wm + 16 * sb, 1, QS, Cs + 16 * nb, NS, 1, Q, lane);
-            // G x_s: A(s, p) = Xs[s][p], B(p, n) = Gs[n][p]
             const f32x4 gx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Xs + 16 * sb * PS, PS, 1, Gs + 16 * nb * PS, 1, PS, P,
                                       lane);
-            const int n = 16 * nb + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = 16 * sb + 4 * lg + i;
-                const float v = acc[i] + wv[s] * gx[i];
-                if (s < len) atomicAdd(prm.dB + ((b * Tn + t0 + s) * G + g) * N + n, v);
-                const float part = group16_sum(Bs[s * NS + n] * gx[i]);
-                if (l16 == 0) partB[s * NB + nb] = part;
-            }
-        }
-        // dC: Q x N tiles (tb, nb)
-        for (int tile = wave; tile < QB * NB; tile += kWaves) {
-            const int tb = tile / NB, nb = tile % NB;
-            // sum_s (L o DYX)_ts B_s: A(t, s) = Wm[t][s], B(s, n) = Bs[s][n]
-            const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Wm + 16 * tb * QS, QS, 1, Bs + 16 * nb, NS, 1, Q, lane);
-            // H dy_t: A(t, p) = Ys[t][p], B(p, n) = Hs[n][p]
-            const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS, P,
+            // dC: sum_s (L o DYX)_ts B_s (A(t, s) = Wm[t][s], B(s, n) = Bs[s][n]) + e_t H dy_t
+            const f32x4 acc2 = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Wm + 16 * sb * QS, QS, 1, Bs + 16 * nb, NS, 1, Q,
+                                        lane);
+            const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * sb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS, P,
                                       lane);
             const int n = 16 * nb + l16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * lg + i;
-                const float v = acc[i] + ev[t] * hd[i];
-                if (t < len) atomicAdd(prm.dC + ((b * Tn + t0 + t) * G + g) * N + n, v);
-                const float part = group16_sum(Cs[t * NS + n] * hd[i]);
-                if (l16 == 0) partC[t * NB + nb] = part;
+                const int s = 16 * sb + 4 * lg + i;  // (the row: s for dB, t for dC)
+                if (s < len) {
+                    atomicAdd(prm.dB + ((b * Tn + t0 + s) * G + g) * N + n, acc[i] + wv[s] * gx[i]);
+                    atomicAdd(prm.dC + ((b * Tn + t0 + s) * G + g) * N + n, acc2[i] + ev[s] * hd[i]);
+                }
+                const float pbv = group16_sum(Bs[s * NS + n] * gx[i]);
+                const float pcv = group16_sum(Cs[s * NS + n] * hd[i]);
+                if (l16 == 0) {
+                    partB[s * NB + nb] = pbv;
+                    partC[s * NB + nb] = pcv;
+                }
             }
         }
         // <G, H>, block-wide
         float gh = 0.f;
-        for (int i = tid; i < N * P; i += kThreads) gh += Gs[(i / P) * PS + i % P] * Hs[(i / P) * PS + i % P];
+        for (int i = tid; i < N * P; i += kBThreads) gh += Gs[(i / P) * PS + i % P] * Hs[(i / P) * PS + i % P];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off, kWave);
         if (lane == 0) red[wave] = gh;
         __syncthreads();
 
-        // ---- 4. dcum, then dlog a as its reverse running sum (wave 0)
+        // ---- 4. dcum and dlog a as its reverse running sum (wave 0); the gradient entering the
+        //         chunk, G <- e_last G + sum_t e_t C_t dy_t^T (every wave)
+        const float el = ev[Q - 1];
         if (tid < kWave) {
             float d = 0.f, wpb = 0.f;
             if (tid < Q) {
                 const int t = tid;
-                float row = 0.f, col = 0.f, pb_ = 0.f, pc_ = 0.f;
-                for (int s = 0; s <= t; ++s) row += Mm[t * QS + s];
-                for (int u = t; u < Q; ++u) col += Mm[u * QS + t];
+                float pb_ = 0.f, pc_ = 0.f;
+#pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     pb_ += partB[t * NB + nb];
                     pc_ += partC[t * NB + nb];
                 }
-                d = row - col + ev[t] * pc_ - wv[t] * pb_;
+                d = rowM[t] - colM[t] + ev[t] * pc_ - wv[t] * pb_;
                 wpb = wv[t] * pb_;
             }
             // the last token's term: e_last <G, H> + sum_s w_s B_s . (G x_s)
@@ -351,7 +418,8 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
             for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off, kWave);
             if (tid == Q - 1) {
                 float ghs = 0.f;
-                for (int k = 0; k < kWaves; ++k) ghs += red[k];
+#pragma unroll
+                for (int k = 0; k < kBWaves; ++k) ghs += red[k];
                 d += el * ghs + ws;
             }
             // reverse inclusive running sum over t
@@ -363,14 +431,12 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
             }
             if (tid < len) prm.dlog_a[(b * Tn + t0 + tid) * H + h] = r;
         }
-
-        // ---- 5. the gradient entering the chunk: G <- e_last G + sum_t e_t C_t dy_t^T
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kWaves * j;
+            const int tile = wave + kBWaves * j;
             if (tile < NTILE) {
                 const int nb = tile / PB, pb = tile % PB;
-                // A(n, t) = e_t Cs[t][n] (the e_t folded in through Cs below), B(t, p) = Ys[t][p]
+                // A(n, t) = e_t Cs[t][n], B(t, p) = Ys[t][p]
                 f32x4 acc = gs[j] * el;
                 const int r = lane % 16, gq = lane / 16;
 #pragma unroll 4
@@ -386,7 +452,7 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
     if (prm.dinit) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kWaves * j;
+            const int tile = wave + kBWaves * j;
             if (tile < NTILE) {
                 const int nb = tile / PB, pb = tile % PB;
 #pragma unroll
@@ -401,7 +467,7 @@ __global__ void __launch_bounds__(kThreads) bwd_walk_kernel(BwdParams prm) {
     __syncthreads();
     if (tid == 0) {
         float s = 0.f;
-        for (int k = 0; k < kWaves; ++k) s += red[k];
+        for (int k = 0; k < kBWaves; ++k) s += red[k];
         prm.dD_part[unit] = s;
     }
 }
@@ -445,10 +511,10 @@ int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
                   dim3(kThreads), 0, stream, p.dB, nbc, p.dC, nbc))
         return -1;
     if (units > 0) {
-        if (!launch_k(bl, k, bwd_states_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kThreads),
+        if (!launch_k(bl, k, bwd_states_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
                       S::states_lds, stream, p))
             return -1;
-        if (!launch_k(bl, k, bwd_walk_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kThreads), S::walk_lds,
+        if (!launch_k(bl, k, bwd_walk_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads), S::walk_lds,
                       stream, p))
             return -1;
     }
