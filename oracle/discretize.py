@@ -62,3 +62,40 @@ def forward_dt(orc, x, dt, A_log, Bm, Cm, D=None, dt_bias=None, scale_input=True
     if D is not None:
         y = y + np.asarray(D, dtype=np.float64)[None, None, :, None] * x
     return y, final
+
+
+def sigmoid(v):
+    """1 / (1 + e^-v), the derivative of softplus, in float64."""
+    return 0.5 * (1.0 + np.tanh(0.5 * np.asarray(v, dtype=np.float64)))
+
+
+def backward_dt(adj, x, dt, A_log, Bm, Cm, D=None, dt_bias=None, scale_input=True, init_state=None, dy=None,
+                dfinal=None):
+    """Gradients of <dy, y> + <dfinal, final> for ``forward_dt`` (scalar decay), by the chain rule
+    through the discretisation on top of the recurrence's adjoint ``adj`` (``oracle.backward``):
+    with u = dt + bias, Delta = softplus(u), log a = Delta A (A = -exp(A_log)) and the recurrence
+    run on x_in = Delta x (scale_input) or x,
+        dx       = Delta dx_in (or dx_in) + D dy
+        dDelta   = dlog_a A + sum_p dx_in x      (the second term with scale_input only)
+        ddt      = dDelta sigmoid(u),   ddt_bias = sum_{b,t} ddt,   dA_log = sum_{b,t} dlog_a log a
+        dD       = sum_{b,t,p} dy x
+    and dB, dC, dinit as the adjoint gives them.  Returns a dict of float64 arrays."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    delta, log_a = discretize(dt, A_log, dt_bias, False)
+    u = np.asarray(dt, dtype=np.float64)
+    if dt_bias is not None:
+        u = u + np.asarray(dt_bias, dtype=np.float64)[None, None, :]
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))
+    xin = (x * delta[..., None]) if scale_input else x
+    g = adj.backward(xin, log_a, Bm, Cm, None, init_state, dy, dfinal)
+    dxin = g["dx"]
+    dx = dxin * delta[..., None] if scale_input else dxin.copy()
+    if D is not None:
+        dx = dx + np.asarray(D, dtype=np.float64)[None, None, :, None] * dy
+    ddelta = g["dlog_a"] * A[None, None, :]
+    if scale_input:
+        ddelta = ddelta + np.sum(dxin * x, axis=-1)
+    ddt = ddelta * sigmoid(u)
+    return dict(dx=dx, ddt=ddt, ddt_bias=ddt.sum(axis=(0, 1)), dA_log=np.sum(g["dlog_a"] * log_a, axis=(0, 1)),
+                dB=g["dB"], dC=g["dC"], dD=np.einsum("bthp,bthp->h", dy, x), dinit=g["dinit"])

@@ -6,9 +6,12 @@ import tempfile
 
 import pytest
 
+import importlib.util
+
 import oracle
 import oracle.backward as bwd
-from pins_bwd import BWD_PINS
+import oracle.discretize
+from pins_bwd import BWD_DT_PINS, BWD_PINS
 
 
 @pytest.fixture(scope="module")
@@ -60,6 +63,44 @@ def test_backward_mutant_is_caught(orc, workdir, name):
     for pin in BWD_PINS:
         try:
             pin(orc, mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "planted mistake %r passed every pin" % name
+
+
+@pytest.mark.parametrize("pin", BWD_DT_PINS, ids=lambda p: p.__name__)
+def test_backward_dt_pin(orc, pin):
+    pin(orc, bwd.default_adjoint(), oracle.discretize)
+
+
+# planted mistakes in a copy of the discretisation module's chain rule
+DT_MUTANTS = {
+    "sigmoid_is_softplus": ("ddt = ddelta * sigmoid(u)", "ddt = ddelta * softplus(u)"),
+    "A_sign": ("ddelta = g[\"dlog_a\"] * A[None, None, :]", "ddelta = -g[\"dlog_a\"] * A[None, None, :]"),
+    "scale_term_dropped": ("ddelta = ddelta + np.sum(dxin * x, axis=-1)", "ddelta = ddelta"),
+    "dx_not_scaled": ("dx = dxin * delta[..., None] if scale_input else dxin.copy()", "dx = dxin.copy()"),
+    "dA_log_uses_delta": ("np.sum(g[\"dlog_a\"] * log_a, axis=(0, 1))", "np.sum(g[\"dlog_a\"] * delta, axis=(0, 1))"),
+    "bias_not_in_sigmoid": ("u = u + np.asarray(dt_bias, dtype=np.float64)[None, None, :]", "u = u"),
+    "dD_on_scaled_input": ("dD=np.einsum(\"bthp,bthp->h\", dy, x)", "dD=np.einsum(\"bthp,bthp->h\", dy, xin)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DT_MUTANTS))
+def test_backward_dt_mutant_is_caught(orc, workdir, name):
+    before, after = DT_MUTANTS[name]
+    with open(oracle.discretize.__file__) as f:
+        src = f.read()
+    assert src.count(before) == 1, "mutation site for %s must occur exactly once" % name
+    path = os.path.join(workdir, "disc_%s.py" % name)
+    with open(path, "w") as f:
+        f.write(src.replace(before, after))
+    spec = importlib.util.spec_from_file_location("disc_%s" % name, path)
+    mutant = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mutant)
+    caught = []
+    for pin in BWD_DT_PINS:
+        try:
+            pin(orc, bwd.default_adjoint(), mutant)
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, "planted mistake %r passed every pin" % name
