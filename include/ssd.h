@@ -210,6 +210,24 @@ int ssd_backward_profiled(const ssd_dims* dims, const void* x, const float* log_
                           float* dD, float* dinit, void* workspace, size_t workspace_bytes,
                           void* stream, void* const* events, int n_events, int* n_launches);
 
+/*
+ * The backward pass of ssd_forward_dt (scalar decay): the gradients of <dy, y> + <dfinal,
+ * final_state> with respect to x, dt, A_log, dt_bias, B, C, D and init_state, by the chain rule
+ * through the discretisation (Delta = softplus(dt + bias), log a = -Delta exp(A_log), and with
+ * scale_input the input term Delta B x^T) around ssd_backward.
+ *   ddt [B,T,H] fp32 (required); dA_log [H] and ddt_bias [H] fp32 (NULL to skip each);
+ *   dx, dB, dC, dD, dinit as for ssd_backward.
+ *   workspace: at least ssd_backward_dt_workspace_bytes(dims, scale_input) bytes.
+ * Supported shapes and dtypes as ssd_backward.
+ */
+size_t ssd_backward_dt_workspace_bytes(const ssd_dims* dims, int scale_input);
+
+int ssd_backward_dt(const ssd_dims* dims, const void* x, const float* dt, const float* dt_bias,
+                    const float* A_log, int scale_input, const void* B, const void* C,
+                    const float* D, const float* init_state, const void* dy, const float* dfinal,
+                    void* dx, float* ddt, float* dA_log, float* ddt_bias, float* dB, float* dC,
+                    float* dD, float* dinit, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable description of a return code. */
 const char* ssd_strerror(int code);
 

@@ -17,6 +17,8 @@ The functions carry the names of the C entry points declared in ``include/ssd.h`
   ssd_backward_workspace_bytes(dims) -> int
   ssd_backward(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, ...) -> dict of gradients
   ssd_backward_profiled(..., events=(hipEvent_t handles)) -> (gradients, n_launches)
+  ssd_backward_dt_workspace_bytes(dims, scale_input) -> int
+  ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input=True, ...) -> dict
   ssd_strerror(code) -> str
 """
 from __future__ import annotations
@@ -30,6 +32,7 @@ __all__ = ["SSDError", "Dims", "library_path", "load_library", "dims_for",
            "ssd_forward_workspace_bytes", "ssd_forward", "ssd_forward_profiled", "ssd_step",
            "ssd_forward_dt_workspace_bytes", "ssd_forward_dt", "ssd_forward_dt_profiled",
            "ssd_step_dt", "ssd_backward_workspace_bytes", "ssd_backward", "ssd_backward_profiled",
+           "ssd_backward_dt_workspace_bytes", "ssd_backward_dt",
            "ssd_strerror",
            "SSD_F32", "SSD_BF16", "SSD_DECAY_SCALAR", "SSD_DECAY_DIAG"]
 
@@ -98,6 +101,10 @@ def load_library():
         lib.ssd_backward_profiled.argtypes = [dp] + [vp] * 15 + [sz, vp, ctypes.POINTER(vp), i32,
                                                                  ctypes.POINTER(i32)]
         lib.ssd_backward_profiled.restype = i32
+        lib.ssd_backward_dt_workspace_bytes.argtypes = [dp, i32]
+        lib.ssd_backward_dt_workspace_bytes.restype = sz
+        lib.ssd_backward_dt.argtypes = [dp, vp, vp, vp, vp, i32] + [vp] * 15 + [sz, vp]
+        lib.ssd_backward_dt.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -372,6 +379,50 @@ def ssd_backward(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, want_
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_backward")
     return out if _events is None else (out, count.value)
+
+
+def ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input: bool = True,
+                    init_state=None, dfinal=None, want_dD=True, want_dinit=True, workspace=None,
+                    stream=None):
+    """Run ``ssd_backward_dt``: gradients of <dy, y> + <dfinal, final_state> for ssd_forward_dt
+    (scalar decay).  Returns a dict: dx (dtype of x), ddt [B,T,H], dA_log [H], ddt_bias [H] (or
+    None without dt_bias), dB, dC (fp32), dD (or None), dinit (or None)."""
+    bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16")
+    dims = Dims(bsz, T, H, G, P, N, _DTYPE_CODE[x.dtype], SSD_DECAY_SCALAR)
+    dev = x.device
+    _check(x, "x", (bsz, T, H, P), x.dtype, dev)
+    _check(dt, "dt", (bsz, T, H), torch.float32, dev)
+    _check(A_log, "A_log", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(B, "B", (bsz, T, G, N), x.dtype, dev)
+    _check(C, "C", (bsz, T, G, N), x.dtype, dev)
+    _check(dy, "dy", (bsz, T, H, P), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (bsz, H, N, P), torch.float32, dev)
+    _check(dfinal, "dfinal", (bsz, H, N, P), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty((bsz, T, H), **f32), dA_log=torch.empty(H, **f32),
+               ddt_bias=torch.empty(H, **f32) if dt_bias is not None else None,
+               dB=torch.empty((bsz, T, G, N), **f32), dC=torch.empty((bsz, T, G, N), **f32),
+               dD=torch.empty(H, **f32) if want_dD else None,
+               dinit=torch.empty((bsz, H, N, P), **f32) if want_dinit else None)
+    lib = load_library()
+    scale = 1 if scale_input else 0
+    need = int(lib.ssd_backward_dt_workspace_bytes(ctypes.byref(dims), scale))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ssd_backward_dt(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), scale,
+                             _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal),
+                             _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA_log"]),
+                             _ptr(out["ddt_bias"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                             _ptr(out["dinit"]), _ptr(workspace), ws_bytes, _stream_handle(stream, dev))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_backward_dt")
+    return out
 
 
 def ssd_step(state, x_t, log_a_t, B_t, C_t, D=None, y_t=None, stream=None):

@@ -308,6 +308,55 @@ int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, 
     return rc == 0 ? SSD_OK : SSD_ERR_HIP;
 }
 
+size_t ssd_backward_dt_workspace_bytes(const ssd_dims* d, int scale_input) {
+    if (check_backward(d) != SSD_OK || d->batch == 0) return 0;
+    return ssd::dt_backward_layout(d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim,
+                                   d->dtype == SSD_BF16 ? 2 : 4, scale_input != 0)
+        .total;
+}
+
+int ssd_backward_dt(const ssd_dims* d, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                    int scale_input, const void* B, const void* C, const float* D, const float* init_state,
+                    const void* dy, const float* dfinal, void* dx, float* ddt, float* dA_log, float* ddt_bias,
+                    float* dB, float* dC, float* dD, float* dinit, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    int rc = check_backward(d);
+    if (rc != SSD_OK) return rc;
+    const bool has_tokens = d->batch > 0 && d->seqlen > 0;
+    if (has_tokens && (!x || !dt || !A_log || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_INVALID;
+    if (!A_log && (dA_log || ddt_bias)) return SSD_ERR_INVALID;
+    const void* ptrs[] = {x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, dx, ddt, dA_log, ddt_bias,
+                          dB, dC, dD, dinit, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    const size_t need = ssd_backward_dt_workspace_bytes(d, scale_input);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
+    ssd::BackwardLaunch bl{};
+    bl.dtype = d->dtype;
+    bl.headdim = d->headdim;
+    bl.dstate = d->dstate;
+    ssd::BwdParams& p = bl.p;
+    p.Bm = B;
+    p.Cm = C;
+    p.init = init_state;
+    p.dy = dy;
+    p.dfinal = dfinal;
+    p.dB = dB;
+    p.dC = dC;
+    p.dinit = dinit;
+    p.batch = d->batch;
+    p.seqlen = d->seqlen;
+    p.nheads = d->nheads;
+    p.ngroups = d->ngroups;
+    p.nchunks = (int)((d->seqlen + ssd::backward_chunk() - 1) / ssd::backward_chunk());
+    int count = 0;
+    bl.n_launches = &count;
+    ssd::DtBackwardArgs a{x, dt, dt_bias, A_log, scale_input != 0, D, dy, dx, ddt, dA_log, ddt_bias, dD, workspace};
+    rc = ssd::launch_backward_dt(bl, a, static_cast<hipStream_t>(stream));
+    if (rc == -2) return SSD_ERR_UNSUPPORTED;
+    return rc == 0 ? SSD_OK : SSD_ERR_HIP;
+}
+
 const char* ssd_strerror(int code) {
     switch (code) {
         case SSD_OK: return "success";

@@ -49,6 +49,9 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float* a, int am, int
     return acc;
 }
 
+__device__ __forceinline__ double softplus_ct(double v) { return softplus(v); }
+__device__ __forceinline__ float softplus_ct(float v) { return softplusf(v); }
+
 // Sum over the 16 lanes of a lane group (the 16 columns of one accumulator row).
 __device__ __forceinline__ float group16_sum(float v) {
 #pragma unroll
@@ -524,6 +527,75 @@ int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
     return 0;
 }
 
+// ---------------------------------------------------------------------------------------
+// The discretised form's backward (ssd_backward_dt), by the chain rule around the backward pass
+// above: with u = dt + bias, Delta = softplus(u), log a = -Delta exp(A_log) and the walk run on
+// x_in = Delta x (with the input scale) or x,
+//   dx = Delta dx_in (or dx_in) + D dy,   dDelta = -exp(A_log) dlog a + [scale] sum_p dx_in x,
+//   ddt = dDelta sigmoid(u),   ddt_bias = sum_{b,t} ddt,   dA_log = sum_{b,t} dlog a log a,
+//   dD = sum_{b,t,p} dy x.
+// CT (double for fp32 inputs, float for bf16) carries the per-row arithmetic.
+
+// Per (b, t, h) row: log a into la, and with the input scale Delta x into xs.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) disc_rows_kernel(const float* dt, const float* dt_bias, const float* A_log,
+                                                             const T* x, float* la, T* xs, int64_t rows, int64_t H,
+                                                             int P) {
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (r >= rows) return;
+    const int64_t h = r % H;
+    const CT u = (CT)dt[r] + (dt_bias ? (CT)dt_bias[h] : (CT)0);
+    const CT delta = softplus_ct(u);
+    la[r] = (float)(-delta * exp((CT)A_log[h]));
+    if (xs)
+        for (int p = 0; p < P; ++p) xs[r * P + p] = from_f32<T>((float)(delta * (CT)to_f32(x[r * P + p])));
+}
+
+// Per row: dx, ddt, and the row terms of dA_log (dlog a log a) and dD (dy . x).
+template <typename T>
+__global__ void __launch_bounds__(kThreads) disc_grad_rows_kernel(const float* dt, const float* dt_bias,
+                                                                  const float* A_log, const float* D, const T* x,
+                                                                  const T* dy, const T* dxs, const float* la,
+                                                                  const float* dla, int scale, T* dx, float* ddt,
+                                                                  float* rowA, float* rowD, int64_t rows, int64_t H,
+                                                                  int P) {
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (r >= rows) return;
+    const int64_t h = r % H;
+    const CT u = (CT)dt[r] + (dt_bias ? (CT)dt_bias[h] : (CT)0);
+    const CT delta = softplus_ct(u);
+    const CT dskip = D ? (CT)D[h] : (CT)0;
+    CT xdx = 0, xdy = 0;
+    for (int p = 0; p < P; ++p) {
+        const CT xv = (CT)to_f32(x[r * P + p]), gv = (CT)to_f32(dxs[r * P + p]), yv = (CT)to_f32(dy[r * P + p]);
+        xdx += xv * gv;
+        xdy += xv * yv;
+        dx[r * P + p] = from_f32<T>((float)((scale ? delta * gv : gv) + dskip * yv));
+    }
+    const CT dlog = (CT)dla[r];
+    const CT ddelta = -exp((CT)A_log[h]) * dlog + (scale ? xdx : (CT)0);
+    ddt[r] = (float)(ddelta / (1 + exp(-u)));
+    rowA[r] = (float)(dlog * (CT)la[r]);
+    rowD[r] = (float)xdy;
+}
+
+// out[h] = sum over the (b, t) rows of head h of v (rows = (b, t) * H + h), one workgroup per head.
+__global__ void __launch_bounds__(kThreads) head_sum_kernel(const float* v, float* out, int64_t bt, int64_t H) {
+    const int64_t h = blockIdx.x;
+    float s = 0.f;
+    for (int64_t i = threadIdx.x; i < bt; i += kThreads) s += v[i * H + h];
+    __shared__ float red[kThreads];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[h] = red[0];
+}
+
 #define SSD_BWD_SHAPES(X) \
     X(16, 16) X(16, 32) X(16, 64) X(32, 16) X(32, 32) X(32, 64) X(64, 16) X(64, 32) X(64, 64) X(128, 16) X(128, 32) X(128, 64)
 
@@ -555,5 +627,79 @@ int launch_backward(const BackwardLaunch& bl, hipStream_t stream) {
 }
 
 int backward_chunk() { return kBQ; }
+
+DtBackwardLayout dt_backward_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int elem_bytes,
+                                    bool scale_input) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t rows = (size_t)batch * (size_t)seqlen * (size_t)nheads;
+    DtBackwardLayout l;
+    size_t off = 0;
+    l.la = off; off = up(off + rows * 4);
+    l.xs = off; if (scale_input) off = up(off + rows * P * elem_bytes);
+    l.dxs = off; off = up(off + rows * P * elem_bytes);
+    l.dla = off; off = up(off + rows * 4);
+    l.ddt_rows = 0;  // (the caller's ddt holds them)
+    l.rowA = off; off = up(off + rows * 4);
+    l.rowD = off; off = up(off + rows * 4);
+    l.inner = off; off += backward_workspace_bytes(batch, nheads, seqlen, N, P);
+    l.total = off;
+    return l;
+}
+
+int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipStream_t stream) {
+    const int64_t H = bl0.p.nheads, rows = bl0.p.batch * bl0.p.seqlen * H;
+    const int P = (int)bl0.headdim;
+    const int eb = bl0.dtype == 0 ? 4 : 2;
+    const DtBackwardLayout l = dt_backward_layout(bl0.p.batch, H, bl0.p.seqlen, (int)bl0.dstate, P, eb, a.scale_input != 0);
+    char* ws = static_cast<char*>(a.workspace);
+    float* la = reinterpret_cast<float*>(ws + l.la);
+    void* xs = a.scale_input ? static_cast<void*>(ws + l.xs) : nullptr;
+    void* dxs = ws + l.dxs;
+    float* dla = reinterpret_cast<float*>(ws + l.dla);
+    float* rowA = reinterpret_cast<float*>(ws + l.rowA);
+    float* rowD = reinterpret_cast<float*>(ws + l.rowD);
+    const unsigned grid = (unsigned)((rows + kThreads - 1) / kThreads);
+    if (rows > 0) {
+        if (bl0.dtype == 0)
+            hipLaunchKernelGGL(disc_rows_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias, a.A_log,
+                               static_cast<const float*>(a.x), la, static_cast<float*>(xs), rows, H, P);
+        else
+            hipLaunchKernelGGL(disc_rows_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias,
+                               a.A_log, static_cast<const __bf16*>(a.x), la, static_cast<__bf16*>(xs), rows, H, P);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    // the backward pass on (x_in, log a) with no skip term; dx_in and dlog a into the workspace
+    BackwardLaunch bl = bl0;
+    bl.p.x = xs ? xs : a.x;
+    bl.p.log_a = la;
+    bl.p.D = nullptr;
+    bl.p.dx = dxs;
+    bl.p.dlog_a = dla;
+    bl.p.dD = nullptr;
+    bl.p.ckpt = reinterpret_cast<float*>(ws + l.inner);
+    const int64_t nchunks = bl.p.nchunks;
+    const size_t ck = (size_t)(bl.p.batch * H * nchunks) * (size_t)(bl0.dstate * P) * 4;
+    bl.p.dD_part = reinterpret_cast<float*>(ws + l.inner + (ck + 255) / 256 * 256);
+    const int rc = launch_backward(bl, stream);
+    if (rc != 0) return rc;
+    if (rows > 0) {
+        if (bl0.dtype == 0)
+            hipLaunchKernelGGL(disc_grad_rows_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias,
+                               a.A_log, a.D, static_cast<const float*>(a.x), static_cast<const float*>(a.dy),
+                               static_cast<const float*>(dxs), la, dla, a.scale_input, static_cast<float*>(a.dx), a.ddt,
+                               rowA, rowD, rows, H, P);
+        else
+            hipLaunchKernelGGL(disc_grad_rows_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias,
+                               a.A_log, a.D, static_cast<const __bf16*>(a.x), static_cast<const __bf16*>(a.dy),
+                               static_cast<const __bf16*>(dxs), la, dla, a.scale_input, static_cast<__bf16*>(a.dx),
+                               a.ddt, rowA, rowD, rows, H, P);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    const int64_t bt = bl0.p.batch * bl0.p.seqlen;
+    if (a.ddt_bias) hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, stream, a.ddt, a.ddt_bias, bt, H);
+    if (a.dA_log) hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, stream, rowA, a.dA_log, bt, H);
+    if (a.dD) hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, stream, rowD, a.dD, bt, H);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 }  // namespace ssd

@@ -28,7 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ssd_backward", "ssd_backward_profiled", "ssd_backward_workspace_bytes",
+    assert declared_functions() == ["ssd_backward", "ssd_backward_dt", "ssd_backward_dt_workspace_bytes",
+                                    "ssd_backward_profiled", "ssd_backward_workspace_bytes",
                                     "ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
                                     "ssd_forward_dt_workspace_bytes", "ssd_forward_profiled",
                                     "ssd_forward_workspace_bytes", "ssd_step", "ssd_step_dt",

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle.backward
+import oracle.discretize
 import ssd_chunked_scan_02_amd as ssd
 import ssd_inputs
 from gpu_helpers import announce, rel_l2, to_gpu, TOL
@@ -81,3 +82,49 @@ def test_backward_empty_sequence():
                            init_state=torch.ones((1, 1, 16, 64), device="cuda"), dfinal=dfinal)
     torch.cuda.synchronize()
     assert torch.equal(got["dinit"], dfinal) and float(got["dD"][0]) == 0.0
+
+
+DT_CASES = [
+    ("mamba2_layer", dict(batch=2, seqlen=300, nheads=4, init=True), "bf16"),
+    ("gqa_decode", dict(batch=1, seqlen=700, nheads=8, ngroups=2, decode_steps=0, init=True), "bf16-gqa"),
+    ("tiny_fp32", dict(seqlen=200, nheads=2, skip=True, init=True, a_log="uniform16", dt_mean=-1.0), "fp32"),
+]
+
+
+@pytest.mark.parametrize("scale", [True, False], ids=["scaled", "unscaled"])
+@pytest.mark.parametrize("name,over,label", DT_CASES, ids=[c[2] for c in DT_CASES])
+def test_backward_dt_matches_chain_rule(name, over, label, scale):
+    """ssd_backward_dt against the oracle's chain rule through the discretisation
+    (oracle.discretize.backward_dt on the fp64 adjoint), every gradient."""
+    cfg = ssd_inputs.config(name, **over)
+    announce("backward_dt %s scale=%d" % (label, scale))
+    inp = ssd_inputs.make_inputs(cfg, 75)
+    og = ssd_inputs.output_gradients(cfg, 175)
+    bias = ssd_inputs.dt_bias(cfg["nheads"], 275)
+    g = to_gpu(dict(inp, **og))
+    got = ssd.ssd_backward_dt(g["x"], g["dt"], g["A_log"], g["B"], g["C"], g["dy"], g.get("D"), dt_bias=bias.cuda(),
+                              scale_input=scale, init_state=g.get("init_state"), dfinal=g["dfinal"])
+    torch.cuda.synchronize()
+    want = oracle.discretize.backward_dt(oracle.backward.default_adjoint(), f64(inp["x"]), f64(inp["dt"]),
+                                         f64(inp["A_log"]), f64(inp["B"]), f64(inp["C"]), f64(inp.get("D")),
+                                         dt_bias=f64(bias), scale_input=scale, init_state=f64(inp.get("init_state")),
+                                         dy=f64(og["dy"]), dfinal=f64(og["dfinal"]))
+    tol = TOL[cfg["dtype"]]
+    errs = {k: rel_l2(got[k].double().cpu().numpy(), want[k]) for k in ("dx", "ddt", "dB", "dC", "dD", "dinit")}
+    # dA_log and ddt_bias are sums over every (batch, token) of terms of both signs: their error is
+    # measured against the size of the terms (sum of magnitudes per head), since cancellation in
+    # the sum can leave it far smaller than the rounding its terms carry
+    la = oracle.discretize.discretize(f64(inp["dt"]), f64(inp["A_log"]), f64(bias))[1]
+    mag = dict(ddt_bias=np.abs(want["ddt"]).sum(axis=(0, 1)))
+    # the dA_log terms are dlog_a log a: dlog_a from the adjoint on the same inputs
+    xin = f64(inp["x"]) * oracle.discretize.discretize(f64(inp["dt"]), f64(inp["A_log"]), f64(bias))[0][..., None] \
+        if scale else f64(inp["x"])
+    adj = oracle.backward.backward(xin, la, f64(inp["B"]), f64(inp["C"]), None, f64(inp.get("init_state")),
+                                   f64(og["dy"]), f64(og["dfinal"]))
+    mag["dA_log"] = np.abs(adj["dlog_a"] * la).sum(axis=(0, 1))
+    for k in ("dA_log", "ddt_bias"):
+        diff = got[k].double().cpu().numpy() - want[k]
+        errs[k] = float(np.linalg.norm(diff) / np.linalg.norm(mag[k]))
+    announce("backward_dt %s scale=%d: " % (label, scale) + " ".join("%s %.2e" % kv for kv in errs.items())
+             + " (tol %.0e)" % tol)
+    assert all(e <= tol for e in errs.values()), errs
