@@ -95,11 +95,23 @@ KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.h
                   "bwd_walk_kernel": "ssd_bwd.hip", "zero_kernel": "ssd_bwd.hip", "bwd_reduce_kernel": "ssd_bwd.hip"}
 
 
+def _included_headers(name, seen):
+    """The headers of csrc that source `name` includes, directly or through other headers."""
+    for line in open(os.path.join(CSRC, name)):
+        line = line.strip()
+        if line.startswith("#include \""):
+            inc = line.split("\"")[1]
+            if inc not in seen and os.path.exists(os.path.join(CSRC, inc)):
+                seen.add(inc)
+                _included_headers(inc, seen)
+    return seen
+
+
 def kernel_source_hash(kernel):
-    """Hash of the sources `kernel` is built from (its .hip file and the shared headers):
+    """Hash of the sources `kernel` is built from (its .hip file and the headers it includes):
     counter figures taken on other sources are stale."""
-    names = [KERNEL_SOURCES[kernel.split("<")[0]]] + sorted(
-        n for n in os.listdir(CSRC) if n.endswith(".h"))
+    src = KERNEL_SOURCES[kernel.split("<")[0]]
+    names = [src] + sorted(_included_headers(src, set()))
     h = hashlib.sha256()
     for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
@@ -258,6 +270,19 @@ def time_decode(ssd, cfg, g, stream, ev, dev):
             "effective_gbs": (state_bytes + io_bytes) / (us / 1e6) / 1e9}
 
 
+def calibrate_copy(dev, mib):
+    """A plain streaming kernel of known traffic for the counter calibration: torch's elementwise
+    negation reads and writes `mib` MiB each."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    torch.cuda.synchronize()
+    dst = torch.neg(src)
+    torch.cuda.synchronize()
+    del dst
+    log("calibration: neg kernel reading and writing %d MiB each" % mib)
+
+
 BWD_CHUNK = 32  # tokens per backward chunk (the library's)
 
 
@@ -335,6 +360,8 @@ def run_backward(args, cfg, inp, dev):
         names = ["launch%d" % k for k in range(launches)]
     log("backward ms/step %.4f; per kernel avg ms: %s" % (ms, ", ".join("%s %.4f" % kv for kv in zip(names, kernel_avg))))
     walk = next((k for k, n in enumerate(names) if n.startswith("bwd_walk")), max(range(launches), key=lambda k: kernel_avg[k]))
+    if args.calibrate_copy_mib:
+        calibrate_copy(dev, args.calibrate_copy_mib)
     tokens = cfg["batch"] * cfg["seqlen"]
     achieved = f_walk / (kernel_avg[walk] / 1e3) / 1e12
     result = {
@@ -492,15 +519,7 @@ def main():
         % (ms, timed_ms, ", ".join("%s %.4f" % (n, t) for n, t in zip(names, kernel_avg))))
 
     if args.calibrate_copy_mib:
-        # a plain streaming kernel of known traffic for the counter calibration: torch's
-        # elementwise negation reads and writes calibrate_copy_mib MiB each
-        n = args.calibrate_copy_mib * (1 << 20) // 4
-        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        torch.cuda.synchronize()
-        dst = torch.neg(src)
-        torch.cuda.synchronize()
-        del dst
-        log("calibration: neg kernel reading and writing %d MiB each" % args.calibrate_copy_mib)
+        calibrate_copy(dev, args.calibrate_copy_mib)
 
     tokens = cfg["batch"] * cfg["seqlen"]
     tok_s = tokens / (ms / 1e3)

@@ -4,7 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "ssd_launch.h"
+#include "ssd_bwd_launch.h"
 
 namespace {
 

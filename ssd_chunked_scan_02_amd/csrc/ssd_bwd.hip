@@ -31,7 +31,7 @@
 #include <type_traits>
 
 #include "ssd_common.h"
-#include "ssd_launch.h"
+#include "ssd_bwd_launch.h"
 
 namespace ssd {
 namespace {

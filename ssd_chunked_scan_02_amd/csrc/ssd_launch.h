@@ -106,68 +106,6 @@ struct Walk2Params {
     float* seg_decay;
 };
 
-// The backward pass (ssd_bwd.hip), scalar decay: inputs, the gradients it writes, and its
-// workspace (the state entering every backward chunk, and per-(batch, head) sums for dD).
-struct BwdParams {
-    const void* x;
-    const float* log_a;
-    const void* Bm;
-    const void* Cm;
-    const float* D;
-    const float* init;
-    const void* dy;
-    const float* dfinal;
-    void* dx;
-    float* dlog_a;
-    float* dB;
-    float* dC;
-    float* dD;
-    float* dinit;
-    float* ckpt;
-    float* dD_part;
-    int64_t batch, seqlen, nheads, ngroups;
-    int nchunks;  // backward chunks (backward_chunk() tokens each)
-    int64_t per_xcd;
-};
-struct BackwardLaunch {
-    int dtype;
-    int64_t headdim, dstate;
-    BwdParams p;
-    // optional timing events, as in ForwardLaunch
-    hipEvent_t const* events;
-    int n_events;
-    int* n_launches;
-};
-bool backward_shape_supported(int N, int P);
-size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P);
-int backward_chunk();
-// 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.
-int launch_backward(const BackwardLaunch& bl, hipStream_t stream);
-
-// The discretised form's backward (ssd_backward_dt): its own arguments, and its workspace (log a,
-// the scaled input, dx_in, dlog a, per-row sums, then the backward pass's own workspace).
-struct DtBackwardArgs {
-    const void* x;
-    const float* dt;
-    const float* dt_bias;
-    const float* A_log;
-    int scale_input;
-    const float* D;
-    const void* dy;
-    void* dx;
-    float* ddt;
-    float* dA_log;
-    float* ddt_bias;
-    float* dD;
-    void* workspace;
-};
-struct DtBackwardLayout {
-    size_t la, xs, dxs, dla, ddt_rows, rowA, rowD, inner, total;
-};
-DtBackwardLayout dt_backward_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int elem_bytes,
-                                    bool scale_input);
-int launch_backward_dt(const BackwardLaunch& bl, const DtBackwardArgs& a, hipStream_t stream);
-
 // Everything one forward call needs, already validated.
 struct ForwardLaunch {
     int dtype;  // 0 fp32, 1 bf16
