@@ -92,7 +92,8 @@ KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.h
                   "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
                   "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
                   "skip_kernel": "ssd_kernels.hip", "bwd_states_kernel": "ssd_bwd.hip",
-                  "bwd_walk_kernel": "ssd_bwd.hip", "zero_kernel": "ssd_bwd.hip", "bwd_reduce_kernel": "ssd_bwd.hip"}
+                  "bwd_walk_kernel": "ssd_bwd.hip", "zero_kernel": "ssd_bwd.hip", "bwd_reduce_kernel": "ssd_bwd.hip",
+                  "bwd_states_diag_kernel": "ssd_bwd.hip", "bwd_walk_diag_kernel": "ssd_bwd.hip"}
 
 
 def _included_headers(name, seen):
@@ -295,9 +296,15 @@ def backward_counts(cfg):
     Bsz, T, H, G = cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["ngroups"]
     P, N, Q = cfg["headdim"], cfg["dstate"], BWD_CHUNK
     sx = 4 if cfg["dtype"] == "fp32" else 2
-    f_walk = Bsz * T * (G * N * (Q + 1) + H * ((2 * P + 2 * N) * (Q + 1) + 8 * N * P))
+    diag = cfg["decay"] == "diag"
+    if diag:
+        # per head: the scores with the decay inside (per n), dB, dC and M per (t, s, n)
+        f_walk = Bsz * T * H * ((2 * P + 4 * N) * (Q + 1) + 8 * N * P)
+    else:
+        f_walk = Bsz * T * (G * N * (Q + 1) + H * ((2 * P + 2 * N) * (Q + 1) + 8 * N * P))
     f_states = Bsz * T * H * 2 * N * P
-    nbytes = Bsz * T * (3 * H * P * sx + 2 * G * N * sx + 2 * G * N * 4 + 2 * 4 * H) \
+    K = N if diag else 1
+    nbytes = Bsz * T * (3 * H * P * sx + 2 * G * N * sx + 2 * G * N * 4 + 2 * 4 * H * K) \
         + (2 * 4 * H if cfg["skip"] else 0) + 4 * Bsz * H * N * P * (2 * int(cfg["init"]) + int(cfg["final"]))
     return f_walk, f_states, nbytes
 
@@ -354,7 +361,8 @@ def run_backward(args, cfg, inp, dev):
             ev.destroy(h)
     kernel_avg = [sum(v) / len(v) for v in per_kernel]
     N, P = cfg["dstate"], cfg["headdim"]
-    names = ["zero_kernel", "bwd_states_kernel<%d,%d>" % (N, P), "bwd_walk_kernel<%d,%d>" % (N, P)] + \
+    sfx = "_diag" if cfg["decay"] == "diag" else ""
+    names = ["zero_kernel", "bwd_states%s_kernel<%d,%d>" % (sfx, N, P), "bwd_walk%s_kernel<%d,%d>" % (sfx, N, P)] + \
         (["bwd_reduce_kernel"] if cfg["skip"] else [])
     if len(names) != launches:
         names = ["launch%d" % k for k in range(launches)]
@@ -437,9 +445,6 @@ def main():
     torch.cuda.set_device(dev)
     inp = ssd_inputs.make_inputs(cfg, seed)
     if args.backward:
-        if cfg["decay"] != "scalar":
-            print("the backward pass covers scalar decay only", file=sys.stderr)
-            sys.exit(2)
         return run_backward(args, cfg, inp, dev)
     fe = args.front_end
     flops, nbytes, per_token = algorithmic_counts(cfg, fe)

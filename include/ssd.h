@@ -174,7 +174,7 @@ int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float
                 const void* C_t, const float* D, void* y_t, void* stream);
 
 /*
- * The backward pass of ssd_forward (scalar decay): the gradients of L = <dy, y> + <dfinal,
+ * The backward pass of ssd_forward: the gradients of L = <dy, y> + <dfinal,
  * final_state> with respect to every input, for training.  It is the chain rule through the
  * recurrence above, evaluated chunk by chunk (the state entering every chunk is recomputed into
  * the workspace, then a reverse walk carries dL/dh from chunk to chunk); the pages define the
@@ -185,14 +185,14 @@ int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float
  *   dy            [B,T,H,P] in `dtype`: dL/dy.
  *   dfinal        [B,H,N,P] fp32 dL/dfinal_state, or NULL for zeros.
  *   dx            [B,T,H,P] output in `dtype`.
- *   dlog_a        [B,T,H] fp32 output.
+ *   dlog_a        [B,T,H] (or [B,T,H,N] for diagonal decay) fp32 output.
  *   dB, dC        [B,T,G,N] fp32 outputs (summed over the heads of each group).
  *   dD            [H] fp32 output, or NULL to skip it.
  *   dinit         [B,H,N,P] fp32 output dL/dinit_state, or NULL to skip it.
  *   workspace     device scratch of at least ssd_backward_workspace_bytes(dims) bytes: one fp32
  *                 N x P state per (batch, head, 32 tokens), plus 4 bytes per (batch, head).
- * Supported: SSD_DECAY_SCALAR, N in {16, 32, 64, 128}, P in {16, 32, 64}, fp32 or bf16
- * (else SSD_ERR_UNSUPPORTED).  dB and dC are accumulated with atomic adds, so their last bits
+ * Supported: SSD_DECAY_SCALAR with N in {16, 32, 64, 128}, or SSD_DECAY_DIAG with N in {16, 32,
+ * 64} (dlog_a is then [B,T,H,N]); P in {16, 32, 64}; fp32 or bf16 (else SSD_ERR_UNSUPPORTED).  dB and dC are accumulated with atomic adds, so their last bits
  * may differ from run to run.
  */
 size_t ssd_backward_workspace_bytes(const ssd_dims* dims);
@@ -218,7 +218,7 @@ int ssd_backward_profiled(const ssd_dims* dims, const void* x, const float* log_
  *   ddt [B,T,H] fp32 (required); dA_log [H] and ddt_bias [H] fp32 (NULL to skip each);
  *   dx, dB, dC, dD, dinit as for ssd_backward.
  *   workspace: at least ssd_backward_dt_workspace_bytes(dims, scale_input) bytes.
- * Supported shapes and dtypes as ssd_backward.
+ * Supported shapes and dtypes as ssd_backward, scalar decay only.
  */
 size_t ssd_backward_dt_workspace_bytes(const ssd_dims* dims, int scale_input);
 

@@ -341,21 +341,22 @@ def ssd_backward_profiled(x, log_a, B, C, dy, D=None, init_state=None, dfinal=No
 def ssd_backward(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, want_dD=True,
                  want_dinit=True, workspace=None, stream=None, _events=None):
     """Run ``ssd_backward``: gradients of <dy, y> + <dfinal, final_state> for the forward pass
-    on (x, log_a, B, C, D, init_state), scalar decay.  Returns a dict: dx (dtype of x), dlog_a,
+    on (x, log_a, B, C, D, init_state), scalar or diagonal decay (log_a [B,T,H] or [B,T,H,N]).  Returns a dict: dx (dtype of x), dlog_a,
     dB, dC (fp32), dD (fp32 [H], or None) and dinit (fp32 [B,H,N,P], or None)."""
     dims = dims_for(x, log_a, B)
     dev = x.device
     bsz, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     _check(x, "x", (bsz, T, H, P), x.dtype, dev)
-    _check(log_a, "log_a", (bsz, T, H), torch.float32, dev)
+    la_shape = (bsz, T, H, N) if dims.decay == SSD_DECAY_DIAG else (bsz, T, H)
+    _check(log_a, "log_a", la_shape, torch.float32, dev)
     _check(B, "B", (bsz, T, G, N), x.dtype, dev)
     _check(C, "C", (bsz, T, G, N), x.dtype, dev)
     _check(dy, "dy", (bsz, T, H, P), x.dtype, dev)
     _check(D, "D", (H,), torch.float32, dev)
     _check(init_state, "init_state", (bsz, H, N, P), torch.float32, dev)
     _check(dfinal, "dfinal", (bsz, H, N, P), torch.float32, dev)
-    out = dict(dx=torch.empty_like(x), dlog_a=torch.empty((bsz, T, H), dtype=torch.float32, device=dev),
+    out = dict(dx=torch.empty_like(x), dlog_a=torch.empty(la_shape, dtype=torch.float32, device=dev),
                dB=torch.empty((bsz, T, G, N), dtype=torch.float32, device=dev),
                dC=torch.empty((bsz, T, G, N), dtype=torch.float32, device=dev),
                dD=torch.empty(H, dtype=torch.float32, device=dev) if want_dD else None,

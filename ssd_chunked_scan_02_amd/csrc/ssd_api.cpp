@@ -81,12 +81,12 @@ int check_forward(const ssd_dims* d, int chunk) {
     return SSD_OK;
 }
 
-// Backward pass: scalar decay, N in {16, 32, 64, 128}, P in {16, 32, 64}, either dtype.
+// Backward pass: scalar decay with N in {16, 32, 64, 128}, or diagonal decay with N in {16, 32,
+// 64}; P in {16, 32, 64}; either dtype.
 int check_backward(const ssd_dims* d) {
     int rc = check_dims(d, true);
     if (rc != SSD_OK) return rc;
-    if (d->decay != SSD_DECAY_SCALAR) return SSD_ERR_UNSUPPORTED;
-    if (!ssd::backward_shape_supported((int)d->dstate, (int)d->headdim)) return SSD_ERR_UNSUPPORTED;
+    if (!ssd::backward_shape_supported((int)d->dstate, (int)d->headdim, d->decay)) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -272,6 +272,7 @@ int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, 
     if (d->batch == 0 && !dD) return SSD_OK;
     ssd::BackwardLaunch bl{};
     bl.dtype = d->dtype;
+    bl.decay = d->decay;
     bl.headdim = d->headdim;
     bl.dstate = d->dstate;
     ssd::BwdParams& p = bl.p;
@@ -309,7 +310,7 @@ int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, 
 }
 
 size_t ssd_backward_dt_workspace_bytes(const ssd_dims* d, int scale_input) {
-    if (check_backward(d) != SSD_OK || d->batch == 0) return 0;
+    if (check_backward(d) != SSD_OK || d->decay != SSD_DECAY_SCALAR || d->batch == 0) return 0;
     return ssd::dt_backward_layout(d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim,
                                    d->dtype == SSD_BF16 ? 2 : 4, scale_input != 0)
         .total;
@@ -322,6 +323,7 @@ int ssd_backward_dt(const ssd_dims* d, const void* x, const float* dt, const flo
                     void* stream) {
     int rc = check_backward(d);
     if (rc != SSD_OK) return rc;
+    if (d->decay != SSD_DECAY_SCALAR) return SSD_ERR_UNSUPPORTED;
     const bool has_tokens = d->batch > 0 && d->seqlen > 0;
     if (has_tokens && (!x || !dt || !A_log || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_INVALID;
     if (!A_log && (dA_log || ddt_bias)) return SSD_ERR_INVALID;

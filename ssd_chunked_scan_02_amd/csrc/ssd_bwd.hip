@@ -475,6 +475,395 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Diagonal decay (one log a per state dimension n).  The same chain rule, with per-(t, n) running
+// sums cum_tn, e_tn = exp(cum_tn), w_sn = exp(cum_last,n - cum_sn), L_tsn = exp(cum_tn - cum_sn):
+//   A_ts    = sum_n C_tn B_sn L_tsn                      (the scores, decay inside the sum)
+//   dx_s    = sum_t A_ts dy_t + sum_n w_sn B_sn G_n + D dy_s
+//   dB_sn  += sum_t L_tsn DYX_ts C_tn + w_sn (G x_s)_n
+//   dC_tn  += sum_s L_tsn DYX_ts B_sn + e_tn (H dy_t)_n
+//   dcum_tn = sum_s M_tsn - sum_t' M_t'tn + e_tn C_tn (H dy_t)_n - w_tn B_tn (G x_t)_n
+//             + [t = last] (e_last,n <G_n, H_n> + sum_s w_sn B_sn (G x_s)_n),  M_tsn = C_tn B_sn L_tsn DYX_ts
+//   G_n    <- e_last,n G_n + sum_t e_tn C_tn dy_t^T
+// Over a chunk of fast-decaying dimensions exp(cum_tn - cum_sn) spans more than fp32 can hold in any
+// pair of factors, so the intra-chunk sums run on the vector units with an exact exp per (t, s, n);
+// the carried-state terms stay on the matrix cores with the per-(t, n) factor folded into an operand.
+template <int N, int P, typename CT>
+struct BwdDiagShape {
+    // NC: row stride of the [Q][N] arrays (padded so that rows fall on different LDS banks)
+    static constexpr int Q = kBQ, QS = Q + 1, NS = N + 1, PS = P + 1, NC = N + 1;
+    static constexpr int NB = N / 16, PB = P / 16, QB = Q / 16;
+    static constexpr int NTILE = NB * PB, TPW = (NTILE + kBWaves - 1) / kBWaves;
+    // walk LDS: cum [Q][NC] of CT; then floats: X, dY [Q][PS]; B, C [Q][NS]; e, w [Q][NC]; A, DYX
+    // [Q][QS]; intra dB, intra dC, dcum [Q][NC]; H, G [N][PS]; e_last, <G_n, H_n> [N]; partial
+    // last-token sums [QB][N]
+    static constexpr size_t walk_floats = (size_t)2 * Q * PS + 2 * Q * NS + 2 * Q * NC + 2 * Q * QS + 3 * Q * NC +
+                                          2 * N * PS + 2 * N + QB * N;
+    static constexpr size_t walk_lds = ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16 + walk_floats * 4;
+    // states LDS: cum [Q][NC] of CT; floats: w o B [Q][NS], X [Q][PS], log a then w [Q][NC], e_last [N]
+    static constexpr size_t states_lds =
+        ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16 + ((size_t)Q * NS + Q * PS + Q * NC + N) * 4;
+};
+
+// The diagonal path's running sums: fp64 natural-log units with the library exp for fp32 inputs;
+// log2 units with the hardware exp2 (v_exp_f32) for bf16 inputs, one instruction per factor.
+template <typename CT> struct DiagExp;
+template <> struct DiagExp<double> {
+    static constexpr double kScale = 1.0;
+    __device__ static double ex(double v) { return exp(v); }
+};
+template <> struct DiagExp<float> {
+    static constexpr float kScale = 1.4426950408889634f;
+    __device__ static float ex(float v) { return __builtin_amdgcn_exp2f(v); }
+};
+
+// Per-dimension running sums of one chunk's log a (la [Q][N], 0 past the end), by threads n < N:
+// cum, e (when e is not null), w (may be la itself: each thread overwrites only its own column
+// after reading it) and e_last.
+template <int N, typename CT>
+__device__ __forceinline__ void diag_chunk_factors(const float* la, CT* cum, float* e, float* w, float* el, int tid) {
+    constexpr int NC = N + 1;  // (row stride of every [Q][N] array)
+    if (tid < N) {
+        const int n = tid;
+        CT run = 0;
+        for (int t = 0; t < kBQ; ++t) {
+            run += (CT)la[t * NC + n] * DiagExp<CT>::kScale;
+            cum[t * NC + n] = run;
+        }
+        for (int t = 0; t < kBQ; ++t) {
+            if (e) e[t * NC + n] = (float)DiagExp<CT>::ex(cum[t * NC + n]);
+            w[t * NC + n] = (float)DiagExp<CT>::ex(run - cum[t * NC + n]);
+        }
+        el[n] = (float)DiagExp<CT>::ex(run);
+    }
+}
+
+template <typename T, int N, int P>
+__global__ void __launch_bounds__(kBThreads) bwd_states_diag_kernel(BwdParams prm) {
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    using S = BwdDiagShape<N, P, CT>;
+    constexpr int Q = S::Q, NS = S::NS, PS = S::PS, PB = S::PB, NTILE = S::NTILE, TPW = S::TPW, NC = S::NC;
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    CT* cum = reinterpret_cast<CT*>(smem);                                             // [Q][NC]
+    float* Bw = reinterpret_cast<float*>(smem + ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16);  // w o B [Q][NS]
+    float* Xs = Bw + Q * NS;                                                           // [Q][PS]
+    float* Ls = Xs + Q * PS;                                                           // log a, then w [Q][NC]
+    float* el = Ls + Q * NC;                                                           // [N]
+    const T* xg = static_cast<const T*>(prm.x);
+    const T* Bg = static_cast<const T*>(prm.Bm);
+
+    f32x4 hs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kBWaves * j;
+        if (tile < NTILE && prm.init) {
+            const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hs[j][i] = prm.init[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16];
+        }
+    }
+    ChunkRows<T, Q, N> rb;
+    ChunkRows<T, Q, P> rx;
+    ChunkRows<float, Q, N> rl;
+    auto load = [&](int c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
+        rl.load(prm.log_a + ((b * Tn + t0) * H + h) * N, H * N, len, tid);
+    };
+    if (prm.nchunks > 0) load(0);
+    for (int c = 0; c < prm.nchunks; ++c) {
+        float* ck = prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ck[(16 * nb + 4 * lg + i) * P + 16 * pb + l16] = hs[j][i];
+            }
+        }
+        rb.stage(Bw, NS, tid);
+        rx.stage(Xs, PS, tid);
+        rl.stage(Ls, NC, tid);
+        __syncthreads();
+        diag_chunk_factors<N, CT>(Ls, cum, nullptr, Ls, el, tid);
+        __syncthreads();
+        for (int i = tid; i < Q * N; i += kBThreads) Bw[(i / N) * NS + i % N] *= Ls[(i / N) * NC + i % N];
+        __syncthreads();
+        if (c + 1 < prm.nchunks) load(c + 1);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                f32x4 acc = hs[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] *= el[16 * nb + 4 * lg + i];
+                hs[j] = tile_mma(acc, Bw + 16 * nb, 1, NS, Xs + 16 * pb, PS, 1, Q, lane);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T, int N, int P>
+__global__ void __launch_bounds__(kBThreads) bwd_walk_diag_kernel(BwdParams prm) {
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    using S = BwdDiagShape<N, P, CT>;
+    constexpr int Q = S::Q, QS = S::QS, NS = S::NS, PS = S::PS, NB = S::NB, PB = S::PB, QB = S::QB, NC = S::NC;
+    constexpr int NTILE = S::NTILE, TPW = S::TPW;
+    static_assert(QB * QB <= kBWaves / 2, "DYX tiles on the first half of the waves");
+    static_assert(N >= kBWaves, "the final reduction borrows kBWaves floats of <G_n, H_n>");
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    CT* cum = reinterpret_cast<CT*>(smem);               // [Q][NC]
+    float* Xs = reinterpret_cast<float*>(smem + ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16);  // [Q][PS]
+    float* Ys = Xs + Q * PS;                             // dy [Q][PS]
+    float* Bs = Ys + Q * PS;                             // [Q][NS]
+    float* Cs = Bs + Q * NS;                             // [Q][NS]
+    float* Ev = Cs + Q * NS;                             // e [Q][NC]
+    float* Wv = Ev + Q * NC;                             // w [Q][NC]
+    float* Am = Wv + Q * NC;                             // A [Q][QS] (rows t, columns s)
+    float* Dm = Am + Q * QS;                             // DYX [Q][QS]
+    float* dBi = Dm + Q * QS;                            // intra-chunk dB [Q][NC]
+    float* dCi = dBi + Q * NC;                           // intra-chunk dC [Q][NC]
+    float* dcum = dCi + Q * NC;                          // [Q][NC] (first the chunk's log a)
+    float* Hs = dcum + Q * NC;                           // H [N][PS]
+    float* Gs = Hs + N * PS;                             // G [N][PS]
+    float* el = Gs + N * PS;                             // e_last [N]
+    float* ghn = el + N;                                 // <G_n, H_n> [N]
+    float* partL = ghn + N;                              // [QB][N]: sum_s w_sn B_sn (G x_s)_n per 16-row block
+
+    const T* xg = static_cast<const T*>(prm.x);
+    const T* yg = static_cast<const T*>(prm.dy);
+    const T* Bg = static_cast<const T*>(prm.Bm);
+    const T* Cg = static_cast<const T*>(prm.Cm);
+    T* dxg = static_cast<T*>(prm.dx);
+    const float dskip = prm.D ? prm.D[h] : 0.f;
+
+    f32x4 gs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        gs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kBWaves * j;
+        if (tile < NTILE && prm.dfinal) {
+            const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gs[j][i] = prm.dfinal[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16];
+        }
+    }
+    auto write_g = [&]() {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Gs[(16 * nb + 4 * lg + i) * PS + 16 * pb + l16] = gs[j][i];
+            }
+        }
+    };
+    write_g();
+    float dD_acc = 0.f;
+
+    ChunkRows<T, Q, P> rx, ry;
+    ChunkRows<T, Q, N> rb, rc;
+    ChunkRows<float, N, P> rh;
+    ChunkRows<float, Q, N> rl;
+    auto load = [&](int c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
+        ry.load(yg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
+        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rc.load(Cg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rh.load(prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P, P, N, tid);
+        rl.load(prm.log_a + ((b * Tn + t0) * H + h) * N, H * N, len, tid);
+    };
+    if (prm.nchunks > 0) load(prm.nchunks - 1);
+
+    for (int c = prm.nchunks - 1; c >= 0; --c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+        // ---- 1. the chunk into LDS; per-dimension running sums
+        rx.stage(Xs, PS, tid);
+        ry.stage(Ys, PS, tid);
+        rb.stage(Bs, NS, tid);
+        rc.stage(Cs, NS, tid);
+        rh.stage(Hs, PS, tid);
+        rl.stage(dcum, NC, tid);
+#pragma unroll
+        for (int i = 0; i < ChunkRows<T, Q, P>::PT; ++i)
+#pragma unroll
+            for (int j = 0; j < ChunkRows<T, Q, P>::VE; ++j) dD_acc += rx.elem(i, j) * ry.elem(i, j);
+        __syncthreads();
+        diag_chunk_factors<N, CT>(dcum, cum, Ev, Wv, el, tid);
+        __syncthreads();
+        if (c > 0) load(c - 1);
+
+        // ---- 2. DYX on the matrix cores (the first waves, first); A_ts = sum_n C_tn B_sn L_tsn on
+        //         the vector units (every thread; the sum over n unrolled by 4 with independent
+        //         partial sums, so the LDS reads of one step overlap the arithmetic of the last)
+        if (wave < QB * QB) {
+            const int tb = wave / QB, sb = wave % QB;
+            const f32x4 v = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Xs + 16 * sb * PS, 1, PS, P,
+                                     lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Dm[(16 * tb + 4 * lg + i) * QS + 16 * sb + l16] = v[i];
+        }
+        for (int idx = tid; idx < Q * Q; idx += kBThreads) {
+            const int t = idx / Q, s = idx % Q;
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
+            if (s <= t) {
+#pragma unroll 4
+                for (int n = 0; n < N; n += 4)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        a[u] += Cs[t * NS + n + u] * Bs[s * NS + n + u] *
+                                (float)DiagExp<CT>::ex(cum[t * NC + n + u] - cum[s * NC + n + u]);
+            }
+            Am[t * QS + s] = (a[0] + a[1]) + (a[2] + a[3]);
+        }
+        __syncthreads();
+
+        // ---- 3a. intra-chunk dB, dC and dcum = (row sums - column sums of M), per (q, n)
+        // (fixed-length loops over the chunk, masked: fully unrolled, their loads run ahead)
+        for (int idx = tid; idx < Q * N; idx += kBThreads) {
+            const int q = idx / N, n = idx % N;
+            const CT cq = cum[q * NC + n];
+            float db = 0.f, dc = 0.f;
+#pragma unroll
+            for (int u = 0; u < Q; ++u) {
+                // u in the role of t (q as s), then of s (q as t)
+                const float vb = u >= q ? Dm[u * QS + q] * (float)DiagExp<CT>::ex(cum[u * NC + n] - cq) * Cs[u * NS + n] : 0.f;
+                const float vc = u <= q ? Dm[q * QS + u] * (float)DiagExp<CT>::ex(cq - cum[u * NC + n]) * Bs[u * NS + n] : 0.f;
+                db += vb;
+                dc += vc;
+            }
+            dBi[q * NC + n] = db;
+            dCi[q * NC + n] = dc;
+            // row sum of M at t = q minus its column sum at s = q: C_qn dC_intra - B_qn dB_intra
+            dcum[q * NC + n] = Cs[q * NS + n] * dc - Bs[q * NS + n] * db;
+        }
+        __syncthreads();
+
+        // ---- 3b. the carried-state terms (matrix cores): dx, dB, dC out; dcum's state terms
+        for (int tile = wave; tile < QB * PB; tile += kBWaves) {
+            const int sb = tile / PB, pb = tile % PB;
+            f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
+            // sum_n w_sn B_sn G_np: A(s, n) = Wv[s][n] Bs[s][n]
+            const int r = lane % 16, gq = lane / 16;
+#pragma unroll 4
+            for (int k = 0; k < N; k += 4) {
+                const int s = 16 * sb + r, n = k + gq;
+                acc = mfma_f32(Wv[s * NC + n] * Bs[s * NS + n], Gs[n * PS + 16 * pb + r], acc);
+            }
+            const int p = 16 * pb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * sb + 4 * lg + i;
+                if (s < len) dxg[((b * Tn + t0 + s) * H + h) * P + p] = from_f32<T>(acc[i] + dskip * Ys[s * PS + p]);
+            }
+        }
+        for (int tile = wave; tile < QB * NB; tile += kBWaves) {
+            const int qb = tile / NB, nb = tile % NB;
+            const f32x4 gx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Xs + 16 * qb * PS, PS, 1, Gs + 16 * nb * PS, 1, PS, P,
+                                      lane);
+            const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * qb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS, P,
+                                      lane);
+            const int n = 16 * nb + l16;
+            float lastp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = 16 * qb + 4 * lg + i;
+                const float wb = Wv[q * NC + n] * Bs[q * NS + n] * gx[i];
+                const float ec = Ev[q * NC + n] * Cs[q * NS + n] * hd[i];
+                if (q < len) {
+                    atomicAdd(prm.dB + ((b * Tn + t0 + q) * G + g) * N + n, dBi[q * NC + n] + Wv[q * NC + n] * gx[i]);
+                    atomicAdd(prm.dC + ((b * Tn + t0 + q) * G + g) * N + n, dCi[q * NC + n] + Ev[q * NC + n] * hd[i]);
+                }
+                dcum[q * NC + n] += ec - wb;
+                lastp += wb;
+            }
+            lastp += __shfl_xor(lastp, 16, kWave);
+            lastp += __shfl_xor(lastp, 32, kWave);
+            if (lg == 0) partL[qb * N + n] = lastp;
+        }
+        if (tid < N) {
+            float acc = 0.f;
+            for (int p = 0; p < P; ++p) acc += Gs[tid * PS + p] * Hs[tid * PS + p];
+            ghn[tid] = acc;
+        }
+        __syncthreads();
+
+        // ---- 4. dlog a per dimension (reverse running sum, the last token's term first); G
+        if (tid < N) {
+            const int n = tid;
+            float last = el[n] * ghn[n];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) last += partL[qb * N + n];
+            float r = last;
+            for (int t = Q - 1; t >= 0; --t) {
+                r += dcum[t * NC + n];
+                if (t < len) prm.dlog_a[((b * Tn + t0 + t) * H + h) * N + n] = r;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+                f32x4 acc = gs[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] *= el[16 * nb + 4 * lg + i];
+                const int r = lane % 16, gq = lane / 16;
+#pragma unroll 4
+                for (int k = 0; k < Q; k += 4) {
+                    const int t = k + gq, n = 16 * nb + r;
+                    acc = mfma_f32(Ev[t * NC + n] * Cs[t * NS + n], Ys[t * PS + 16 * pb + r], acc);
+                }
+                gs[j] = acc;
+            }
+        }
+        __syncthreads();
+        write_g();
+    }
+    __syncthreads();
+    if (prm.dinit) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int nb = tile / PB, pb = tile % PB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) prm.dinit[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16] = gs[j][i];
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dD_acc += __shfl_xor(dD_acc, off, kWave);
+    if (lane == 0) ghn[wave] = dD_acc;
+    __syncthreads();
+    if (tid == 0) {
+        float s2 = 0.f;
+        for (int k = 0; k < kBWaves; ++k) s2 += ghn[k];
+        prm.dD_part[unit] = s2;
+    }
+}
+
 // dD[h] = sum over the batch of the walk's per-(batch, head) sums; dB, dC zeroed by zero_kernel.
 __global__ void __launch_bounds__(kThreads) bwd_reduce_kernel(const float* part, float* dD, int64_t batch, int64_t H) {
     const int64_t h = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -596,14 +985,57 @@ __global__ void __launch_bounds__(kThreads) head_sum_kernel(const float* v, floa
     if (threadIdx.x == 0) out[h] = red[0];
 }
 
+template <typename T, int N, int P>
+int launch_backward_diag_t(const BackwardLaunch& bl, hipStream_t stream) {
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    using S = BwdDiagShape<N, P, CT>;
+    static_assert(S::walk_lds <= kMaxLds, "diagonal backward walk LDS budget");
+    static bool attr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    if (!attr[dev]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_walk_diag_kernel<T, N, P>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::walk_lds) != hipSuccess)
+            return -1;
+        attr[dev] = true;
+    }
+    const int64_t units = bl.p.batch * bl.p.nheads;
+    BwdParams p = bl.p;
+    p.per_xcd = (units + 7) / 8;
+    const int64_t nbc = bl.p.batch * bl.p.seqlen * bl.p.ngroups * N;
+    int k = 0;
+    if (nbc > 0 &&
+        !launch_k(bl, k, zero_kernel, dim3((unsigned)std::min<int64_t>((nbc + kThreads - 1) / kThreads, 4096)),
+                  dim3(kThreads), 0, stream, p.dB, nbc, p.dC, nbc))
+        return -1;
+    if (units > 0) {
+        if (!launch_k(bl, k, bwd_states_diag_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
+                      S::states_lds, stream, p))
+            return -1;
+        if (!launch_k(bl, k, bwd_walk_diag_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
+                      S::walk_lds, stream, p))
+            return -1;
+    }
+    if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)((bl.p.nheads + kThreads - 1) / kThreads)),
+                          dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads))
+        return -1;
+    return 0;
+}
+
+#define SSD_BWD_DIAG_SHAPES(X) X(16, 16) X(16, 32) X(16, 64) X(32, 16) X(32, 32) X(32, 64) X(64, 16) X(64, 32) X(64, 64)
+
 #define SSD_BWD_SHAPES(X) \
     X(16, 16) X(16, 32) X(16, 64) X(32, 16) X(32, 32) X(32, 64) X(64, 16) X(64, 32) X(64, 64) X(128, 16) X(128, 32) X(128, 64)
 
 }  // namespace
 
-bool backward_shape_supported(int N, int P) {
+bool backward_shape_supported(int N, int P, int decay) {
 #define SSD_BWD_MATCH(NN, PP) \
     if (N == NN && P == PP) return true;
+    if (decay == 1) {
+        SSD_BWD_DIAG_SHAPES(SSD_BWD_MATCH)
+        return false;
+    }
     SSD_BWD_SHAPES(SSD_BWD_MATCH)
 #undef SSD_BWD_MATCH
     return false;
@@ -617,6 +1049,15 @@ size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, i
 
 int launch_backward(const BackwardLaunch& bl, hipStream_t stream) {
     const int N = (int)bl.dstate, P = (int)bl.headdim;
+    if (bl.decay == 1) {
+#define SSD_BWD_DLAUNCH(NN, PP)                                                           \
+    if (N == NN && P == PP)                                                               \
+        return bl.dtype == 0 ? launch_backward_diag_t<float, NN, PP>(bl, stream)          \
+                             : launch_backward_diag_t<__bf16, NN, PP>(bl, stream);
+        SSD_BWD_DIAG_SHAPES(SSD_BWD_DLAUNCH)
+#undef SSD_BWD_DLAUNCH
+        return -2;
+    }
 #define SSD_BWD_LAUNCH(NN, PP)                                                             \
     if (N == NN && P == PP)                                                                \
         return bl.dtype == 0 ? launch_backward_t<float, NN, PP>(bl, stream)              \

@@ -6,7 +6,7 @@
 
 namespace ssd {
 
-// The backward pass (ssd_bwd.hip), scalar decay: inputs, the gradients it writes, and its
+// The backward pass (ssd_bwd.hip), scalar or diagonal decay: inputs, the gradients it writes, and its
 // workspace (the state entering every backward chunk, and per-(batch, head) sums for dD).
 struct BwdParams {
     const void* x;
@@ -31,6 +31,7 @@ struct BwdParams {
 };
 struct BackwardLaunch {
     int dtype;
+    int decay;  // 0 scalar, 1 diagonal
     int64_t headdim, dstate;
     BwdParams p;
     // optional timing events, as in ForwardLaunch
@@ -38,7 +39,7 @@ struct BackwardLaunch {
     int n_events;
     int* n_launches;
 };
-bool backward_shape_supported(int N, int P);
+bool backward_shape_supported(int N, int P, int decay);
 size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P);
 int backward_chunk();
 // 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.

@@ -268,7 +268,9 @@ def test_backward_workspace_bytes(lib):
     d = mamba2_dims(batch=2, seqlen=300, nheads=4)
     assert ssd.ssd_backward_workspace_bytes(d) == up(2 * 4 * 10 * 128 * 64 * 4) + up(2 * 4 * 4)
     assert ssd.ssd_backward_workspace_bytes(mamba2_dims(batch=0)) == 0
-    assert ssd.ssd_backward_workspace_bytes(mamba2_dims(decay=1)) == 0          # scalar decay only
+    assert ssd.ssd_backward_workspace_bytes(mamba2_dims(decay=1)) == 0          # diagonal decay: N <= 64
+    dd = mamba2_dims(decay=1, dstate=64, batch=1, seqlen=100, nheads=2)
+    assert ssd.ssd_backward_workspace_bytes(dd) == up(1 * 2 * 4 * 64 * 64 * 4) + up(1 * 2 * 4)
     assert ssd.ssd_backward_workspace_bytes(mamba2_dims(headdim=128)) == 0      # P <= 64
 
 

@@ -27,6 +27,12 @@ CASES = [
     ("gqa_decode", dict(batch=2, seqlen=1500, nheads=16, ngroups=2, decode_steps=0, init=True), "bf16-long-gqa"),
     ("tiny_fp32", dict(batch=2, seqlen=1100, nheads=2, dstate=128, headdim=64, init=True, skip=True,
                        a_log="uniform16", dt_mean=-2.0), "fp32-long"),
+    # diagonal decay: per-(head, dim) rates, fast and slow dimensions in one head
+    ("diag_multiscale", dict(batch=2, seqlen=300, nheads=3, a_log="rand_hn", init=True), "diag-bf16"),
+    ("diag_multiscale", dict(batch=1, seqlen=500, nheads=2, dstate=32, headdim=32, init=True), "diag-bf16-32"),
+    ("diag_multiscale", dict(batch=2, seqlen=170, nheads=2, ngroups=2, dstate=16, headdim=16, dtype="fp32",
+                             a_log="rand_hn", init=True), "diag-fp32"),
+    ("diag_multiscale", dict(batch=1, seqlen=130, nheads=2, dtype="fp32", init=True), "diag-fp32-64"),
 ]
 
 
