@@ -93,7 +93,8 @@ KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.h
                   "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
                   "skip_kernel": "ssd_kernels.hip", "bwd_states_kernel": "ssd_bwd.hip",
                   "bwd_walk_kernel": "ssd_bwd.hip", "zero_kernel": "ssd_bwd.hip", "bwd_reduce_kernel": "ssd_bwd.hip",
-                  "bwd_states_diag_kernel": "ssd_bwd.hip", "bwd_walk_diag_kernel": "ssd_bwd.hip"}
+                  "bwd_local_diag_kernel": "ssd_bwd.hip", "bwd_scan_diag_kernel": "ssd_bwd.hip",
+                  "bwd_terms_diag_kernel": "ssd_bwd.hip"}
 
 
 def _included_headers(name, seen):
@@ -362,8 +363,12 @@ def run_backward(args, cfg, inp, dev):
     kernel_avg = [sum(v) / len(v) for v in per_kernel]
     N, P = cfg["dstate"], cfg["headdim"]
     sfx = "_diag" if cfg["decay"] == "diag" else ""
-    names = ["zero_kernel", "bwd_states%s_kernel<%d,%d>" % (sfx, N, P), "bwd_walk%s_kernel<%d,%d>" % (sfx, N, P)] + \
-        (["bwd_reduce_kernel"] if cfg["skip"] else [])
+    if sfx:
+        names = ["bwd_local_diag_kernel<%d,%d>" % (N, P), "bwd_scan_diag_kernel<%d,%d>" % (N, P),
+                 "bwd_terms_diag_kernel<%d,%d>" % (N, P)]
+    else:
+        names = ["zero_kernel", "bwd_states_kernel<%d,%d>" % (N, P), "bwd_walk_kernel<%d,%d>" % (N, P)]
+    names += ["bwd_reduce_kernel"] if cfg["skip"] else []
     if len(names) != launches:
         names = ["launch%d" % k for k in range(launches)]
     log("backward ms/step %.4f; per kernel avg ms: %s" % (ms, ", ".join("%s %.4f" % kv for kv in zip(names, kernel_avg))))

@@ -243,7 +243,7 @@ int ssd_step_dt(const ssd_dims* d, float* state, const void* x_t, const float* d
 
 size_t ssd_backward_workspace_bytes(const ssd_dims* d) {
     if (check_backward(d) != SSD_OK || d->batch == 0) return 0;
-    return ssd::backward_workspace_bytes(d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim);
+    return ssd::backward_workspace_bytes(d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim, d->decay);
 }
 
 int ssd_backward(const ssd_dims* d, const void* x, const float* log_a, const void* B, const void* C,
@@ -295,10 +295,7 @@ int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, 
     p.nheads = d->nheads;
     p.ngroups = d->ngroups;
     p.nchunks = (int)((d->seqlen + ssd::backward_chunk() - 1) / ssd::backward_chunk());
-    char* ws = static_cast<char*>(workspace);
-    const size_t ck = (size_t)(d->batch * d->nheads * p.nchunks) * (size_t)(d->dstate * d->headdim) * 4;
-    p.ckpt = reinterpret_cast<float*>(ws);
-    p.dD_part = ws ? reinterpret_cast<float*>(ws + (ck + 255) / 256 * 256) : nullptr;
+    ssd::bind_backward_workspace(p, workspace, (int)d->dstate, (int)d->headdim, d->decay);
     int count = 0;
     bl.events = reinterpret_cast<hipEvent_t const*>(events);
     bl.n_events = events ? n_events : 0;

@@ -186,14 +186,14 @@ __global__ void __launch_bounds__(kBThreads) bwd_states_kernel(BwdParams prm) {
             }
         }
         chunk_factors<CT>(rla, cum, e_unused, w_s, tid);
-        __syncthreads();
+        lds_barrier();
         rb.stage(Bw, NS, tid);
         rx.stage(Xs, PS, tid);
-        __syncthreads();
+        lds_barrier();
         // w o B in place (rows past the end are zero already)
         for (int i = tid; i < Q * N; i += kBThreads) Bw[(i / N) * NS + i % N] *= w_s[i / N];
         const float el = (float)exp(cum[Q - 1]);
-        __syncthreads();
+        lds_barrier();
         if (c + 1 < prm.nchunks) load(c + 1);
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_states_kernel(BwdParams prm) {
                 hs[j] = tile_mma(hs[j] * el, Bw + 16 * nb, 1, NS, Xs + 16 * pb, PS, 1, Q, lane);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < ChunkRows<T, Q, P>::VE; ++j) dD_acc += rx.elem(i, j) * ry.elem(i, j);
         chunk_factors<CT>(rla, cum, ev, wv, tid);
-        __syncthreads();
+        lds_barrier();
         if (c > 0) load(c - 1);
 
         // ---- 2. S o L (waves 0 .. 3) and DYX, L o DYX (waves 4 .. 7), one 16 x 16 tile (tb, sb) each:
@@ -331,7 +331,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 3. row and column sums of M = (S o L) o DYX (16 threads per row or column); dx,
         //         dB, dC and the state terms of dcum, tiles dealt to the waves
@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off, kWave);
         if (lane == 0) red[wave] = gh;
-        __syncthreads();
+        lds_barrier();
 
         // ---- 4. dcum and dlog a as its reverse running sum (wave 0); the gradient entering the
         //         chunk, G <- e_last G + sum_t e_t C_t dy_t^T (every wave)
@@ -448,10 +448,10 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
                 gs[j] = acc;
             }
         }
-        __syncthreads();  // every read of Gs, Hs and the chunk tiles above is done
+        lds_barrier();  // every read of Gs, Hs and the chunk tiles above is done
         write_g();
     }
-    __syncthreads();
+    lds_barrier();
     if (prm.dinit) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
@@ -467,7 +467,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dD_acc += __shfl_xor(dD_acc, off, kWave);
     if (lane == 0) red[wave] = dD_acc;
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         float s = 0.f;
         for (int k = 0; k < kBWaves; ++k) s += red[k];
@@ -484,7 +484,12 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
 //   dC_tn  += sum_s L_tsn DYX_ts B_sn + e_tn (H dy_t)_n
 //   dcum_tn = sum_s M_tsn - sum_t' M_t'tn + e_tn C_tn (H dy_t)_n - w_tn B_tn (G x_t)_n
 //             + [t = last] (e_last,n <G_n, H_n> + sum_s w_sn B_sn (G x_s)_n),  M_tsn = C_tn B_sn L_tsn DYX_ts
-//   G_n    <- e_last,n G_n + sum_t e_tn C_tn dy_t^T
+// with H the state entering the chunk and G the gradient of the state at its end.  Both are chains
+// over the chunks, H_{c+1} = e_last,n H_c + sum_s w_sn B_sn x_s^T and G_{c-1} = e_last,n G_c +
+// sum_t e_tn C_tn dy_t^T, of the same associative form as the forward's state passing.  So the pass
+// runs every chunk at once: a local kernel per (unit, chunk) forms the intra-chunk terms and the
+// two local sums; a scan per state element chains the sums into H and G in place; a second kernel
+// per (unit, chunk) adds the terms that need H and G.
 // Over a chunk of fast-decaying dimensions exp(cum_tn - cum_sn) spans more than fp32 can hold in any
 // pair of factors, so the intra-chunk sums run on the vector units with an exact exp per (t, s, n);
 // the carried-state terms stay on the matrix cores with the per-(t, n) factor folded into an operand.
@@ -493,16 +498,15 @@ struct BwdDiagShape {
     // NC: row stride of the [Q][N] arrays (padded so that rows fall on different LDS banks)
     static constexpr int Q = kBQ, QS = Q + 1, NS = N + 1, PS = P + 1, NC = N + 1;
     static constexpr int NB = N / 16, PB = P / 16, QB = Q / 16;
-    static constexpr int NTILE = NB * PB, TPW = (NTILE + kBWaves - 1) / kBWaves;
-    // walk LDS: cum [Q][NC] of CT; then floats: X, dY [Q][PS]; B, C [Q][NS]; e, w [Q][NC]; A, DYX
-    // [Q][QS]; intra dB, intra dC, dcum [Q][NC]; H, G [N][PS]; e_last, <G_n, H_n> [N]; partial
-    // last-token sums [QB][N]
-    static constexpr size_t walk_floats = (size_t)2 * Q * PS + 2 * Q * NS + 2 * Q * NC + 2 * Q * QS + 3 * Q * NC +
-                                          2 * N * PS + 2 * N + QB * N;
-    static constexpr size_t walk_lds = ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16 + walk_floats * 4;
-    // states LDS: cum [Q][NC] of CT; floats: w o B [Q][NS], X [Q][PS], log a then w [Q][NC], e_last [N]
-    static constexpr size_t states_lds =
-        ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16 + ((size_t)Q * NS + Q * PS + Q * NC + N) * 4;
+    static constexpr size_t cum_bytes = ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16;
+    // local LDS: cum [Q][NC] of CT; floats: X, dY [Q][PS]; B, C [Q][NS]; A, DYX [Q][QS]; w, e
+    // [Q][NC]; e_last [N]; partial sums [kWaves]
+    static constexpr size_t local_lds =
+        cum_bytes + ((size_t)2 * Q * PS + 2 * Q * NS + 2 * Q * QS + 2 * Q * NC + N + kWaves) * 4;
+    // state-terms LDS: cum [Q][NC] of CT; floats: X, dY [Q][PS]; B, C [Q][NS]; e, w, dcum [Q][NC];
+    // H, G [N][PS]; e_last, <G_n, H_n> [N]; partial last-token sums [QB][N]
+    static constexpr size_t terms_lds =
+        cum_bytes + ((size_t)2 * Q * PS + 2 * Q * NS + 3 * Q * NC + 2 * N * PS + 2 * N + QB * N) * 4;
 };
 
 // The diagonal path's running sums: fp64 natural-log units with the library exp for fp32 inputs;
@@ -518,358 +522,375 @@ template <> struct DiagExp<float> {
 };
 
 // Per-dimension running sums of one chunk's log a (la [Q][N], 0 past the end), by threads n < N:
-// cum, e (when e is not null), w (may be la itself: each thread overwrites only its own column
-// after reading it) and e_last.
+// cum, e, w (may be la itself: each thread overwrites only its own column, after reading all of it)
+// and e_last.  The column is read into registers first, so the LDS loads run back to back.
 template <int N, typename CT>
 __device__ __forceinline__ void diag_chunk_factors(const float* la, CT* cum, float* e, float* w, float* el, int tid) {
     constexpr int NC = N + 1;  // (row stride of every [Q][N] array)
     if (tid < N) {
         const int n = tid;
+        CT c[kBQ];
         CT run = 0;
+#pragma unroll
         for (int t = 0; t < kBQ; ++t) {
             run += (CT)la[t * NC + n] * DiagExp<CT>::kScale;
-            cum[t * NC + n] = run;
+            c[t] = run;
         }
+#pragma unroll
         for (int t = 0; t < kBQ; ++t) {
-            if (e) e[t * NC + n] = (float)DiagExp<CT>::ex(cum[t * NC + n]);
-            w[t * NC + n] = (float)DiagExp<CT>::ex(run - cum[t * NC + n]);
+            cum[t * NC + n] = c[t];
+            e[t * NC + n] = (float)DiagExp<CT>::ex(c[t]);
+            w[t * NC + n] = (float)DiagExp<CT>::ex(run - c[t]);
         }
         el[n] = (float)DiagExp<CT>::ex(run);
     }
 }
 
+// The local kernel of the diagonal backward, one workgroup per (batch, head, chunk).  For the
+// chunk's rows it writes dx_intra = sum_t A_ts dy_t, intra dB and dC, and dcum_intra = sum_s M_tsn -
+// sum_t' M_t'tn; for the chunk, its local state sum S = sum_s w_sn B_sn x_s^T (into the checkpoint
+// slot), its local gradient sum U = sum_t e_tn C_tn dy_t^T (into the gradient slot), e_last and
+// sum x . dy.  The grid also clears dB and dC, which the state-terms kernel accumulates into.
 template <typename T, int N, int P>
-__global__ void __launch_bounds__(kBThreads) bwd_states_diag_kernel(BwdParams prm) {
-    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
-    using S = BwdDiagShape<N, P, CT>;
-    constexpr int Q = S::Q, NS = S::NS, PS = S::PS, PB = S::PB, NTILE = S::NTILE, TPW = S::TPW, NC = S::NC;
-    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
-    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
-    if (unit < 0) return;
-    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
-    extern __shared__ __align__(16) unsigned char smem[];
-    CT* cum = reinterpret_cast<CT*>(smem);                                             // [Q][NC]
-    float* Bw = reinterpret_cast<float*>(smem + ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16);  // w o B [Q][NS]
-    float* Xs = Bw + Q * NS;                                                           // [Q][PS]
-    float* Ls = Xs + Q * PS;                                                           // log a, then w [Q][NC]
-    float* el = Ls + Q * NC;                                                           // [N]
-    const T* xg = static_cast<const T*>(prm.x);
-    const T* Bg = static_cast<const T*>(prm.Bm);
-
-    f32x4 hs[TPW];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int tile = wave + kBWaves * j;
-        if (tile < NTILE && prm.init) {
-            const int nb = tile / PB, pb = tile % PB;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hs[j][i] = prm.init[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16];
-        }
-    }
-    ChunkRows<T, Q, N> rb;
-    ChunkRows<T, Q, P> rx;
-    ChunkRows<float, Q, N> rl;
-    auto load = [&](int c) {
-        const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
-        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
-        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
-        rl.load(prm.log_a + ((b * Tn + t0) * H + h) * N, H * N, len, tid);
-    };
-    if (prm.nchunks > 0) load(0);
-    for (int c = 0; c < prm.nchunks; ++c) {
-        float* ck = prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kBWaves * j;
-            if (tile < NTILE) {
-                const int nb = tile / PB, pb = tile % PB;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ck[(16 * nb + 4 * lg + i) * P + 16 * pb + l16] = hs[j][i];
-            }
-        }
-        rb.stage(Bw, NS, tid);
-        rx.stage(Xs, PS, tid);
-        rl.stage(Ls, NC, tid);
-        __syncthreads();
-        diag_chunk_factors<N, CT>(Ls, cum, nullptr, Ls, el, tid);
-        __syncthreads();
-        for (int i = tid; i < Q * N; i += kBThreads) Bw[(i / N) * NS + i % N] *= Ls[(i / N) * NC + i % N];
-        __syncthreads();
-        if (c + 1 < prm.nchunks) load(c + 1);
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kBWaves * j;
-            if (tile < NTILE) {
-                const int nb = tile / PB, pb = tile % PB;
-                f32x4 acc = hs[j];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= el[16 * nb + 4 * lg + i];
-                hs[j] = tile_mma(acc, Bw + 16 * nb, 1, NS, Xs + 16 * pb, PS, 1, Q, lane);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-template <typename T, int N, int P>
-__global__ void __launch_bounds__(kBThreads) bwd_walk_diag_kernel(BwdParams prm) {
+__global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm) {
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     using S = BwdDiagShape<N, P, CT>;
     constexpr int Q = S::Q, QS = S::QS, NS = S::NS, PS = S::PS, NB = S::NB, PB = S::PB, QB = S::QB, NC = S::NC;
-    constexpr int NTILE = S::NTILE, TPW = S::TPW;
-    static_assert(QB * QB <= kBWaves / 2, "DYX tiles on the first half of the waves");
-    static_assert(N >= kBWaves, "the final reduction borrows kBWaves floats of <G_n, H_n>");
+    static_assert(QB * QB == kWaves, "one DYX tile per wave");
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
-    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
-    if (unit < 0) return;
-    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
-
-    extern __shared__ __align__(16) unsigned char smem[];
-    CT* cum = reinterpret_cast<CT*>(smem);               // [Q][NC]
-    float* Xs = reinterpret_cast<float*>(smem + ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16);  // [Q][PS]
-    float* Ys = Xs + Q * PS;                             // dy [Q][PS]
-    float* Bs = Ys + Q * PS;                             // [Q][NS]
-    float* Cs = Bs + Q * NS;                             // [Q][NS]
-    float* Ev = Cs + Q * NS;                             // e [Q][NC]
-    float* Wv = Ev + Q * NC;                             // w [Q][NC]
-    float* Am = Wv + Q * NC;                             // A [Q][QS] (rows t, columns s)
-    float* Dm = Am + Q * QS;                             // DYX [Q][QS]
-    float* dBi = Dm + Q * QS;                            // intra-chunk dB [Q][NC]
-    float* dCi = dBi + Q * NC;                           // intra-chunk dC [Q][NC]
-    float* dcum = dCi + Q * NC;                          // [Q][NC] (first the chunk's log a)
-    float* Hs = dcum + Q * NC;                           // H [N][PS]
-    float* Gs = Hs + N * PS;                             // G [N][PS]
-    float* el = Gs + N * PS;                             // e_last [N]
-    float* ghn = el + N;                                 // <G_n, H_n> [N]
-    float* partL = ghn + N;                              // [QB][N]: sum_s w_sn B_sn (G x_s)_n per 16-row block
-
-    const T* xg = static_cast<const T*>(prm.x);
-    const T* yg = static_cast<const T*>(prm.dy);
-    const T* Bg = static_cast<const T*>(prm.Bm);
-    const T* Cg = static_cast<const T*>(prm.Cm);
-    T* dxg = static_cast<T*>(prm.dx);
-    const float dskip = prm.D ? prm.D[h] : 0.f;
-
-    f32x4 gs[TPW];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        gs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int tile = wave + kBWaves * j;
-        if (tile < NTILE && prm.dfinal) {
-            const int nb = tile / PB, pb = tile % PB;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gs[j][i] = prm.dfinal[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16];
+    const int64_t nch = prm.nchunks;
+    {
+        const int64_t nbc = prm.batch * Tn * G * N, stride = (int64_t)gridDim.x * kThreads;
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbc; i += stride) {
+            prm.dB[i] = 0.f;
+            prm.dC[i] = 0.f;
         }
     }
-    auto write_g = [&]() {
+    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd_intra, units * nch);
+    if (work < 0) return;
+    const int64_t unit = work / nch;
+    const int c = (int)(work % nch);
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+    const int r = lane % 16, gq = lane / 16;
+    const int64_t t0 = (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, Tn - t0);
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    CT* cum = reinterpret_cast<CT*>(smem);                    // [Q][NC]
+    float* Xs = reinterpret_cast<float*>(smem + S::cum_bytes);  // [Q][PS]
+    float* Ys = Xs + Q * PS;                                  // dy [Q][PS]
+    float* Bs = Ys + Q * PS;                                  // [Q][NS]
+    float* Cs = Bs + Q * NS;                                  // [Q][NS]
+    float* Am = Cs + Q * NS;                                  // A [Q][QS]
+    float* Dm = Am + Q * QS;                                  // DYX [Q][QS]
+    float* Wv = Dm + Q * QS;                                  // log a, then w [Q][NC]
+    float* Ev = Wv + Q * NC;                                  // e [Q][NC]
+    float* el = Ev + Q * NC;                                  // e_last [N]
+    float* red = el + N;                                      // [kWaves]
+
+    // the chunk's rows straight into LDS (zeros past the end); sum x . dy on the way
+    const T* xg = static_cast<const T*>(prm.x) + ((b * Tn + t0) * H + h) * P;
+    const T* yg = static_cast<const T*>(prm.dy) + ((b * Tn + t0) * H + h) * P;
+    const T* Bg = static_cast<const T*>(prm.Bm) + ((b * Tn + t0) * G + g) * N;
+    const T* Cg = static_cast<const T*>(prm.Cm) + ((b * Tn + t0) * G + g) * N;
+    const float* lg0 = prm.log_a + ((b * Tn + t0) * H + h) * N;
+    float xdy = 0.f;
+    for (int i = tid; i < Q * P; i += kThreads) {
+        const int q = i / P, p = i % P;
+        const float xv = q < len ? to_f32(xg[(int64_t)q * H * P + p]) : 0.f;
+        const float yv = q < len ? to_f32(yg[(int64_t)q * H * P + p]) : 0.f;
+        Xs[q * PS + p] = xv;
+        Ys[q * PS + p] = yv;
+        xdy += xv * yv;
+    }
+    for (int i = tid; i < Q * N; i += kThreads) {
+        const int q = i / N, n = i % N;
+        Bs[q * NS + n] = q < len ? to_f32(Bg[(int64_t)q * G * N + n]) : 0.f;
+        Cs[q * NS + n] = q < len ? to_f32(Cg[(int64_t)q * G * N + n]) : 0.f;
+        Wv[q * NC + n] = q < len ? lg0[(int64_t)q * H * N + n] : 0.f;
+    }
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kBWaves * j;
-            if (tile < NTILE) {
-                const int nb = tile / PB, pb = tile % PB;
+    for (int off = 32; off > 0; off >>= 1) xdy += __shfl_xor(xdy, off, kWave);
+    if (lane == 0) red[wave] = xdy;
+    lds_barrier();
+    diag_chunk_factors<N, CT>(Wv, cum, Ev, Wv, el, tid);
+    {
+        const int tb = wave / QB, sb = wave % QB;
+        const f32x4 v = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Xs + 16 * sb * PS, 1, PS, P,
+                                 lane);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Gs[(16 * nb + 4 * lg + i) * PS + 16 * pb + l16] = gs[j][i];
+        for (int i = 0; i < 4; ++i) Dm[(16 * tb + 4 * lg + i) * QS + 16 * sb + l16] = v[i];
+    }
+    lds_barrier();
+    const int64_t row0 = (b * Tn + t0) * H + h;
+    if (tid < N) prm.elw[(unit * nch + c) * N + tid] = el[tid];
+    if (tid == 0) {
+        float s = 0.f;
+        for (int k = 0; k < kWaves; ++k) s += red[k];
+        prm.dD_part[unit * nch + c] = s;
+    }
+    // the local sums S = (w o B)^T X and U = (e o C)^T dY, fp32 on the matrix cores
+    {
+        float* Sg = prm.ckpt + (unit * nch + c) * (int64_t)N * P;
+        float* Ug = prm.gst + (unit * nch + c) * (int64_t)N * P;
+        for (int tile = wave; tile < 2 * NB * PB; tile += kWaves) {
+            const bool isU = tile >= NB * PB;
+            const int tt = isU ? tile - NB * PB : tile, nb = tt / PB, pb = tt % PB;
+            const float* F = isU ? Ev : Wv;
+            const float* V = isU ? Cs : Bs;
+            const float* R = isU ? Ys : Xs;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < Q; k += 4) {
+                const int s = k + gq, n = 16 * nb + r;
+                acc = mfma_f32(F[s * NC + n] * V[s * NS + n], R[s * PS + 16 * pb + r], acc);
+            }
+            float* out = isU ? Ug : Sg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(16 * nb + 4 * lg + i) * P + 16 * pb + l16] = acc[i];
+        }
+    }
+    // A_ts = sum_n C_tn B_sn L_tsn on the vector units (the sum over n unrolled by 4 with independent
+    // partial sums)
+    for (int idx = tid; idx < Q * Q; idx += kThreads) {
+        const int t = idx / Q, s = idx % Q;
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+        if (s <= t) {
+#pragma unroll 4
+            for (int n = 0; n < N; n += 4)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    a[u] += Cs[t * NS + n + u] * Bs[s * NS + n + u] *
+                            (float)DiagExp<CT>::ex(cum[t * NC + n + u] - cum[s * NC + n + u]);
+        }
+        Am[t * QS + s] = (a[0] + a[1]) + (a[2] + a[3]);
+    }
+    // intra dB, dC and the M sums per (q, n) (fixed-length masked loops, fully unrolled)
+    for (int idx = tid; idx < Q * N; idx += kThreads) {
+        const int q = idx / N, n = idx % N;
+        const CT cq = cum[q * NC + n];
+        float db = 0.f, dc = 0.f;
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+            // u in the role of t (q as s), then of s (q as t)
+            const float vb = u >= q ? Dm[u * QS + q] * (float)DiagExp<CT>::ex(cum[u * NC + n] - cq) * Cs[u * NS + n] : 0.f;
+            const float vc = u <= q ? Dm[q * QS + u] * (float)DiagExp<CT>::ex(cq - cum[u * NC + n]) * Bs[u * NS + n] : 0.f;
+            db += vb;
+            dc += vc;
+        }
+        if (q < len) {
+            const int64_t o = (row0 + (int64_t)q * H) * N + n;
+            prm.dBi[o] = db;
+            prm.dCi[o] = dc;
+            // row sum of M at t = q minus its column sum at s = q: C_qn dC_intra - B_qn dB_intra
+            prm.dcumi[o] = Cs[q * NS + n] * dc - Bs[q * NS + n] * db;
+        }
+    }
+    lds_barrier();
+    // dx_intra = sum_t A_ts dy_t: A(s, t) = Am[t][s]
+    for (int tile = wave; tile < QB * PB; tile += kWaves) {
+        const int sb = tile / PB, pb = tile % PB;
+        const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * sb + 4 * lg + i;
+            if (s < len) prm.dxi[(row0 + (int64_t)s * H) * P + 16 * pb + l16] = acc[i];
+        }
+    }
+}
+
+// The chains over the chunks, in place, one thread per (batch, head, state element) and direction:
+// the checkpoint slots hold S_c on entry and H_c (the state entering chunk c) on exit, from
+// H_0 = init; the gradient slots hold U_c on entry and G_c (the gradient of the state at the end of
+// chunk c) on exit, from dfinal; dinit = e_last,0 G_0 + U_0.  Loads go 8 chunks at a time.
+template <int N, int P>
+__global__ void __launch_bounds__(kThreads) bwd_scan_diag_kernel(BwdParams prm) {
+    constexpr int64_t per = (int64_t)N * P;
+    constexpr int kB = 8;
+    const int64_t units = prm.batch * prm.nheads;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= 2 * units * per) return;
+    const bool fwd = i < units * per;
+    const int64_t j = fwd ? i : i - units * per;
+    const int64_t unit = j / per, e = j % per, n = e / P;
+    const int nch = prm.nchunks;
+    const float* el = prm.elw + unit * nch * N + n;
+    float* slot = (fwd ? prm.ckpt : prm.gst) + unit * nch * per + e;
+    const float* start = fwd ? prm.init : prm.dfinal;
+    float v = start ? start[unit * per + e] : 0.f;
+    for (int k0 = 0; k0 < nch; k0 += kB) {
+        float s[kB], a[kB];
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+            const int c = fwd ? k0 + k : nch - 1 - k0 - k;
+            if (k0 + k < nch) {
+                s[k] = slot[c * per];
+                a[k] = el[c * N];
             }
         }
-    };
-    write_g();
-    float dD_acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < kB; ++k) {
+            const int c = fwd ? k0 + k : nch - 1 - k0 - k;
+            if (k0 + k < nch) {
+                slot[c * per] = v;
+                v = a[k] * v + s[k];
+            }
+        }
+    }
+    if (!fwd && prm.dinit) prm.dinit[unit * per + e] = v;
+}
 
-    ChunkRows<T, Q, P> rx, ry;
-    ChunkRows<T, Q, N> rb, rc;
-    ChunkRows<float, N, P> rh;
-    ChunkRows<float, Q, N> rl;
-    auto load = [&](int c) {
-        const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
-        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
-        ry.load(yg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
-        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
-        rc.load(Cg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
-        rh.load(prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P, P, N, tid);
-        rl.load(prm.log_a + ((b * Tn + t0) * H + h) * N, H * N, len, tid);
-    };
-    if (prm.nchunks > 0) load(prm.nchunks - 1);
+// The state-terms kernel of the diagonal backward, one workgroup per (batch, head, chunk): with the
+// chunk's H and G from the scan and its intra-chunk terms from the local kernel, the dx, dB, dC and
+// dlog a of the chunk's rows (dB and dC accumulated over the heads of a group).
+template <typename T, int N, int P>
+__global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm) {
+    using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+    using S = BwdDiagShape<N, P, CT>;
+    constexpr int Q = S::Q, NS = S::NS, PS = S::PS, NB = S::NB, PB = S::PB, QB = S::QB, NC = S::NC;
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
+    const int64_t nch = prm.nchunks;
+    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd_intra, units * nch);
+    if (work < 0) return;
+    const int64_t unit = work / nch;
+    const int c = (int)(work % nch);
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+    const int r = lane % 16, gq = lane / 16;
+    const int64_t t0 = (int64_t)c * Q;
+    const int len = (int)min((int64_t)Q, Tn - t0);
+    const int64_t row0 = (b * Tn + t0) * H + h;
 
-    for (int c = prm.nchunks - 1; c >= 0; --c) {
-        const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
-        // ---- 1. the chunk into LDS; per-dimension running sums
+    extern __shared__ __align__(16) unsigned char smem[];
+    CT* cum = reinterpret_cast<CT*>(smem);                    // [Q][NC]
+    float* Xs = reinterpret_cast<float*>(smem + S::cum_bytes);  // [Q][PS]
+    float* Ys = Xs + Q * PS;                                  // dy [Q][PS]
+    float* Bs = Ys + Q * PS;                                  // [Q][NS]
+    float* Cs = Bs + Q * NS;                                  // [Q][NS]
+    float* Ev = Cs + Q * NS;                                  // e [Q][NC]
+    float* Wv = Ev + Q * NC;                                  // log a, then w [Q][NC]
+    float* dcum = Wv + Q * NC;                                // [Q][NC]
+    float* Hs = dcum + Q * NC;                                // H [N][PS]
+    float* Gs = Hs + N * PS;                                  // G [N][PS]
+    float* el = Gs + N * PS;                                  // e_last [N]
+    float* ghn = el + N;                                      // <G_n, H_n> [N]
+    float* partL = ghn + N;                                   // [QB][N]: sum_s w_sn B_sn (G x_s)_n per 16 rows
+
+    {
+        ChunkRows<T, Q, P> rx, ry;
+        ChunkRows<T, Q, N> rb, rc;
+        ChunkRows<float, N, P> rh, rg;
+        ChunkRows<float, Q, N> rl, rm;
+        rx.load(static_cast<const T*>(prm.x) + row0 * P, H * P, len, tid);
+        ry.load(static_cast<const T*>(prm.dy) + row0 * P, H * P, len, tid);
+        rb.load(static_cast<const T*>(prm.Bm) + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rc.load(static_cast<const T*>(prm.Cm) + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rh.load(prm.ckpt + (unit * nch + c) * (int64_t)N * P, P, N, tid);
+        rg.load(prm.gst + (unit * nch + c) * (int64_t)N * P, P, N, tid);
+        rl.load(prm.log_a + row0 * N, H * N, len, tid);
+        rm.load(prm.dcumi + row0 * N, H * N, len, tid);
         rx.stage(Xs, PS, tid);
         ry.stage(Ys, PS, tid);
         rb.stage(Bs, NS, tid);
         rc.stage(Cs, NS, tid);
         rh.stage(Hs, PS, tid);
-        rl.stage(dcum, NC, tid);
-#pragma unroll
-        for (int i = 0; i < ChunkRows<T, Q, P>::PT; ++i)
-#pragma unroll
-            for (int j = 0; j < ChunkRows<T, Q, P>::VE; ++j) dD_acc += rx.elem(i, j) * ry.elem(i, j);
-        __syncthreads();
-        diag_chunk_factors<N, CT>(dcum, cum, Ev, Wv, el, tid);
-        __syncthreads();
-        if (c > 0) load(c - 1);
-
-        // ---- 2. DYX on the matrix cores (the first waves, first); A_ts = sum_n C_tn B_sn L_tsn on
-        //         the vector units (every thread; the sum over n unrolled by 4 with independent
-        //         partial sums, so the LDS reads of one step overlap the arithmetic of the last)
-        if (wave < QB * QB) {
-            const int tb = wave / QB, sb = wave % QB;
-            const f32x4 v = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * tb * PS, PS, 1, Xs + 16 * sb * PS, 1, PS, P,
-                                     lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Dm[(16 * tb + 4 * lg + i) * QS + 16 * sb + l16] = v[i];
-        }
-        for (int idx = tid; idx < Q * Q; idx += kBThreads) {
-            const int t = idx / Q, s = idx % Q;
-            float a[4] = {0.f, 0.f, 0.f, 0.f};
-            if (s <= t) {
-#pragma unroll 4
-                for (int n = 0; n < N; n += 4)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        a[u] += Cs[t * NS + n + u] * Bs[s * NS + n + u] *
-                                (float)DiagExp<CT>::ex(cum[t * NC + n + u] - cum[s * NC + n + u]);
-            }
-            Am[t * QS + s] = (a[0] + a[1]) + (a[2] + a[3]);
-        }
-        __syncthreads();
-
-        // ---- 3a. intra-chunk dB, dC and dcum = (row sums - column sums of M), per (q, n)
-        // (fixed-length loops over the chunk, masked: fully unrolled, their loads run ahead)
-        for (int idx = tid; idx < Q * N; idx += kBThreads) {
-            const int q = idx / N, n = idx % N;
-            const CT cq = cum[q * NC + n];
-            float db = 0.f, dc = 0.f;
-#pragma unroll
-            for (int u = 0; u < Q; ++u) {
-                // u in the role of t (q as s), then of s (q as t)
-                const float vb = u >= q ? Dm[u * QS + q] * (float)DiagExp<CT>::ex(cum[u * NC + n] - cq) * Cs[u * NS + n] : 0.f;
-                const float vc = u <= q ? Dm[q * QS + u] * (float)DiagExp<CT>::ex(cq - cum[u * NC + n]) * Bs[u * NS + n] : 0.f;
-                db += vb;
-                dc += vc;
-            }
-            dBi[q * NC + n] = db;
-            dCi[q * NC + n] = dc;
-            // row sum of M at t = q minus its column sum at s = q: C_qn dC_intra - B_qn dB_intra
-            dcum[q * NC + n] = Cs[q * NS + n] * dc - Bs[q * NS + n] * db;
-        }
-        __syncthreads();
-
-        // ---- 3b. the carried-state terms (matrix cores): dx, dB, dC out; dcum's state terms
-        for (int tile = wave; tile < QB * PB; tile += kBWaves) {
-            const int sb = tile / PB, pb = tile % PB;
-            f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
-            // sum_n w_sn B_sn G_np: A(s, n) = Wv[s][n] Bs[s][n]
-            const int r = lane % 16, gq = lane / 16;
-#pragma unroll 4
-            for (int k = 0; k < N; k += 4) {
-                const int s = 16 * sb + r, n = k + gq;
-                acc = mfma_f32(Wv[s * NC + n] * Bs[s * NS + n], Gs[n * PS + 16 * pb + r], acc);
-            }
-            const int p = 16 * pb + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = 16 * sb + 4 * lg + i;
-                if (s < len) dxg[((b * Tn + t0 + s) * H + h) * P + p] = from_f32<T>(acc[i] + dskip * Ys[s * PS + p]);
-            }
-        }
-        for (int tile = wave; tile < QB * NB; tile += kBWaves) {
-            const int qb = tile / NB, nb = tile % NB;
-            const f32x4 gx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Xs + 16 * qb * PS, PS, 1, Gs + 16 * nb * PS, 1, PS, P,
-                                      lane);
-            const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * qb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS, P,
-                                      lane);
-            const int n = 16 * nb + l16;
-            float lastp = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = 16 * qb + 4 * lg + i;
-                const float wb = Wv[q * NC + n] * Bs[q * NS + n] * gx[i];
-                const float ec = Ev[q * NC + n] * Cs[q * NS + n] * hd[i];
-                if (q < len) {
-                    atomicAdd(prm.dB + ((b * Tn + t0 + q) * G + g) * N + n, dBi[q * NC + n] + Wv[q * NC + n] * gx[i]);
-                    atomicAdd(prm.dC + ((b * Tn + t0 + q) * G + g) * N + n, dCi[q * NC + n] + Ev[q * NC + n] * hd[i]);
-                }
-                dcum[q * NC + n] += ec - wb;
-                lastp += wb;
-            }
-            lastp += __shfl_xor(lastp, 16, kWave);
-            lastp += __shfl_xor(lastp, 32, kWave);
-            if (lg == 0) partL[qb * N + n] = lastp;
-        }
-        if (tid < N) {
-            float acc = 0.f;
-            for (int p = 0; p < P; ++p) acc += Gs[tid * PS + p] * Hs[tid * PS + p];
-            ghn[tid] = acc;
-        }
-        __syncthreads();
-
-        // ---- 4. dlog a per dimension (reverse running sum, the last token's term first); G
-        if (tid < N) {
-            const int n = tid;
-            float last = el[n] * ghn[n];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) last += partL[qb * N + n];
-            float r = last;
-            for (int t = Q - 1; t >= 0; --t) {
-                r += dcum[t * NC + n];
-                if (t < len) prm.dlog_a[((b * Tn + t0 + t) * H + h) * N + n] = r;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kBWaves * j;
-            if (tile < NTILE) {
-                const int nb = tile / PB, pb = tile % PB;
-                f32x4 acc = gs[j];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= el[16 * nb + 4 * lg + i];
-                const int r = lane % 16, gq = lane / 16;
-#pragma unroll 4
-                for (int k = 0; k < Q; k += 4) {
-                    const int t = k + gq, n = 16 * nb + r;
-                    acc = mfma_f32(Ev[t * NC + n] * Cs[t * NS + n], Ys[t * PS + 16 * pb + r], acc);
-                }
-                gs[j] = acc;
-            }
-        }
-        __syncthreads();
-        write_g();
+        rg.stage(Gs, PS, tid);
+        rl.stage(Wv, NC, tid);
+        rm.stage(dcum, NC, tid);
     }
-    __syncthreads();
-    if (prm.dinit) {
+    lds_barrier();
+    diag_chunk_factors<N, CT>(Wv, cum, Ev, Wv, el, tid);
+    if (tid >= kBThreads - N) {
+        const int n = tid - (kBThreads - N);
+        float acc = 0.f;
+#pragma unroll 8
+        for (int p = 0; p < P; ++p) acc += Gs[n * PS + p] * Hs[n * PS + p];
+        ghn[n] = acc;
+    }
+    lds_barrier();
+
+    // dx = dx_intra + sum_n w_sn B_sn G_np + D dy_s
+    T* dxg = static_cast<T*>(prm.dx);
+    const float dskip = prm.D ? prm.D[h] : 0.f;
+    for (int tile = wave; tile < QB * PB; tile += kBWaves) {
+        const int sb = tile / PB, pb = tile % PB, p = 16 * pb + l16;
+        float base[4];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int tile = wave + kBWaves * j;
-            if (tile < NTILE) {
-                const int nb = tile / PB, pb = tile % PB;
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * sb + 4 * lg + i;
+            base[i] = s < len ? prm.dxi[(row0 + (int64_t)s * H) * P + p] : 0.f;
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int k = 0; k < N; k += 4) {
+            const int s = 16 * sb + r, n = k + gq;
+            acc = mfma_f32(Wv[s * NC + n] * Bs[s * NS + n], Gs[n * PS + 16 * pb + r], acc);
+        }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) prm.dinit[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16] = gs[j][i];
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * sb + 4 * lg + i;
+            if (s < len) dxg[(row0 + (int64_t)s * H) * P + p] = from_f32<T>(base[i] + acc[i] + dskip * Ys[s * PS + p]);
         }
     }
+    // dB, dC out; dcum's state terms
+    for (int tile = wave; tile < QB * NB; tile += kBWaves) {
+        const int qb = tile / NB, nb = tile % NB, n = 16 * nb + l16;
+        float dbi[4], dci[4];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dD_acc += __shfl_xor(dD_acc, off, kWave);
-    if (lane == 0) ghn[wave] = dD_acc;
-    __syncthreads();
-    if (tid == 0) {
-        float s2 = 0.f;
-        for (int k = 0; k < kBWaves; ++k) s2 += ghn[k];
-        prm.dD_part[unit] = s2;
+        for (int i = 0; i < 4; ++i) {
+            const int q = 16 * qb + 4 * lg + i;
+            const int64_t o = (row0 + (int64_t)q * H) * N + n;
+            dbi[i] = q < len ? prm.dBi[o] : 0.f;
+            dci[i] = q < len ? prm.dCi[o] : 0.f;
+        }
+        const f32x4 gx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Xs + 16 * qb * PS, PS, 1, Gs + 16 * nb * PS, 1, PS, P,
+                                  lane);
+        const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * qb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS, P,
+                                  lane);
+        float lastp = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = 16 * qb + 4 * lg + i;
+            const float wb = Wv[q * NC + n] * Bs[q * NS + n] * gx[i];
+            const float ec = Ev[q * NC + n] * Cs[q * NS + n] * hd[i];
+            if (q < len) {
+                atomicAdd(prm.dB + ((b * Tn + t0 + q) * G + g) * N + n, dbi[i] + Wv[q * NC + n] * gx[i]);
+                atomicAdd(prm.dC + ((b * Tn + t0 + q) * G + g) * N + n, dci[i] + Ev[q * NC + n] * hd[i]);
+            }
+            dcum[q * NC + n] += ec - wb;
+            lastp += wb;
+        }
+        lastp += __shfl_xor(lastp, 16, kWave);
+        lastp += __shfl_xor(lastp, 32, kWave);
+        if (lg == 0) partL[qb * N + n] = lastp;
+    }
+    lds_barrier();
+
+    // dlog a per dimension: reverse running sum, the last token's term first
+    if (tid < N) {
+        const int n = tid;
+        float last = el[n] * ghn[n];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) last += partL[qb * N + n];
+        float acc = last;
+        for (int t = Q - 1; t >= 0; --t) {
+            acc += dcum[t * NC + n];
+            if (t < len) prm.dlog_a[(row0 + (int64_t)t * H) * N + n] = acc;
+        }
     }
 }
 
-// dD[h] = sum over the batch of the walk's per-(batch, head) sums; dB, dC zeroed by zero_kernel.
-__global__ void __launch_bounds__(kThreads) bwd_reduce_kernel(const float* part, float* dD, int64_t batch, int64_t H) {
+// dD[h] = sum over the batch (and for the diagonal path the chunks) of the per-unit sums,
+// part[(b H + h) nper + k].  (dB and dC are cleared by zero_kernel on the scalar path, by the local
+// kernel on the diagonal one.)
+__global__ void __launch_bounds__(kThreads) bwd_reduce_kernel(const float* part, float* dD, int64_t batch, int64_t H,
+                                                              int64_t nper) {
     const int64_t h = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (h >= H) return;
     float s = 0.f;
-    for (int64_t b = 0; b < batch; ++b) s += part[b * H + h];
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t k = 0; k < nper; ++k) s += part[(b * H + h) * nper + k];
     dD[h] = s;
 }
 
@@ -911,7 +932,8 @@ int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
             return -1;
     }
     if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)((bl.p.nheads + kThreads - 1) / kThreads)),
-                          dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads))
+                          dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads,
+                          (int64_t)1))
         return -1;
     return 0;
 }
@@ -977,10 +999,10 @@ __global__ void __launch_bounds__(kThreads) head_sum_kernel(const float* v, floa
     for (int64_t i = threadIdx.x; i < bt; i += kThreads) s += v[i * H + h];
     __shared__ float red[kThreads];
     red[threadIdx.x] = s;
-    __syncthreads();
+    lds_barrier();
     for (int w = kThreads / 2; w > 0; w >>= 1) {
         if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
+        lds_barrier();
     }
     if (threadIdx.x == 0) out[h] = red[0];
 }
@@ -989,35 +1011,39 @@ template <typename T, int N, int P>
 int launch_backward_diag_t(const BackwardLaunch& bl, hipStream_t stream) {
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     using S = BwdDiagShape<N, P, CT>;
-    static_assert(S::walk_lds <= kMaxLds, "diagonal backward walk LDS budget");
+    static_assert(S::local_lds <= kMaxLds && S::terms_lds <= kMaxLds, "diagonal backward LDS budget");
     static bool attr[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
     if (!attr[dev]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_walk_diag_kernel<T, N, P>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::walk_lds) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_local_diag_kernel<T, N, P>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::local_lds) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_terms_diag_kernel<T, N, P>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::terms_lds) != hipSuccess)
             return -1;
         attr[dev] = true;
     }
-    const int64_t units = bl.p.batch * bl.p.nheads;
+    const int64_t units = bl.p.batch * bl.p.nheads, work = units * bl.p.nchunks;
     BwdParams p = bl.p;
     p.per_xcd = (units + 7) / 8;
-    const int64_t nbc = bl.p.batch * bl.p.seqlen * bl.p.ngroups * N;
+    p.per_xcd_intra = (work + 7) / 8;
     int k = 0;
-    if (nbc > 0 &&
-        !launch_k(bl, k, zero_kernel, dim3((unsigned)std::min<int64_t>((nbc + kThreads - 1) / kThreads, 4096)),
-                  dim3(kThreads), 0, stream, p.dB, nbc, p.dC, nbc))
-        return -1;
     if (units > 0) {
-        if (!launch_k(bl, k, bwd_states_diag_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
-                      S::states_lds, stream, p))
+        // (seqlen 0: no chunks, so nothing to clear either; the scan still gives dinit = dfinal)
+        if (work > 0 && !launch_k(bl, k, bwd_local_diag_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd_intra)),
+                                  dim3(kThreads), S::local_lds, stream, p))
             return -1;
-        if (!launch_k(bl, k, bwd_walk_diag_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
-                      S::walk_lds, stream, p))
+        const int64_t scan_threads = 2 * units * N * P;
+        if (!launch_k(bl, k, bwd_scan_diag_kernel<N, P>, dim3((unsigned)((scan_threads + kThreads - 1) / kThreads)),
+                      dim3(kThreads), 0, stream, p))
+            return -1;
+        if (work > 0 && !launch_k(bl, k, bwd_terms_diag_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd_intra)),
+                                  dim3(kBThreads), S::terms_lds, stream, p))
             return -1;
     }
     if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)((bl.p.nheads + kThreads - 1) / kThreads)),
-                          dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads))
+                          dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads,
+                          (int64_t)bl.p.nchunks))
         return -1;
     return 0;
 }
@@ -1041,10 +1067,51 @@ bool backward_shape_supported(int N, int P, int decay) {
     return false;
 }
 
-size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P) {
+namespace {
+// Workspace of the backward pass: checkpoints [B,H,nchunks,N,P] fp32 and per-(batch, head) dD sums
+// (per (batch, head, chunk) for the diagonal decay); with the diagonal decay also the gradient
+// slots [B,H,nchunks,N,P], e_last [B,H,nchunks,N] and the intra-chunk terms dx [B,T,H,P] and dB,
+// dC, dcum [B,T,H,N], all fp32.
+struct BwdLayout {
+    size_t ckpt, part, gst, elw, dxi, dBi, dCi, dcumi, total;
+};
+BwdLayout bwd_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int decay) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     const int64_t nchunks = (seqlen + kBQ - 1) / kBQ;
-    const size_t ck = (size_t)(batch * nheads * nchunks) * (size_t)N * (size_t)P * 4;
-    return (ck + 255) / 256 * 256 + ((size_t)(batch * nheads) * 4 + 255) / 256 * 256;
+    const size_t rows = (size_t)batch * (size_t)seqlen * (size_t)nheads;
+    BwdLayout l{};
+    size_t off = 0;
+    l.ckpt = off; off = up(off + (size_t)(batch * nheads * nchunks) * (size_t)N * (size_t)P * 4);
+    l.part = off; off = up(off + (size_t)(batch * nheads) * (size_t)(decay == 1 ? nchunks : 1) * 4);
+    if (decay == 1) {
+        l.gst = off; off = up(off + (size_t)(batch * nheads * nchunks) * (size_t)N * (size_t)P * 4);
+        l.elw = off; off = up(off + (size_t)(batch * nheads * nchunks) * (size_t)N * 4);
+        l.dxi = off; off = up(off + rows * P * 4);
+        l.dBi = off; off = up(off + rows * N * 4);
+        l.dCi = off; off = up(off + rows * N * 4);
+        l.dcumi = off; off = up(off + rows * N * 4);
+    }
+    l.total = off;
+    return l;
+}
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int decay) {
+    return bwd_layout(batch, nheads, seqlen, N, P, decay).total;
+}
+
+void bind_backward_workspace(BwdParams& p, void* ws, int N, int P, int decay) {
+    const BwdLayout l = bwd_layout(p.batch, p.nheads, p.seqlen, N, P, decay);
+    char* w = static_cast<char*>(ws);
+    auto at = [&](size_t off) { return w ? reinterpret_cast<float*>(w + off) : nullptr; };
+    p.ckpt = at(l.ckpt);
+    p.dD_part = at(l.part);
+    p.gst = decay == 1 ? at(l.gst) : nullptr;
+    p.elw = decay == 1 ? at(l.elw) : nullptr;
+    p.dxi = decay == 1 ? at(l.dxi) : nullptr;
+    p.dBi = decay == 1 ? at(l.dBi) : nullptr;
+    p.dCi = decay == 1 ? at(l.dCi) : nullptr;
+    p.dcumi = decay == 1 ? at(l.dcumi) : nullptr;
 }
 
 int launch_backward(const BackwardLaunch& bl, hipStream_t stream) {
@@ -1082,7 +1149,7 @@ DtBackwardLayout dt_backward_layout(int64_t batch, int64_t nheads, int64_t seqle
     l.ddt_rows = 0;  // (the caller's ddt holds them)
     l.rowA = off; off = up(off + rows * 4);
     l.rowD = off; off = up(off + rows * 4);
-    l.inner = off; off += backward_workspace_bytes(batch, nheads, seqlen, N, P);
+    l.inner = off; off += backward_workspace_bytes(batch, nheads, seqlen, N, P, 0);
     l.total = off;
     return l;
 }
@@ -1117,10 +1184,7 @@ int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipSt
     bl.p.dx = dxs;
     bl.p.dlog_a = dla;
     bl.p.dD = nullptr;
-    bl.p.ckpt = reinterpret_cast<float*>(ws + l.inner);
-    const int64_t nchunks = bl.p.nchunks;
-    const size_t ck = (size_t)(bl.p.batch * H * nchunks) * (size_t)(bl0.dstate * P) * 4;
-    bl.p.dD_part = reinterpret_cast<float*>(ws + l.inner + (ck + 255) / 256 * 256);
+    bind_backward_workspace(bl.p, ws + l.inner, (int)bl0.dstate, P, 0);
     const int rc = launch_backward(bl, stream);
     if (rc != 0) return rc;
     if (rows > 0) {

@@ -7,7 +7,9 @@
 namespace ssd {
 
 // The backward pass (ssd_bwd.hip), scalar or diagonal decay: inputs, the gradients it writes, and its
-// workspace (the state entering every backward chunk, and per-(batch, head) sums for dD).
+// workspace (the state entering every backward chunk, per-(batch, head) sums for dD, and for the
+// diagonal decay the gradient of the state at every chunk's end, per-chunk decays, and the
+// intra-chunk terms of dx, dB, dC and dlog a, per (b, t, h) row).
 struct BwdParams {
     const void* x;
     const float* log_a;
@@ -25,9 +27,15 @@ struct BwdParams {
     float* dinit;
     float* ckpt;
     float* dD_part;
+    float* gst;    // diagonal decay: [B,H,nchunks,N,P] (the checkpoints' layout)
+    float* elw;    // diagonal decay: [B,H,nchunks,N]
+    float* dxi;    // diagonal decay: [B,T,H,P]
+    float* dBi;    // diagonal decay: [B,T,H,N] (dCi, dcumi likewise)
+    float* dCi;
+    float* dcumi;
     int64_t batch, seqlen, nheads, ngroups;
     int nchunks;  // backward chunks (backward_chunk() tokens each)
-    int64_t per_xcd;
+    int64_t per_xcd, per_xcd_intra;
 };
 struct BackwardLaunch {
     int dtype;
@@ -40,7 +48,9 @@ struct BackwardLaunch {
     int* n_launches;
 };
 bool backward_shape_supported(int N, int P, int decay);
-size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P);
+size_t backward_workspace_bytes(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int decay);
+// Points p's workspace fields into ws (backward_workspace_bytes of it); p.batch, nheads and seqlen set.
+void bind_backward_workspace(BwdParams& p, void* ws, int N, int P, int decay);
 int backward_chunk();
 // 0 on success, -1 when HIP rejects a launch, -2 for an unsupported shape.
 int launch_backward(const BackwardLaunch& bl, hipStream_t stream);

@@ -85,6 +85,14 @@ __device__ __forceinline__ float log2_softplus_hw(float v, float sp) {
     return v < -20.f ? v * 1.4426950408889634f : __builtin_amdgcn_logf(sp);
 }
 
+// Barrier that orders LDS accesses only: global loads, stores and atomics issued before it stay in
+// flight (a kernel whose threads share data only through LDS needs no more).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Block-wide inclusive scan of one value per thread (kThreads threads).  `scratch` holds
 // kWaves values of type V in LDS.  Contains two __syncthreads().
 template <typename V>

@@ -51,13 +51,6 @@ __device__ __forceinline__ v4i16 lds_read_tr(const __bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
-// Barrier that orders LDS accesses only: global loads issued before it stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Operand fragment of a row-major [token][col] bf16 tile in LDS, contracting over tokens:
 // lane (g, i) receives tile[32k + kperm(g, j)][col0 + i], j = 0..7.
 __device__ __forceinline__ bf16x8 token_frag(const __bf16* tile, int stride, int col0, int k, int lane) {

@@ -269,8 +269,13 @@ def test_backward_workspace_bytes(lib):
     assert ssd.ssd_backward_workspace_bytes(d) == up(2 * 4 * 10 * 128 * 64 * 4) + up(2 * 4 * 4)
     assert ssd.ssd_backward_workspace_bytes(mamba2_dims(batch=0)) == 0
     assert ssd.ssd_backward_workspace_bytes(mamba2_dims(decay=1)) == 0          # diagonal decay: N <= 64
+    # diagonal decay: the dD sums per (batch, head, chunk); a gradient slot per checkpoint; an fp32
+    # decay per (batch, head, chunk, state dim); the intra-chunk terms per (b, t, h) row, fp32: dx [P],
+    # dB, dC, dcum [N] each
     dd = mamba2_dims(decay=1, dstate=64, batch=1, seqlen=100, nheads=2)
-    assert ssd.ssd_backward_workspace_bytes(dd) == up(1 * 2 * 4 * 64 * 64 * 4) + up(1 * 2 * 4)
+    rows = 1 * 100 * 2
+    assert ssd.ssd_backward_workspace_bytes(dd) == 2 * up(1 * 2 * 4 * 64 * 64 * 4) + up(1 * 2 * 4 * 4) + \
+        up(1 * 2 * 4 * 64 * 4) + up(rows * 64 * 4) + 3 * up(rows * 64 * 4)
     assert ssd.ssd_backward_workspace_bytes(mamba2_dims(headdim=128)) == 0      # P <= 64
 
 
