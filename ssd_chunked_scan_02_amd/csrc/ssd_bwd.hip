@@ -36,7 +36,8 @@
 namespace ssd {
 namespace {
 
-constexpr int kBQ = 32;  // tokens per backward chunk
+constexpr int kBQ = 32;       // tokens per backward chunk
+constexpr int kBwdCUs = 256;  // compute units: the persistent kernels' workgroup count
 
 // acc += A B for one 16x16 tile (fp32 MFMA 16x16x4; lane l gives A(l % 16, k + l / 16) and
 // B(k + l / 16, l % 16) and holds rows 4 (l / 16) + i, column l % 16 of the tile).  Element
@@ -84,17 +85,17 @@ struct BwdShape {
 
 // One chunk's rows of a [.., rows, width] tensor in 16-byte pieces, a chunk ahead of their use:
 // piece u of the chunk is row u / (width / VE), elements VE (u % (width / VE)) .. + VE; rows at
-// or past len are zeros.  Each thread holds pieces tid + kBThreads i.
-template <typename T, int ROWS, int WIDTH>
+// or past len are zeros.  Each of the NT threads holds pieces tid + NT i.
+template <typename T, int ROWS, int WIDTH, int NT = kBThreads>
 struct ChunkRows {
     static constexpr int VE = 16 / (int)sizeof(T), PER_ROW = WIDTH / VE, PIECES = ROWS * PER_ROW;
-    static constexpr int PT = (PIECES + kBThreads - 1) / kBThreads;
+    static constexpr int PT = (PIECES + NT - 1) / NT;
     uint4 v[PT];
     // row r of the chunk starts at base + r * stride (elements)
     __device__ void load(const T* base, int64_t stride, int len, int tid) {
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
-            const int u = tid + kBThreads * i, r = u / PER_ROW, c = (u % PER_ROW) * VE;
+            const int u = tid + NT * i, r = u / PER_ROW, c = (u % PER_ROW) * VE;
             v[i] = (u < PIECES && r < len) ? ld16(base + r * stride + c) : uint4{0u, 0u, 0u, 0u};
         }
     }
@@ -102,7 +103,7 @@ struct ChunkRows {
     __device__ void stage(float* dst, int ld, int tid) const {
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
-            const int u = tid + kBThreads * i, r = u / PER_ROW, c = (u % PER_ROW) * VE;
+            const int u = tid + NT * i, r = u / PER_ROW, c = (u % PER_ROW) * VE;
             if (u < PIECES)
 #pragma unroll
                 for (int j = 0; j < VE; ++j) dst[r * ld + c + j] = piece_elem<T>(v[i], j);
@@ -500,9 +501,9 @@ struct BwdDiagShape {
     static constexpr int NB = N / 16, PB = P / 16, QB = Q / 16;
     static constexpr size_t cum_bytes = ((size_t)Q * NC * sizeof(CT) + 15) / 16 * 16;
     // local LDS: cum [Q][NC] of CT; floats: X, dY [Q][PS]; B, C [Q][NS]; A, DYX [Q][QS]; w, e
-    // [Q][NC]; e_last [N]; partial sums [kWaves]
+    // [Q][NC]; C o f, B o g [16][NC]; e_last [N]; partial sums [kWaves]
     static constexpr size_t local_lds =
-        cum_bytes + ((size_t)2 * Q * PS + 2 * Q * NS + 2 * Q * QS + 2 * Q * NC + N + kWaves) * 4;
+        cum_bytes + ((size_t)2 * Q * PS + 2 * Q * NS + 2 * Q * QS + 2 * Q * NC + 32 * NC + N + kWaves) * 4;
     // state-terms LDS: cum [Q][NC] of CT; floats: X, dY [Q][PS]; B, C [Q][NS]; e, w, dcum [Q][NC];
     // H, G [N][PS]; e_last, <G_n, H_n> [N]; partial last-token sums [QB][N]
     static constexpr size_t terms_lds =
@@ -551,12 +552,21 @@ __device__ __forceinline__ void diag_chunk_factors(const float* la, CT* cum, flo
 // sum_t' M_t'tn; for the chunk, its local state sum S = sum_s w_sn B_sn x_s^T (into the checkpoint
 // slot), its local gradient sum U = sum_t e_tn C_tn dy_t^T (into the gradient slot), e_last and
 // sum x . dy.  The grid also clears dB and dC, which the state-terms kernel accumulates into.
+//
+// The intra-chunk sums over pairs t >= s split by 16-token blocks.  Across the two blocks (t in the
+// second, s in the first) L_tsn = f_tn g_sn with f_tn = exp(cum_tn - cum_15,n) and g_sn =
+// exp(cum_15,n - cum_sn), both at most 1 because log a <= 0: those terms are products on the matrix
+// cores, (C o f)(B o g)^T for A, DYX^T (C o f) for dB and DYX (B o g) for dC.  Inside a block each
+// L_tsn is one exact exp, used once for A (a thread per pair, summing over n) and once for dB and dC
+// together (a thread per (block, n), summing over the block's pairs).
 template <typename T, int N, int P>
 __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm) {
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     using S = BwdDiagShape<N, P, CT>;
     constexpr int Q = S::Q, QS = S::QS, NS = S::NS, PS = S::PS, NB = S::NB, PB = S::PB, QB = S::QB, NC = S::NC;
-    static_assert(QB * QB == kWaves, "one DYX tile per wave");
+    static_assert(QB == 2 && QB * QB == kWaves, "two 16-token blocks; one DYX tile per wave");
+    static_assert(N <= kWave, "one lane per state dim in the exact block sums");
+    constexpr int kPairs = 16 * 17 / 2;  // pairs t >= s inside one block
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
     const int64_t nch = prm.nchunks;
     {
@@ -584,31 +594,36 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
     float* Cs = Bs + Q * NS;                                  // [Q][NS]
     float* Am = Cs + Q * NS;                                  // A [Q][QS]
     float* Dm = Am + Q * QS;                                  // DYX [Q][QS]
-    float* Wv = Dm + Q * QS;                                  // log a, then w [Q][NC]
-    float* Ev = Wv + Q * NC;                                  // e [Q][NC]
-    float* el = Ev + Q * NC;                                  // e_last [N]
+    float* Wv = Dm + Q * QS;                                  // log a, then w, then the in-block dB [Q][NC]
+    float* Ev = Wv + Q * NC;                                  // e, then the in-block dC [Q][NC]
+    float* Cf = Ev + Q * NC;                                  // C_tn f_tn, t = 16 + row [16][NC]
+    float* Bg = Cf + 16 * NC;                                 // B_sn g_sn [16][NC]
+    float* el = Bg + 16 * NC;                                 // e_last [N]
     float* red = el + N;                                      // [kWaves]
 
-    // the chunk's rows straight into LDS (zeros past the end); sum x . dy on the way
-    const T* xg = static_cast<const T*>(prm.x) + ((b * Tn + t0) * H + h) * P;
-    const T* yg = static_cast<const T*>(prm.dy) + ((b * Tn + t0) * H + h) * P;
-    const T* Bg = static_cast<const T*>(prm.Bm) + ((b * Tn + t0) * G + g) * N;
-    const T* Cg = static_cast<const T*>(prm.Cm) + ((b * Tn + t0) * G + g) * N;
-    const float* lg0 = prm.log_a + ((b * Tn + t0) * H + h) * N;
+    // the chunk's rows into LDS in 16-byte pieces, every load issued first (zeros past the end);
+    // sum x . dy on the way
     float xdy = 0.f;
-    for (int i = tid; i < Q * P; i += kThreads) {
-        const int q = i / P, p = i % P;
-        const float xv = q < len ? to_f32(xg[(int64_t)q * H * P + p]) : 0.f;
-        const float yv = q < len ? to_f32(yg[(int64_t)q * H * P + p]) : 0.f;
-        Xs[q * PS + p] = xv;
-        Ys[q * PS + p] = yv;
-        xdy += xv * yv;
-    }
-    for (int i = tid; i < Q * N; i += kThreads) {
-        const int q = i / N, n = i % N;
-        Bs[q * NS + n] = q < len ? to_f32(Bg[(int64_t)q * G * N + n]) : 0.f;
-        Cs[q * NS + n] = q < len ? to_f32(Cg[(int64_t)q * G * N + n]) : 0.f;
-        Wv[q * NC + n] = q < len ? lg0[(int64_t)q * H * N + n] : 0.f;
+    {
+        const int64_t rowx = (b * Tn + t0) * H + h, rowb = (b * Tn + t0) * G + g;
+        ChunkRows<T, Q, P, kThreads> rx, ry;
+        ChunkRows<T, Q, N, kThreads> rb, rc;
+        ChunkRows<float, Q, N, kThreads> rl;
+        rx.load(static_cast<const T*>(prm.x) + rowx * P, H * P, len, tid);
+        ry.load(static_cast<const T*>(prm.dy) + rowx * P, H * P, len, tid);
+        rb.load(static_cast<const T*>(prm.Bm) + rowb * N, G * N, len, tid);
+        rc.load(static_cast<const T*>(prm.Cm) + rowb * N, G * N, len, tid);
+        rl.load(prm.log_a + rowx * N, H * N, len, tid);
+        rx.stage(Xs, PS, tid);
+        ry.stage(Ys, PS, tid);
+        rb.stage(Bs, NS, tid);
+        rc.stage(Cs, NS, tid);
+        rl.stage(Wv, NC, tid);
+        using RX = ChunkRows<T, Q, P, kThreads>;
+#pragma unroll
+        for (int i = 0; i < RX::PT; ++i)
+#pragma unroll
+            for (int j = 0; j < RX::VE; ++j) xdy += rx.elem(i, j) * ry.elem(i, j);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) xdy += __shfl_xor(xdy, off, kWave);
@@ -623,14 +638,12 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
         for (int i = 0; i < 4; ++i) Dm[(16 * tb + 4 * lg + i) * QS + 16 * sb + l16] = v[i];
     }
     lds_barrier();
+
+    // ---- 1. e_last and sum x . dy out; the local sums S = (w o B)^T X and U = (e o C)^T dY; the
+    //         cross-block operands C o f and B o g
     const int64_t row0 = (b * Tn + t0) * H + h;
     if (tid < N) prm.elw[(unit * nch + c) * N + tid] = el[tid];
-    if (tid == 0) {
-        float s = 0.f;
-        for (int k = 0; k < kWaves; ++k) s += red[k];
-        prm.dD_part[unit * nch + c] = s;
-    }
-    // the local sums S = (w o B)^T X and U = (e o C)^T dY, fp32 on the matrix cores
+    if (tid == 0) prm.dD_part[unit * nch + c] = (red[0] + red[1]) + (red[2] + red[3]);
     {
         float* Sg = prm.ckpt + (unit * nch + c) * (int64_t)N * P;
         float* Ug = prm.gst + (unit * nch + c) * (int64_t)N * P;
@@ -651,51 +664,117 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
             for (int i = 0; i < 4; ++i) out[(16 * nb + 4 * lg + i) * P + 16 * pb + l16] = acc[i];
         }
     }
-    // A_ts = sum_n C_tn B_sn L_tsn on the vector units (the sum over n unrolled by 4 with independent
-    // partial sums)
-    for (int idx = tid; idx < Q * Q; idx += kThreads) {
-        const int t = idx / Q, s = idx % Q;
-        float a[4] = {0.f, 0.f, 0.f, 0.f};
-        if (s <= t) {
+    for (int i = tid; i < 16 * N; i += kThreads) {
+        const int j = i / N, n = i % N;
+        const CT ref = cum[15 * NC + n];
+        Cf[j * NC + n] = Cs[(16 + j) * NS + n] * (float)DiagExp<CT>::ex(cum[(16 + j) * NC + n] - ref);
+        Bg[j * NC + n] = Bs[j * NS + n] * (float)DiagExp<CT>::ex(ref - cum[j * NC + n]);
+    }
+    lds_barrier();
+
+    // ---- 2. waves 0, 1: the in-block dB, dC of block `wave` for dim `lane` (into Wv, Ev);
+    //         waves 2, 3: A, in-block pairs exact, the cross block on the matrix cores, zeros above
+    if (wave < 2) {
+        const int o = 16 * wave, n = lane;
+        if (n < N) {
+            float cv[16], bv[16], db[16], dc[16];
+            CT cm[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                cv[j] = Cs[(o + j) * NS + n];
+                bv[j] = Bs[(o + j) * NS + n];
+                cm[j] = cum[(o + j) * NC + n];
+                db[j] = 0.f;
+                dc[j] = 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 <= t; ++s2) {
+                    const float d = Dm[(o + t) * QS + o + s2] * (float)DiagExp<CT>::ex(cm[t] - cm[s2]);
+                    db[s2] += d * cv[t];
+                    dc[t] += d * bv[s2];
+                }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                Wv[(o + j) * NC + n] = db[j];
+                Ev[(o + j) * NC + n] = dc[j];
+            }
+        }
+    } else {
+        const int u = tid - 2 * kWave;  // 0 .. 127
+        if (wave == 2) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k = 0; k < N; k += 4) acc = mfma_f32(Cf[r * NC + k + gq], Bg[r * NC + k + gq], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Am[(16 + 4 * lg + i) * QS + l16] = acc[i];
+                Am[(4 * lg + i) * QS + 16 + l16] = 0.f;
+            }
+        }
+        for (int z = u; z < 2 * 256; z += 2 * kWave) {
+            const int blk = z / 256, i = (z % 256) / 16, j = z % 16;
+            if (j > i) Am[(16 * blk + i) * QS + 16 * blk + j] = 0.f;
+        }
+        for (int pi = u; pi < 2 * kPairs; pi += 2 * kWave) {
+            const int blk = pi / kPairs, pr = pi % kPairs;
+            int i = (int)((sqrtf(8.f * pr + 1.f) - 1.f) * 0.5f);
+            if ((i + 1) * (i + 2) / 2 <= pr) ++i;
+            if (i * (i + 1) / 2 > pr) --i;
+            const int j = pr - i * (i + 1) / 2;
+            const int t = 16 * blk + i, s2 = 16 * blk + j;
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
             for (int n = 0; n < N; n += 4)
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    a[u] += Cs[t * NS + n + u] * Bs[s * NS + n + u] *
-                            (float)DiagExp<CT>::ex(cum[t * NC + n + u] - cum[s * NC + n + u]);
-        }
-        Am[t * QS + s] = (a[0] + a[1]) + (a[2] + a[3]);
-    }
-    // intra dB, dC and the M sums per (q, n) (fixed-length masked loops, fully unrolled)
-    for (int idx = tid; idx < Q * N; idx += kThreads) {
-        const int q = idx / N, n = idx % N;
-        const CT cq = cum[q * NC + n];
-        float db = 0.f, dc = 0.f;
-#pragma unroll
-        for (int u = 0; u < Q; ++u) {
-            // u in the role of t (q as s), then of s (q as t)
-            const float vb = u >= q ? Dm[u * QS + q] * (float)DiagExp<CT>::ex(cum[u * NC + n] - cq) * Cs[u * NS + n] : 0.f;
-            const float vc = u <= q ? Dm[q * QS + u] * (float)DiagExp<CT>::ex(cq - cum[u * NC + n]) * Bs[u * NS + n] : 0.f;
-            db += vb;
-            dc += vc;
-        }
-        if (q < len) {
-            const int64_t o = (row0 + (int64_t)q * H) * N + n;
-            prm.dBi[o] = db;
-            prm.dCi[o] = dc;
-            // row sum of M at t = q minus its column sum at s = q: C_qn dC_intra - B_qn dB_intra
-            prm.dcumi[o] = Cs[q * NS + n] * dc - Bs[q * NS + n] * db;
+                for (int v = 0; v < 4; ++v)
+                    a[v] += Cs[t * NS + n + v] * Bs[s2 * NS + n + v] *
+                            (float)DiagExp<CT>::ex(cum[t * NC + n + v] - cum[s2 * NC + n + v]);
+            Am[t * QS + s2] = (a[0] + a[1]) + (a[2] + a[3]);
         }
     }
     lds_barrier();
-    // dx_intra = sum_t A_ts dy_t: A(s, t) = Am[t][s]
-    for (int tile = wave; tile < QB * PB; tile += kWaves) {
-        const int sb = tile / PB, pb = tile % PB;
-        const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
+
+    // ---- 3. the cross-block dB (rows s < 16) and dC (rows t >= 16) on the matrix cores, added to the
+    //         in-block sums; every (q, n) written once, with dcum_intra = C dC - B dB; then dx_intra
+    for (int tile = wave; tile < 2 * NB + QB * PB; tile += kWaves) {
+        if (tile < 2 * NB) {
+            const bool isB = tile < NB;
+            const int nb = isB ? tile : tile - NB, n = 16 * nb + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * sb + 4 * lg + i;
-            if (s < len) prm.dxi[(row0 + (int64_t)s * H) * P + 16 * pb + l16] = acc[i];
+            for (int k = 0; k < 16; k += 4) {
+                // dB: A(s, t') = DYX[16 + t'][s], B(t', n) = Cf[t'][n];  dC: A(t', s) = DYX[16 + t'][s], B(s, n) = Bg[s][n]
+                const float av = isB ? Dm[(16 + k + gq) * QS + r] : Dm[(16 + r) * QS + k + gq];
+                const float bv = isB ? Cf[(k + gq) * NC + n - l16 + r] : Bg[(k + gq) * NC + n - l16 + r];
+                acc = mfma_f32(av, bv, acc);
+            }
+            const CT ref = cum[15 * NC + n];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = (isB ? 0 : 16) + 4 * lg + i;
+                float dbv = Wv[q * NC + n], dcv = Ev[q * NC + n];
+                if (isB)
+                    dbv += acc[i] * (float)DiagExp<CT>::ex(ref - cum[q * NC + n]);
+                else
+                    dcv += acc[i] * (float)DiagExp<CT>::ex(cum[q * NC + n] - ref);
+                if (q < len) {
+                    const int64_t o = (row0 + (int64_t)q * H) * N + n;
+                    prm.dBi[o] = dbv;
+                    prm.dCi[o] = dcv;
+                    prm.dcumi[o] = Cs[q * NS + n] * dcv - Bs[q * NS + n] * dbv;
+                }
+            }
+        } else {
+            // dx_intra = sum_t A_ts dy_t: A(s, t) = Am[t][s]
+            const int tt = tile - 2 * NB, sb = tt / PB, pb = tt % PB;
+            const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Am + 16 * sb, 1, QS, Ys + 16 * pb, PS, 1, Q, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s2 = 16 * sb + 4 * lg + i;
+                if (s2 < len) prm.dxi[(row0 + (int64_t)s2 * H) * P + 16 * pb + l16] = acc[i];
+            }
         }
     }
 }
@@ -703,11 +782,11 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
 // The chains over the chunks, in place, one thread per (batch, head, state element) and direction:
 // the checkpoint slots hold S_c on entry and H_c (the state entering chunk c) on exit, from
 // H_0 = init; the gradient slots hold U_c on entry and G_c (the gradient of the state at the end of
-// chunk c) on exit, from dfinal; dinit = e_last,0 G_0 + U_0.  Loads go 8 chunks at a time.
+// chunk c) on exit, from dfinal; dinit = e_last,0 G_0 + U_0.  Loads go 16 chunks at a time.
 template <int N, int P>
 __global__ void __launch_bounds__(kThreads) bwd_scan_diag_kernel(BwdParams prm) {
     constexpr int64_t per = (int64_t)N * P;
-    constexpr int kB = 8;
+    constexpr int kB = 16;
     const int64_t units = prm.batch * prm.nheads;
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= 2 * units * per) return;
@@ -741,26 +820,23 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_diag_kernel(BwdParams prm) 
     if (!fwd && prm.dinit) prm.dinit[unit * per + e] = v;
 }
 
-// The state-terms kernel of the diagonal backward, one workgroup per (batch, head, chunk): with the
-// chunk's H and G from the scan and its intra-chunk terms from the local kernel, the dx, dB, dC and
-// dlog a of the chunk's rows (dB and dC accumulated over the heads of a group).
+// The state-terms kernel of the diagonal backward: with each chunk's H and G from the scan and its
+// intra-chunk terms from the local kernel, the dx, dB, dC and dlog a of the chunk's rows (dB and dC
+// accumulated over the heads of a group).  Persistent: the workgroups of one XCD walk a contiguous
+// range of (batch, head, chunk) items, each loading the next item's rows while it works on the
+// current one.
 template <typename T, int N, int P>
 __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm) {
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     using S = BwdDiagShape<N, P, CT>;
     constexpr int Q = S::Q, NS = S::NS, PS = S::PS, NB = S::NB, PB = S::PB, QB = S::QB, NC = S::NC;
+    static_assert(QB * PB <= kBWaves && QB * NB <= kBWaves, "at most one dx and one dB/dC tile per wave");
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
-    const int64_t nch = prm.nchunks;
-    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd_intra, units * nch);
-    if (work < 0) return;
-    const int64_t unit = work / nch;
-    const int c = (int)(work % nch);
-    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int64_t nch = prm.nchunks, items = units * nch;
+    const int64_t xcd = blockIdx.x % 8, wg_per_xcd = gridDim.x / 8;
+    const int64_t first = xcd * prm.per_xcd_intra, last = min(first + prm.per_xcd_intra, items);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
     const int r = lane % 16, gq = lane / 16;
-    const int64_t t0 = (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, Tn - t0);
-    const int64_t row0 = (b * Tn + t0) * H + h;
 
     extern __shared__ __align__(16) unsigned char smem[];
     CT* cum = reinterpret_cast<CT*>(smem);                    // [Q][NC]
@@ -777,19 +853,54 @@ __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm
     float* ghn = el + N;                                      // <G_n, H_n> [N]
     float* partL = ghn + N;                                   // [QB][N]: sum_s w_sn B_sn (G x_s)_n per 16 rows
 
-    {
-        ChunkRows<T, Q, P> rx, ry;
-        ChunkRows<T, Q, N> rb, rc;
-        ChunkRows<float, N, P> rh, rg;
-        ChunkRows<float, Q, N> rl, rm;
+    ChunkRows<T, Q, P> rx, ry;
+    ChunkRows<T, Q, N> rb, rc;
+    ChunkRows<float, N, P> rh, rg;
+    ChunkRows<float, Q, N> rl, rm;
+    float dxb[4], dbb[4], dcb[4];
+    // every input of item w into registers (this wave's intra-chunk dx, dB and dC elements too)
+    auto load = [&](int64_t w) {
+        const int64_t unit = w / nch, b = unit / H, h = unit % H, g = h / (H / G);
+        const int c = (int)(w % nch);
+        const int64_t t0 = (int64_t)c * Q, row0 = (b * Tn + t0) * H + h;
+        const int len = (int)min((int64_t)Q, Tn - t0);
         rx.load(static_cast<const T*>(prm.x) + row0 * P, H * P, len, tid);
         ry.load(static_cast<const T*>(prm.dy) + row0 * P, H * P, len, tid);
         rb.load(static_cast<const T*>(prm.Bm) + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
         rc.load(static_cast<const T*>(prm.Cm) + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
-        rh.load(prm.ckpt + (unit * nch + c) * (int64_t)N * P, P, N, tid);
-        rg.load(prm.gst + (unit * nch + c) * (int64_t)N * P, P, N, tid);
+        rh.load(prm.ckpt + w * (int64_t)N * P, P, N, tid);
+        rg.load(prm.gst + w * (int64_t)N * P, P, N, tid);
         rl.load(prm.log_a + row0 * N, H * N, len, tid);
         rm.load(prm.dcumi + row0 * N, H * N, len, tid);
+        if (wave < QB * PB) {
+            const int sb = wave / PB, p = 16 * (wave % PB) + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s2 = 16 * sb + 4 * lg + i;
+                dxb[i] = s2 < len ? prm.dxi[(row0 + (int64_t)s2 * H) * P + p] : 0.f;
+            }
+        }
+        if (wave < QB * NB) {
+            const int qb = wave / NB, n = 16 * (wave % NB) + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = 16 * qb + 4 * lg + i;
+                const int64_t o = (row0 + (int64_t)q * H) * N + n;
+                dbb[i] = q < len ? prm.dBi[o] : 0.f;
+                dcb[i] = q < len ? prm.dCi[o] : 0.f;
+            }
+        }
+    };
+    int64_t w = first + blockIdx.x / 8;
+    if (w < last) load(w);
+    T* dxg = static_cast<T*>(prm.dx);
+    for (; w < last; w += wg_per_xcd) {
+        const int64_t unit = w / nch, b = unit / H, h = unit % H, g = h / (H / G);
+        const int c = (int)(w % nch);
+        const int64_t t0 = (int64_t)c * Q, row0 = (b * Tn + t0) * H + h;
+        const int len = (int)min((int64_t)Q, Tn - t0);
+        const float dskip = prm.D ? prm.D[h] : 0.f;
+        lds_barrier();  // the previous item is done with every LDS array
         rx.stage(Xs, PS, tid);
         ry.stage(Ys, PS, tid);
         rb.stage(Bs, NS, tid);
@@ -798,85 +909,78 @@ __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm
         rg.stage(Gs, PS, tid);
         rl.stage(Wv, NC, tid);
         rm.stage(dcum, NC, tid);
-    }
-    lds_barrier();
-    diag_chunk_factors<N, CT>(Wv, cum, Ev, Wv, el, tid);
-    if (tid >= kBThreads - N) {
-        const int n = tid - (kBThreads - N);
-        float acc = 0.f;
+        float cxb[4], cbb[4], ccb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cxb[i] = dxb[i];
+            cbb[i] = dbb[i];
+            ccb[i] = dcb[i];
+        }
+        lds_barrier();
+        if (w + wg_per_xcd < last) load(w + wg_per_xcd);
+        diag_chunk_factors<N, CT>(Wv, cum, Ev, Wv, el, tid);
+        if (tid >= kBThreads - N) {
+            const int n = tid - (kBThreads - N);
+            float acc = 0.f;
 #pragma unroll 8
-        for (int p = 0; p < P; ++p) acc += Gs[n * PS + p] * Hs[n * PS + p];
-        ghn[n] = acc;
-    }
-    lds_barrier();
-
-    // dx = dx_intra + sum_n w_sn B_sn G_np + D dy_s
-    T* dxg = static_cast<T*>(prm.dx);
-    const float dskip = prm.D ? prm.D[h] : 0.f;
-    for (int tile = wave; tile < QB * PB; tile += kBWaves) {
-        const int sb = tile / PB, pb = tile % PB, p = 16 * pb + l16;
-        float base[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * sb + 4 * lg + i;
-            base[i] = s < len ? prm.dxi[(row0 + (int64_t)s * H) * P + p] : 0.f;
+            for (int p = 0; p < P; ++p) acc += Gs[n * PS + p] * Hs[n * PS + p];
+            ghn[n] = acc;
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        lds_barrier();
+
+        // dx = dx_intra + sum_n w_sn B_sn G_np + D dy_s
+        if (wave < QB * PB) {
+            const int sb = wave / PB, pb = wave % PB, p = 16 * pb + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-        for (int k = 0; k < N; k += 4) {
-            const int s = 16 * sb + r, n = k + gq;
-            acc = mfma_f32(Wv[s * NC + n] * Bs[s * NS + n], Gs[n * PS + 16 * pb + r], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * sb + 4 * lg + i;
-            if (s < len) dxg[(row0 + (int64_t)s * H) * P + p] = from_f32<T>(base[i] + acc[i] + dskip * Ys[s * PS + p]);
-        }
-    }
-    // dB, dC out; dcum's state terms
-    for (int tile = wave; tile < QB * NB; tile += kBWaves) {
-        const int qb = tile / NB, nb = tile % NB, n = 16 * nb + l16;
-        float dbi[4], dci[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = 16 * qb + 4 * lg + i;
-            const int64_t o = (row0 + (int64_t)q * H) * N + n;
-            dbi[i] = q < len ? prm.dBi[o] : 0.f;
-            dci[i] = q < len ? prm.dCi[o] : 0.f;
-        }
-        const f32x4 gx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Xs + 16 * qb * PS, PS, 1, Gs + 16 * nb * PS, 1, PS, P,
-                                  lane);
-        const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * qb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS, P,
-                                  lane);
-        float lastp = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = 16 * qb + 4 * lg + i;
-            const float wb = Wv[q * NC + n] * Bs[q * NS + n] * gx[i];
-            const float ec = Ev[q * NC + n] * Cs[q * NS + n] * hd[i];
-            if (q < len) {
-                atomicAdd(prm.dB + ((b * Tn + t0 + q) * G + g) * N + n, dbi[i] + Wv[q * NC + n] * gx[i]);
-                atomicAdd(prm.dC + ((b * Tn + t0 + q) * G + g) * N + n, dci[i] + Ev[q * NC + n] * hd[i]);
+            for (int k = 0; k < N; k += 4) {
+                const int s2 = 16 * sb + r, n = k + gq;
+                acc = mfma_f32(Wv[s2 * NC + n] * Bs[s2 * NS + n], Gs[n * PS + 16 * pb + r], acc);
             }
-            dcum[q * NC + n] += ec - wb;
-            lastp += wb;
-        }
-        lastp += __shfl_xor(lastp, 16, kWave);
-        lastp += __shfl_xor(lastp, 32, kWave);
-        if (lg == 0) partL[qb * N + n] = lastp;
-    }
-    lds_barrier();
-
-    // dlog a per dimension: reverse running sum, the last token's term first
-    if (tid < N) {
-        const int n = tid;
-        float last = el[n] * ghn[n];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) last += partL[qb * N + n];
-        float acc = last;
-        for (int t = Q - 1; t >= 0; --t) {
-            acc += dcum[t * NC + n];
-            if (t < len) prm.dlog_a[(row0 + (int64_t)t * H) * N + n] = acc;
+            for (int i = 0; i < 4; ++i) {
+                const int s2 = 16 * sb + 4 * lg + i;
+                if (s2 < len)
+                    dxg[(row0 + (int64_t)s2 * H) * P + p] = from_f32<T>(cxb[i] + acc[i] + dskip * Ys[s2 * PS + p]);
+            }
+        }
+        // dB, dC out; dcum's state terms
+        if (wave < QB * NB) {
+            const int qb = wave / NB, nb = wave % NB, n = 16 * nb + l16;
+            const f32x4 gx = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Xs + 16 * qb * PS, PS, 1, Gs + 16 * nb * PS, 1, PS,
+                                      P, lane);
+            const f32x4 hd = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, Ys + 16 * qb * PS, PS, 1, Hs + 16 * nb * PS, 1, PS,
+                                      P, lane);
+            float lastp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = 16 * qb + 4 * lg + i;
+                const float wb = Wv[q * NC + n] * Bs[q * NS + n] * gx[i];
+                const float ec = Ev[q * NC + n] * Cs[q * NS + n] * hd[i];
+                if (q < len) {
+                    atomicAdd(prm.dB + ((b * Tn + t0 + q) * G + g) * N + n, cbb[i] + Wv[q * NC + n] * gx[i]);
+                    atomicAdd(prm.dC + ((b * Tn + t0 + q) * G + g) * N + n, ccb[i] + Ev[q * NC + n] * hd[i]);
+                }
+                dcum[q * NC + n] += ec - wb;
+                lastp += wb;
+            }
+            lastp += __shfl_xor(lastp, 16, kWave);
+            lastp += __shfl_xor(lastp, 32, kWave);
+            if (lg == 0) partL[qb * N + n] = lastp;
+        }
+        lds_barrier();
+
+        // dlog a per dimension: reverse running sum, the last token's term first
+        if (tid < N) {
+            const int n = tid;
+            float last2 = el[n] * ghn[n];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) last2 += partL[qb * N + n];
+            float acc = last2;
+            for (int t = Q - 1; t >= 0; --t) {
+                acc += dcum[t * NC + n];
+                if (t < len) prm.dlog_a[(row0 + (int64_t)t * H) * N + n] = acc;
+            }
         }
     }
 }
@@ -886,12 +990,20 @@ __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm
 // kernel on the diagonal one.)
 __global__ void __launch_bounds__(kThreads) bwd_reduce_kernel(const float* part, float* dD, int64_t batch, int64_t H,
                                                               int64_t nper) {
-    const int64_t h = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (h >= H) return;
+    // one workgroup per head
+    const int64_t h = blockIdx.x;
     float s = 0.f;
-    for (int64_t b = 0; b < batch; ++b)
-        for (int64_t k = 0; k < nper; ++k) s += part[(b * H + h) * nper + k];
-    dD[h] = s;
+    for (int64_t i = threadIdx.x; i < batch * nper; i += kThreads) s += part[((i / nper) * H + h) * nper + i % nper];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    __shared__ float red[kWaves];
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = s;
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        float t = 0.f;
+        for (int k = 0; k < kWaves; ++k) t += red[k];
+        dD[h] = t;
+    }
 }
 
 __global__ void __launch_bounds__(kThreads) zero_kernel(float* a, int64_t n, float* b2, int64_t n2) {
@@ -931,7 +1043,7 @@ int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
                       stream, p))
             return -1;
     }
-    if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)((bl.p.nheads + kThreads - 1) / kThreads)),
+    if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)bl.p.nheads),
                           dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads,
                           (int64_t)1))
         return -1;
@@ -1037,11 +1149,13 @@ int launch_backward_diag_t(const BackwardLaunch& bl, hipStream_t stream) {
         if (!launch_k(bl, k, bwd_scan_diag_kernel<N, P>, dim3((unsigned)((scan_threads + kThreads - 1) / kThreads)),
                       dim3(kThreads), 0, stream, p))
             return -1;
-        if (work > 0 && !launch_k(bl, k, bwd_terms_diag_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd_intra)),
-                                  dim3(kBThreads), S::terms_lds, stream, p))
+        // (persistent: up to kBwdCUs workgroups, a multiple of 8, over the items)
+        const int64_t wgs = std::min<int64_t>(kBwdCUs, (work + 7) / 8 * 8);
+        if (work > 0 && !launch_k(bl, k, bwd_terms_diag_kernel<T, N, P>, dim3((unsigned)wgs), dim3(kBThreads),
+                                  S::terms_lds, stream, p))
             return -1;
     }
-    if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)((bl.p.nheads + kThreads - 1) / kThreads)),
+    if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)bl.p.nheads),
                           dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads,
                           (int64_t)bl.p.nchunks))
         return -1;
