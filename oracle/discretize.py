@@ -70,19 +70,20 @@ def sigmoid(v):
 
 
 def backward_dt(adj, x, dt, A_log, Bm, Cm, D=None, dt_bias=None, scale_input=True, init_state=None, dy=None,
-                dfinal=None):
-    """Gradients of <dy, y> + <dfinal, final> for ``forward_dt`` (scalar decay), by the chain rule
-    through the discretisation on top of the recurrence's adjoint ``adj`` (``oracle.backward``):
-    with u = dt + bias, Delta = softplus(u), log a = Delta A (A = -exp(A_log)) and the recurrence
-    run on x_in = Delta x (scale_input) or x,
+                dfinal=None, diag=False):
+    """Gradients of <dy, y> + <dfinal, final> for ``forward_dt``, by the chain rule through the
+    discretisation on top of the recurrence's adjoint ``adj`` (``oracle.backward``): with
+    u = dt + bias, Delta = softplus(u), log a = Delta A (A = -exp(A_log), [H] or with ``diag``
+    [H,N]) and the recurrence run on x_in = Delta x (scale_input) or x,
         dx       = Delta dx_in (or dx_in) + D dy
-        dDelta   = dlog_a A + sum_p dx_in x      (the second term with scale_input only)
+        dDelta   = sum_n dlog_a A + sum_p dx_in x   (the sum over n for diag only; the second term
+                                                      with scale_input only)
         ddt      = dDelta sigmoid(u),   ddt_bias = sum_{b,t} ddt,   dA_log = sum_{b,t} dlog_a log a
         dD       = sum_{b,t,p} dy x
     and dB, dC, dinit as the adjoint gives them.  Returns a dict of float64 arrays."""
     x = np.asarray(x, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
-    delta, log_a = discretize(dt, A_log, dt_bias, False)
+    delta, log_a = discretize(dt, A_log, dt_bias, diag)
     u = np.asarray(dt, dtype=np.float64)
     if dt_bias is not None:
         u = u + np.asarray(dt_bias, dtype=np.float64)[None, None, :]
@@ -93,7 +94,10 @@ def backward_dt(adj, x, dt, A_log, Bm, Cm, D=None, dt_bias=None, scale_input=Tru
     dx = dxin * delta[..., None] if scale_input else dxin.copy()
     if D is not None:
         dx = dx + np.asarray(D, dtype=np.float64)[None, None, :, None] * dy
-    ddelta = g["dlog_a"] * A[None, None, :]
+    if diag:
+        ddelta = np.sum(g["dlog_a"] * A[None, None, :, :], axis=-1)
+    else:
+        ddelta = g["dlog_a"] * A[None, None, :]
     if scale_input:
         ddelta = ddelta + np.sum(dxin * x, axis=-1)
     ddt = ddelta * sigmoid(u)

@@ -108,33 +108,36 @@ def pin_bwd_dt_finite_differences(orc, adj, disc):
     """The discretised form's gradients (disc.backward_dt on the adjoint adj) against central
     differences of L = <dy, y> + <dfinal, final> evaluated with disc.forward_dt on the forward
     oracle alone, along a random direction in each of x, dt, A_log, dt_bias, B, C, D and init;
-    with and without the input scale."""
+    with and without the input scale, for one rate per head (A_log [H]) and one per head and state
+    dimension (A_log [H,N])."""
     rng = np.random.default_rng(81)
     nb, T, H, G, P, N = 2, 9, 4, 2, 3, 5
     x = rng.standard_normal((nb, T, H, P))
     Bm = rng.standard_normal((nb, T, G, N)) / np.sqrt(N)
     Cm = rng.standard_normal((nb, T, G, N)) / np.sqrt(N)
-    inp = dict(x=x, dt=rng.standard_normal((nb, T, H)) - 1.0, A_log=rng.uniform(0.0, 2.0, H),
-               dt_bias=rng.standard_normal(H) * 0.5, Bm=Bm, Cm=Cm, D=rng.standard_normal(H),
-               init=rng.standard_normal((nb, H, N, P)))
+    base = dict(x=x, dt=rng.standard_normal((nb, T, H)) - 1.0, dt_bias=rng.standard_normal(H) * 0.5, Bm=Bm, Cm=Cm,
+                D=rng.standard_normal(H), init=rng.standard_normal((nb, H, N, P)))
     dy = rng.standard_normal((nb, T, H, P))
     dfin = rng.standard_normal((nb, H, N, P))
     names = dict(x="dx", dt="ddt", A_log="dA_log", dt_bias="ddt_bias", Bm="dB", Cm="dC", D="dD", init="dinit")
-    for scale in (True, False):
-        def loss(d):
-            y, fin = disc.forward_dt(orc, d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"],
-                                     dt_bias=d["dt_bias"], scale_input=scale, init_state=d["init"])
-            return float(np.sum(dy * y) + np.sum(dfin * fin))
-        g = disc.backward_dt(adj, inp["x"], inp["dt"], inp["A_log"], inp["Bm"], inp["Cm"], inp["D"],
-                             dt_bias=inp["dt_bias"], scale_input=scale, init_state=inp["init"], dy=dy, dfinal=dfin)
-        eps = 1e-6
-        for name, gname in names.items():
-            v = rng.standard_normal(np.shape(inp[name]))
-            fd = (loss(dict(inp, **{name: inp[name] + eps * v})) - loss(dict(inp, **{name: inp[name] - eps * v}))) \
-                / (2 * eps)
-            an = float(np.sum(g[gname] * v))
-            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), "%s (scale=%d): fd %.12g chain rule %.12g" % (
-                gname, scale, fd, an)
+    for diag in (False, True):
+        inp = dict(base, A_log=rng.uniform(0.0, 2.0, (H, N) if diag else H))
+        for scale in (True, False):
+            def loss(d):
+                y, fin = disc.forward_dt(orc, d["x"], d["dt"], d["A_log"], d["Bm"], d["Cm"], d["D"],
+                                         dt_bias=d["dt_bias"], scale_input=scale, init_state=d["init"], diag=diag)
+                return float(np.sum(dy * y) + np.sum(dfin * fin))
+            g = disc.backward_dt(adj, inp["x"], inp["dt"], inp["A_log"], inp["Bm"], inp["Cm"], inp["D"],
+                                 dt_bias=inp["dt_bias"], scale_input=scale, init_state=inp["init"], dy=dy,
+                                 dfinal=dfin, diag=diag)
+            eps = 1e-6
+            for name, gname in names.items():
+                v = rng.standard_normal(np.shape(inp[name]))
+                fd = (loss(dict(inp, **{name: inp[name] + eps * v})) - loss(dict(inp, **{name: inp[name] - eps * v}))) \
+                    / (2 * eps)
+                an = float(np.sum(g[gname] * v))
+                assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), "%s (diag=%d, scale=%d): fd %.12g chain rule %.12g" % (
+                    gname, diag, scale, fd, an)
 
 
 BWD_DT_PINS = [pin_bwd_dt_finite_differences]
