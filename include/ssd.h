@@ -202,8 +202,10 @@ int ssd_backward(const ssd_dims* dims, const void* x, const float* log_a, const 
                  const float* dfinal, void* dx, float* dlog_a, float* dB, float* dC, float* dD,
                  float* dinit, void* workspace, size_t workspace_bytes, void* stream);
 
-/* ssd_backward with per-launch timing events, as ssd_forward_profiled.  Launch order: zeroing of
- * dB and dC, the state checkpoints, the reverse walk, the dD reduction (when dD is requested). */
+/* ssd_backward with per-launch timing events, as ssd_forward_profiled.  Launch order, scalar
+ * decay: zeroing of dB and dC, the state checkpoints, the reverse walk, the dD reduction (when dD
+ * is requested).  Diagonal decay: the per-chunk local kernel (which also clears dB and dC), the
+ * scan over chunks, the state-terms kernel, the dD reduction (when dD is requested). */
 int ssd_backward_profiled(const ssd_dims* dims, const void* x, const float* log_a, const void* B,
                           const void* C, const float* D, const float* init_state, const void* dy,
                           const float* dfinal, void* dx, float* dlog_a, float* dB, float* dC,
@@ -211,14 +213,15 @@ int ssd_backward_profiled(const ssd_dims* dims, const void* x, const float* log_
                           void* stream, void* const* events, int n_events, int* n_launches);
 
 /*
- * The backward pass of ssd_forward_dt (scalar decay): the gradients of <dy, y> + <dfinal,
- * final_state> with respect to x, dt, A_log, dt_bias, B, C, D and init_state, by the chain rule
- * through the discretisation (Delta = softplus(dt + bias), log a = -Delta exp(A_log), and with
- * scale_input the input term Delta B x^T) around ssd_backward.
- *   ddt [B,T,H] fp32 (required); dA_log [H] and ddt_bias [H] fp32 (NULL to skip each);
+ * The backward pass of ssd_forward_dt: the gradients of <dy, y> + <dfinal, final_state> with
+ * respect to x, dt, A_log, dt_bias, B, C, D and init_state, by the chain rule through the
+ * discretisation (Delta = softplus(dt + bias), log a = -Delta exp(A_log), and with scale_input the
+ * input term Delta B x^T) around ssd_backward.
+ *   A_log [H] (scalar decay) or [H,N] (dims->decay = SSD_DECAY_DIAG), as for ssd_forward_dt.
+ *   ddt [B,T,H] fp32 (required); dA_log (A_log's shape) and ddt_bias [H] fp32 (NULL to skip each);
  *   dx, dB, dC, dD, dinit as for ssd_backward.
  *   workspace: at least ssd_backward_dt_workspace_bytes(dims, scale_input) bytes.
- * Supported shapes and dtypes as ssd_backward, scalar decay only.
+ * Supported shapes and dtypes as ssd_backward, for either decay kind.
  */
 size_t ssd_backward_dt_workspace_bytes(const ssd_dims* dims, int scale_input);
 

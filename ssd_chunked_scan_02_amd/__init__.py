@@ -386,17 +386,19 @@ def ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input: b
                     init_state=None, dfinal=None, want_dD=True, want_dinit=True, workspace=None,
                     stream=None):
     """Run ``ssd_backward_dt``: gradients of <dy, y> + <dfinal, final_state> for ssd_forward_dt
-    (scalar decay).  Returns a dict: dx (dtype of x), ddt [B,T,H], dA_log [H], ddt_bias [H] (or
-    None without dt_bias), dB, dC (fp32), dD (or None), dinit (or None)."""
+    (scalar decay with A_log [H], diagonal with A_log [H,N]).  Returns a dict: dx (dtype of x),
+    ddt [B,T,H], dA_log (A_log's shape), ddt_bias [H] (or None without dt_bias), dB, dC (fp32),
+    dD (or None), dinit (or None)."""
     bsz, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     if x.dtype not in _DTYPE_CODE:
         raise TypeError("x must be float32 or bfloat16")
-    dims = Dims(bsz, T, H, G, P, N, _DTYPE_CODE[x.dtype], SSD_DECAY_SCALAR)
+    decay = SSD_DECAY_DIAG if A_log.dim() == 2 else SSD_DECAY_SCALAR
+    dims = Dims(bsz, T, H, G, P, N, _DTYPE_CODE[x.dtype], decay)
     dev = x.device
     _check(x, "x", (bsz, T, H, P), x.dtype, dev)
     _check(dt, "dt", (bsz, T, H), torch.float32, dev)
-    _check(A_log, "A_log", (H,), torch.float32, dev)
+    _check(A_log, "A_log", (H, N) if decay == SSD_DECAY_DIAG else (H,), torch.float32, dev)
     _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
     _check(B, "B", (bsz, T, G, N), x.dtype, dev)
     _check(C, "C", (bsz, T, G, N), x.dtype, dev)
@@ -405,7 +407,7 @@ def ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input: b
     _check(init_state, "init_state", (bsz, H, N, P), torch.float32, dev)
     _check(dfinal, "dfinal", (bsz, H, N, P), torch.float32, dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = dict(dx=torch.empty_like(x), ddt=torch.empty((bsz, T, H), **f32), dA_log=torch.empty(H, **f32),
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty((bsz, T, H), **f32), dA_log=torch.empty(A_log.shape, **f32),
                ddt_bias=torch.empty(H, **f32) if dt_bias is not None else None,
                dB=torch.empty((bsz, T, G, N), **f32), dC=torch.empty((bsz, T, G, N), **f32),
                dD=torch.empty(H, **f32) if want_dD else None,

@@ -307,9 +307,9 @@ int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, 
 }
 
 size_t ssd_backward_dt_workspace_bytes(const ssd_dims* d, int scale_input) {
-    if (check_backward(d) != SSD_OK || d->decay != SSD_DECAY_SCALAR || d->batch == 0) return 0;
+    if (check_backward(d) != SSD_OK || d->batch == 0) return 0;
     return ssd::dt_backward_layout(d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim,
-                                   d->dtype == SSD_BF16 ? 2 : 4, scale_input != 0)
+                                   d->dtype == SSD_BF16 ? 2 : 4, scale_input != 0, d->decay)
         .total;
 }
 
@@ -320,7 +320,6 @@ int ssd_backward_dt(const ssd_dims* d, const void* x, const float* dt, const flo
                     void* stream) {
     int rc = check_backward(d);
     if (rc != SSD_OK) return rc;
-    if (d->decay != SSD_DECAY_SCALAR) return SSD_ERR_UNSUPPORTED;
     const bool has_tokens = d->batch > 0 && d->seqlen > 0;
     if (has_tokens && (!x || !dt || !A_log || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_INVALID;
     if (!A_log && (dA_log || ddt_bias)) return SSD_ERR_INVALID;
@@ -332,6 +331,7 @@ int ssd_backward_dt(const ssd_dims* d, const void* x, const float* dt, const flo
     if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
     ssd::BackwardLaunch bl{};
     bl.dtype = d->dtype;
+    bl.decay = d->decay;
     bl.headdim = d->headdim;
     bl.dstate = d->dstate;
     ssd::BwdParams& p = bl.p;

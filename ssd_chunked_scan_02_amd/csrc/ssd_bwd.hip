@@ -1059,30 +1059,31 @@ int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
 //   dD = sum_{b,t,p} dy x.
 // CT (double for fp32 inputs, float for bf16) carries the per-row arithmetic.
 
-// Per (b, t, h) row: log a into la, and with the input scale Delta x into xs.
+// Per (b, t, h) row: its K log a values (K = 1 scalar decay, N diagonal) into la, and with the input
+// scale Delta x into xs.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) disc_rows_kernel(const float* dt, const float* dt_bias, const float* A_log,
                                                              const T* x, float* la, T* xs, int64_t rows, int64_t H,
-                                                             int P) {
+                                                             int P, int K) {
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (r >= rows) return;
     const int64_t h = r % H;
     const CT u = (CT)dt[r] + (dt_bias ? (CT)dt_bias[h] : (CT)0);
     const CT delta = softplus_ct(u);
-    la[r] = (float)(-delta * exp((CT)A_log[h]));
+    for (int n = 0; n < K; ++n) la[r * K + n] = (float)(-delta * exp((CT)A_log[h * K + n]));
     if (xs)
         for (int p = 0; p < P; ++p) xs[r * P + p] = from_f32<T>((float)(delta * (CT)to_f32(x[r * P + p])));
 }
 
-// Per row: dx, ddt, and the row terms of dA_log (dlog a log a) and dD (dy . x).
+// Per row: dx, ddt, and the row terms of dA_log (dlog a log a, K per row) and dD (dy . x).
 template <typename T>
 __global__ void __launch_bounds__(kThreads) disc_grad_rows_kernel(const float* dt, const float* dt_bias,
                                                                   const float* A_log, const float* D, const T* x,
                                                                   const T* dy, const T* dxs, const float* la,
                                                                   const float* dla, int scale, T* dx, float* ddt,
                                                                   float* rowA, float* rowD, int64_t rows, int64_t H,
-                                                                  int P) {
+                                                                  int P, int K) {
     using CT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (r >= rows) return;
@@ -1097,10 +1098,13 @@ __global__ void __launch_bounds__(kThreads) disc_grad_rows_kernel(const float* d
         xdy += xv * yv;
         dx[r * P + p] = from_f32<T>((float)((scale ? delta * gv : gv) + dskip * yv));
     }
-    const CT dlog = (CT)dla[r];
-    const CT ddelta = -exp((CT)A_log[h]) * dlog + (scale ? xdx : (CT)0);
+    CT ddelta = scale ? xdx : (CT)0;
+    for (int n = 0; n < K; ++n) {
+        const CT dlog = (CT)dla[r * K + n];
+        ddelta += -exp((CT)A_log[h * K + n]) * dlog;
+        rowA[r * K + n] = (float)(dlog * (CT)la[r * K + n]);
+    }
     ddt[r] = (float)(ddelta / (1 + exp(-u)));
-    rowA[r] = (float)(dlog * (CT)la[r]);
     rowD[r] = (float)xdy;
 }
 
@@ -1251,19 +1255,20 @@ int launch_backward(const BackwardLaunch& bl, hipStream_t stream) {
 int backward_chunk() { return kBQ; }
 
 DtBackwardLayout dt_backward_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int elem_bytes,
-                                    bool scale_input) {
+                                    bool scale_input, int decay) {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     const size_t rows = (size_t)batch * (size_t)seqlen * (size_t)nheads;
+    const size_t K = decay == 1 ? (size_t)N : 1;
     DtBackwardLayout l;
     size_t off = 0;
-    l.la = off; off = up(off + rows * 4);
+    l.la = off; off = up(off + rows * K * 4);
     l.xs = off; if (scale_input) off = up(off + rows * P * elem_bytes);
     l.dxs = off; off = up(off + rows * P * elem_bytes);
-    l.dla = off; off = up(off + rows * 4);
+    l.dla = off; off = up(off + rows * K * 4);
     l.ddt_rows = 0;  // (the caller's ddt holds them)
-    l.rowA = off; off = up(off + rows * 4);
+    l.rowA = off; off = up(off + rows * K * 4);
     l.rowD = off; off = up(off + rows * 4);
-    l.inner = off; off += backward_workspace_bytes(batch, nheads, seqlen, N, P, 0);
+    l.inner = off; off += backward_workspace_bytes(batch, nheads, seqlen, N, P, decay);
     l.total = off;
     return l;
 }
@@ -1272,7 +1277,9 @@ int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipSt
     const int64_t H = bl0.p.nheads, rows = bl0.p.batch * bl0.p.seqlen * H;
     const int P = (int)bl0.headdim;
     const int eb = bl0.dtype == 0 ? 4 : 2;
-    const DtBackwardLayout l = dt_backward_layout(bl0.p.batch, H, bl0.p.seqlen, (int)bl0.dstate, P, eb, a.scale_input != 0);
+    const int K = bl0.decay == 1 ? (int)bl0.dstate : 1;
+    const DtBackwardLayout l =
+        dt_backward_layout(bl0.p.batch, H, bl0.p.seqlen, (int)bl0.dstate, P, eb, a.scale_input != 0, bl0.decay);
     char* ws = static_cast<char*>(a.workspace);
     float* la = reinterpret_cast<float*>(ws + l.la);
     void* xs = a.scale_input ? static_cast<void*>(ws + l.xs) : nullptr;
@@ -1284,10 +1291,10 @@ int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipSt
     if (rows > 0) {
         if (bl0.dtype == 0)
             hipLaunchKernelGGL(disc_rows_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias, a.A_log,
-                               static_cast<const float*>(a.x), la, static_cast<float*>(xs), rows, H, P);
+                               static_cast<const float*>(a.x), la, static_cast<float*>(xs), rows, H, P, K);
         else
             hipLaunchKernelGGL(disc_rows_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias,
-                               a.A_log, static_cast<const __bf16*>(a.x), la, static_cast<__bf16*>(xs), rows, H, P);
+                               a.A_log, static_cast<const __bf16*>(a.x), la, static_cast<__bf16*>(xs), rows, H, P, K);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     // the backward pass on (x_in, log a) with no skip term; dx_in and dlog a into the workspace
@@ -1298,7 +1305,7 @@ int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipSt
     bl.p.dx = dxs;
     bl.p.dlog_a = dla;
     bl.p.dD = nullptr;
-    bind_backward_workspace(bl.p, ws + l.inner, (int)bl0.dstate, P, 0);
+    bind_backward_workspace(bl.p, ws + l.inner, (int)bl0.dstate, P, bl0.decay);
     const int rc = launch_backward(bl, stream);
     if (rc != 0) return rc;
     if (rows > 0) {
@@ -1306,17 +1313,18 @@ int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipSt
             hipLaunchKernelGGL(disc_grad_rows_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias,
                                a.A_log, a.D, static_cast<const float*>(a.x), static_cast<const float*>(a.dy),
                                static_cast<const float*>(dxs), la, dla, a.scale_input, static_cast<float*>(a.dx), a.ddt,
-                               rowA, rowD, rows, H, P);
+                               rowA, rowD, rows, H, P, K);
         else
             hipLaunchKernelGGL(disc_grad_rows_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, stream, a.dt, a.dt_bias,
                                a.A_log, a.D, static_cast<const __bf16*>(a.x), static_cast<const __bf16*>(a.dy),
                                static_cast<const __bf16*>(dxs), la, dla, a.scale_input, static_cast<__bf16*>(a.dx),
-                               a.ddt, rowA, rowD, rows, H, P);
+                               a.ddt, rowA, rowD, rows, H, P, K);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     const int64_t bt = bl0.p.batch * bl0.p.seqlen;
     if (a.ddt_bias) hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, stream, a.ddt, a.ddt_bias, bt, H);
-    if (a.dA_log) hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, stream, rowA, a.dA_log, bt, H);
+    if (a.dA_log)
+        hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)(H * K)), dim3(kThreads), 0, stream, rowA, a.dA_log, bt, H * K);
     if (a.dD) hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, stream, rowD, a.dD, bt, H);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -56,7 +56,8 @@ int backward_chunk();
 int launch_backward(const BackwardLaunch& bl, hipStream_t stream);
 
 // The discretised form's backward (ssd_backward_dt): its own arguments, and its workspace (log a,
-// the scaled input, dx_in, dlog a, per-row sums, then the backward pass's own workspace).
+// the scaled input, dx_in, dlog a, per-row sums (per row and state dim for dA_log with the
+// diagonal decay), then the backward pass's own workspace).
 struct DtBackwardArgs {
     const void* x;
     const float* dt;
@@ -76,7 +77,7 @@ struct DtBackwardLayout {
     size_t la, xs, dxs, dla, ddt_rows, rowA, rowD, inner, total;
 };
 DtBackwardLayout dt_backward_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int elem_bytes,
-                                    bool scale_input);
+                                    bool scale_input, int decay);
 int launch_backward_dt(const BackwardLaunch& bl, const DtBackwardArgs& a, hipStream_t stream);
 
 }  // namespace ssd

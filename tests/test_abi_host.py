@@ -299,3 +299,20 @@ def test_backward_rejects_bad_arguments(lib):
     assert call_backward(lib, mamba2_dims(dstate=256)) == ssd.SSD_ERR_UNSUPPORTED
     need = ssd.ssd_backward_workspace_bytes(mamba2_dims())
     assert call_backward(lib, mamba2_dims(), ws_bytes=need - 1) == ssd.SSD_ERR_INVALID
+
+
+def test_backward_dt_workspace_bytes(lib):
+    # the front-end's rows (log a, dx_in, dlog a and the dA_log terms: K = 1 scalar, N diagonal, per
+    # row; the scaled input with scale_input; dD terms), each on a 256-byte boundary, then the
+    # backward pass's own workspace
+    up = lambda v: (v + 255) // 256 * 256
+    fn = lib.ssd_backward_dt_workspace_bytes
+    for decay, N, P in ((0, 128, 64), (1, 64, 32)):
+        d = mamba2_dims(batch=2, seqlen=300, nheads=4, decay=decay, dstate=N, headdim=P)
+        rows, K = 2 * 300 * 4, (N if decay else 1)
+        inner = ssd.ssd_backward_workspace_bytes(d)
+        own = up(rows * K * 4) + up(rows * P * 2) + up(rows * K * 4) + up(rows * K * 4) + up(rows * 4)
+        assert fn(ctypes.byref(d), 0) == own + inner
+        assert fn(ctypes.byref(d), 1) == own + up(rows * P * 2) + inner
+    assert fn(ctypes.byref(mamba2_dims(decay=1)), 1) == 0                  # diagonal decay: N <= 64
+    assert fn(ctypes.byref(mamba2_dims(batch=0)), 1) == 0

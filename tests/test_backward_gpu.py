@@ -94,6 +94,10 @@ DT_CASES = [
     ("mamba2_layer", dict(batch=2, seqlen=300, nheads=4, init=True), "bf16"),
     ("gqa_decode", dict(batch=1, seqlen=700, nheads=8, ngroups=2, decode_steps=0, init=True), "bf16-gqa"),
     ("tiny_fp32", dict(seqlen=200, nheads=2, skip=True, init=True, a_log="uniform16", dt_mean=-1.0), "fp32"),
+    # diagonal decay: A_log [H,N]
+    ("diag_multiscale", dict(batch=2, seqlen=300, nheads=3, a_log="rand_hn", init=True), "diag-bf16"),
+    ("diag_multiscale", dict(batch=1, seqlen=170, nheads=2, dstate=32, headdim=16, dtype="fp32", a_log="rand_hn",
+                             init=True), "diag-fp32"),
 ]
 
 
@@ -111,19 +115,20 @@ def test_backward_dt_matches_chain_rule(name, over, label, scale):
     got = ssd.ssd_backward_dt(g["x"], g["dt"], g["A_log"], g["B"], g["C"], g["dy"], g.get("D"), dt_bias=bias.cuda(),
                               scale_input=scale, init_state=g.get("init_state"), dfinal=g["dfinal"])
     torch.cuda.synchronize()
+    diag = cfg["decay"] == "diag"
     want = oracle.discretize.backward_dt(oracle.backward.default_adjoint(), f64(inp["x"]), f64(inp["dt"]),
                                          f64(inp["A_log"]), f64(inp["B"]), f64(inp["C"]), f64(inp.get("D")),
                                          dt_bias=f64(bias), scale_input=scale, init_state=f64(inp.get("init_state")),
-                                         dy=f64(og["dy"]), dfinal=f64(og["dfinal"]))
+                                         dy=f64(og["dy"]), dfinal=f64(og["dfinal"]), diag=diag)
     tol = TOL[cfg["dtype"]]
     errs = {k: rel_l2(got[k].double().cpu().numpy(), want[k]) for k in ("dx", "ddt", "dB", "dC", "dD", "dinit")}
     # dA_log and ddt_bias are sums over every (batch, token) of terms of both signs: their error is
     # measured against the size of the terms (sum of magnitudes per head), since cancellation in
     # the sum can leave it far smaller than the rounding its terms carry
-    la = oracle.discretize.discretize(f64(inp["dt"]), f64(inp["A_log"]), f64(bias))[1]
+    la = oracle.discretize.discretize(f64(inp["dt"]), f64(inp["A_log"]), f64(bias), diag)[1]
     mag = dict(ddt_bias=np.abs(want["ddt"]).sum(axis=(0, 1)))
     # the dA_log terms are dlog_a log a: dlog_a from the adjoint on the same inputs
-    xin = f64(inp["x"]) * oracle.discretize.discretize(f64(inp["dt"]), f64(inp["A_log"]), f64(bias))[0][..., None] \
+    xin = f64(inp["x"]) * oracle.discretize.discretize(f64(inp["dt"]), f64(inp["A_log"]), f64(bias), diag)[0][..., None] \
         if scale else f64(inp["x"])
     adj = oracle.backward.backward(xin, la, f64(inp["B"]), f64(inp["C"]), None, f64(inp.get("init_state")),
                                    f64(og["dy"]), f64(og["dfinal"]))
