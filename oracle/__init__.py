@@ -18,10 +18,14 @@ Contents
                         ``discretize.forward_dt`` runs the recurrence in that form.
   backward              the adjoint of the recurrence in fp64 (plain C, ``ssd_oracle_bwd.c``):
                         the gradients of <dy, y> + <dfinal, final> with respect to every input.
+  varlen                packed variable-length batches: every sequence of a packed batch
+                        through the recurrence by itself (``varlen.forward_varlen``).
 """
 from .recurrence import Oracle, build, default_oracle, forward, default_threads
 from .chunked import chunked_forward
 from . import discretize
 from . import backward
+from . import varlen
 
-__all__ = ["Oracle", "build", "default_oracle", "forward", "default_threads", "chunked_forward", "discretize", "backward"]
+__all__ = ["Oracle", "build", "default_oracle", "forward", "default_threads", "chunked_forward", "discretize", "backward",
+           "varlen"]
