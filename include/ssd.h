@@ -174,6 +174,35 @@ int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float
                 const void* C_t, const float* D, void* y_t, void* stream);
 
 /*
+ * Packed variable-length batch.  dims->batch sequences lie one after another on one token axis
+ * of total_tokens tokens: x [total,H,P], log_a [total,H] or [total,H,N], B, C [total,G,N] and
+ * y [total,H,P], in the layouts and types of ssd_forward with the batch axis folded into the token
+ * axis.  Sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1.  Each sequence runs the
+ * recurrence by itself, from init_state[b] (zeros when init_state is NULL) to final_state[b]
+ * (init_state, final_state [batch,H,N,P] fp32, optional): nothing passes from one sequence to the
+ * next (llms.blog "State Space Models and Mamba", "Continuous-to-Discrete Discretization": the
+ * recurrence starts from its initial state for each sequence).
+ *   cu_seqlens: DEVICE memory, batch + 1 int64 values, 8-byte aligned, non-decreasing from 0 to
+ *     total_tokens.  The kernels read it: a sequence's tokens are clamped into [0, total_tokens)
+ *     and to its first dims->seqlen tokens, so malformed offsets give wrong outputs but never an
+ *     access outside the tensors or the workspace.  The host does not read it.
+ *   dims->seqlen: a bound on every sequence's length (the longest one's length is the natural
+ *     choice); it sizes the workspace, which is that of a [batch][seqlen] batch without the
+ *     segmented walks.  Tokens past that bound are neither read nor written.
+ *   chunk, shapes, dtypes and decay kinds as ssd_forward; no discretisation front-end.
+ *   events, n_events, n_launches: as ssd_forward_profiled (NULL, 0, NULL: no timing).
+ * Returns as ssd_forward; SSD_ERR_INVALID also for total_tokens < 0 or a NULL or misaligned
+ * cu_seqlens with batch > 0.
+ */
+size_t ssd_forward_varlen_workspace_bytes(const ssd_dims* dims, int chunk);
+
+int ssd_forward_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                       const void* x, const float* log_a, const void* B, const void* C,
+                       const float* D, int chunk, const float* init_state, void* y,
+                       float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                       void* const* events, int n_events, int* n_launches);
+
+/*
  * The backward pass of ssd_forward: the gradients of L = <dy, y> + <dfinal,
  * final_state> with respect to every input, for training.  It is the chain rule through the
  * recurrence above, evaluated chunk by chunk (the state entering every chunk is recomputed into

@@ -105,6 +105,11 @@ def load_library():
         lib.ssd_backward_dt_workspace_bytes.restype = sz
         lib.ssd_backward_dt.argtypes = [dp, vp, vp, vp, vp, i32] + [vp] * 15 + [sz, vp]
         lib.ssd_backward_dt.restype = i32
+        lib.ssd_forward_varlen_workspace_bytes.argtypes = [dp, i32]
+        lib.ssd_forward_varlen_workspace_bytes.restype = sz
+        lib.ssd_forward_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz,
+                                           vp, ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
+        lib.ssd_forward_varlen.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -218,6 +223,70 @@ def _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, st
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_forward")
     return y, final_state, launches
+
+
+def varlen_dims(x: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, nseq: int, max_seqlen: int) -> Dims:
+    """ssd_dims of a packed variable-length call: x [T,H,P], log_a [T,H] or [T,H,N], B [T,G,N];
+    nseq sequences of at most max_seqlen tokens."""
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [T,H,P] and B [T,G,N]")
+    _, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    decay = SSD_DECAY_DIAG if log_a.dim() == 3 else SSD_DECAY_SCALAR
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+    return Dims(int(nseq), int(max_seqlen), H, G, P, N, _DTYPE_CODE[x.dtype], decay)
+
+
+def ssd_forward_varlen_workspace_bytes(dims: Dims, chunk: int) -> int:
+    return int(load_library().ssd_forward_varlen_workspace_bytes(ctypes.byref(dims), int(chunk)))
+
+
+def ssd_forward_varlen(x, log_a, B, C, cu_seqlens, max_seqlen: int, D=None, chunk: int = 64, init_state=None,
+                       y=None, final_state=None, workspace=None, stream=None, events=None):
+    """Run ``ssd_forward_varlen``: a packed batch of len(cu_seqlens) - 1 sequences, sequence i
+    being tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1 of x [T,H,P], log_a [T,H] or [T,H,N],
+    B, C [T,G,N].  cu_seqlens: int64 tensor on the GPU; max_seqlen: a bound on every length
+    (host int).  init_state / final_state [nseq,H,N,P] fp32 as in ssd_forward.  With ``events``
+    (hipEvent_t handles) launch k stamps events[2k] and events[2k+1].
+    Returns (y, final_state, n_launches or None)."""
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    nseq = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or nseq < 0 or cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens must be a 1-D int64 tensor of nseq + 1 offsets on x's device")
+    dims = varlen_dims(x, log_a, B, nseq, max_seqlen)
+    _check(x, "x", (T, H, P), x.dtype, dev)
+    _check(log_a, "log_a", (T, H, N) if dims.decay == SSD_DECAY_DIAG else (T, H), torch.float32, dev)
+    _check(B, "B", (T, G, N), x.dtype, dev)
+    _check(C, "C", (T, G, N), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (nseq, H, N, P), torch.float32, dev)
+    if y is None:
+        y = torch.empty((T, H, P), dtype=x.dtype, device=dev)
+    _check(y, "y", (T, H, P), x.dtype, dev)
+    if final_state is True:
+        final_state = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    _check(final_state, "final_state", (nseq, H, N, P), torch.float32, dev)
+    lib = load_library()
+    need = int(lib.ssd_forward_varlen_workspace_bytes(ctypes.byref(dims), int(chunk)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    arr, n, count = None, 0, ctypes.c_int(0)
+    if events is not None:
+        n = max(len(events), 2 * SSD_MAX_LAUNCHES)
+        arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+    rc = lib.ssd_forward_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(log_a), _ptr(B),
+                                _ptr(C), _ptr(D), int(chunk), _ptr(init_state), _ptr(y), _ptr(final_state),
+                                _ptr(workspace), ws_bytes, _stream_handle(stream, dev), arr, n,
+                                ctypes.byref(count))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_forward_varlen")
+    return y, final_state, (count.value if events is not None else None)
 
 
 def ssd_forward_dt_workspace_bytes(dims: Dims, chunk: int, scale_input: bool = True) -> int:

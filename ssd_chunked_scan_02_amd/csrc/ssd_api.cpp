@@ -39,14 +39,16 @@ int check_dims(const ssd_dims* d, bool forward) {
     return SSD_OK;
 }
 
-size_t workspace_needed(const ssd_dims* d, int chunk) {
+// (varlen: a packed variable-length batch of d->batch sequences of at most d->seqlen tokens)
+size_t workspace_needed(const ssd_dims* d, int chunk, bool varlen = false) {
     if (d->seqlen == 0 || d->batch == 0) return 0;
     const int64_t nchunks = (d->seqlen + chunk - 1) / chunk;
     if (d->decay == SSD_DECAY_DIAG)
         return ssd::diag_workspace_bytes(d->dtype, d->batch, d->nheads, d->seqlen, (int)d->dstate, (int)d->headdim,
-                                         chunk);
+                                         chunk, varlen);
     if (ssd::fast_path_applies(d->dtype, d->decay, (int)d->dstate, (int)d->headdim, chunk, d->nheads, d->ngroups))
-        return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, d->seqlen, (int)d->dstate, chunk);
+        return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, d->seqlen, (int)d->dstate, chunk, false,
+                                         varlen);
     return ssd::scores_bytes(d->batch, d->ngroups, nchunks, chunk);
 }
 
@@ -97,16 +99,31 @@ struct Discretization {
     bool scale_input;
 };
 
-// ssd_forward (disc null: log_a given) and ssd_forward_dt (disc set: log_a null).
+// A packed variable-length batch: sequence offsets on the device and the packed token count.
+struct Varlen {
+    const int64_t* cu_seqlens;
+    int64_t total;
+};
+
+// ssd_forward (disc null: log_a given), ssd_forward_dt (disc set: log_a null) and
+// ssd_forward_varlen (vl set, disc null).
 int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Discretization* disc,
                  const void* B, const void* C, const float* D, int chunk, const float* init_state,
                  void* y, float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                 void* const* events, int n_events, int* n_launches) {
+                 void* const* events, int n_events, int* n_launches, const Varlen* vl = nullptr) {
     if (n_launches) *n_launches = 0;
     if (events && n_events < 2 * SSD_MAX_LAUNCHES) return SSD_ERR_INVALID;
     int rc = check_forward(d, chunk);
     if (rc != SSD_OK) return rc;
-    const bool has_tokens = d->batch > 0 && d->seqlen > 0;
+    if (vl) {
+        if (vl->total < 0 || vl->total > kMaxElems) return SSD_ERR_INVALID;
+        if (d->batch > 0 && (!vl->cu_seqlens || ((uintptr_t)vl->cu_seqlens & 7u) != 0)) return SSD_ERR_INVALID;
+        // (every packed tensor's element count must stay well inside int64, as for the batched form)
+        if ((double)vl->total * (double)d->nheads * (double)(d->headdim > d->dstate ? d->headdim : d->dstate) >
+            (double)kMaxElems * 1024.0)
+            return SSD_ERR_INVALID;
+    }
+    const bool has_tokens = d->batch > 0 && d->seqlen > 0 && (!vl || vl->total > 0);
     const float* decay_in = disc ? disc->dt : log_a;
     if (has_tokens && (!x || !decay_in || !B || !C || !y)) return SSD_ERR_INVALID;
     if (has_tokens && disc && !disc->A_log) return SSD_ERR_INVALID;
@@ -114,10 +131,10 @@ int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Dis
                           disc ? disc->dt : nullptr, disc ? disc->dt_bias : nullptr, disc ? disc->A_log : nullptr};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return SSD_ERR_ALIGN;
-    const size_t need = disc ? workspace_needed_dt(d, chunk, disc->scale_input) : workspace_needed(d, chunk);
+    const size_t need = disc ? workspace_needed_dt(d, chunk, disc->scale_input) : workspace_needed(d, chunk, vl != nullptr);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
     if (d->batch == 0) return SSD_OK;
-    if (d->seqlen == 0 && !final_state) return SSD_OK;
+    if ((d->seqlen == 0 || (vl && vl->total == 0)) && !final_state) return SSD_OK;
 
     int count = 0;
     ssd::ForwardLaunch fl{};
@@ -150,6 +167,12 @@ int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Dis
     fl.n_events = events ? n_events : 0;
     fl.n_launches = &count;
     fl.first_launch = 0;
+    if (vl) {
+        fl.seq_off = vl->cu_seqlens;
+        fl.total = vl->total;
+        // (no tokens at all: every sequence is empty, its final state its initial state)
+        if (vl->total == 0) fl.seqlen = 0;
+    }
     rc = ssd::launch_forward(fl, static_cast<hipStream_t>(stream));
     if (n_launches) *n_launches = count;
     if (rc == -2) return SSD_ERR_UNSUPPORTED;
@@ -184,6 +207,20 @@ int step_impl(const ssd_dims* d, float* state, const void* x_t, const float* log
 }  // namespace
 
 extern "C" {
+
+size_t ssd_forward_varlen_workspace_bytes(const ssd_dims* dims, int chunk) {
+    if (check_forward(dims, chunk) != SSD_OK) return 0;
+    return workspace_needed(dims, chunk, true);
+}
+
+int ssd_forward_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens, const void* x,
+                       const float* log_a, const void* B, const void* C, const float* D, int chunk,
+                       const float* init_state, void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                       void* stream, void* const* events, int n_events, int* n_launches) {
+    const Varlen vl{cu_seqlens, total_tokens};
+    return forward_impl(dims, x, log_a, nullptr, B, C, D, chunk, init_state, y, final_state, workspace,
+                        workspace_bytes, stream, events, n_events, n_launches, &vl);
+}
 
 size_t ssd_forward_workspace_bytes(const ssd_dims* dims, int chunk) {
     if (check_forward(dims, chunk) != SSD_OK) return 0;

@@ -115,6 +115,21 @@ __device__ __forceinline__ V block_inclusive_scan(V v, V* scratch) {
 // Maps a launch index to a work index so that each of the 8 XCDs (which receive workgroups
 // round-robin) gets one contiguous range of work: neighbouring heads of one (batch, group)
 // then share that XCD's L2.  Returns -1 for padding workgroups.
+// The rows of sequence b.  Batched layout (seq_off null): tokens b * seqlen .. + seqlen of the
+// [batch][seqlen] token axis.  Packed variable-length batch: tokens seq_off[b] .. seq_off[b+1] of the
+// packed axis of `total` tokens, clamped into [0, total] and to at most seqlen tokens, so that any
+// offsets keep every access inside the tensors and the workspace.
+struct SeqSpan {
+    int64_t row0, len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int64_t* seq_off, int64_t b, int64_t seqlen, int64_t total) {
+    if (!seq_off) return SeqSpan{b * seqlen, seqlen};
+    int64_t s = seq_off[b], e = seq_off[b + 1];
+    s = s < 0 ? 0 : (s > total ? total : s);
+    e = e < s ? s : (e > total ? total : e);
+    return SeqSpan{s, e - s < seqlen ? e - s : seqlen};
+}
+
 __device__ __forceinline__ int64_t xcd_work_index(int64_t bid, int64_t per_xcd, int64_t total) {
     const int64_t w = (bid % 8) * per_xcd + bid / 8;
     return w < total ? w : -1;

@@ -123,6 +123,7 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
     const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
     if (unit < 0) return;
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane % 16, lg = lane / 16;
     const int koff = (KB / 4) * lg;
@@ -177,9 +178,10 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
     };
     write_state_lds();
 
-    for (int c = 0; c < prm.nchunks; ++c) {
+    const int nch = (int)((sq.len + Q - 1) / Q);
+    for (int c = 0; c < nch; ++c) {
         const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
+        const int len = (int)min((int64_t)Q, sq.len - t0);
         __syncthreads();  // previous chunk done with every LDS buffer
 
         // ---- 1. log a into LDS, then running sums down each state column (past the end: 0):
@@ -187,7 +189,7 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
         //         thread, then every group offset by the totals of the groups before it
         for (int i = tid; i < QK * N; i += kThreads) {
             const int t = i / N, n = i % N;
-            cum[i] = t < len ? (CT)prm.log_a[((b * Tn + t0 + t) * H + h) * N + n] : (CT)0;
+            cum[i] = t < len ? (CT)prm.log_a[((sq.row0 + t0 + t) * H + h) * N + n] : (CT)0;
         }
         __syncthreads();
         {
@@ -219,8 +221,8 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
         for (int item = tid; item < QK * (N / VE); item += kThreads) {
             const int t = item / (N / VE), cc = item % (N / VE);
             const bool ok = t < len;
-            const uint4 cv = ok ? ld16(Cg + ((b * Tn + t0 + t) * G + g) * N + cc * VE) : zero;
-            const uint4 bv = ok ? ld16(Bg + ((b * Tn + t0 + t) * G + g) * N + cc * VE) : zero;
+            const uint4 cv = ok ? ld16(Cg + ((sq.row0 + t0 + t) * G + g) * N + cc * VE) : zero;
+            const uint4 bv = ok ? ld16(Bg + ((sq.row0 + t0 + t) * G + g) * N + cc * VE) : zero;
             const int a = t & ~15, e = t | 15;
             float fe[VE], ff_[VE], fu[VE];
 #pragma unroll
@@ -246,7 +248,7 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int r = 4 * rg + k;
-                u[k] = r < len ? ld16(xg + ((b * Tn + t0 + r) * H + h) * P + cc * VE) : zero;
+                u[k] = r < len ? ld16(xg + ((sq.row0 + t0 + r) * H + h) * P + cc * VE) : zero;
             }
 #pragma unroll
             for (int j = 0; j < VE; ++j)
@@ -259,7 +261,7 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int r = 4 * rg + k;
-                u[k] = r < len ? ld16(Bg + ((b * Tn + t0 + r) * G + g) * N + cc * VE) : zero;
+                u[k] = r < len ? ld16(Bg + ((sq.row0 + t0 + r) * G + g) * N + cc * VE) : zero;
             }
 #pragma unroll
             for (int j = 0; j < VE; ++j) {
@@ -309,14 +311,14 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
                     const CT ct = cum[t * N + n];
                     const float craw =
                         kRawLds ? (float)Craw[t * NP + n]
-                                : (float)Cg[((b * Tn + t0 + min(t, len - 1)) * G + g) * N + n] * (t < len ? 1.f : 0.f);
+                                : (float)Cg[((sq.row0 + t0 + min(t, len - 1)) * G + g) * N + n] * (t < len ? 1.f : 0.f);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int s = 16 * sb + 4 * lg + i;
                         const bool causal = s <= t && s < len;
                         const float braw = !causal ? 0.f
                                            : kRawLds ? (float)Braw[s * NP + n]
-                                                     : (float)Bg[((b * Tn + t0 + s) * G + g) * N + n];
+                                                     : (float)Bg[((sq.row0 + t0 + s) * G + g) * N + n];
                         const CT d = causal ? (CT)(ct - cum[s * N + n]) : (CT)0;
                         acc[i] += craw * braw * dexp(d);
                     }
@@ -330,7 +332,7 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
         for (int tb = wave; tb < nt; tb += kWaves) {
             const int tl = 16 * tb + l16;
             const bool tvalid = tl < len;
-            const int64_t trow = b * Tn + t0 + tl;
+            const int64_t trow = sq.row0 + t0 + tl;
             f32x4 acc[PB];
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -486,9 +488,18 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane % 16, lg = lane / 16;
-    const int nchunks = prm.nchunks;
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+    // (a packed sequence: its own chunk count; it is never segmented)
+    const int nchunks = prm.seq_off ? (int)((sq.len + Q - 1) / Q) : prm.nchunks;
     const int c0 = seg * prm.seg_chunks, c1 = min(c0 + prm.seg_chunks, nchunks);
     const int64_t sidx = seg * units + unit;  // (segment, unit) index of the segment buffers
+    if (c1 <= c0) {
+        // an empty packed sequence: its final state is its initial state
+        if (FULL && prm.final_state)
+            for (int i = tid; i < N * P; i += kThreads)
+                prm.final_state[unit * N * P + i] = prm.init ? prm.init[unit * N * P + i] : 0.f;
+        return;
+    }
 
     extern __shared__ __align__(16) unsigned char smem[];
     __bf16* Xt = reinterpret_cast<__bf16*>(smem + L::xt);
@@ -524,7 +535,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     __bf16* yg = static_cast<__bf16*>(prm.y);
     const uint4 zero = {0u, 0u, 0u, 0u};
     const float dskip = prm.D ? prm.D[h] : 0.f;
-    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, sq.len - (int64_t)c * Q); };
 
     // ---- prefetch registers: one chunk of log a, B, C and x rows (rows clamped into the
     //      sequence; staged as zeros past its end)
@@ -536,16 +547,16 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     auto load_chunk = [&](int c) {
         const int64_t t0 = (int64_t)c * Q;
         const int last = chunk_len(c) - 1;
-        if (DT) rdt = dtg[(b * Tn + t0 + min(lane, last)) * H + h];
+        if (DT) rdt = dtg[(sq.row0 + t0 + min(lane, last)) * H + h];
 #pragma unroll
         for (int m = 0; m < LAI; ++m) {
             const int id = tid + kThreads * m, t = min(id / (N / 4), last), c4 = id % (N / 4);
-            if (!DT && id < LAT) rla[m] = ld16(lag + ((b * Tn + t0 + t) * H + h) * N + 4 * c4);
+            if (!DT && id < LAT) rla[m] = ld16(lag + ((sq.row0 + t0 + t) * H + h) * N + 4 * c4);
         }
 #pragma unroll
         for (int m = 0; m < BCI; ++m) {
             const int id = tid + kThreads * m, t = min(id / (N / 8), last), c8 = id % (N / 8);
-            const int64_t off = ((b * Tn + t0 + t) * G + g) * N + 8 * c8;
+            const int64_t off = ((sq.row0 + t0 + t) * G + g) * N + 8 * c8;
             if (id < BCT) {
                 rb[m] = ld16(Bg + off);
                 if (FULL) rc[m] = ld16(Cg + off);
@@ -554,7 +565,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 #pragma unroll
         for (int m = 0; m < XI; ++m) {
             const int id = tid + kThreads * m, t = min(id / (P / 8), last), c8 = id % (P / 8);
-            if (id < XT) rx[m] = ld16(xg + ((b * Tn + t0 + t) * H + h) * P + 8 * c8);
+            if (id < XT) rx[m] = ld16(xg + ((sq.row0 + t0 + t) * H + h) * P + 8 * c8);
         }
     };
     auto stage_chunk = [&](int c) {
@@ -851,7 +862,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[q][i] += dskip * (float)Xt[(16 * (pb0 + q) + 4 * lg + i) * QP + tl];
             if (tl < len) {
-                __bf16* yr = yg + ((b * Tn + t0 + tl) * H + h) * P + 4 * lg;
+                __bf16* yr = yg + ((sq.row0 + t0 + tl) * H + h) * P + 4 * lg;
 #pragma unroll
                 for (int q = 0; q < PH; ++q)
                     store4(yr + 16 * (pb0 + q), acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
@@ -913,6 +924,8 @@ int launch_diag_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int64_t per_xcd = (units + 7) / 8;
     WalkParams wp{fl.x, fl.log_a, fl.Bm, fl.Cm, fl.D, nullptr, fl.init, fl.y, fl.final_state,
                   fl.batch, fl.seqlen, fl.nheads, fl.ngroups, fl.chunk, fl.nchunks, per_xcd};
+    wp.seq_off = fl.seq_off;
+    wp.total = fl.total;
     const size_t lds = DiagLayout<T, N, P>(fl.chunk).total;
     int k = fl.first_launch;
     return launch_k(fl, k, walk_diag_kernel<T, N, P>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, stream, wp)
@@ -937,18 +950,24 @@ size_t diag_lds_bytes(int dtype, int N, int P, int chunk) {
 }
 
 // Workspace of the pipelined diagonal walk: nothing, or for a segmented walk two fp32 states
-// and a log2 decay per state row for every (segment, unit).
+// and a log2 decay per state row for every (segment, unit).  Packed variable-length batches are
+// never segmented.
 struct DiagSegLayout {
     int nseg, seg_chunks;
     size_t state, init, decay, total;
 };
 
-DiagSegLayout diag_seg_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P) {
+DiagSegLayout diag_seg_layout(int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, bool varlen) {
     DiagSegLayout l;
     const int64_t units = batch * nheads, nchunks = (seqlen + kDiagQ - 1) / kDiagQ;
     // two rounds of walk workgroups (one per CU each): the walk takes as long as one round of
     // twice-longer segments, while the state-only pass (three per CU) gets shorter
-    l.nseg = walk_segments(units, nchunks, 512, &l.seg_chunks);
+    if (varlen) {
+        l.nseg = 1;
+        l.seg_chunks = (int)(nchunks > 0 ? nchunks : 1);
+    } else {
+        l.nseg = walk_segments(units, nchunks, 512, &l.seg_chunks);
+    }
     l.state = l.init = l.decay = l.total = 0;
     if (l.nseg > 1) {
         const size_t st = (size_t)l.nseg * units * N * P * 4;
@@ -977,7 +996,7 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
             return -1;
         attr_set[dev] = true;
     }
-    const DiagSegLayout sl = diag_seg_layout(fl.batch, fl.nheads, fl.seqlen, N, P);
+    const DiagSegLayout sl = diag_seg_layout(fl.batch, fl.nheads, fl.seqlen, N, P, fl.seq_off != nullptr);
     const int64_t units = fl.batch * fl.nheads;
     const int64_t per_xcd = (sl.nseg * units + 7) / 8;
     char* ws = reinterpret_cast<char*>(fl.scores);
@@ -987,7 +1006,7 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.init) : nullptr,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.state) : nullptr,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.decay) : nullptr,
-                  fl.dt, fl.dt_bias, fl.A_log, fl.scale_input};
+                  fl.dt, fl.dt_bias, fl.A_log, fl.scale_input, fl.seq_off, fl.total};
     const size_t lds = DiagPipeLayout<N, P, true>::total, slds = DiagPipeLayout<N, P, false>::total;
     int k = fl.first_launch;
     if (sl.nseg > 1) {
@@ -1010,9 +1029,10 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
 
 bool diag_pipe_applies(int dtype, int N, int P, int chunk) { return diag_pipe_shape(dtype, N, P, chunk); }
 
-size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk) {
+size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk,
+                            bool varlen) {
     if (!diag_pipe_shape(dtype, N, P, chunk)) return 0;
-    return diag_seg_layout(batch, nheads, seqlen, N, P).total;
+    return diag_seg_layout(batch, nheads, seqlen, N, P, varlen).total;
 }
 
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream) {

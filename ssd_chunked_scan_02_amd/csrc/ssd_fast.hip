@@ -117,10 +117,12 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
     const int64_t bg = blk / prm.nchunks;
     const int64_t b = bg / prm.ngroups, g = bg % prm.ngroups;
     const int64_t t0 = (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, prm.seqlen - t0);
+    const SeqSpan sq = seq_span(prm.seq_off, b, prm.seqlen, prm.total);
+    if (t0 >= sq.len) return;  // (a packed sequence shorter than seqlen: no such chunk)
+    const int len = (int)min((int64_t)Q, sq.len - t0);
     const int64_t rs = prm.ngroups * N;
-    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm) + ((b * prm.seqlen + t0) * prm.ngroups + g) * N;
-    const __bf16* Cg = static_cast<const __bf16*>(prm.Cm) + ((b * prm.seqlen + t0) * prm.ngroups + g) * N;
+    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm) + ((sq.row0 + t0) * prm.ngroups + g) * N;
+    const __bf16* Cg = static_cast<const __bf16*>(prm.Cm) + ((sq.row0 + t0) * prm.ngroups + g) * N;
     const uint4 zero = {0u, 0u, 0u, 0u};
 
     // every global load first, so one wait covers them all
@@ -139,7 +141,7 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
         // turn it into log a and log2 of the input scale)
         const int HG = (int)(prm.nheads / prm.ngroups);
         const int nla = HG * (Q / 4);
-        const float* lag = (prm.dt ? prm.dt : prm.log_a) + (b * prm.seqlen + t0) * prm.nheads + g * HG;
+        const float* lag = (prm.dt ? prm.dt : prm.log_a) + (sq.row0 + t0) * prm.nheads + g * HG;
         const int wave0 = tid - lane;  // first thread of this wave
         f32x4 lv[kPrepLa];
 #pragma unroll
@@ -338,13 +340,14 @@ struct WalkLds {
 };
 
 // The piece of work of one workgroup: a (batch, head) unit and the chunks [c0, c1) of one
-// segment of its sequence (the whole sequence unless the walk is split into segments).
+// segment of its sequence (the whole sequence unless the walk is split into segments); the
+// sequence's first row, length and chunk count (a packed sequence: its own).
 struct WalkSpan {
-    int64_t unit, b, h, g;
-    int seg, c0, c1;
+    int64_t unit, b, h, g, row0, len;
+    int seg, c0, c1, nch;
 };
 
-__device__ __forceinline__ WalkSpan walk_span(const Walk2Params& prm, int64_t work) {
+__device__ __forceinline__ WalkSpan walk_span(const Walk2Params& prm, int64_t work, int Q) {
     WalkSpan sp;
     const int64_t units = prm.batch * prm.nheads;
     sp.seg = (int)(work / units);
@@ -352,8 +355,12 @@ __device__ __forceinline__ WalkSpan walk_span(const Walk2Params& prm, int64_t wo
     sp.b = sp.unit / prm.nheads;
     sp.h = sp.unit % prm.nheads;
     sp.g = sp.h / (prm.nheads / prm.ngroups);
+    const SeqSpan sq = seq_span(prm.seq_off, sp.b, prm.seqlen, prm.total);
+    sp.row0 = sq.row0;
+    sp.len = sq.len;
+    sp.nch = prm.seq_off ? (int)((sq.len + Q - 1) / Q) : prm.nchunks;
     sp.c0 = sp.seg * prm.seg_chunks;
-    sp.c1 = min(sp.c0 + prm.seg_chunks, prm.nchunks);
+    sp.c1 = min(sp.c0 + prm.seg_chunks, sp.nch);
     return sp;
 }
 
@@ -367,7 +374,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     constexpr int PB = WS::PB, HS = WS::HS;
     constexpr int KDMAX = wave_tb(TBW - 1, OW) / 2 > wave_tb(0, OW) / 2 ? wave_tb(TBW - 1, OW) / 2 : wave_tb(0, OW) / 2;
     const int l16 = lane % 16, lg = lane / 16;
-    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
+    const int64_t H = prm.nheads, G = prm.ngroups;
     const int nchunks = prm.nchunks;
     const uint32_t y_row = (uint32_t)(H * kP * 2);
     const __bf16* ct0 = prm.ct + (b * G + g) * (int64_t)nchunks * NT * KN * 512;
@@ -376,7 +383,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     const float dskip = prm.D ? prm.D[h] : 0.f;
     constexpr int YROWS = WS::YROWS, YST = YROWS * 8 / kWave;  // 16-byte stores per lane per chunk
     __bf16* ys = L.Ys + OW * YROWS * kXStr;
-    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, span.len - (int64_t)c * Q); };
 
     // Operands come from the prep kernel in lane order (one contiguous 1 KiB per load); rows
     // past a short chunk's end are zeros there and are never stored here.
@@ -408,7 +415,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         // As many stores as one chunk's outputs, all dropped (empty resource): the loop is then
         // entered with the same memory operations in flight as each later chunk, and the
         // compiler's load counting at the loop head stays exact instead of waiting for stores.
-        const __amdgpu_buffer_rsrc_t none = buffer_rsrc(yg + (b * Tn * H + h) * kP, 0u);
+        const __amdgpu_buffer_rsrc_t none = buffer_rsrc(yg + (span.row0 * H + h) * kP, 0u);
 #pragma unroll
         for (int m = 0; m < YST; ++m) buffer_store16(none, 0u, uint4{0u, 0u, 0u, 0u});
     }
@@ -532,7 +539,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         }
         wave_lds_fence();
         const __amdgpu_buffer_rsrc_t yr =
-            buffer_rsrc(yg + ((b * Tn + (int64_t)c * Q) * H + h) * kP, (uint32_t)len * y_row);
+            buffer_rsrc(yg + ((span.row0 + (int64_t)c * Q) * H + h) * kP, (uint32_t)len * y_row);
 #pragma unroll
         for (int m = 0; m < YST; ++m) {
             const int id = lane + kWave * m, row = id / 8, c8 = id % 8;
@@ -553,7 +560,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     constexpr int NT = WS::NT, KS = WS::KS, NBW = WS::NBW, LA = WS::LA, QW = WS::QW, XCH = WS::XCH;
     constexpr int PB = WS::PB, HS = WS::HS;
     const int l16 = lane % 16, lg = lane / 16;
-    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
+    const int64_t H = prm.nheads, G = prm.ngroups;
     const int nchunks = prm.nchunks;
     const uint32_t x_row = (uint32_t)(H * kP * 2);
     const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
@@ -561,7 +568,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     const __bf16* xg = static_cast<const __bf16*>(prm.x);
     const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * (N / 16) * KS * 512;
     const uint4 zero = {0u, 0u, 0u, 0u};
-    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, span.len - (int64_t)c * Q); };
 
     float la[LA];
     float lgs[DT ? LA : 1];  // (DT) log2 of the input scale of the same tokens
@@ -580,7 +587,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     };
     auto load_x = [&](int c) {
         const int last = chunk_len(c) - 1;
-        const void* xbase = xg + ((b * Tn + (int64_t)c * Q) * H + h) * kP;
+        const void* xbase = xg + ((span.row0 + (int64_t)c * Q) * H + h) * kP;
 #pragma unroll
         for (int m = 0; m < XCH; ++m) {
             const int id = lane + kWave * m, row = min(QW * SW + id / 8, last), c16 = id % 8;
@@ -755,7 +762,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         lds_barrier();
     }
 
-    float* fin = (c1 == prm.nchunks && prm.final_state) ? prm.final_state + unit * N * kP : nullptr;
+    float* fin = (c1 == span.nch && prm.final_state) ? prm.final_state + unit * N * kP : nullptr;
     if (fin) {
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
@@ -775,7 +782,14 @@ template <int N, int Q, bool DT>
 __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm) {
     const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
     if (work < 0) return;
-    const WalkSpan span = walk_span(prm, work);
+    const WalkSpan span = walk_span(prm, work, Q);
+    if (span.c1 <= span.c0) {
+        // an empty packed sequence: its final state is its initial state
+        if (prm.final_state)
+            for (int i = threadIdx.x; i < N * kP; i += kWalkThreads)
+                prm.final_state[span.unit * N * kP + i] = prm.init ? prm.init[span.unit * N * kP + i] : 0.f;
+        return;
+    }
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     extern __shared__ __align__(16) unsigned char smem[];
@@ -828,11 +842,11 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     const int64_t units = prm.batch * prm.nheads;
     const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, (prm.nseg - 1) * units);
     if (work < 0) return;
-    const WalkSpan span = walk_span(prm, work);
+    const WalkSpan span = walk_span(prm, work, Q);
     const int lane = threadIdx.x;
     const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
     const int c0 = span.c0, c1 = span.c1;
-    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
+    const int64_t H = prm.nheads, G = prm.ngroups;
     const int nchunks = prm.nchunks;
     const uint32_t x_row = (uint32_t)(H * kP * 2);
     const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
@@ -843,7 +857,7 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     __bf16* Xw = reinterpret_cast<__bf16*>(smem);
     // W, permuted so that the XR rows a lane stages (lane / 8 + 8 m) are contiguous
     float* wv = reinterpret_cast<float*>(smem + (size_t)Q * kXStr * 2);
-    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, Tn - (int64_t)c * Q); };
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, span.len - (int64_t)c * Q); };
     // staging piece m of this lane: row lane / 8 + 8 m, bytes 16 (lane % 8) of it
     const uint32_t xoff = (uint32_t)(lane / 8) * x_row + 16 * (lane % 8);
 
@@ -861,7 +875,7 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     // end read as zeros
     auto load_x = [&](int c) {
         const __amdgpu_buffer_rsrc_t xr =
-            buffer_rsrc(xg + ((b * Tn + (int64_t)c * Q) * H + h) * kP, (uint32_t)chunk_len(c) * x_row);
+            buffer_rsrc(xg + ((span.row0 + (int64_t)c * Q) * H + h) * kP, (uint32_t)chunk_len(c) * x_row);
 #pragma unroll
         for (int m = 0; m < XR; ++m) xs[m] = buffer_load16(xr, xoff + (uint32_t)(8 * m) * x_row);
     };
@@ -1003,16 +1017,22 @@ struct FastLayout {
     size_t pairs, bt, ct, la_t, lg_t, seg_state, seg_decay, total;
 };
 
-// (with_lg: log2 of the input scale head-major, laid out as la_t)
+// (with_lg: log2 of the input scale head-major, laid out as la_t; varlen: a packed
+// variable-length batch, never segmented)
 FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int Q,
-                       bool with_lg = false) {
+                       bool with_lg = false, bool varlen = false) {
     FastLayout l;
     l.nchunks = (seqlen + Q - 1) / Q;
     l.nblk = batch * ngroups * l.nchunks;
     l.units = batch * nheads;
     // Two rounds of workgroups per CU for the walk: its time is the same as with one round of
     // twice-longer segments, while the state-only pass (one wave per segment) gets shorter.
-    l.nseg = walk_segments(l.units, l.nchunks, kSegTarget, &l.seg_chunks);
+    if (varlen) {
+        l.nseg = 1;
+        l.seg_chunks = (int)(l.nchunks > 0 ? l.nchunks : 1);
+    } else {
+        l.nseg = walk_segments(l.units, l.nchunks, kSegTarget, &l.seg_chunks);
+    }
     size_t off = 0;
     l.pairs = off; off += (size_t)l.nblk * n_pairs(Q / 16) * 1024;
     l.bt = off; off += (size_t)l.nblk * N * Q * 2;
@@ -1034,7 +1054,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     static_assert(WalkShape<N, Q>::lds_bytes <= kMaxLds, "walk LDS budget");
     static bool prep_attr[64] = {}, walk_attr[64] = {};
     const bool with_lg = fl.dt && fl.scale_input;
-    const FastLayout lay = fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q, with_lg);
+    const FastLayout lay = fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q, with_lg, fl.seq_off != nullptr);
     char* ws = reinterpret_cast<char*>(fl.scores);
     __bf16* pairs = reinterpret_cast<__bf16*>(ws + lay.pairs);
     __bf16* bt = reinterpret_cast<__bf16*>(ws + lay.bt);
@@ -1043,7 +1063,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int nch = (int)lay.nchunks;
     float* lg_t = with_lg ? reinterpret_cast<float*>(ws + lay.lg_t) : nullptr;
     PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.dt, fl.dt_bias, fl.A_log, lg_t,
-                  fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0};
+                  fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0, fl.seq_off, fl.total};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q, DT>), walk_attr)) return -1;
     int k = fl.first_launch;
@@ -1059,7 +1079,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     Walk2Params wp{fl.x, la_t, lg_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, nch, per_xcd,
                    lay.seg_chunks, lay.nseg, reinterpret_cast<float*>(ws + lay.seg_state),
-                   reinterpret_cast<float*>(ws + lay.seg_decay)};
+                   reinterpret_cast<float*>(ws + lay.seg_decay), fl.seq_off, fl.total};
     if (lay.nseg > 1) {
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         const int64_t state_work = (lay.nseg - 1) * lay.units;
@@ -1092,8 +1112,8 @@ bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nh
 }
 
 size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk,
-                            bool with_lg) {
-    return fast_layout(batch, nheads, ngroups, seqlen, N, fast_chunk(chunk), with_lg).total;
+                            bool with_lg, bool varlen) {
+    return fast_layout(batch, nheads, ngroups, seqlen, N, fast_chunk(chunk), with_lg, varlen).total;
 }
 
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream) {

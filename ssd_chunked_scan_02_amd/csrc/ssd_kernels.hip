@@ -77,7 +77,9 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(ScoresParams prm) {
     const int64_t g = bg % prm.ngroups;
     const int Q = prm.chunk, nt = Q / 16, ntiles = nt * (nt + 1) / 2;
     const int64_t t0 = (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, prm.seqlen - t0);
+    const SeqSpan sq = seq_span(prm.seq_off, b, prm.seqlen, prm.total);
+    if (t0 >= sq.len) return;  // (a packed sequence shorter than seqlen: no such chunk)
+    const int len = (int)min((int64_t)Q, sq.len - t0);
     const T* Bm = static_cast<const T*>(prm.Bm);
     const T* Cm = static_cast<const T*>(prm.Cm);
     float* out = prm.scores + blk * (int64_t)ntiles * 256;
@@ -88,8 +90,8 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(ScoresParams prm) {
         for (int sb = 0; sb <= tb; ++sb, ++idx) {
             if (idx % kWaves != wave) continue;
             const int s = 16 * sb + l16, t = 16 * tb + l16;
-            const T* brow = Bm + ((b * prm.seqlen + t0 + s) * prm.ngroups + g) * N;
-            const T* crow = Cm + ((b * prm.seqlen + t0 + t) * prm.ngroups + g) * N;
+            const T* brow = Bm + ((sq.row0 + t0 + s) * prm.ngroups + g) * N;
+            const T* crow = Cm + ((sq.row0 + t0 + t) * prm.ngroups + g) * N;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < N / KB; ++kb) {
@@ -130,11 +132,13 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
     const int64_t b = unit / H;
     const int64_t h = unit % H;
     const int64_t g = h / (H / G);
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int l16 = lane % 16, lg = lane / 16;
     const int koff = (KB / 4) * lg;  // this lane group's first K index inside a K block
     const int Q = prm.chunk;
+    const int nch = (int)((sq.len + Q - 1) / Q);
     const int QK = (Q + KB - 1) / KB * KB;
     const int QP = QK + TR::kPad;
     const int nt = Q / 16;
@@ -182,13 +186,13 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
     const float dskip = prm.D ? prm.D[h] : 0.f;
     const float* scores_bg = prm.scores + (b * G + g) * (int64_t)prm.nchunks * ntiles * 256;
 
-    for (int c = 0; c < prm.nchunks; ++c) {
+    for (int c = 0; c < nch; ++c) {
         const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
+        const int len = (int)min((int64_t)Q, sq.len - t0);
 
         // ---- 1. running sum of log a inside the chunk (tokens past the end add 0)
         CT v = 0;
-        if (tid < len) v = (CT)prm.log_a[(b * Tn + t0 + tid) * H + h];
+        if (tid < len) v = (CT)prm.log_a[(sq.row0 + t0 + tid) * H + h];
         v = block_inclusive_scan(v, scan_tmp);
         if (tid < Q) cum[tid] = v;
         __syncthreads();
@@ -201,7 +205,7 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int r = 4 * rg + k;
-                u[k] = r < len ? ld16(xg + ((b * Tn + t0 + r) * H + h) * P + cc * VE) : zero;
+                u[k] = r < len ? ld16(xg + ((sq.row0 + t0 + r) * H + h) * P + cc * VE) : zero;
             }
 #pragma unroll
             for (int j = 0; j < VE; ++j)
@@ -216,7 +220,7 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
             for (int k = 0; k < 4; ++k) {
                 const int r = 4 * rg + k;
                 const bool ok = r < len;
-                u[k] = ok ? ld16(Bg + ((b * Tn + t0 + r) * G + g) * N + cc * VE) : zero;
+                u[k] = ok ? ld16(Bg + ((sq.row0 + t0 + r) * G + g) * N + cc * VE) : zero;
                 w[k] = ok ? decay_exp(cum_last - cum[r]) : 0.f;
             }
 #pragma unroll
@@ -234,7 +238,7 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
         for (int tb = wave; tb < nt; tb += kWaves) {
             const int tl = 16 * tb + l16;  // this lane's token inside the chunk
             const bool tvalid = tl < len;
-            const int64_t trow = b * Tn + t0 + tl;
+            const int64_t trow = sq.row0 + t0 + tl;
             f32x4 acc[PB];
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -485,7 +489,7 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int Q = fl.chunk;
     const int nt = Q / 16;
     const int ntiles = nt * (nt + 1) / 2;
-    ScoresParams sp{fl.Bm, fl.Cm, fl.scores, fl.seqlen, fl.ngroups, Q, fl.nchunks};
+    ScoresParams sp{fl.Bm, fl.Cm, fl.scores, fl.seqlen, fl.ngroups, Q, fl.nchunks, fl.seq_off, fl.total};
     const int64_t nscore = fl.batch * fl.ngroups * fl.nchunks;
     (void)ntiles;
     int k = fl.first_launch;
@@ -495,6 +499,8 @@ int launch_forward_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int64_t per_xcd = (units + 7) / 8;
     WalkParams wp{fl.x, fl.log_a, fl.Bm, fl.Cm, fl.D, fl.scores, fl.init, fl.y, fl.final_state,
                   fl.batch, fl.seqlen, fl.nheads, fl.ngroups, Q, fl.nchunks, per_xcd};
+    wp.seq_off = fl.seq_off;
+    wp.total = fl.total;
     const size_t lds = walk_lds_bytes_t<T, N, P>(Q);
     // Allow the full 160 KiB of LDS, once per device.
     static bool attr_set[64] = {};

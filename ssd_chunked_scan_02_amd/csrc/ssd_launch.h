@@ -17,6 +17,9 @@ struct ScoresParams {
     int64_t ngroups;
     int chunk;
     int nchunks;
+    // packed variable-length batch (null: batched layout), as in ForwardLaunch
+    const int64_t* seq_off;
+    int64_t total;
 };
 
 struct WalkParams {
@@ -44,6 +47,9 @@ struct WalkParams {
     const float* dt_bias;
     const float* A_log;
     int scale_input;
+    // packed variable-length batch (null: batched layout), as in ForwardLaunch
+    const int64_t* seq_off;
+    int64_t total;
 };
 
 struct StepParams {
@@ -83,6 +89,9 @@ struct PrepParams {
     int nchunks;
     int64_t nblk;  // batch * ngroups * nchunks
     int split;     // 1: two workgroups per block (see prep_kernel)
+    // packed variable-length batch (null: batched layout), as in ForwardLaunch
+    const int64_t* seq_off;
+    int64_t total;
 };
 
 struct Walk2Params {
@@ -104,6 +113,9 @@ struct Walk2Params {
     int seg_chunks, nseg;
     float* seg_state;
     float* seg_decay;
+    // packed variable-length batch (null: batched layout; never segmented), as in ForwardLaunch
+    const int64_t* seq_off;
+    int64_t total;
 };
 
 // Everything one forward call needs, already validated.
@@ -134,6 +146,12 @@ struct ForwardLaunch {
     int n_events;
     int* n_launches;
     int first_launch;  // index of this call's first launch (a composed path continues the count)
+    // Packed variable-length batch (ssd_forward_varlen): with seq_off non-null (device, batch + 1
+    // offsets) sequence b is tokens seq_off[b] .. seq_off[b+1] of a packed token axis of `total`
+    // tokens, seqlen bounds every length, and the workspace layouts are those of [batch][seqlen]
+    // with no segmented walks.
+    const int64_t* seq_off;
+    int64_t total;
 };
 
 bool shape_supported(int dtype, int N, int P);
@@ -157,12 +175,14 @@ bool launch_k(const L& fl, int& k, F kernel, dim3 grid, dim3 block, size_t lds, 
 bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nheads, int64_t ngroups);
 // (with_lg: the workspace also holds log2 of the input scale, for ssd_forward_dt's scaled input)
 size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk,
-                            bool with_lg = false);
+                            bool with_lg = false, bool varlen = false);
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream);
 // The diagonal-decay walk (ssd_diag.hip): LDS bytes (0 = unsupported) and launch.
 size_t diag_lds_bytes(int dtype, int N, int P, int chunk);
 int launch_forward_diag(const ForwardLaunch& fl, hipStream_t stream);
-size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk);
+// (varlen: a packed variable-length batch, never segmented)
+size_t diag_workspace_bytes(int dtype, int64_t batch, int64_t nheads, int64_t seqlen, int N, int P, int chunk,
+                            bool varlen = false);
 bool diag_pipe_applies(int dtype, int N, int P, int chunk);
 // Segment prefix of a segmented walk (ssd_fast.hip): per_n = 1 for one decay per state row.
 int launch_seg_prefix(const ForwardLaunch& fl, int& k, const float* init, float* seg_init, const float* seg_state,

@@ -142,3 +142,35 @@ def output_gradients(cfg: dict, seed: int) -> dict:
     dy = torch.randn((Bsz, T, H, P), generator=gen, dtype=torch.float32).to(STORAGE[cfg["dtype"]]).contiguous()
     dfinal = torch.randn((Bsz, H, N, P), generator=gen, dtype=torch.float32)
     return dict(dy=dy, dfinal=dfinal)
+
+
+def packed_lengths(nseq: int, total: int, seed: int, spread: float = 1.0) -> list:
+    """nseq sequence lengths summing to total (each >= 1): a seeded log-normal mix (sigma
+    ``spread``) of the kind a serving batch of prompts has, short and long together."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    w = torch.exp(torch.randn(nseq, generator=gen, dtype=torch.float64) * spread)
+    raw = (w / w.sum() * (total - nseq)).floor().to(torch.int64) + 1
+    raw[int(torch.argmax(raw))] += total - int(raw.sum())
+    return [int(v) for v in raw]
+
+
+def packed_inputs(cfg: dict, lengths, seed: int) -> dict:
+    """A packed variable-length batch with the workload's value distributions: the sequences of
+    ``lengths`` one after another on one token axis (x [T,H,P], log_a [T,H] or [T,H,N], B, C
+    [T,G,N], dt [T,H]), cu_seqlens (int64 [nseq + 1]), max_seqlen, D as the workload's, and with
+    cfg["init"] one initial state per sequence ~ N(0, 0.1) [nseq,H,N,P]."""
+    lengths = [int(v) for v in lengths]
+    total = sum(lengths)
+    one = make_inputs(dict(cfg, batch=1, seqlen=total, init=False, decode_steps=0), seed)
+    out = {k: (v[0].contiguous() if k in ("x", "log_a", "B", "C", "dt") else v) for k, v in one.items()}
+    out.pop("init_state", None)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
+    out["cu_seqlens"] = cu
+    out["max_seqlen"] = max(lengths) if lengths else 0
+    out["init_state"] = None
+    if cfg["init"]:
+        gen = torch.Generator(device="cpu").manual_seed(int(seed) + 7919)
+        out["init_state"] = torch.randn((len(lengths), cfg["nheads"], cfg["dstate"], cfg["headdim"]), generator=gen,
+                                        dtype=torch.float32) * math.sqrt(0.1)
+    return out

@@ -32,6 +32,7 @@ def test_header_declares_the_entry_points():
                                     "ssd_backward_profiled", "ssd_backward_workspace_bytes",
                                     "ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
                                     "ssd_forward_dt_workspace_bytes", "ssd_forward_profiled",
+                                    "ssd_forward_varlen", "ssd_forward_varlen_workspace_bytes",
                                     "ssd_forward_workspace_bytes", "ssd_step", "ssd_step_dt",
                                     "ssd_strerror"]
 
@@ -316,3 +317,38 @@ def test_backward_dt_workspace_bytes(lib):
         assert fn(ctypes.byref(d), 1) == own + up(rows * P * 2) + inner
     assert fn(ctypes.byref(mamba2_dims(decay=1)), 1) == 0                  # diagonal decay: N <= 64
     assert fn(ctypes.byref(mamba2_dims(batch=0)), 1) == 0
+
+
+# ---- packed variable-length batches
+def call_varlen(lib, dims, cu=FAKE, total=1000, ws_bytes=1 << 30, **over):
+    p = dict(x=FAKE, la=FAKE, B=FAKE, C=FAKE, D=None, init=None, y=FAKE, fin=None, ws=FAKE)
+    p.update(over)
+    return lib.ssd_forward_varlen(ctypes.byref(dims), cu, total, p["x"], p["la"], p["B"], p["C"], p["D"], 64,
+                                  p["init"], p["y"], p["fin"], p["ws"], ws_bytes, None, None, 0, None)
+
+
+def test_varlen_workspace_bytes(lib):
+    # a [batch][seqlen] batch's workspace without segmented walks: the same as ssd_forward's when
+    # the batched walk is not segmented either, less when it is
+    many = mamba2_dims(batch=64, seqlen=1000)
+    assert ssd.ssd_forward_varlen_workspace_bytes(many, 128) == ssd.ssd_forward_workspace_bytes(many, 128)
+    few = mamba2_dims(batch=1, seqlen=65536, nheads=32)
+    assert 0 < ssd.ssd_forward_varlen_workspace_bytes(few, 128) < ssd.ssd_forward_workspace_bytes(few, 128)
+    dd = mamba2_dims(decay=1, dstate=64, batch=1, nheads=2, seqlen=4096)
+    assert ssd.ssd_forward_varlen_workspace_bytes(dd, 64) == 0 < ssd.ssd_forward_workspace_bytes(dd, 64)
+    assert ssd.ssd_forward_varlen_workspace_bytes(mamba2_dims(), 48) == 0
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    d = mamba2_dims(batch=4, seqlen=512)
+    assert call_varlen(lib, d, total=-1) == ssd.SSD_ERR_INVALID
+    assert call_varlen(lib, d, cu=None) == ssd.SSD_ERR_INVALID
+    assert call_varlen(lib, d, cu=FAKE + 4) == ssd.SSD_ERR_INVALID
+    assert call_varlen(lib, d, x=None) == ssd.SSD_ERR_INVALID
+    assert call_varlen(lib, d, y=FAKE + 2) == ssd.SSD_ERR_ALIGN
+    need = ssd.ssd_forward_varlen_workspace_bytes(d, 64)
+    assert call_varlen(lib, d, ws_bytes=need - 1) == ssd.SSD_ERR_INVALID
+    assert call_varlen(lib, mamba2_dims(dstate=48)) == ssd.SSD_ERR_UNSUPPORTED
+    # nothing to do: no sequences, or no tokens and no final state wanted (no HIP call)
+    assert call_varlen(lib, mamba2_dims(batch=0), cu=None) == ssd.SSD_OK
+    assert call_varlen(lib, d, total=0, x=None, la=None, B=None, C=None, y=None) == ssd.SSD_OK

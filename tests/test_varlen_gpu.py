@@ -1,0 +1,108 @@
+"""ssd_forward_varlen (packed variable-length batches) against the oracle's per-sequence
+recurrence (oracle.varlen.forward_varlen), element by element on the same seeded inputs, on each
+path: the bf16 fast path (chunks 64 and 128, grouped heads), the pipelined diagonal walk, and the
+generic scalar and diagonal walks (fp32, and bf16 with a head dim off the fast path).  Lengths mix
+empty, one-token, chunk-multiple and ragged sequences.  Bounds as for ssd_forward: relative L2
+<= 1e-5 for fp32 inputs, <= 2e-2 for bf16, on y and on the final states."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.varlen
+import ssd_inputs
+import ssd_chunked_scan_02_amd as ssd
+from gpu_helpers import announce, rel_l2, TOL
+
+pytestmark = pytest.mark.gpu
+
+f64 = ssd_inputs.to_f64
+
+CASES = [
+    ("mamba2_layer", dict(nheads=4, init=True), 128, [300, 1, 0, 129, 1000, 128, 57], "fast-q128"),
+    ("gqa_decode", dict(nheads=8, ngroups=2, init=True, decode_steps=0), 64, [64, 700, 0, 3, 250], "fast-q64-gqa"),
+    ("mamba2_layer", dict(nheads=2, dstate=64, init=False), 256, [1500, 255, 2], "fast-q256-n64"),
+    ("diag_multiscale", dict(nheads=3, init=True), 64, [200, 0, 64, 1, 517], "diag-pipe"),
+    ("diag_multiscale", dict(nheads=2, dstate=32, headdim=32, init=True, a_log="rand_hn"), 64, [100, 333, 7],
+     "diag-pipe-32"),
+    ("tiny_fp32", dict(nheads=3, skip=True, init=True), 64, [90, 0, 257, 64, 1], "generic-fp32"),
+    ("mamba2_layer", dict(nheads=2, headdim=32, init=True), 128, [130, 400, 5], "generic-bf16-p32"),
+    ("diag_multiscale", dict(nheads=2, dstate=16, headdim=32, dtype="fp32", init=True, a_log="rand_hn"), 32,
+     [77, 0, 140], "generic-diag-fp32"),
+]
+
+
+def _run(name, over, chunk, lengths, label, seed=41):
+    cfg = ssd_inputs.config(name, **over)
+    announce("varlen %s lengths=%s chunk=%d" % (label, lengths, chunk))
+    p = ssd_inputs.packed_inputs(cfg, lengths, seed)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    y, fin, _ = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], g["cu_seqlens"], p["max_seqlen"],
+                                       g.get("D"), chunk=chunk, init_state=g.get("init_state"), final_state=True)
+    torch.cuda.synchronize()
+    yr, fr = oracle.varlen.forward_varlen(oracle.default_oracle(), f64(p["x"]), f64(p["log_a"]), f64(p["B"]),
+                                          f64(p["C"]), p["cu_seqlens"].numpy(), f64(p.get("D")),
+                                          f64(p.get("init_state")))
+    tol = TOL[cfg["dtype"]]
+    ey = rel_l2(y.double().cpu().numpy(), yr) if yr.size else 0.0
+    ef = rel_l2(fin.double().cpu().numpy(), fr)
+    announce("varlen %s: y %.2e final %.2e (tol %.0e)" % (label, ey, ef, tol))
+    assert ey <= tol and ef <= tol, (ey, ef)
+    # each sequence on its own too: no sequence may hide another's error
+    for i, n in enumerate(lengths):
+        s, e = int(p["cu_seqlens"][i]), int(p["cu_seqlens"][i + 1])
+        if n > 0:
+            assert rel_l2(y[s:e].double().cpu().numpy(), yr[s:e]) <= tol, "sequence %d y" % i
+        assert rel_l2(fin[i].double().cpu().numpy(), fr[i]) <= tol or np.abs(fr[i]).max() == 0, "sequence %d final" % i
+
+
+@pytest.mark.parametrize("name,over,chunk,lengths,label", CASES, ids=[c[4] for c in CASES])
+def test_varlen_matches_oracle(name, over, chunk, lengths, label):
+    _run(name, over, chunk, lengths, label)
+
+
+def test_varlen_equals_batched_forward_for_equal_lengths():
+    """Equal lengths: a packed batch is a [batch][seqlen] batch laid out flat; ssd_forward_varlen
+    and ssd_forward take the same kernels and give the same bits."""
+    cfg = ssd_inputs.config("mamba2_layer", batch=3, seqlen=300, nheads=4, init=True)
+    announce("varlen equal lengths vs batched")
+    inp = ssd_inputs.make_inputs(cfg, 43)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    yb, fb = ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g.get("D"), chunk=128,
+                             init_state=g["init_state"], final_state=True)
+    cu = torch.arange(0, 4 * 300, 300, dtype=torch.int64, device="cuda")
+    yv, fv, _ = ssd.ssd_forward_varlen(g["x"].reshape(900, 4, 64), g["log_a"].reshape(900, 4),
+                                       g["B"].reshape(900, 1, 128), g["C"].reshape(900, 1, 128), cu, 300, g.get("D"),
+                                       chunk=128, init_state=g["init_state"], final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(yv.reshape(3, 300, 4, 64), yb) and torch.equal(fv, fb)
+
+
+def test_varlen_all_empty_and_clamped_offsets():
+    """No tokens at all: every final state is its initial state.  Offsets past the token count and
+    a sequence longer than max_seqlen are clamped (the header's contract): the result is that of the
+    clamped sequences, and rows past the clamped end are left as they were."""
+    cfg = ssd_inputs.config("mamba2_layer", nheads=2, init=True)
+    announce("varlen all-empty")
+    p = ssd_inputs.packed_inputs(cfg, [0, 0, 0], 44)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    _, fin, _ = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], g["cu_seqlens"], 0, g.get("D"),
+                                       chunk=128, init_state=g["init_state"], final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, g["init_state"])
+
+    announce("varlen clamped offsets")
+    p = ssd_inputs.packed_inputs(cfg, [50, 150], 45)      # 200 tokens
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    cu = torch.tensor([0, 50, 500], dtype=torch.int64, device="cuda")   # ends past the 200 tokens
+    y = torch.full((200, 2, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    _, fin, _ = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], cu, 120, g.get("D"), chunk=128,
+                                       init_state=g["init_state"], y=y, final_state=True)
+    torch.cuda.synchronize()
+    # as the clamped batch: [0, 50) and [50, 170)
+    yr, fr = oracle.varlen.forward_varlen(oracle.default_oracle(), f64(p["x"][:170]), f64(p["log_a"][:170]),
+                                          f64(p["B"][:170]), f64(p["C"][:170]), np.array([0, 50, 170]),
+                                          f64(p.get("D")), f64(p["init_state"]))
+    assert rel_l2(y[:170].double().cpu().numpy(), yr) <= TOL["bf16"]
+    assert rel_l2(fin.double().cpu().numpy(), fr) <= TOL["bf16"]
+    assert bool((y[170:] == 7.0).all())
