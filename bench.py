@@ -135,8 +135,9 @@ def fast_segments(cfg, target=512):
     return -(-nch // per)
 
 
-def kernel_names(cfg, front_end="log_a"):
-    """Kernels one forward launches, in order (mirrors the library's dispatch)."""
+def kernel_names(cfg, front_end="log_a", segmented=True):
+    """Kernels one forward launches, in order (mirrors the library's dispatch; a packed
+    variable-length batch is never segmented)."""
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
     if front_end == "dt":
         fused = (cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64)) if cfg["decay"] == "diag" \
@@ -145,14 +146,14 @@ def kernel_names(cfg, front_end="log_a"):
             return ["discretize_kernel"] + kernel_names(cfg) + (["skip_kernel"] if cfg["skip"] else [])
     if cfg["decay"] == "diag":
         if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
-            if fast_segments(dict(cfg, chunk=64), 512) > 1:
+            if segmented and fast_segments(dict(cfg, chunk=64), 512) > 1:
                 return ["walk_diag_pipe_kernel<%d,%d,state>" % (N, P), "seg_prefix_kernel",
                         "walk_diag_pipe_kernel<%d,%d>" % (N, P)]
             return ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]
         return ["walk_diag_kernel<%d,%d>" % (N, P)]
     if cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256):
         q = min(Q, 128)
-        if fast_segments(cfg) > 1:
+        if segmented and fast_segments(cfg) > 1:
             return ["prep_kernel<%d,%d>" % (N, q), "seg_state_kernel<%d,%d>" % (N, q),
                     "walk_fast_kernel<%d,%d>" % (N, q)]
         return ["prep_kernel<%d,%d>" % (N, q), "walk_fast_kernel<%d,%d>" % (N, q)]
@@ -417,6 +418,114 @@ def run_backward(args, cfg, inp, dev):
     print(json.dumps(result), flush=True)
 
 
+def run_varlen(args, cfg, dev):
+    """One JSON line for ssd_forward_varlen: the workload's tokens split into args.varlen
+    sequences of a seeded log-normal length mix, packed on one token axis; tokens/s of the whole
+    packed forward, the dominant kernel against HBM, and the oracle's per-sequence recurrence on
+    the host's cores."""
+    import torch
+    import ssd_inputs
+    import ssd_chunked_scan_02_amd as ssd
+    seed = ssd_inputs.SEEDS[args.workload]
+    total = cfg["batch"] * cfg["seqlen"]
+    lengths = ssd_inputs.packed_lengths(args.varlen, total, seed)
+    p = ssd_inputs.packed_inputs(cfg, lengths, seed)
+    nseq, maxT = len(lengths), p["max_seqlen"]
+    H, N, P = cfg["nheads"], cfg["dstate"], cfg["headdim"]
+    flops, nbytes, per_token = algorithmic_counts(cfg)
+    states = 4 * H * N * P * (int(cfg["init"]) + int(cfg["final"]))
+    nbytes += (nseq - cfg["batch"]) * states
+    copies = args.copies or min(64, max(2, math.ceil(1.0e9 / nbytes)))
+    log("workload %s packed into %d sequences (lengths %d..%d, max %d): %.1f MB algorithmic per step, %d copies"
+        % (args.workload, nseq, min(lengths), max(lengths), maxT, nbytes / 1e6, copies))
+    cu = p["cu_seqlens"].to(dev)
+    bufs = []
+    for _ in range(copies):
+        g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in p.items()}
+        g["y"] = torch.empty_like(g["x"])
+        g["final"] = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev) if cfg["final"] else None
+        bufs.append(g)
+    dims = ssd.varlen_dims(bufs[0]["x"], bufs[0]["log_a"], bufs[0]["B"], nseq, maxT)
+    ws = torch.empty(max(1, ssd.ssd_forward_varlen_workspace_bytes(dims, cfg["chunk"])), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = HipEvents()
+
+    def step(i, events=None):
+        g = bufs[i % copies]
+        return ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], cu, maxT, g.get("D"), chunk=cfg["chunk"],
+                                      init_state=g.get("init_state"), y=g["y"], final_state=g["final"], workspace=ws,
+                                      stream=stream, events=events)[2]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    begin, end = ev.create(), ev.create()
+    ev.lib.hipEventRecord(begin, stream.cuda_stream)
+    for i in range(K):
+        step(i)
+    ev.lib.hipEventRecord(end, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(begin, end) / K
+    step_events = [[ev.create() for _ in range(2 * ssd.SSD_MAX_LAUNCHES)] for _ in range(K)]
+    launches = None
+    for i in range(K):
+        launches = step(i, step_events[i])
+    torch.cuda.synchronize()
+    per_kernel = [[ev.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in step_events] for k in range(launches)]
+    for e in step_events:
+        for h in e:
+            ev.destroy(h)
+    kernel_avg = [sum(v) / len(v) for v in per_kernel]
+    names = kernel_names(cfg, segmented=False)
+    if len(names) != launches:
+        names = ["launch%d" % k for k in range(launches)]
+    dom = max(range(launches), key=lambda k: kernel_avg[k])
+    log("varlen ms/step %.4f; per kernel avg ms: %s" % (ms, ", ".join("%s %.4f" % kv for kv in zip(names, kernel_avg))))
+    if args.calibrate_copy_mib:
+        calibrate_copy(dev, args.calibrate_copy_mib)
+    if names[dom].startswith("walk_fast_kernel"):
+        dom_bytes = total * (H * P * 4 + 4 * H) + (4 * H if cfg["skip"] else 0) + nseq * states
+    else:
+        dom_bytes = nbytes
+    achieved = dom_bytes / (kernel_avg[dom] / 1e3) / 1e9
+    result = {
+        "metric": "SSD forward tokens/s, packed variable-length batch (ssd_forward_varlen)",
+        "value": total / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded; the workload's value distributions on one packed token axis, lengths log-normal)",
+        "config": {"workload": args.workload, "varlen_sequences": nseq, "tokens": total, "max_seqlen": maxT,
+                   "min_seqlen": min(lengths), "nheads": H, "ngroups": cfg["ngroups"], "headdim": P, "dstate": N,
+                   "chunk": cfg["chunk"], "decay": cfg["decay"], "parallelism": "single GPU"},
+        "kernels_ms": {n: t for n, t in zip(names, kernel_avg)},
+        "roofline": {"kernel": names[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload + "_varlen", names[dom]),
+                     "algorithmic_bytes_per_launch": dom_bytes, "tokens_per_launch": total},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        import oracle.varlen
+        f = ssd_inputs.to_f64
+        a = [f(p["x"]), f(p["log_a"]), f(p["B"]), f(p["C"])]
+        threads = oracle.default_threads()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.varlen.forward_varlen(oracle.default_oracle(), *a, p["cu_seqlens"].numpy(), f(p.get("D")),
+                                         f(p.get("init_state")), want_final=cfg["final"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        result["cpu_baseline"] = {"value": total * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "sample": "the whole packed batch (%d tokens in %d sequences x %d heads), %d run(s) "
+                                            "in %.1f s, fp64 recurrence per sequence, OpenMP over heads"
+                                            % (total, nseq, H, reps, el)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +536,8 @@ def main():
                     help="time ssd_backward (the gradients) instead of the forward pass")
     ap.add_argument("--front-end", choices=("log_a", "dt"), default="log_a",
                     help="decay input: log a (ssd_forward), or dt and A_log (ssd_forward_dt)")
+    ap.add_argument("--varlen", type=int, default=0,
+                    help="time ssd_forward_varlen: the workload's tokens packed as this many sequences")
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -451,6 +562,8 @@ def main():
     inp = ssd_inputs.make_inputs(cfg, seed)
     if args.backward:
         return run_backward(args, cfg, inp, dev)
+    if args.varlen:
+        return run_varlen(args, cfg, dev)
     fe = args.front_end
     flops, nbytes, per_token = algorithmic_counts(cfg, fe)
     copies = args.copies or min(64, max(2, math.ceil(1.0e9 / nbytes)))
