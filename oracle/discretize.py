@@ -95,7 +95,7 @@ def backward_dt(adj, x, dt, A_log, Bm, Cm, D=None, dt_bias=None, scale_input=Tru
     if D is not None:
         dx = dx + np.asarray(D, dtype=np.float64)[None, None, :, None] * dy
     if diag:
-        ddelta = np.sum(g["dlog_a"] * A[None, None, :, :], axis=-1)
+        ddelta = np.einsum("bthn,hn->bth", g["dlog_a"], A)
     else:
         ddelta = g["dlog_a"] * A[None, None, :]
     if scale_input:

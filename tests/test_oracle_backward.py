@@ -82,9 +82,9 @@ DT_MUTANTS = {
     "dA_log_uses_delta": ("np.sum(g[\"dlog_a\"] * log_a, axis=(0, 1))", "np.sum(g[\"dlog_a\"] * delta, axis=(0, 1))"),
     "bias_not_in_sigmoid": ("u = u + np.asarray(dt_bias, dtype=np.float64)[None, None, :]", "u = u"),
     "dD_on_scaled_input": ("dD=np.einsum(\"bthp,bthp->h\", dy, x)", "dD=np.einsum(\"bthp,bthp->h\", dy, xin)"),
-    "diag_rates_summed_first": ("ddelta = np.sum(g[\"dlog_a\"] * A[None, None, :, :], axis=-1)",
+    "diag_rates_summed_first": ("ddelta = np.einsum(\"bthn,hn->bth\", g[\"dlog_a\"], A)",
                                 "ddelta = np.sum(g[\"dlog_a\"], axis=-1) * np.mean(A, axis=-1)[None, None, :]"),
-    "diag_one_rate": ("ddelta = np.sum(g[\"dlog_a\"] * A[None, None, :, :], axis=-1)",
+    "diag_one_rate": ("ddelta = np.einsum(\"bthn,hn->bth\", g[\"dlog_a\"], A)",
                       "ddelta = np.sum(g[\"dlog_a\"], axis=-1) * A[None, None, :, 0]"),
 }
 
