@@ -189,10 +189,10 @@ int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float
  *   dims->seqlen: a bound on every sequence's length (the longest one's length is the natural
  *     choice); it sizes the workspace, which is that of a [batch][seqlen] batch without the
  *     segmented walks.  Tokens past that bound are neither read nor written.
- *   chunk, shapes, dtypes and decay kinds as ssd_forward; no discretisation front-end.
+ *   chunk, shapes, dtypes and decay kinds as ssd_forward.
  *   events, n_events, n_launches: as ssd_forward_profiled (NULL, 0, NULL: no timing).
- * Returns as ssd_forward; SSD_ERR_INVALID also for total_tokens < 0 or a NULL or misaligned
- * cu_seqlens with batch > 0.
+ * Returns as ssd_forward; SSD_ERR_INVALID also for total_tokens < 0 or above batch * seqlen, or a
+ * NULL or misaligned cu_seqlens with batch > 0.
  */
 size_t ssd_forward_varlen_workspace_bytes(const ssd_dims* dims, int chunk);
 
@@ -201,6 +201,17 @@ int ssd_forward_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t 
                        const float* D, int chunk, const float* init_state, void* y,
                        float* final_state, void* workspace, size_t workspace_bytes, void* stream,
                        void* const* events, int n_events, int* n_launches);
+
+/* ssd_forward_varlen with the discretisation front-end, as ssd_forward_dt: dt [total,H], dt_bias
+ * [H] (may be NULL), A_log [H] or [H,N], scale_input; the workspace from its own query. */
+size_t ssd_forward_dt_varlen_workspace_bytes(const ssd_dims* dims, int chunk, int scale_input);
+
+int ssd_forward_dt_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                          const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                          int scale_input, const void* B, const void* C, const float* D, int chunk,
+                          const float* init_state, void* y, float* final_state, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                          int* n_launches);
 
 /*
  * The backward pass of ssd_forward: the gradients of L = <dy, y> + <dfinal,

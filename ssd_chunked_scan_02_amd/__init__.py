@@ -110,6 +110,11 @@ def load_library():
         lib.ssd_forward_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz,
                                            vp, ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
         lib.ssd_forward_varlen.restype = i32
+        lib.ssd_forward_dt_varlen_workspace_bytes.argtypes = [dp, i32, i32]
+        lib.ssd_forward_dt_varlen_workspace_bytes.restype = sz
+        lib.ssd_forward_dt_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp,
+                                              vp, vp, sz, vp, ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
+        lib.ssd_forward_dt_varlen.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -286,6 +291,62 @@ def ssd_forward_varlen(x, log_a, B, C, cu_seqlens, max_seqlen: int, D=None, chun
                                 ctypes.byref(count))
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_forward_varlen")
+    return y, final_state, (count.value if events is not None else None)
+
+
+def ssd_forward_dt_varlen_workspace_bytes(dims: Dims, chunk: int, scale_input: bool = True) -> int:
+    return int(load_library().ssd_forward_dt_varlen_workspace_bytes(ctypes.byref(dims), int(chunk),
+                                                                    1 if scale_input else 0))
+
+
+def ssd_forward_dt_varlen(x, dt, A_log, B, C, cu_seqlens, max_seqlen: int, D=None, dt_bias=None,
+                          scale_input: bool = True, chunk: int = 64, init_state=None, y=None, final_state=None,
+                          workspace=None, stream=None, events=None):
+    """Run ``ssd_forward_dt_varlen``: ssd_forward_varlen with log a = -softplus(dt + dt_bias)
+    exp(A_log) and (scale_input) the input scale formed in the kernels.  dt [T,H] fp32; A_log [H]
+    or [H,N]; dt_bias [H] or None.  Returns (y, final_state, n_launches or None)."""
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    nseq = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or nseq < 0 or cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens must be a 1-D int64 tensor of nseq + 1 offsets on x's device")
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+    decay = SSD_DECAY_DIAG if A_log.dim() == 2 else SSD_DECAY_SCALAR
+    dims = Dims(int(nseq), int(max_seqlen), H, G, P, N, _DTYPE_CODE[x.dtype], decay)
+    _check(x, "x", (T, H, P), x.dtype, dev)
+    _check(dt, "dt", (T, H), torch.float32, dev)
+    _check(A_log, "A_log", (H, N) if decay == SSD_DECAY_DIAG else (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(B, "B", (T, G, N), x.dtype, dev)
+    _check(C, "C", (T, G, N), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (nseq, H, N, P), torch.float32, dev)
+    if y is None:
+        y = torch.empty((T, H, P), dtype=x.dtype, device=dev)
+    _check(y, "y", (T, H, P), x.dtype, dev)
+    if final_state is True:
+        final_state = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    _check(final_state, "final_state", (nseq, H, N, P), torch.float32, dev)
+    lib = load_library()
+    scale = 1 if scale_input else 0
+    need = int(lib.ssd_forward_dt_varlen_workspace_bytes(ctypes.byref(dims), int(chunk), scale))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    arr, n, count = None, 0, ctypes.c_int(0)
+    if events is not None:
+        n = max(len(events), 2 * SSD_MAX_LAUNCHES)
+        arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+    rc = lib.ssd_forward_dt_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(dt), _ptr(dt_bias),
+                                   _ptr(A_log), scale, _ptr(B), _ptr(C), _ptr(D), int(chunk), _ptr(init_state),
+                                   _ptr(y), _ptr(final_state), _ptr(workspace), ws_bytes,
+                                   _stream_handle(stream, dev), arr, n, ctypes.byref(count))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_forward_dt_varlen")
     return y, final_state, (count.value if events is not None else None)
 
 

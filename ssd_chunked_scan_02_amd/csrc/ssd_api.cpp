@@ -53,14 +53,15 @@ size_t workspace_needed(const ssd_dims* d, int chunk, bool varlen = false) {
 }
 
 // Workspace of ssd_forward_dt: the fused paths need what ssd_forward needs (plus log2 of the
-// input scale on the scalar fast path); the generic composition adds log a and the scaled input.
-size_t workspace_needed_dt(const ssd_dims* d, int chunk, bool scale_input) {
+// input scale on the scalar fast path); the generic composition adds log a and the scaled input
+// (for a packed batch, rows for batch * seqlen tokens, which bound its token count).
+size_t workspace_needed_dt(const ssd_dims* d, int chunk, bool scale_input, bool varlen = false) {
     if (d->seqlen == 0 || d->batch == 0) return 0;
     const int N = (int)d->dstate, P = (int)d->headdim;
     if (ssd::discretization_fused(d->dtype, d->decay, N, P, chunk, d->nheads, d->ngroups)) {
         if (d->decay == SSD_DECAY_DIAG)
-            return ssd::diag_workspace_bytes(d->dtype, d->batch, d->nheads, d->seqlen, N, P, chunk);
-        return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, d->seqlen, N, chunk, scale_input);
+            return ssd::diag_workspace_bytes(d->dtype, d->batch, d->nheads, d->seqlen, N, P, chunk, varlen);
+        return ssd::fast_workspace_bytes(d->batch, d->nheads, d->ngroups, d->seqlen, N, chunk, scale_input, varlen);
     }
     const size_t own = ssd::generic_workspace_bytes(d->dtype, d->decay, d->batch, d->nheads, d->ngroups,
                                                     d->seqlen, N, P, chunk);
@@ -105,8 +106,8 @@ struct Varlen {
     int64_t total;
 };
 
-// ssd_forward (disc null: log_a given), ssd_forward_dt (disc set: log_a null) and
-// ssd_forward_varlen (vl set, disc null).
+// ssd_forward (disc null: log_a given), ssd_forward_dt (disc set: log_a null), and their packed
+// variable-length forms (vl set).
 int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Discretization* disc,
                  const void* B, const void* C, const float* D, int chunk, const float* init_state,
                  void* y, float* final_state, void* workspace, size_t workspace_bytes, void* stream,
@@ -116,7 +117,8 @@ int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Dis
     int rc = check_forward(d, chunk);
     if (rc != SSD_OK) return rc;
     if (vl) {
-        if (vl->total < 0 || vl->total > kMaxElems) return SSD_ERR_INVALID;
+        // (every sequence has at most seqlen tokens, so the packed axis has at most batch * seqlen)
+        if (vl->total < 0 || vl->total > kMaxElems || vl->total > d->batch * d->seqlen) return SSD_ERR_INVALID;
         if (d->batch > 0 && (!vl->cu_seqlens || ((uintptr_t)vl->cu_seqlens & 7u) != 0)) return SSD_ERR_INVALID;
         // (every packed tensor's element count must stay well inside int64, as for the batched form)
         if ((double)vl->total * (double)d->nheads * (double)(d->headdim > d->dstate ? d->headdim : d->dstate) >
@@ -131,7 +133,8 @@ int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Dis
                           disc ? disc->dt : nullptr, disc ? disc->dt_bias : nullptr, disc ? disc->A_log : nullptr};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return SSD_ERR_ALIGN;
-    const size_t need = disc ? workspace_needed_dt(d, chunk, disc->scale_input) : workspace_needed(d, chunk, vl != nullptr);
+    const size_t need = disc ? workspace_needed_dt(d, chunk, disc->scale_input, vl != nullptr)
+                             : workspace_needed(d, chunk, vl != nullptr);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
     if (d->batch == 0) return SSD_OK;
     if ((d->seqlen == 0 || (vl && vl->total == 0)) && !final_state) return SSD_OK;
@@ -219,6 +222,22 @@ int ssd_forward_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t 
                        void* stream, void* const* events, int n_events, int* n_launches) {
     const Varlen vl{cu_seqlens, total_tokens};
     return forward_impl(dims, x, log_a, nullptr, B, C, D, chunk, init_state, y, final_state, workspace,
+                        workspace_bytes, stream, events, n_events, n_launches, &vl);
+}
+
+size_t ssd_forward_dt_varlen_workspace_bytes(const ssd_dims* dims, int chunk, int scale_input) {
+    if (check_forward(dims, chunk) != SSD_OK) return 0;
+    return workspace_needed_dt(dims, chunk, scale_input != 0, true);
+}
+
+int ssd_forward_dt_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens, const void* x,
+                          const float* dt, const float* dt_bias, const float* A_log, int scale_input, const void* B,
+                          const void* C, const float* D, int chunk, const float* init_state, void* y,
+                          float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events, int n_events, int* n_launches) {
+    const Varlen vl{cu_seqlens, total_tokens};
+    const Discretization disc{dt, dt_bias, A_log, scale_input != 0};
+    return forward_impl(dims, x, nullptr, &disc, B, C, D, chunk, init_state, y, final_state, workspace,
                         workspace_bytes, stream, events, n_events, n_launches, &vl);
 }
 

@@ -441,7 +441,9 @@ int launch_forward_discretized_t(const ForwardLaunch& fl, hipStream_t stream) {
     char* ws = reinterpret_cast<char*>(fl.scores);
     float* la = reinterpret_cast<float*>(ws + lay.la);
     T* xs = fl.scale_input ? reinterpret_cast<T*>(ws + lay.xs) : nullptr;
-    const int64_t tokens = fl.batch * fl.seqlen * fl.nheads;
+    // (a packed batch: its tokens, which the caller's contract keeps within batch * seqlen, the
+    // size of the workspace rows)
+    const int64_t tokens = (fl.seq_off ? fl.total : fl.batch * fl.seqlen) * fl.nheads;
     const int64_t work = tokens * (K > P ? K : P);
     const unsigned grid = (unsigned)std::min<int64_t>((work + kThreads - 1) / kThreads, 8192);
     int k = fl.first_launch;

@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["ssd_backward", "ssd_backward_dt", "ssd_backward_dt_workspace_bytes",
                                     "ssd_backward_profiled", "ssd_backward_workspace_bytes",
                                     "ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
+                                    "ssd_forward_dt_varlen", "ssd_forward_dt_varlen_workspace_bytes",
                                     "ssd_forward_dt_workspace_bytes", "ssd_forward_profiled",
                                     "ssd_forward_varlen", "ssd_forward_varlen_workspace_bytes",
                                     "ssd_forward_workspace_bytes", "ssd_step", "ssd_step_dt",
@@ -350,5 +351,22 @@ def test_varlen_rejects_bad_arguments(lib):
     assert call_varlen(lib, d, ws_bytes=need - 1) == ssd.SSD_ERR_INVALID
     assert call_varlen(lib, mamba2_dims(dstate=48)) == ssd.SSD_ERR_UNSUPPORTED
     # nothing to do: no sequences, or no tokens and no final state wanted (no HIP call)
-    assert call_varlen(lib, mamba2_dims(batch=0), cu=None) == ssd.SSD_OK
+    assert call_varlen(lib, mamba2_dims(batch=0), cu=None, total=0) == ssd.SSD_OK
     assert call_varlen(lib, d, total=0, x=None, la=None, B=None, C=None, y=None) == ssd.SSD_OK
+
+
+def test_dt_varlen_workspace_and_checks(lib):
+    # the fused paths: the packed log a form's workspace (plus log2 of the input scale on the scalar
+    # fast path); the generic composition adds rows for batch * seqlen tokens
+    d = mamba2_dims(batch=4, seqlen=512)
+    assert ssd.ssd_forward_dt_varlen_workspace_bytes(d, 128, False) == ssd.ssd_forward_varlen_workspace_bytes(d, 128)
+    assert ssd.ssd_forward_dt_varlen_workspace_bytes(d, 128, True) == \
+        ssd.ssd_forward_varlen_workspace_bytes(d, 128) + 4 * 24 * 4 * 128 * 4
+    g = mamba2_dims(batch=2, seqlen=300, nheads=3, dtype=0, dstate=16)
+    assert ssd.ssd_forward_dt_varlen_workspace_bytes(g, 64, True) == ssd.ssd_forward_dt_workspace_bytes(g, 64, True)
+    fn = lib.ssd_forward_dt_varlen
+    args = lambda dims, total: (ctypes.byref(dims), FAKE, total, FAKE, FAKE, None, FAKE, 1, FAKE, FAKE, None, 128,
+                                None, FAKE, None, FAKE, 1 << 30, None, None, 0, None)
+    assert fn(*args(d, 4 * 512 + 1)) == ssd.SSD_ERR_INVALID        # more tokens than batch * seqlen
+    assert fn(*args(d, -1)) == ssd.SSD_ERR_INVALID
+    assert call_varlen(lib, d, total=4 * 512 + 1) == ssd.SSD_ERR_INVALID

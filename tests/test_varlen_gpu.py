@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.discretize
 import oracle.varlen
 import ssd_inputs
 import ssd_chunked_scan_02_amd as ssd
@@ -106,3 +107,42 @@ def test_varlen_all_empty_and_clamped_offsets():
     assert rel_l2(y[:170].double().cpu().numpy(), yr) <= TOL["bf16"]
     assert rel_l2(fin.double().cpu().numpy(), fr) <= TOL["bf16"]
     assert bool((y[170:] == 7.0).all())
+
+
+DT_CASES = [
+    ("mamba2_layer", dict(nheads=4, init=True), 128, [300, 0, 129, 1000, 57], True, "fast-dt"),
+    ("mamba2_layer", dict(nheads=4, init=False), 64, [70, 1, 640], False, "fast-dt-unscaled"),
+    ("diag_multiscale", dict(nheads=2, init=True, a_log="rand_hn"), 64, [200, 0, 517], True, "diag-pipe-dt"),
+    ("tiny_fp32", dict(nheads=3, skip=True, init=True, a_log="uniform16", dt_mean=-1.0), 64, [90, 0, 257, 1], True,
+     "generic-fp32-dt"),
+    ("diag_multiscale", dict(nheads=2, dstate=16, headdim=32, dtype="fp32", init=True, a_log="rand_hn"), 32,
+     [77, 140], True, "generic-diag-fp32-dt"),
+]
+
+
+@pytest.mark.parametrize("name,over,chunk,lengths,scale,label", DT_CASES, ids=[c[5] for c in DT_CASES])
+def test_dt_varlen_matches_oracle(name, over, chunk, lengths, scale, label):
+    """ssd_forward_dt_varlen against the oracle's discretisation (oracle.discretize) followed by
+    its per-sequence recurrence, with D x on the raw x."""
+    cfg = ssd_inputs.config(name, **over)
+    announce("dt varlen %s lengths=%s chunk=%d scale=%d" % (label, lengths, chunk, scale))
+    p = ssd_inputs.packed_inputs(cfg, lengths, 47)
+    bias = ssd_inputs.dt_bias(cfg["nheads"], 48)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    y, fin, _ = ssd.ssd_forward_dt_varlen(g["x"], g["dt"], g["A_log"], g["B"], g["C"], g["cu_seqlens"],
+                                          p["max_seqlen"], g.get("D"), dt_bias=bias.cuda(), scale_input=scale,
+                                          chunk=chunk, init_state=g.get("init_state"), final_state=True)
+    torch.cuda.synchronize()
+    diag = cfg["decay"] == "diag"
+    delta, la = oracle.discretize.discretize(f64(p["dt"])[None], f64(p["A_log"]), f64(bias), diag)
+    x = f64(p["x"])
+    xin = x * delta[0][..., None] if scale else x
+    yr, fr = oracle.varlen.forward_varlen(oracle.default_oracle(), xin, la[0], f64(p["B"]), f64(p["C"]),
+                                          p["cu_seqlens"].numpy(), None, f64(p.get("init_state")))
+    if p.get("D") is not None:
+        yr = yr + f64(p["D"])[None, :, None] * x
+    tol = TOL[cfg["dtype"]]
+    ey = rel_l2(y.double().cpu().numpy(), yr)
+    ef = rel_l2(fin.double().cpu().numpy(), fr)
+    announce("dt varlen %s: y %.2e final %.2e (tol %.0e)" % (label, ey, ef, tol))
+    assert ey <= tol and ef <= tol, (ey, ef)
