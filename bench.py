@@ -88,6 +88,7 @@ class HipEvents:
 # the source file each kernel (by name prefix) and its launch code are compiled from
 KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.hip",
                   "seg_state_kernel": "ssd_fast.hip", "seg_prefix_kernel": "ssd_fast.hip",
+                  "seq_order_kernel": "ssd_fast.hip",
                   "walk_diag_pipe_kernel": "ssd_diag.hip", "walk_diag_kernel": "ssd_diag.hip",
                   "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
                   "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
@@ -135,9 +136,10 @@ def fast_segments(cfg, target=512):
     return -(-nch // per)
 
 
-def kernel_names(cfg, front_end="log_a", segmented=True):
+def kernel_names(cfg, front_end="log_a", segmented=True, packed=0):
     """Kernels one forward launches, in order (mirrors the library's dispatch; a packed
-    variable-length batch is never segmented)."""
+    variable-length batch of `packed` sequences is never segmented, and on the fast path up to 4096
+    of them are first ranked by length)."""
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
     if front_end == "dt":
         fused = (cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64)) if cfg["decay"] == "diag" \
@@ -156,7 +158,8 @@ def kernel_names(cfg, front_end="log_a", segmented=True):
         if segmented and fast_segments(cfg) > 1:
             return ["prep_kernel<%d,%d>" % (N, q), "seg_state_kernel<%d,%d>" % (N, q),
                     "walk_fast_kernel<%d,%d>" % (N, q)]
-        return ["prep_kernel<%d,%d>" % (N, q), "walk_fast_kernel<%d,%d>" % (N, q)]
+        order = ["seq_order_kernel"] if 0 < packed <= 4096 else []
+        return order + ["prep_kernel<%d,%d>" % (N, q), "walk_fast_kernel<%d,%d>" % (N, q)]
     return ["scores_kernel<%d>" % N, "walk_kernel<%d,%d>" % (N, P)]
 
 
@@ -484,7 +487,7 @@ def run_varlen(args, cfg, dev):
         for h in e:
             ev.destroy(h)
     kernel_avg = [sum(v) / len(v) for v in per_kernel]
-    names = kernel_names(cfg, segmented=False)
+    names = kernel_names(cfg, segmented=False, packed=nseq)
     if len(names) != launches:
         names = ["launch%d" % k for k in range(launches)]
     dom = max(range(launches), key=lambda k: kernel_avg[k])

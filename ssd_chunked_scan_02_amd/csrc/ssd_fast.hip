@@ -776,11 +776,39 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     }
 }
 
+// Ranks of a packed batch's sequences by length, longest first (ties by index): order[rank] = b.
+// Every workgroup stages all the (at most kOrderMax) lengths in LDS; one thread per sequence then
+// counts the sequences ahead of it, every lane reading the same length at each step.
+constexpr int64_t kOrderMax = 4096;
+__global__ void __launch_bounds__(kThreads) seq_order_kernel(const int64_t* seq_off, int64_t nseq, int64_t seqlen,
+                                                             int64_t total, int* order) {
+    __shared__ int lens[kOrderMax];
+    for (int64_t j = threadIdx.x; j < nseq; j += kThreads) lens[j] = (int)seq_span(seq_off, j, seqlen, total).len;
+    __syncthreads();
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= nseq) return;
+    const int li = lens[i];
+    int rank = 0;
+    for (int j = 0; j < (int)nseq; ++j) rank += (lens[j] > li || (lens[j] == li && j < (int)i)) ? 1 : 0;
+    order[rank] = (int)i;
+}
+
+// The work index of workgroup bid of a packed batch's walk: the sequences go to the 8 XCDs in
+// turn in seq_order's order (longest first), and each XCD runs the heads of its sequences one
+// sequence after another, so every XCD gets a like share of the work, the longest sequences start
+// first, and the heads of a sequence share one L2.  -1 past the last sequence.
+__device__ __forceinline__ int64_t packed_work_index(const Walk2Params& prm, int64_t bid) {
+    const int64_t x = bid % 8, l = bid / 8, r = x + 8 * (l / prm.nheads);
+    if (r >= prm.batch) return -1;
+    return (int64_t)prm.seq_order[r] * prm.nheads + l % prm.nheads;
+}
+
 // DT: with log2 of an input scale per token (prm.lg_t, the discretisation front-end's Delta):
 // the input side of every factor carries it, so the input term is Delta_s B_s x_s^T.
 template <int N, int Q, bool DT>
 __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm) {
-    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
+    const int64_t work = prm.seq_order ? packed_work_index(prm, blockIdx.x)
+                                       : xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
     if (work < 0) return;
     const WalkSpan span = walk_span(prm, work, Q);
     if (span.c1 <= span.c0) {
@@ -1014,7 +1042,7 @@ bool allow_full_lds(const void* kernel, bool* done) {
 struct FastLayout {
     int64_t nchunks, nblk, units;
     int nseg, seg_chunks;
-    size_t pairs, bt, ct, la_t, lg_t, seg_state, seg_decay, total;
+    size_t pairs, bt, ct, la_t, lg_t, seg_state, seg_decay, order, total;
 };
 
 // (with_lg: log2 of the input scale head-major, laid out as la_t; varlen: a packed
@@ -1045,6 +1073,9 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
         l.seg_state = off; off += (size_t)l.nseg * l.units * N * kP * 4;
         l.seg_decay = off; off += ((size_t)l.nseg * l.units * 4 + 255) / 256 * 256;
     }
+    // a packed batch of at most kOrderMax sequences: their order, longest first
+    l.order = off;
+    if (varlen && batch <= kOrderMax) off += ((size_t)batch * 4 + 255) / 256 * 256;
     l.total = off;
     return l;
 }
@@ -1072,14 +1103,20 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     // split each block over two workgroups when even then they fit on the CUs at once
     pp.split = 2 * lay.nblk <= kPrepSplitMax ? 1 : 0;
     const unsigned pgrid = pp.split ? (unsigned)((lay.nblk + 7) / 8 * 16) : (unsigned)lay.nblk;
+    // (a packed batch: the sequences ranked longest first, for the walk's workgroup order)
+    int* order = (fl.seq_off && fl.batch <= kOrderMax) ? reinterpret_cast<int*>(ws + lay.order) : nullptr;
+    if (order && !launch_k(fl, k, seq_order_kernel, dim3((unsigned)((fl.batch + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, fl.seq_off, fl.batch, fl.seqlen, fl.total, order))
+        return -1;
     if (!launch_k(fl, k, prep_kernel<N, Q>, dim3(pgrid), dim3(pthreads), plds, stream, pp)) return -1;
 
     const int64_t work = lay.nseg * lay.units;
-    const int64_t per_xcd = (work + 7) / 8;
+    // (ordered packed walk: ceil(batch / 8) sequences' heads per XCD)
+    const int64_t per_xcd = order ? (fl.batch + 7) / 8 * fl.nheads : (work + 7) / 8;
     Walk2Params wp{fl.x, la_t, lg_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, nch, per_xcd,
                    lay.seg_chunks, lay.nseg, reinterpret_cast<float*>(ws + lay.seg_state),
-                   reinterpret_cast<float*>(ws + lay.seg_decay), fl.seq_off, fl.total};
+                   reinterpret_cast<float*>(ws + lay.seg_decay), fl.seq_off, fl.total, order};
     if (lay.nseg > 1) {
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         const int64_t state_work = (lay.nseg - 1) * lay.units;

@@ -113,9 +113,11 @@ struct Walk2Params {
     int seg_chunks, nseg;
     float* seg_state;
     float* seg_decay;
-    // packed variable-length batch (null: batched layout; never segmented), as in ForwardLaunch
+    // packed variable-length batch (null: batched layout; never segmented), as in ForwardLaunch;
+    // seq_order (or null): the sequences longest first, dealt round-robin to the XCDs by the walk
     const int64_t* seq_off;
     int64_t total;
+    const int* seq_order;
 };
 
 // Everything one forward call needs, already validated.

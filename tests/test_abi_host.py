@@ -331,8 +331,12 @@ def call_varlen(lib, dims, cu=FAKE, total=1000, ws_bytes=1 << 30, **over):
 def test_varlen_workspace_bytes(lib):
     # a [batch][seqlen] batch's workspace without segmented walks: the same as ssd_forward's when
     # the batched walk is not segmented either, less when it is
+    # (and on the fast path, for at most 4096 sequences, their order by length: 4 bytes each)
     many = mamba2_dims(batch=64, seqlen=1000)
-    assert ssd.ssd_forward_varlen_workspace_bytes(many, 128) == ssd.ssd_forward_workspace_bytes(many, 128)
+    up = lambda v: (v + 255) // 256 * 256
+    assert ssd.ssd_forward_varlen_workspace_bytes(many, 128) == ssd.ssd_forward_workspace_bytes(many, 128) + up(64 * 4)
+    lots = mamba2_dims(batch=5000, seqlen=64)
+    assert ssd.ssd_forward_varlen_workspace_bytes(lots, 128) == ssd.ssd_forward_workspace_bytes(lots, 128)
     few = mamba2_dims(batch=1, seqlen=65536, nheads=32)
     assert 0 < ssd.ssd_forward_varlen_workspace_bytes(few, 128) < ssd.ssd_forward_workspace_bytes(few, 128)
     dd = mamba2_dims(decay=1, dstate=64, batch=1, nheads=2, seqlen=4096)
