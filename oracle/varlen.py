@@ -47,3 +47,37 @@ def forward_varlen(orc, x, log_a, Bm, Cm, cu_seqlens, D=None, init_states=None, 
         if want_final:
             finals[i] = fi[0]
     return y, finals
+
+
+def backward_varlen(adj, x, log_a, Bm, Cm, cu_seqlens, D=None, init_states=None, dy=None, dfinal=None):
+    """Gradients of <dy, y> + <dfinal, finals> for ``forward_varlen``: every sequence through the
+    fp64 adjoint of ``ssd_oracle_bwd.c`` (``adj``, an ``oracle.backward.Adjoint``) by itself.
+    Each token's dx, dlog_a, dB and dC come from its own sequence; dD sums over all of them; dinit
+    [nseq,H,N,P] is each sequence's (dfinal[i] for an empty one).  Returns a dict of float64
+    arrays."""
+    x = np.asarray(x, dtype=np.float64)
+    log_a = np.asarray(log_a, dtype=np.float64)
+    Bm = np.asarray(Bm, dtype=np.float64)
+    Cm = np.asarray(Cm, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    T, H, P = x.shape
+    N = Bm.shape[2]
+    cu = check_cu_seqlens(cu_seqlens, T)
+    nseq = cu.size - 1
+    out = dict(dx=np.zeros_like(x), dlog_a=np.zeros_like(log_a), dB=np.zeros_like(Bm), dC=np.zeros_like(Cm),
+               dD=np.zeros(H), dinit=np.zeros((nseq, H, N, P)))
+    for i in range(nseq):
+        s = int(cu[i])
+        e = int(cu[i + 1])
+        fin = None if dfinal is None else np.asarray(dfinal, dtype=np.float64)[i:i + 1]
+        if e == s:
+            if fin is not None:
+                out["dinit"][i] = fin[0]
+            continue
+        init = None if init_states is None else np.asarray(init_states, dtype=np.float64)[i][None]
+        g = adj.backward(x[None, s:e], log_a[None, s:e], Bm[None, s:e], Cm[None, s:e], D, init, dy[None, s:e], fin)
+        for k in ("dx", "dlog_a", "dB", "dC"):
+            out[k][s:e] = g[k][0]
+        out["dD"] += g["dD"]
+        out["dinit"][i] = g["dinit"][0]
+    return out

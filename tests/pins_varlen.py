@@ -72,3 +72,33 @@ def pin_varlen_initial_states_closed_form(orc, vl):
 
 
 VARLEN_PINS = [pin_varlen_is_packed_run_with_resets, pin_varlen_initial_states_closed_form]
+
+
+def pin_varlen_backward_finite_differences(orc, vl, adj):
+    """backward_varlen against central differences (step 1e-6) of <dy, y> + <dfinal, finals> from
+    forward_varlen, along a random direction in each of x, log a, B, C, D and the initial states;
+    scalar and diagonal decay, lengths 0, 1 and longer."""
+    rng = np.random.default_rng(93)
+    for diag in (False, True):
+        lens = [6, 0, 1, 11]
+        H, G, P, N = 4, 2, 3, 5
+        cu, x, log_a, Bm, Cm, D = _packed(rng, lens, H=H, G=G, P=P, N=N, diag=diag)
+        h0 = rng.standard_normal((len(lens), H, N, P))
+        dy = rng.standard_normal(x.shape)
+        dfin = rng.standard_normal(h0.shape)
+        inp = dict(x=x, log_a=log_a, Bm=Bm, Cm=Cm, D=D, init=h0)
+
+        def loss(d):
+            y, fin = vl.forward_varlen(orc, d["x"], d["log_a"], d["Bm"], d["Cm"], cu, d["D"], d["init"])
+            return float(np.sum(dy * y) + np.sum(dfin * fin))
+
+        g = vl.backward_varlen(adj, x, log_a, Bm, Cm, cu, D, h0, dy, dfin)
+        names = dict(x="dx", log_a="dlog_a", Bm="dB", Cm="dC", D="dD", init="dinit")
+        eps = 1e-6
+        for name, gname in names.items():
+            v = rng.standard_normal(np.shape(inp[name]))
+            fd = (loss(dict(inp, **{name: inp[name] + eps * v})) - loss(dict(inp, **{name: inp[name] - eps * v}))) \
+                / (2 * eps)
+            an = float(np.sum(g[gname] * v))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), "%s (diag=%d): fd %.12g adjoint %.12g" % (
+                gname, diag, fd, an)

@@ -8,8 +8,9 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.backward
 import oracle.varlen
-from pins_varlen import VARLEN_PINS
+from pins_varlen import VARLEN_PINS, pin_varlen_backward_finite_differences
 
 
 @pytest.fixture(scope="module")
@@ -59,3 +60,31 @@ def test_varlen_mutant_is_caught(orc, name):
             except (AssertionError, ValueError):
                 caught.append(pin.__name__)
     assert caught, "planted mistake %r passed every pin" % name
+
+
+def test_varlen_backward_pin(orc):
+    pin_varlen_backward_finite_differences(orc, oracle.varlen, oracle.backward.default_adjoint())
+
+
+BWD_MUTANTS = {
+    "dD_of_last_sequence_only": ('        out["dD"] += g["dD"]', '        out["dD"] = g["dD"].copy()'),
+    "empty_drops_dfinal": ('            if fin is not None:\n                out["dinit"][i] = fin[0]\n', '            pass\n'),
+    "dfinal_of_first_for_all": ('np.asarray(dfinal, dtype=np.float64)[i:i + 1]', 'np.asarray(dfinal, dtype=np.float64)[0:1]'),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_varlen_backward_mutant_is_caught(orc, name):
+    before, after = BWD_MUTANTS[name]
+    with open(oracle.varlen.__file__) as f:
+        src = f.read()
+    assert src.count(before) == 1, "mutation site for %s must occur exactly once" % name
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "varlen_bwd_%s.py" % name)
+        with open(path, "w") as f:
+            f.write(src.replace(before, after))
+        spec = importlib.util.spec_from_file_location("varlen_bwd_%s" % name, path)
+        mutant = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mutant)
+        with pytest.raises(AssertionError):
+            pin_varlen_backward_finite_differences(orc, mutant, oracle.backward.default_adjoint())
