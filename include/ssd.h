@@ -253,6 +253,24 @@ int ssd_backward_profiled(const ssd_dims* dims, const void* x, const float* log_
                           void* stream, void* const* events, int n_events, int* n_launches);
 
 /*
+ * The backward pass of ssd_forward_varlen: a packed variable-length batch (the layouts, cu_seqlens,
+ * total_tokens and dims->seqlen bound of ssd_forward_varlen), every sequence's gradients taken by
+ * themselves: dx, dlog_a, dB, dC per packed token, dD summed over every sequence and head's tokens,
+ * dinit [batch,H,N,P] per sequence (dfinal [batch,H,N,P] per sequence, may be NULL).  Shapes,
+ * dtypes and decay kinds as ssd_backward; the workspace is ssd_backward's for these dims.
+ * events, n_events, n_launches as ssd_backward_profiled (NULL, 0, NULL: no timing).  Offsets are
+ * clamped as in ssd_forward_varlen.
+ */
+size_t ssd_backward_varlen_workspace_bytes(const ssd_dims* dims);
+
+int ssd_backward_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                        const void* x, const float* log_a, const void* B, const void* C,
+                        const float* D, const float* init_state, const void* dy,
+                        const float* dfinal, void* dx, float* dlog_a, float* dB, float* dC,
+                        float* dD, float* dinit, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* events, int n_events, int* n_launches);
+
+/*
  * The backward pass of ssd_forward_dt: the gradients of <dy, y> + <dfinal, final_state> with
  * respect to x, dt, A_log, dt_bias, B, C, D and init_state, by the chain rule through the
  * discretisation (Delta = softplus(dt + bias), log a = -Delta exp(A_log), and with scale_input the

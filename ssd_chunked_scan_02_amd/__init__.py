@@ -115,6 +115,11 @@ def load_library():
         lib.ssd_forward_dt_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp,
                                               vp, vp, sz, vp, ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
         lib.ssd_forward_dt_varlen.restype = i32
+        lib.ssd_backward_varlen_workspace_bytes.argtypes = [dp]
+        lib.ssd_backward_varlen_workspace_bytes.restype = sz
+        lib.ssd_backward_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 15 + [sz, vp, ctypes.POINTER(vp), i32,
+                                                                             ctypes.POINTER(i32)]
+        lib.ssd_backward_varlen.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -510,6 +515,50 @@ def ssd_backward(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, want_
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_backward")
     return out if _events is None else (out, count.value)
+
+
+def ssd_backward_varlen(x, log_a, B, C, dy, cu_seqlens, max_seqlen: int, D=None, init_state=None, dfinal=None,
+                        want_dD=True, want_dinit=True, workspace=None, stream=None, events=None):
+    """Run ``ssd_backward_varlen``: gradients of <dy, y> + <dfinal, final_states> for
+    ssd_forward_varlen on the packed batch (x [T,H,P], log_a [T,H] or [T,H,N], B, C [T,G,N],
+    cu_seqlens int64 on the GPU, max_seqlen a bound on every length).  Returns a dict: dx (dtype of
+    x), dlog_a, dB, dC (fp32, packed), dD (or None), dinit [nseq,H,N,P] (or None)."""
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    nseq = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or nseq < 0 or cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens must be a 1-D int64 tensor of nseq + 1 offsets on x's device")
+    dims = varlen_dims(x, log_a, B, nseq, max_seqlen)
+    _check(x, "x", (T, H, P), x.dtype, dev)
+    _check(log_a, "log_a", (T, H, N) if dims.decay == SSD_DECAY_DIAG else (T, H), torch.float32, dev)
+    _check(B, "B", (T, G, N), x.dtype, dev)
+    _check(C, "C", (T, G, N), x.dtype, dev)
+    _check(dy, "dy", (T, H, P), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (nseq, H, N, P), torch.float32, dev)
+    _check(dfinal, "dfinal", (nseq, H, N, P), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), dlog_a=torch.empty(log_a.shape, **f32), dB=torch.empty((T, G, N), **f32),
+               dC=torch.empty((T, G, N), **f32), dD=torch.empty(H, **f32) if want_dD else None,
+               dinit=torch.empty((nseq, H, N, P), **f32) if want_dinit else None)
+    lib = load_library()
+    need = int(lib.ssd_backward_varlen_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    arr, n, count = None, 0, ctypes.c_int(0)
+    if events is not None:
+        n = max(len(events), 2 * SSD_MAX_LAUNCHES)
+        arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+    rc = lib.ssd_backward_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(log_a), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal), _ptr(out["dx"]),
+                                 _ptr(out["dlog_a"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                                 _ptr(out["dinit"]), _ptr(workspace), ws_bytes, _stream_handle(stream, dev), arr, n,
+                                 ctypes.byref(count))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_backward_varlen")
+    return out
 
 
 def ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input: bool = True,

@@ -310,15 +310,24 @@ int ssd_backward(const ssd_dims* d, const void* x, const float* log_a, const voi
                                  workspace, workspace_bytes, stream, nullptr, 0, nullptr);
 }
 
-int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, const void* B, const void* C,
-                          const float* D, const float* init_state, const void* dy, const float* dfinal, void* dx,
-                          float* dlog_a, float* dB, float* dC, float* dD, float* dinit, void* workspace,
-                          size_t workspace_bytes, void* stream, void* const* events, int n_events, int* n_launches) {
+}  // extern "C"
+
+namespace {
+
+// ssd_backward(_profiled) (vl null) and ssd_backward_varlen (vl set).
+int backward_impl(const ssd_dims* d, const void* x, const float* log_a, const void* B, const void* C, const float* D,
+                  const float* init_state, const void* dy, const float* dfinal, void* dx, float* dlog_a, float* dB,
+                  float* dC, float* dD, float* dinit, void* workspace, size_t workspace_bytes, void* stream,
+                  void* const* events, int n_events, int* n_launches, const Varlen* vl) {
     if (n_launches) *n_launches = 0;
     if (events && n_events < 2 * SSD_MAX_LAUNCHES) return SSD_ERR_INVALID;
     int rc = check_backward(d);
     if (rc != SSD_OK) return rc;
-    const bool has_tokens = d->batch > 0 && d->seqlen > 0;
+    if (vl) {
+        if (vl->total < 0 || vl->total > d->batch * d->seqlen) return SSD_ERR_INVALID;
+        if (d->batch > 0 && (!vl->cu_seqlens || ((uintptr_t)vl->cu_seqlens & 7u) != 0)) return SSD_ERR_INVALID;
+    }
+    const bool has_tokens = d->batch > 0 && d->seqlen > 0 && (!vl || vl->total > 0);
     if (has_tokens && (!x || !log_a || !B || !C || !dy || !dx || !dlog_a || !dB || !dC)) return SSD_ERR_INVALID;
     const void* ptrs[] = {x, log_a, B, C, D, init_state, dy, dfinal, dx, dlog_a, dB, dC, dD, dinit, workspace};
     for (const void* p : ptrs)
@@ -352,6 +361,10 @@ int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, 
     p.ngroups = d->ngroups;
     p.nchunks = (int)((d->seqlen + ssd::backward_chunk() - 1) / ssd::backward_chunk());
     ssd::bind_backward_workspace(p, workspace, (int)d->dstate, (int)d->headdim, d->decay);
+    if (vl) {
+        p.seq_off = vl->cu_seqlens;
+        p.total = vl->total;
+    }
     int count = 0;
     bl.events = reinterpret_cast<hipEvent_t const*>(events);
     bl.n_events = events ? n_events : 0;
@@ -360,6 +373,30 @@ int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, 
     if (n_launches) *n_launches = count;
     if (rc == -2) return SSD_ERR_UNSUPPORTED;
     return rc == 0 ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_backward_profiled(const ssd_dims* d, const void* x, const float* log_a, const void* B, const void* C,
+                          const float* D, const float* init_state, const void* dy, const float* dfinal, void* dx,
+                          float* dlog_a, float* dB, float* dC, float* dD, float* dinit, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events, int n_events, int* n_launches) {
+    return backward_impl(d, x, log_a, B, C, D, init_state, dy, dfinal, dx, dlog_a, dB, dC, dD, dinit, workspace,
+                         workspace_bytes, stream, events, n_events, n_launches, nullptr);
+}
+
+size_t ssd_backward_varlen_workspace_bytes(const ssd_dims* d) { return ssd_backward_workspace_bytes(d); }
+
+int ssd_backward_varlen(const ssd_dims* d, const int64_t* cu_seqlens, int64_t total_tokens, const void* x,
+                        const float* log_a, const void* B, const void* C, const float* D, const float* init_state,
+                        const void* dy, const float* dfinal, void* dx, float* dlog_a, float* dB, float* dC, float* dD,
+                        float* dinit, void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                        int n_events, int* n_launches) {
+    const Varlen vl{cu_seqlens, total_tokens};
+    return backward_impl(d, x, log_a, B, C, D, init_state, dy, dfinal, dx, dlog_a, dB, dC, dD, dinit, workspace,
+                         workspace_bytes, stream, events, n_events, n_launches, &vl);
 }
 
 size_t ssd_backward_dt_workspace_bytes(const ssd_dims* d, int scale_input) {

@@ -143,6 +143,9 @@ __global__ void __launch_bounds__(kBThreads) bwd_states_kernel(BwdParams prm) {
     const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
     if (unit < 0) return;
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+    // (the sequence's own chunks; the checkpoints keep the stride of prm.nchunks)
+    const int nch = prm.seq_off ? (int)((sq.len + kBQ - 1) / kBQ) : prm.nchunks;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
     extern __shared__ __align__(16) unsigned char smem[];
     float* Bw = reinterpret_cast<float*>(smem);  // w o B [Q][NS]
@@ -168,13 +171,13 @@ __global__ void __launch_bounds__(kBThreads) bwd_states_kernel(BwdParams prm) {
     float rla = 0.f;
     auto load = [&](int c) {
         const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
-        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
-        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
-        rla = tid < len && tid < Q ? prm.log_a[(b * Tn + t0 + tid) * H + h] : 0.f;
+        const int len = (int)min((int64_t)Q, sq.len - t0);
+        rb.load(Bg + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
+        rx.load(xg + ((sq.row0 + t0) * H + h) * P, H * P, len, tid);
+        rla = tid < len && tid < Q ? prm.log_a[(sq.row0 + t0 + tid) * H + h] : 0.f;
     };
-    if (prm.nchunks > 0) load(0);
-    for (int c = 0; c < prm.nchunks; ++c) {
+    if (nch > 0) load(0);
+    for (int c = 0; c < nch; ++c) {
         // the checkpoint: the state entering chunk c
         float* ck = prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
 #pragma unroll
@@ -195,7 +198,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_states_kernel(BwdParams prm) {
         for (int i = tid; i < Q * N; i += kBThreads) Bw[(i / N) * NS + i % N] *= w_s[i / N];
         const float el = (float)exp(cum[Q - 1]);
         lds_barrier();
-        if (c + 1 < prm.nchunks) load(c + 1);
+        if (c + 1 < nch) load(c + 1);
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int tile = wave + kBWaves * j;
@@ -221,6 +224,9 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
     const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
     if (unit < 0) return;
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+    // (the sequence's own chunks; the checkpoints keep the stride of prm.nchunks)
+    const int nch = prm.seq_off ? (int)((sq.len + kBQ - 1) / kBQ) : prm.nchunks;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -283,19 +289,19 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
     float rla = 0.f;
     auto load = [&](int c) {
         const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
-        rx.load(xg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
-        ry.load(yg + ((b * Tn + t0) * H + h) * P, H * P, len, tid);
-        rb.load(Bg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
-        rc.load(Cg + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        const int len = (int)min((int64_t)Q, sq.len - t0);
+        rx.load(xg + ((sq.row0 + t0) * H + h) * P, H * P, len, tid);
+        ry.load(yg + ((sq.row0 + t0) * H + h) * P, H * P, len, tid);
+        rb.load(Bg + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
+        rc.load(Cg + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
         rh.load(prm.ckpt + (unit * prm.nchunks + c) * (int64_t)N * P, P, N, tid);
-        rla = tid < len && tid < Q ? prm.log_a[(b * Tn + t0 + tid) * H + h] : 0.f;
+        rla = tid < len && tid < Q ? prm.log_a[(sq.row0 + t0 + tid) * H + h] : 0.f;
     };
-    if (prm.nchunks > 0) load(prm.nchunks - 1);
+    if (nch > 0) load(nch - 1);
 
-    for (int c = prm.nchunks - 1; c >= 0; --c) {
+    for (int c = nch - 1; c >= 0; --c) {
         const int64_t t0 = (int64_t)c * Q;
-        const int len = (int)min((int64_t)Q, Tn - t0);
+        const int len = (int)min((int64_t)Q, sq.len - t0);
         // ---- 1. the chunk's x, dy, B, C and entering state into LDS (zeros past the end)
         rx.stage(Xs, PS, tid);
         ry.stage(Ys, PS, tid);
@@ -362,7 +368,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
             for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * lg + i;
                 const float v = acc[i] + wv[s] * bg[i] + dskip * Ys[s * PS + p];
-                if (s < len) dxg[((b * Tn + t0 + s) * H + h) * P + p] = from_f32<T>(v);
+                if (s < len) dxg[((sq.row0 + t0 + s) * H + h) * P + p] = from_f32<T>(v);
             }
         }
         for (int tile = wave; tile < QB * NB; tile += kBWaves) {
@@ -381,8 +387,8 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
             for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * lg + i;  // (the row: s for dB, t for dC)
                 if (s < len) {
-                    atomicAdd(prm.dB + ((b * Tn + t0 + s) * G + g) * N + n, acc[i] + wv[s] * gx[i]);
-                    atomicAdd(prm.dC + ((b * Tn + t0 + s) * G + g) * N + n, acc2[i] + ev[s] * hd[i]);
+                    atomicAdd(prm.dB + ((sq.row0 + t0 + s) * G + g) * N + n, acc[i] + wv[s] * gx[i]);
+                    atomicAdd(prm.dC + ((sq.row0 + t0 + s) * G + g) * N + n, acc2[i] + ev[s] * hd[i]);
                 }
                 const float pbv = group16_sum(Bs[s * NS + n] * gx[i]);
                 const float pcv = group16_sum(Cs[s * NS + n] * hd[i]);
@@ -433,7 +439,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
                 const float o = __shfl_down(r, off, kWave);
                 if (tid + off < kWave) r += o;
             }
-            if (tid < len) prm.dlog_a[(b * Tn + t0 + tid) * H + h] = r;
+            if (tid < len) prm.dlog_a[(sq.row0 + t0 + tid) * H + h] = r;
         }
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
@@ -570,7 +576,7 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
     const int64_t nch = prm.nchunks;
     {
-        const int64_t nbc = prm.batch * Tn * G * N, stride = (int64_t)gridDim.x * kThreads;
+        const int64_t nbc = (prm.seq_off ? prm.total : prm.batch * Tn) * G * N, stride = (int64_t)gridDim.x * kThreads;
         for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbc; i += stride) {
             prm.dB[i] = 0.f;
             prm.dC[i] = 0.f;
@@ -584,7 +590,13 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
     const int r = lane % 16, gq = lane / 16;
     const int64_t t0 = (int64_t)c * Q;
-    const int len = (int)min((int64_t)Q, Tn - t0);
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+    if (t0 >= sq.len) {
+        // (a packed sequence shorter than seqlen: no such chunk; nothing for dD from it)
+        if (threadIdx.x == 0) prm.dD_part[unit * nch + c] = 0.f;
+        return;
+    }
+    const int len = (int)min((int64_t)Q, sq.len - t0);
 
     extern __shared__ __align__(16) unsigned char smem[];
     CT* cum = reinterpret_cast<CT*>(smem);                    // [Q][NC]
@@ -605,7 +617,7 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
     // sum x . dy on the way
     float xdy = 0.f;
     {
-        const int64_t rowx = (b * Tn + t0) * H + h, rowb = (b * Tn + t0) * G + g;
+        const int64_t rowx = (sq.row0 + t0) * H + h, rowb = (sq.row0 + t0) * G + g;
         ChunkRows<T, Q, P, kThreads> rx, ry;
         ChunkRows<T, Q, N, kThreads> rb, rc;
         ChunkRows<float, Q, N, kThreads> rl;
@@ -641,7 +653,7 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
 
     // ---- 1. e_last and sum x . dy out; the local sums S = (w o B)^T X and U = (e o C)^T dY; the
     //         cross-block operands C o f and B o g
-    const int64_t row0 = (b * Tn + t0) * H + h;
+    const int64_t row0 = (sq.row0 + t0) * H + h;
     if (tid < N) prm.elw[(unit * nch + c) * N + tid] = el[tid];
     if (tid == 0) prm.dD_part[unit * nch + c] = (red[0] + red[1]) + (red[2] + red[3]);
     {
@@ -793,25 +805,29 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_diag_kernel(BwdParams prm) 
     const bool fwd = i < units * per;
     const int64_t j = fwd ? i : i - units * per;
     const int64_t unit = j / per, e = j % per, n = e / P;
-    const int nch = prm.nchunks;
+    const int nch = prm.nchunks;  // (the slots' stride)
+    // (a packed sequence: its own chunks)
+    const int ncb = prm.seq_off
+                        ? (int)((seq_span(prm.seq_off, unit / prm.nheads, prm.seqlen, prm.total).len + kBQ - 1) / kBQ)
+                        : nch;
     const float* el = prm.elw + unit * nch * N + n;
     float* slot = (fwd ? prm.ckpt : prm.gst) + unit * nch * per + e;
     const float* start = fwd ? prm.init : prm.dfinal;
     float v = start ? start[unit * per + e] : 0.f;
-    for (int k0 = 0; k0 < nch; k0 += kB) {
+    for (int k0 = 0; k0 < ncb; k0 += kB) {
         float s[kB], a[kB];
 #pragma unroll
         for (int k = 0; k < kB; ++k) {
-            const int c = fwd ? k0 + k : nch - 1 - k0 - k;
-            if (k0 + k < nch) {
+            const int c = fwd ? k0 + k : ncb - 1 - k0 - k;
+            if (k0 + k < ncb) {
                 s[k] = slot[c * per];
                 a[k] = el[c * N];
             }
         }
 #pragma unroll
         for (int k = 0; k < kB; ++k) {
-            const int c = fwd ? k0 + k : nch - 1 - k0 - k;
-            if (k0 + k < nch) {
+            const int c = fwd ? k0 + k : ncb - 1 - k0 - k;
+            if (k0 + k < ncb) {
                 slot[c * per] = v;
                 v = a[k] * v + s[k];
             }
@@ -862,12 +878,14 @@ __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm
     auto load = [&](int64_t w) {
         const int64_t unit = w / nch, b = unit / H, h = unit % H, g = h / (H / G);
         const int c = (int)(w % nch);
-        const int64_t t0 = (int64_t)c * Q, row0 = (b * Tn + t0) * H + h;
-        const int len = (int)min((int64_t)Q, Tn - t0);
+        const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+        const int64_t t0 = (int64_t)c * Q, row0 = (sq.row0 + t0) * H + h;
+        // (rows past a packed sequence's end are neither read nor written: len <= 0 masks them)
+        const int len = (int)min((int64_t)Q, sq.len - t0);
         rx.load(static_cast<const T*>(prm.x) + row0 * P, H * P, len, tid);
         ry.load(static_cast<const T*>(prm.dy) + row0 * P, H * P, len, tid);
-        rb.load(static_cast<const T*>(prm.Bm) + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
-        rc.load(static_cast<const T*>(prm.Cm) + ((b * Tn + t0) * G + g) * N, G * N, len, tid);
+        rb.load(static_cast<const T*>(prm.Bm) + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
+        rc.load(static_cast<const T*>(prm.Cm) + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
         rh.load(prm.ckpt + w * (int64_t)N * P, P, N, tid);
         rg.load(prm.gst + w * (int64_t)N * P, P, N, tid);
         rl.load(prm.log_a + row0 * N, H * N, len, tid);
@@ -897,8 +915,9 @@ __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm
     for (; w < last; w += wg_per_xcd) {
         const int64_t unit = w / nch, b = unit / H, h = unit % H, g = h / (H / G);
         const int c = (int)(w % nch);
-        const int64_t t0 = (int64_t)c * Q, row0 = (b * Tn + t0) * H + h;
-        const int len = (int)min((int64_t)Q, Tn - t0);
+        const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+        const int64_t t0 = (int64_t)c * Q, row0 = (sq.row0 + t0) * H + h;
+        const int len = (int)min((int64_t)Q, sq.len - t0);
         const float dskip = prm.D ? prm.D[h] : 0.f;
         lds_barrier();  // the previous item is done with every LDS array
         rx.stage(Xs, PS, tid);
@@ -918,6 +937,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm
         }
         lds_barrier();
         if (w + wg_per_xcd < last) load(w + wg_per_xcd);
+        if (len <= 0) continue;  // (a packed sequence shorter than seqlen: no such chunk)
         diag_chunk_factors<N, CT>(Wv, cum, Ev, Wv, el, tid);
         if (tid >= kBThreads - N) {
             const int n = tid - (kBThreads - N);
@@ -958,8 +978,8 @@ __global__ void __launch_bounds__(kBThreads) bwd_terms_diag_kernel(BwdParams prm
                 const float wb = Wv[q * NC + n] * Bs[q * NS + n] * gx[i];
                 const float ec = Ev[q * NC + n] * Cs[q * NS + n] * hd[i];
                 if (q < len) {
-                    atomicAdd(prm.dB + ((b * Tn + t0 + q) * G + g) * N + n, cbb[i] + Wv[q * NC + n] * gx[i]);
-                    atomicAdd(prm.dC + ((b * Tn + t0 + q) * G + g) * N + n, ccb[i] + Ev[q * NC + n] * hd[i]);
+                    atomicAdd(prm.dB + ((sq.row0 + t0 + q) * G + g) * N + n, cbb[i] + Wv[q * NC + n] * gx[i]);
+                    atomicAdd(prm.dC + ((sq.row0 + t0 + q) * G + g) * N + n, ccb[i] + Ev[q * NC + n] * hd[i]);
                 }
                 dcum[q * NC + n] += ec - wb;
                 lastp += wb;
@@ -1029,7 +1049,7 @@ int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
     const int64_t units = bl.p.batch * bl.p.nheads;
     BwdParams p = bl.p;
     p.per_xcd = (units + 7) / 8;
-    const int64_t nbc = bl.p.batch * bl.p.seqlen * bl.p.ngroups * N;
+    const int64_t nbc = (bl.p.seq_off ? bl.p.total : bl.p.batch * bl.p.seqlen) * bl.p.ngroups * N;
     int k = 0;
     if (nbc > 0 &&
         !launch_k(bl, k, zero_kernel, dim3((unsigned)std::min<int64_t>((nbc + kThreads - 1) / kThreads, 4096)),

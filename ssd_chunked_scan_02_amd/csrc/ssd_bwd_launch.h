@@ -36,6 +36,10 @@ struct BwdParams {
     int64_t batch, seqlen, nheads, ngroups;
     int nchunks;  // backward chunks (backward_chunk() tokens each)
     int64_t per_xcd, per_xcd_intra;
+    // packed variable-length batch (null: batched layout), as in ForwardLaunch: the workspace keeps
+    // the [batch][seqlen] layout, and each (sequence, head) covers its own chunks
+    const int64_t* seq_off;
+    int64_t total;
 };
 struct BackwardLaunch {
     int dtype;

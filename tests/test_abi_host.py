@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["ssd_backward", "ssd_backward_dt", "ssd_backward_dt_workspace_bytes",
-                                    "ssd_backward_profiled", "ssd_backward_workspace_bytes",
+                                    "ssd_backward_profiled", "ssd_backward_varlen",
+                                    "ssd_backward_varlen_workspace_bytes", "ssd_backward_workspace_bytes",
                                     "ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
                                     "ssd_forward_dt_varlen", "ssd_forward_dt_varlen_workspace_bytes",
                                     "ssd_forward_dt_workspace_bytes", "ssd_forward_profiled",
@@ -374,3 +375,22 @@ def test_dt_varlen_workspace_and_checks(lib):
     assert fn(*args(d, 4 * 512 + 1)) == ssd.SSD_ERR_INVALID        # more tokens than batch * seqlen
     assert fn(*args(d, -1)) == ssd.SSD_ERR_INVALID
     assert call_varlen(lib, d, total=4 * 512 + 1) == ssd.SSD_ERR_INVALID
+
+
+def test_backward_varlen_checks(lib):
+    d = mamba2_dims(batch=4, seqlen=512)
+    assert ssd.ssd_forward_varlen_workspace_bytes  # (the forward's query is separate)
+    assert lib.ssd_backward_varlen_workspace_bytes(ctypes.byref(d)) == ssd.ssd_backward_workspace_bytes(d)
+    fn = lib.ssd_backward_varlen
+    def call(dims, cu=FAKE, total=1000, ws=FAKE, ws_bytes=1 << 32, **over):
+        p = dict(x=FAKE, la=FAKE, B=FAKE, C=FAKE, dy=FAKE, dx=FAKE, dla=FAKE, dB=FAKE, dC=FAKE)
+        p.update(over)
+        return fn(ctypes.byref(dims), cu, total, p["x"], p["la"], p["B"], p["C"], None, None, p["dy"], None, p["dx"],
+                  p["dla"], p["dB"], p["dC"], None, None, ws, ws_bytes, None, None, 0, None)
+    assert call(d, total=4 * 512 + 1) == ssd.SSD_ERR_INVALID
+    assert call(d, total=-1) == ssd.SSD_ERR_INVALID
+    assert call(d, cu=None) == ssd.SSD_ERR_INVALID
+    assert call(d, cu=FAKE + 4) == ssd.SSD_ERR_INVALID
+    assert call(d, dy=None) == ssd.SSD_ERR_INVALID
+    assert call(d, ws_bytes=ssd.ssd_backward_workspace_bytes(d) - 1) == ssd.SSD_ERR_INVALID
+    assert call(mamba2_dims(decay=1)) == ssd.SSD_ERR_UNSUPPORTED

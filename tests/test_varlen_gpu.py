@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.backward
 import oracle.discretize
 import oracle.varlen
 import ssd_inputs
@@ -146,3 +147,59 @@ def test_dt_varlen_matches_oracle(name, over, chunk, lengths, scale, label):
     ef = rel_l2(fin.double().cpu().numpy(), fr)
     announce("dt varlen %s: y %.2e final %.2e (tol %.0e)" % (label, ey, ef, tol))
     assert ey <= tol and ef <= tol, (ey, ef)
+
+
+BWD_CASES = [
+    ("mamba2_layer", dict(nheads=4, init=True), [300, 0, 129, 1000, 1, 57], "bwd-bf16-n128"),
+    ("tiny_fp32", dict(nheads=3, skip=True, init=True, a_log="uniform16", dt_mean=-2.0), [90, 0, 257, 64], "bwd-fp32"),
+    ("gqa_decode", dict(nheads=8, ngroups=2, init=True, decode_steps=0, dstate=64), [64, 700, 3], "bwd-bf16-gqa"),
+    ("diag_multiscale", dict(nheads=3, init=True, a_log="rand_hn"), [200, 0, 64, 1, 517], "bwd-diag-bf16"),
+    ("diag_multiscale", dict(nheads=2, ngroups=2, dstate=16, headdim=16, dtype="fp32", init=True, a_log="rand_hn"),
+     [77, 0, 140], "bwd-diag-fp32"),
+]
+
+
+@pytest.mark.parametrize("name,over,lengths,label", BWD_CASES, ids=[c[3] for c in BWD_CASES])
+def test_backward_varlen_matches_oracle(name, over, lengths, label):
+    """ssd_backward_varlen against the oracle's per-sequence adjoint (oracle.varlen.backward_varlen):
+    every gradient, with initial states and a gradient for every final state."""
+    cfg = ssd_inputs.config(name, **over)
+    announce("backward varlen %s lengths=%s" % (label, lengths))
+    p = ssd_inputs.packed_inputs(cfg, lengths, 51)
+    gen = torch.Generator().manual_seed(52)
+    dy = torch.randn(p["x"].shape, generator=gen).to(p["x"].dtype)
+    dfin = torch.randn((len(lengths), cfg["nheads"], cfg["dstate"], cfg["headdim"]), generator=gen)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    got = ssd.ssd_backward_varlen(g["x"], g["log_a"], g["B"], g["C"], dy.cuda(), g["cu_seqlens"], p["max_seqlen"],
+                                  g.get("D"), init_state=g.get("init_state"), dfinal=dfin.cuda())
+    torch.cuda.synchronize()
+    want = oracle.varlen.backward_varlen(oracle.backward.default_adjoint(), f64(p["x"]), f64(p["log_a"]), f64(p["B"]),
+                                         f64(p["C"]), p["cu_seqlens"].numpy(), f64(p.get("D")),
+                                         f64(p.get("init_state")), f64(dy), f64(dfin))
+    tol = TOL[cfg["dtype"]]
+    keys = ("dx", "dlog_a", "dB", "dC", "dinit") + (("dD",) if cfg["skip"] else ())
+    errs = {k: rel_l2(got[k].double().cpu().numpy(), want[k]) for k in keys}
+    announce("backward varlen %s: " % label + " ".join("%s %.2e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
+    assert all(e <= tol for e in errs.values()), errs
+
+
+def test_backward_varlen_equals_batched_for_equal_lengths():
+    """Equal lengths: the packed backward takes the same kernels as the batched one; every gradient
+    but dB and dC (added atomically over heads, so their last bits may differ) comes out the same."""
+    cfg = ssd_inputs.config("mamba2_layer", batch=3, seqlen=300, nheads=4, init=True)
+    announce("backward varlen equal lengths vs batched")
+    inp = ssd_inputs.make_inputs(cfg, 53)
+    og = ssd_inputs.output_gradients(cfg, 54)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in dict(inp, **og).items()}
+    gb = ssd.ssd_backward(g["x"], g["log_a"], g["B"], g["C"], g["dy"], g.get("D"), init_state=g["init_state"],
+                          dfinal=g["dfinal"])
+    cu = torch.arange(0, 4 * 300, 300, dtype=torch.int64, device="cuda")
+    gv = ssd.ssd_backward_varlen(g["x"].reshape(900, 4, 64), g["log_a"].reshape(900, 4), g["B"].reshape(900, 1, 128),
+                                 g["C"].reshape(900, 1, 128), g["dy"].reshape(900, 4, 64), cu, 300, g.get("D"),
+                                 init_state=g["init_state"], dfinal=g["dfinal"])
+    torch.cuda.synchronize()
+    assert torch.equal(gv["dx"].reshape(gb["dx"].shape), gb["dx"])
+    assert torch.equal(gv["dlog_a"].reshape(gb["dlog_a"].shape), gb["dlog_a"])
+    assert torch.equal(gv["dinit"], gb["dinit"]) and torch.equal(gv["dD"], gb["dD"])
+    for k in ("dB", "dC"):
+        assert rel_l2(gv[k].reshape(gb[k].shape).double().cpu().numpy(), gb[k].double().cpu().numpy()) <= 1e-6
