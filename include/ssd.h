@@ -289,6 +289,19 @@ int ssd_backward_dt(const ssd_dims* dims, const void* x, const float* dt, const 
                     void* dx, float* ddt, float* dA_log, float* ddt_bias, float* dB, float* dC,
                     float* dD, float* dinit, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ssd_backward_dt for a packed variable-length batch (the layouts, cu_seqlens, total_tokens and
+ * dims->seqlen bound of ssd_forward_varlen; dt [total,H]): every sequence's gradients by themselves,
+ * with ddt per packed token and dA_log, ddt_bias, dD summed over every sequence.  The workspace is
+ * ssd_backward_dt's for these dims. */
+size_t ssd_backward_dt_varlen_workspace_bytes(const ssd_dims* dims, int scale_input);
+
+int ssd_backward_dt_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int64_t total_tokens,
+                           const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                           int scale_input, const void* B, const void* C, const float* D,
+                           const float* init_state, const void* dy, const float* dfinal, void* dx,
+                           float* ddt, float* dA_log, float* ddt_bias, float* dB, float* dC, float* dD,
+                           float* dinit, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable description of a return code. */
 const char* ssd_strerror(int code);
 

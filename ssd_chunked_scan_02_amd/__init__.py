@@ -120,6 +120,10 @@ def load_library():
         lib.ssd_backward_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 15 + [sz, vp, ctypes.POINTER(vp), i32,
                                                                              ctypes.POINTER(i32)]
         lib.ssd_backward_varlen.restype = i32
+        lib.ssd_backward_dt_varlen_workspace_bytes.argtypes = [dp, i32]
+        lib.ssd_backward_dt_varlen_workspace_bytes.restype = sz
+        lib.ssd_backward_dt_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, i32] + [vp] * 15 + [sz, vp]
+        lib.ssd_backward_dt_varlen.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -604,6 +608,54 @@ def ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input: b
                              _ptr(out["dinit"]), _ptr(workspace), ws_bytes, _stream_handle(stream, dev))
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_backward_dt")
+    return out
+
+
+def ssd_backward_dt_varlen(x, dt, A_log, B, C, dy, cu_seqlens, max_seqlen: int, D=None, dt_bias=None,
+                           scale_input: bool = True, init_state=None, dfinal=None, want_dD=True, want_dinit=True,
+                           workspace=None, stream=None):
+    """Run ``ssd_backward_dt_varlen``: the gradients of ssd_forward_dt_varlen on a packed batch
+    (x [T,H,P], dt [T,H], B, C [T,G,N], cu_seqlens int64 on the GPU).  Returns a dict as
+    ssd_backward_dt's, with dx, ddt, dB, dC packed and dinit [nseq,H,N,P]."""
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    nseq = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or nseq < 0 or cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens must be a 1-D int64 tensor of nseq + 1 offsets on x's device")
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16")
+    decay = SSD_DECAY_DIAG if A_log.dim() == 2 else SSD_DECAY_SCALAR
+    dims = Dims(int(nseq), int(max_seqlen), H, G, P, N, _DTYPE_CODE[x.dtype], decay)
+    _check(x, "x", (T, H, P), x.dtype, dev)
+    _check(dt, "dt", (T, H), torch.float32, dev)
+    _check(A_log, "A_log", (H, N) if decay == SSD_DECAY_DIAG else (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(B, "B", (T, G, N), x.dtype, dev)
+    _check(C, "C", (T, G, N), x.dtype, dev)
+    _check(dy, "dy", (T, H, P), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (nseq, H, N, P), torch.float32, dev)
+    _check(dfinal, "dfinal", (nseq, H, N, P), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty((T, H), **f32), dA_log=torch.empty(A_log.shape, **f32),
+               ddt_bias=torch.empty(H, **f32) if dt_bias is not None else None,
+               dB=torch.empty((T, G, N), **f32), dC=torch.empty((T, G, N), **f32),
+               dD=torch.empty(H, **f32) if want_dD else None,
+               dinit=torch.empty((nseq, H, N, P), **f32) if want_dinit else None)
+    lib = load_library()
+    scale = 1 if scale_input else 0
+    need = int(lib.ssd_backward_dt_varlen_workspace_bytes(ctypes.byref(dims), scale))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ssd_backward_dt_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(dt), _ptr(dt_bias),
+                                    _ptr(A_log), scale, _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy),
+                                    _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA_log"]),
+                                    _ptr(out["ddt_bias"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                                    _ptr(out["dinit"]), _ptr(workspace), ws_bytes, _stream_handle(stream, dev))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_backward_dt_varlen")
     return out
 
 

@@ -406,14 +406,23 @@ size_t ssd_backward_dt_workspace_bytes(const ssd_dims* d, int scale_input) {
         .total;
 }
 
-int ssd_backward_dt(const ssd_dims* d, const void* x, const float* dt, const float* dt_bias, const float* A_log,
-                    int scale_input, const void* B, const void* C, const float* D, const float* init_state,
-                    const void* dy, const float* dfinal, void* dx, float* ddt, float* dA_log, float* ddt_bias,
-                    float* dB, float* dC, float* dD, float* dinit, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ssd_backward_dt (vl null) and ssd_backward_dt_varlen (vl set).
+int backward_dt_impl(const ssd_dims* d, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                     int scale_input, const void* B, const void* C, const float* D, const float* init_state,
+                     const void* dy, const float* dfinal, void* dx, float* ddt, float* dA_log, float* ddt_bias,
+                     float* dB, float* dC, float* dD, float* dinit, void* workspace, size_t workspace_bytes,
+                     void* stream, const Varlen* vl) {
     int rc = check_backward(d);
     if (rc != SSD_OK) return rc;
-    const bool has_tokens = d->batch > 0 && d->seqlen > 0;
+    if (vl) {
+        if (vl->total < 0 || vl->total > d->batch * d->seqlen) return SSD_ERR_INVALID;
+        if (d->batch > 0 && (!vl->cu_seqlens || ((uintptr_t)vl->cu_seqlens & 7u) != 0)) return SSD_ERR_INVALID;
+    }
+    const bool has_tokens = d->batch > 0 && d->seqlen > 0 && (!vl || vl->total > 0);
     if (has_tokens && (!x || !dt || !A_log || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_INVALID;
     if (!A_log && (dA_log || ddt_bias)) return SSD_ERR_INVALID;
     const void* ptrs[] = {x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, dx, ddt, dA_log, ddt_bias,
@@ -441,12 +450,44 @@ int ssd_backward_dt(const ssd_dims* d, const void* x, const float* dt, const flo
     p.nheads = d->nheads;
     p.ngroups = d->ngroups;
     p.nchunks = (int)((d->seqlen + ssd::backward_chunk() - 1) / ssd::backward_chunk());
+    if (vl) {
+        p.seq_off = vl->cu_seqlens;
+        p.total = vl->total;
+    }
     int count = 0;
     bl.n_launches = &count;
     ssd::DtBackwardArgs a{x, dt, dt_bias, A_log, scale_input != 0, D, dy, dx, ddt, dA_log, ddt_bias, dD, workspace};
     rc = ssd::launch_backward_dt(bl, a, static_cast<hipStream_t>(stream));
     if (rc == -2) return SSD_ERR_UNSUPPORTED;
     return rc == 0 ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_backward_dt(const ssd_dims* d, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                    int scale_input, const void* B, const void* C, const float* D, const float* init_state,
+                    const void* dy, const float* dfinal, void* dx, float* ddt, float* dA_log, float* ddt_bias,
+                    float* dB, float* dC, float* dD, float* dinit, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    return backward_dt_impl(d, x, dt, dt_bias, A_log, scale_input, B, C, D, init_state, dy, dfinal, dx, ddt, dA_log,
+                            ddt_bias, dB, dC, dD, dinit, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t ssd_backward_dt_varlen_workspace_bytes(const ssd_dims* d, int scale_input) {
+    return ssd_backward_dt_workspace_bytes(d, scale_input);
+}
+
+int ssd_backward_dt_varlen(const ssd_dims* d, const int64_t* cu_seqlens, int64_t total_tokens, const void* x,
+                           const float* dt, const float* dt_bias, const float* A_log, int scale_input, const void* B,
+                           const void* C, const float* D, const float* init_state, const void* dy,
+                           const float* dfinal, void* dx, float* ddt, float* dA_log, float* ddt_bias, float* dB,
+                           float* dC, float* dD, float* dinit, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    const Varlen vl{cu_seqlens, total_tokens};
+    return backward_dt_impl(d, x, dt, dt_bias, A_log, scale_input, B, C, D, init_state, dy, dfinal, dx, ddt, dA_log,
+                            ddt_bias, dB, dC, dD, dinit, workspace, workspace_bytes, stream, &vl);
 }
 
 const char* ssd_strerror(int code) {

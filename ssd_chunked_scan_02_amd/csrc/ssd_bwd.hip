@@ -1294,7 +1294,9 @@ DtBackwardLayout dt_backward_layout(int64_t batch, int64_t nheads, int64_t seqle
 }
 
 int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipStream_t stream) {
-    const int64_t H = bl0.p.nheads, rows = bl0.p.batch * bl0.p.seqlen * H;
+    // (a packed batch: its tokens, at most batch * seqlen, which the workspace rows are sized for)
+    const int64_t bt = bl0.p.seq_off ? bl0.p.total : bl0.p.batch * bl0.p.seqlen;
+    const int64_t H = bl0.p.nheads, rows = bt * H;
     const int P = (int)bl0.headdim;
     const int eb = bl0.dtype == 0 ? 4 : 2;
     const int K = bl0.decay == 1 ? (int)bl0.dstate : 1;
@@ -1341,7 +1343,6 @@ int launch_backward_dt(const BackwardLaunch& bl0, const DtBackwardArgs& a, hipSt
                                a.ddt, rowA, rowD, rows, H, P, K);
         if (hipGetLastError() != hipSuccess) return -1;
     }
-    const int64_t bt = bl0.p.batch * bl0.p.seqlen;
     if (a.ddt_bias) hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)H), dim3(kThreads), 0, stream, a.ddt, a.ddt_bias, bt, H);
     if (a.dA_log)
         hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)(H * K)), dim3(kThreads), 0, stream, rowA, a.dA_log, bt, H * K);

@@ -28,7 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ssd_backward", "ssd_backward_dt", "ssd_backward_dt_workspace_bytes",
+    assert declared_functions() == ["ssd_backward", "ssd_backward_dt", "ssd_backward_dt_varlen",
+                                    "ssd_backward_dt_varlen_workspace_bytes", "ssd_backward_dt_workspace_bytes",
                                     "ssd_backward_profiled", "ssd_backward_varlen",
                                     "ssd_backward_varlen_workspace_bytes", "ssd_backward_workspace_bytes",
                                     "ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",

@@ -203,3 +203,63 @@ def test_backward_varlen_equals_batched_for_equal_lengths():
     assert torch.equal(gv["dinit"], gb["dinit"]) and torch.equal(gv["dD"], gb["dD"])
     for k in ("dB", "dC"):
         assert rel_l2(gv[k].reshape(gb[k].shape).double().cpu().numpy(), gb[k].double().cpu().numpy()) <= 1e-6
+
+
+DT_BWD_CASES = [
+    ("mamba2_layer", dict(nheads=4, init=True), [300, 0, 129, 57], True, "bwd-dt-bf16"),
+    ("tiny_fp32", dict(nheads=3, skip=True, init=True, a_log="uniform16", dt_mean=-1.0), [90, 0, 257], False,
+     "bwd-dt-fp32-unscaled"),
+    ("diag_multiscale", dict(nheads=2, init=True, a_log="rand_hn"), [200, 1, 317], True, "bwd-dt-diag-bf16"),
+]
+
+
+@pytest.mark.parametrize("name,over,lengths,scale,label", DT_BWD_CASES, ids=[c[4] for c in DT_BWD_CASES])
+def test_backward_dt_varlen_matches_oracle(name, over, lengths, scale, label):
+    """ssd_backward_dt_varlen against the oracle's chain rule (oracle.discretize.backward_dt) run
+    on every sequence by itself, the per-head sums (dA_log, d bias, dD) added over the sequences;
+    the sums over tokens measured against the size of their terms, as in the batched test."""
+    cfg = ssd_inputs.config(name, **over)
+    diag = cfg["decay"] == "diag"
+    announce("backward dt varlen %s lengths=%s scale=%d" % (label, lengths, scale))
+    p = ssd_inputs.packed_inputs(cfg, lengths, 55)
+    bias = ssd_inputs.dt_bias(cfg["nheads"], 56)
+    gen = torch.Generator().manual_seed(57)
+    dy = torch.randn(p["x"].shape, generator=gen).to(p["x"].dtype)
+    dfin = torch.randn((len(lengths), cfg["nheads"], cfg["dstate"], cfg["headdim"]), generator=gen)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    got = ssd.ssd_backward_dt_varlen(g["x"], g["dt"], g["A_log"], g["B"], g["C"], dy.cuda(), g["cu_seqlens"],
+                                     p["max_seqlen"], g.get("D"), dt_bias=bias.cuda(), scale_input=scale,
+                                     init_state=g.get("init_state"), dfinal=dfin.cuda())
+    torch.cuda.synchronize()
+    T, H = p["dt"].shape
+    want = dict(dx=np.zeros(p["x"].shape), ddt=np.zeros((T, H)), dB=np.zeros(p["B"].shape), dC=np.zeros(p["C"].shape),
+                dinit=np.zeros(dfin.shape), dA_log=np.zeros(p["A_log"].shape), ddt_bias=np.zeros(H), dD=np.zeros(H))
+    mag = dict(dA_log=np.zeros(p["A_log"].shape), ddt_bias=np.zeros(H))
+    adj = oracle.backward.default_adjoint()
+    cu = p["cu_seqlens"].numpy()
+    for i in range(len(lengths)):
+        s, e = int(cu[i]), int(cu[i + 1])
+        if e == s:
+            want["dinit"][i] = f64(dfin[i])
+            continue
+        sl = lambda t: f64(t[s:e])[None]
+        init = None if p.get("init_state") is None else f64(p["init_state"][i:i + 1])
+        w = oracle.discretize.backward_dt(adj, sl(p["x"]), sl(p["dt"]), f64(p["A_log"]), sl(p["B"]), sl(p["C"]),
+                                          f64(p.get("D")), dt_bias=f64(bias), scale_input=scale, init_state=init,
+                                          dy=sl(dy), dfinal=f64(dfin[i:i + 1]), diag=diag)
+        for k in ("dx", "ddt", "dB", "dC"):
+            want[k][s:e] = w[k][0]
+        want["dinit"][i] = w["dinit"][0]
+        for k in ("dA_log", "ddt_bias", "dD"):
+            want[k] += w[k]
+        mag["ddt_bias"] += np.abs(w["ddt"][0]).sum(axis=0)
+        delta, la = oracle.discretize.discretize(sl(p["dt"]), f64(p["A_log"]), f64(bias), diag)
+        xin = sl(p["x"]) * delta[..., None] if scale else sl(p["x"])
+        a = adj.backward(xin, la, sl(p["B"]), sl(p["C"]), None, init, sl(dy), f64(dfin[i:i + 1]))
+        mag["dA_log"] += np.abs(a["dlog_a"] * la).sum(axis=(0, 1))
+    tol = TOL[cfg["dtype"]]
+    errs = {k: rel_l2(got[k].double().cpu().numpy(), want[k]) for k in ("dx", "ddt", "dB", "dC", "dinit", "dD")}
+    for k in ("dA_log", "ddt_bias"):
+        errs[k] = float(np.linalg.norm(got[k].double().cpu().numpy() - want[k]) / np.linalg.norm(mag[k]))
+    announce("backward dt varlen %s: " % label + " ".join("%s %.2e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
+    assert all(e <= tol for e in errs.values()), errs
