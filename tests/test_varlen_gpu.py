@@ -263,3 +263,48 @@ def test_backward_dt_varlen_matches_oracle(name, over, lengths, scale, label):
         errs[k] = float(np.linalg.norm(got[k].double().cpu().numpy() - want[k]) / np.linalg.norm(mag[k]))
     announce("backward dt varlen %s: " % label + " ".join("%s %.2e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
     assert all(e <= tol for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("name,over,chunk,label", [
+    ("diag_multiscale", dict(nheads=2, init=True), 64, "diag-pipe"),
+    ("tiny_fp32", dict(nheads=2, skip=True, init=True), 64, "generic-fp32"),
+    ("diag_multiscale", dict(nheads=2, dstate=16, headdim=32, dtype="fp32", init=True), 32, "generic-diag-fp32"),
+], ids=["diag-pipe", "generic-fp32", "generic-diag-fp32"])
+def test_varlen_clamped_offsets_other_paths(name, over, chunk, label):
+    """The clamping contract on the diagonal and generic paths: offsets past the token count and a
+    sequence longer than max_seqlen give the clamped sequences' results, rows past the clamped end
+    untouched."""
+    cfg = ssd_inputs.config(name, **over)
+    announce("varlen clamped offsets %s" % label)
+    p = ssd_inputs.packed_inputs(cfg, [50, 150], 58)      # 200 tokens
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    cu = torch.tensor([0, 50, 500], dtype=torch.int64, device="cuda")
+    y = torch.full(p["x"].shape, 7.0, dtype=p["x"].dtype, device="cuda")
+    _, fin, _ = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], cu, 120, g.get("D"), chunk=chunk,
+                                       init_state=g["init_state"], y=y, final_state=True)
+    torch.cuda.synchronize()
+    yr, fr = oracle.varlen.forward_varlen(oracle.default_oracle(), f64(p["x"][:170]), f64(p["log_a"][:170]),
+                                          f64(p["B"][:170]), f64(p["C"][:170]), np.array([0, 50, 170]),
+                                          f64(p.get("D")), f64(p["init_state"]))
+    tol = TOL[cfg["dtype"]]
+    assert rel_l2(y[:170].double().cpu().numpy(), yr) <= tol
+    assert rel_l2(fin.double().cpu().numpy(), fr) <= tol
+    assert bool((y[170:] == 7.0).all())
+
+
+def test_varlen_one_long_sequence():
+    """One 65 536-token sequence among short ones: a packed batch is never segmented, so one
+    workgroup per head walks all 512 of its chunks (the batched walk would split it)."""
+    cfg = ssd_inputs.config("long_seq", nheads=2, init=True)
+    lengths = [65536, 3, 700]
+    announce("varlen one long sequence %s" % lengths)
+    p = ssd_inputs.packed_inputs(cfg, lengths, 59)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    y, fin, _ = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], g["cu_seqlens"], p["max_seqlen"],
+                                       g.get("D"), chunk=256, init_state=g["init_state"], final_state=True)
+    torch.cuda.synchronize()
+    yr, fr = oracle.varlen.forward_varlen(oracle.default_oracle(), f64(p["x"]), f64(p["log_a"]), f64(p["B"]),
+                                          f64(p["C"]), p["cu_seqlens"].numpy(), f64(p.get("D")), f64(p["init_state"]))
+    ey, ef = rel_l2(y.double().cpu().numpy(), yr), rel_l2(fin.double().cpu().numpy(), fr)
+    announce("varlen one long sequence: y %.2e final %.2e" % (ey, ef))
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
