@@ -33,6 +33,12 @@ CASES = [
     ("diag_multiscale", dict(batch=2, seqlen=170, nheads=2, ngroups=2, dstate=16, headdim=16, dtype="fp32",
                              a_log="rand_hn", init=True), "diag-fp32"),
     ("diag_multiscale", dict(batch=1, seqlen=130, nheads=2, dtype="fp32", init=True), "diag-fp32-64"),
+    # extreme rates: whole blocks decay to exact zeros (fast), or nothing decays (slow)
+    ("diag_multiscale", dict(batch=1, seqlen=200, nheads=2, a_log="rand_hn", dt_mean=3.0, init=True), "diag-fast"),
+    ("diag_multiscale", dict(batch=1, seqlen=200, nheads=2, dt_mean=-8.0, init=True), "diag-slow"),
+    # lopsided shapes: one 16-wide block of state dims, or of head dims
+    ("diag_multiscale", dict(batch=2, seqlen=150, nheads=2, dstate=64, headdim=16, init=True), "diag-n64-p16"),
+    ("diag_multiscale", dict(batch=2, seqlen=150, nheads=2, dstate=16, headdim=64, init=True), "diag-n16-p64"),
 ]
 
 
