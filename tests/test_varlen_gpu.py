@@ -308,3 +308,30 @@ def test_varlen_one_long_sequence():
     ey, ef = rel_l2(y.double().cpu().numpy(), yr), rel_l2(fin.double().cpu().numpy(), fr)
     announce("varlen one long sequence: y %.2e final %.2e" % (ey, ef))
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,over,chunk", [("mamba2_layer", dict(nheads=4, init=True), 128),
+                                             ("diag_multiscale", dict(nheads=2, init=True), 64)],
+                         ids=["fast", "diag-pipe"])
+def test_varlen_packing_order_is_irrelevant(name, over, chunk):
+    """The same sequences packed in another order (so ranked and scheduled differently) give the
+    same outputs and final states bit for bit: every (sequence, head) is computed by itself."""
+    cfg = ssd_inputs.config(name, **over)
+    lengths = [300, 17, 0, 1000, 129, 64, 5]
+    announce("varlen packing order %s" % name)
+    p = ssd_inputs.packed_inputs(cfg, lengths, 61)
+    perm = [3, 0, 6, 2, 5, 1, 4]
+    cu = p["cu_seqlens"]
+    cat = lambda t: torch.cat([t[int(cu[i]):int(cu[i + 1])] for i in perm])
+    q = {k: cat(p[k]) for k in ("x", "log_a", "B", "C")}
+    cu2 = torch.zeros(len(perm) + 1, dtype=torch.int64)
+    cu2[1:] = torch.cumsum(torch.tensor([lengths[i] for i in perm]), 0)
+    init = p["init_state"]
+    run = lambda d, c, h0: ssd.ssd_forward_varlen(d["x"].cuda(), d["log_a"].cuda(), d["B"].cuda(), d["C"].cuda(),
+                                                 c.cuda(), max(lengths), p["D"].cuda(), chunk=chunk,
+                                                 init_state=h0.cuda(), final_state=True)
+    y1, f1, _ = run(p, cu, init)
+    y2, f2, _ = run(q, cu2, init[perm])
+    torch.cuda.synchronize()
+    assert torch.equal(cat(y1.cpu()), y2.cpu())
+    assert torch.equal(f1.cpu()[perm], f2.cpu())
