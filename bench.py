@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -193,6 +194,17 @@ def measured_traffic(workload, kernel):
         return None
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, cfg, min_seconds, front_end="log_a"):
     """The fp64 oracle as it stands, on this host's cores, over the whole workload, repeated
     until at least ``min_seconds`` of CPU wall time (with the dt front-end, the oracle's
@@ -217,7 +229,7 @@ def cpu_baseline(inp, cfg, min_seconds, front_end="log_a"):
         if el >= min_seconds and reps >= 1:
             break
     tokens = cfg["batch"] * cfg["seqlen"] * reps
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "the whole workload (%d x %d tokens x %d heads), %d run(s) in %.1f s, "
                       "fp64 sequential recurrence, OpenMP over (batch, head)"
                       % (cfg["batch"], cfg["seqlen"], cfg["nheads"], reps, el)}
@@ -420,7 +432,7 @@ def run_backward(args, cfg, inp, dev):
         # (the adjoint runs one (batch, group) pair per thread: the sample has G of them)
         result["cpu_baseline"] = {"value": cfg["seqlen"] * reps / el, "unit": "tokens/s",
                                   "cores": min(threads, cfg["ngroups"]),
-                                  "kind": "oracle",
+                                  "kind": "oracle", "cpu_model": cpu_model(),
                                   "sample": "batch element 0 of the workload (%d tokens x %d heads), %d run(s) in "
                                             "%.1f s, fp64 adjoint of the recurrence, OpenMP over (batch, group)"
                                             % (cfg["seqlen"], cfg["nheads"], reps, el)}
@@ -529,6 +541,7 @@ def run_varlen(args, cfg, dev):
             if el >= args.cpu_seconds:
                 break
         result["cpu_baseline"] = {"value": total * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "cpu_model": cpu_model(),
                                   "sample": "the whole packed batch (%d tokens in %d sequences x %d heads), %d run(s) "
                                             "in %.1f s, fp64 recurrence per sequence, OpenMP over heads"
                                             % (total, nseq, H, reps, el)}
@@ -685,6 +698,7 @@ def main():
         "mfma_peak_frac": tflops / peak_tf,
         "hbm_gbs_whole_step": nbytes / (ms / 1e3) / 1e9,
         "kernels_ms": {n: t for n, t in zip(names, kernel_avg)},
+        "dominant_kernel_ms_median_min": [statistics.median(per_kernel[dom]), min(per_kernel[dom])],
         "ms_per_step_with_kernel_timing": timed_ms,
         "roofline": {"kernel": names[dom], "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
