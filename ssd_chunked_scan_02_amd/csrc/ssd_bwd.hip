@@ -794,11 +794,11 @@ __global__ void __launch_bounds__(kThreads) bwd_local_diag_kernel(BwdParams prm)
 // The chains over the chunks, in place, one thread per (batch, head, state element) and direction:
 // the checkpoint slots hold S_c on entry and H_c (the state entering chunk c) on exit, from
 // H_0 = init; the gradient slots hold U_c on entry and G_c (the gradient of the state at the end of
-// chunk c) on exit, from dfinal; dinit = e_last,0 G_0 + U_0.  Loads go 16 chunks at a time.
+// chunk c) on exit, from dfinal; dinit = e_last,0 G_0 + U_0.  Loads go 32 chunks at a time.
 template <int N, int P>
 __global__ void __launch_bounds__(kThreads) bwd_scan_diag_kernel(BwdParams prm) {
     constexpr int64_t per = (int64_t)N * P;
-    constexpr int kB = 16;
+    constexpr int kB = 32;
     const int64_t units = prm.batch * prm.nheads;
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= 2 * units * per) return;
