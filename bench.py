@@ -569,7 +569,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
