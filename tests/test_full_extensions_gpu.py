@@ -1,8 +1,9 @@
-"""Full-size checks of the backward pass and the packed batches, in the launch configuration
-bench.py times, on outputs the oracle computes in seconds: the backward pass over the whole workload
-compared on batch element 0 (its dx, d log a, dB, dC and d init depend on that element alone), and
-the 32-sequence packed batch of ``bench.py --varlen 32`` compared on sampled sequences (the shortest,
-the longest and two others).  Bounds as everywhere: relative L2 <= 2e-2 for bf16 inputs."""
+"""Full-size checks of the backward pass, the packed batches and the discretisation front-end, in
+the launch configuration bench.py times, on outputs the oracle computes in seconds: the backward
+pass over the whole workload compared on batch element 0 (its dx, d log a, dB, dC and d init depend
+on that element alone), the 32-sequence packed batch of ``bench.py --varlen 32`` compared on sampled
+sequences (the shortest, the longest and two others), and the front-end's forward over the whole
+workload, every output.  Bounds as everywhere: relative L2 <= 2e-2 for bf16 inputs."""
 import numpy as np
 import pytest
 import torch
@@ -56,3 +57,23 @@ def test_varlen_bench_batch_sampled():
         ef = rel_l2(fin[i].double().cpu().numpy(), fr[0])
         announce("full varlen sequence %d (%d tokens): y %.2e final %.2e" % (i, e - s, ey, ef))
         assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (i, ey, ef)
+
+
+@pytest.mark.parametrize("name", ["mamba2_layer", "diag_multiscale"])
+def test_forward_dt_full_workload(name):
+    """ssd_forward_dt over the whole workload as ``bench.py --front-end dt`` runs it (dt and A_log in,
+    input scaled, no bias) against the oracle's discretisation and recurrence, every output."""
+    import oracle.discretize
+    cfg = ssd_inputs.config(name)
+    announce("full forward_dt %s" % name)
+    inp = ssd_inputs.make_inputs(cfg, ssd_inputs.SEEDS[name])
+    g = to_gpu(inp)
+    y, fin = ssd.ssd_forward_dt(g["x"], g["dt"], g["A_log"], g["B"], g["C"], g.get("D"), chunk=cfg["chunk"],
+                                init_state=g.get("init_state"), final_state=True)
+    torch.cuda.synchronize()
+    yr, fr = oracle.discretize.forward_dt(oracle.default_oracle(), f64(inp["x"]), f64(inp["dt"]), f64(inp["A_log"]),
+                                          f64(inp["B"]), f64(inp["C"]), f64(inp.get("D")),
+                                          init_state=f64(inp.get("init_state")), diag=cfg["decay"] == "diag")
+    ey, ef = rel_l2(y.double().cpu().numpy(), yr), rel_l2(fin.double().cpu().numpy(), fr)
+    announce("full forward_dt %s: y %.2e final %.2e" % (name, ey, ef))
+    assert ey <= TOL[cfg["dtype"]] and ef <= TOL[cfg["dtype"]]
