@@ -174,6 +174,18 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(stream, *tensors):
+    """Mark the tensors a call reads or writes as used on the caller's launch stream when that is
+    not torch's current stream: the caching allocator then waits for the kernels on that stream
+    before it hands their memory to another allocation (the wrapper's own workspace is freed on
+    return, and outputs may be dropped by the caller on another stream)."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 SSD_MAX_LAUNCHES = 4
 
 
@@ -225,6 +237,7 @@ def _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, st
     args = (ctypes.byref(dims), _ptr(x), _ptr(log_a), _ptr(B), _ptr(C), _ptr(D), int(chunk),
             _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(workspace), ws_bytes,
             _stream_handle(stream, dev))
+    _on_stream(stream, y, final_state, workspace)
     if events is None:
         rc = lib.ssd_forward(*args)
         launches = None
@@ -294,6 +307,7 @@ def ssd_forward_varlen(x, log_a, B, C, cu_seqlens, max_seqlen: int, D=None, chun
     if events is not None:
         n = max(len(events), 2 * SSD_MAX_LAUNCHES)
         arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+    _on_stream(stream, y, final_state, workspace)
     rc = lib.ssd_forward_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(log_a), _ptr(B),
                                 _ptr(C), _ptr(D), int(chunk), _ptr(init_state), _ptr(y), _ptr(final_state),
                                 _ptr(workspace), ws_bytes, _stream_handle(stream, dev), arr, n,
@@ -350,6 +364,7 @@ def ssd_forward_dt_varlen(x, dt, A_log, B, C, cu_seqlens, max_seqlen: int, D=Non
     if events is not None:
         n = max(len(events), 2 * SSD_MAX_LAUNCHES)
         arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+    _on_stream(stream, y, final_state, workspace)
     rc = lib.ssd_forward_dt_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(dt), _ptr(dt_bias),
                                    _ptr(A_log), scale, _ptr(B), _ptr(C), _ptr(D), int(chunk), _ptr(init_state),
                                    _ptr(y), _ptr(final_state), _ptr(workspace), ws_bytes,
@@ -420,6 +435,7 @@ def _forward_dt(x, dt, A_log, B, C, D, dt_bias, scale_input, chunk, init_state, 
     args = (ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), scale, _ptr(B),
             _ptr(C), _ptr(D), int(chunk), _ptr(init_state), _ptr(y), _ptr(final_state),
             _ptr(workspace), ws_bytes, _stream_handle(stream, dev))
+    _on_stream(stream, y, final_state, workspace)
     if events is None:
         rc = lib.ssd_forward_dt(*args)
         launches = None
@@ -455,6 +471,7 @@ def ssd_step_dt(state, x_t, dt_t, A_log, B_t, C_t, D=None, dt_bias=None, scale_i
     _check(D, "D", (H,), torch.float32, dev)
     if y_t is None:
         y_t = torch.empty((bsz, H, P), dtype=x_t.dtype, device=dev)
+        _on_stream(stream, y_t)
     _check(y_t, "y_t", (bsz, H, P), x_t.dtype, dev)
     rc = load_library().ssd_step_dt(ctypes.byref(dims), _ptr(state), _ptr(x_t), _ptr(dt_t),
                                     _ptr(dt_bias), _ptr(A_log), 1 if scale_input else 0,
@@ -509,6 +526,7 @@ def ssd_backward(x, log_a, B, C, dy, D=None, init_state=None, dfinal=None, want_
             _ptr(dy), _ptr(dfinal), _ptr(out["dx"]), _ptr(out["dlog_a"]), _ptr(out["dB"]),
             _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]), _ptr(workspace), ws_bytes,
             _stream_handle(stream, dev))
+    _on_stream(stream, workspace, *out.values())
     if _events is None:
         rc = lib.ssd_backward(*args)
     else:
@@ -555,6 +573,7 @@ def ssd_backward_varlen(x, log_a, B, C, dy, cu_seqlens, max_seqlen: int, D=None,
     if events is not None:
         n = max(len(events), 2 * SSD_MAX_LAUNCHES)
         arr = (ctypes.c_void_p * n)(*(list(events) + [None] * (n - len(events))))
+    _on_stream(stream, workspace, *out.values())
     rc = lib.ssd_backward_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(log_a), _ptr(B),
                                  _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal), _ptr(out["dx"]),
                                  _ptr(out["dlog_a"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
@@ -601,6 +620,7 @@ def ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input: b
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _on_stream(stream, workspace, *out.values())
     rc = lib.ssd_backward_dt(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), scale,
                              _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal),
                              _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA_log"]),
@@ -649,6 +669,7 @@ def ssd_backward_dt_varlen(x, dt, A_log, B, C, dy, cu_seqlens, max_seqlen: int, 
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _on_stream(stream, workspace, *out.values())
     rc = lib.ssd_backward_dt_varlen(ctypes.byref(dims), _ptr(cu_seqlens), int(T), _ptr(x), _ptr(dt), _ptr(dt_bias),
                                     _ptr(A_log), scale, _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy),
                                     _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA_log"]),
@@ -678,6 +699,7 @@ def ssd_step(state, x_t, log_a_t, B_t, C_t, D=None, y_t=None, stream=None):
     _check(D, "D", (H,), torch.float32, dev)
     if y_t is None:
         y_t = torch.empty((bsz, H, P), dtype=x_t.dtype, device=dev)
+        _on_stream(stream, y_t)
     _check(y_t, "y_t", (bsz, H, P), x_t.dtype, dev)
     rc = load_library().ssd_step(ctypes.byref(dims), _ptr(state), _ptr(x_t), _ptr(log_a_t),
                                  _ptr(B_t), _ptr(C_t), _ptr(D), _ptr(y_t),

@@ -97,3 +97,53 @@ def compare(inp: dict, y_gpu, fin_gpu, ref: dict, dtype: str, check_final: bool,
     assert np.all(np.isfinite(got_y)), label + ": non-finite outputs"
     assert ok, msg
     return e_y
+
+
+def per_unit_rel_l2(got, want):
+    """relL2 of every (batch, head) unit of [B, T, H, ...] arrays over its own elements
+    (units whose reference is all zeros report their absolute error)."""
+    d = (np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+    w = np.asarray(want, dtype=np.float64)
+    axes = tuple(a for a in range(d.ndim) if a not in (0, 2))
+    num = np.sqrt((d * d).sum(axis=axes))
+    den = np.sqrt((w * w).sum(axis=axes))
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def compare_all_units(inp: dict, y_gpu, fin_gpu, dtype: str, label: str):
+    """Every (batch, head) unit of a forward against the oracle run over the whole batch: the
+    pooled relL2 of y, of the SSD part y - D x and of the final state, and the same per unit
+    (an error confined to one unit is not diluted by the others).  The SSD part's bound adds
+    the output rounding it cannot avoid, per unit as pooled."""
+    f = ssd_inputs.to_f64
+    x = f(inp["x"])
+    D = f(inp.get("D"))
+    want_y, want_f = oracle.forward(x, f(inp["log_a"]), f(inp["B"]), f(inp["C"]), D, f(inp.get("init_state")))
+    got_y = y_gpu.double().cpu().numpy()
+    got_f = fin_gpu.double().cpu().numpy()
+    skip = np.zeros_like(x) if D is None else D[None, None, :, None] * x
+    tol, u = TOL[dtype], OUT_ROUNDOFF[dtype]
+    e_y, e_f = rel_l2(got_y, want_y), rel_l2(got_f, want_f)
+    e_ssd = rel_l2(got_y - skip, want_y - skip)
+    y_norm = float(np.linalg.norm(want_y.ravel()))
+    ssd_norm = float(np.linalg.norm((want_y - skip).ravel()))
+    tol_ssd = tol + (u * y_norm / ssd_norm if ssd_norm > 0 else 0.0)
+    uy = per_unit_rel_l2(got_y, want_y)
+    ussd = per_unit_rel_l2(got_y - skip, want_y - skip)
+    axes = (1, 3)
+    uy_norm = np.sqrt((want_y ** 2).sum(axis=axes))
+    ussd_norm = np.sqrt(((want_y - skip) ** 2).sum(axis=axes))
+    utol_ssd = tol + np.where(ussd_norm > 0, u * uy_norm / np.where(ussd_norm > 0, ussd_norm, 1.0), 0.0)
+    # final states per unit: [B, H, N, P] -> relL2 over (N, P)
+    df = got_f - want_f
+    uf = np.sqrt((df ** 2).sum(axis=(2, 3))) / np.maximum(np.sqrt((want_f ** 2).sum(axis=(2, 3))), 1e-300)
+    worst = np.unravel_index(int(np.argmax(uy)), uy.shape)
+    announce("%s: relL2 y %.3e ssd-part %.3e (tol %.2e) final %.3e; worst unit %s: y %.3e, max per unit "
+             "ssd-part/bound %.3f, final %.3e (tol %.0e)"
+             % (label, e_y, e_ssd, tol_ssd, e_f, tuple(int(v) for v in worst), float(uy.max()),
+                float((ussd / utol_ssd).max()), float(uf.max()), tol))
+    assert np.all(np.isfinite(got_y)) and np.all(np.isfinite(got_f)), label + ": non-finite outputs"
+    assert e_y <= tol and e_ssd <= tol_ssd and e_f <= tol, (e_y, e_ssd, e_f)
+    assert float(uy.max()) <= tol, "unit %s: y %.3e" % (worst, float(uy.max()))
+    assert float((ussd / utol_ssd).max()) <= 1.0, "a unit's SSD part is over its bound"
+    assert float(uf.max()) <= tol, "a unit's final state: %.3e" % float(uf.max())

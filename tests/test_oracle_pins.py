@@ -28,9 +28,10 @@ def test_discretization_pin(orc, pin):
 @pytest.mark.parametrize("diag", [False, True])
 @pytest.mark.parametrize("chunk", [1, 5, 16, 32, 64, 100, 256])
 def test_chunked_model_matches_recurrence(orc, diag, chunk):
-    """Chunk-size invariance of the two-algorithm form (aiwiki "State Space Duality": the two
-    halves of the loop are separated by the chunk boundary and nothing else), including a
-    last chunk shorter than the others."""
+    """Chunk-size invariance of the two-algorithm form (aiwiki "State Space Duality", "Two
+    algorithms for one operator": where the chunk boundaries fall changes only which pairs the
+    quadratic form covers and which the state carries, not the result), including a last chunk
+    shorter than the others."""
     rng = np.random.default_rng(100 + chunk)
     prob = _problem(rng, nb=2, T=100, H=4, G=2, P=5, N=6, diag=diag, decay_scale=3.0)
     y, fin = orc.forward(*prob)
