@@ -311,3 +311,64 @@ def test_decode_steps_in_a_hip_graph():
         assert torch.equal(state, want_state), rep
         for y, w in zip(ys, want_y):
             assert torch.equal(y.view(torch.int16), w.view(torch.int16)), rep
+
+
+def test_side_stream_call_keeps_its_memory():
+    """A call on a side stream whose workspace and outputs the binding allocates: right after it
+    returns (its kernels still running), same-sized allocations on torch's current stream are
+    filled with NaN.  The allocator must not hand them the call's memory before its kernels end,
+    so the outputs equal those of a call on the current stream bit for bit."""
+    import ssd_chunked_scan_02_amd as ssd
+    cfg = ssd_inputs.config("mamba2_layer")
+    g = to_gpu(ssd_inputs.make_inputs(cfg, 211))
+    announce("side-stream call with allocations on the current stream")
+    y0, _ = ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g["D"], chunk=cfg["chunk"])
+    torch.cuda.synchronize()
+    dims = ssd.dims_for(g["x"], g["log_a"], g["B"])
+    ws_bytes = ssd.ssd_forward_workspace_bytes(dims, cfg["chunk"])
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        y, _ = ssd.ssd_forward(g["x"], g["log_a"], g["B"], g["C"], g["D"], chunk=cfg["chunk"], stream=side)
+        junk = [torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda"),
+                torch.full(tuple(y.shape), float("nan"), dtype=y.dtype, device="cuda")]
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), rep
+        del junk
+
+
+# (bf16 covers N 32..256, fp32 N 16..128; rows per thread 1, 2, 4, 8 and 16)
+STEP_SHAPES = [("bf16", "scalar", 32, 16), ("bf16", "scalar", 256, 64), ("bf16", "scalar", 128, 128),
+               ("bf16", "diag", 32, 32), ("fp32", "scalar", 128, 128), ("fp32", "diag", 16, 64),
+               ("fp32", "scalar", 64, 16), ("bf16", "diag", 256, 32), ("fp32", "diag", 64, 64),
+               ("bf16", "scalar", 32, 64)]
+
+
+@pytest.mark.parametrize("dtype,decay,N,P", STEP_SHAPES, ids=["%s-%s-n%d-p%d" % s for s in STEP_SHAPES])
+def test_step_shapes_continue_forward(dtype, decay, N, P):
+    """Decode steps at every rows-per-thread split of the step kernel (state dims 16..256, head
+    dims 16..128, both element types and both decay kinds): k steps from an initial state equal
+    the oracle's recurrence over the same k tokens, y of every step and the final state."""
+    import oracle
+    import ssd_chunked_scan_02_amd as ssd
+    from gpu_helpers import rel_l2
+    name = "diag_multiscale" if decay == "diag" else "mamba2_layer"
+    cfg = ssd_inputs.config(name, batch=2, seqlen=1, nheads=4, ngroups=2, dstate=N, headdim=P, dtype=dtype,
+                            init=True, decode_steps=9)
+    inp = ssd_inputs.make_inputs(cfg, 223)
+    g = to_gpu(inp)
+    announce("step shapes %s %s N=%d P=%d" % (dtype, decay, N, P))
+    state = g["init_state"].clone()
+    ys = [ssd.ssd_step(state, g["x_dec"][:, t].contiguous(), g["log_a_dec"][:, t].contiguous(),
+                       g["B_dec"][:, t].contiguous(), g["C_dec"][:, t].contiguous(), g["D"]).clone()
+          for t in range(cfg["decode_steps"])]
+    torch.cuda.synchronize()
+    f = ssd_inputs.to_f64
+    yr, fr = oracle.forward(f(inp["x_dec"]), f(inp["log_a_dec"]), f(inp["B_dec"]), f(inp["C_dec"]), f(inp["D"]),
+                            f(inp["init_state"]))
+    y_dec = np.stack([y.double().cpu().numpy() for y in ys], 1)
+    e_y = rel_l2(y_dec, yr)
+    e_f = rel_l2(state.double().cpu().numpy(), fr)
+    announce("step shapes %s %s N=%d P=%d: y %.2e final %.2e" % (dtype, decay, N, P, e_y, e_f))
+    assert e_y <= TOL[dtype] and e_f <= TOL[dtype]
