@@ -219,20 +219,53 @@ def cpu_baseline(inp, cfg, min_seconds, front_end="log_a"):
     reps, t0 = 0, time.perf_counter()
     while True:
         if front_end == "dt":
-            oracle.discretize.forward_dt(oracle.default_oracle(), args[0], f(inp["dt"]), f(inp["A_log"]), args[2],
-                                         args[3], args[4], init_state=args[5], want_final=cfg["final"],
-                                         diag=cfg["decay"] == "diag", nthreads=threads)
+            out = oracle.discretize.forward_dt(oracle.default_oracle(), args[0], f(inp["dt"]), f(inp["A_log"]),
+                                               args[2], args[3], args[4], init_state=args[5], want_final=True,
+                                               diag=cfg["decay"] == "diag", nthreads=threads)
         else:
-            oracle.forward(*args, want_final=cfg["final"], nthreads=threads)
+            out = oracle.forward(*args, want_final=True, nthreads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds and reps >= 1:
             break
     tokens = cfg["batch"] * cfg["seqlen"] * reps
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": "the whole workload (%d x %d tokens x %d heads), %d run(s) in %.1f s, "
-                      "fp64 sequential recurrence, OpenMP over (batch, head)"
-                      % (cfg["batch"], cfg["seqlen"], cfg["nheads"], reps, el)}
+    return ({"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+             "sample": "the whole workload (%d x %d tokens x %d heads), %d run(s) in %.1f s, "
+                       "fp64 sequential recurrence, OpenMP over (batch, head)"
+                       % (cfg["batch"], cfg["seqlen"], cfg["nheads"], reps, el)}, out)
+
+
+def output_parity(cfg, inp, y, final, ref):
+    """The timed run's outputs against the oracle's on the same stored inputs: relative L2 of y,
+    of the SSD part y - D x and of the final state, with the bounds of the parity tests (1e-5
+    for fp32 inputs, 2e-2 for bf16; the SSD part's bound adds the one rounding of y, relative to
+    the whole of y, that it cannot avoid)."""
+    import numpy as np
+    import ssd_inputs
+    tol = 1e-5 if cfg["dtype"] == "fp32" else 2e-2
+    u = 2.0 ** -24 if cfg["dtype"] == "fp32" else 2.0 ** -8
+    yr, fr = ref
+    yg = y.double().cpu().numpy()
+    x = ssd_inputs.to_f64(inp["x"])
+    D = ssd_inputs.to_f64(inp.get("D"))
+    skip = np.zeros_like(x) if D is None else D[None, None, :, None] * x
+
+    def rel(a, b):
+        n = float(np.linalg.norm((b).ravel()))
+        return float(np.linalg.norm((a - b).ravel())) / n if n > 0 else float(np.linalg.norm(a.ravel()))
+
+    e_y = rel(yg, yr)
+    e_ssd = rel(yg - skip, yr - skip)
+    ssd_norm = float(np.linalg.norm((yr - skip).ravel()))
+    tol_ssd = tol + (u * float(np.linalg.norm(yr.ravel())) / ssd_norm if ssd_norm > 0 else 0.0)
+    out = {"rel_l2_y": e_y, "rel_l2_ssd_part": e_ssd, "tol": tol, "tol_ssd_part": tol_ssd,
+           "reference": "fp64 oracle on the same stored inputs; outputs of the timed run"}
+    ok = e_y <= tol and e_ssd <= tol_ssd and bool(np.isfinite(yg).all())
+    if final is not None and fr is not None:
+        out["rel_l2_final"] = rel(final.double().cpu().numpy(), fr)
+        ok = ok and out["rel_l2_final"] <= tol
+    out["pass"] = bool(ok)
+    return out
 
 
 def time_decode(ssd, cfg, g, stream, ev, dev):
@@ -266,14 +299,19 @@ def time_decode(ssd, cfg, g, stream, ev, dev):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cap):
         run()
-    graph.replay()
+    # torch replays a graph on its current stream: replay on `cap`, where the events are recorded
+    with torch.cuda.stream(cap):
+        graph.replay()
     torch.cuda.synchronize()
+    reps = 5
     b, e = ev.create(), ev.create()
     ev.lib.hipEventRecord(b, cap.cuda_stream)
-    graph.replay()
+    with torch.cuda.stream(cap):
+        for _ in range(reps):
+            graph.replay()
     ev.lib.hipEventRecord(e, cap.cuda_stream)
     torch.cuda.synchronize()
-    us = ev.elapsed_ms(b, e) * 1e3 / steps
+    us = ev.elapsed_ms(b, e) * 1e3 / (steps * reps)
     ev.destroy(b)
     ev.destroy(e)
     esz = 2 if cfg["dtype"] == "bf16" else 4
@@ -283,7 +321,8 @@ def time_decode(ssd, cfg, g, stream, ev, dev):
     log("decode: %d steps, %.2f us/step" % (steps, us))
     # (each (batch, head) state lands on the same XCD every step, so it stays in that XCD's L2:
     # the effective rate is not bounded by HBM)
-    return {"steps": steps, "us_per_step": us, "timing": "one replay of a HIP graph of all steps",
+    return {"steps": steps, "us_per_step": us,
+            "timing": "%d replays of a HIP graph of all steps, events on the replay stream" % reps,
             "bytes_per_step": state_bytes + io_bytes,
             "effective_gbs": (state_bytes + io_bytes) / (us / 1e6) / 1e9}
 
@@ -299,6 +338,73 @@ def calibrate_copy(dev, mib):
     torch.cuda.synchronize()
     del dst
     log("calibration: neg kernel reading and writing %d MiB each" % mib)
+
+
+def measured_copy_gbs(dev, ev, stream, mib=1024, reps=5):
+    """HBM bandwidth this GPU reaches in a plain device copy of `mib` MiB (read once, written
+    once), timed with events on the launch stream: the practical ceiling beside the published
+    8 TB/s."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    b, e = ev.create(), ev.create()
+    ev.lib.hipEventRecord(b, stream.cuda_stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    ev.lib.hipEventRecord(e, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(b, e) / reps
+    ev.destroy(b)
+    ev.destroy(e)
+    del src, dst
+    gbs = 2.0 * n / (ms / 1e3) / 1e9
+    log("device copy of %d MiB: %.1f GB/s (read + write)" % (mib, gbs))
+    return gbs
+
+
+def shape_text(cfg):
+    """The workload's shape as the metric names it: B, T, H, P, N (and G, chunk and the decay
+    kind where they differ from one group, chunk 128 and scalar decay)."""
+    t = "B=%d,T=%d,H=%d,P=%d,N=%d" % (cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"])
+    if cfg["ngroups"] != 1:
+        t += ",G=%d" % cfg["ngroups"]
+    if cfg["chunk"] != 128:
+        t += ",chunk=%d" % cfg["chunk"]
+    if cfg["decay"] != "scalar":
+        t += ",%s decay" % cfg["decay"]
+    if cfg["dtype"] != "bf16":
+        t += ",%s" % cfg["dtype"]
+    return t
+
+
+def provenance(workload, seed):
+    """Where the numbers come from: the seed, the sources' hash (and the git commit when a
+    checkout is present), the GPU and the ROCm / torch versions."""
+    import subprocess
+    import torch
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.abspath(__file__), "rb") as f:
+        h.update(f.read())
+    try:
+        head = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True,
+                              text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        head = None
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"workload": workload, "seed": seed, "sources_sha256_16": h.hexdigest()[:16], "git_head": head,
+            "gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "cus": props.multi_processor_count, "rocm": rocm, "hip": torch.version.hip, "torch": torch.__version__}
 
 
 BWD_CHUNK = 32  # tokens per backward chunk (the library's)
@@ -665,6 +771,7 @@ def main():
 
     if args.calibrate_copy_mib:
         calibrate_copy(dev, args.calibrate_copy_mib)
+    copy_gbs = measured_copy_gbs(dev, ev, stream)
 
     tokens = cfg["batch"] * cfg["seqlen"]
     tok_s = tokens / (ms / 1e3)
@@ -676,7 +783,7 @@ def main():
     profile_key = args.workload if fe == "log_a" else args.workload + "_dt"
     traffic = measured_traffic(profile_key, names[dom])
     result = {
-        "metric": "SSD forward tokens/s + TFLOP/s (% MFMA peak) at B=8,T=2048,H=24,P=64,N=128",
+        "metric": "SSD forward tokens/s + TFLOP/s (% MFMA peak) at " + shape_text(cfg),
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -704,14 +811,26 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
                      "bytes_per_token": dom_bytes / tokens, "tokens_per_launch": tokens,
-                     "forward_bytes_per_token": per_token},
+                     "forward_bytes_per_token": per_token,
+                     "peak_measured_copy": copy_gbs, "frac_of_measured_copy": achieved / copy_gbs},
+        "provenance": provenance(args.workload, seed),
     }
     if cfg.get("decode_steps", 0) > 0:
         result["decode"] = time_decode(ssd, cfg, bufs[0], stream, ev, dev)
+    ok = True
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle (>= %.0f s)..." % args.cpu_seconds)
-        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds, fe)
+        result["cpu_baseline"], ref = cpu_baseline(inp, cfg, args.cpu_seconds, fe)
+        # the same oracle run checks the timed kernels' outputs (every copy holds the same inputs)
+        result["parity"] = output_parity(cfg, inp, bufs[0]["y"], bufs[0]["final"], ref)
+        log("parity: relL2 y %.3e, SSD part %.3e%s -> %s"
+            % (result["parity"]["rel_l2_y"], result["parity"]["rel_l2_ssd_part"],
+               (", final %.3e" % result["parity"]["rel_l2_final"]) if "rel_l2_final" in result["parity"] else "",
+               "ok" if result["parity"]["pass"] else "FAILED"))
+        ok = result["parity"]["pass"]
     print(json.dumps(result), flush=True)
+    if not ok:
+        sys.exit(1)
 
 
 if __name__ == "__main__":
