@@ -35,16 +35,20 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libssd.so next to this file; returns its path."""
+    """Compile every source (in parallel) and link libssd.so next to this file; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", CSRC]
-    objs, logs = [], []
+    cmds, objs = [], []
     for src in DEVICE_SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        logs.append(_run([HIPCC, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj]))
+        cmds.append([HIPCC, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     a_obj = os.path.join(BUILD_DIR, "ssd_api.o")
-    logs.append(_run([HIPCC, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "ssd_api.cpp"), "-o", a_obj]))
+    cmds.append([HIPCC, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "ssd_api.cpp"), "-o", a_obj])
+    jobs = max(1, min(len(cmds), len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        logs = list(pool.map(_run, cmds))
     tmp = LIBRARY + ".tmp%d" % os.getpid()
     logs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, a_obj, "-o", tmp]))
     os.replace(tmp, LIBRARY)
