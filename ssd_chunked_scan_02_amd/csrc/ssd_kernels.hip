@@ -344,46 +344,111 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Decode step: one workgroup per (batch, head); thread (r, p) updates state rows
-// n = r, r + R, ... of column p and the column's readout is summed over r in LDS.
-template <typename T>
+// Decode step (llms.blog "The Duality of Inference and Training in Linear Time-Invariant
+// SSMs": the recurrent mode, one token at a time): h <- a h + B_t x_t^T, y_t = C_t^T h + D x_t.
+// One 256-thread workgroup per (batch, head).  Thread (r, q) owns columns 4q .. 4q + 3 of the
+// state rows r RPT .. r RPT + RPT - 1; it issues every load of its rows (16 bytes each, with
+// the rows' B, C and decays) before its first FMA, so a workgroup has the whole 32 KiB state of
+// its head in flight at once, then writes its rows back and reduces its part of the readout
+// over the row groups (wave shuffles, then one LDS exchange between the four waves).
+template <typename T, int RPT>
+__device__ __forceinline__ void load_rows(const T* src, float (&v)[RPT]) {
+    if constexpr ((RPT * sizeof(T)) % 16 == 0) {
+        constexpr int E = 16 / sizeof(T), L = RPT / E;
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            const uint4 w = ld16(src + E * l);
+            if constexpr (sizeof(T) == 4) {
+                const f32x4 f = as_f32x4(w);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * l + e] = f[e];
+            } else {
+                const bf16x8 f = as_bf16x8(w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[8 * l + e] = (float)f[e];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) v[k] = to_f32(src[k]);
+    }
+}
+
+template <typename T, int RPT>
 __global__ void __launch_bounds__(kThreads) step_kernel(StepParams prm) {
     const int64_t unit = blockIdx.x;
     const int64_t H = prm.nheads, G = prm.ngroups;
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
     const int P = prm.headdim, N = prm.dstate;
-    const int R = kThreads / P;
-    const int p = threadIdx.x % P, r = threadIdx.x / P;
-    const T* xt = static_cast<const T*>(prm.x_t);
-    const T* Bt = static_cast<const T*>(prm.B_t) + (b * G + g) * N;
-    const T* Ct = static_cast<const T*>(prm.C_t) + (b * G + g) * N;
-    const float xp = to_f32(xt[unit * P + p]);
+    const int QP = P / 4;                      // column quads per row
+    const int q = threadIdx.x % QP, r = threadIdx.x / QP;
+    const int n0 = r * RPT;                    // first row of this thread
+    const bool active = n0 < N;                // (more row groups than rows for small N)
+    const int nrow = active ? n0 : 0;
+    const T* __restrict__ xt = static_cast<const T*>(prm.x_t) + unit * P + 4 * q;
+    const T* __restrict__ Bt = static_cast<const T*>(prm.B_t) + (b * G + g) * N + nrow;
+    const T* __restrict__ Ct = static_cast<const T*>(prm.C_t) + (b * G + g) * N + nrow;
+    float* __restrict__ st = prm.state + unit * N * P + (int64_t)nrow * P + 4 * q;
+
+    // every load first: the state rows, x, B, C and the decays of this thread's rows
+    f32x4 s[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) s[k] = *reinterpret_cast<const f32x4*>(st + k * P);
+    float xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = to_f32(xt[i]);
+    const float d = prm.D ? prm.D[h] : 0.f;  // (loaded with the rest, not after the reduction)
+    float bv[RPT], cv[RPT];
+    load_rows<T, RPT>(Bt, bv);
+    load_rows<T, RPT>(Ct, cv);
     // with the discretisation front-end: Delta = softplus(dt + bias), log a = -Delta exp(A_log)
     // (per head, or per (head, n)), and the input term scaled by Delta
     const bool disc = prm.dt_t != nullptr;
     const float delta = disc ? softplusf(prm.dt_t[unit] + (prm.dt_bias ? prm.dt_bias[h] : 0.f)) : 0.f;
-    const float xin = disc && prm.scale_input ? delta * xp : xp;
-    auto log_a = [&](int n) {
-        if (disc) return -delta * expf(prm.diag ? prm.A_log[h * N + n] : prm.A_log[h]);
-        return prm.diag ? prm.log_a_t[unit * N + n] : prm.log_a_t[unit];
-    };
-    const float a_head = prm.diag ? 0.f : expf(log_a(0));
-    float* st = prm.state + unit * N * P;
-    float acc = 0.f;
-    for (int n = r; n < N; n += R) {
-        const float a = prm.diag ? expf(log_a(n)) : a_head;
-        const float s = a * st[n * P + p] + to_f32(Bt[n]) * xin;
-        st[n * P + p] = s;
-        acc += to_f32(Ct[n]) * s;
+    float av[RPT];  // the decay factor a of each row
+    if (prm.diag) {
+        load_rows<float, RPT>(disc ? prm.A_log + h * N + nrow : prm.log_a_t + unit * N + nrow, av);
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) av[k] = expf(disc ? -delta * expf(av[k]) : av[k]);
+    } else {
+        const float a = expf(disc ? -delta * expf(prm.A_log[h]) : prm.log_a_t[unit]);
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) av[k] = a;
     }
-    __shared__ float red[kThreads];
-    red[threadIdx.x] = acc;
+    const float sc = disc && prm.scale_input ? delta : 1.f;
+    float xin[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xin[i] = sc * xv[i];
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[k][i] = av[k] * s[k][i] + bv[k] * xin[i];
+            acc[i] += cv[k] * s[k][i];
+        }
+    }
+    if (active)  // (an active thread's rows all lie below N: N is a multiple of RPT)
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) *reinterpret_cast<f32x4*>(st + k * P) = s[k];
+    if (!active) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    // partial readouts of the row groups of one column quad: first inside the wave ...
+#pragma unroll
+    for (int off = QP; off < kWave; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off, kWave);
+    // ... then between the waves
+    __shared__ f32x4 red[kWaves][kWave];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (lane < QP) red[wave][lane] = acc;
     __syncthreads();
-    if (r == 0) {
-        float sum = 0.f;
-        for (int q = 0; q < R; ++q) sum += red[q * P + p];
-        if (prm.D) sum += prm.D[h] * xp;
-        static_cast<T*>(prm.y_t)[unit * P + p] = from_f32<T>(sum);
+    if (threadIdx.x < QP) {
+        f32x4 y = red[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) y += red[w][threadIdx.x];
+        store4(static_cast<T*>(prm.y_t) + unit * P + 4 * q, y[0] + d * xv[0], y[1] + d * xv[1], y[2] + d * xv[2],
+               y[3] + d * xv[3]);
     }
 }
 
@@ -589,12 +654,29 @@ int launch_forward(const ForwardLaunch& fl, hipStream_t stream) {
     return -2;
 }
 
+template <typename T>
+bool launch_step_t(const StepParams& sp, int64_t units, hipStream_t stream) {
+    // rows per thread: the state's N rows over the 256 / (P / 4) row groups of a workgroup
+    const int groups = kThreads / (sp.headdim / 4);
+    const int rpt = (sp.dstate + groups - 1) / groups;
+    const dim3 grid((unsigned)units), block(kThreads);
+    switch (rpt) {
+        case 1: hipLaunchKernelGGL((step_kernel<T, 1>), grid, block, 0, stream, sp); break;
+        case 2: hipLaunchKernelGGL((step_kernel<T, 2>), grid, block, 0, stream, sp); break;
+        case 4: hipLaunchKernelGGL((step_kernel<T, 4>), grid, block, 0, stream, sp); break;
+        case 8: hipLaunchKernelGGL((step_kernel<T, 8>), grid, block, 0, stream, sp); break;
+        case 16: hipLaunchKernelGGL((step_kernel<T, 16>), grid, block, 0, stream, sp); break;
+        case 32: hipLaunchKernelGGL((step_kernel<T, 32>), grid, block, 0, stream, sp); break;
+        default: return false;
+    }
+    return true;
+}
+
 int launch_step(const StepParams& sp, int dtype, int64_t units, hipStream_t stream) {
     if (units == 0) return 0;
-    if (dtype == 0)
-        hipLaunchKernelGGL(step_kernel<float>, dim3((unsigned)units), dim3(kThreads), 0, stream, sp);
-    else
-        hipLaunchKernelGGL(step_kernel<__bf16>, dim3((unsigned)units), dim3(kThreads), 0, stream, sp);
+    // (the supported shapes: P in {16, 32, 64, 128}, N in {16, ..., 256}, so 1 <= rows per thread <= 32)
+    const bool ok = dtype == 0 ? launch_step_t<float>(sp, units, stream) : launch_step_t<__bf16>(sp, units, stream);
+    if (!ok) return -2;
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
