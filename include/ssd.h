@@ -24,7 +24,8 @@
  *     init_state, final_state, state   [B, H, N, P] fp32
  *
  * Ownership: every pointer belongs to the caller; the library never allocates, frees or
- * retains device memory, and keeps no state between calls.  Tensor pointers are DEVICE
+ * retains device memory, and keeps no state between calls (one exception: the fixed scratch
+ * array behind ssd_forward_noalloc, below).  Tensor pointers are DEVICE
  * pointers; `dims` is a HOST pointer read during the call only.  Work is enqueued on
  * `stream` (a hipStream_t passed as an opaque pointer; NULL = the default stream) and the
  * call returns without synchronising: outputs are valid once the stream has reached this
@@ -68,7 +69,8 @@ enum {
     SSD_ERR_INVALID = -1,     /* NULL required pointer, bad dimension, workspace too small */
     SSD_ERR_UNSUPPORTED = -2, /* valid but not implemented: chunk, N, P or dtype combination */
     SSD_ERR_ALIGN = -3,       /* a tensor pointer is not 16-byte aligned */
-    SSD_ERR_HIP = -4          /* the HIP runtime rejected a launch */
+    SSD_ERR_HIP = -4,         /* the HIP runtime rejected a launch */
+    SSD_ERR_SCRATCH = -5      /* ssd_forward_noalloc: workspace larger than its fixed scratch */
 };
 
 /*
@@ -301,6 +303,29 @@ int ssd_backward_dt_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int6
                            const float* init_state, const void* dy, const float* dfinal, void* dx,
                            float* ddt, float* dA_log, float* ddt_bias, float* dB, float* dC, float* dD,
                            float* dinit, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssd_forward without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It runs
+ * the same kernels as ssd_forward (same results, bit for bit) with the workspace placed in a
+ * fixed array of ssd_noalloc_scratch_bytes() bytes (96 MiB) that the library holds on each GPU
+ * it runs on, from the first use of the library's code on that GPU until the process ends.  The
+ * call allocates and frees nothing.  Arguments are those of ssd_forward minus the workspace.
+ *
+ * Limit: a call whose ssd_forward_workspace_bytes(dims, chunk) exceeds the array fails with
+ * SSD_ERR_SCRATCH before doing anything (the Mamba-2 layer shape, 8 x 2048 tokens x 24 heads at
+ * N = 128, needs 12 MiB; one 65 536-token sequence of 32 heads, 66 MiB; 4 x 8192 tokens x 64 heads
+ * in 8 groups, 183 MiB, which does not fit).
+ * Races: every call on one GPU uses that GPU's one array, so calls that overlap in time on one
+ * GPU (on different streams, or from several threads without ordering) corrupt each other's
+ * workspace.  Calls ordered on one stream are safe: no call needs anything the previous one left
+ * in the array.  The first call on each device looks up the array's device address (one HIP
+ * runtime query, done before any launch); a failure there returns SSD_ERR_HIP.
+ */
+size_t ssd_noalloc_scratch_bytes(void);
+int ssd_forward_noalloc(const ssd_dims* dims, const void* x, const float* log_a, const void* B,
+                        const void* C, const float* D, int chunk, const float* init_state, void* y,
+                        float* final_state, void* stream);
 
 /* Static, human-readable description of a return code. */
 const char* ssd_strerror(int code);

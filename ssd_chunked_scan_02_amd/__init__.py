@@ -19,6 +19,9 @@ The functions carry the names of the C entry points declared in ``include/ssd.h`
   ssd_backward_profiled(..., events=(hipEvent_t handles)) -> (gradients, n_launches)
   ssd_backward_dt_workspace_bytes(dims, scale_input) -> int
   ssd_backward_dt(x, dt, A_log, B, C, dy, D=None, dt_bias=None, scale_input=True, ...) -> dict
+  ssd_noalloc_scratch_bytes() -> int
+  ssd_forward_noalloc(x, log_a, B, C, D=None, chunk=..., init_state=None, y=None,
+                      final_state=None, stream=None) -> (y, final_state)
   ssd_strerror(code) -> str
 """
 from __future__ import annotations
@@ -33,12 +36,12 @@ __all__ = ["SSDError", "Dims", "library_path", "load_library", "dims_for",
            "ssd_forward_dt_workspace_bytes", "ssd_forward_dt", "ssd_forward_dt_profiled",
            "ssd_step_dt", "ssd_backward_workspace_bytes", "ssd_backward", "ssd_backward_profiled",
            "ssd_backward_dt_workspace_bytes", "ssd_backward_dt",
-           "ssd_strerror",
+           "ssd_forward_noalloc", "ssd_noalloc_scratch_bytes", "ssd_strerror",
            "SSD_F32", "SSD_BF16", "SSD_DECAY_SCALAR", "SSD_DECAY_DIAG"]
 
 SSD_F32, SSD_BF16 = 0, 1
 SSD_DECAY_SCALAR, SSD_DECAY_DIAG = 0, 1
-SSD_OK, SSD_ERR_INVALID, SSD_ERR_UNSUPPORTED, SSD_ERR_ALIGN, SSD_ERR_HIP = 0, -1, -2, -3, -4
+SSD_OK, SSD_ERR_INVALID, SSD_ERR_UNSUPPORTED, SSD_ERR_ALIGN, SSD_ERR_HIP, SSD_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
@@ -124,6 +127,10 @@ def load_library():
         lib.ssd_backward_dt_varlen_workspace_bytes.restype = sz
         lib.ssd_backward_dt_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, i32] + [vp] * 15 + [sz, vp]
         lib.ssd_backward_dt_varlen.restype = i32
+        lib.ssd_noalloc_scratch_bytes.argtypes = []
+        lib.ssd_noalloc_scratch_bytes.restype = sz
+        lib.ssd_forward_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+        lib.ssd_forward_noalloc.restype = i32
         lib.ssd_strerror.argtypes = [i32]
         lib.ssd_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -250,6 +257,45 @@ def _forward(x, log_a, B, C, D, chunk, init_state, y, final_state, workspace, st
     if rc != SSD_OK:
         raise SSDError(rc, "ssd_forward")
     return y, final_state, launches
+
+
+def ssd_noalloc_scratch_bytes() -> int:
+    return int(load_library().ssd_noalloc_scratch_bytes())
+
+
+def ssd_forward_noalloc(x, log_a, B, C, D=None, chunk: int = 64, init_state=None, y=None, final_state=None,
+                        stream=None):
+    """Run ``ssd_forward_noalloc``: ssd_forward with its workspace in the library's fixed per-GPU
+    scratch array, so the C call allocates nothing (pass ``y`` and ``final_state`` as well for a
+    call that allocates nothing at all, e.g. under graph capture).  Raises SSDError with
+    SSD_ERR_SCRATCH when the workload's workspace is larger than the array.
+    Returns (y, final_state)."""
+    dims = dims_for(x, log_a, B)
+    dev = x.device
+    bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _check(x, "x", (bsz, T, H, P), x.dtype, dev)
+    _check(log_a, "log_a", (bsz, T, H, N) if dims.decay == SSD_DECAY_DIAG else (bsz, T, H), torch.float32, dev)
+    _check(B, "B", (bsz, T, G, N), x.dtype, dev)
+    _check(C, "C", (bsz, T, G, N), x.dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(init_state, "init_state", (bsz, H, N, P), torch.float32, dev)
+    if y is None:
+        y = torch.empty((bsz, T, H, P), dtype=x.dtype, device=dev)
+        _on_stream(stream, y)
+    _check(y, "y", (bsz, T, H, P), x.dtype, dev)
+    if final_state is True:
+        final_state = torch.empty((bsz, H, N, P), dtype=torch.float32, device=dev)
+        _on_stream(stream, final_state)
+    elif final_state is False:
+        final_state = None
+    _check(final_state, "final_state", (bsz, H, N, P), torch.float32, dev)
+    rc = load_library().ssd_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(log_a), _ptr(B), _ptr(C), _ptr(D),
+                                            int(chunk), _ptr(init_state), _ptr(y), _ptr(final_state),
+                                            _stream_handle(stream, dev))
+    if rc != SSD_OK:
+        raise SSDError(rc, "ssd_forward_noalloc")
+    return y, final_state
 
 
 def varlen_dims(x: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, nseq: int, max_seqlen: int) -> Dims:

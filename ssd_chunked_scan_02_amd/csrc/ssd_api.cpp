@@ -111,7 +111,8 @@ struct Varlen {
 int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Discretization* disc,
                  const void* B, const void* C, const float* D, int chunk, const float* init_state,
                  void* y, float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                 void* const* events, int n_events, int* n_launches, const Varlen* vl = nullptr) {
+                 void* const* events, int n_events, int* n_launches, const Varlen* vl = nullptr,
+                 bool check_only = false) {
     if (n_launches) *n_launches = 0;
     if (events && n_events < 2 * SSD_MAX_LAUNCHES) return SSD_ERR_INVALID;
     int rc = check_forward(d, chunk);
@@ -136,7 +137,7 @@ int forward_impl(const ssd_dims* d, const void* x, const float* log_a, const Dis
     const size_t need = disc ? workspace_needed_dt(d, chunk, disc->scale_input, vl != nullptr)
                              : workspace_needed(d, chunk, vl != nullptr);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SSD_ERR_INVALID;
-    if (d->batch == 0) return SSD_OK;
+    if (check_only || d->batch == 0) return SSD_OK;
     if ((d->seqlen == 0 || (vl && vl->total == 0)) && !final_state) return SSD_OK;
 
     int count = 0;
@@ -490,6 +491,32 @@ int ssd_backward_dt_varlen(const ssd_dims* d, const int64_t* cu_seqlens, int64_t
                             ddt_bias, dB, dC, dD, dinit, workspace, workspace_bytes, stream, &vl);
 }
 
+size_t ssd_noalloc_scratch_bytes(void) { return ssd::noalloc_scratch_bytes(); }
+
+int ssd_forward_noalloc(const ssd_dims* d, const void* x, const float* log_a, const void* B, const void* C,
+                        const float* D, int chunk, const float* init_state, void* y, float* final_state,
+                        void* stream) {
+    // every check first (the workspace stands in as the scratch array's size at a dummy aligned
+    // address), then the one HIP call that finds this device's copy of the array
+    int rc = check_forward(d, chunk);
+    if (rc != SSD_OK) return rc;
+    const size_t need = workspace_needed(d, chunk);
+    if (need > ssd::noalloc_scratch_bytes()) return SSD_ERR_SCRATCH;
+    alignas(256) static const unsigned char probe[16] = {};
+    rc = forward_impl(d, x, log_a, nullptr, B, C, D, chunk, init_state, y, final_state, (void*)probe,
+                      ssd::noalloc_scratch_bytes(), stream, nullptr, 0, nullptr, nullptr, true);
+    if (rc != SSD_OK) return rc;
+    if (d->batch == 0) return SSD_OK;
+    void* ws = nullptr;
+    if (need > 0) {
+        int hip_rc = 0;
+        ws = ssd::noalloc_scratch(&hip_rc);
+        if (!ws) return SSD_ERR_HIP;
+    }
+    return forward_impl(d, x, log_a, nullptr, B, C, D, chunk, init_state, y, final_state, ws, need, stream,
+                        nullptr, 0, nullptr);
+}
+
 const char* ssd_strerror(int code) {
     switch (code) {
         case SSD_OK: return "success";
@@ -497,6 +524,9 @@ const char* ssd_strerror(int code) {
         case SSD_ERR_UNSUPPORTED: return "unsupported configuration (chunk, dstate, headdim, dtype or decay kind)";
         case SSD_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case SSD_ERR_HIP: return "HIP runtime rejected a kernel launch";
+        case SSD_ERR_SCRATCH:
+            return "the call needs more workspace than ssd_forward_noalloc's fixed scratch array holds "
+                   "(ssd_noalloc_scratch_bytes); call ssd_forward with a workspace instead";
         default: return "unknown error code";
     }
 }

@@ -223,6 +223,11 @@ size_t generic_workspace_bytes(int dtype, int decay, int64_t batch, int64_t nhea
 
 constexpr size_t kMaxLds = 160 * 1024;
 
+// The fixed per-device scratch array of ssd_forward_noalloc (ssd_noalloc.hip): its size, and the
+// device address of the current device's copy (null with *hip_rc set on failure).
+size_t noalloc_scratch_bytes();
+void* noalloc_scratch(int* hip_rc);
+
 // Segmented walks: with few (batch, head) units on a long sequence (at most half as many as the
 // 256 CUs), each sequence is split into segments of at least 4 chunks so that about `target`
 // workgroups walk (one per CU per round).  Returns the number of segments and sets *seg_chunks

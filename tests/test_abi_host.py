@@ -34,10 +34,10 @@ def test_header_declares_the_entry_points():
                                     "ssd_backward_varlen_workspace_bytes", "ssd_backward_workspace_bytes",
                                     "ssd_forward", "ssd_forward_dt", "ssd_forward_dt_profiled",
                                     "ssd_forward_dt_varlen", "ssd_forward_dt_varlen_workspace_bytes",
-                                    "ssd_forward_dt_workspace_bytes", "ssd_forward_profiled",
+                                    "ssd_forward_dt_workspace_bytes", "ssd_forward_noalloc", "ssd_forward_profiled",
                                     "ssd_forward_varlen", "ssd_forward_varlen_workspace_bytes",
-                                    "ssd_forward_workspace_bytes", "ssd_step", "ssd_step_dt",
-                                    "ssd_strerror"]
+                                    "ssd_forward_workspace_bytes", "ssd_noalloc_scratch_bytes", "ssd_step",
+                                    "ssd_step_dt", "ssd_strerror"]
 
 
 def test_library_exports_every_declared_function(lib):
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert ssd.ssd_strerror(code)
     assert "unknown" in ssd.ssd_strerror(7)
 
@@ -395,3 +395,25 @@ def test_backward_varlen_checks(lib):
     assert call(d, dy=None) == ssd.SSD_ERR_INVALID
     assert call(d, ws_bytes=ssd.ssd_backward_workspace_bytes(d) - 1) == ssd.SSD_ERR_INVALID
     assert call(mamba2_dims(decay=1)) == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """ssd_forward_noalloc: a workload whose workspace exceeds the fixed scratch array fails with
+    SSD_ERR_SCRATCH, and bad arguments with the codes of ssd_forward, all before any HIP call (so
+    also on a machine without a GPU)."""
+    cap = lib.ssd_noalloc_scratch_bytes()
+    assert cap == 96 << 20
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every check fails first
+    big = Dims(batch=4, seqlen=8192, nheads=64, ngroups=8, headdim=64, dstate=128, dtype=1, decay=0)
+    assert lib.ssd_forward_workspace_bytes(ctypes.byref(big), 128) > cap
+    args = (fake, fake, fake, fake, None, 128, None, fake, None, None)
+    assert lib.ssd_forward_noalloc(ctypes.byref(big), *args) == ssd.SSD_ERR_SCRATCH
+    fits = mamba2_dims()
+    assert 0 < lib.ssd_forward_workspace_bytes(ctypes.byref(fits), 128) <= cap
+    # a null input, a misaligned output, an unsupported chunk
+    assert lib.ssd_forward_noalloc(ctypes.byref(fits), None, fake, fake, fake, None, 128, None, fake, None,
+                                   None) == ssd.SSD_ERR_INVALID
+    assert lib.ssd_forward_noalloc(ctypes.byref(fits), fake, fake, fake, fake, None, 128, None,
+                                   ctypes.c_void_p((1 << 20) + 8), None, None) == ssd.SSD_ERR_ALIGN
+    assert lib.ssd_forward_noalloc(ctypes.byref(fits), *((fake,) * 4), None, 48, None, fake, None,
+                                   None) == ssd.SSD_ERR_UNSUPPORTED
