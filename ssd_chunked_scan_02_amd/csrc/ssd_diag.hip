@@ -124,7 +124,8 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
     if (unit < 0) return;
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
     const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // (the wave index made wave-uniform, so that the per-wave item loops run as scalar loops)
+    const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, lg = lane / 16;
     const int koff = (KB / 4) * lg;
     const L lay(prm.chunk);
@@ -437,16 +438,38 @@ constexpr float kSplitMax2 = kSplitMax * kLog2eD;  // the same bound in log2 uni
 __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kDiagThreads = kDiagWaves * kWave;
 
-// (FULL = false, the state-only pass, keeps only x^T, (w o B)^T, B, the running sums and the
+// An MFMA operand of a row-major [token][col] bf16 tile in LDS, contracting over tokens, with
+// the gfx950 transposing read ds_read_b64_tr_b16 (a 16-lane group whose lane 4r + q points at
+// row r, columns 4q .. 4q + 3 returns in lane i column i of those four rows): lane (g, i)
+// receives tile[32 k + tok(g, j)][col0 + i], j = 0..7, with tok(g, j) = 4g + j, 16 + 4g + j - 4
+// (KPERM, the row order of two stacked accumulator tiles) or 8g + j (natural order).
+template <bool KPERM>
+__device__ __forceinline__ bf16x8 x_frag(const __bf16* tile, int stride, int col0, int k, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int g = lane / 16, r = (lane % 16) / 4, q = lane % 4;
+    const int row0 = KPERM ? 32 * k + 4 * g + r : 32 * k + 8 * g + r;
+    const int row1 = KPERM ? row0 + 16 : row0 + 4;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + row0 * stride + col0 + 4 * q));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + row1 * stride + col0 + 4 * q));
+    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// (FULL = false, the state-only pass, keeps only x, (w o B)^T, B, the running sums and the
 // state-row decays: the other buffers have size 0, so three such workgroups fit on a CU)
 template <int N, int P, bool FULL = true>
 struct DiagPipeLayout {
     static constexpr int Q = kDiagQ, NT = Q / 16, QP = Q + 8, NP = N + 8, CS = N + 4;
+    // x staged row-major with rows P + 16 elements apart: eight consecutive rows then start on
+    // distinct banks for the transposing reads of its MFMA operands
+    static constexpr int XS = P + 16;
     static constexpr int NOFF = NT * (NT - 1) / 2;
     static constexpr size_t F = FULL ? 1 : 0;
     // offsets in bytes
-    static constexpr size_t xt = 0;                                   // x^T          [P][QP] bf16
-    static constexpr size_t bt = xt + (size_t)P * QP * 2;            // (w o B)^T    [N][QP] bf16
+    static constexpr size_t xt = 0;                                   // x            [Q][XS] bf16
+    static constexpr size_t bt = xt + (size_t)Q * XS * 2;            // (w o B)^T    [N][QP] bf16
     static constexpr size_t ht = bt + (size_t)N * QP * 2;            // H^T          [P][NP] bf16
     static constexpr size_t cc = ht + F * P * NP * 2;                // C o exp(cum) [Q][NP] bf16
     static constexpr size_t cf = cc + F * Q * NP * 2;                // C o f        [Q][NP] bf16
@@ -471,7 +494,7 @@ template <int N, int P, bool FULL, bool DT = false>
 __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams prm) {
     constexpr int kThreads = kDiagThreads, kWaves = kDiagWaves;  // (this kernel's own workgroup)
     using L = DiagPipeLayout<N, P, FULL>;
-    constexpr int Q = L::Q, NT = L::NT, QP = L::QP, NP = L::NP, CS = L::CS;
+    constexpr int Q = L::Q, NT = L::NT, QP = L::QP, NP = L::NP, CS = L::CS, XS = L::XS;
     constexpr int PB = P / 16, NB = N / 16, NTILE = NB * PB, TPW = (NTILE + kWaves - 1) / kWaves;
     // 16-byte pieces per chunk of log a, of B (and of C) and of x, and per thread (rounded up;
     // the pieces past the total are skipped, which is uniform over a wave)
@@ -486,7 +509,8 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     const int seg = (int)(work / units);
     const int64_t unit = work % units;
     const int64_t b = unit / H, h = unit % H, g = h / (H / G);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // (the wave index made wave-uniform, so that the per-wave item loops run as scalar loops)
+    const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, lg = lane / 16;
     const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
     // (a packed sequence: its own chunk count; it is never segmented)
@@ -502,7 +526,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     }
 
     extern __shared__ __align__(16) unsigned char smem[];
-    __bf16* Xt = reinterpret_cast<__bf16*>(smem + L::xt);
+    __bf16* Xr = reinterpret_cast<__bf16*>(smem + L::xt);
     __bf16* Bt = reinterpret_cast<__bf16*>(smem + L::bt);
     __bf16* Ht = reinterpret_cast<__bf16*>(smem + L::ht);
     __bf16* Cc = reinterpret_cast<__bf16*>(smem + L::cc);
@@ -601,11 +625,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 #pragma unroll
         for (int m = 0; m < XI; ++m) {
             const int id = tid + kThreads * m, t = id / (P / 8), c8 = id % (P / 8);
-            if (id < XT) {
-                const bf16x8 v = as_bf16x8(t < len ? rx[m] : zero);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) Xt[(8 * c8 + j) * QP + t] = v[j];
-            }
+            if (id < XT) st16(Xr + t * XS + 8 * c8, t < len ? rx[m] : zero);
         }
     };
 
@@ -650,20 +670,25 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 
         // ---- 1. running sums down each state column (kThreads / N token groups per column)
         {
+            // (each thread's PER values read at once and kept in registers; the partial sums of the
+            // groups before it read at once, unrolled and masked)
             constexpr int NGR = kThreads / N, PER = Q / NGR;
             const int n = tid % N, grp = tid / N;
-            float run = 0.f;
+            float v[PER];
 #pragma unroll
-            for (int t = grp * PER; t < grp * PER + PER; ++t) {
-                run += cum[t * CS + n];
-                cum[t * CS + n] = run;
-            }
-            part[grp * N + n] = run;
+            for (int k = 0; k < PER; ++k) v[k] = cum[(grp * PER + k) * CS + n];
+#pragma unroll
+            for (int k = 1; k < PER; ++k) v[k] += v[k - 1];
+            part[grp * N + n] = v[PER - 1];
             __syncthreads();
-            float off = 0.f;
-            for (int q = 0; q < grp; ++q) off += part[q * N + n];
+            float pv[NGR - 1];
 #pragma unroll
-            for (int t = grp * PER; t < grp * PER + PER; ++t) cum[t * CS + n] += off;
+            for (int q = 0; q < NGR - 1; ++q) pv[q] = part[q * N + n];
+            float off = 0.f;
+#pragma unroll
+            for (int q = 0; q < NGR - 1; ++q) off += q < grp ? pv[q] : 0.f;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) cum[(grp * PER + k) * CS + n] = v[k] + off;
         }
         __syncthreads();
 
@@ -792,28 +817,52 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] = causal[i] ? acc[i] : 0.f;
                 }
-                // exact part: groups of 4 dimensions holding a fast one, alternately to the two waves
+                // exact part: groups of 4 dimensions holding a fast one, alternately to the two waves,
+                // two groups at a time with every LDS read of both issued before the arithmetic (the
+                // second of a last odd group is group 0 with no dimension selected: it adds zeros)
                 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                for (int g4 = nh; g4 < N / 4; g4 += 2) {
-                    const uint32_t gbits = (uint32_t)(fast >> (4 * g4)) & 0xfu;
-                    if (gbits == 0) continue;
-                    const int n = 4 * g4;
-                    const f32x4 ct = *reinterpret_cast<const f32x4*>(cum + t * CS + n);
-                    const bf16x4 cr = *reinterpret_cast<const bf16x4*>(Craw + t * NP + n);
-                    float cm[4];  // C on the group's fast dimensions only
+                uint32_t gmask = 0;  // this wave's groups holding a fast dimension (bit g4)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) cm[j] = ((gbits >> j) & 1) ? (float)cr[j] : 0.f;
+                for (int g4 = nh; g4 < N / 4; g4 += 2)
+                    gmask |= (((uint32_t)(fast >> (4 * g4)) & 0xfu) != 0u ? 1u : 0u) << g4;
+                while (gmask) {
+                    int gsel[2];
+                    uint32_t gbits[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int s = a + 4 * lg + i;
-                        const f32x4 cs = *reinterpret_cast<const f32x4*>(cum + s * CS + n);
-                        const bf16x4 br = *reinterpret_cast<const bf16x4*>(Braw + s * NP + n);
-                        // (the exponent is clamped at 0 so that the entries above the diagonal,
-                        // dropped below, stay finite; on and below it, it is <= 0 already)
-                        float sum = 0.f;
+                    for (int u = 0; u < 2; ++u) {
+                        gsel[u] = gmask ? __builtin_ctz(gmask) : 0;
+                        gbits[u] = gmask ? (uint32_t)(fast >> (4 * gsel[u])) & 0xfu : 0u;
+                        gmask &= gmask - 1u;
+                    }
+                    f32x4 ct[2], cs[2][4];
+                    bf16x4 cr[2], br[2][4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) sum = fmaf(cm[j] * (float)br[j], dexp2(fminf(ct[j] - cs[j], 0.f)), sum);
-                        acc[i] += causal[i] ? sum : 0.f;
+                    for (int u = 0; u < 2; ++u) {
+                        const int n = 4 * gsel[u];
+                        ct[u] = *reinterpret_cast<const f32x4*>(cum + t * CS + n);
+                        cr[u] = *reinterpret_cast<const bf16x4*>(Craw + t * NP + n);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int s = a + 4 * lg + i;
+                            cs[u][i] = *reinterpret_cast<const f32x4*>(cum + s * CS + n);
+                            br[u][i] = *reinterpret_cast<const bf16x4*>(Braw + s * NP + n);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        float cm[4];  // C on the group's fast dimensions only
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) cm[j] = ((gbits[u] >> j) & 1) ? (float)cr[u][j] : 0.f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            // (the exponent is clamped at 0 so that the entries above the diagonal,
+                            // dropped below, stay finite; on and below it, it is <= 0 already)
+                            float sum = 0.f;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                sum = fmaf(cm[j] * (float)br[u][i][j], dexp2(fminf(ct[u][j] - cs[u][i][j], 0.f)), sum);
+                            acc[i] += causal[i] ? sum : 0.f;
+                        }
                     }
                 }
                 dst = Sl + (nh == 0 ? tile_index(tb, tb) : NTILES + tb) * 256;
@@ -850,17 +899,16 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 const bf16x8 bop = {(__bf16)m0[0], (__bf16)m0[1], (__bf16)m0[2], (__bf16)m0[3],
                                     (__bf16)m1[0], (__bf16)m1[1], (__bf16)m1[2], (__bf16)m1[3]};
 #pragma unroll
-                for (int q = 0; q < PH; ++q) {
-                    const __bf16* xr = Xt + (16 * (pb0 + q) + l16) * QP + 32 * k + 4 * lg;
-                    const uint2 lo = ld8(xr), hi = ld8(xr + 16);
-                    const uint4 a = {lo.x, lo.y, hi.x, hi.y};
-                    acc[q] = mfma_bf16(as_bf16x8(a), bop, acc[q]);
-                }
+                for (int q = 0; q < PH; ++q)
+                    acc[q] = mfma_bf16(x_frag<true>(Xr, XS, 16 * (pb0 + q), k, lane), bop, acc[q]);
             }
 #pragma unroll
-            for (int q = 0; q < PH; ++q)
+            for (int q = 0; q < PH; ++q) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(Xr + tl * XS + 16 * (pb0 + q) + 4 * lg);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[q][i] += dskip * (float)Xt[(16 * (pb0 + q) + 4 * lg + i) * QP + tl];
+                for (int i = 0; i < 4; ++i) acc[q][i] += dskip * (float)x4[i];
+            }
             if (tl < len) {
                 __bf16* yr = yg + ((sq.row0 + t0 + tl) * H + h) * P + 4 * lg;
 #pragma unroll
@@ -879,10 +927,9 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 #pragma unroll
                 for (int i = 0; i < 4; ++i) a[i] *= el[16 * nb + 4 * lg + i];
                 const __bf16* br = Bt + (16 * nb + l16) * QP + 8 * lg;
-                const __bf16* xr = Xt + (16 * pb + l16) * QP + 8 * lg;
 #pragma unroll
                 for (int kb = 0; kb < Q / 32; ++kb)
-                    a = mfma_bf16(as_bf16x8(ld16(br + 32 * kb)), as_bf16x8(ld16(xr + 32 * kb)), a);
+                    a = mfma_bf16(as_bf16x8(ld16(br + 32 * kb)), x_frag<false>(Xr, XS, 16 * pb, kb, lane), a);
                 hs[j] = a;
             }
         }

@@ -103,7 +103,7 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
     extern __shared__ __align__(16) unsigned char smem[];
     __bf16* Bs = reinterpret_cast<__bf16*>(smem);   // [Q][NS]
     __bf16* Cs = Bs + Q * NS;                       // [Q][NS]
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, lg = lane / 16;
     // With prm.split, two workgroups per block on the same XCD (workgroup i runs on XCD i % 8),
     // which shortens the chain each one waits through: part 0 writes the score pairs, part 1 the

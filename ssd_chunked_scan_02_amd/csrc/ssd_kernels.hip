@@ -68,7 +68,7 @@ template <typename T, int N>
 __global__ void __launch_bounds__(kThreads) scores_kernel(ScoresParams prm) {
     using TR = Traits<T>;
     constexpr int KB = TR::kKBlock;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int l16 = lane % 16, lg = lane / 16;
     const int64_t blk = blockIdx.x;
     const int c = (int)(blk % prm.nchunks);
@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
     const int64_t g = h / (H / G);
     const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, lg = lane / 16;
     const int koff = (KB / 4) * lg;  // this lane group's first K index inside a K block
     const int Q = prm.chunk;
@@ -440,7 +440,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(StepParams prm) {
         for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off, kWave);
     // ... then between the waves
     __shared__ f32x4 red[kWaves][kWave];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     if (lane < QP) red[wave][lane] = acc;
     __syncthreads();
     if (threadIdx.x < QP) {
