@@ -457,7 +457,17 @@ __device__ __forceinline__ bf16x8 x_frag(const __bf16* tile, int stride, int col
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// (FULL = false, the state-only pass, keeps only x, (w o B)^T, B, the running sums and the
+// A 16x16x16 MFMA operand contracting over the 16 rows row0 .. row0 + 15 of a row-major bf16 tile in
+// LDS: lane (g, i) receives tile[row0 + 4g + j][col0 + i], j = 0..3 (one transposing read).
+__device__ __forceinline__ short __attribute__((ext_vector_type(4))) tr16(const __bf16* tile, int stride, int row0,
+                                                                         int col0, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int g = lane / 16, r = (lane % 16) / 4, q = lane % 4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + (row0 + 4 * g + r) * stride + col0 + 4 * q));
+}
+
+// (FULL = false, the state-only pass, keeps only x, B o u, B, the running sums and the
 // state-row decays: the other buffers have size 0, so three such workgroups fit on a CU)
 template <int N, int P, bool FULL = true>
 struct DiagPipeLayout {
@@ -469,19 +479,18 @@ struct DiagPipeLayout {
     static constexpr size_t F = FULL ? 1 : 0;
     // offsets in bytes
     static constexpr size_t xt = 0;                                   // x            [Q][XS] bf16
-    static constexpr size_t bt = xt + (size_t)Q * XS * 2;            // (w o B)^T    [N][QP] bf16
-    static constexpr size_t ht = bt + (size_t)N * QP * 2;            // H^T          [P][NP] bf16
+    static constexpr size_t ht = xt + (size_t)Q * XS * 2;            // H^T          [P][NP] bf16
     static constexpr size_t cc = ht + F * P * NP * 2;                // C o exp(cum) [Q][NP] bf16
     static constexpr size_t cf = cc + F * Q * NP * 2;                // C o f        [Q][NP] bf16
     static constexpr size_t bu = cf + F * Q * NP * 2;                // B o u        [Q][NP] bf16
-    static constexpr size_t braw = bu + F * Q * NP * 2;              // B            [Q][NP] bf16
+    static constexpr size_t braw = bu + (size_t)Q * NP * 2;          // B            [Q][NP] bf16
     static constexpr size_t craw = braw + (size_t)Q * NP * 2;        // C            [Q][NP] bf16
     static constexpr size_t cum = craw + F * Q * NP * 2;             // running sums [Q][CS] f32
     static constexpr size_t part = cum + (size_t)Q * CS * 4;         // scan partials [threads/N][N]
     static constexpr size_t beta = part + (size_t)kDiagThreads * 4;  // [NOFF][N]
-    static constexpr size_t el = beta + F * (NOFF + 1) * N * 4;      // [N]
+    static constexpr size_t el = beta + F * (NOFF + 1) * N * 4;      // [NT][N] decay over each block
     // score tiles [NT(NT+1)/2][256], then the second state-dimension half of each diagonal tile
-    static constexpr size_t sl = el + (size_t)N * 4;
+    static constexpr size_t sl = el + (size_t)NT * N * 4;
     static constexpr size_t total = sl + F * (NT * (NT + 1) / 2 + NT) * 256 * 4;
 };
 
@@ -527,7 +536,6 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 
     extern __shared__ __align__(16) unsigned char smem[];
     __bf16* Xr = reinterpret_cast<__bf16*>(smem + L::xt);
-    __bf16* Bt = reinterpret_cast<__bf16*>(smem + L::bt);
     __bf16* Ht = reinterpret_cast<__bf16*>(smem + L::ht);
     __bf16* Cc = reinterpret_cast<__bf16*>(smem + L::cc);
     __bf16* Cf = reinterpret_cast<__bf16*>(smem + L::cf);
@@ -693,9 +701,11 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         __syncthreads();
 
         // ---- 2. factor tables and scaled operands (all from LDS)
-        if (tid < N) {
-            el[tid] = dexp2(cum[(Q - 1) * CS + tid]);
-            lsum += cum[(Q - 1) * CS + tid];
+        if (tid < N) lsum += cum[(Q - 1) * CS + tid];
+        // decay over each 16-token block per state dimension: E_b = exp(cum_end(b) - cum_end(b-1))
+        for (int i = tid; i < NT * N; i += kThreads) {
+            const int bk = i / N, n = i % N;
+            el[i] = dexp2(cum[(16 * bk + 15) * CS + n] - (bk > 0 ? cum[(16 * bk - 1) * CS + n] : 0.f));
         }
         for (int i = tid; FULL && i < L::NOFF * N; i += kThreads) {
             const int p = i / N, n = i % N;
@@ -707,6 +717,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         for (int item = tid; FULL && item < Q * (N / 8); item += kThreads) {
             const int t = item / (N / 8), c8 = item % (N / 8);
             const int a = t & ~15, e = t | 15;
+            // (C o exp(cum), C o f for the output side; B o u, which also feeds the state update)
             const f32x4 ct0 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8);
             const f32x4 ct1 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8 + 4);
             const f32x4 ca0 = *reinterpret_cast<const f32x4*>(cum + a * CS + 8 * c8);
@@ -729,15 +740,19 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             *reinterpret_cast<bf16x8*>(Cf + t * NP + 8 * c8) = vcf;
             *reinterpret_cast<bf16x8*>(Bu + t * NP + 8 * c8) = vbu;
         }
-        // (w o B)^T: four tokens of one state column per item
-        for (int item = tid; item < (Q / 4) * N; item += kThreads) {
-            const int n = item % N, t4 = 4 * (item / N);
-            const float cl = cum[(Q - 1) * CS + n];
-            float v[4];
+        // (the state-only pass needs B o u alone)
+        for (int item = tid; !FULL && item < Q * (N / 8); item += kThreads) {
+            const int t = item / (N / 8), c8 = item % (N / 8), e = t | 15;
+            const f32x4 ct0 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8);
+            const f32x4 ct1 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8 + 4);
+            const f32x4 ce0 = *reinterpret_cast<const f32x4*>(cum + e * CS + 8 * c8);
+            const f32x4 ce1 = *reinterpret_cast<const f32x4*>(cum + e * CS + 8 * c8 + 4);
+            const bf16x8 bv = as_bf16x8(ld16(Braw + t * NP + 8 * c8));
+            bf16x8 vbu;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                v[k] = (float)Braw[(t4 + k) * NP + n] * dexp2(cl - cum[(t4 + k) * CS + n]);
-            lds_store4(Bt + n * QP + t4, v[0], v[1], v[2], v[3]);
+            for (int j = 0; j < 8; ++j)
+                vbu[j] = (__bf16)((float)bv[j] * dexp2((j < 4 ? ce0[j] : ce1[j - 4]) - (j < 4 ? ct0[j] : ct1[j - 4])));
+            *reinterpret_cast<bf16x8*>(Bu + t * NP + 8 * c8) = vbu;
         }
         __syncthreads();
 
@@ -917,7 +932,9 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             }
         }
 
-        // ---- 5. state: H_k[n,:] = exp(cum_last,n) H_{k-1}[n,:] + (w o B)^T X
+        // ---- 5. state: H_k[n,:] = exp(cum_last,n) H_{k-1}[n,:] + sum_s B_sn exp(cum_last,n - cum_sn) x_s,
+        //         block by block (Horner): H <- E_b o H + (B o u)_b^T X_b, the decay from each token
+        //         to its block's end inside B o u and from block to block in E_b (every factor <= 1)
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int tile = wave + kWaves * j;
@@ -925,11 +942,12 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 const int nb = tile / PB, pb = tile % PB;
                 f32x4 a = hs[j];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] *= el[16 * nb + 4 * lg + i];
-                const __bf16* br = Bt + (16 * nb + l16) * QP + 8 * lg;
-#pragma unroll
-                for (int kb = 0; kb < Q / 32; ++kb)
-                    a = mfma_bf16(as_bf16x8(ld16(br + 32 * kb)), x_frag<false>(Xr, XS, 16 * pb, kb, lane), a);
+                for (int bk = 0; bk < NT; ++bk) {
+                    const f32x4 eb = *reinterpret_cast<const f32x4*>(el + bk * N + 16 * nb + 4 * lg);
+                    a *= eb;
+                    a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr16(Bu, NP, 16 * bk, 16 * nb, lane),
+                                                                 tr16(Xr, XS, 16 * bk, 16 * pb, lane), a, 0, 0, 0);
+                }
                 hs[j] = a;
             }
         }
