@@ -95,6 +95,7 @@ KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.h
                   "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
                   "skip_kernel": "ssd_kernels.hip", "bwd_states_kernel": "ssd_bwd.hip",
                   "bwd_walk_kernel": "ssd_bwd.hip", "zero_kernel": "ssd_bwd.hip", "bwd_reduce_kernel": "ssd_bwd.hip",
+                  "bwd_states_bf16_kernel": "ssd_bwd.hip", "bwd_walk_bf16_kernel": "ssd_bwd.hip",
                   "bwd_local_diag_kernel": "ssd_bwd.hip", "bwd_scan_diag_kernel": "ssd_bwd.hip",
                   "bwd_terms_diag_kernel": "ssd_bwd.hip"}
 
@@ -264,6 +265,29 @@ def output_parity(cfg, inp, y, final, ref):
     if final is not None and fr is not None:
         out["rel_l2_final"] = rel(final.double().cpu().numpy(), fr)
         ok = ok and out["rel_l2_final"] <= tol
+    out["pass"] = bool(ok)
+    return out
+
+
+def backward_parity(cfg, got, want):
+    """The timed run's gradients of batch element 0 against the fp64 adjoint's on the same stored
+    inputs (the cpu_baseline leg's result): relative L2 of dx, dlog a, dB, dC and dinit, with the
+    bounds of the parity tests (1e-5 for fp32 inputs, 2e-2 for bf16).  (dD sums over the batch, so
+    it is left to the tests.)"""
+    import numpy as np
+    tol = 1e-5 if cfg["dtype"] == "fp32" else 2e-2
+    out, ok = {}, True
+    for k in ("dx", "dlog_a", "dB", "dC", "dinit"):
+        if got.get(k) is None or want.get(k) is None:
+            continue
+        a = got[k][:1].double().cpu().numpy()
+        b = np.asarray(want[k])
+        n = float(np.linalg.norm(b.ravel()))
+        e = float(np.linalg.norm((a - b).ravel())) / n if n > 0 else float(np.linalg.norm(a.ravel()))
+        out["rel_l2_" + k] = e
+        ok = ok and e <= tol and bool(np.isfinite(a).all())
+    out["tol"] = tol
+    out["reference"] = "fp64 adjoint on batch element 0 of the same stored inputs; gradients of the timed run"
     out["pass"] = bool(ok)
     return out
 
@@ -462,8 +486,7 @@ def run_backward(args, cfg, inp, dev):
         kw = dict(D=g.get("D"), init_state=g.get("init_state"), dfinal=g["dfinal"], want_dD=cfg["skip"],
                   want_dinit=cfg["init"], workspace=ws, stream=stream)
         if events is None:
-            ssd.ssd_backward(g["x"], g["log_a"], g["B"], g["C"], g["dy"], **kw)
-            return None
+            return ssd.ssd_backward(g["x"], g["log_a"], g["B"], g["C"], g["dy"], **kw)
         return ssd.ssd_backward_profiled(g["x"], g["log_a"], g["B"], g["C"], g["dy"], events=events, **kw)[1]
 
     for i in range(args.warmup):
@@ -471,9 +494,12 @@ def run_backward(args, cfg, inp, dev):
     torch.cuda.synchronize()
     K = args.steps
     begin, end = ev.create(), ev.create()
+    kept = None  # the gradients of the last timed call on the first input copy
     ev.lib.hipEventRecord(begin, stream.cuda_stream)
     for i in range(K):
-        step(i)
+        r = step(i)
+        if i % copies == 0:
+            kept = r
     ev.lib.hipEventRecord(end, stream.cuda_stream)
     torch.cuda.synchronize()
     ms = ev.elapsed_ms(begin, end) / K
@@ -489,9 +515,14 @@ def run_backward(args, cfg, inp, dev):
     kernel_avg = [sum(v) / len(v) for v in per_kernel]
     N, P = cfg["dstate"], cfg["headdim"]
     sfx = "_diag" if cfg["decay"] == "diag" else ""
+    # scalar decay, bf16 inputs, N in {32, 64, 128}, P in {32, 64}: the bf16-MFMA kernels
+    bf16_path = not sfx and cfg["dtype"] == "bf16" and N in (32, 64, 128) and P in (32, 64)
+    peak = BF16_PEAK_TFLOPS if bf16_path else FP32_PEAK_TFLOPS
     if sfx:
         names = ["bwd_local_diag_kernel<%d,%d>" % (N, P), "bwd_scan_diag_kernel<%d,%d>" % (N, P),
                  "bwd_terms_diag_kernel<%d,%d>" % (N, P)]
+    elif bf16_path:
+        names = ["zero_kernel", "bwd_states_bf16_kernel<%d,%d>" % (N, P), "bwd_walk_bf16_kernel<%d,%d>" % (N, P)]
     else:
         names = ["zero_kernel", "bwd_states_kernel<%d,%d>" % (N, P), "bwd_walk_kernel<%d,%d>" % (N, P)]
     names += ["bwd_reduce_kernel"] if cfg["skip"] else []
@@ -509,15 +540,15 @@ def run_backward(args, cfg, inp, dev):
                   % (cfg["batch"], cfg["seqlen"], cfg["nheads"], P, N),
         "value": tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if bf16_path else "f32",
         "data": "synthetic (seeded; the forward workload's inputs, dL/dy ~ N(0,1) in the input dtype)",
         "config": {"workload": args.workload, "pass": "backward", "batch": cfg["batch"], "seqlen": cfg["seqlen"],
                    "nheads": cfg["nheads"], "ngroups": cfg["ngroups"], "headdim": P, "dstate": N,
                    "input_dtype": cfg["dtype"], "backward_chunk": BWD_CHUNK, "parallelism": "single GPU"},
         "tflops": (f_walk + f_states) / (ms / 1e3) / 1e12,
         "kernels_ms": {n: t for n, t in zip(names, kernel_avg)},
-        "roofline": {"kernel": names[walk], "bound": "mfma", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS,
+        "roofline": {"kernel": names[walk], "bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": measured_traffic(args.workload + "_bwd", names[walk]),
                      "algorithmic_flops_per_launch": f_dom, "hbm_gbs_whole_step": nbytes / (ms / 1e3) / 1e9},
     }
@@ -528,9 +559,9 @@ def run_backward(args, cfg, inp, dev):
         threads = oracle.default_threads() if hasattr(oracle, "default_threads") else 1
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.backward.backward(one(inp["x"]), one(inp["log_a"]), one(inp["B"]), one(inp["C"]), f(inp.get("D")),
-                                     one(inp.get("init_state")), one(og["dy"]),
-                                     one(og["dfinal"]) if cfg["final"] else None, nthreads=threads)
+            want = oracle.backward.backward(one(inp["x"]), one(inp["log_a"]), one(inp["B"]), one(inp["C"]),
+                                            f(inp.get("D")), one(inp.get("init_state")), one(og["dy"]),
+                                            one(og["dfinal"]) if cfg["final"] else None, nthreads=threads)
             reps += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:
@@ -542,7 +573,10 @@ def run_backward(args, cfg, inp, dev):
                                   "sample": "batch element 0 of the workload (%d tokens x %d heads), %d run(s) in "
                                             "%.1f s, fp64 adjoint of the recurrence, OpenMP over (batch, group)"
                                             % (cfg["seqlen"], cfg["nheads"], reps, el)}
+        result["parity"] = backward_parity(cfg, kept, want)
     print(json.dumps(result), flush=True)
+    if "parity" in result and not result["parity"]["pass"]:
+        sys.exit(1)
 
 
 def run_varlen(args, cfg, dev):

@@ -110,6 +110,14 @@ struct ChunkRows {
         }
     }
     __device__ float elem(int i, int j) const { return piece_elem<T>(v[i], j); }
+    // as they are, into a tile of the input type with row stride ld (16-byte aligned rows)
+    __device__ void stage_raw(T* dst, int ld, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int u = tid + NT * i, r = u / PER_ROW, c = (u % PER_ROW) * VE;
+            if (u < PIECES) st16(dst + r * ld + c, v[i]);
+        }
+    }
 };
 
 // Running sum of log a over one chunk from la_v (token tid's log a in lanes tid < Q of wave 0, 0
@@ -467,6 +475,495 @@ __global__ void __launch_bounds__(kBThreads) bwd_walk_kernel(BwdParams prm) {
                 const int nb = tile / PB, pb = tile % PB;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) prm.dinit[(unit * N + 16 * nb + 4 * lg + i) * P + 16 * pb + l16] = gs[j][i];
+            }
+        }
+    }
+    // dy . x over the unit, for dD
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dD_acc += __shfl_xor(dD_acc, off, kWave);
+    if (lane == 0) red[wave] = dD_acc;
+    lds_barrier();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int k = 0; k < kBWaves; ++k) s += red[k];
+        prm.dD_part[unit] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 inputs (N in {32, 64, 128}, P in {32, 64}): the same two passes with every tile product a
+// bf16 MFMA (16x16x32) on bf16 LDS tiles.  Operands that contract along a tile's rows come from the
+// transposing LDS read, the others from one 16-byte read per lane.  The products whose results go to
+// memory (the state, dx, dB, dC, G) are formed transposed, so that each accumulator lane holds four
+// consecutive elements of a row in memory.  The checkpoints are stored in bf16: H only enters bf16
+// products and <G, H>.  The state and its gradient stay fp32 in the accumulators, and the row and
+// column sums of M that dlog a needs come from fp32 copies of the S o L and DYX tiles.  Rounded to
+// bf16 for the products: S o L, L o DYX, H, G, w o B and e o C (x, dy, B and C are bf16 already).
+// The forward pass rounds S o L and H the same way.
+template <int N, int P>
+struct BwdBf16Shape {
+    static constexpr int Q = kBQ, NB = N / 16, PB = P / 16, QB = Q / 16, QF = Q + 1;
+    static constexpr int XS = P + 16, NSB = N + 8, QSB = Q + 16;  // bf16 row strides (elements)
+    static constexpr int NTILE = NB * PB, TPW = (NTILE + kBWaves - 1) / kBWaves;
+    // checkpoint pass: w o B [Q][NSB], x [Q][XS]
+    static constexpr size_t states_lds = ((size_t)Q * NSB + (size_t)Q * XS) * 2;
+    // walk: x, dy [Q][XS]; B, C [Q][NSB]; S o L, L o DYX [Q][QSB]; H, G [N][XS] (bf16); then S o L,
+    // DYX [Q][QF], e, w, row and column sums of M [Q], the partial row sums of B . (G x) and
+    // C . (H dy) [Q][NB] each, and the reduction [kBWaves] (fp32)
+    static constexpr size_t bf_elems = (size_t)2 * Q * XS + 2 * Q * NSB + 2 * Q * QSB + 2 * N * XS;
+    static constexpr size_t f_floats = (size_t)2 * Q * QF + 4 * Q + 2 * Q * NB + kBWaves;
+    static constexpr size_t walk_lds = bf_elems * 2 + f_floats * 4;
+    static_assert(bf_elems % 8 == 0, "fp32 part 16-byte aligned");
+};
+
+template <int N, int P>
+constexpr bool bwd_bf16_shape() {
+    return (N == 32 || N == 64 || N == 128) && (P == 32 || P == 64);
+}
+
+// Lane-to-lane moves inside 16-lane rows with DPP (no LDS round trip): the source lane's value
+// under pattern CTRL for the rows in ROWS, 0 where the pattern has no source lane.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float bdpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+// Sum over the 16 lanes of a row, in every lane: swap neighbours, swap pairs, mirror each half,
+// mirror the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += bdpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += bdpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += bdpp<0x141>(v);  // row_half_mirror
+    v += bdpp<0x140>(v);  // row_mirror
+    return v;
+}
+// Sum over the wave (the same value in every lane): row sums, then the four rows' from lanes 0, 16,
+// 32 and 48.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = row16_sum(v);
+    auto at = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+    return (at(0) + at(16)) + (at(32) + at(48));
+}
+// chunk_factors for fp32 running sums, with the scan over the chunk's 32 tokens in DPP steps (row
+// shifts, then row 0's total into row 1) and the hardware exponential.
+__device__ __forceinline__ void chunk_factors_dpp(float la_v, float* cum, float* e, float* w, int tid) {
+    static_assert(kBQ == 32, "two 16-lane rows");
+    if (tid < kWave) {
+        float v = tid < kBQ ? la_v : 0.f;
+        v += bdpp<0x111>(v);       // row_shr:1
+        v += bdpp<0x112>(v);       // row_shr:2
+        v += bdpp<0x114>(v);       // row_shr:4
+        v += bdpp<0x118>(v);       // row_shr:8
+        v += bdpp<0x142, 0xa>(v);  // row_bcast:15 into row 1
+        const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kBQ - 1));
+        if (tid < kBQ) {
+            cum[tid] = v;
+            e[tid] = __expf(v);
+            w[tid] = __expf(last - v);
+        }
+    }
+}
+
+// An MFMA operand contracting over rows k0 .. k0 + 31 of a row-major bf16 LDS tile [k][col]: lane
+// (g, i) receives tile[k0 + 8 g + j][col0 + i], j = 0..7 (two transposing reads, ds_read_b64_tr_b16:
+// a 16-lane group whose lane 4 r + q points at row r, columns 4 q .. 4 q + 3 returns column i of
+// those four rows in its lane i).
+__device__ __forceinline__ bf16x8 kfrag(const __bf16* tile, int stride, int k0, int col0, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int g = lane / 16, r = (lane % 16) / 4, q = lane % 4;
+    const __bf16* p = tile + (k0 + 8 * g + r) * stride + col0 + 4 * q;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * stride));
+    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+// An MFMA operand contracting over columns k0 .. k0 + 31 of a row-major bf16 LDS tile [row][k]:
+// lane (g, i) receives tile[row0 + i][k0 + 8 g + j], j = 0..7 (one 16-byte read).
+__device__ __forceinline__ bf16x8 rfrag(const __bf16* tile, int stride, int row0, int k0, int lane) {
+    return as_bf16x8(ld16(tile + (row0 + lane % 16) * stride + k0 + 8 * (lane / 16)));
+}
+
+template <int N, int P>
+__global__ void __launch_bounds__(kBThreads) bwd_states_bf16_kernel(BwdParams prm) {
+    using S = BwdBf16Shape<N, P>;
+    constexpr int Q = S::Q, PB = S::PB, XS = S::XS, NSB = S::NSB, NTILE = S::NTILE, TPW = S::TPW;
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+    const int nch = prm.seq_off ? (int)((sq.len + kBQ - 1) / kBQ) : prm.nchunks;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __bf16* Bw = reinterpret_cast<__bf16*>(smem);  // w o B [Q][NSB]
+    __bf16* Xs = Bw + Q * NSB;                     // x [Q][XS]
+    __shared__ float cum[kBQ];
+    __shared__ float e_unused[kBQ], w_s[kBQ];
+    const __bf16* xg = static_cast<const __bf16*>(prm.x);
+    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm);
+    __bf16* ckpt = reinterpret_cast<__bf16*>(prm.ckpt);  // [B,H,nchunks,N,P] bf16
+
+    // H^T in accumulators: tile (pb, nb) holds rows p = 16 pb + 4 lg + i, column n = 16 nb + l16
+    f32x4 hs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kBWaves * j;
+        if (tile < NTILE && prm.init) {
+            const int pb = tile % PB, nb = tile / PB;
+            hs[j] = *reinterpret_cast<const f32x4*>(prm.init + (unit * N + 16 * nb + l16) * P + 16 * pb + 4 * lg);
+        }
+    }
+    ChunkRows<__bf16, Q, N> rb;
+    ChunkRows<__bf16, Q, P> rx;
+    float rla = 0.f;
+    auto load = [&](int c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, sq.len - t0);
+        rb.load(Bg + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
+        rx.load(xg + ((sq.row0 + t0) * H + h) * P, H * P, len, tid);
+        rla = tid < len && tid < Q ? prm.log_a[(sq.row0 + t0 + tid) * H + h] : 0.f;
+    };
+    if (nch > 0) load(0);
+    for (int c = 0; c < nch; ++c) {
+        // the checkpoint: the state entering chunk c, four consecutive p per lane
+        __bf16* ck = ckpt + (unit * prm.nchunks + c) * (int64_t)N * P;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int pb = tile % PB, nb = tile / PB;
+                store4(ck + (16 * nb + l16) * P + 16 * pb + 4 * lg, hs[j][0], hs[j][1], hs[j][2], hs[j][3]);
+            }
+        }
+        chunk_factors_dpp(rla, cum, e_unused, w_s, tid);
+        lds_barrier();
+        rx.stage_raw(Xs, XS, tid);
+        // w o B, rounded once (rows past the end are zeros)
+#pragma unroll
+        for (int i = 0; i < ChunkRows<__bf16, Q, N>::PT; ++i) {
+            constexpr int PER_ROW = ChunkRows<__bf16, Q, N>::PER_ROW, PIECES = ChunkRows<__bf16, Q, N>::PIECES;
+            const int u = tid + kBThreads * i, r = u / PER_ROW, cc = (u % PER_ROW) * 8;
+            if (u < PIECES) {
+                const float wr = w_s[r];
+                const bf16x8 bv = as_bf16x8(rb.v[i]);
+                bf16x8 o;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) o[k] = (__bf16)((float)bv[k] * wr);
+                *reinterpret_cast<bf16x8*>(Bw + r * NSB + cc) = o;
+            }
+        }
+        const float el = __expf(cum[Q - 1]);
+        lds_barrier();
+        if (c + 1 < nch) load(c + 1);
+        // H^T <- e_last H^T + X^T (w o B): A(p, t) = x[t][p], B(t, n) = (w o B)[t][n]
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int pb = tile % PB, nb = tile / PB;
+                hs[j] = mfma_bf16(kfrag(Xs, XS, 0, 16 * pb, lane), kfrag(Bw, NSB, 0, 16 * nb, lane), hs[j] * el);
+            }
+        }
+        lds_barrier();
+    }
+}
+
+template <int N, int P>
+__global__ void __launch_bounds__(kBThreads) bwd_walk_bf16_kernel(BwdParams prm) {
+    using S = BwdBf16Shape<N, P>;
+    constexpr int Q = S::Q, QF = S::QF, NB = S::NB, PB = S::PB, QB = S::QB;
+    constexpr int XS = S::XS, NSB = S::NSB, QSB = S::QSB, NTILE = S::NTILE, TPW = S::TPW;
+    static_assert(2 * QB * QB <= kBWaves, "one S o L or DYX tile per wave");
+    static_assert(Q * 16 == kBThreads, "row and column sums: 16 threads per row");
+    const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen, units = prm.batch * H;
+    const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, units);
+    if (unit < 0) return;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const SeqSpan sq = seq_span(prm.seq_off, b, Tn, prm.total);
+    const int nch = prm.seq_off ? (int)((sq.len + kBQ - 1) / kBQ) : prm.nchunks;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, lg = lane / 16, l16 = lane % 16;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    __bf16* Xb = reinterpret_cast<__bf16*>(smem);  // x [Q][XS]
+    __bf16* Yb = Xb + Q * XS;                      // dy [Q][XS]
+    __bf16* Bb = Yb + Q * XS;                      // B [Q][NSB]
+    __bf16* Cb = Bb + Q * NSB;                     // C [Q][NSB]
+    __bf16* Ab = Cb + Q * NSB;                     // S o L [Q][QSB] (rows t, columns s)
+    __bf16* Wb = Ab + Q * QSB;                     // L o DYX [Q][QSB]
+    __bf16* Hb = Wb + Q * QSB;                     // H [N][XS]
+    __bf16* Gb = Hb + N * XS;                      // G [N][XS]
+    float* Af = reinterpret_cast<float*>(Gb + N * XS);  // S o L [Q][QF]
+    float* Df = Af + Q * QF;                            // DYX [Q][QF]
+    float* ev = Df + Q * QF;
+    float* wv = ev + Q;
+    float* rowM = wv + Q;           // sum_s M_ts
+    float* colM = rowM + Q;         // sum_t M_ts
+    float* partB = colM + Q;        // [Q][NB]: B_s . (G x_s) over 16-row pieces of n
+    float* partC = partB + Q * NB;  // [Q][NB]: C_t . (H dy_t)
+    float* red = partC + Q * NB;    // [kBWaves]
+    __shared__ float cum[kBQ];
+
+    const __bf16* xg = static_cast<const __bf16*>(prm.x);
+    const __bf16* yg = static_cast<const __bf16*>(prm.dy);
+    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm);
+    const __bf16* Cg = static_cast<const __bf16*>(prm.Cm);
+    const __bf16* ckpt = reinterpret_cast<const __bf16*>(prm.ckpt);
+    __bf16* dxg = static_cast<__bf16*>(prm.dx);
+    const float dskip = prm.D ? prm.D[h] : 0.f;
+
+    // G^T, the gradient of the state leaving the current chunk, in accumulators: tile (pb, nb)
+    // holds rows p = 16 pb + 4 lg + i, column n = 16 nb + l16; its bf16 copy in Gb
+    f32x4 gs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        gs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wave + kBWaves * j;
+        if (tile < NTILE && prm.dfinal) {
+            const int pb = tile % PB, nb = tile / PB;
+            gs[j] = *reinterpret_cast<const f32x4*>(prm.dfinal + (unit * N + 16 * nb + l16) * P + 16 * pb + 4 * lg);
+        }
+    }
+    auto write_g = [&]() {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int pb = tile % PB, nb = tile / PB;
+                store4(Gb + (16 * nb + l16) * XS + 16 * pb + 4 * lg, gs[j][0], gs[j][1], gs[j][2], gs[j][3]);
+            }
+        }
+    };
+    write_g();
+    float dD_acc = 0.f;
+
+    // the next chunk's inputs, a chunk ahead (chunks run last to first)
+    ChunkRows<__bf16, Q, P> rx, ry;
+    ChunkRows<__bf16, Q, N> rb, rc;
+    ChunkRows<__bf16, N, P> rh;
+    float rla = 0.f;
+    auto load = [&](int c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, sq.len - t0);
+        rx.load(xg + ((sq.row0 + t0) * H + h) * P, H * P, len, tid);
+        ry.load(yg + ((sq.row0 + t0) * H + h) * P, H * P, len, tid);
+        rb.load(Bg + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
+        rc.load(Cg + ((sq.row0 + t0) * G + g) * N, G * N, len, tid);
+        rh.load(ckpt + (unit * prm.nchunks + c) * (int64_t)N * P, P, N, tid);
+        rla = tid < len && tid < Q ? prm.log_a[(sq.row0 + t0 + tid) * H + h] : 0.f;
+    };
+    if (nch > 0) load(nch - 1);
+
+    constexpr int JDX = QB * PB, JDB = QB * NB;  // phase-3 jobs: dx tiles; dB and dC tiles (one job each)
+    for (int c = nch - 1; c >= 0; --c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int len = (int)min((int64_t)Q, sq.len - t0);
+        // ---- 1. the chunk's x, dy, B, C and entering state into LDS (zeros past the end)
+        rx.stage_raw(Xb, XS, tid);
+        ry.stage_raw(Yb, XS, tid);
+        rb.stage_raw(Bb, NSB, tid);
+        rc.stage_raw(Cb, NSB, tid);
+        rh.stage_raw(Hb, XS, tid);
+#pragma unroll
+        for (int i = 0; i < ChunkRows<__bf16, Q, P>::PT; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dD_acc += rx.elem(i, j) * ry.elem(i, j);
+        chunk_factors_dpp(rla, cum, ev, wv, tid);
+        lds_barrier();
+        if (c > 0) load(c - 1);
+
+        // ---- 2. S o L (waves 0 .. 3) and DYX, L o DYX (waves 4 .. 7), one 16 x 16 tile (tb, sb) each:
+        //         rows t, columns s
+        {
+            const int job = wave % (QB * QB), tb = job / QB, sb = job % QB;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (wave < QB * QB) {
+#pragma unroll
+                for (int k = 0; k < N / 32; ++k)
+                    v = mfma_bf16(rfrag(Cb, NSB, 16 * tb, 32 * k, lane), rfrag(Bb, NSB, 16 * sb, 32 * k, lane), v);
+            } else {
+#pragma unroll
+                for (int k = 0; k < P / 32; ++k)
+                    v = mfma_bf16(rfrag(Yb, XS, 16 * tb, 32 * k, lane), rfrag(Xb, XS, 16 * sb, 32 * k, lane), v);
+            }
+            const int s = 16 * sb + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * lg + i;
+                const float L = s <= t ? __expf(cum[t] - cum[s]) : 0.f;
+                if (wave < QB * QB) {
+                    Af[t * QF + s] = v[i] * L;
+                    Ab[t * QSB + s] = (__bf16)(v[i] * L);
+                } else {
+                    Df[t * QF + s] = v[i];
+                    Wb[t * QSB + s] = (__bf16)(v[i] * L);
+                }
+            }
+        }
+        lds_barrier();
+
+        // ---- 3. row and column sums of M = (S o L) o DYX (16 threads per row or column); dx, dB, dC
+        //         and the state terms of dcum, tiles dealt to the waves
+        {
+            const int r = tid / 16, j = tid % 16;
+            float rs = 0.f, cs = 0.f;
+#pragma unroll
+            for (int k = 2 * j; k < 2 * j + 2; ++k) {
+                rs += Af[r * QF + k] * Df[r * QF + k];
+                cs += Af[k * QF + r] * Df[k * QF + r];
+            }
+            rs = row16_sum(rs);
+            cs = row16_sum(cs);
+            if (j == 0) {
+                rowM[r] = rs;
+                colM[r] = cs;
+            }
+        }
+        // This wave's jobs: dx tiles (wave + kBWaves u), then dB and dC tiles of the same rows and
+        // columns together (dB rows s, dC rows t, both columns n), each job's products straight-line
+        // and its epilogue right after them.
+        {
+            constexpr int UX = (JDX + kBWaves - 1) / kBWaves, UB = (JDB + kBWaves - 1) / kBWaves;
+#pragma unroll
+            for (int u = 0; u < UX; ++u) {
+                // dx^T (rows p, columns s) = dY^T (S o L) + w_s G^T B_s + D dy
+                const int job = min(wave + kBWaves * u, JDX - 1), sb = job % QB, pb = job / QB;
+                const f32x4 xa = mfma_bf16(kfrag(Yb, XS, 0, 16 * pb, lane), kfrag(Ab, QSB, 0, 16 * sb, lane),
+                                           f32x4{0.f, 0.f, 0.f, 0.f});
+                f32x4 xg = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < N / 32; ++k)
+                    xg = mfma_bf16(kfrag(Gb, XS, 32 * k, 16 * pb, lane), rfrag(Bb, NSB, 16 * sb, 32 * k, lane), xg);
+                const int s = 16 * sb + l16, p0 = 16 * pb + 4 * lg;
+                if (wave + kBWaves * u < JDX && s < len) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    const bf16x4 dy4 = *reinterpret_cast<const bf16x4*>(Yb + s * XS + p0);
+                    const float ws_ = wv[s];
+                    float o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = xa[i] + ws_ * xg[i] + dskip * (float)dy4[i];
+                    store4(dxg + ((sq.row0 + t0 + s) * H + h) * P + p0, o[0], o[1], o[2], o[3]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                // dB (rows s, columns n) = (L o DYX)^T C + w_s (G x_s) and dC (rows t, columns n) =
+                // (L o DYX) B + e_t (H dy_t): one instruction's atomic adds cover 4 rows x 64
+                // contiguous bytes (the heads of a group add into the same rows)
+                const int job = min(wave + kBWaves * u, JDB - 1), sb = job % QB, nb = job / QB;
+                const f32x4 ba = mfma_bf16(kfrag(Wb, QSB, 0, 16 * sb, lane), kfrag(Cb, NSB, 0, 16 * nb, lane),
+                                           f32x4{0.f, 0.f, 0.f, 0.f});
+                f32x4 bg = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < P / 32; ++k)
+                    bg = mfma_bf16(rfrag(Xb, XS, 16 * sb, 32 * k, lane), rfrag(Gb, XS, 16 * nb, 32 * k, lane), bg);
+                const f32x4 ca = mfma_bf16(rfrag(Wb, QSB, 16 * sb, 0, lane), kfrag(Bb, NSB, 0, 16 * nb, lane),
+                                           f32x4{0.f, 0.f, 0.f, 0.f});
+                f32x4 ch = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < P / 32; ++k)
+                    ch = mfma_bf16(rfrag(Yb, XS, 16 * sb, 32 * k, lane), rfrag(Hb, XS, 16 * nb, 32 * k, lane), ch);
+                if (wave + kBWaves * u < JDB) {
+                    const int n = 16 * nb + l16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int s = 16 * sb + 4 * lg + i;
+                        if (s < len) {
+                            atomicAdd(prm.dB + ((sq.row0 + t0 + s) * G + g) * N + n, ba[i] + wv[s] * bg[i]);
+                            atomicAdd(prm.dC + ((sq.row0 + t0 + s) * G + g) * N + n, ca[i] + ev[s] * ch[i]);
+                        }
+                        // B_s . (G x_s) and C_t . (H dy_t) over this tile's 16 columns of n
+                        const float pb_ = row16_sum((float)Bb[s * NSB + n] * bg[i]);
+                        const float pc_ = row16_sum((float)Cb[s * NSB + n] * ch[i]);
+                        if (l16 == 0) {
+                            partB[s * NB + nb] = pb_;
+                            partC[s * NB + nb] = pc_;
+                        }
+                    }
+                }
+            }
+        }
+        // <G, H> over this wave's tiles
+        float gh = 0.f;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int pb = tile % PB, nb = tile / PB;
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 h4 = *reinterpret_cast<const bf16x4*>(Hb + (16 * nb + l16) * XS + 16 * pb + 4 * lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gh += gs[j][i] * (float)h4[i];
+            }
+        }
+        gh = wave_sum_dpp(gh);
+        if (lane == 0) red[wave] = gh;
+        lds_barrier();
+
+        // ---- 4. dcum and dlog a as its reverse running sum (wave 0); the gradient entering the
+        //         chunk, G^T <- e_last G^T + dY^T (e o C) (every wave)
+        const float el = ev[Q - 1];
+        if (tid < kWave) {
+            float d = 0.f, wpb = 0.f;
+            if (tid < Q) {
+                const int t = tid;
+                float pb_ = 0.f, pc_ = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    pb_ += partB[t * NB + nb];
+                    pc_ += partC[t * NB + nb];
+                }
+                d = rowM[t] - colM[t] + ev[t] * pc_ - wv[t] * pb_;
+                wpb = wv[t] * pb_;
+            }
+            // the last token's term: e_last <G, H> + sum_s w_s B_s . (G x_s)
+            const float wsum = wave_sum_dpp(wpb);
+            if (tid == Q - 1) {
+                float ghs = 0.f;
+#pragma unroll
+                for (int k = 0; k < kBWaves; ++k) ghs += red[k];
+                d += el * ghs + wsum;
+            }
+            // reverse inclusive running sum over t: inside each 16-lane row by DPP left shifts, then
+            // row 1's total into row 0
+            float r = tid < Q ? d : 0.f;
+            r += bdpp<0x101>(r);  // row_shl:1
+            r += bdpp<0x102>(r);  // row_shl:2
+            r += bdpp<0x104>(r);  // row_shl:4
+            r += bdpp<0x108>(r);  // row_shl:8
+            const float row1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), 16));
+            r += tid < 16 ? row1 : 0.f;
+            if (tid < len) prm.dlog_a[(sq.row0 + t0 + tid) * H + h] = r;
+        }
+        {
+            // e_t for the operand's tokens 8 lg + j
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(ev + 8 * lg);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(ev + 8 * lg + 4);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                const int tile = wave + kBWaves * j;
+                if (tile < NTILE) {
+                    const int pb = tile % PB, nb = tile / PB;
+                    const bf16x8 cv = kfrag(Cb, NSB, 0, 16 * nb, lane);
+                    bf16x8 ec;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) ec[k] = (__bf16)((float)cv[k] * (k < 4 ? e0[k] : e1[k - 4]));
+                    gs[j] = mfma_bf16(kfrag(Yb, XS, 0, 16 * pb, lane), ec, gs[j] * el);
+                }
+            }
+        }
+        lds_barrier();  // every read of Gb, Hb and the chunk tiles above is done
+        write_g();
+    }
+    lds_barrier();
+    if (prm.dinit) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kBWaves * j;
+            if (tile < NTILE) {
+                const int pb = tile % PB, nb = tile / PB;
+                *reinterpret_cast<f32x4*>(prm.dinit + (unit * N + 16 * nb + l16) * P + 16 * pb + 4 * lg) = gs[j];
             }
         }
     }
@@ -1035,15 +1532,26 @@ __global__ void __launch_bounds__(kThreads) zero_kernel(float* a, int64_t n, flo
 template <typename T, int N, int P>
 int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
     using S = BwdShape<N, P>;
+    using SB = BwdBf16Shape<N, P>;
+    // bf16 inputs at the shapes the bf16 kernels cover take them
+    constexpr bool kBf16 = std::is_same<T, __bf16>::value && bwd_bf16_shape<N, P>();
     static_assert(S::walk_lds + 1024 <= kMaxLds, "backward walk LDS budget (with its static running sums)");
+    static_assert(SB::walk_lds + 1024 <= kMaxLds, "bf16 backward walk LDS budget");
     static bool attr[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
     if (!attr[dev]) {
         // (the dynamic size the kernel uses, not the whole 160 KiB: its static LDS counts too)
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_walk_kernel<T, N, P>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::walk_lds) != hipSuccess)
-            return -1;
+        const void* walk;
+        size_t lds;
+        if constexpr (kBf16) {
+            walk = reinterpret_cast<const void*>(&bwd_walk_bf16_kernel<N, P>);
+            lds = SB::walk_lds;
+        } else {
+            walk = reinterpret_cast<const void*>(&bwd_walk_kernel<T, N, P>);
+            lds = S::walk_lds;
+        }
+        if (hipFuncSetAttribute(walk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return -1;
         attr[dev] = true;
     }
     const int64_t units = bl.p.batch * bl.p.nheads;
@@ -1056,12 +1564,21 @@ int launch_backward_t(const BackwardLaunch& bl, hipStream_t stream) {
                   dim3(kThreads), 0, stream, p.dB, nbc, p.dC, nbc))
         return -1;
     if (units > 0) {
-        if (!launch_k(bl, k, bwd_states_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
-                      S::states_lds, stream, p))
-            return -1;
-        if (!launch_k(bl, k, bwd_walk_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads), S::walk_lds,
-                      stream, p))
-            return -1;
+        if constexpr (kBf16) {
+            if (!launch_k(bl, k, bwd_states_bf16_kernel<N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
+                          SB::states_lds, stream, p))
+                return -1;
+            if (!launch_k(bl, k, bwd_walk_bf16_kernel<N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
+                          SB::walk_lds, stream, p))
+                return -1;
+        } else {
+            if (!launch_k(bl, k, bwd_states_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
+                          S::states_lds, stream, p))
+                return -1;
+            if (!launch_k(bl, k, bwd_walk_kernel<T, N, P>, dim3((unsigned)(8 * p.per_xcd)), dim3(kBThreads),
+                          S::walk_lds, stream, p))
+                return -1;
+        }
     }
     if (p.dD && !launch_k(bl, k, bwd_reduce_kernel, dim3((unsigned)bl.p.nheads),
                           dim3(kThreads), 0, stream, (const float*)p.dD_part, p.dD, bl.p.batch, bl.p.nheads,
