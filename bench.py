@@ -150,7 +150,7 @@ def kernel_names(cfg, front_end="log_a", segmented=True, packed=0):
             return ["discretize_kernel"] + kernel_names(cfg) + (["skip_kernel"] if cfg["skip"] else [])
     if cfg["decay"] == "diag":
         if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
-            if segmented and fast_segments(dict(cfg, chunk=64), 512) > 1:
+            if segmented and fast_segments(dict(cfg, chunk=64), 256) > 1:
                 return ["walk_diag_pipe_kernel<%d,%d,state>" % (N, P), "seg_prefix_kernel",
                         "walk_diag_pipe_kernel<%d,%d>" % (N, P)]
             return ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]
