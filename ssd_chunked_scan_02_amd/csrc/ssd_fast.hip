@@ -793,14 +793,16 @@ __global__ void __launch_bounds__(kThreads) seq_order_kernel(const int64_t* seq_
     order[rank] = (int)i;
 }
 
-// The work index of workgroup bid of a packed batch's walk: the sequences go to the 8 XCDs in
-// turn in seq_order's order (longest first), and each XCD runs the heads of its sequences one
-// sequence after another, so every XCD gets a like share of the work, the longest sequences start
-// first, and the heads of a sequence share one L2.  -1 past the last sequence.
+// The work index of workgroup bid of a packed batch's walk: the (sequence, head) items in
+// seq_order's order (longest first), one per workgroup.  Workgroups go to the 8 XCDs in turn, so
+// every XCD gets every eighth item: a like share of each sequence's heads, and within an XCD the
+// longest items start first.  (Dealing whole sequences to the XCDs kept a sequence's heads on one
+// L2 but gave the XCD holding the longest sequence of each eight the most work.)  -1 past the
+// last item.
 __device__ __forceinline__ int64_t packed_work_index(const Walk2Params& prm, int64_t bid) {
-    const int64_t x = bid % 8, l = bid / 8, r = x + 8 * (l / prm.nheads);
+    const int64_t r = bid / prm.nheads;
     if (r >= prm.batch) return -1;
-    return (int64_t)prm.seq_order[r] * prm.nheads + l % prm.nheads;
+    return (int64_t)prm.seq_order[r] * prm.nheads + bid % prm.nheads;
 }
 
 // DT: with log2 of an input scale per token (prm.lg_t, the discretisation front-end's Delta):
@@ -1111,8 +1113,8 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     if (!launch_k(fl, k, prep_kernel<N, Q>, dim3(pgrid), dim3(pthreads), plds, stream, pp)) return -1;
 
     const int64_t work = lay.nseg * lay.units;
-    // (ordered packed walk: ceil(batch / 8) sequences' heads per XCD)
-    const int64_t per_xcd = order ? (fl.batch + 7) / 8 * fl.nheads : (work + 7) / 8;
+    // (ordered packed walk: one workgroup per (sequence, head), dealt to the XCDs in turn)
+    const int64_t per_xcd = order ? (fl.batch * fl.nheads + 7) / 8 : (work + 7) / 8;
     Walk2Params wp{fl.x, la_t, lg_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, nch, per_xcd,
                    lay.seg_chunks, lay.nseg, reinterpret_cast<float*>(ws + lay.seg_state),
