@@ -89,7 +89,6 @@ class HipEvents:
 # the source file each kernel (by name prefix) and its launch code are compiled from
 KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.hip",
                   "seg_state_kernel": "ssd_fast.hip", "seg_prefix_kernel": "ssd_fast.hip",
-                  "seq_order_kernel": "ssd_fast.hip",
                   "walk_diag_pipe_kernel": "ssd_diag.hip", "walk_diag_kernel": "ssd_diag.hip",
                   "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
                   "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
@@ -160,8 +159,7 @@ def kernel_names(cfg, front_end="log_a", segmented=True, packed=0):
         if segmented and fast_segments(cfg) > 1:
             return ["prep_kernel<%d,%d>" % (N, q), "seg_state_kernel<%d,%d>" % (N, q),
                     "walk_fast_kernel<%d,%d>" % (N, q)]
-        order = ["seq_order_kernel"] if 0 < packed <= 4096 else []
-        return order + ["prep_kernel<%d,%d>" % (N, q), "walk_fast_kernel<%d,%d>" % (N, q)]
+        return ["prep_kernel<%d,%d>" % (N, q), "walk_fast_kernel<%d,%d>" % (N, q)]
     return ["scores_kernel<%d>" % N, "walk_kernel<%d,%d>" % (N, P)]
 
 
@@ -674,8 +672,8 @@ def run_varlen(args, cfg, dev):
         threads = oracle.default_threads()
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.varlen.forward_varlen(oracle.default_oracle(), *a, p["cu_seqlens"].numpy(), f(p.get("D")),
-                                         f(p.get("init_state")), want_final=cfg["final"])
+            ref = oracle.varlen.forward_varlen(oracle.default_oracle(), *a, p["cu_seqlens"].numpy(), f(p.get("D")),
+                                               f(p.get("init_state")), want_final=cfg["final"])
             reps += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:
@@ -685,7 +683,13 @@ def run_varlen(args, cfg, dev):
                                   "sample": "the whole packed batch (%d tokens in %d sequences x %d heads), %d run(s) "
                                             "in %.1f s, fp64 recurrence per sequence, OpenMP over heads"
                                             % (total, nseq, H, reps, el)}
+        # the timed run's outputs (first input copy) against the oracle's, as one batch element
+        yr, fr = ref
+        result["parity"] = output_parity(cfg, {"x": p["x"][None], "D": p.get("D")}, bufs[0]["y"][None],
+                                         bufs[0]["final"], (yr[None], fr))
     print(json.dumps(result), flush=True)
+    if "parity" in result and not result["parity"]["pass"]:
+        sys.exit(1)
 
 
 def main():

@@ -93,6 +93,39 @@ constexpr int kPrepLa = 4;
 constexpr int64_t kPrepSplitMax = 256;  // prep workgroups one round of the CUs holds
 constexpr int kPrepMinThreads = 512;
 
+// Ranks of a packed batch's (at most kOrderMax) sequences by length, longest first (ties by
+// index): order[rank] = b.  Workgroup w of the ranking ranks sequences w THREADS .. + THREADS - 1,
+// one per thread: it stages every length in LDS (lens, padded with -1 to a multiple of 4, which
+// count for nothing), and each thread counts the sequences ahead of its own, four lengths per LDS
+// read, every lane reading the same ones.
+constexpr int64_t kOrderMax = 4096;
+template <int THREADS>
+__device__ void rank_sequences(const int64_t* seq_off, int64_t nseq, int64_t seqlen, int64_t total, int* order,
+                               int* lens, int w, int tid) {
+    const int n4 = (int)((nseq + 3) / 4);
+    for (int64_t j = tid; j < 4 * (int64_t)n4; j += THREADS)
+        lens[j] = j < nseq ? (int)seq_span(seq_off, j, seqlen, total).len : -1;
+    __syncthreads();
+    const int64_t i = (int64_t)w * THREADS + tid;
+    if (i >= nseq) return;
+    const int li = lens[i];
+    int rank = 0;
+    for (int j4 = 0; j4 < n4; ++j4) {
+        const int4 v = reinterpret_cast<const int4*>(lens)[j4];
+        const int j = 4 * j4;
+        rank += (v.x > li || (v.x == li && j < (int)i)) ? 1 : 0;
+        rank += (v.y > li || (v.y == li && j + 1 < (int)i)) ? 1 : 0;
+        rank += (v.z > li || (v.z == li && j + 2 < (int)i)) ? 1 : 0;
+        rank += (v.w > li || (v.w == li && j + 3 < (int)i)) ? 1 : 0;
+    }
+    order[rank] = (int)i;
+}
+// workgroups of the ranking, rounded up to a whole number of XCD rounds (8)
+template <int THREADS>
+constexpr int64_t ranking_groups(int64_t nseq) {
+    return (nseq + 8 * THREADS - 1) / (8 * THREADS) * 8;
+}
+
 template <int N, int Q>
 __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepParams prm) {
     constexpr int kPrepThreads = PrepShape<N, Q>::THREADS, kPrepWaves = PrepShape<N, Q>::WAVES;
@@ -105,10 +138,22 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
     __bf16* Cs = Bs + Q * NS;                       // [Q][NS]
     const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane % 16, lg = lane / 16;
+    // A packed batch's first workgroups (a whole number of XCD rounds, dispatched first so that
+    // they overlap the blocks) rank its sequences for the walk's order, beside the blocks rather
+    // than in a launch of their own before them.
+    int64_t bid = blockIdx.x;
+    if (prm.order) {
+        const int64_t nseq = prm.nblk / (prm.ngroups * prm.nchunks), nrank = ranking_groups<kPrepThreads>(nseq);
+        if (bid < nrank) {
+            rank_sequences<kPrepThreads>(prm.seq_off, nseq, prm.seqlen, prm.total, prm.order,
+                                         reinterpret_cast<int*>(smem), (int)bid, tid);
+            return;
+        }
+        bid -= nrank;
+    }
     // With prm.split, two workgroups per block on the same XCD (workgroup i runs on XCD i % 8),
     // which shortens the chain each one waits through: part 0 writes the score pairs, part 1 the
     // C^T and B^T fragments and log a head-major.  Otherwise one workgroup does all of it.
-    const int64_t bid = blockIdx.x;
     const int part = prm.split ? (int)((bid / 8) % 2) : -1;
     const int64_t blk = prm.split ? (bid / 16) * 8 + bid % 8 : bid;
     if (blk >= prm.nblk) return;
@@ -776,23 +821,6 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     }
 }
 
-// Ranks of a packed batch's sequences by length, longest first (ties by index): order[rank] = b.
-// Every workgroup stages all the (at most kOrderMax) lengths in LDS; one thread per sequence then
-// counts the sequences ahead of it, every lane reading the same length at each step.
-constexpr int64_t kOrderMax = 4096;
-__global__ void __launch_bounds__(kThreads) seq_order_kernel(const int64_t* seq_off, int64_t nseq, int64_t seqlen,
-                                                             int64_t total, int* order) {
-    __shared__ int lens[kOrderMax];
-    for (int64_t j = threadIdx.x; j < nseq; j += kThreads) lens[j] = (int)seq_span(seq_off, j, seqlen, total).len;
-    __syncthreads();
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= nseq) return;
-    const int li = lens[i];
-    int rank = 0;
-    for (int j = 0; j < (int)nseq; ++j) rank += (lens[j] > li || (lens[j] == li && j < (int)i)) ? 1 : 0;
-    order[rank] = (int)i;
-}
-
 // The work index of workgroup bid of a packed batch's walk: the (sequence, head) items in
 // seq_order's order (longest first), one per workgroup.  Workgroups go to the 8 XCDs in turn, so
 // every XCD gets every eighth item: a like share of each sequence's heads, and within an XCD the
@@ -1096,7 +1124,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int nch = (int)lay.nchunks;
     float* lg_t = with_lg ? reinterpret_cast<float*>(ws + lay.lg_t) : nullptr;
     PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.dt, fl.dt_bias, fl.A_log, lg_t,
-                  fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0, fl.seq_off, fl.total};
+                  fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0, fl.seq_off, fl.total, nullptr};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q, DT>), walk_attr)) return -1;
     int k = fl.first_launch;
@@ -1105,12 +1133,13 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     // split each block over two workgroups when even then they fit on the CUs at once
     pp.split = 2 * lay.nblk <= kPrepSplitMax ? 1 : 0;
     const unsigned pgrid = pp.split ? (unsigned)((lay.nblk + 7) / 8 * 16) : (unsigned)lay.nblk;
-    // (a packed batch: the sequences ranked longest first, for the walk's workgroup order)
+    // (a packed batch: the sequences ranked longest first, for the walk's workgroup order, by one
+    // more prep workgroup, whose LDS holds every length)
+    static_assert(prep_lds<N, Q>() >= (size_t)kOrderMax * 4, "sequence lengths in the prep kernel's LDS");
     int* order = (fl.seq_off && fl.batch <= kOrderMax) ? reinterpret_cast<int*>(ws + lay.order) : nullptr;
-    if (order && !launch_k(fl, k, seq_order_kernel, dim3((unsigned)((fl.batch + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, fl.seq_off, fl.batch, fl.seqlen, fl.total, order))
-        return -1;
-    if (!launch_k(fl, k, prep_kernel<N, Q>, dim3(pgrid), dim3(pthreads), plds, stream, pp)) return -1;
+    pp.order = order;
+    const unsigned rgrid = order ? (unsigned)ranking_groups<PrepShape<N, Q>::THREADS>(fl.batch) : 0u;
+    if (!launch_k(fl, k, prep_kernel<N, Q>, dim3(pgrid + rgrid), dim3(pthreads), plds, stream, pp)) return -1;
 
     const int64_t work = lay.nseg * lay.units;
     // (ordered packed walk: one workgroup per (sequence, head), dealt to the XCDs in turn)

@@ -89,9 +89,12 @@ struct PrepParams {
     int nchunks;
     int64_t nblk;  // batch * ngroups * nchunks
     int split;     // 1: two workgroups per block (see prep_kernel)
-    // packed variable-length batch (null: batched layout), as in ForwardLaunch
+    // packed variable-length batch (null: batched layout), as in ForwardLaunch; with order non-null
+    // the grid's first workgroups rank the sequences for the walk (order[rank] = b) and the blocks
+    // follow them
     const int64_t* seq_off;
     int64_t total;
+    int* order;
 };
 
 struct Walk2Params {
