@@ -426,11 +426,15 @@ __global__ void __launch_bounds__(kThreads) walk_diag_kernel(WalkParams prm) {
 // to N + 4 floats so that 16 rows read at once fall on distinct banks.
 constexpr int kDiagQ = 64;
 constexpr int kDiagWaves = 8;
-// bound (natural log) on each of the two factors a diagonal score tile splits into: exp(kSplitMax)
-// and exp(-kSplitMax) are far inside the fp32 and bf16 ranges.  With the split taken halfway
-// (in value) through a block's running sums, a state dimension splits when its decay over the
-// block is at most 2 kSplitMax.
-constexpr float kSplitMax = 64.f;
+// bound (natural log) on each of the two factors a diagonal score tile splits into.  Both bf16
+// and fp32 reach e^88.7 and e^-87.3 (normal range), so exp(+-80) times a B or C entry stays finite
+// and normal for entries of magnitude 1e-3 .. 6e3 (a smaller entry's factor can flush to zero:
+// an absolute error under 1e-3 times the other operand, below that term's bf16 rounding at
+// typical magnitudes).  With the split taken halfway (in value)
+// through a block's running sums, a state dimension splits when its decay over the block is at
+// most 2 kSplitMax; the others take exact exponentials.  (At e^64 the multiscale workload sent
+// 1.6 groups of four dimensions per block to the exact terms, at e^80 0.85: walk 84-86 -> 82 us.)
+constexpr float kSplitMax = 80.f;
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kSplitMax2 = kSplitMax * kLog2eD;  // the same bound in log2 units
 // 2^x on the hardware unit (v_exp_f32); results below the normal range are not kept, which only
