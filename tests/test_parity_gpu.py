@@ -271,6 +271,24 @@ def test_diag_extreme_rates():
     compare(inp, y, fin, oracle_forward(inp), "bf16", True, "diag extreme rates")
 
 
+@pytest.mark.parametrize("scale", [0.02, 4000.0], ids=["small-BC", "large-BC"])
+def test_diag_split_bound_magnitudes(scale):
+    """B and C entries far from unit size (times 0.02: typical magnitude 2.5e-3; times 4000: up
+    to a few thousand) on decays of 6.5 to 10 nats per token, so that every dimension's decay over
+    a 16-token block lies near the split bound of the diagonal score tiles (up to 160 nats, each
+    factor within e^+-80): the split factors times B and C stay finite and normal there."""
+    cfg = ssd_inputs.config("diag_multiscale", batch=1, seqlen=256, nheads=2, init=True)
+    inp = ssd_inputs.make_inputs(cfg, 57)
+    gen = torch.Generator().manual_seed(11)
+    inp["log_a"] = (-(6.5 + 3.5 * torch.rand(inp["log_a"].shape, generator=gen))).to(torch.float32).contiguous()
+    for k in ("B", "C"):
+        inp[k] = (inp[k].float() * scale).to(inp[k].dtype)
+    announce("diag split-bound magnitudes scale=%g" % scale)
+    y, fin = gpu_forward(to_gpu(inp), 64, True)
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+    compare(inp, y, fin, oracle_forward(inp), "bf16", True, "diag split-bound magnitudes x%g" % scale)
+
+
 def test_decode_steps_in_a_hip_graph():
     """ssd_step launches captured in a HIP graph (as the decode timing replays them) give the
     eager result bitwise, on every one of several replays with eager work in between."""
