@@ -25,6 +25,11 @@ CASES = [
     ("mamba2_layer", dict(batch=1, seqlen=64, nheads=2, dt_mean=3.0), "bf16-fast"),
     # many backward chunks and a ragged tail; eight heads per group (dB, dC summed over them)
     ("gqa_decode", dict(batch=2, seqlen=1500, nheads=16, ngroups=2, decode_steps=0, init=True), "bf16-long-gqa"),
+    # the other shapes of the bf16-MFMA backward kernels (N in {32, 64, 128}, P in {32, 64})
+    ("mamba2_layer", dict(batch=2, seqlen=200, nheads=4, ngroups=2, dstate=32, headdim=32, init=True), "bf16-n32-p32"),
+    ("mamba2_layer", dict(batch=1, seqlen=160, nheads=3, dstate=32, headdim=64, init=True), "bf16-n32-p64"),
+    ("mamba2_layer", dict(batch=1, seqlen=160, nheads=2, dstate=64, headdim=32), "bf16-n64-p32"),
+    ("mamba2_layer", dict(batch=2, seqlen=97, nheads=2, dstate=128, headdim=32, init=True), "bf16-n128-p32"),
     ("tiny_fp32", dict(batch=2, seqlen=1100, nheads=2, dstate=128, headdim=64, init=True, skip=True,
                        a_log="uniform16", dt_mean=-2.0), "fp32-long"),
     # diagonal decay: per-(head, dim) rates, fast and slow dimensions in one head
