@@ -123,9 +123,9 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def fast_segments(cfg, target=512):
+def fast_segments(cfg, target=256):
     """Segments the library splits each (batch, head) sequence into (mirrors its workspace
-    layout: only with at most 128 units; about `target` (512) workgroups and at least 4 chunks
+    layout: only with at most 128 units; about `target` (256) workgroups and at least 4 chunks
     per segment)."""
     q = min(cfg["chunk"], 128)
     units = cfg["batch"] * cfg["nheads"]

@@ -314,8 +314,8 @@ int ssd_backward_dt_varlen(const ssd_dims* dims, const int64_t* cu_seqlens, int6
  *
  * Limit: a call whose ssd_forward_workspace_bytes(dims, chunk) exceeds the array fails with
  * SSD_ERR_SCRATCH before doing anything (the Mamba-2 layer shape, 8 x 2048 tokens x 24 heads at
- * N = 128, needs 12 MiB; one 65 536-token sequence of 32 heads, 66 MiB; 4 x 8192 tokens x 64 heads
- * in 8 groups, 183 MiB, which does not fit).
+ * N = 128, needs 12 MiB; one 65 536-token sequence of 32 heads, 58 MiB; 4 x 8192 tokens x 64 heads
+ * in 8 groups, 176 MiB, which does not fit).
  * Races: every call on one GPU uses that GPU's one array, so calls that overlap in time on one
  * GPU (on different streams, or from several threads without ordering) corrupt each other's
  * workspace.  Calls ordered on one stream are safe: no call needs anything the previous one left

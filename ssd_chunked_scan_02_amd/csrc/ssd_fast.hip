@@ -287,7 +287,10 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
 // Global addresses are a wave-uniform 64-bit base per chunk plus a 32-bit per-lane byte
 // offset (the host only takes this path when every offset inside a chunk fits).
 constexpr int kWalkWaves = 8;
-constexpr int64_t kSegTarget = 512;  // workgroups of a segmented fast walk (two rounds per CU)
+// workgroups of a segmented fast walk: one round (one per CU).  Two rounds of half as long
+// segments give the state pass more workgroups but measured slower at the long-sequence workload
+// (255-258 against 249-253 us per forward: walk 175 against 169 us, state pass 31 against 36.5 us).
+constexpr int64_t kSegTarget = 256;
 constexpr int kWalkThreads = kWalkWaves * kWave;
 
 // 16-token block handled by output wave `ow` in its r-th round (snake order balances the

@@ -73,9 +73,10 @@ def test_workspace_bytes(lib):
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(seqlen=2050), 128) == fast(8, 24, 1, 17, 128, 128)
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(ngroups=8, nheads=64), 64) == fast(8, 64, 8, 32, 128, 64)
     # chunk 256 runs as 128-token chunks; with few (batch, head) units on a long sequence the
-    # walk is split into segments (here 32 units, 512 chunks -> 16 segments of 32 chunks), which
-    # adds an fp32 state and a log2 decay per (segment, unit), the decays padded to 256 bytes
-    seg = 16 * 32 * (128 * 64 * 4) + (16 * 32 * 4 + 255) // 256 * 256
+    # walk is split into segments (here 32 units, 512 chunks -> 8 segments of 64 chunks: one
+    # walk workgroup per CU), which adds an fp32 state and a log2 decay per (segment, unit), the
+    # decays padded to 256 bytes
+    seg = 8 * 32 * (128 * 64 * 4) + (8 * 32 * 4 + 255) // 256 * 256
     assert ssd.ssd_forward_workspace_bytes(mamba2_dims(batch=1, nheads=32, seqlen=65536), 256) == \
         fast(1, 32, 1, 512, 128, 128) + seg
     # other shapes: causal 16x16 fp32 score tiles per (batch, group, chunk)
