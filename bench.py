@@ -87,7 +87,7 @@ class HipEvents:
 
 
 # the source file each kernel (by name prefix) and its launch code are compiled from
-KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.hip",
+KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.hip", "mark_tokens_kernel": "ssd_fast.hip",
                   "seg_state_kernel": "ssd_fast.hip", "seg_prefix_kernel": "ssd_fast.hip",
                   "walk_diag_pipe_kernel": "ssd_diag.hip", "walk_diag_kernel": "ssd_diag.hip",
                   "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
@@ -123,10 +123,10 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def fast_segments(cfg, target=256):
+def fast_segments(cfg, target=256, chunks_per_segment=False):
     """Segments the library splits each (batch, head) sequence into (mirrors its workspace
     layout: only with at most 128 units; about `target` (256) workgroups and at least 4 chunks
-    per segment)."""
+    per segment), or with chunks_per_segment the chunks of each segment."""
     q = min(cfg["chunk"], 128)
     units = cfg["batch"] * cfg["nheads"]
     nch = -(-cfg["seqlen"] // q)
@@ -134,14 +134,32 @@ def fast_segments(cfg, target=256):
     if units > 0 and units * 2 <= 256 and nch >= 8:
         nseg = min(target // units, nch // 4)
     per = -(-nch // nseg)
-    return -(-nch // per)
+    return per if chunks_per_segment else -(-nch // per)
 
 
-def kernel_names(cfg, front_end="log_a", segmented=True, packed=0):
-    """Kernels one forward launches, in order (mirrors the library's dispatch; a packed
-    variable-length batch of `packed` sequences is never segmented, and on the fast path up to 4096
-    of them are first ranked by length)."""
+def packed_as_one(cfg, nseq, tokens):
+    """Whether the library walks a packed batch of nseq sequences (tokens in all, lengths bounded
+    by cfg["seqlen"]) with no per-sequence states as one sequence (mirrors its estimate: one
+    segment's chunks x 1.35 + 2 against the longest sequence's chunks or all (sequence, head)
+    chunks over 256 CUs, whichever is more)."""
+    q = min(cfg["chunk"], 128)
+    nch = -(-tokens // q)
+    per = fast_segments(dict(cfg, batch=1, seqlen=tokens), chunks_per_segment=True)
+    longest = -(-cfg["seqlen"] // q)
+    spread = math.ceil((nch + nseq) * cfg["nheads"] / 256.0)
+    return 1.35 * per + 2.0 < max(longest, spread)
+
+
+def kernel_names(cfg, front_end="log_a", segmented=True, packed=0, tokens=0):
+    """Kernels one forward launches, in order (mirrors the library's dispatch).  A packed
+    variable-length batch of `packed` sequences (`tokens` in all) with per-sequence states is walked
+    sequence by sequence, never segmented, and on the fast path up to 4096 of them are first ranked
+    by length; without states the fast path walks it as one sequence of all its tokens (segmented
+    as such), after marking where each sequence starts."""
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
+    fast = cfg["decay"] != "diag" and cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256)
+    if packed and fast and not cfg["init"] and not cfg["final"] and packed_as_one(cfg, packed, tokens):
+        return ["mark_tokens_kernel"] + kernel_names(dict(cfg, batch=1, seqlen=tokens), front_end)
     if front_end == "dt":
         fused = (cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64)) if cfg["decay"] == "diag" \
             else (cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256))
@@ -637,7 +655,7 @@ def run_varlen(args, cfg, dev):
         for h in e:
             ev.destroy(h)
     kernel_avg = [sum(v) / len(v) for v in per_kernel]
-    names = kernel_names(cfg, segmented=False, packed=nseq)
+    names = kernel_names(dict(cfg, seqlen=maxT), segmented=False, packed=nseq, tokens=total)
     if len(names) != launches:
         names = ["launch%d" % k for k in range(launches)]
     dom = max(range(launches), key=lambda k: kernel_avg[k])

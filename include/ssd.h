@@ -189,8 +189,21 @@ int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float
  *     and to its first dims->seqlen tokens, so malformed offsets give wrong outputs but never an
  *     access outside the tensors or the workspace.  The host does not read it.
  *   dims->seqlen: a bound on every sequence's length (the longest one's length is the natural
- *     choice); it sizes the workspace, which is that of a [batch][seqlen] batch without the
- *     segmented walks.  Tokens past that bound are neither read nor written.
+ *     choice).  Tokens past that bound, and tokens outside every sequence, are never written and
+ *     enter no output.
+ *   The bf16 scalar-decay fast path (head dim 64, N 64 or 128) has two forms.  Sequence by
+ *     sequence: one walk per (sequence, head), as a batch; always taken when init_state or
+ *     final_state is given.  As one sequence (init_state and final_state both NULL): the packed
+ *     axis is walked like one long sequence of total_tokens tokens, segmented over the CUs, with
+ *     the recurrence restarted at every sequence's first token (a first launch marks those tokens
+ *     from cu_seqlens on the device), so the work follows the token count, not the sequence count.
+ *     The host takes the form with the shorter estimated walk from batch, total_tokens,
+ *     dims->seqlen and the head count.  Either gives the same operator; outputs differ only in
+ *     rounding.
+ *   Workspace: the larger of the two forms' needs (a [batch][seqlen] batch's without the
+ *     segmented walks, plus 4 bytes per sequence for up to 4096 sequences' order; and the batched
+ *     layout of one sequence of batch * seqlen tokens with its segment states, plus 4 bytes per
+ *     token of whole chunks).
  *   chunk, shapes, dtypes and decay kinds as ssd_forward.
  *   events, n_events, n_launches: as ssd_forward_profiled (NULL, 0, NULL: no timing).
  * Returns as ssd_forward; SSD_ERR_INVALID also for total_tokens < 0 or above batch * seqlen, or a

@@ -27,6 +27,8 @@
 // both exp of a non-positive number; U is one table per chunk, so a masked score costs one
 // multiply.  Only the 16x16 diagonal block of each output block takes exact exps.
 
+#include <cmath>
+
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -312,8 +314,25 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     return x;
 }
 
+// Token flags of a packed batch walked as one sequence (Walk2Params::tok_flags): a token with
+// either bit set begins a new stretch of the recurrence (a sequence start, or a token of no
+// sequence, which stands alone).  Two tokens of one chunk share a sequence exactly when the number
+// of such tokens up to each of them is the same.  Tag of a token outside every sequence: its count
+// plus this (exact in fp32; counts are below 257).
+constexpr int kFlagStart = 1, kFlagDead = 2;
+constexpr float kDeadTag = 65536.f;
+// log2 decay that stands for "the recurrence restarts here": exp2 of it is 0, and it stays hugely
+// negative under the additions of ordinary decays.
+constexpr float kRestart2 = -1.0e30f;
+
 __device__ __forceinline__ float lane_value(float v, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o /= 2) v = max(v, __shfl_xor(v, o, kWave));
+    return v;
 }
 
 // 16-byte global load at a uniform base plus a per-lane byte offset.
@@ -353,8 +372,10 @@ struct WalkShape {
     static constexpr int PB = kP / 16, HS = N + 8;
     // one decay-factor buffer, floats: cum2 [Q] (log2 e times the running sum of log a),
     // f [Q], w [Q], U [NT][Q], ea [NT], cs2 [Q] (the running sums on the input side of a
-    // factor: cum2 - log2 of the input scale, written only with one)
-    static constexpr int FSZ = 4 * Q + NT * Q + NT;
+    // factor: cum2 - log2 of the input scale, written only with one), tag [Q] (a packed batch
+    // walked as one sequence: the count of sequence starts up to each token, plus kDeadTag for a
+    // token outside every sequence; written only then)
+    static constexpr int FSZ = 5 * Q + NT * Q + NT;
     static constexpr int YROWS = 16 * TBW;  // output rows of one output wave per chunk
     static constexpr size_t lds_bytes =
         (size_t)(4 * Q * kXStr + 2 * kP * HS + 4 * YROWS * kXStr) * 2 + (size_t)2 * FSZ * 4;
@@ -388,6 +409,7 @@ struct WalkLds {
     __device__ float* U(int buf) const { return Fs + buf * WS::FSZ + 3 * Q; }
     __device__ float* ea(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q; }
     __device__ float* cs2(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q + WS::NT; }
+    __device__ float* tag(int buf) const { return Fs + buf * WS::FSZ + 4 * Q + WS::NT * Q + WS::NT; }
 };
 
 // The piece of work of one workgroup: a (batch, head) unit and the chunks [c0, c1) of one
@@ -415,7 +437,7 @@ __device__ __forceinline__ WalkSpan walk_span(const Walk2Params& prm, int64_t wo
     return sp;
 }
 
-template <int N, int Q, int OW, bool DT>
+template <int N, int Q, int OW, bool DT, bool PK>
 __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
                                                  int lane) {
     const int64_t b = span.b, h = span.h, g = span.g;
@@ -483,6 +505,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         const float* ffa = L.f(buf);
         const float* Ut = L.U(buf);
         const float* ea = L.ea(buf);
+        const float* tagr = L.tag(buf);
 
         // carried state: acc = exp(cum_a) C_t H_{k-1}  (acc rows: p, columns: t)
         f32x4 acc[TBW][PB];
@@ -546,11 +569,22 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
                     for (int pb = 0; pb < PB; ++pb) acc[r][pb] *= ft;
                     const float ct = cum2[t];
                     const f32x4 cd = *reinterpret_cast<const f32x4*>(cin2 + 16 * tb + 4 * lg);
+                    // (a packed batch: only pairs of one sequence)
+                    bool keep[4];
+                    if constexpr (PK) {
+                        const float tt = tagr[t];
+                        const f32x4 ts = *reinterpret_cast<const f32x4*>(tagr + 16 * tb + 4 * lg);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) keep[j] = causal[j] && ts[j] == tt;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) keep[j] = causal[j];
+                    }
                     if (tb % 2 == 0) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const float v = s8[j] * fexp2(ct - cd[j]);
-                            bop[j] = (__bf16)(causal[j] ? v : 0.f);
+                            bop[j] = (__bf16)(keep[j] ? v : 0.f);
                             bop[j + 4] = (__bf16)0.f;
                         }
                     } else {
@@ -559,7 +593,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
                         for (int j = 0; j < 4; ++j) {
                             bop[j] = (__bf16)(s8[j] * (ft * u0[j]));
                             const float v = s8[j + 4] * fexp2(ct - cd[j]);
-                            bop[j + 4] = (__bf16)(causal[j] ? v : 0.f);
+                            bop[j + 4] = (__bf16)(keep[j] ? v : 0.f);
                         }
                     }
                 }
@@ -595,14 +629,16 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         for (int m = 0; m < YST; ++m) {
             const int id = lane + kWave * m, row = id / 8, c8 = id % 8;
             const int t = 16 * wave_tb(row / 16, OW) + row % 16;
-            buffer_store16_nt(yr, (uint32_t)t * y_row + 16 * c8, ld16(ys + row * kXStr + 8 * c8));
+            // (a packed batch: rows outside every sequence are not written)
+            if (!PK || tagr[t] < kDeadTag)
+                buffer_store16_nt(yr, (uint32_t)t * y_row + 16 * c8, ld16(ys + row * kXStr + 8 * c8));
         }
         lds_barrier();
     }
 }
 
 // The state waves of the walk (they also stage everything the output waves read).
-template <int N, int Q, int SW, bool DT>
+template <int N, int Q, int SW, bool DT, bool PK>
 __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
                                                 int lane) {
     const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
@@ -616,6 +652,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     const uint32_t x_row = (uint32_t)(H * kP * 2);
     const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
     const float* lg0 = DT ? prm.lg_t + unit * (int64_t)nchunks * Q : nullptr;
+    const int* fl0 = PK ? prm.tok_flags : nullptr;
     const __bf16* xg = static_cast<const __bf16*>(prm.x);
     const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * (N / 16) * KS * 512;
     const uint4 zero = {0u, 0u, 0u, 0u};
@@ -623,6 +660,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 
     float la[LA];
     float lgs[DT ? LA : 1];  // (DT) log2 of the input scale of the same tokens
+    int flg[PK ? LA : 1];    // (PK) the token flags of the same tokens
     uint4 xs[XCH];
     uint4 bt[NBW][KS];
     // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
@@ -635,6 +673,9 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         if (DT)
 #pragma unroll
             for (int j = 0; j < LA; ++j) lgs[j] = lg0[t0 + lane * LA + j];
+        if (PK)
+#pragma unroll
+            for (int j = 0; j < LA; ++j) flg[j] = fl0[t0 + lane * LA + j];
     };
     auto load_x = [&](int c) {
         const int last = chunk_len(c) - 1;
@@ -671,6 +712,25 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         float cin[LA];
 #pragma unroll
         for (int j = 0; j < LA; ++j) cin[j] = DT ? cum[j] - lgs[j] : cum[j];
+        // (PK) sequence tags: the running count of tokens that begin a new stretch of the
+        // recurrence; every factor that links two tokens of different tags is 0, and so is the
+        // decay of the state carried into the chunk past the first such token.  (Counts are
+        // exact in fp32.)
+        float cnt[LA];
+        float cnt_e = 0.f, cnt_b = 0.f;
+        if constexpr (PK) {
+            float crun = 0.f;
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                crun += flg[j] != 0 ? 1.f : 0.f;
+                cnt[j] = crun;
+            }
+            const float cincl = wave_inclusive_sum(crun);
+#pragma unroll
+            for (int j = 0; j < LA; ++j) cnt[j] += cincl - crun;
+            cnt_e = lane_value(cincl, kWave - 1);
+            cnt_b = __shfl(cnt[0], lane & ~(16 / LA - 1), kWave);
+        }
         // this wave's quarter of the tokens: lanes [16 SW, 16 SW + 16)
         if (lane / 16 == SW) {
 #pragma unroll
@@ -678,26 +738,34 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
                 const int t = lane * LA + j;
                 L.cum2(buf)[t] = cum[j];
                 if (DT) L.cs2(buf)[t] = cin[j];
-                L.f(buf)[t] = fexp2(cum[j] - blk2);
-                L.w(buf)[t] = fexp2(last2 - cin[j]);
+                if constexpr (PK) {
+                    L.f(buf)[t] = cnt[j] == cnt_b ? fexp2(cum[j] - blk2) : 0.f;
+                    L.w(buf)[t] = cnt[j] == cnt_e ? fexp2(last2 - cin[j]) : 0.f;
+                    L.tag(buf)[t] = cnt[j] + ((flg[j] & kFlagDead) ? kDeadTag : 0.f);
+                } else {
+                    L.f(buf)[t] = fexp2(cum[j] - blk2);
+                    L.w(buf)[t] = fexp2(last2 - cin[j]);
+                }
             }
         }
         // rows SW, SW + 4, ... of U
 #pragma unroll
         for (int tb = SW; tb < NT; tb += 4) {
             const float ca = lane_value(cum[0], 16 * tb / LA);
+            const float cnt_a = PK ? lane_value(cnt[0], 16 * tb / LA) : 0.f;
             float* urow = L.U(buf) + tb * Q;
 #pragma unroll
             for (int j = 0; j < LA; ++j) {
                 const int s = lane * LA + j;
-                urow[s] = s < 16 * tb ? fexp2(ca - cin[j]) : 0.f;
+                urow[s] = s < 16 * tb && (!PK || cnt[j] == cnt_a) ? fexp2(ca - cin[j]) : 0.f;
             }
         }
         if (SW == 0) {
             const float s2 = __shfl(cum[0], (16 * lane) / LA, kWave);
-            if (lane < NT) L.ea(buf)[lane] = fexp2(s2);
+            const float c2 = PK ? __shfl(cnt[0], (16 * lane) / LA, kWave) : 0.f;
+            if (lane < NT) L.ea(buf)[lane] = c2 == 0.f ? fexp2(s2) : 0.f;
         }
-        return fexp2(last2);
+        return cnt_e == 0.f ? fexp2(last2) : 0.f;
     };
     // x of chunk c into the x buffers c & 1, raw and weighted by w (after factors(c)).
     auto stage_x = [&](int c) {
@@ -841,7 +909,9 @@ __device__ __forceinline__ int64_t packed_work_index(const Walk2Params& prm, int
 
 // DT: with log2 of an input scale per token (prm.lg_t, the discretisation front-end's Delta):
 // the input side of every factor carries it, so the input term is Delta_s B_s x_s^T.
-template <int N, int Q, bool DT>
+// PK: a packed batch walked as one sequence, with the recurrence restarted at every token
+// prm.tok_flags marks (above).
+template <int N, int Q, bool DT, bool PK>
 __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm) {
     const int64_t work = prm.seq_order ? packed_work_index(prm, blockIdx.x)
                                        : xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
@@ -859,14 +929,14 @@ __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm
     extern __shared__ __align__(16) unsigned char smem[];
     const WalkLds<N, Q> L(smem);
     switch (wave) {
-        case 0: walk_output_role<N, Q, 0, DT>(prm, L, span, lane); break;
-        case 1: walk_output_role<N, Q, 1, DT>(prm, L, span, lane); break;
-        case 2: walk_output_role<N, Q, 2, DT>(prm, L, span, lane); break;
-        case 3: walk_output_role<N, Q, 3, DT>(prm, L, span, lane); break;
-        case 4: walk_state_role<N, Q, 0, DT>(prm, L, span, lane); break;
-        case 5: walk_state_role<N, Q, 1, DT>(prm, L, span, lane); break;
-        case 6: walk_state_role<N, Q, 2, DT>(prm, L, span, lane); break;
-        default: walk_state_role<N, Q, 3, DT>(prm, L, span, lane); break;
+        case 0: walk_output_role<N, Q, 0, DT, PK>(prm, L, span, lane); break;
+        case 1: walk_output_role<N, Q, 1, DT, PK>(prm, L, span, lane); break;
+        case 2: walk_output_role<N, Q, 2, DT, PK>(prm, L, span, lane); break;
+        case 3: walk_output_role<N, Q, 3, DT, PK>(prm, L, span, lane); break;
+        case 4: walk_state_role<N, Q, 0, DT, PK>(prm, L, span, lane); break;
+        case 5: walk_state_role<N, Q, 1, DT, PK>(prm, L, span, lane); break;
+        case 6: walk_state_role<N, Q, 2, DT, PK>(prm, L, span, lane); break;
+        default: walk_state_role<N, Q, 3, DT, PK>(prm, L, span, lane); break;
     }
 }
 
@@ -877,37 +947,45 @@ constexpr float kVanish2 = -160.f;
 // one, a token weighs at most 2^(decay + 64)
 constexpr float kLog2ScaleMax = 64.f;
 
-// seg_state_kernel: the state-only pass of a segmented walk, shaped for throughput.  One wave
-// per (segment, batch, head) forms the segment's local state (its final state from a zero start)
-// as one sum over the segment's chunks,
+// seg_state_kernel: the state-only pass of a segmented walk.  One workgroup of four waves per
+// (segment, batch, head) forms the segment's local state (its final state from a zero start) as
+// one sum over the segment's chunks,
 //   H_seg = sum_c B_c^T (W_c o X_c),   W_s = exp(decay from token s to the segment's end),
 // which equals the chunk recurrence H_k = exp(cum_last) H_{k-1} + B^T (w o X) unrolled.  The
 // chunks are taken last to first, so the decay from a chunk's end to the segment's end is the
 // running sum of the chunks already done, W_s <= 1, and the state registers are only ever
-// accumulated into.  The wave holds the whole N x P state and stages W o x of a chunk in an LDS
-// tile of its own, read back as MFMA operands contracting over tokens (no barrier: LDS serves one
-// wave's accesses in order).  Per chunk it issues the B^T operand loads, reads its operands out
-// of the tile, stages the next chunk into the tile while those loads are in flight, prefetches
-// the chunk after that, and then issues the chunk's MFMAs.  Once the weights of all tokens left
-// are below 2^-160, where exp2 is 0 in fp32, the rest of the segment would add exact zeros: the
-// wave then only sums the remaining chunks' decay, and the result is the same bit for bit.
+// accumulated into.  Wave v holds rows 16 (v + 4 j) .. + 15 of the N x P state (a quarter of the
+// MFMAs) and stages a quarter of the chunk's rows of W o x into a double-buffered LDS tile, which
+// every wave reads back as MFMA operands contracting over tokens; one barrier per chunk, so the
+// next chunk is staged while this one's MFMAs run.  Every wave scans the whole chunk's log a (the
+// same values, so the same decays and the same early exit in each).  Once the weights of all
+// tokens left are below 2^-160, where exp2 is 0 in fp32, the rest of the segment would add exact
+// zeros: the pass then only sums the remaining chunks' decay, and the result is the same bit for
+// bit.  (One wave holding the whole state took 20 us at the 32-sequence packed batch of the
+// Mamba-2 layer's tokens, 128 MFMAs per chunk on one SIMD.)
+constexpr int kSegWaves = 4;
 template <int N, int Q>
 struct SegStateShape {
-    static constexpr int NBK = N / 16, KS = Q / 32, PB = kP / 16, LA = Q / 64, XR = Q * kP / 8 / kWave;
-    // the W o x tile [Q][kXStr] bf16, then W [Q] fp32
-    static constexpr size_t lds_bytes = (size_t)Q * kXStr * 2 + (size_t)Q * 4;
+    static constexpr int NBK = N / 16, NBW = NBK / kSegWaves, KS = Q / 32, PB = kP / 16, LA = Q / 64;
+    static constexpr int QW = Q / kSegWaves, XR = QW * kP / 8 / kWave;  // rows and 16-byte pieces per wave
+    static_assert(NBW >= 1 && XR >= 1, "segment state shape");
+    // two W o x tiles [Q][kXStr] bf16, then W [Q] fp32
+    static constexpr size_t lds_bytes = (size_t)2 * Q * kXStr * 2 + (size_t)Q * 4;
 };
 
-template <int N, int Q, bool DT>
-__global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
+// PK: a packed batch walked as one sequence: a token marked in prm.tok_flags begins a new stretch
+// of the recurrence, so every token before the segment's last marked token weighs 0, and the
+// segment's decay is kRestart2 when it holds one (the walk's chain then restarts there).
+template <int N, int Q, bool DT, bool PK>
+__global__ void __launch_bounds__(kSegWaves * kWave) seg_state_kernel(Walk2Params prm) {
     using S = SegStateShape<N, Q>;
-    constexpr int NBK = S::NBK, KS = S::KS, PB = S::PB, LA = S::LA, XR = S::XR;
-    constexpr int NBH = NBK / 2;  // B^T operands load in two halves of the state rows
+    constexpr int NBW = S::NBW, KS = S::KS, PB = S::PB, LA = S::LA, QW = S::QW, XR = S::XR;
+    constexpr int NBK = S::NBK;
     const int64_t units = prm.batch * prm.nheads;
     const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, (prm.nseg - 1) * units);
     if (work < 0) return;
     const WalkSpan span = walk_span(prm, work, Q);
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave, wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
     const int c0 = span.c0, c1 = span.c1;
     const int64_t H = prm.nheads, G = prm.ngroups;
@@ -918,15 +996,19 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     __bf16* xg = const_cast<__bf16*>(static_cast<const __bf16*>(prm.x));
     const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * NBK * KS * 512;
     extern __shared__ __align__(16) unsigned char smem[];
-    __bf16* Xw = reinterpret_cast<__bf16*>(smem);
-    // W, permuted so that the XR rows a lane stages (lane / 8 + 8 m) are contiguous
-    float* wv = reinterpret_cast<float*>(smem + (size_t)Q * kXStr * 2);
+    __bf16* Xw = reinterpret_cast<__bf16*>(smem);  // [2][Q][kXStr]
+    // W of this wave's rows, permuted so that the XR rows a lane stages (r0 + lane / 8 + 8 m) are
+    // contiguous
+    float* wv_all = reinterpret_cast<float*>(smem + (size_t)2 * Q * kXStr * 2);
+    float* wvw = wv_all + wv * QW;
+    const int r0 = wv * QW;  // this wave's first row of a chunk
     auto chunk_len = [&](int c) { return (int)min((int64_t)Q, span.len - (int64_t)c * Q); };
-    // staging piece m of this lane: row lane / 8 + 8 m, bytes 16 (lane % 8) of it
-    const uint32_t xoff = (uint32_t)(lane / 8) * x_row + 16 * (lane % 8);
+    // staging piece m of this lane: row r0 + lane / 8 + 8 m, bytes 16 (lane % 8) of it
+    const uint32_t xoff = (uint32_t)(r0 + lane / 8) * x_row + 16 * (lane % 8);
 
     float la[LA];
     float lgs[DT ? LA : 1];  // (DT) log2 of the input scale of the same tokens
+    int flg[PK ? LA : 1];    // (PK) the token flags of the same tokens
     uint4 xs[XR];
     auto load_la = [&](int c) {
 #pragma unroll
@@ -934,17 +1016,20 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
         if (DT)
 #pragma unroll
             for (int j = 0; j < LA; ++j) lgs[j] = lg0[(int64_t)c * Q + lane * LA + j];
+        if (PK)
+#pragma unroll
+            for (int j = 0; j < LA; ++j) flg[j] = prm.tok_flags[(int64_t)c * Q + lane * LA + j];
     };
-    // x rows of the chunk through a buffer resource ending with it: rows past a short chunk's
-    // end read as zeros
+    // this wave's x rows of the chunk through a buffer resource ending with it: rows past a short
+    // chunk's end read as zeros
     auto load_x = [&](int c) {
         const __amdgpu_buffer_rsrc_t xr =
             buffer_rsrc(xg + ((span.row0 + (int64_t)c * Q) * H + h) * kP, (uint32_t)chunk_len(c) * x_row);
 #pragma unroll
         for (int m = 0; m < XR; ++m) xs[m] = buffer_load16(xr, xoff + (uint32_t)(8 * m) * x_row);
     };
-    // W o x of chunk c into the tile (from la and xs of chunk c), with sfx2 the log2 decay from
-    // the chunk's end to the segment's end; returns the chunk's own log2 decay
+    // W o x of this wave's rows of chunk c into tile c & 1 (from la and xs of chunk c), with sfx2
+    // the log2 decay from the chunk's end to the segment's end; returns the chunk's own log2 decay
     auto stage = [&](int c, float sfx2) -> float {
         const int len = chunk_len(c);
         float cum[LA], run = 0.f;
@@ -952,37 +1037,48 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
         for (int j = 0; j < LA; ++j) { run += (lane * LA + j < len) ? la[j] : 0.f; cum[j] = run; }
         const float incl = wave_inclusive_sum(run);
         const float excl = incl - run;
-        const float last2 = lane_value(incl, kWave - 1) * kLog2e;
+        float last2 = lane_value(incl, kWave - 1) * kLog2e;
+        // (PK) the chunk's last marked token: the tokens before it weigh 0, and so does every
+        // earlier chunk (the chunk's decay then stands for a restart)
+        int knew = -1;
+        if constexpr (PK) {
 #pragma unroll
-        for (int j = 0; j < LA; ++j) {
-            const int t = lane * LA + j;
-            wv[(t % 8) * (Q / 8) + t / 8] = fexp2(sfx2 + (last2 - (excl + cum[j]) * kLog2e) + (DT ? lgs[j] : 0.f));
+            for (int j = 0; j < LA; ++j)
+                if (flg[j] != 0) knew = lane * LA + j;
+            knew = wave_max(knew);
         }
+        // (the lanes holding this wave's rows write their weights)
+        if (lane * LA >= r0 && lane * LA < r0 + QW) {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                const int t = lane * LA + j, tl = t - r0;
+                const float wt = fexp2(sfx2 + (last2 - (excl + cum[j]) * kLog2e) + (DT ? lgs[j] : 0.f));
+                wvw[(tl % 8) * (QW / 8) + tl / 8] = (!PK || t >= knew) ? wt : 0.f;
+            }
+        }
+        if (PK && knew >= 0) last2 = kRestart2;
         wave_lds_fence();
+        // (row r0 + lane / 8 + 8 m sits at (lane / 8) XR + m: QW / 8 = XR)
         float w[XR];
 #pragma unroll
-        for (int q = 0; q < XR / 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(wv + (lane / 8) * (Q / 8) + 4 * q);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[4 * q + i] = v[i];
-        }
+        for (int m = 0; m < XR; ++m) w[m] = wvw[(lane / 8) * XR + m];
+        __bf16* tile = Xw + (c & 1) * Q * kXStr;
 #pragma unroll
         for (int m = 0; m < XR; ++m) {
             const bf16x8 rv = as_bf16x8(xs[m]);
             bf16x8 sv;
 #pragma unroll
             for (int j = 0; j < 8; ++j) sv[j] = (__bf16)((float)rv[j] * w[m]);
-            *reinterpret_cast<bf16x8*>(Xw + (lane / 8 + 8 * m) * kXStr + 8 * (lane % 8)) = sv;
+            *reinterpret_cast<bf16x8*>(tile + (r0 + lane / 8 + 8 * m) * kXStr + 8 * (lane % 8)) = sv;
         }
-        wave_lds_fence();
         return last2;
     };
 
-    f32x4 hs[NBK][PB];
+    f32x4 hs[NBW][PB];
 #pragma unroll
-    for (int nb = 0; nb < NBK; ++nb)
+    for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) hs[nb][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int pb = 0; pb < PB; ++pb) hs[j][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // chunks last to first; sfx2 = log2 decay from the end of the chunk being staged to the
     // segment's end
@@ -992,45 +1088,38 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     load_la(max(c1 - 2, c0));
     load_x(max(c1 - 2, c0));
     for (int c = c1 - 1; c >= c0; --c) {
+        // chunk c staged by every wave; every wave done reading tile (c - 1) & 1 (chunk c + 1)
+        __syncthreads();
         const void* bbase = bt0 + (int64_t)c * NBK * KS * 512;
-        uint4 blo[NBH][KS], bhi[NBH][KS];
+        uint4 bt[NBW][KS];
 #pragma unroll
-        for (int nb = 0; nb < NBH; ++nb)
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int k = 0; k < KS; ++k) blo[nb][k] = ldg16(bbase, 16 * lane + (nb * KS + k) * 1024);
+            for (int k = 0; k < KS; ++k) bt[j][k] = ldg16(bbase, 16 * lane + ((wv + kSegWaves * j) * KS + k) * 1024);
+        const __bf16* tile = Xw + (c & 1) * Q * kXStr;
         bf16x8 xfa[KS][PB];
 #pragma unroll
         for (int k = 0; k < KS; ++k)
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) xfa[k][pb] = token_frag(Xw, kXStr, 16 * pb, k, lane);
-        // the chunk before (at the first chunk: a repeat of it that nobody reads)
+            for (int pb = 0; pb < PB; ++pb) xfa[k][pb] = token_frag(tile, kXStr, 16 * pb, k, lane);
+        // the chunk before into the other tile (the other waves may still read this one)
         const float bound2 = sfx2;  // every token before chunk c weighs at most 2^bound2
-        const float d2 = stage(max(c - 1, c0), sfx2);
-        if (c > c0) sfx2 += d2;
-#pragma unroll
-        for (int nb = 0; nb < NBH; ++nb)
-#pragma unroll
-            for (int k = 0; k < KS; ++k) bhi[nb][k] = ldg16(bbase, 16 * lane + ((NBH + nb) * KS + k) * 1024);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int nb = 0; nb < NBH; ++nb)
-#pragma unroll
-            for (int k = 0; k < KS; ++k)
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) hs[nb][pb] = mfma_bf16(as_bf16x8(blo[nb][k]), xfa[k][pb], hs[nb][pb]);
+        if (c > c0) sfx2 += stage(c - 1, sfx2);
         load_la(max(c - 2, c0));
         load_x(max(c - 2, c0));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nb = 0; nb < NBH; ++nb)
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
             for (int k = 0; k < KS; ++k)
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb)
-                    hs[NBH + nb][pb] = mfma_bf16(as_bf16x8(bhi[nb][k]), xfa[k][pb], hs[NBH + nb][pb]);
+                for (int pb = 0; pb < PB; ++pb) hs[j][pb] = mfma_bf16(as_bf16x8(bt[j][k]), xfa[k][pb], hs[j][pb]);
         if (bound2 < kVanish2 - (DT ? kLog2ScaleMax : 0.f)) {
             // The weights of all earlier tokens are 0 in fp32 (exp2 of less than -160), so the
-            // earlier chunks would add exact zeros: only their decay is still summed.
+            // earlier chunks would add exact zeros: only their decay is still summed.  (PK: after
+            // a restart the segment's decay stands for the restart whatever the earlier chunks
+            // hold, so nothing is left to do.)  (Every wave takes this branch together.)
+            if (PK && sfx2 <= 0.5f * kRestart2) break;
             for (int cc = c - 2; cc >= c0; --cc) {
                 load_la(cc);
                 const int len = chunk_len(cc);
@@ -1044,16 +1133,16 @@ __global__ void __launch_bounds__(kWave) seg_state_kernel(Walk2Params prm) {
     }
 
     const int64_t sidx = span.seg * units + unit;
-    if (lane == 0) prm.seg_decay[sidx] = sfx2;
+    if (wv == 0 && lane == 0) prm.seg_decay[sidx] = sfx2;
     float* fin = prm.seg_state + sidx * N * kP;
     const int l16 = lane % 16, lg = lane / 16;
 #pragma unroll
-    for (int nb = 0; nb < NBK; ++nb)
+    for (int j = 0; j < NBW; ++j)
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb) {
-            float* dst = fin + (16 * nb + 4 * lg) * kP + 16 * pb + l16;
+            float* dst = fin + (16 * (wv + kSegWaves * j) + 4 * lg) * kP + 16 * pb + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i * kP] = hs[nb][pb][i];
+            for (int i = 0; i < 4; ++i) dst[i * kP] = hs[j][pb][i];
         }
 }
 
@@ -1078,50 +1167,89 @@ bool allow_full_lds(const void* kernel, bool* done) {
 struct FastLayout {
     int64_t nchunks, nblk, units;
     int nseg, seg_chunks;
-    size_t pairs, bt, ct, la_t, lg_t, seg_state, seg_decay, order, total;
+    size_t pairs, bt, ct, la_t, lg_t, seg_state, seg_decay, order, flags, total;
 };
 
+// segments of a walk over `units` units of any length: at most this many
+constexpr int seg_cap(int64_t units) { return units > 0 && units * 2 <= 256 ? (int)(kSegTarget / units) : 1; }
+
 // (with_lg: log2 of the input scale head-major, laid out as la_t; varlen: a packed
-// variable-length batch, never segmented)
+// variable-length batch walked sequence by sequence, never segmented; packed_cap > 0: a packed
+// batch walked as one sequence of seqlen tokens, batch 1, with every array sized for packed_cap
+// tokens and the most segments any length gives, and the token flags at the end)
 FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int Q,
-                       bool with_lg = false, bool varlen = false) {
+                       bool with_lg = false, bool varlen = false, int64_t packed_cap = 0) {
     FastLayout l;
     l.nchunks = (seqlen + Q - 1) / Q;
     l.nblk = batch * ngroups * l.nchunks;
     l.units = batch * nheads;
-    // Two rounds of workgroups per CU for the walk: its time is the same as with one round of
-    // twice-longer segments, while the state-only pass (one wave per segment) gets shorter.
+    // capacities: chunks per unit and segments
+    const int64_t cap_chunks = packed_cap > 0 ? (packed_cap + Q - 1) / Q : l.nchunks;
+    const int64_t cap_blk = batch * ngroups * cap_chunks;
+    // One round of walk workgroups (see kSegTarget).
     if (varlen) {
         l.nseg = 1;
         l.seg_chunks = (int)(l.nchunks > 0 ? l.nchunks : 1);
     } else {
         l.nseg = walk_segments(l.units, l.nchunks, kSegTarget, &l.seg_chunks);
     }
+    const int cap_seg = packed_cap > 0 ? (l.nseg > seg_cap(l.units) ? l.nseg : seg_cap(l.units)) : l.nseg;
     size_t off = 0;
-    l.pairs = off; off += (size_t)l.nblk * n_pairs(Q / 16) * 1024;
-    l.bt = off; off += (size_t)l.nblk * N * Q * 2;
-    l.ct = off; off += (size_t)l.nblk * N * Q * 2;
-    l.la_t = off; off += (size_t)l.units * l.nchunks * Q * 4;
+    l.pairs = off; off += (size_t)cap_blk * n_pairs(Q / 16) * 1024;
+    l.bt = off; off += (size_t)cap_blk * N * Q * 2;
+    l.ct = off; off += (size_t)cap_blk * N * Q * 2;
+    l.la_t = off; off += (size_t)l.units * cap_chunks * Q * 4;
     l.lg_t = off;
-    if (with_lg) off += (size_t)l.units * l.nchunks * Q * 4;
+    if (with_lg) off += (size_t)l.units * cap_chunks * Q * 4;
     l.seg_state = l.seg_decay = off;
-    if (l.nseg > 1) {
-        l.seg_state = off; off += (size_t)l.nseg * l.units * N * kP * 4;
-        l.seg_decay = off; off += ((size_t)l.nseg * l.units * 4 + 255) / 256 * 256;
+    if (cap_seg > 1) {
+        l.seg_state = off; off += (size_t)cap_seg * l.units * N * kP * 4;
+        l.seg_decay = off; off += ((size_t)cap_seg * l.units * 4 + 255) / 256 * 256;
     }
     // a packed batch of at most kOrderMax sequences: their order, longest first
     l.order = off;
     if (varlen && batch <= kOrderMax) off += ((size_t)batch * 4 + 255) / 256 * 256;
+    // a packed batch walked as one sequence: the token flags, one int per token of whole chunks
+    l.flags = off;
+    if (packed_cap > 0) off += (size_t)cap_chunks * Q * 4;
     l.total = off;
     return l;
 }
 
-template <int N, int Q, bool DT>
-int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
+// The token flags of a packed batch walked as one sequence (Walk2Params::tok_flags), for the
+// tokens of whole chunks (npad): one workgroup clears them, then marks every nonempty sequence's
+// first token as a start, and as outside every sequence the tokens before the first offset, from
+// the last offset on, and those past a sequence's first `bound` (the length bound every sequence is
+// walked to).  Offsets are clamped into [0, total] as the sequence-by-sequence walk clamps them.
+constexpr int kMarkThreads = 1024;
+__global__ void __launch_bounds__(kMarkThreads) mark_tokens_kernel(const int64_t* seq_off, int64_t nseq, int64_t total,
+                                                                   int64_t bound, int* flags, int64_t npad) {
+    const int tid = threadIdx.x;
+    for (int64_t i = 4 * (int64_t)tid; i < npad; i += 4 * kMarkThreads)
+        *reinterpret_cast<int4*>(flags + i) = int4{0, 0, 0, 0};
+    __syncthreads();
+    auto clampt = [&](int64_t v) { return v < 0 ? (int64_t)0 : (v > total ? total : v); };
+    for (int64_t j = tid; j < nseq; j += kMarkThreads) {
+        const int64_t s = clampt(seq_off[j]);
+        int64_t e = clampt(seq_off[j + 1]);
+        e = e < s ? s : e;
+        if (e > s) atomicOr(flags + s, kFlagStart);
+        for (int64_t t = s + bound; t < e; ++t) atomicOr(flags + t, kFlagStart | kFlagDead);
+    }
+    const int64_t lo = clampt(seq_off[0]), hi = clampt(seq_off[nseq]);
+    for (int64_t t = tid; t < lo; t += kMarkThreads) atomicOr(flags + t, kFlagStart | kFlagDead);
+    for (int64_t t = hi + tid; t < total; t += kMarkThreads) atomicOr(flags + t, kFlagStart | kFlagDead);
+}
+
+// packed_cap > 0: fl describes a packed batch walked as one sequence (batch 1, seqlen = its tokens,
+// no offsets), whose token flags the workspace holds (fast_layout with this packed_cap)
+template <int N, int Q, bool DT, bool PK>
+int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed_cap) {
     static_assert(WalkShape<N, Q>::lds_bytes <= kMaxLds, "walk LDS budget");
     static bool prep_attr[64] = {}, walk_attr[64] = {};
     const bool with_lg = fl.dt && fl.scale_input;
-    const FastLayout lay = fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q, with_lg, fl.seq_off != nullptr);
+    const FastLayout lay =
+        fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q, with_lg, fl.seq_off != nullptr, packed_cap);
     char* ws = reinterpret_cast<char*>(fl.scores);
     __bf16* pairs = reinterpret_cast<__bf16*>(ws + lay.pairs);
     __bf16* bt = reinterpret_cast<__bf16*>(ws + lay.bt);
@@ -1132,7 +1260,7 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.dt, fl.dt_bias, fl.A_log, lg_t,
                   fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0, fl.seq_off, fl.total, nullptr};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
-    if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q, DT>), walk_attr)) return -1;
+    if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q, DT, PK>), walk_attr)) return -1;
     int k = fl.first_launch;
     const size_t plds = prep_lds<N, Q>(), slds = SegStateShape<N, Q>::lds_bytes, wlds = WalkShape<N, Q>::lds_bytes;
     const unsigned pthreads = PrepShape<N, Q>::THREADS;
@@ -1153,20 +1281,66 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     Walk2Params wp{fl.x, la_t, lg_t, ct, fl.D, pairs, bt, fl.init, fl.y, fl.final_state,
                    fl.batch, fl.seqlen, fl.nheads, fl.ngroups, nch, per_xcd,
                    lay.seg_chunks, lay.nseg, reinterpret_cast<float*>(ws + lay.seg_state),
-                   reinterpret_cast<float*>(ws + lay.seg_decay), fl.seq_off, fl.total, order};
+                   reinterpret_cast<float*>(ws + lay.seg_decay), fl.seq_off, fl.total, order,
+                   PK ? reinterpret_cast<const int*>(ws + lay.flags) : nullptr};
     if (lay.nseg > 1) {
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         const int64_t state_work = (lay.nseg - 1) * lay.units;
         Walk2Params sp = wp;
         sp.per_xcd = (state_work + 7) / 8;
-        if (!launch_k(fl, k, seg_state_kernel<N, Q, DT>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kWave), slds, stream, sp))
+        if (!launch_k(fl, k, seg_state_kernel<N, Q, DT, PK>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kSegWaves * kWave), slds,
+                      stream, sp))
             return -1;
         // (each walk workgroup chains the segment states into its own start state)
     }
-    return launch_k(fl, k, walk_fast_kernel<N, Q, DT>, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds, stream,
-                    wp)
+    return launch_k(fl, k, walk_fast_kernel<N, Q, DT, PK>, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds,
+                    stream, wp)
                ? 0
                : -1;
+}
+
+// A packed batch with no initial or final states requested can be walked as one sequence of all
+// its tokens (segmented like a long batched sequence), with the recurrence restarted at every
+// sequence's first token: the work is then proportional to tokens, not to sequences, and long
+// sequences are split over several workgroups.  (Per-sequence states need the sequence-by-sequence
+// walk: a sequence that ends or starts inside a chunk has its state nowhere else.)  The host knows
+// the sequence count, the token count and the length bound, and takes the form with the shorter
+// estimated walk, in chunk periods: sequence by sequence at least the longest sequence's chunks
+// and the chunks of all (sequence, head) walks spread over 256 CUs; as one sequence the chunks of
+// one segment, plus its state pass (~0.35 of them) and the marking and segment-state launches (~2).
+// (Mamba-2 layer tokens, log-normal lengths: 8 / 32 / 128 / 1024 sequences 68.8 / 69.1 / 64.7 /
+// 60.5 us as one sequence, 92 / 62 / 113 / 545 us sequence by sequence.)
+template <int Q>
+bool packed_as_one(const ForwardLaunch& fl) {
+    if (!fl.seq_off || fl.init || fl.final_state || fl.total <= 0) return false;
+    const int64_t nch = (fl.total + Q - 1) / Q;
+    int per = 1;
+    walk_segments(fl.nheads, nch, kSegTarget, &per);
+    const double as_one = 1.35 * per + 2.0;
+    const double longest = (double)((fl.seqlen + Q - 1) / Q);
+    const double spread = std::ceil((double)(nch + fl.batch) * (double)fl.nheads / 256.0);
+    return as_one < (longest > spread ? longest : spread);
+}
+
+template <int N, int Q, bool DT>
+int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
+    if (!packed_as_one<Q>(fl)) return launch_fast_core<N, Q, DT, false>(fl, stream, 0);
+    ForwardLaunch one = fl;
+    one.batch = 1;
+    one.seqlen = fl.total;
+    one.nchunks = (int)((fl.total + Q - 1) / Q);
+    one.seq_off = nullptr;
+    // arrays sized for the most tokens the batch can hold, as the workspace query sizes them
+    const int64_t cap = fl.batch * fl.seqlen;
+    const bool with_lg = fl.dt && fl.scale_input;
+    const FastLayout lay = fast_layout(1, fl.nheads, fl.ngroups, one.seqlen, N, Q, with_lg, false, cap);
+    int* flags = reinterpret_cast<int*>(reinterpret_cast<char*>(fl.scores) + lay.flags);
+    int k = fl.first_launch;
+    if (!launch_k(fl, k, mark_tokens_kernel, dim3(1), dim3(kMarkThreads), 0, stream, fl.seq_off, fl.batch, fl.total,
+                  fl.seqlen, flags, (int64_t)lay.nchunks * Q))
+        return -1;
+    one.first_launch = k;
+    return launch_fast_core<N, Q, DT, true>(one, stream, cap);
 }
 
 }  // namespace
@@ -1187,7 +1361,13 @@ bool fast_path_applies(int dtype, int decay, int N, int P, int chunk, int64_t nh
 
 size_t fast_workspace_bytes(int64_t batch, int64_t nheads, int64_t ngroups, int64_t seqlen, int N, int chunk,
                             bool with_lg, bool varlen) {
-    return fast_layout(batch, nheads, ngroups, seqlen, N, fast_chunk(chunk), with_lg, varlen).total;
+    const int Q = fast_chunk(chunk);
+    const size_t own = fast_layout(batch, nheads, ngroups, seqlen, N, Q, with_lg, varlen).total;
+    if (!varlen) return own;
+    // (a packed batch may be walked as one sequence of up to batch * seqlen tokens)
+    const int64_t cap = batch * seqlen;
+    const size_t one = fast_layout(1, nheads, ngroups, cap, N, Q, with_lg, false, cap).total;
+    return own > one ? own : one;
 }
 
 int launch_forward_fast(const ForwardLaunch& fl, hipStream_t stream) {

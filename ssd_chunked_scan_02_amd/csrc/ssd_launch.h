@@ -121,6 +121,10 @@ struct Walk2Params {
     const int64_t* seq_off;
     int64_t total;
     const int* seq_order;
+    // a packed batch walked as one sequence (batch 1, seqlen = its token count): per token, bit 0
+    // set where a sequence starts and bits 0 and 1 where a token lies outside every sequence (or
+    // past the length bound); null otherwise
+    const int* tok_flags;
 };
 
 // Everything one forward call needs, already validated.

@@ -331,17 +331,39 @@ def call_varlen(lib, dims, cu=FAKE, total=1000, ws_bytes=1 << 30, **over):
                                   p["init"], p["y"], p["fin"], p["ws"], ws_bytes, None, None, 0, None)
 
 
+def packed_as_one_bytes(H, G, N, cap, Q=128, P=64):
+    """The fast path's workspace for a packed batch walked as one sequence of up to `cap` tokens:
+    the batched layout of one sequence of cap tokens (score pairs, B^T, C^T, log a head-major) with
+    segment states for the most segments any length gives (256 // H when 2 H <= 256), then one int
+    of token flags per token of whole chunks."""
+    up = lambda v: (v + 255) // 256 * 256
+    nch = -(-cap // Q)
+    blk = G * nch
+    own = blk * n_pairs(Q // 16) * 1024 + 2 * blk * N * Q * 2 + H * nch * Q * 4
+    segs = 256 // H if 2 * H <= 256 else 1
+    if segs > 1:
+        own += segs * H * N * P * 4 + up(segs * H * 4)
+    return own + nch * Q * 4
+
+
 def test_varlen_workspace_bytes(lib):
-    # a [batch][seqlen] batch's workspace without segmented walks: the same as ssd_forward's when
-    # the batched walk is not segmented either, less when it is
-    # (and on the fast path, for at most 4096 sequences, their order by length: 4 bytes each)
+    # the larger of two layouts on the fast path: a [batch][seqlen] batch's workspace without
+    # segmented walks (the same as ssd_forward's when the batched walk is not segmented either,
+    # less when it is), with, for at most 4096 sequences, their order by length (4 bytes each);
+    # and the packed batch walked as one sequence of batch * seqlen tokens (no per-sequence states)
     many = mamba2_dims(batch=64, seqlen=1000)
     up = lambda v: (v + 255) // 256 * 256
-    assert ssd.ssd_forward_varlen_workspace_bytes(many, 128) == ssd.ssd_forward_workspace_bytes(many, 128) + up(64 * 4)
+    seq_by_seq = ssd.ssd_forward_workspace_bytes(many, 128) + up(64 * 4)
+    as_one = packed_as_one_bytes(24, 1, 128, 64 * 1000)
+    assert as_one > seq_by_seq
+    assert ssd.ssd_forward_varlen_workspace_bytes(many, 128) == as_one
     lots = mamba2_dims(batch=5000, seqlen=64)
-    assert ssd.ssd_forward_varlen_workspace_bytes(lots, 128) == ssd.ssd_forward_workspace_bytes(lots, 128)
+    assert ssd.ssd_forward_varlen_workspace_bytes(lots, 128) == max(ssd.ssd_forward_workspace_bytes(lots, 128),
+                                                                     packed_as_one_bytes(24, 1, 128, 5000 * 64))
     few = mamba2_dims(batch=1, seqlen=65536, nheads=32)
-    assert 0 < ssd.ssd_forward_varlen_workspace_bytes(few, 128) < ssd.ssd_forward_workspace_bytes(few, 128)
+    # (one sequence: walked as one it is the batched layout, segmented alike, plus the flags)
+    assert ssd.ssd_forward_varlen_workspace_bytes(few, 128) == ssd.ssd_forward_workspace_bytes(few, 128) + 65536 * 4
+    assert ssd.ssd_forward_varlen_workspace_bytes(few, 128) == packed_as_one_bytes(32, 1, 128, 65536)
     dd = mamba2_dims(decay=1, dstate=64, batch=1, nheads=2, seqlen=4096)
     assert ssd.ssd_forward_varlen_workspace_bytes(dd, 64) == 0 < ssd.ssd_forward_workspace_bytes(dd, 64)
     assert ssd.ssd_forward_varlen_workspace_bytes(mamba2_dims(), 48) == 0
