@@ -90,6 +90,7 @@ class HipEvents:
 KERNEL_SOURCES = {"prep_kernel": "ssd_fast.hip", "walk_fast_kernel": "ssd_fast.hip", "mark_tokens_kernel": "ssd_fast.hip",
                   "seg_state_kernel": "ssd_fast.hip", "seg_prefix_kernel": "ssd_fast.hip",
                   "walk_diag_pipe_kernel": "ssd_diag.hip", "walk_diag_kernel": "ssd_diag.hip",
+                  "seg_state_diag_kernel": "ssd_diag.hip",
                   "scores_kernel": "ssd_kernels.hip", "walk_kernel": "ssd_kernels.hip",
                   "step_kernel": "ssd_kernels.hip", "discretize_kernel": "ssd_kernels.hip",
                   "skip_kernel": "ssd_kernels.hip", "bwd_states_kernel": "ssd_bwd.hip",
@@ -168,7 +169,7 @@ def kernel_names(cfg, front_end="log_a", segmented=True, packed=0, tokens=0):
     if cfg["decay"] == "diag":
         if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
             if segmented and fast_segments(dict(cfg, chunk=64), 256) > 1:
-                return ["walk_diag_pipe_kernel<%d,%d,state>" % (N, P), "seg_prefix_kernel",
+                return ["seg_state_diag_kernel<%d,%d>" % (N, P), "seg_prefix_kernel",
                         "walk_diag_pipe_kernel<%d,%d>" % (N, P)]
             return ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]
         return ["walk_diag_kernel<%d,%d>" % (N, P)]

@@ -471,43 +471,38 @@ __device__ __forceinline__ short __attribute__((ext_vector_type(4))) tr16(const 
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + (row0 + 4 * g + r) * stride + col0 + 4 * q));
 }
 
-// (FULL = false, the state-only pass, keeps only x, B o u, B, the running sums and the
-// state-row decays: the other buffers have size 0, so three such workgroups fit on a CU)
-template <int N, int P, bool FULL = true>
+template <int N, int P>
 struct DiagPipeLayout {
     static constexpr int Q = kDiagQ, NT = Q / 16, QP = Q + 8, NP = N + 8, CS = N + 4;
     // x staged row-major with rows P + 16 elements apart: eight consecutive rows then start on
     // distinct banks for the transposing reads of its MFMA operands
     static constexpr int XS = P + 16;
     static constexpr int NOFF = NT * (NT - 1) / 2;
-    static constexpr size_t F = FULL ? 1 : 0;
     // offsets in bytes
     static constexpr size_t xt = 0;                                   // x            [Q][XS] bf16
     static constexpr size_t ht = xt + (size_t)Q * XS * 2;            // H^T          [P][NP] bf16
-    static constexpr size_t cc = ht + F * P * NP * 2;                // C o exp(cum) [Q][NP] bf16
-    static constexpr size_t cf = cc + F * Q * NP * 2;                // C o f        [Q][NP] bf16
-    static constexpr size_t bu = cf + F * Q * NP * 2;                // B o u        [Q][NP] bf16
+    static constexpr size_t cc = ht + (size_t)P * NP * 2;            // C o exp(cum) [Q][NP] bf16
+    static constexpr size_t cf = cc + (size_t)Q * NP * 2;            // C o f        [Q][NP] bf16
+    static constexpr size_t bu = cf + (size_t)Q * NP * 2;            // B o u        [Q][NP] bf16
     static constexpr size_t braw = bu + (size_t)Q * NP * 2;          // B            [Q][NP] bf16
     static constexpr size_t craw = braw + (size_t)Q * NP * 2;        // C            [Q][NP] bf16
-    static constexpr size_t cum = craw + F * Q * NP * 2;             // running sums [Q][CS] f32
+    static constexpr size_t cum = craw + (size_t)Q * NP * 2;         // running sums [Q][CS] f32
     static constexpr size_t part = cum + (size_t)Q * CS * 4;         // scan partials [threads/N][N]
     static constexpr size_t beta = part + (size_t)kDiagThreads * 4;  // [NOFF][N]
-    static constexpr size_t el = beta + F * (NOFF + 1) * N * 4;      // [NT][N] decay over each block
+    static constexpr size_t el = beta + (size_t)(NOFF + 1) * N * 4;  // [NT][N] decay over each block
     // score tiles [NT(NT+1)/2][256], then the second state-dimension half of each diagonal tile
     static constexpr size_t sl = el + (size_t)NT * N * 4;
-    static constexpr size_t total = sl + F * (NT * (NT + 1) / 2 + NT) * 256 * 4;
+    static constexpr size_t total = sl + (size_t)(NT * (NT + 1) / 2 + NT) * 256 * 4;
 };
 
-// FULL: the walk.  !FULL: the state-only pass of a segmented walk (H over the segment from a
-// zero state, written to seg_state with the segment's log2 decay per state row in seg_decay).
 // DT: the discretisation front-end (prm.dt): log a = -softplus(dt + bias) exp(A_log[h, n]) is
 // formed as each chunk is staged, and with prm.scale_input the staged B rows carry the input
 // scale softplus(dt + bias) (B-bar = Delta B: B only ever enters as the key/input side).
-template <int N, int P, bool FULL, bool DT = false>
+template <int N, int P, bool DT = false>
 __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams prm) {
     constexpr int kThreads = kDiagThreads, kWaves = kDiagWaves;  // (this kernel's own workgroup)
-    using L = DiagPipeLayout<N, P, FULL>;
-    constexpr int Q = L::Q, NT = L::NT, QP = L::QP, NP = L::NP, CS = L::CS, XS = L::XS;
+    using L = DiagPipeLayout<N, P>;
+    constexpr int Q = L::Q, NT = L::NT, NP = L::NP, CS = L::CS, XS = L::XS;
     constexpr int PB = P / 16, NB = N / 16, NTILE = NB * PB, TPW = (NTILE + kWaves - 1) / kWaves;
     // 16-byte pieces per chunk of log a, of B (and of C) and of x, and per thread (rounded up;
     // the pieces past the total are skipped, which is uniform over a wave)
@@ -532,7 +527,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     const int64_t sidx = seg * units + unit;  // (segment, unit) index of the segment buffers
     if (c1 <= c0) {
         // an empty packed sequence: its final state is its initial state
-        if (FULL && prm.final_state)
+        if (prm.final_state)
             for (int i = tid; i < N * P; i += kThreads)
                 prm.final_state[unit * N * P + i] = prm.init ? prm.init[unit * N * P + i] : 0.f;
         return;
@@ -595,7 +590,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             const int64_t off = ((sq.row0 + t0 + t) * G + g) * N + 8 * c8;
             if (id < BCT) {
                 rb[m] = ld16(Bg + off);
-                if (FULL) rc[m] = ld16(Cg + off);
+                rc[m] = ld16(Cg + off);
             }
         }
 #pragma unroll
@@ -631,7 +626,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                     bv = __builtin_bit_cast(uint4, sv);
                 }
                 st16(Braw + t * NP + 8 * c8, t < len ? bv : zero);
-                if (FULL) st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
+                st16(Craw + t * NP + 8 * c8, t < len ? rc[m] : zero);
             }
         }
 #pragma unroll
@@ -643,9 +638,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 
     // ---- state registers (tiles (nb, pb) dealt round-robin to the waves)
     f32x4 hs[TPW];
-    const float* init = !FULL ? nullptr
-                        : prm.nseg > 1 ? prm.seg_init + sidx * N * P
-                                       : (prm.init ? prm.init + unit * N * P : nullptr);
+    const float* init = prm.nseg > 1 ? prm.seg_init + sidx * N * P : (prm.init ? prm.init + unit * N * P : nullptr);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -658,7 +651,6 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         }
     }
     auto write_state_lds = [&]() {
-        if (!FULL) return;
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int tile = wave + kWaves * j;
@@ -669,7 +661,6 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         }
     };
 
-    float lsum = 0.f;  // (threads < N) the segment's summed log2 a of state row tid
     load_chunk(c0);
     write_state_lds();
     stage_chunk(c0);
@@ -705,20 +696,19 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         __syncthreads();
 
         // ---- 2. factor tables and scaled operands (all from LDS)
-        if (tid < N) lsum += cum[(Q - 1) * CS + tid];
         // decay over each 16-token block per state dimension: E_b = exp(cum_end(b) - cum_end(b-1))
         for (int i = tid; i < NT * N; i += kThreads) {
             const int bk = i / N, n = i % N;
             el[i] = dexp2(cum[(16 * bk + 15) * CS + n] - (bk > 0 ? cum[(16 * bk - 1) * CS + n] : 0.f));
         }
-        for (int i = tid; FULL && i < L::NOFF * N; i += kThreads) {
+        for (int i = tid; i < L::NOFF * N; i += kThreads) {
             const int p = i / N, n = i % N;
             int tb = 1;
             while (offdiag_index(tb + 1, 0) <= p) ++tb;
             const int sb = p - offdiag_index(tb, 0);
             beta[i] = dexp2(cum[(16 * tb) * CS + n] - cum[(16 * sb + 15) * CS + n]);
         }
-        for (int item = tid; FULL && item < Q * (N / 8); item += kThreads) {
+        for (int item = tid; item < Q * (N / 8); item += kThreads) {
             const int t = item / (N / 8), c8 = item % (N / 8);
             const int a = t & ~15, e = t | 15;
             // (C o exp(cum), C o f for the output side; B o u, which also feeds the state update)
@@ -744,20 +734,6 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             *reinterpret_cast<bf16x8*>(Cf + t * NP + 8 * c8) = vcf;
             *reinterpret_cast<bf16x8*>(Bu + t * NP + 8 * c8) = vbu;
         }
-        // (the state-only pass needs B o u alone)
-        for (int item = tid; !FULL && item < Q * (N / 8); item += kThreads) {
-            const int t = item / (N / 8), c8 = item % (N / 8), e = t | 15;
-            const f32x4 ct0 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8);
-            const f32x4 ct1 = *reinterpret_cast<const f32x4*>(cum + t * CS + 8 * c8 + 4);
-            const f32x4 ce0 = *reinterpret_cast<const f32x4*>(cum + e * CS + 8 * c8);
-            const f32x4 ce1 = *reinterpret_cast<const f32x4*>(cum + e * CS + 8 * c8 + 4);
-            const bf16x8 bv = as_bf16x8(ld16(Braw + t * NP + 8 * c8));
-            bf16x8 vbu;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vbu[j] = (__bf16)((float)bv[j] * dexp2((j < 4 ? ce0[j] : ce1[j - 4]) - (j < 4 ? ct0[j] : ct1[j - 4])));
-            *reinterpret_cast<bf16x8*>(Bu + t * NP + 8 * c8) = vbu;
-        }
         __syncthreads();
 
         // ---- 3. masked score tiles S^T[s][t] (s block sb <= t block tb), fp32 in LDS, in
@@ -766,7 +742,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         constexpr int NTILES = NT * (NT + 1) / 2;
         // items: the two state-dimension halves of every diagonal tile (costly: one wave each),
         // then the off-diagonal tiles
-        for (int item = wave; FULL && item < 2 * NT + L::NOFF; item += kWaves) {
+        for (int item = wave; item < 2 * NT + L::NOFF; item += kWaves) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             float* dst;
             if (item >= 2 * NT) {
@@ -808,7 +784,8 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                     const int n = min(q * kWave + lane, N - 1);
                     const float dec = cum[a * CS + n] - cum[(a + 15) * CS + n];
                     const uint64_t bits = __ballot(dec > 2.f * kSplitMax2);
-                    fast |= (N >= kWave ? bits : bits & ((1ull << N) - 1)) << (q * kWave);
+                    constexpr uint64_t kRowMask = N >= kWave ? ~0ull : (1ull << (N % kWave)) - 1;
+                    fast |= (bits & kRowMask) << (q * kWave);
                 }
                 if (nh == 0) {
 #pragma unroll
@@ -892,7 +869,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
 
         // ---- 4. outputs: carried state (C o exp(cum)) H_{k-1}, plus masked scores times x;
         //         two waves per 16-token block, each with half of the head dimension
-        for (int item = wave; FULL && item < 2 * NT; item += kWaves) {
+        for (int item = wave; item < 2 * NT; item += kWaves) {
             constexpr int PH = PB / 2;
             const int tb = item % NT, pb0 = (item / NT) * PH;
             const int tl = 16 * tb + l16;
@@ -961,9 +938,7 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
         load_chunk(min(c + 2, c1 - 1));
     }
 
-    if (!FULL && tid < N) prm.seg_decay[sidx * N + tid] = lsum;
-    float* fin = !FULL ? prm.seg_state + sidx * N * P
-                       : (c1 == nchunks && prm.final_state) ? prm.final_state + unit * N * P : nullptr;
+    float* fin = (c1 == nchunks && prm.final_state) ? prm.final_state + unit * N * P : nullptr;
     if (fin) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
@@ -975,6 +950,183 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
                 for (int i = 0; i < 4; ++i) dst[i * P] = hs[j][i];
             }
         }
+    }
+}
+
+// log2 weight below which exp2 is 0 in fp32 whatever its last-bit error (the smallest denormal
+// is 2^-149), and the log2 of the largest input scale (the front-end's Delta) allowed for
+constexpr float kVanishDiag2 = -160.f;
+constexpr float kLog2ScaleMaxDiag = 64.f;
+
+// seg_state_diag_kernel: the state-only pass of the segmented diagonal walk.  One workgroup per
+// (segment, batch, head) forms the segment's local state (its final state from a zero start) as
+// one sum over its tokens,
+//   H_seg[n, :] = sum_s W_sn B_sn x_s^T,   W_sn = exp(decay of state row n from token s to the
+//   segment's end),
+// the diagonal chunk recurrence unrolled, and the segment's log2 decay per state row.  The chunks
+// are taken last to first, so the decay from a chunk's end to the segment's end is the running sum
+// (per row) of the chunks already done and every W_sn <= 1: the weights go onto B, (B o W)^T x is
+// one bf16 MFMA contraction over the chunk's tokens, and the state registers are only ever
+// accumulated into.  In a workgroup of eight waves, thread (n, part) scans log a down state column
+// n over its part of the chunk's tokens (the partial sums of the parts through LDS) and forms B o W
+// for those tokens; the waves split the N x P state's 16 x 16 tiles.  With the front-end every
+// wave forms the chunk's step sizes, one token per lane (Q = 64), and takes those of its tokens by
+// lane shuffles.  The next chunk's log a (or dt), B and x are loaded while the current one is
+// computed.  Once every row's weights are below 2^-160 (2^-224 with an input scale of up to
+// 2^64), where exp2 is 0 in fp32, the earlier tokens would add exact zeros and the pass stops: the
+// decays it records are then below that bound too, and the prefix of segment states weighs their
+// states by exp2 of them, which is 0 either way.  (The first form ran the 8-wave walk with its
+// per-block factor tables: 30 us at the multiscale shape.)
+constexpr int kSegDiagWaves = 8, kSegDiagThreads = kSegDiagWaves * kWave;
+template <int N, int P>
+struct SegDiagShape {
+    static constexpr int Q = kDiagQ, PARTS = kSegDiagThreads / N, TP = Q / PARTS;
+    // 16-byte pieces of B (and of x) per chunk, and per thread (rounded up; the rest skipped)
+    static constexpr int BCT = Q * N / 8, XT = Q * P / 8;
+    static constexpr int BCI = (BCT + kSegDiagThreads - 1) / kSegDiagThreads, XI = (XT + kSegDiagThreads - 1) / kSegDiagThreads;
+    static constexpr int NS = N + 8, XS = P + 8;  // LDS row strides (elements)
+    static constexpr int NTILE = (N / 16) * (P / 16), TPW = (NTILE + kSegDiagWaves - 1) / kSegDiagWaves;
+    static_assert(PARTS * N == kSegDiagThreads && TP >= 1 && Q == kWave, "segment state shape");
+    // B [Q][NS] bf16, B o W [Q][NS] bf16, x [Q][XS] bf16, partial sums [PARTS][N] f32
+    static constexpr size_t bs = 0, bw = bs + (size_t)Q * NS * 2, xs = bw + (size_t)Q * NS * 2;
+    static constexpr size_t tot = xs + (size_t)Q * XS * 2, lds_bytes = tot + (size_t)PARTS * N * 4;
+};
+
+template <int N, int P, bool DT>
+__global__ void __launch_bounds__(kSegDiagThreads) seg_state_diag_kernel(WalkParams prm) {
+    using S = SegDiagShape<N, P>;
+    constexpr int Q = S::Q, TP = S::TP, BCI = S::BCI, XI = S::XI, NS = S::NS, XS = S::XS;
+    constexpr int PB = P / 16, TPW = S::TPW, NTILE = S::NTILE;
+    const int64_t H = prm.nheads, G = prm.ngroups;
+    const int64_t units = prm.batch * H;
+    const int64_t work = xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * units);
+    if (work < 0) return;
+    const int seg = (int)(work / units);
+    const int64_t unit = work % units;
+    const int64_t b = unit / H, h = unit % H, g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int n = tid % N, part = tid / N;
+    const int64_t row0 = b * prm.seqlen;
+    const int c0 = seg * prm.seg_chunks, c1 = min(c0 + prm.seg_chunks, prm.nchunks);
+    const int64_t sidx = seg * units + unit;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __bf16* Bs = reinterpret_cast<__bf16*>(smem + S::bs);
+    __bf16* BWs = reinterpret_cast<__bf16*>(smem + S::bw);
+    __bf16* Xs = reinterpret_cast<__bf16*>(smem + S::xs);
+    float* tot = reinterpret_cast<float*>(smem + S::tot);
+    const __bf16* xg = static_cast<const __bf16*>(prm.x);
+    const __bf16* Bg = static_cast<const __bf16*>(prm.Bm);
+    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, prm.seqlen - (int64_t)c * Q); };
+    // (DT) -exp(A_log[h, n]) log2(e) of this thread's state row, and the step-size bias
+    const float an = DT ? -expf(prm.A_log[h * N + n]) * kLog2eD : 0.f;
+    const float dtb = DT && prm.dt_bias ? prm.dt_bias[h] : 0.f;
+
+    // prefetch registers: this thread's log a column over its tokens (with the front-end: the dt
+    // of token `lane`), its pieces of B and of x (rows clamped into the sequence, staged as zeros
+    // past its end)
+    float la[DT ? 1 : TP];
+    uint4 rb[BCI], rx[XI];
+    auto load_chunk = [&](int c) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int last = chunk_len(c) - 1;
+        if (DT) {
+            la[0] = prm.dt[(row0 + t0 + min(lane, last)) * H + h];
+        } else {
+#pragma unroll
+            for (int i = 0; i < TP; ++i)
+                la[i] = prm.log_a[((row0 + t0 + min(part * TP + i, last)) * H + h) * N + n];
+        }
+#pragma unroll
+        for (int m = 0; m < BCI; ++m) {
+            const int id = min(tid + kSegDiagThreads * m, S::BCT - 1), t = min(id / (N / 8), last), c8 = id % (N / 8);
+            rb[m] = ld16(Bg + ((row0 + t0 + t) * G + g) * N + 8 * c8);
+        }
+#pragma unroll
+        for (int m = 0; m < XI; ++m) {
+            const int id = min(tid + kSegDiagThreads * m, S::XT - 1), t = min(id / (P / 8), last), c8 = id % (P / 8);
+            rx[m] = ld16(xg + ((row0 + t0 + t) * H + h) * P + 8 * c8);
+        }
+    };
+
+    f32x4 hs[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float sfx = 0.f;  // log2 decay of row n from the end of the chunk in hand to the segment's end
+    // (with an input scale its B entries carry a factor of up to 2^64)
+    const float vanish = kVanishDiag2 - (DT && prm.scale_input ? kLog2ScaleMaxDiag : 0.f);
+    load_chunk(c1 - 1);
+    for (int c = c1 - 1; c >= c0; --c) {
+        const int len = chunk_len(c);
+        // stage B and x (and the step size of each token)
+#pragma unroll
+        for (int m = 0; m < BCI; ++m) {
+            const int id = tid + kSegDiagThreads * m, t = id / (N / 8), c8 = id % (N / 8);
+            if (id < S::BCT) st16(Bs + t * NS + 8 * c8, t < len ? rb[m] : uint4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int m = 0; m < XI; ++m) {
+            const int id = tid + kSegDiagThreads * m, t = id / (P / 8), c8 = id % (P / 8);
+            if (id < S::XT) st16(Xs + t * XS + 8 * c8, t < len ? rx[m] : uint4{0u, 0u, 0u, 0u});
+        }
+        // (DT) the step sizes of this thread's tokens, from the lanes that formed them
+        float dt_i[DT ? TP : 1];
+        if (DT) {
+            const float delta = softplus_hw(la[0] + dtb);  // of token `lane`
+#pragma unroll
+            for (int i = 0; i < TP; ++i) dt_i[i] = __shfl(delta, part * TP + i, kWave);
+        }
+        // log a of this thread's tokens in log2 units, summed down its part of column n
+        float cum[TP], run = 0.f;
+#pragma unroll
+        for (int i = 0; i < TP; ++i) {
+            const float l2 = DT ? dt_i[i] * an : la[i] * kLog2eD;
+            run += part * TP + i < len ? l2 : 0.f;
+            cum[i] = run;
+        }
+        tot[part * N + n] = run;
+        if (c > c0) load_chunk(c - 1);
+        __syncthreads();  // staged; partial sums in
+        float before = 0.f, last = 0.f;
+#pragma unroll
+        for (int q = 0; q < S::PARTS; ++q) {
+            const float v = tot[q * N + n];
+            before += q < part ? v : 0.f;
+            last += v;
+        }
+        // B o W of this thread's tokens in row n (with the front-end's input scale: Delta_t B_tn)
+#pragma unroll
+        for (int i = 0; i < TP; ++i) {
+            const int t = part * TP + i;
+            const float w = dexp2(sfx + (last - (before + cum[i])));
+            const float sc = DT && prm.scale_input ? dt_i[i] : 1.f;
+            BWs[t * NS + n] = (__bf16)((float)Bs[t * NS + n] * (w * sc));
+        }
+        __syncthreads();  // B o W in
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wave + kSegDiagWaves * j, nb = tile / PB, pb = tile % PB;
+            if (tile < NTILE)
+#pragma unroll
+                for (int k = 0; k < Q / 32; ++k)
+                    hs[j] = mfma_bf16(x_frag<false>(BWs, NS, 16 * nb, k, lane), x_frag<false>(Xs, XS, 16 * pb, k, lane),
+                                      hs[j]);
+        }
+        sfx += last;
+        // every read of this chunk's tiles done before the next chunk is staged; and the pass
+        // stops together once no row's weights are left
+        if (__syncthreads_and(sfx < vanish ? 1 : 0)) break;
+    }
+
+    if (part == 0) prm.seg_decay[sidx * N + n] = sfx;
+    const int l16 = lane % 16, lg = lane / 16;
+    float* fin = prm.seg_state + sidx * N * P;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int tile = wave + kSegDiagWaves * j, nb = tile / PB, pb = tile % PB;
+        if (tile >= NTILE) continue;
+        float* dst = fin + (16 * nb + 4 * lg) * P + 16 * pb + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i * P] = hs[j][i];
     }
 }
 
@@ -1060,9 +1212,7 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
     if (!attr_set[dev]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, true, DT>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, false, DT>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_diag_pipe_kernel<N, P, DT>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds) != hipSuccess)
             return -1;
         attr_set[dev] = true;
@@ -1078,21 +1228,21 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.state) : nullptr,
                   sl.nseg > 1 ? reinterpret_cast<float*>(ws + sl.decay) : nullptr,
                   fl.dt, fl.dt_bias, fl.A_log, fl.scale_input, fl.seq_off, fl.total};
-    const size_t lds = DiagPipeLayout<N, P, true>::total, slds = DiagPipeLayout<N, P, false>::total;
+    const size_t lds = DiagPipeLayout<N, P>::total, slds = SegDiagShape<N, P>::lds_bytes;
     int k = fl.first_launch;
     if (sl.nseg > 1) {
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         WalkParams sp = wp;
         sp.per_xcd = ((sl.nseg - 1) * units + 7) / 8;
         sp.nseg = sl.nseg - 1;
-        if (!launch_k(fl, k, walk_diag_pipe_kernel<N, P, false, DT>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kDiagThreads),
+        if (!launch_k(fl, k, seg_state_diag_kernel<N, P, DT>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kSegDiagThreads),
                       slds, stream, sp))
             return -1;
         if (launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1,
                               stream) != 0)
             return -1;
     }
-    return launch_k(fl, k, walk_diag_pipe_kernel<N, P, true, DT>, dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
+    return launch_k(fl, k, walk_diag_pipe_kernel<N, P, DT>, dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
                     stream, wp)
                ? 0
                : -1;
