@@ -680,7 +680,7 @@ def run_varlen(args, cfg, dev):
         "kernels_ms": {n: t for n, t in zip(names, kernel_avg)},
         "roofline": {"kernel": names[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.workload + "_varlen", names[dom]),
+                     "traffic": measured_traffic("%s_varlen%d" % (args.workload, nseq), names[dom]),
                      "algorithmic_bytes_per_launch": dom_bytes, "tokens_per_launch": total},
     }
     if not args.no_cpu_baseline:
