@@ -55,3 +55,22 @@ def test_oracle_threads_do_not_change_result(orc):
     y1, f1 = orc.forward(*prob, nthreads=1)
     y4, f4 = orc.forward(*prob, nthreads=4)
     assert np.array_equal(y1, y4) and np.array_equal(f1, f4)
+
+
+@pytest.mark.parametrize("diag", [False, True])
+@pytest.mark.parametrize("chunk", [7, 32])
+def test_chunked_model_states_are_the_recurrence_states(orc, diag, chunk):
+    """The states the chunked model carries between chunks (the H_{k-1} that enters chunk k) are
+    the recurrence's state after the first k chunk-lengths of tokens: the oracle run on that
+    prefix alone, from the same initial state, ends in it (the state passing of llms.blog "The
+    Chunk-Wise SSD Algorithm").  Chunk 0 enters with the initial state itself."""
+    rng = np.random.default_rng(300 + chunk)
+    x, log_a, Bm, Cm, D, h0 = _problem(rng, nb=2, T=90, H=3, G=1, P=4, N=5, diag=diag, decay_scale=2.0)
+    _, fin, prev = oracle.chunked_forward(x, log_a, Bm, Cm, D, h0, chunk=chunk, return_states=True)
+    nchunks = -(-x.shape[1] // chunk)
+    assert prev.shape[2] == nchunks
+    _close(prev[:, :, 0], h0, "state entering chunk 0", rtol=0.0)
+    for k in range(1, nchunks):
+        t = k * chunk
+        _, fk = orc.forward(x[:, :t], log_a[:, :t], Bm[:, :t], Cm[:, :t], D, h0)
+        _close(prev[:, :, k], fk, "state entering chunk %d" % k, rtol=1e-11)
