@@ -156,11 +156,13 @@ def kernel_names(cfg, front_end="log_a", segmented=True, packed=0, tokens=0):
     variable-length batch of `packed` sequences (`tokens` in all) with per-sequence states is walked
     sequence by sequence, never segmented, and on the fast path up to 4096 of them are first ranked
     by length; without states the fast path walks it as one sequence of all its tokens (segmented
-    as such), after marking where each sequence starts."""
+    as such), with the tokens where each sequence starts marked by the prep kernel (by a launch
+    of their own beyond 4095 sequences)."""
     Q, N, P = cfg["chunk"], cfg["dstate"], cfg["headdim"]
     fast = cfg["decay"] != "diag" and cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256)
     if packed and fast and not cfg["init"] and not cfg["final"] and packed_as_one(cfg, packed, tokens):
-        return ["mark_tokens_kernel"] + kernel_names(dict(cfg, batch=1, seqlen=tokens), front_end)
+        marking = ["mark_tokens_kernel"] if packed + 1 > 4096 else []
+        return marking + kernel_names(dict(cfg, batch=1, seqlen=tokens), front_end)
     if front_end == "dt":
         fused = (cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64)) if cfg["decay"] == "diag" \
             else (cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256))

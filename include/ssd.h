@@ -195,8 +195,9 @@ int ssd_step_dt(const ssd_dims* dims, float* state, const void* x_t, const float
  *     sequence: one walk per (sequence, head), as a batch; always taken when init_state or
  *     final_state is given.  As one sequence (init_state and final_state both NULL): the packed
  *     axis is walked like one long sequence of total_tokens tokens, segmented over the CUs, with
- *     the recurrence restarted at every sequence's first token (a first launch marks those tokens
- *     from cu_seqlens on the device), so the work follows the token count, not the sequence count.
+ *     the recurrence restarted at every sequence's first token (marked on the device from
+ *     cu_seqlens, by the first kernel, or from 4096 sequences on by a launch of its own), so the
+ *     work follows the token count, not the sequence count.
  *     The host takes the form with the shorter estimated walk from batch, total_tokens,
  *     dims->seqlen and the head count.  Either gives the same operator; outputs differ only in
  *     rounding.

@@ -39,6 +39,15 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// Token flags of a packed batch walked as one sequence (Walk2Params::tok_flags): a token with
+// either bit set begins a new stretch of the recurrence (a sequence start, or a token of no
+// sequence, which stands alone).  Two tokens of one chunk share a sequence exactly when the number
+// of such tokens up to each of them is the same.  Tag of a token outside every sequence: its count
+// plus this (exact in fp32; counts are below 257).
+constexpr int kFlagStart = 1, kFlagDead = 2;
+// offsets of a packed batch that the prep kernel can stage in LDS to mark the tokens itself
+// (more sequences take a marking launch of their own)
+constexpr int kMarkLdsMax = 4096;
 constexpr int kP = 64;            // head dim handled here
 constexpr int kXStr = kP + 8;     // LDS row stride of the x tile, elements
 constexpr float kLog2e = 1.4426950408889634f;
@@ -181,6 +190,19 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
         vb[m] = ld16(Bg + off);
         vc[m] = ld16(Cg + off);
     }
+    // (a packed batch walked as one sequence: its offsets, clamped into [0, total] as the
+    // sequence-by-sequence walk clamps them, for the token flags of this chunk)
+    const bool do_mark = prm.flags && do_rest && g == 0;
+    constexpr int MO = (kMarkLdsMax + kPrepThreads - 1) / kPrepThreads;
+    int mo[MO];
+    if (do_mark) {
+#pragma unroll
+        for (int i = 0; i < MO; ++i) {
+            const int64_t j = tid + (int64_t)kPrepThreads * i;
+            const int64_t v = j <= prm.mark_nseq ? prm.mark_off[j] : 0;
+            mo[i] = (int)(v < 0 ? 0 : (v > prm.total ? prm.total : v));
+        }
+    }
     if (do_rest) {
         // log a head-major: item (head, 4 tokens) gathers 4 rows (consecutive threads read
         // consecutive heads of a row) and writes 16 contiguous bytes; rows clamped, masked below
@@ -236,7 +258,42 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
         st16(Bs + row * NS + 8 * c8, row < len ? vb[m] : zero);
         st16(Cs + row * NS + 8 * c8, row < len ? vc[m] : zero);
     }
+    int* offs = reinterpret_cast<int*>(Cs + Q * NS);  // [mark_nseq + 1]
+    if (do_mark) {
+#pragma unroll
+        for (int i = 0; i < MO; ++i) {
+            const int j = tid + kPrepThreads * i;
+            if (j <= prm.mark_nseq) offs[j] = mo[i];
+        }
+    }
     __syncthreads();
+    if (do_mark && tid < Q) {
+        // Token t of the packed axis: outside every sequence before the first offset and from the
+        // last one on; otherwise in sequence a, the last one starting at or before t (offsets are
+        // non-decreasing, so a nonempty one), which it starts when t is its first token and which
+        // has left it behind when t lies past its first mark_bound tokens.  (Malformed offsets
+        // give wrong flags, and every read stays inside [0, mark_nseq].)  Tokens past the packed
+        // axis, in the last chunk's tail, stay 0.
+        const int64_t t = t0 + tid;
+        const int nseq = (int)prm.mark_nseq;
+        int flag = 0;
+        if (t < prm.total) {
+            if (t < offs[0] || t >= offs[nseq]) {
+                flag = kFlagStart | kFlagDead;
+            } else {
+                int a = 0, z = nseq;  // offs[a] <= t < offs[z] for well-formed offsets
+                while (z - a > 1) {
+                    const int m = (a + z) >> 1;
+                    if (offs[m] <= t) a = m;
+                    else z = m;
+                }
+                const int64_t s0 = offs[a];
+                if (t == s0) flag = kFlagStart;
+                if (t - s0 >= prm.mark_bound) flag = kFlagStart | kFlagDead;
+            }
+        }
+        prm.flags[t] = flag;
+    }
 
     if (do_rest) {
         __bf16* ct = prm.ct + blk * (int64_t)NT * KN * 512 + lane * 8;
@@ -314,12 +371,7 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     return x;
 }
 
-// Token flags of a packed batch walked as one sequence (Walk2Params::tok_flags): a token with
-// either bit set begins a new stretch of the recurrence (a sequence start, or a token of no
-// sequence, which stands alone).  Two tokens of one chunk share a sequence exactly when the number
-// of such tokens up to each of them is the same.  Tag of a token outside every sequence: its count
-// plus this (exact in fp32; counts are below 257).
-constexpr int kFlagStart = 1, kFlagDead = 2;
+// (token flags: see kFlagStart)
 constexpr float kDeadTag = 65536.f;
 // log2 decay that stands for "the recurrence restarts here": exp2 of it is 0, and it stays hugely
 // negative under the additions of ordinary decays.
@@ -1217,7 +1269,8 @@ FastLayout fast_layout(int64_t batch, int64_t nheads, int64_t ngroups, int64_t s
 }
 
 // The token flags of a packed batch walked as one sequence (Walk2Params::tok_flags), for the
-// tokens of whole chunks (npad): one workgroup clears them, then marks every nonempty sequence's
+// tokens of whole chunks (npad), when the batch has too many sequences for the prep kernel to
+// mark them: one workgroup clears them, then marks every nonempty sequence's
 // first token as a start, and as outside every sequence the tokens before the first offset, from
 // the last offset on, and those past a sequence's first `bound` (the length bound every sequence is
 // walked to).  Offsets are clamped into [0, total] as the sequence-by-sequence walk clamps them.
@@ -1242,9 +1295,12 @@ __global__ void __launch_bounds__(kMarkThreads) mark_tokens_kernel(const int64_t
 }
 
 // packed_cap > 0: fl describes a packed batch walked as one sequence (batch 1, seqlen = its tokens,
-// no offsets), whose token flags the workspace holds (fast_layout with this packed_cap)
+// no offsets), whose token flags the workspace holds (fast_layout with this packed_cap); with
+// mark_off non-null the prep kernel writes them from the batch's mark_nseq + 1 offsets (at most
+// kMarkLdsMax) and its length bound, else a marking launch already has
 template <int N, int Q, bool DT, bool PK>
-int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed_cap) {
+int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed_cap, const int64_t* mark_off = nullptr,
+                     int64_t mark_nseq = 0, int64_t mark_bound = 0) {
     static_assert(WalkShape<N, Q>::lds_bytes <= kMaxLds, "walk LDS budget");
     static bool prep_attr[64] = {}, walk_attr[64] = {};
     const bool with_lg = fl.dt && fl.scale_input;
@@ -1262,7 +1318,17 @@ int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
     if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q, DT, PK>), walk_attr)) return -1;
     int k = fl.first_launch;
-    const size_t plds = prep_lds<N, Q>(), slds = SegStateShape<N, Q>::lds_bytes, wlds = WalkShape<N, Q>::lds_bytes;
+    size_t plds = prep_lds<N, Q>();
+    const size_t slds = SegStateShape<N, Q>::lds_bytes, wlds = WalkShape<N, Q>::lds_bytes;
+    if (PK && mark_off) {
+        if (mark_nseq < 0 || mark_nseq + 1 > kMarkLdsMax) return -1;
+        pp.mark_off = mark_off;
+        pp.mark_nseq = mark_nseq;
+        pp.mark_bound = mark_bound;
+        pp.flags = reinterpret_cast<int*>(ws + lay.flags);
+        plds += ((size_t)(mark_nseq + 1) * 4 + 15) / 16 * 16;
+        static_assert(prep_lds<N, Q>() + (size_t)kMarkLdsMax * 4 <= kMaxLds, "offsets in the prep kernel's LDS");
+    }
     const unsigned pthreads = PrepShape<N, Q>::THREADS;
     // split each block over two workgroups when even then they fit on the CUs at once
     pp.split = 2 * lay.nblk <= kPrepSplitMax ? 1 : 0;
@@ -1307,9 +1373,10 @@ int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed
 // the sequence count, the token count and the length bound, and takes the form with the shorter
 // estimated walk, in chunk periods: sequence by sequence at least the longest sequence's chunks
 // and the chunks of all (sequence, head) walks spread over 256 CUs; as one sequence the chunks of
-// one segment, plus its state pass (~0.35 of them) and the marking and segment-state launches (~2).
-// (Mamba-2 layer tokens, log-normal lengths: 8 / 32 / 128 / 1024 sequences 68.8 / 69.1 / 64.7 /
-// 60.5 us as one sequence, 92 / 62 / 113 / 545 us sequence by sequence.)
+// one segment, plus its state pass (~0.35 of them), the segment-state launch and the marking in
+// prep (~2).  (Mamba-2 layer tokens, log-normal lengths: 8 / 128 / 1024 sequences 66.5 / 61.5 /
+// 58.9 us as one sequence, 92 / 113 / 545 us sequence by sequence; 32 sequences 60.8 us sequence
+// by sequence, 69 us as one with the marking in a launch of its own.)
 template <int Q>
 bool packed_as_one(const ForwardLaunch& fl) {
     if (!fl.seq_off || fl.init || fl.final_state || fl.total <= 0) return false;
@@ -1334,6 +1401,9 @@ int launch_fast_t(const ForwardLaunch& fl, hipStream_t stream) {
     const int64_t cap = fl.batch * fl.seqlen;
     const bool with_lg = fl.dt && fl.scale_input;
     const FastLayout lay = fast_layout(1, fl.nheads, fl.ngroups, one.seqlen, N, Q, with_lg, false, cap);
+    // (up to kMarkLdsMax - 1 sequences the prep kernel marks the tokens; more take a launch)
+    if (fl.batch + 1 <= kMarkLdsMax && fl.total <= INT32_MAX)
+        return launch_fast_core<N, Q, DT, true>(one, stream, cap, fl.seq_off, fl.batch, fl.seqlen);
     int* flags = reinterpret_cast<int*>(reinterpret_cast<char*>(fl.scores) + lay.flags);
     int k = fl.first_launch;
     if (!launch_k(fl, k, mark_tokens_kernel, dim3(1), dim3(kMarkThreads), 0, stream, fl.seq_off, fl.batch, fl.total,

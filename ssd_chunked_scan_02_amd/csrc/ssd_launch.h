@@ -95,6 +95,15 @@ struct PrepParams {
     const int64_t* seq_off;
     int64_t total;
     int* order;
+    // a packed batch walked as one sequence (flags non-null; the layout is then batch 1 with
+    // seq_off null): the workgroups of group 0 that write the C^T and B^T fragments also write
+    // their chunk's token flags (Walk2Params::tok_flags) from the batch's mark_nseq + 1 offsets
+    // mark_off (at most kMarkLdsMax of them, staged in LDS after the B and C tiles), with
+    // mark_bound the length bound and `total` the packed token count
+    const int64_t* mark_off;
+    int64_t mark_nseq;
+    int64_t mark_bound;
+    int* flags;
 };
 
 struct Walk2Params {

@@ -67,11 +67,15 @@ class _Events:
             self.ev.destroy(h)
 
 
-def _check_per_sequence(y, yr, cu, lengths, tol, skip=()):
+def _check_per_sequence(y, yr, cu, lengths, x, D, dtype):
+    """Every nonempty sequence by itself, on its SSD part under _ssd_part_error's bound: a short
+    sequence's y can nearly cancel (a one-token sequence has y = (C.B + D) x, and C.B close to -D
+    leaves the bf16 rounding of the score C.B as a large part of what remains)."""
     for i, n in enumerate(lengths):
         s, e = int(cu[i]), int(cu[i + 1])
-        if n > 0 and i not in skip:
-            assert rel_l2(y[s:e], yr[s:e]) <= tol, "sequence %d y" % i
+        if n > 0:
+            err, bound = _ssd_part_error(y[s:e], yr[s:e], x[s:e], D, dtype)
+            assert err <= bound, "sequence %d: SSD part %.3e, bound %.3e" % (i, err, bound)
 
 
 @pytest.mark.parametrize("name,over,chunk,lengths,label", CASES, ids=[c[4] for c in CASES])
@@ -88,8 +92,8 @@ def test_packed_as_one_matches_oracle(name, over, chunk, lengths, label):
         y, fin, launches = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], g["cu_seqlens"],
                                                   p["max_seqlen"], g.get("D"), chunk=chunk, workspace=ws, events=events)
     assert fin is None
-    # the token flags, the prep and the walk (and the segment states when segmented)
-    assert launches in (3, 4), launches
+    # the prep (which also marks the tokens) and the walk, and the segment states when segmented
+    assert launches in (2, 3), launches
     yr, _ = oracle.varlen.forward_varlen(oracle.default_oracle(), f64(p["x"]), f64(p["log_a"]), f64(p["B"]),
                                          f64(p["C"]), p["cu_seqlens"].numpy(), f64(p.get("D")), None, want_final=False)
     tol = TOL[cfg["dtype"]]
@@ -98,7 +102,7 @@ def test_packed_as_one_matches_oracle(name, over, chunk, lengths, label):
     es, bound = _ssd_part_error(yg, yr, f64(p["x"]), f64(p.get("D")), cfg["dtype"])
     announce("packed-as-one %s: y %.2e, SSD part %.2e (bound %.2e), %d launches" % (label, ey, es, bound, launches))
     assert ey <= tol and es <= bound, (ey, es, bound)
-    _check_per_sequence(yg, yr, p["cu_seqlens"].numpy(), lengths, tol)
+    _check_per_sequence(yg, yr, p["cu_seqlens"].numpy(), lengths, f64(p["x"]), f64(p.get("D")), cfg["dtype"])
 
 
 def test_packed_as_one_front_end_matches_oracle():
@@ -114,7 +118,7 @@ def test_packed_as_one_front_end_matches_oracle():
         y, fin, launches = ssd.ssd_forward_dt_varlen(g["x"], g["dt"], g["A_log"], g["B"], g["C"], g["cu_seqlens"],
                                                      p["max_seqlen"], g.get("D"), dt_bias=bias.cuda(),
                                                      scale_input=True, chunk=128, events=events)
-    assert fin is None and launches in (3, 4), launches
+    assert fin is None and launches in (2, 3), launches
     delta, la = oracle.discretize.discretize(f64(p["dt"])[None], f64(p["A_log"]), f64(bias), False)
     x = f64(p["x"])
     yr, _ = oracle.varlen.forward_varlen(oracle.default_oracle(), x * delta[0][..., None], la[0], f64(p["B"]),
@@ -125,7 +129,7 @@ def test_packed_as_one_front_end_matches_oracle():
     ey = rel_l2(yg, yr)
     announce("packed-as-one dt: y %.2e (tol %.0e)" % (ey, tol))
     assert ey <= tol, ey
-    _check_per_sequence(yg, yr, p["cu_seqlens"].numpy(), lengths, tol)
+    _check_per_sequence(yg, yr, p["cu_seqlens"].numpy(), lengths, x, f64(p["D"]), cfg["dtype"])
 
 
 def test_packed_as_one_length_bound_and_uncovered_tokens():
@@ -144,7 +148,7 @@ def test_packed_as_one_length_bound_and_uncovered_tokens():
     with _Events() as events:
         _, _, launches = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], cu.cuda(), bound, g.get("D"),
                                                 chunk=128, y=y, events=events)
-    assert launches in (3, 4), launches
+    assert launches in (2, 3), launches
     yg = y.double().cpu().numpy()
     tol = TOL[cfg["dtype"]]
     x, la, Bm, Cm, D = f64(p["x"]), f64(p["log_a"]), f64(p["B"]), f64(p["C"]), f64(p["D"])
@@ -171,7 +175,7 @@ def test_packed_as_one_many_sequences_full_size():
     with _Events() as events:
         y, _, launches = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], g["cu_seqlens"],
                                                 p["max_seqlen"], g.get("D"), chunk=cfg["chunk"], events=events)
-    assert launches == 4, launches
+    assert launches == 3, launches
     yr, _ = oracle.varlen.forward_varlen(oracle.default_oracle(), f64(p["x"]), f64(p["log_a"]), f64(p["B"]),
                                          f64(p["C"]), p["cu_seqlens"].numpy(), f64(p["D"]), None, want_final=False)
     tol = TOL[cfg["dtype"]]
@@ -180,4 +184,29 @@ def test_packed_as_one_many_sequences_full_size():
     es, bound = _ssd_part_error(yg, yr, f64(p["x"]), f64(p["D"]), cfg["dtype"])
     announce("packed-as-one full size: y %.2e, SSD part %.2e (bound %.2e)" % (ey, es, bound))
     assert ey <= tol and es <= bound, (ey, es, bound)
-    _check_per_sequence(yg, yr, p["cu_seqlens"].numpy(), lengths, tol)
+    _check_per_sequence(yg, yr, p["cu_seqlens"].numpy(), lengths, f64(p["x"]), f64(p["D"]), cfg["dtype"])
+
+
+def test_packed_as_one_more_sequences_than_prep_marks():
+    """5000 sequences of 0-9 tokens (more offsets than the prep kernel stages in LDS): the token
+    flags come from a marking launch of their own; every sequence against the oracle."""
+    cfg = ssd_inputs.config("mamba2_layer", nheads=2, init=False)
+    rng = np.random.default_rng(83)
+    lengths = [int(v) for v in rng.integers(0, 10, size=5000)]
+    announce("packed-as-one, marking launch: %d sequences, %d tokens" % (len(lengths), sum(lengths)))
+    p = ssd_inputs.packed_inputs(cfg, lengths, 79)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    with _Events() as events:
+        y, _, launches = ssd.ssd_forward_varlen(g["x"], g["log_a"], g["B"], g["C"], g["cu_seqlens"],
+                                                p["max_seqlen"], g.get("D"), chunk=128, events=events)
+    # the marking, the prep and the walk, and the segment states when segmented
+    assert launches in (3, 4), launches
+    yr, _ = oracle.varlen.forward_varlen(oracle.default_oracle(), f64(p["x"]), f64(p["log_a"]), f64(p["B"]),
+                                         f64(p["C"]), p["cu_seqlens"].numpy(), f64(p["D"]), None, want_final=False)
+    tol = TOL[cfg["dtype"]]
+    yg = y.double().cpu().numpy()
+    ey = rel_l2(yg, yr)
+    es, bound = _ssd_part_error(yg, yr, f64(p["x"]), f64(p["D"]), cfg["dtype"])
+    announce("packed-as-one, marking launch: y %.2e, SSD part %.2e (bound %.2e), %d launches" % (ey, es, bound, launches))
+    assert ey <= tol and es <= bound, (ey, es, bound)
+    _check_per_sequence(yg, yr, p["cu_seqlens"].numpy(), lengths, f64(p["x"]), f64(p["D"]), cfg["dtype"])
