@@ -25,6 +25,22 @@ def test_full_workload_every_unit(name):
     compare_all_units(inp, y, fin, cfg["dtype"], "full " + name)
 
 
+@pytest.mark.parametrize("name", ["mamba2_layer", "long_seq", "gqa_decode", "diag_multiscale"])
+def test_full_workload_without_skip_term(name):
+    """The same full-size inputs with the skip term removed (D absent): y is then the SSD part
+    alone, so the plain bound applies to it pooled and on every unit, with no allowance for the
+    output rounding of a D x that dominates y (the launch configuration is the same: the kernels
+    add D x with D = 0 when it is absent)."""
+    cfg = ssd_inputs.config(name)
+    seed = ssd_inputs.SEEDS[name]
+    announce("full %s without the skip term (seed %d)" % (name, seed))
+    inp = ssd_inputs.make_inputs(cfg, seed)
+    inp["D"] = None
+    g = to_gpu(inp)
+    y, fin = gpu_forward(g, cfg["chunk"], True)
+    compare_all_units(inp, y, fin, cfg["dtype"], "full %s, no skip" % name)
+
+
 def test_decode_continues_forward():
     """gqa_decode: forward over T tokens, then 256 ssd_step calls from its final state, equal
     the oracle run over all T + 256 tokens, for both y and the state, on every (batch, head)."""
