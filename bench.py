@@ -170,9 +170,11 @@ def kernel_names(cfg, front_end="log_a", segmented=True, packed=0, tokens=0):
             return ["discretize_kernel"] + kernel_names(cfg) + (["skip_kernel"] if cfg["skip"] else [])
     if cfg["decay"] == "diag":
         if cfg["dtype"] == "bf16" and Q == 64 and N in (32, 64) and P in (32, 64):
-            if segmented and fast_segments(dict(cfg, chunk=64), 256) > 1:
-                return ["seg_state_diag_kernel<%d,%d>" % (N, P), "seg_prefix_kernel",
-                        "walk_diag_pipe_kernel<%d,%d>" % (N, P)]
+            nseg = fast_segments(dict(cfg, chunk=64), 256) if segmented else 1
+            if nseg > 1:
+                # (up to 4 segments the walk chains the segment states itself)
+                prefix = ["seg_prefix_kernel"] if nseg > 4 else []
+                return ["seg_state_diag_kernel<%d,%d>" % (N, P)] + prefix + ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]
             return ["walk_diag_pipe_kernel<%d,%d>" % (N, P)]
         return ["walk_diag_kernel<%d,%d>" % (N, P)]
     if cfg["dtype"] == "bf16" and P == 64 and N in (64, 128) and Q in (64, 128, 256):

@@ -495,6 +495,10 @@ struct DiagPipeLayout {
     static constexpr size_t total = sl + (size_t)(NT * (NT + 1) / 2 + NT) * 256 * 4;
 };
 
+// segments of a diagonal walk whose states each walk workgroup chains itself (a workgroup of the
+// last segment reads kDiagChainMax - 1 local states of N x P floats); more go through a prefix launch
+constexpr int kDiagChainMax = 4;
+
 // DT: the discretisation front-end (prm.dt): log a = -softplus(dt + bias) exp(A_log[h, n]) is
 // formed as each chunk is staged, and with prm.scale_input the staged B rows carry the input
 // scale softplus(dt + bias) (B-bar = Delta B: B only ever enters as the key/input side).
@@ -637,8 +641,14 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     };
 
     // ---- state registers (tiles (nb, pb) dealt round-robin to the waves)
+    // The state entering the segment: the caller's initial state for the first one; for a later
+    // one either the prefix launch's chained state (seg_init), or, with seg_init null, the chain
+    // h <- exp2(decay_j) o h + state_j over the segments j < seg run here from the caller's initial
+    // state (per state dimension n; local states and log2 decays from seg_state_diag_kernel).
     f32x4 hs[TPW];
-    const float* init = prm.nseg > 1 ? prm.seg_init + sidx * N * P : (prm.init ? prm.init + unit * N * P : nullptr);
+    const bool chain = prm.nseg > 1 && !prm.seg_init;
+    const float* init = prm.nseg > 1 && !chain ? prm.seg_init + sidx * N * P
+                                               : (prm.init ? prm.init + unit * N * P : nullptr);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         hs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -650,6 +660,37 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
             for (int i = 0; i < 4; ++i) hs[j][i] = src[i * P];
         }
     }
+    // (the chain's loads issued here, with the first chunk's; its arithmetic once they are in)
+    constexpr int CH = kDiagChainMax - 1;
+    f32x4 cst[CH][TPW], cdc[CH][TPW];
+    if (chain) {
+#pragma unroll
+        for (int js = 0; js < CH; ++js)
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                const int tile = wave + kWaves * j;
+                cst[js][j] = cdc[js][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (js < seg && tile < NTILE) {
+                    const int nb = tile / PB, pb = tile % PB, n = 16 * nb + 4 * lg;
+                    const float* src = prm.seg_state + (js * units + unit) * N * P + n * P + 16 * pb + l16;
+                    const float* dc = prm.seg_decay + (js * units + unit) * N + n;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        cst[js][j][i] = src[i * P];
+                        cdc[js][j][i] = dc[i];
+                    }
+                }
+            }
+    }
+    auto chain_states = [&]() {
+#pragma unroll
+        for (int js = 0; js < CH; ++js)
+#pragma unroll
+            for (int j = 0; j < TPW; ++j)
+                if (js < seg)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hs[j][i] = exp2f(cdc[js][j][i]) * hs[j][i] + cst[js][j][i];
+    };
     auto write_state_lds = [&]() {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
@@ -662,8 +703,9 @@ __global__ void __launch_bounds__(kDiagThreads) walk_diag_pipe_kernel(WalkParams
     };
 
     load_chunk(c0);
-    write_state_lds();
     stage_chunk(c0);
+    if (chain) chain_states();
+    write_state_lds();
     load_chunk(min(c0 + 1, c1 - 1));
 
     for (int c = c0; c < c1; ++c) {
@@ -1230,6 +1272,10 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
                   fl.dt, fl.dt_bias, fl.A_log, fl.scale_input, fl.seq_off, fl.total};
     const size_t lds = DiagPipeLayout<N, P>::total, slds = SegDiagShape<N, P>::lds_bytes;
     int k = fl.first_launch;
+    // (up to kDiagChainMax segments each walk workgroup chains the segment states into its own
+    // start state; more take a prefix launch, whose chained states the walk then reads)
+    const bool chain = sl.nseg <= kDiagChainMax;
+    if (chain) wp.seg_init = nullptr;
     if (sl.nseg > 1) {
         // (the last segment's local state is never needed: only segments 0 .. nseg-2)
         WalkParams sp = wp;
@@ -1238,8 +1284,8 @@ int launch_diag_pipe_t(const ForwardLaunch& fl, hipStream_t stream) {
         if (!launch_k(fl, k, seg_state_diag_kernel<N, P, DT>, dim3((unsigned)(8 * sp.per_xcd)), dim3(kSegDiagThreads),
                       slds, stream, sp))
             return -1;
-        if (launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P, sl.nseg, 1,
-                              stream) != 0)
+        if (!chain && launch_seg_prefix(fl, k, fl.init, wp.seg_init, wp.seg_state, wp.seg_decay, units, N, P,
+                                        sl.nseg, 1, stream) != 0)
             return -1;
     }
     return launch_k(fl, k, walk_diag_pipe_kernel<N, P, DT>, dim3((unsigned)(8 * per_xcd)), dim3(kDiagThreads), lds,
