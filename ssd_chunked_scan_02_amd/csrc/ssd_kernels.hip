@@ -59,6 +59,9 @@ __device__ __forceinline__ float decay_exp(double d) { return expf((float)d); }
 __device__ __forceinline__ float decay_exp(float d) { return __expf(d); }
 
 __host__ __device__ constexpr int tile_index(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
+// score tiles of a block row that the walk reads ahead of the carried-state products: four for
+// states of up to 4096 elements, none above (where the registers are needed for the state)
+template <int N, int P> constexpr int pre_tiles() { return N * P <= 4096 ? 4 : 0; }
 
 // ---------------------------------------------------------------------------------------
 // scores_kernel: one workgroup per (batch, group, chunk); wave w forms causal tiles
@@ -125,6 +128,7 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
     constexpr int NTILE = NB * PB;
     constexpr int TPW = (NTILE + kWaves - 1) / kWaves;
     constexpr int NP = N + TR::kPad;
+    constexpr int kPre = pre_tiles<N, P>();
 
     const int64_t H = prm.nheads, G = prm.ngroups, Tn = prm.seqlen;
     const int64_t unit = xcd_work_index(blockIdx.x, prm.per_xcd, prm.batch * H);
@@ -185,16 +189,21 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
 
     const float dskip = prm.D ? prm.D[h] : 0.f;
     const float* scores_bg = prm.scores + (b * G + g) * (int64_t)prm.nchunks * ntiles * 256;
+    // log a of token tid of chunk cc (0 past the sequence end), loaded a chunk ahead of its use
+    auto load_la = [&](int cc) -> CT {
+        const int64_t tt = (int64_t)cc * Q + tid;
+        return (tid < Q && tt < sq.len) ? (CT)prm.log_a[(sq.row0 + tt) * H + h] : (CT)0;
+    };
+    CT la_next = load_la(0);
 
     for (int c = 0; c < nch; ++c) {
         const int64_t t0 = (int64_t)c * Q;
         const int len = (int)min((int64_t)Q, sq.len - t0);
 
         // ---- 1. running sum of log a inside the chunk (tokens past the end add 0)
-        CT v = 0;
-        if (tid < len) v = (CT)prm.log_a[(sq.row0 + t0 + tid) * H + h];
-        v = block_inclusive_scan(v, scan_tmp);
+        CT v = block_inclusive_scan(la_next, scan_tmp);
         if (tid < Q) cum[tid] = v;
+        la_next = load_la(c + 1);
         __syncthreads();
         const CT cum_last = cum[Q - 1];
 
@@ -242,6 +251,14 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
             f32x4 acc[PB];
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // the first kPre score tiles of this block row, read now so that their latency
+            // overlaps the carried-state products (the rest are read where they are used)
+            auto load_tile = [&](int sb) -> f32x4 {
+                return as_f32x4(ld16(scores_c + tile_index(tb, sb) * 256 + lane * 4));
+            };
+            f32x4 pre[kPre > 0 ? kPre : 1];
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) pre[i] = i <= tb ? load_tile(i) : f32x4{0.f, 0.f, 0.f, 0.f};
 
             // carried state: C_t . H_{k-1}, then the decay from the chunk start, exp(cum_t)
             const T* crow = Cg + (trow * G + g) * N;
@@ -257,9 +274,21 @@ __global__ void __launch_bounds__(kThreads) walk_kernel(WalkParams prm) {
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) acc[pb] *= ec;
 
-            // within the chunk: (S o L) X, mask selected before the exp
+            // within the chunk: (S o L) X, mask selected before the exp; the first kPre tiles come
+            // from the registers read above (sb is uniform over the wave: a scalar branch)
             auto masked_tile = [&](int sb) -> f32x4 {
-                f32x4 s4 = as_f32x4(ld16(scores_c + tile_index(tb, sb) * 256 + lane * 4));
+                f32x4 s4;
+                if constexpr (kPre > 0) {
+                    if (sb < kPre) {
+                        s4 = pre[0];
+#pragma unroll
+                        for (int i = 1; i < kPre; ++i) s4 = sb == i ? pre[i] : s4;
+                    } else {
+                        s4 = load_tile(sb);
+                    }
+                } else {
+                    s4 = load_tile(sb);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s = 16 * sb + 4 * lg + i;
