@@ -350,6 +350,8 @@ constexpr int kWalkWaves = 8;
 // segments give the state pass more workgroups but measured slower at the long-sequence workload
 // (255-258 against 249-253 us per forward: walk 175 against 169 us, state pass 31 against 36.5 us).
 constexpr int64_t kSegTarget = 256;
+// bytes of x above which the walk reads x with streaming loads (the MI355X last-level cache is 256 MB)
+constexpr double kXStreamBytes = 128.0 * 1024 * 1024;
 constexpr int kWalkThreads = kWalkWaves * kWave;
 
 // 16-token block handled by output wave `ow` in its r-th round (snake order balances the
@@ -405,6 +407,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // of a group share (C2 walk 44.6 -> 40.8 us against plain stores).
 __device__ __forceinline__ void buffer_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 2);
+}
+// 16-byte global load marked non-temporal (streaming): the line is taken into the caches at the
+// lowest priority, so that a stream read once does not evict what other waves read again.
+__device__ __forceinline__ uint4 ldg16_stream(const void* base, uint32_t off) {
+    return __builtin_bit_cast(
+        uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + off)));
 }
 // 16-byte load through a buffer resource; reads at or past its size return zeros.
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -690,7 +698,8 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
 }
 
 // The state waves of the walk (they also stage everything the output waves read).
-template <int N, int Q, int SW, bool DT, bool PK>
+// XS: x read with streaming loads (ldg16_stream).
+template <int N, int Q, int SW, bool DT, bool PK, bool XS>
 __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
                                                 int lane) {
     const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
@@ -735,7 +744,8 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
         for (int m = 0; m < XCH; ++m) {
             const int id = lane + kWave * m, row = min(QW * SW + id / 8, last), c16 = id % 8;
-            xs[m] = ldg16(xbase, (uint32_t)row * x_row + 16 * c16);
+            const uint32_t off = (uint32_t)row * x_row + 16 * c16;
+            xs[m] = XS ? ldg16_stream(xbase, off) : ldg16(xbase, off);
         }
     };
     auto load_b = [&](int c) {
@@ -963,7 +973,8 @@ __device__ __forceinline__ int64_t packed_work_index(const Walk2Params& prm, int
 // the input side of every factor carries it, so the input term is Delta_s B_s x_s^T.
 // PK: a packed batch walked as one sequence, with the recurrence restarted at every token
 // prm.tok_flags marks (above).
-template <int N, int Q, bool DT, bool PK>
+// XS: x read with streaming loads (the host's choice for walks whose x is larger than the caches).
+template <int N, int Q, bool DT, bool PK, bool XS>
 __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm) {
     const int64_t work = prm.seq_order ? packed_work_index(prm, blockIdx.x)
                                        : xcd_work_index(blockIdx.x, prm.per_xcd, prm.nseg * prm.batch * prm.nheads);
@@ -985,10 +996,10 @@ __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm
         case 1: walk_output_role<N, Q, 1, DT, PK>(prm, L, span, lane); break;
         case 2: walk_output_role<N, Q, 2, DT, PK>(prm, L, span, lane); break;
         case 3: walk_output_role<N, Q, 3, DT, PK>(prm, L, span, lane); break;
-        case 4: walk_state_role<N, Q, 0, DT, PK>(prm, L, span, lane); break;
-        case 5: walk_state_role<N, Q, 1, DT, PK>(prm, L, span, lane); break;
-        case 6: walk_state_role<N, Q, 2, DT, PK>(prm, L, span, lane); break;
-        default: walk_state_role<N, Q, 3, DT, PK>(prm, L, span, lane); break;
+        case 4: walk_state_role<N, Q, 0, DT, PK, XS>(prm, L, span, lane); break;
+        case 5: walk_state_role<N, Q, 1, DT, PK, XS>(prm, L, span, lane); break;
+        case 6: walk_state_role<N, Q, 2, DT, PK, XS>(prm, L, span, lane); break;
+        default: walk_state_role<N, Q, 3, DT, PK, XS>(prm, L, span, lane); break;
     }
 }
 
@@ -1302,7 +1313,7 @@ template <int N, int Q, bool DT, bool PK>
 int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed_cap, const int64_t* mark_off = nullptr,
                      int64_t mark_nseq = 0, int64_t mark_bound = 0) {
     static_assert(WalkShape<N, Q>::lds_bytes <= kMaxLds, "walk LDS budget");
-    static bool prep_attr[64] = {}, walk_attr[64] = {};
+    static bool prep_attr[64] = {}, walk_attr[64] = {}, walk_xs_attr[64] = {};
     const bool with_lg = fl.dt && fl.scale_input;
     const FastLayout lay =
         fast_layout(fl.batch, fl.nheads, fl.ngroups, fl.seqlen, N, Q, with_lg, fl.seq_off != nullptr, packed_cap);
@@ -1316,7 +1327,14 @@ int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed
     PrepParams pp{fl.Bm, fl.Cm, fl.log_a, pairs, bt, ct, la_t, fl.dt, fl.dt_bias, fl.A_log, lg_t,
                   fl.seqlen, fl.nheads, fl.ngroups, nch, lay.nblk, 0, fl.seq_off, fl.total, nullptr};
     if (!allow_full_lds(reinterpret_cast<const void*>(&prep_kernel<N, Q>), prep_attr)) return -1;
-    if (!allow_full_lds(reinterpret_cast<const void*>(&walk_fast_kernel<N, Q, DT, PK>), walk_attr)) return -1;
+    // x read with streaming loads when the walk's x alone is larger than the 256 MB last-level
+    // cache (packed batches excepted): then keeping x would only evict the group-shared operands
+    // that every head of a group reads again.  (Gqa decode workload, 268 MB of x: walk 196 -> 179
+    // us; long sequence 268 MB: forward 256-263 -> 249-251 us; at the Mamba-2 layer shape, 50 MB of
+    // x, the streaming loads cost 2-3 us per forward.)
+    const bool xs = !PK && (double)fl.batch * (double)fl.seqlen * (double)fl.nheads * kP * 2.0 > kXStreamBytes;
+    const auto walk = xs ? walk_fast_kernel<N, Q, DT, PK, !PK> : walk_fast_kernel<N, Q, DT, PK, false>;
+    if (!allow_full_lds(reinterpret_cast<const void*>(walk), xs ? walk_xs_attr : walk_attr)) return -1;
     int k = fl.first_launch;
     size_t plds = prep_lds<N, Q>();
     const size_t slds = SegStateShape<N, Q>::lds_bytes, wlds = WalkShape<N, Q>::lds_bytes;
@@ -1359,7 +1377,7 @@ int launch_fast_core(const ForwardLaunch& fl, hipStream_t stream, int64_t packed
             return -1;
         // (each walk workgroup chains the segment states into its own start state)
     }
-    return launch_k(fl, k, walk_fast_kernel<N, Q, DT, PK>, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds,
+    return launch_k(fl, k, walk, dim3((unsigned)(8 * per_xcd)), dim3(kWalkThreads), wlds,
                     stream, wp)
                ? 0
                : -1;
