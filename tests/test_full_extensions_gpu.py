@@ -59,10 +59,12 @@ def test_varlen_bench_batch_sampled():
         assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (i, ey, ef)
 
 
-@pytest.mark.parametrize("name", ["mamba2_layer", "diag_multiscale"])
+@pytest.mark.parametrize("name", ["mamba2_layer", "diag_multiscale", "gqa_decode", "long_seq"])
 def test_forward_dt_full_workload(name):
     """ssd_forward_dt over the whole workload as ``bench.py --front-end dt`` runs it (dt and A_log in,
-    input scaled, no bias) against the oracle's discretisation and recurrence, every output."""
+    input scaled, no bias) against the oracle's discretisation and recurrence, every output.  (The
+    grouped-heads and long-sequence workloads carry 268 MB of x, which the scalar walk reads with
+    streaming loads.)"""
     import oracle.discretize
     cfg = ssd_inputs.config(name)
     announce("full forward_dt %s" % name)
