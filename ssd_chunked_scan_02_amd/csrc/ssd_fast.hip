@@ -7,7 +7,7 @@
 //                 "pairs" (two 16x16 tiles along s) and the B^T MFMA operand fragments, both
 //                 stored in the lane order the walk reads them, so each is one coalesced
 //                 16-byte load per lane.
-//   walk_fast_kernel  one workgroup (8 waves, two roles) per (batch, head) walks the chunks
+//   walk_fast_kernel  one workgroup (12 waves, three roles) per (batch, head) walks the chunks
 //                 with the fp32 N x P state in registers.  Every global operand of chunk c+1
 //                 is loaded into registers right after its last use in chunk c (one register
 //                 set, rolling), and the one workgroup barrier per chunk orders LDS only, so
@@ -332,20 +332,25 @@ __global__ void __launch_bounds__((PrepShape<N, Q>::THREADS)) prep_kernel(PrepPa
 }
 
 // ---------------------------------------------------------------------------------------
-// walk_fast_kernel: 8 waves per (batch, head) in two roles; wave i runs on SIMD i % 4, so
-// each SIMD interleaves one wave of each role.  Each role body is compiled once per wave
-// index, so every causal branch and block index below is resolved at compile time.
+// walk_fast_kernel: 12 waves per (batch, head) in three roles; wave i runs on SIMD i % 4, so
+// each SIMD interleaves one wave of each role (three waves per SIMD, at most 168 VGPRs each).
+// Each role body is compiled once per wave index, so every causal branch and block index below
+// is resolved at compile time.
 //   output waves 0-3: y of their 16-token blocks for chunk c, from H_{k-1} (LDS), the staged
-//       x and decay factors of chunk c, C rows and score pairs (registers).
+//       x and decay factors of chunk c, C rows and score pairs (registers); y staged in LDS.
 //   state waves 4-7: H_k = exp(cum_last) H_{k-1} + B^T (w o X) for chunk c, written to the
-//       other LDS state buffer; then they prepare chunk c+1 for everyone: running sums of
-//       log a (wave-wide DPP scan), decay factors, x staged raw and weighted by w.
+//       other LDS state buffer.
+//   helper waves 8-11: chunk c+1 for everyone (running sums of log a by a wave-wide DPP scan,
+//       decay factors, x staged raw and weighted by w) and the stores of chunk c-1's y.
 // One LDS barrier per chunk; everything written for chunk c+1 goes to the other of two
-// buffers, whose previous contents (chunk c-1) every wave finished before the last barrier.
+// buffers (y: staged for chunk c, stored during chunk c+1), whose previous contents every wave
+// finished before the last barrier.  (Two roles, with the state waves also doing the helpers'
+// work and the output waves storing y, took 42.1-44.3 us for the walk at the Mamba-2 layer
+// shape; three roles 41.9-42.0 us.)
 //
 // Global addresses are a wave-uniform 64-bit base per chunk plus a 32-bit per-lane byte
 // offset (the host only takes this path when every offset inside a chunk fits).
-constexpr int kWalkWaves = 8;
+constexpr int kWalkWaves = 12;
 // workgroups of a segmented fast walk: one round (one per CU).  Two rounds of half as long
 // segments give the state pass more workgroups but measured slower at the long-sequence workload
 // (255-258 against 249-253 us per forward: walk 175 against 169 us, state pass 31 against 36.5 us).
@@ -435,10 +440,11 @@ struct WalkShape {
     // factor: cum2 - log2 of the input scale, written only with one), tag [Q] (a packed batch
     // walked as one sequence: the count of sequence starts up to each token, plus kDeadTag for a
     // token outside every sequence; written only then)
-    static constexpr int FSZ = 5 * Q + NT * Q + NT;
+    // el [4]: exp(cum_last) in its first float (the state's decay over the chunk), padded
+    static constexpr int FSZ = 5 * Q + NT * Q + NT + 4;
     static constexpr int YROWS = 16 * TBW;  // output rows of one output wave per chunk
     static constexpr size_t lds_bytes =
-        (size_t)(4 * Q * kXStr + 2 * kP * HS + 4 * YROWS * kXStr) * 2 + (size_t)2 * FSZ * 4;
+        (size_t)(4 * Q * kXStr + 2 * kP * HS + 8 * YROWS * kXStr) * 2 + (size_t)2 * FSZ * 4;
 };
 
 // Factors of one chunk, with cum the running sum of log a inside the chunk (inclusive),
@@ -454,14 +460,14 @@ struct WalkLds {
     __bf16* Xs;  // [2][Q][kXStr] x
     __bf16* Xw;  // [2][Q][kXStr] w o x
     __bf16* Hs;  // [2][kP][HS] H^T, bf16
-    __bf16* Ys;  // [4][YROWS][kXStr] each output wave's rows of y, staged for full-row stores
+    __bf16* Ys;  // [2][4][YROWS][kXStr] each output wave's rows of y by chunk parity, staged for full-row stores
     float* Fs;   // [2][FSZ]
     __device__ explicit WalkLds(unsigned char* smem) {
         Xs = reinterpret_cast<__bf16*>(smem);
         Xw = Xs + 2 * Q * kXStr;
         Hs = Xw + 2 * Q * kXStr;
         Ys = Hs + 2 * kP * WS::HS;
-        Fs = reinterpret_cast<float*>(Ys + 4 * WS::YROWS * kXStr);
+        Fs = reinterpret_cast<float*>(Ys + 8 * WS::YROWS * kXStr);
     }
     __device__ float* cum2(int buf) const { return Fs + buf * WS::FSZ; }
     __device__ float* f(int buf) const { return Fs + buf * WS::FSZ + Q; }
@@ -470,6 +476,7 @@ struct WalkLds {
     __device__ float* ea(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q; }
     __device__ float* cs2(int buf) const { return Fs + buf * WS::FSZ + 3 * Q + WS::NT * Q + WS::NT; }
     __device__ float* tag(int buf) const { return Fs + buf * WS::FSZ + 4 * Q + WS::NT * Q + WS::NT; }
+    __device__ float* el(int buf) const { return Fs + buf * WS::FSZ + 5 * Q + WS::NT * Q + WS::NT; }
 };
 
 // The piece of work of one workgroup: a (batch, head) unit and the chunks [c0, c1) of one
@@ -507,16 +514,12 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
     constexpr int PB = WS::PB, HS = WS::HS;
     constexpr int KDMAX = wave_tb(TBW - 1, OW) / 2 > wave_tb(0, OW) / 2 ? wave_tb(TBW - 1, OW) / 2 : wave_tb(0, OW) / 2;
     const int l16 = lane % 16, lg = lane / 16;
-    const int64_t H = prm.nheads, G = prm.ngroups;
+    const int64_t G = prm.ngroups;
     const int nchunks = prm.nchunks;
-    const uint32_t y_row = (uint32_t)(H * kP * 2);
     const __bf16* ct0 = prm.ct + (b * G + g) * (int64_t)nchunks * NT * KN * 512;
-    __bf16* yg = static_cast<__bf16*>(prm.y);
     const __bf16* pairs0 = prm.pairs + (b * G + g) * (int64_t)nchunks * NPAIR * 512;
     const float dskip = prm.D ? prm.D[h] : 0.f;
-    constexpr int YROWS = WS::YROWS, YST = YROWS * 8 / kWave;  // 16-byte stores per lane per chunk
-    __bf16* ys = L.Ys + OW * YROWS * kXStr;
-    auto chunk_len = [&](int c) { return (int)min((int64_t)Q, span.len - (int64_t)c * Q); };
+    constexpr int YROWS = WS::YROWS;
 
     // Operands come from the prep kernel in lane order (one contiguous 1 KiB per load); rows
     // past a short chunk's end are zeros there and are never stored here.
@@ -544,18 +547,9 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
 
     load_c(c0);
     load_s(c0);
-    {
-        // As many stores as one chunk's outputs, all dropped (empty resource): the loop is then
-        // entered with the same memory operations in flight as each later chunk, and the
-        // compiler's load counting at the loop head stays exact instead of waiting for stores.
-        const __amdgpu_buffer_rsrc_t none = buffer_rsrc(yg + (span.row0 * H + h) * kP, 0u);
-#pragma unroll
-        for (int m = 0; m < YST; ++m) buffer_store16_nt(none, 0u, uint4{0u, 0u, 0u, 0u});
-    }
     lds_barrier();
 
     for (int c = c0; c < c1; ++c) {
-        const int len = chunk_len(c);
         const int cn = min(c + 1, c1 - 1);
         const int buf = c & 1;
         const __bf16* xsm = L.Xs + buf * Q * kXStr;
@@ -566,6 +560,7 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         const float* Ut = L.U(buf);
         const float* ea = L.ea(buf);
         const float* tagr = L.tag(buf);
+        __bf16* ys = L.Ys + (buf * 4 + OW) * YROWS * kXStr;  // (the helper waves store it next chunk)
 
         // carried state: acc = exp(cum_a) C_t H_{k-1}  (acc rows: p, columns: t)
         f32x4 acc[TBW][PB];
@@ -573,24 +568,18 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         for (int r = 0; r < TBW; ++r)
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) acc[r][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 hfa[KN][PB];
+        // (operands read step by step: with three waves per SIMD the other waves cover the LDS
+        // latency, and the registers stay under the 168 that three waves allow)
 #pragma unroll
-        for (int k = 0; k < KN; ++k)
+        for (int k = 0; k < KN; ++k) {
+            bf16x8 hk[PB];
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) hfa[k][pb] = as_bf16x8(ld16(hcur + (16 * pb + l16) * HS + 32 * k + 8 * lg));
-        // every x operand of the intra-chunk product too, so their LDS latency overlaps the
-        // carried-state MFMAs
-        bf16x8 xall[KDMAX + 1][PB];
-#pragma unroll
-        for (int k = 0; k <= KDMAX; ++k)
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb) xall[k][pb] = token_frag(xsm, kXStr, 16 * pb, k, lane);
-#pragma unroll
-        for (int k = 0; k < KN; ++k)
+            for (int pb = 0; pb < PB; ++pb) hk[pb] = as_bf16x8(ld16(hcur + (16 * pb + l16) * HS + 32 * k + 8 * lg));
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-                for (int r = 0; r < TBW; ++r) acc[r][pb] = mfma_bf16(hfa[k][pb], as_bf16x8(cf[r][k]), acc[r][pb]);
+                for (int r = 0; r < TBW; ++r) acc[r][pb] = mfma_bf16(hk[pb], as_bf16x8(cf[r][k]), acc[r][pb]);
+        }
         load_c(cn);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
 #pragma unroll
@@ -603,7 +592,9 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
         // inside the chunk: (S o L) X over the 32-token steps
 #pragma unroll
         for (int k = 0; k <= KDMAX; ++k) {
-            const bf16x8* xf = xall[k];
+            bf16x8 xf[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) xf[pb] = token_frag(xsm, kXStr, 16 * pb, k, lane);
 #pragma unroll
             for (int r = 0; r < TBW; ++r) {
                 const int tb = wave_tb(r, OW);
@@ -682,40 +673,29 @@ __device__ __forceinline__ void walk_output_role(const Walk2Params& prm, const W
                 store4(ys + (16 * r + l16) * kXStr + 16 * pb + 4 * lg, acc[r][pb][0], acc[r][pb][1], acc[r][pb][2],
                        acc[r][pb][3]);
         }
-        wave_lds_fence();
-        const __amdgpu_buffer_rsrc_t yr =
-            buffer_rsrc(yg + ((span.row0 + (int64_t)c * Q) * H + h) * kP, (uint32_t)len * y_row);
-#pragma unroll
-        for (int m = 0; m < YST; ++m) {
-            const int id = lane + kWave * m, row = id / 8, c8 = id % 8;
-            const int t = 16 * wave_tb(row / 16, OW) + row % 16;
-            // (a packed batch: rows outside every sequence are not written)
-            if (!PK || tagr[t] < kDeadTag)
-                buffer_store16_nt(yr, (uint32_t)t * y_row + 16 * c8, ld16(ys + row * kXStr + 8 * c8));
-        }
         lds_barrier();
     }
 }
 
-// The state waves of the walk (they also stage everything the output waves read).
-// XS: x read with streaming loads (ldg16_stream).
+// The helper waves of the walk: for chunk c + 1 the decay factors (running sums of log a, f, w, U,
+// ea and the state's decay el) and x staged raw and weighted by w, while the other roles work on
+// chunk c; and the y rows the output waves staged for chunk c - 1, stored as whole 128-byte rows.
+// Helper wave SW takes the factors and x rows of the chunk's quarter SW and the y rows of output
+// wave SW.  XS: x read with streaming loads (ldg16_stream).
 template <int N, int Q, int SW, bool DT, bool PK, bool XS>
-__device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
+__device__ __forceinline__ void walk_helper_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
                                                 int lane) {
-    const int64_t b = span.b, h = span.h, g = span.g, unit = span.unit;
+    const int64_t h = span.h, unit = span.unit;
     const int c0 = span.c0, c1 = span.c1;
     using WS = WalkShape<N, Q>;
-    constexpr int NT = WS::NT, KS = WS::KS, NBW = WS::NBW, LA = WS::LA, QW = WS::QW, XCH = WS::XCH;
-    constexpr int PB = WS::PB, HS = WS::HS;
-    const int l16 = lane % 16, lg = lane / 16;
-    const int64_t H = prm.nheads, G = prm.ngroups;
+    constexpr int NT = WS::NT, LA = WS::LA, QW = WS::QW, XCH = WS::XCH;
+    const int64_t H = prm.nheads;
     const int nchunks = prm.nchunks;
     const uint32_t x_row = (uint32_t)(H * kP * 2);
     const float* la0 = prm.la_t + unit * (int64_t)nchunks * Q;
     const float* lg0 = DT ? prm.lg_t + unit * (int64_t)nchunks * Q : nullptr;
     const int* fl0 = PK ? prm.tok_flags : nullptr;
     const __bf16* xg = static_cast<const __bf16*>(prm.x);
-    const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * (N / 16) * KS * 512;
     const uint4 zero = {0u, 0u, 0u, 0u};
     auto chunk_len = [&](int c) { return (int)min((int64_t)Q, span.len - (int64_t)c * Q); };
 
@@ -723,7 +703,6 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
     float lgs[DT ? LA : 1];  // (DT) log2 of the input scale of the same tokens
     int flg[PK ? LA : 1];    // (PK) the token flags of the same tokens
     uint4 xs[XCH];
-    uint4 bt[NBW][KS];
     // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
     // quarter of the chunk; rows clamped into the chunk, masked when staged.  Each is loaded
     // a full chunk ahead of its use.
@@ -748,15 +727,8 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             xs[m] = XS ? ldg16_stream(xbase, off) : ldg16(xbase, off);
         }
     };
-    auto load_b = [&](int c) {
-        const void* base = bt0 + (int64_t)c * (N / 16) * KS * 512;
-#pragma unroll
-        for (int jn = 0; jn < NBW; ++jn)
-#pragma unroll
-            for (int k = 0; k < KS; ++k) bt[jn][k] = ldg16(base, 16 * lane + ((SW + 4 * jn) * KS + k) * 1024);
-    };
-    // Decay factors of chunk c into factor buffer c & 1.  Returns exp(cum_last).
-    auto factors = [&](int c) -> float {
+    // Decay factors of chunk c into factor buffer c & 1, with exp(cum_last) in its el slot.
+    auto factors = [&](int c) {
         const int len = chunk_len(c);
         const int buf = c & 1;
         float cum[LA], run = 0.f;
@@ -827,7 +799,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             const float c2 = PK ? __shfl(cnt[0], (16 * lane) / LA, kWave) : 0.f;
             if (lane < NT) L.ea(buf)[lane] = c2 == 0.f ? fexp2(s2) : 0.f;
         }
-        return cnt_e == 0.f ? fexp2(last2) : 0.f;
+        if (SW == 0 && lane == 0) L.el(buf)[0] = cnt_e == 0.f ? fexp2(last2) : 0.f;
     };
     // x of chunk c into the x buffers c & 1, raw and weighted by w (after factors(c)).
     auto stage_x = [&](int c) {
@@ -851,6 +823,76 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
         }
     };
 
+    // y rows of output wave SW for chunk c, from its staging buffer (parity c & 1), as whole 128-byte
+    // rows (rows past a short chunk's end fall outside the buffer resource and are dropped; with
+    // `none` every store is dropped, which keeps one path through the loop)
+    constexpr int TBW = WS::TBW, YROWS = WS::YROWS, YST = YROWS * 8 / kWave;
+    const uint32_t y_row = (uint32_t)(H * kP * 2);
+    __bf16* yg = static_cast<__bf16*>(prm.y);
+    auto store_y = [&](int c, bool none) {
+        const int len = chunk_len(c);
+        const __bf16* ys = L.Ys + ((c & 1) * 4 + SW) * YROWS * kXStr;
+        const float* tagr = L.tag(c & 1);
+        const __amdgpu_buffer_rsrc_t yr =
+            buffer_rsrc(yg + ((span.row0 + (int64_t)c * Q) * H + h) * kP, none ? 0u : (uint32_t)len * y_row);
+#pragma unroll
+        for (int m = 0; m < YST; ++m) {
+            const int id = lane + kWave * m, row = id / 8, c8 = id % 8;
+            const int t = 16 * wave_tb(row / 16, SW) + row % 16;
+            // (a packed batch: rows outside every sequence are not written)
+            if (!PK || tagr[t] < kDeadTag)
+                buffer_store16_nt(yr, (uint32_t)t * y_row + 16 * c8, ld16(ys + row * kXStr + 8 * c8));
+        }
+    };
+    (void)TBW;
+
+    load_la(c0);
+    load_x(c0);
+    factors(c0);
+    load_la(min(c0 + 1, c1 - 1));
+    stage_x(c0);
+    load_x(min(c0 + 1, c1 - 1));
+    lds_barrier();
+
+    // Per chunk: chunk c - 1's y (before its factor buffer, which holds the packed batch's tags, is
+    // rewritten), the next chunk's factors and x staging, the loads a chunk ahead.  All of it runs
+    // unconditionally (past the last chunk the next chunk's buffers get zeros nobody reads).
+    for (int c = c0; c < c1; ++c) {
+        store_y(c > c0 ? c - 1 : c0, c == c0);
+        factors(c + 1);
+        load_la(min(c + 2, c1 - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
+        stage_x(c + 1);
+        load_x(min(c + 2, c1 - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+    }
+    store_y(c1 - 1, false);
+}
+
+// The state waves of the walk: H_k = exp(cum_last) H_{k-1} + B^T (w o X) for chunk c, with the
+// factors and w o x the helper waves staged, written to the other LDS state buffer.
+template <int N, int Q, int SW, bool DT, bool PK>
+__device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const WalkLds<N, Q>& L, const WalkSpan& span,
+                                                int lane) {
+    const int64_t b = span.b, g = span.g, unit = span.unit;
+    const int c0 = span.c0, c1 = span.c1;
+    using WS = WalkShape<N, Q>;
+    constexpr int KS = WS::KS, NBW = WS::NBW;
+    constexpr int PB = WS::PB, HS = WS::HS;
+    const int l16 = lane % 16, lg = lane / 16;
+    const int64_t G = prm.ngroups;
+    const int nchunks = prm.nchunks;
+    const __bf16* bt0 = prm.bt + (b * G + g) * (int64_t)nchunks * (N / 16) * KS * 512;
+
+    uint4 bt[NBW][KS];  // B^T operands, loaded a full chunk ahead of their use
+    auto load_b = [&](int c) {
+        const void* base = bt0 + (int64_t)c * (N / 16) * KS * 512;
+#pragma unroll
+        for (int jn = 0; jn < NBW; ++jn)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) bt[jn][k] = ldg16(base, 16 * lane + ((SW + 4 * jn) * KS + k) * 1024);
+    };
     // The state entering the first chunk.  For segment s > 0 of a segmented walk it is the chain
     // h <- exp2(decay_j) h + state_j over the segments j < s (local states and log2 decays from
     // seg_state_kernel), started from the caller's initial state.  Where a factor exp2(decay_j)
@@ -897,26 +939,15 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
             }
     };
 
-    load_la(c0);
     load_b(c0);
-    load_x(c0);
-    float el = factors(c0);
-    load_la(min(c0 + 1, c1 - 1));
-    stage_x(c0);
-    load_x(min(c0 + 1, c1 - 1));
     write_state(L.Hs + (c0 & 1) * kP * HS);
     lds_barrier();
 
-    // Per chunk: the next chunk's factors, the state MFMAs, the next chunk's x while they
-    // drain, then the state.  All of it runs unconditionally (past the last chunk the next
-    // chunk's buffers get zeros nobody reads), so the loop body has one path and the
-    // compiler's load counting stays exact.
+    // Per chunk: the state MFMAs, the next chunk's B^T loads while they drain, then the state.
     for (int c = c0; c < c1; ++c) {
         const int cn = min(c + 1, c1 - 1);
         const __bf16* xwm = L.Xw + (c & 1) * Q * kXStr;
-        const float el_next = factors(c + 1);
-        load_la(min(c + 2, c1 - 1));
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a chunk ahead of its use
+        const float el = L.el(c & 1)[0];
         // H_k = exp(cum_last) H_{k-1} + B^T (w o X)
 #pragma unroll
         for (int jn = 0; jn < NBW; ++jn)
@@ -935,10 +966,7 @@ __device__ __forceinline__ void walk_state_role(const Walk2Params& prm, const Wa
 #pragma unroll
                 for (int jn = 0; jn < NBW; ++jn) hs[jn][pb] = mfma_bf16(as_bf16x8(bt[jn][k]), xfa[k][pb], hs[jn][pb]);
         load_b(cn);
-        stage_x(c + 1);
-        load_x(min(c + 2, c1 - 1));
         __builtin_amdgcn_sched_barrier(0);
-        el = el_next;
         write_state(L.Hs + ((c + 1) & 1) * kP * HS);
         lds_barrier();
     }
@@ -996,10 +1024,14 @@ __global__ void __launch_bounds__(kWalkThreads) walk_fast_kernel(Walk2Params prm
         case 1: walk_output_role<N, Q, 1, DT, PK>(prm, L, span, lane); break;
         case 2: walk_output_role<N, Q, 2, DT, PK>(prm, L, span, lane); break;
         case 3: walk_output_role<N, Q, 3, DT, PK>(prm, L, span, lane); break;
-        case 4: walk_state_role<N, Q, 0, DT, PK, XS>(prm, L, span, lane); break;
-        case 5: walk_state_role<N, Q, 1, DT, PK, XS>(prm, L, span, lane); break;
-        case 6: walk_state_role<N, Q, 2, DT, PK, XS>(prm, L, span, lane); break;
-        default: walk_state_role<N, Q, 3, DT, PK, XS>(prm, L, span, lane); break;
+        case 4: walk_state_role<N, Q, 0, DT, PK>(prm, L, span, lane); break;
+        case 5: walk_state_role<N, Q, 1, DT, PK>(prm, L, span, lane); break;
+        case 6: walk_state_role<N, Q, 2, DT, PK>(prm, L, span, lane); break;
+        case 7: walk_state_role<N, Q, 3, DT, PK>(prm, L, span, lane); break;
+        case 8: walk_helper_role<N, Q, 0, DT, PK, XS>(prm, L, span, lane); break;
+        case 9: walk_helper_role<N, Q, 1, DT, PK, XS>(prm, L, span, lane); break;
+        case 10: walk_helper_role<N, Q, 2, DT, PK, XS>(prm, L, span, lane); break;
+        default: walk_helper_role<N, Q, 3, DT, PK, XS>(prm, L, span, lane); break;
     }
 }
 
