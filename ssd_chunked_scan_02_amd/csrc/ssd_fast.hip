@@ -703,7 +703,7 @@ __device__ __forceinline__ void walk_helper_role(const Walk2Params& prm, const W
     float lgs[DT ? LA : 1];  // (DT) log2 of the input scale of the same tokens
     int flg[PK ? LA : 1];    // (PK) the token flags of the same tokens
     uint4 xs[XCH];
-    // log a of the whole chunk (every state wave scans it all) and x rows of this wave's
+    // log a of the whole chunk (every helper wave scans it all) and x rows of this wave's
     // quarter of the chunk; rows clamped into the chunk, masked when staged.  Each is loaded
     // a full chunk ahead of its use.
     auto load_la = [&](int c) {
